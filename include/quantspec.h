@@ -1,0 +1,189 @@
+/*
+ * quantspec.h -- C ABI of the hierarchical INT8 KV cache (QuantSpec) decode-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * A per-(layer, sequence, head) KV cache in two tiers:
+ *
+ *  - a quantized tier: every group of G tokens is quantized once to 8-bit codes with an
+ *    asymmetric scale s and zero-point z per group (keys: one (s, z) per channel over the G
+ *    tokens of the group; values: one (s, z) per token over its head_dim channels), and each
+ *    8-bit code C8 is stored as two 4-bit planes, C8 = 16*C_U + C_L, with s and z shared by both
+ *    planes.  [QuantSpec Guide (aifetchly), "1. Hierarchical Two-Level Quantization with
+ *    Bit-Sharing" and the "Hierarchical Quantizer with Bit-Packing" listing; Pith review of
+ *    arXiv:2502.10424, "What carries the argument" and Fig. 3; Fig. 7 and reference [128] for
+ *    the channel-wise key / token-wise value axes.]
+ *  - a full-precision fp16 tail: a ring of 2G slots made of two G-token halves that holds the
+ *    most recent tokens unquantized until they are committed.  [Pith review, "What carries the
+ *    argument" and "Core claim" (double full-precision buffer of size 2G); QuantSpec Guide,
+ *    "3. Double Full-Precision Cache Buffer (CF1 and CF2)".]
+ *
+ * Two attention passes read the cache:
+ *  - the draft pass reads only the upper plane C_U of the quantized tier (dequantized as
+ *    ((16*C_U + draft_offset) - z) * s) plus the fp16 tail;  [QuantSpec Guide, "Upper 4-Bit
+ *    Representation (Draft)" and unpack_for_draft in the quantizer listing.]
+ *  - the verify pass reads both planes ((C8 - z) * s) plus the fp16 tail, for m = gamma+1 query
+ *    tokens in one pass, causally masked inside the tail.  [QuantSpec Guide, "Lower 4-Bit
+ *    Representation (Residual)" and the verification loop; Pith review, one-line read.]
+ * Both passes split the context into chunks whose softmax partials are merged by their
+ * log-sum-exp (Flash-Decoding style).  [Pith review, reference [128]: appendix E, compatibility of
+ * the full-precision buffer with Flash Decoding.]
+ *
+ * Rejected speculative tokens are removed from the tail (qs_rollback) before they are ever
+ * quantized; qs_flush quantizes the oldest G-token half of the tail once per G committed tokens.
+ * [QuantSpec Guide, "Zero-Overhead Rollback" and "Periodic Group Quantization".]
+ *
+ * Conventions
+ * -----------
+ *  - Every call returns a qs_status.  Nothing throws across this boundary.
+ *  - Every argument is validated before any state changes: on error the cache is unchanged and
+ *    qs_last_error() describes the problem.
+ *  - Pointers named d_* are device pointers (HBM of the current HIP device); pointers named h_*
+ *    are host pointers.  The caller owns all device memory (the arena, q, k, v, out); the
+ *    library owns only the host-side handle.  Device buffers must stay alive until the stream
+ *    has executed the enqueued kernels.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls are
+ *    asynchronous; all bookkeeping (lengths, ring head) lives on the host and is updated at
+ *    enqueue time, so no call synchronizes with the device.  All calls on one cache must be
+ *    ordered on one stream: they share the arena's split workspace.
+ *  - A handle is not thread-safe.
+ *  - fp16 means IEEE binary16; fp32 means IEEE binary32.
+ *
+ * Supported shapes: group == 128, head_dim in {64, 128}, 1 <= gamma_max + 1 <= 16,
+ * 1 <= batch <= QS_MAX_BATCH, max_ctx a positive multiple of group.
+ */
+#ifndef QUANTSPEC_H
+#define QUANTSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QS_MAX_BATCH 64
+#define QS_MAX_QUERIES 16
+
+typedef enum {
+  QS_OK = 0,
+  QS_ERR_INVALID_ARG = 1, /* null pointer, out-of-range layer, unsupported shape, bad count  */
+  QS_ERR_CAPACITY = 2,    /* append past the 2G-slot tail, or flush past max_ctx               */
+  QS_ERR_STATE = 3,       /* rollback of more tokens than the tail holds, verify with m > nt,
+                             attention over a sequence that holds no token                     */
+  QS_ERR_BUFFER = 4,      /* arena null, misaligned or smaller than qs_arena_bytes()           */
+  QS_ERR_DEVICE = 5       /* a HIP runtime call failed (message in qs_last_error)              */
+} qs_status;
+
+typedef struct qs_cache qs_cache; /* opaque host handle */
+
+typedef struct {
+  int32_t n_layers;     /* L >= 1                                                              */
+  int32_t batch;        /* B, 1..QS_MAX_BATCH                                                  */
+  int32_t n_heads;      /* H >= 1 (key/value heads; one query head per key/value head)         */
+  int32_t head_dim;     /* D, 64 or 128                                                        */
+  int32_t group;        /* G, must be 128; the tail ring holds 2G tokens                       */
+  int32_t max_ctx;      /* quantized-token capacity per sequence, positive multiple of G       */
+  int32_t gamma_max;    /* verify accepts m <= gamma_max + 1 queries; gamma_max + 1 <= 16      */
+  int32_t draft_offset; /* constant added to 16*C_U by the draft dequantization: 8 or 0        */
+} qs_config;
+
+/* Byte offsets (from the arena base) and sizes of the arena sections.  Every section starts
+ * on a 256-byte boundary.  The logical layout of each section, with T = max_ctx, NG = T / G:
+ *
+ *  uk, lk   u8  [L][B][H][T][D/2]      key planes, token-major rows.  Byte j of a token row
+ *                                      holds channel 2j in bits 0-3 and channel 2j+1 in bits
+ *                                      4-7 (uk: C_U = C8 >> 4, lk: C_L = C8 & 15).
+ *  uv, lv   u8  [L][B][H][NG][D][G/2]  value planes, channel-major inside each group.  Byte j
+ *                                      of the row of channel d holds token 2j of the group in
+ *                                      bits 0-3 and token 2j+1 in bits 4-7.
+ *  kmeta    f32 [L][B][H][NG][D][2]    key (scale, zero-point) per group and channel.
+ *  vmeta    f32 [L][B][H][T][2]        value (scale, zero-point) per token.
+ *  tail_k,  f16 [L][B][H][2G][D]       fp16 tail ring.  Logical tail token i of a sequence
+ *  tail_v                              lives in slot (head + i) mod 2G, head in {0, G}.
+ *  work     --                         split-softmax workspace (library private).
+ */
+typedef struct {
+  size_t uk, lk, uv, lv, kmeta, vmeta, tail_k, tail_v, work;               /* offsets */
+  size_t uk_bytes, uv_bytes, kmeta_bytes, vmeta_bytes, tail_bytes, work_bytes; /* per section */
+  size_t total;                                                             /* = qs_arena_bytes */
+} qs_layout;
+
+/* Size in bytes of the device arena for `cfg` (0 if cfg is invalid). */
+size_t qs_arena_bytes(const qs_config* cfg);
+
+/* Fills *out with the arena's section offsets for `cfg`.  Host only. */
+qs_status qs_arena_layout(const qs_config* cfg, qs_layout* out);
+
+/* Creates a cache over the caller's arena (d_arena: device pointer, 256-byte aligned, at least
+ * qs_arena_bytes(cfg) bytes).  Every sequence starts empty (nq = nt = 0, head = 0).  The arena
+ * contents need not be initialised.  Host only: enqueues nothing. */
+qs_status qs_cache_create(const qs_config* cfg, void* d_arena, size_t arena_bytes, qs_cache** out);
+
+/* Frees the host handle (never the arena).  NULL is accepted. */
+qs_status qs_cache_destroy(qs_cache* cache);
+
+/* Appends n_b new tokens to the fp16 tail of every sequence b of `layer`:
+ *   d_k, d_v : fp16 [B][n_max][H][D], row (b, i) is read for i < n_b.
+ *   h_n      : host int32 [B] with 0 <= n_b <= n_max, or NULL for n_b = n_max.
+ * Token i goes to logical tail position nt_b + i; then nt_b += n_b.
+ * Errors: QS_ERR_CAPACITY if nt_b + n_b > 2G for any b.  [QuantSpec Guide,
+ * append_speculative_token in the cache-manager listing; Pith review, "What carries the
+ * argument": new tokens are absorbed by the full-precision buffer.] */
+qs_status qs_append(qs_cache* cache, int32_t layer, const void* d_k, const void* d_v,
+                    int32_t n_max, const int32_t* h_n, void* stream);
+
+/* Drops the newest h_n_drop[b] tail tokens of every sequence b (nt_b -= h_n_drop[b]) of
+ * `layer`, or of every layer when layer == -1.  h_n_drop: host int32 [B] (NULL drops nothing).
+ * Quantized tokens are never rolled back: QS_ERR_STATE if h_n_drop[b] > nt_b.  Host only.
+ * [QuantSpec Guide, "Zero-Overhead Rollback"; Pith review, "What carries the argument".] */
+qs_status qs_rollback(qs_cache* cache, int32_t layer, const int32_t* h_n_drop);
+
+/* Quantizes the oldest G tail tokens (one ring half) of every sequence b of `layer` (every
+ * layer when layer == -1) whose nt_b >= max(G, min_tail): computes the key and value
+ * (scale, zero-point) and 8-bit codes, splits each code into C_U and C_L, writes both planes
+ * and the metadata at quantized position nq_b, then nq_b += G, nt_b -= G, head_b ^= G.
+ * Sequences below the threshold are left unchanged.  h_flushed: host int32 [B] (or NULL),
+ * receives 1 for flushed sequences (of the last layer when layer == -1), else 0.
+ * Must be called only when every tail token is committed.
+ * Errors: QS_ERR_CAPACITY if a selected sequence has nq_b + G > max_ctx; QS_ERR_INVALID_ARG
+ * if min_tail > 2G.  [QuantSpec Guide, "Periodic Group Quantization" and the quantizer
+ * listing; Pith review, "What carries the argument" and Fig. 3.] */
+qs_status qs_flush(qs_cache* cache, int32_t layer, int32_t min_tail, void* stream,
+                   int32_t* h_flushed);
+
+/* Draft attention: one query per (sequence, head) over the upper plane of every quantized
+ * token plus every tail token.
+ *   d_q   : fp16 [B][H][D]      d_out : fp32 [B][H][D]
+ *   out = softmax(sm_scale * q . k_j) weighted sum of v_j over all cached tokens j, with
+ *   quantized k, v dequantized as ((16*C_U + draft_offset) - z) * s.
+ * Errors: QS_ERR_STATE if a sequence holds no token.  [QuantSpec Guide, "Upper 4-Bit
+ * Representation (Draft)"; Pith review, one-line read.] */
+qs_status qs_attend_draft(qs_cache* cache, int32_t layer, const void* d_q, float sm_scale,
+                          float* d_out, void* stream);
+
+/* Verify attention: m queries per (sequence, head) over both planes of every quantized token
+ * plus the tail, causally masked: query i sees every quantized token and tail positions
+ * 0 .. nt_b - m + i (the last m tail tokens are the m verified tokens themselves).
+ *   d_q   : fp16 [B][m][H][D]   d_out : fp32 [B][m][H][D]
+ *   quantized k, v dequantized as (C8 - z) * s with C8 = 16*C_U + C_L.
+ * Errors: QS_ERR_INVALID_ARG if m < 1 or m > gamma_max + 1; QS_ERR_STATE if m > nt_b.
+ * [QuantSpec Guide, "Lower 4-Bit Representation (Residual)" and "3. The Self-Speculative
+ * Verification Loop"; Pith review, one-line read.] */
+qs_status qs_attend_verify(qs_cache* cache, int32_t layer, const void* d_q, int32_t m,
+                           float sm_scale, float* d_out, void* stream);
+
+/* Host copies of the bookkeeping of `layer`: h_nq, h_nt, h_head are int32 [B] (any may be
+ * NULL). */
+qs_status qs_get_state(const qs_cache* cache, int32_t layer, int32_t* h_nq, int32_t* h_nt,
+                       int32_t* h_head);
+
+/* Message of the last error on this handle ("" if none).  Valid until the next call. */
+const char* qs_last_error(const qs_cache* cache);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUANTSPEC_H */

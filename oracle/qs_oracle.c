@@ -1,0 +1,425 @@
+/*
+ * qs_oracle.c -- CPU oracle of the hierarchical INT8 KV cache.
+ *
+ * TEST INFRASTRUCTURE.  Plain, slow and written for a reader to check against the pages by
+ * eye; it is the reference the GPU library is compared with and is never linked into it.
+ * Built with gcc -O2 -ffp-contract=off and no fast-math, so every fp32 operation of the
+ * quantizer is a single IEEE-754 operation in round-to-nearest-even.
+ *
+ * Sources (page titles and sections):
+ *  [G]  QuantSpec Guide: Self-Speculative Decoding & Quantized KV (aifetchly blog)
+ *  [R]  Pith review of arXiv:2502.10424, QuantSpec: Self-Speculative Decoding with
+ *       Hierarchical Quantized KV Cache (pith.science)
+ */
+#include "qs_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------------------------- */
+/* fp16                                                                                      */
+/* ---------------------------------------------------------------------------------------- */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.  Normal
+ * numbers are (1 + f/1024) * 2^(e-15); subnormals (e = 0) are (f/1024) * 2^-14; e = 31 is
+ * infinity (f = 0) or NaN. */
+float orc_half_to_float(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int f = h & 1023;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -24);
+  } else if (e == 31) {
+    v = f ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + f), e - 25);
+  }
+  return (float)(sign ? -v : v);
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Quantizer and split                                                                       */
+/* ---------------------------------------------------------------------------------------- */
+
+/* Asymmetric 8-bit quantization of one group, in the order of the quantizer listing of [G]
+ * ("Hierarchical Quantizer with Bit-Packing"), computed in fp32:
+ *   mn, mx = min, max of the group
+ *   s      = (mx - mn) / 255, then clamped to at least 1e-8
+ *   z      = round(-mn / s)                                  (not clamped)
+ *   c      = clamp(round(x / s) + z, 0, 255)
+ * round() is round-half-to-even, like torch.round. */
+void orc_quantize_group(const uint16_t* x, int n, int stride, float* s_out, float* z_out,
+                        uint8_t* c, int cstride) {
+  float mn = orc_half_to_float(x[0]);
+  float mx = mn;
+  for (int i = 1; i < n; ++i) {
+    float v = orc_half_to_float(x[(size_t)i * stride]);
+    if (v < mn) mn = v;
+    if (v > mx) mx = v;
+  }
+  float s = (mx - mn) / 255.0f;
+  if (s < 1e-8f) s = 1e-8f;
+  float z = rintf(-mn / s);
+  for (int i = 0; i < n; ++i) {
+    float v = orc_half_to_float(x[(size_t)i * stride]);
+    float q = rintf(v / s) + z;
+    if (q < 0.0f) q = 0.0f;
+    if (q > 255.0f) q = 255.0f;
+    c[(size_t)i * cstride] = (uint8_t)q;
+  }
+  *s_out = s;
+  *z_out = z;
+}
+
+/* C8 = 2^4 * C_U + C_L ([R] "What carries the argument", Fig. 3): the upper plane is the high
+ * nibble and the lower "error-residual" plane the low nibble of the 8-bit code. */
+static uint8_t upper_nibble(uint8_t c8) { return (uint8_t)(c8 >> 4); }
+static uint8_t lower_nibble(uint8_t c8) { return (uint8_t)(c8 & 15); }
+
+/* Target (verify) dequantization: (C8 - z) * s ([G] unpack_for_target), in fp64. */
+double orc_dequant_full(uint8_t c8, float s, float z) {
+  return ((double)c8 - (double)z) * (double)s;
+}
+
+/* Draft dequantization from the upper plane only: ((C_U << 4) + off - z) * s, off = 8 is the
+ * midpoint centering of [G] unpack_for_draft, off = 0 the bare 2^4 * C_U of [R]. */
+double orc_dequant_upper(uint8_t cu, float s, float z, int off) {
+  return ((double)(16 * (int)cu + off) - (double)z) * (double)s;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Cache                                                                                     */
+/* ---------------------------------------------------------------------------------------- */
+
+struct orc_cache {
+  int L, B, H, D, G, T, NG, gamma_max, off;
+  uint8_t* kc;      /* [L][B][H][T][D] key codes                        */
+  uint8_t* vc;      /* [L][B][H][T][D] value codes                      */
+  float* ks;        /* [L][B][H][NG][D] key scale per group and channel */
+  float* kz;        /* [L][B][H][NG][D] key zero-point                  */
+  float* vs;        /* [L][B][H][T] value scale per token               */
+  float* vz;        /* [L][B][H][T] value zero-point                    */
+  uint16_t* tk;     /* [L][B][H][2G][D] fp16 tail ring (keys)           */
+  uint16_t* tv;     /* [L][B][H][2G][D] fp16 tail ring (values)         */
+  int* nq;          /* [L][B] quantized tokens                          */
+  int* nt;          /* [L][B] tail tokens                               */
+  int* head;        /* [L][B] ring slot of logical tail token 0         */
+};
+
+static size_t lbh(const orc_cache* c, int l, int b, int h) {
+  return ((size_t)l * c->B + b) * c->H + h;
+}
+
+orc_cache* orc_create(int L, int B, int H, int D, int G, int T, int gamma_max, int off) {
+  if (L < 1 || B < 1 || H < 1 || D < 2 || (D & 1) || G < 2 || (G & 1) || T < G || T % G ||
+      gamma_max < 0 || gamma_max + 1 > G)
+    return NULL;
+  orc_cache* c = (orc_cache*)calloc(1, sizeof(orc_cache));
+  if (!c) return NULL;
+  c->L = L; c->B = B; c->H = H; c->D = D; c->G = G; c->T = T; c->NG = T / G;
+  c->gamma_max = gamma_max; c->off = off;
+  size_t nbh = (size_t)L * B * H;
+  c->kc = (uint8_t*)calloc(nbh * T * D, 1);
+  c->vc = (uint8_t*)calloc(nbh * T * D, 1);
+  c->ks = (float*)calloc(nbh * c->NG * D, sizeof(float));
+  c->kz = (float*)calloc(nbh * c->NG * D, sizeof(float));
+  c->vs = (float*)calloc(nbh * T, sizeof(float));
+  c->vz = (float*)calloc(nbh * T, sizeof(float));
+  c->tk = (uint16_t*)calloc(nbh * 2 * G * D, sizeof(uint16_t));
+  c->tv = (uint16_t*)calloc(nbh * 2 * G * D, sizeof(uint16_t));
+  c->nq = (int*)calloc((size_t)L * B, sizeof(int));
+  c->nt = (int*)calloc((size_t)L * B, sizeof(int));
+  c->head = (int*)calloc((size_t)L * B, sizeof(int));
+  if (!c->kc || !c->vc || !c->ks || !c->kz || !c->vs || !c->vz || !c->tk || !c->tv || !c->nq ||
+      !c->nt || !c->head) {
+    orc_destroy(c);
+    return NULL;
+  }
+  return c;
+}
+
+void orc_destroy(orc_cache* c) {
+  if (!c) return;
+  free(c->kc); free(c->vc); free(c->ks); free(c->kz); free(c->vs); free(c->vz);
+  free(c->tk); free(c->tv); free(c->nq); free(c->nt); free(c->head);
+  free(c);
+}
+
+/* Ring slot of logical tail position i of (l, b). */
+static int slot_of(const orc_cache* c, int l, int b, int i) {
+  return (c->head[l * c->B + b] + i) % (2 * c->G);
+}
+
+/* New tokens go to the back of the full-precision buffer, unquantized ([G]
+ * append_speculative_token; [R] "What carries the argument"). */
+int orc_append(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, int n_max,
+               const int* n) {
+  if (!c || layer < 0 || layer >= c->L || !k || !v || n_max < 0) return 1;
+  for (int b = 0; b < c->B; ++b) {
+    int nb = n ? n[b] : n_max;
+    if (nb < 0 || nb > n_max) return 1;
+    if (c->nt[layer * c->B + b] + nb > 2 * c->G) return 2;
+  }
+  for (int b = 0; b < c->B; ++b) {
+    int nb = n ? n[b] : n_max;
+    int* nt = &c->nt[layer * c->B + b];
+    for (int i = 0; i < nb; ++i) {
+      int slot = slot_of(c, layer, b, *nt + i);
+      for (int h = 0; h < c->H; ++h) {
+        const size_t src = (((size_t)b * n_max + i) * c->H + h) * c->D;
+        const size_t dst = (lbh(c, layer, b, h) * 2 * c->G + slot) * c->D;
+        memcpy(&c->tk[dst], &k[src], (size_t)c->D * sizeof(uint16_t));
+        memcpy(&c->tv[dst], &v[src], (size_t)c->D * sizeof(uint16_t));
+      }
+    }
+    *nt += nb;
+  }
+  return 0;
+}
+
+/* Rejected speculative tokens are dropped from the full-precision buffer; the quantized tier
+ * is never touched ([G] "Zero-Overhead Rollback"). */
+int orc_rollback(orc_cache* c, int layer, const int* n_drop) {
+  if (!c || layer < -1 || layer >= c->L) return 1;
+  if (!n_drop) return 0;
+  int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->L : layer + 1;
+  for (int l = l0; l < l1; ++l)
+    for (int b = 0; b < c->B; ++b) {
+      if (n_drop[b] < 0) return 1;
+      if (n_drop[b] > c->nt[l * c->B + b]) return 3;
+    }
+  for (int l = l0; l < l1; ++l)
+    for (int b = 0; b < c->B; ++b) c->nt[l * c->B + b] -= n_drop[b];
+  return 0;
+}
+
+/* Quantizes the oldest G tail tokens (one ring half) of (l, b) into quantized group nq/G:
+ * keys channel-wise over the G tokens, values token-wise over the D channels ([R] Fig. 7,
+ * reference [128]); then the half is released ([G] "Periodic Group Quantization"). */
+static void flush_one(orc_cache* c, int l, int b) {
+  const int G = c->G, D = c->D;
+  const int t0 = c->nq[l * c->B + b];
+  const int g = t0 / G;
+  const int head = c->head[l * c->B + b];
+  for (int h = 0; h < c->H; ++h) {
+    const size_t r = lbh(c, l, b, h);
+    const uint16_t* tk = &c->tk[(r * 2 * G + head) * D]; /* G consecutive slots */
+    const uint16_t* tv = &c->tv[(r * 2 * G + head) * D];
+    uint8_t* kc = &c->kc[(r * c->T + t0) * D];
+    uint8_t* vc = &c->vc[(r * c->T + t0) * D];
+    for (int d = 0; d < D; ++d) /* key group: channel d over tokens t0 .. t0+G-1 */
+      orc_quantize_group(&tk[d], G, D, &c->ks[(r * c->NG + g) * D + d],
+                         &c->kz[(r * c->NG + g) * D + d], &kc[d], D);
+    for (int t = 0; t < G; ++t) /* value group: token t over channels 0 .. D-1 */
+      orc_quantize_group(&tv[(size_t)t * D], D, 1, &c->vs[r * c->T + t0 + t],
+                         &c->vz[r * c->T + t0 + t], &vc[(size_t)t * D], 1);
+  }
+  c->nq[l * c->B + b] += G;
+  c->nt[l * c->B + b] -= G;
+  c->head[l * c->B + b] = (head + G) % (2 * G);
+}
+
+int orc_flush(orc_cache* c, int layer, int min_tail, int* flushed) {
+  if (!c || layer < -1 || layer >= c->L || min_tail > 2 * c->G) return 1;
+  int need = min_tail > c->G ? min_tail : c->G;
+  int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->L : layer + 1;
+  for (int l = l0; l < l1; ++l)
+    for (int b = 0; b < c->B; ++b)
+      if (c->nt[l * c->B + b] >= need && c->nq[l * c->B + b] + c->G > c->T) return 2;
+  for (int l = l0; l < l1; ++l)
+    for (int b = 0; b < c->B; ++b) {
+      int sel = c->nt[l * c->B + b] >= need;
+      if (sel) flush_one(c, l, b);
+      if (flushed) flushed[b] = sel;
+    }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Attention                                                                                 */
+/* ---------------------------------------------------------------------------------------- */
+
+/* One query row of one (l, b, h): plain softmax attention in fp64 over the concatenation of
+ *   - the nq quantized tokens, dequantized with the draft (upper plane) or verify (both planes)
+ *     formula, and
+ *   - the first n_vis tail tokens in logical order (fp16 -> exact).
+ * out_d = sum_j exp(s_j - max) v_jd / sum_j exp(s_j - max),  s_j = sm_scale * q . k_j. */
+static void attend_row(const orc_cache* c, int l, int b, int h, const uint16_t* q, int draft,
+                       int n_vis, double sm_scale, double* score, float* out) {
+  const int D = c->D, G = c->G;
+  const size_t r = lbh(c, l, b, h);
+  const int nq = c->nq[l * c->B + b];
+  const int n = nq + n_vis;
+  double* qd = (double*)malloc((size_t)D * sizeof(double));
+  double* acc = (double*)calloc((size_t)D, sizeof(double));
+  for (int d = 0; d < D; ++d) qd[d] = orc_half_to_float(q[d]);
+
+  for (int t = 0; t < nq; ++t) {
+    const uint8_t* kc = &c->kc[(r * c->T + t) * D];
+    const int g = t / G;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) {
+      float s = c->ks[(r * c->NG + g) * D + d], z = c->kz[(r * c->NG + g) * D + d];
+      double kd = draft ? orc_dequant_upper(upper_nibble(kc[d]), s, z, c->off)
+                        : orc_dequant_full(kc[d], s, z);
+      dot += qd[d] * kd;
+    }
+    score[t] = sm_scale * dot;
+  }
+  for (int j = 0; j < n_vis; ++j) {
+    const uint16_t* kt = &c->tk[(r * 2 * G + slot_of(c, l, b, j)) * D];
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += qd[d] * (double)orc_half_to_float(kt[d]);
+    score[nq + j] = sm_scale * dot;
+  }
+
+  double mx = -INFINITY;
+  for (int j = 0; j < n; ++j)
+    if (score[j] > mx) mx = score[j];
+  double sum = 0.0;
+  for (int j = 0; j < n; ++j) sum += exp(score[j] - mx);
+
+  for (int t = 0; t < nq; ++t) {
+    const double p = exp(score[t] - mx);
+    const uint8_t* vc = &c->vc[(r * c->T + t) * D];
+    const float s = c->vs[r * c->T + t], z = c->vz[r * c->T + t];
+    for (int d = 0; d < D; ++d) {
+      double vd = draft ? orc_dequant_upper(upper_nibble(vc[d]), s, z, c->off)
+                        : orc_dequant_full(vc[d], s, z);
+      acc[d] += p * vd;
+    }
+  }
+  for (int j = 0; j < n_vis; ++j) {
+    const double p = exp(score[nq + j] - mx);
+    const uint16_t* vt = &c->tv[(r * 2 * G + slot_of(c, l, b, j)) * D];
+    for (int d = 0; d < D; ++d) acc[d] += p * (double)orc_half_to_float(vt[d]);
+  }
+  for (int d = 0; d < D; ++d) out[d] = (float)(acc[d] / sum);
+  free(qd);
+  free(acc);
+}
+
+int orc_attend_draft(const orc_cache* c, int layer, const uint16_t* q, double sm_scale,
+                     float* out) {
+  if (!c || layer < 0 || layer >= c->L || !q || !out) return 1;
+  for (int b = 0; b < c->B; ++b)
+    if (c->nq[layer * c->B + b] + c->nt[layer * c->B + b] == 0) return 3;
+  double* score = (double*)malloc(((size_t)c->T + 2 * c->G) * sizeof(double));
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t row = ((size_t)b * c->H + h) * c->D;
+      attend_row(c, layer, b, h, &q[row], 1, c->nt[layer * c->B + b], sm_scale, score,
+                 &out[row]);
+    }
+  free(score);
+  return 0;
+}
+
+/* Query i of the verify block is the (nt - m + i)-th tail token itself: it sees the quantized
+ * tier and tail positions 0 .. nt - m + i (causal). */
+int orc_attend_verify(const orc_cache* c, int layer, const uint16_t* q, int m, double sm_scale,
+                      float* out) {
+  if (!c || layer < 0 || layer >= c->L || !q || !out || m < 1 || m > c->gamma_max + 1) return 1;
+  for (int b = 0; b < c->B; ++b)
+    if (m > c->nt[layer * c->B + b]) return 3;
+  double* score = (double*)malloc(((size_t)c->T + 2 * c->G) * sizeof(double));
+  for (int b = 0; b < c->B; ++b)
+    for (int i = 0; i < m; ++i)
+      for (int h = 0; h < c->H; ++h) {
+        const size_t row = (((size_t)b * m + i) * c->H + h) * c->D;
+        const int n_vis = c->nt[layer * c->B + b] - m + i + 1;
+        attend_row(c, layer, b, h, &q[row], 0, n_vis, sm_scale, score, &out[row]);
+      }
+  free(score);
+  return 0;
+}
+
+int orc_get_state(const orc_cache* c, int layer, int* nq, int* nt, int* head) {
+  if (!c || layer < 0 || layer >= c->L) return 1;
+  for (int b = 0; b < c->B; ++b) {
+    if (nq) nq[b] = c->nq[layer * c->B + b];
+    if (nt) nt[b] = c->nt[layer * c->B + b];
+    if (head) head[b] = c->head[layer * c->B + b];
+  }
+  return 0;
+}
+
+int orc_read_codes(const orc_cache* c, int layer, int b, int h, int which_v, uint8_t* codes) {
+  if (!c || layer < 0 || layer >= c->L || b < 0 || b >= c->B || h < 0 || h >= c->H || !codes)
+    return 1;
+  const size_t r = lbh(c, layer, b, h);
+  memcpy(codes, &(which_v ? c->vc : c->kc)[r * c->T * c->D], (size_t)c->T * c->D);
+  return 0;
+}
+
+int orc_read_meta(const orc_cache* c, int layer, int b, int h, float* kmeta, float* vmeta) {
+  if (!c || layer < 0 || layer >= c->L || b < 0 || b >= c->B || h < 0 || h >= c->H) return 1;
+  const size_t r = lbh(c, layer, b, h);
+  if (kmeta)
+    for (size_t i = 0; i < (size_t)c->NG * c->D; ++i) {
+      kmeta[2 * i] = c->ks[r * c->NG * c->D + i];
+      kmeta[2 * i + 1] = c->kz[r * c->NG * c->D + i];
+    }
+  if (vmeta)
+    for (int t = 0; t < c->T; ++t) {
+      vmeta[2 * t] = c->vs[r * c->T + t];
+      vmeta[2 * t + 1] = c->vz[r * c->T + t];
+    }
+  return 0;
+}
+
+/* Arena layout of one layer, written out index by index from its definition:
+ *   key planes   [B][H][T][D/2]      byte j of token row t: channel 2j in bits 0-3, 2j+1 in 4-7
+ *   value planes [B][H][NG][D][G/2]  byte j of channel row d of group g: token gG+2j in bits
+ *                                    0-3, token gG+2j+1 in bits 4-7
+ *   kmeta [B][H][NG][D][2], vmeta [B][H][T][2], tails [B][H][2G][D] (ring slots). */
+int orc_export_layer(const orc_cache* c, int layer, uint8_t* uk, uint8_t* lk, uint8_t* uv,
+                     uint8_t* lv, float* kmeta, float* vmeta, uint16_t* tail_k,
+                     uint16_t* tail_v) {
+  if (!c || layer < 0 || layer >= c->L) return 1;
+  const int D = c->D, G = c->G, T = c->T, NG = c->NG;
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t r = lbh(c, layer, b, h);
+      const size_t bh = (size_t)b * c->H + h;
+      const int nq = c->nq[layer * c->B + b];
+      for (int t = 0; t < T; ++t)
+        for (int j = 0; j < D / 2; ++j) {
+          uint8_t c0 = t < nq ? c->kc[(r * T + t) * D + 2 * j] : 0;
+          uint8_t c1 = t < nq ? c->kc[(r * T + t) * D + 2 * j + 1] : 0;
+          size_t o = (bh * T + t) * (D / 2) + j;
+          if (uk) uk[o] = (uint8_t)(upper_nibble(c0) | (upper_nibble(c1) << 4));
+          if (lk) lk[o] = (uint8_t)(lower_nibble(c0) | (lower_nibble(c1) << 4));
+        }
+      for (int g = 0; g < NG; ++g)
+        for (int d = 0; d < D; ++d)
+          for (int j = 0; j < G / 2; ++j) {
+            int t0 = g * G + 2 * j, t1 = t0 + 1;
+            uint8_t c0 = t0 < nq ? c->vc[(r * T + t0) * D + d] : 0;
+            uint8_t c1 = t1 < nq ? c->vc[(r * T + t1) * D + d] : 0;
+            size_t o = ((bh * NG + g) * D + d) * (G / 2) + j;
+            if (uv) uv[o] = (uint8_t)(upper_nibble(c0) | (upper_nibble(c1) << 4));
+            if (lv) lv[o] = (uint8_t)(lower_nibble(c0) | (lower_nibble(c1) << 4));
+          }
+      if (kmeta)
+        for (int g = 0; g < NG; ++g)
+          for (int d = 0; d < D; ++d) {
+            size_t o = ((bh * NG + g) * D + d) * 2;
+            int live = (g + 1) * G <= nq;
+            kmeta[o] = live ? c->ks[(r * NG + g) * D + d] : 0.0f;
+            kmeta[o + 1] = live ? c->kz[(r * NG + g) * D + d] : 0.0f;
+          }
+      if (vmeta)
+        for (int t = 0; t < T; ++t) {
+          vmeta[(bh * T + t) * 2] = t < nq ? c->vs[r * T + t] : 0.0f;
+          vmeta[(bh * T + t) * 2 + 1] = t < nq ? c->vz[r * T + t] : 0.0f;
+        }
+      if (tail_k)
+        memcpy(&tail_k[bh * 2 * G * D], &c->tk[r * 2 * G * D], (size_t)2 * G * D * 2);
+      if (tail_v)
+        memcpy(&tail_v[bh * 2 * G * D], &c->tv[r * 2 * G * D], (size_t)2 * G * D * 2);
+    }
+  return 0;
+}

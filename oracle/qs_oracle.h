@@ -1,0 +1,88 @@
+/*
+ * qs_oracle.h -- CPU oracle of the hierarchical INT8 KV cache.
+ *
+ * TEST INFRASTRUCTURE.  This is the plain, slow, obviously-correct reference that the GPU
+ * library is checked against.  Only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark may load it; the library never does.  It shares no code with the GPU library.
+ *
+ * Every function follows the pages' definitions step by step:
+ *  - quantizer: asymmetric per-group min/max quantization to 8 bits, computed in fp32
+ *    ("Hierarchical Quantizer with Bit-Packing" listing of the QuantSpec Guide);
+ *  - split: C_U = C8 >> 4, C_L = C8 & 15, so C8 = 16*C_U + C_L (Pith review of arXiv:2502.10424,
+ *    "What carries the argument"; Fig. 3);
+ *  - key groups are channel-wise over G tokens, value groups token-wise over the head's
+ *    channels (Pith review, Fig. 7 and reference [128]);
+ *  - draft dequantization ((16*C_U + off) - z) * s, verify dequantization (C8 - z) * s, both in
+ *    fp64 (QuantSpec Guide, unpack_for_draft / unpack_for_target);
+ *  - attention: one fp64 softmax over the concatenation of the dequantized quantized tier and
+ *    the fp16 tail (the plain definition; the split-softmax merge of the GPU path reaches it
+ *    exactly in real arithmetic -- Pith review, reference [128], Flash Decoding);
+ *  - tail ring of 2G fp16 slots with append / rollback / flush bookkeeping (QuantSpec Guide,
+ *    "3. Double Full-Precision Cache Buffer (CF1 and CF2)"; Pith review, "Core claim").
+ *
+ * Status codes are the integers 0 (ok), 1 (invalid argument), 2 (capacity), 3 (state).
+ */
+#ifndef QS_ORACLE_H
+#define QS_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* IEEE binary16 bit pattern -> float (exact). */
+float orc_half_to_float(uint16_t h);
+
+/* Quantizes one group of n values x[i * stride] (fp16 bit patterns) to codes c[i * cstride];
+ * writes the fp32 scale and zero-point. */
+void orc_quantize_group(const uint16_t* x, int n, int stride, float* s, float* z, uint8_t* c,
+                        int cstride);
+
+/* Dequantizations, in fp64. */
+double orc_dequant_full(uint8_t c8, float s, float z);
+double orc_dequant_upper(uint8_t cu, float s, float z, int off);
+
+typedef struct orc_cache orc_cache;
+
+/* L layers, B sequences, H heads, head_dim D, group G, quantized capacity T (multiple of G),
+ * gamma_max, draft offset off.  Returns NULL on invalid arguments or allocation failure. */
+orc_cache* orc_create(int L, int B, int H, int D, int G, int T, int gamma_max, int off);
+void orc_destroy(orc_cache* c);
+
+/* k, v: fp16 bits [B][n_max][H][D]; n: [B] or NULL (= n_max). */
+int orc_append(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, int n_max,
+               const int* n);
+/* layer -1 = every layer; n_drop: [B] or NULL. */
+int orc_rollback(orc_cache* c, int layer, const int* n_drop);
+/* layer -1 = every layer; flushed: [B] or NULL. */
+int orc_flush(orc_cache* c, int layer, int min_tail, int* flushed);
+
+/* q: fp16 bits [B][H][D]; out [B][H][D]. */
+int orc_attend_draft(const orc_cache* c, int layer, const uint16_t* q, double sm_scale,
+                     float* out);
+/* q: fp16 bits [B][m][H][D]; out [B][m][H][D]. */
+int orc_attend_verify(const orc_cache* c, int layer, const uint16_t* q, int m, double sm_scale,
+                      float* out);
+
+int orc_get_state(const orc_cache* c, int layer, int* nq, int* nt, int* head);
+
+/* Logical read-back for one (layer, b, h):
+ *   codes  [T][D]   8-bit codes of the quantized tokens (rows >= nq are zero)
+ *   kmeta  [T/G][D][2] key (s, z);  vmeta [T][2] value (s, z). */
+int orc_read_codes(const orc_cache* c, int layer, int b, int h, int which_v, uint8_t* codes);
+int orc_read_meta(const orc_cache* c, int layer, int b, int h, float* kmeta, float* vmeta);
+
+/* Packs one layer into the arena layout of the library (per-layer slices of each section):
+ *   uk, lk [B][H][T][D/2]; uv, lv [B][H][T/G][D][G/2]; kmeta [B][H][T/G][D][2];
+ *   vmeta [B][H][T][2]; tail_k, tail_v [B][H][2G][D] (fp16 bits, the ring slots).
+ * Quantized rows >= nq and ring slots never written are zero. */
+int orc_export_layer(const orc_cache* c, int layer, uint8_t* uk, uint8_t* lk, uint8_t* uv,
+                     uint8_t* lv, float* kmeta, float* vmeta, uint16_t* tail_k,
+                     uint16_t* tail_v);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,443 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Nothing here compares the oracle with itself: every expectation comes from a closed form
+(grid-exact groups, ties, constant groups), a bound the quantizer must satisfy, an identity of
+the cache's bookkeeping, or an independent library routine (numpy's fp16 conversion, torch's
+float64 scaled_dot_product_attention on the CPU).
+
+Sources: QuantSpec Guide (aifetchly), quantizer listing and "Double Full-Precision Cache
+Buffer"; Pith review of arXiv:2502.10424, "What carries the argument", Fig. 3, Fig. 7 and
+reference [128].
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import OracleCache, OracleError
+from hierarchical_quantized_kv_amd import synth
+
+G = 128
+
+
+def setup_module(_):
+    oracle.build(force=False)
+
+
+# ------------------------------------------------------------------------------------------
+# fp16
+# ------------------------------------------------------------------------------------------
+
+def test_half_to_float_matches_numpy_for_every_bit_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.lib().orc_half_to_float(int(b)) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------
+# Quantizer
+# ------------------------------------------------------------------------------------------
+
+def grid_group(rng, n, z0):
+    """x = (k - z0) * 2^-5 with k in 0..255 and both 0 and 255 present: exact in fp16,
+    so the quantizer must return s = 2^-5, z = z0 and codes k exactly."""
+    k = rng.integers(0, 256, size=n)
+    k[rng.choice(n, 2, replace=False)] = [0, 255]
+    x = ((k - z0) * 2.0 ** -5).astype(np.float16)
+    assert np.array_equal(x.astype(np.float64), (k - z0) * 2.0 ** -5)
+    return k, x
+
+
+@pytest.mark.parametrize("n", [64, 128])
+def test_grid_exact_group_roundtrips_exactly(n):
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        z0 = int(rng.integers(0, 256))
+        k, x = grid_group(rng, n, z0)
+        s, z, c = oracle.quantize_group(x)
+        assert s == 2.0 ** -5 and z == z0
+        assert np.array_equal(c, k)
+        # full dequantization is exact; the draft dequantization is the midpoint of the
+        # upper nibble's 16-code bucket (off = 8) or its lower edge (off = 0)
+        for i in range(0, n, 7):
+            assert oracle.dequant_full(c[i], s, z) == float(x[i])
+            cu = int(k[i]) >> 4
+            assert oracle.dequant_upper(cu, s, z, 8) == (16 * cu + 8 - z0) * 2.0 ** -5
+            assert oracle.dequant_upper(cu, s, z, 0) == (16 * cu - z0) * 2.0 ** -5
+
+
+def test_round_half_to_even_on_exact_ties():
+    """Values exactly halfway between two codes round to the even one, like torch.round."""
+    z0 = 100
+    for k in range(1, 255):
+        x = np.array([(0 - z0) * 2.0 ** -5, (255 - z0) * 2.0 ** -5, (k + 0.5 - z0) * 2.0 ** -5],
+                     dtype=np.float16)
+        s, z, c = oracle.quantize_group(x)
+        assert s == 2.0 ** -5 and z == z0
+        t = k + 0.5 - z0                      # exact x / s: a tie
+        assert c[2] == round(t) + z0          # Python's round() is half-to-even
+        assert c[2] % 2 == (z0 % 2)           # the rounded quotient is even
+
+
+def test_constant_group_clamps_scale():
+    for v in (0.0, 0.5, -3.25, 1000.0):
+        x = np.full(128, v, dtype=np.float16)
+        s, z, c = oracle.quantize_group(x)
+        assert s == np.float32(1e-8)
+        assert np.all(c == 0)
+        assert abs(oracle.dequant_full(0, s, z) - v) <= abs(v) * 2.0 ** -20 + 1e-12
+
+
+def random_groups(rng, n_groups, n):
+    for i in range(n_groups):
+        kind = i % 4
+        if kind == 0:
+            x = rng.standard_normal(n)
+        elif kind == 1:
+            x = rng.standard_normal(n) * 8.0 + rng.standard_normal()
+        elif kind == 2:
+            z = rng.standard_normal(n)
+            x = z / np.sqrt((rng.standard_normal((3, n)) ** 2).sum(0) / 3)
+        else:
+            x = rng.uniform(0.5, 2.0, n)      # all-positive group: zero-point below 0
+        yield x.astype(np.float16)
+
+
+@pytest.mark.parametrize("n", [64, 128])
+def test_code_range_and_roundtrip_bounds(n):
+    """code(min) = 0, code(max) in {254, 255}; |x - xhat| <= s/2 (plus the fp32 division
+    slack); draft error <= 8.5 s (off = 8) or 15.5 s (off = 0), under one upper step 16 s."""
+    rng = np.random.default_rng(2)
+    slack = 2.0 ** -14
+    for x in random_groups(rng, 400, n):
+        s, z, c = oracle.quantize_group(x)
+        xf = x.astype(np.float64)
+        assert s > 1e-8
+        assert c[np.argmin(xf)] == 0
+        assert c[np.argmax(xf)] in (254, 255)
+        full = np.array([oracle.dequant_full(ci, s, z) for ci in c])
+        assert np.max(np.abs(full - xf)) <= (0.5 + slack) * s
+        for off, bound in ((8, 8.5), (0, 15.5)):
+            up = np.array([oracle.dequant_upper(ci >> 4, s, z, off) for ci in c])
+            assert np.max(np.abs(up - xf)) <= (bound + slack) * s < 16 * s
+
+
+# ------------------------------------------------------------------------------------------
+# Attention: reference computations with torch float64 SDPA on the CPU
+# ------------------------------------------------------------------------------------------
+
+def sdpa(q, k, v, mask=None, scale=1.0):
+    """q [m][D], k/v [n][D] (float64) -> [m][D] via torch's CPU float64 SDPA."""
+    qt = torch.as_tensor(np.asarray(q, np.float64))[None, None]
+    kt = torch.as_tensor(np.asarray(k, np.float64))[None, None]
+    vt = torch.as_tensor(np.asarray(v, np.float64))[None, None]
+    mt = None if mask is None else torch.as_tensor(mask)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt,
+                                                            scale=scale)[0, 0].numpy()
+
+
+def f64(a):
+    return np.asarray(a, np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_tail_only_attention_matches_sdpa(D):
+    """nq = 0: draft is plain softmax attention over the fp16 tail; verify is the same with the
+    causal mask of the last m tokens."""
+    B, H, n = 2, 3, 150
+    k, v = synth.kv_host(B, n, H, D, 11, 12)
+    c = OracleCache(1, B, H, D, G, 4 * G, 6)
+    c.append(0, k, v)
+    q = synth.queries_host(B, None, H, D, 13)
+    out = c.attend_draft(0, q, sm_scale=0.7)
+    for b in range(B):
+        for h in range(H):
+            ref = sdpa(f64(q[b, h])[None], f64(k[b, :, h]), f64(v[b, :, h]), scale=0.7)[0]
+            assert np.max(np.abs(out[b, h] - ref)) < 1e-6
+    m = 7
+    qv = synth.queries_host(B, m, H, D, 14)
+    outv = c.attend_verify(0, qv, sm_scale=1.3)
+    mask = np.zeros((m, n), dtype=bool)
+    for i in range(m):
+        mask[i, : n - m + i + 1] = True
+    for b in range(B):
+        for h in range(H):
+            ref = sdpa(f64(qv[b, :, h]), f64(k[b, :, h]), f64(v[b, :, h]), mask, scale=1.3)
+            assert np.max(np.abs(outv[b, :, h] - ref)) < 1e-6
+
+
+def grid_kv(rng, n_groups, H, D):
+    """Keys and values [1][n][H][D] whose every quantization group is grid-exact: keys per
+    (head, channel) over each G-token group, values per (token, head) over D channels."""
+    n = n_groups * G
+    kk = np.zeros((n, H, D), np.int64)
+    vk = np.zeros((n, H, D), np.int64)
+    kz = rng.integers(0, 256, size=(n_groups, H, D))
+    vz = rng.integers(0, 256, size=(n, H))
+    for g in range(n_groups):
+        blk = rng.integers(0, 256, size=(G, H, D))
+        blk[0], blk[1] = 0, 255
+        kk[g * G:(g + 1) * G] = blk
+    vk[:] = rng.integers(0, 256, size=(n, H, D))
+    vk[:, :, 0], vk[:, :, 1] = 0, 255
+    kx = (kk - np.repeat(kz, G, axis=0)) * 2.0 ** -5
+    vx = (vk - vz[:, :, None]) * 2.0 ** -5
+    return (kk, kz, kx.astype(np.float16)[None], vk, vz, vx.astype(np.float16)[None])
+
+
+def test_grid_exact_cache_verify_equals_unquantized_and_draft_equals_upper_formula():
+    """On a grid-exact cache the verify dequantization is lossless, so verify attention equals
+    plain attention over the original fp16 keys/values; the draft attention equals plain
+    attention over (16 * (k >> 4) + 8 - z0) * 2^-5 built here from the integer grid."""
+    rng = np.random.default_rng(3)
+    H, D, ng = 2, 64, 3
+    kk, kz, kx, vk, vz, vx = grid_kv(rng, ng, H, D)
+    c = OracleCache(1, 1, H, D, G, 4 * G, 4)
+    for g in range(ng):
+        c.append(0, kx[:, g * G:(g + 1) * G], vx[:, g * G:(g + 1) * G])
+        assert c.flush(0)[0] == 1
+    tk, tv = synth.kv_host(1, 40, H, D, 21, 22)
+    c.append(0, tk, tv)
+    nq, nt, head = c.state(0)
+    assert (nq[0], nt[0]) == (ng * G, 40)
+    for h in range(H):
+        assert np.array_equal(c.codes(0, 0, h)[: ng * G], kk[:, h])
+        assert np.array_equal(c.codes(0, 0, h, which_v=True)[: ng * G], vk[:, h])
+    q = synth.queries_host(1, None, H, D, 23, gain=3.0)
+    draft = c.attend_draft(0, q)
+    m = 5
+    qv = synth.queries_host(1, m, H, D, 24)
+    ver = c.attend_verify(0, qv)
+    kz_tok = np.repeat(kz, G, axis=0)
+    for h in range(H):
+        kall = np.concatenate([f64(kx[0, :, h]), f64(tk[0, :, h])])
+        vall = np.concatenate([f64(vx[0, :, h]), f64(tv[0, :, h])])
+        mask = np.zeros((m, len(kall)), bool)
+        for i in range(m):
+            mask[i, : ng * G + 40 - m + i + 1] = True
+        ref = sdpa(f64(qv[0, :, h]), kall, vall, mask)
+        assert np.max(np.abs(ver[0, :, h] - ref)) < 1e-6
+        ku = (16 * (kk[:, h] >> 4) + 8 - kz_tok[:, h]) * 2.0 ** -5
+        vu = (16 * (vk[:, h] >> 4) + 8 - vz[:, h][:, None]) * 2.0 ** -5
+        refd = sdpa(f64(q[0, h])[None], np.concatenate([ku, f64(tk[0, :, h])]),
+                    np.concatenate([vu, f64(tv[0, :, h])]))[0]
+        assert np.max(np.abs(draft[0, h] - refd)) < 1e-6
+
+
+def test_single_token_and_zero_query_closed_forms():
+    rng = np.random.default_rng(4)
+    H, D = 2, 64
+    k, v = synth.kv_host(1, 1, H, D, 31, 32)
+    c = OracleCache(1, 1, H, D, G, 2 * G, 4)
+    c.append(0, k, v)
+    out = c.attend_draft(0, synth.queries_host(1, None, H, D, 33))
+    assert np.array_equal(out[0], v[0, 0].astype(np.float32))      # one key: out = v
+    # q = 0: uniform softmax, out = mean of every dequantized value (exact on a grid cache)
+    kk, kz, kx, vk, vz, vx = grid_kv(rng, 2, H, D)
+    c2 = OracleCache(1, 1, H, D, G, 2 * G, 4)
+    for g in range(2):
+        c2.append(0, kx[:, g * G:(g + 1) * G], vx[:, g * G:(g + 1) * G])
+        c2.flush(0)
+    tk, tv = synth.kv_host(1, 10, H, D, 34, 35)
+    c2.append(0, tk, tv)
+    out = c2.attend_verify(0, np.zeros((1, 1, H, D), np.float16))
+    ref = np.concatenate([f64(vx[0]), f64(tv[0])]).mean(axis=0)
+    assert np.max(np.abs(out[0, 0] - ref)) < 1e-6
+
+
+def test_attention_over_explicit_dequantized_cache():
+    """Random (not grid) cache: the oracle's attention equals SDPA over keys/values
+    dequantized here from the read-back codes and metadata, with the tail appended in
+    logical order (checks the token bookkeeping, group indexing and tail ordering)."""
+    B, H, D = 2, 2, 64
+    c = OracleCache(1, B, H, D, G, 4 * G, 6)
+    k, v = synth.kv_host(B, 2 * G, H, D, 41, 42, outliers=synth.outlier_channels(H, D, 43))
+    c.append(0, k[:, :G], v[:, :G])
+    c.flush(0)
+    c.append(0, k[:, G:], v[:, G:])
+    c.rollback(0, [5, 0])
+    c.flush(0, min_tail=G)                 # b=0 has 123 < G tail tokens: only b=1 flushes
+    k2, v2 = synth.kv_host(B, 9, H, D, 44, 45)
+    c.append(0, k2, v2, n=[9, 4])
+    nq, nt, head = c.state(0)
+    assert list(nq) == [G, 2 * G] and list(nt) == [G - 5 + 9, 4] and list(head) == [G, 0]
+    q = synth.queries_host(B, None, H, D, 46)
+    out = c.attend_draft(0, q, sm_scale=1.1)
+    m = 3
+    qv = synth.queries_host(B, m, H, D, 47)
+    outv = c.attend_verify(0, qv)
+    for b in range(B):
+        logical = [k[b, G:2 * G - 5]] if b == 0 else []
+        vlog = [v[b, G:2 * G - 5]] if b == 0 else []
+        n2 = 9 if b == 0 else 4
+        tk = np.concatenate(logical + [k2[b, :n2]]) if logical else k2[b, :n2]
+        tvv = np.concatenate(vlog + [v2[b, :n2]]) if vlog else v2[b, :n2]
+        for h in range(H):
+            codes_k = c.codes(0, b, h)[: nq[b]].astype(np.float64)
+            codes_v = c.codes(0, b, h, True)[: nq[b]].astype(np.float64)
+            km, vm = c.meta(0, b, h)
+            ks = np.repeat(km[:, :, 0], G, axis=0)[: nq[b]].astype(np.float64)
+            kz = np.repeat(km[:, :, 1], G, axis=0)[: nq[b]].astype(np.float64)
+            vs = vm[: nq[b], 0:1].astype(np.float64)
+            vz = vm[: nq[b], 1:2].astype(np.float64)
+            kf, vf = (codes_k - kz) * ks, (codes_v - vz) * vs
+            ku = (16 * np.floor(codes_k / 16) + 8 - kz) * ks
+            vu = (16 * np.floor(codes_v / 16) + 8 - vz) * vs
+            ka = np.concatenate([ku, f64(tk[:, h])])
+            va = np.concatenate([vu, f64(tvv[:, h])])
+            ref = sdpa(f64(q[b, h])[None], ka, va, scale=1.1)[0]
+            assert np.max(np.abs(out[b, h] - ref)) < 1e-6
+            ka = np.concatenate([kf, f64(tk[:, h])])
+            va = np.concatenate([vf, f64(tvv[:, h])])
+            n = len(ka)
+            mask = np.zeros((m, n), bool)
+            for i in range(m):
+                mask[i, : n - m + i + 1] = True
+            ref = sdpa(f64(qv[b, :, h]), ka, va, mask)
+            assert np.max(np.abs(outv[b, :, h] - ref)) < 1e-6
+
+
+# ------------------------------------------------------------------------------------------
+# State machine
+# ------------------------------------------------------------------------------------------
+
+def test_append_rollback_append_is_identity():
+    B, H, D = 2, 2, 64
+    k, v = synth.kv_host(B, 20, H, D, 51, 52)
+    a = OracleCache(1, B, H, D, G, 2 * G, 4)
+    b = OracleCache(1, B, H, D, G, 2 * G, 4)
+    a.append(0, k[:, :10], v[:, :10])
+    b.append(0, k[:, :10], v[:, :10])
+    junk_k, junk_v = synth.kv_host(B, 4, H, D, 53, 54)
+    a.append(0, junk_k, junk_v)
+    a.rollback(0, [4, 4])
+    a.append(0, k[:, 10:], v[:, 10:])
+    b.append(0, k[:, 10:], v[:, 10:])
+    for x, y in zip(a.state(0), b.state(0)):
+        assert np.array_equal(x, y)
+    q = synth.queries_host(B, None, H, D, 55)
+    assert np.array_equal(a.attend_draft(0, q), b.attend_draft(0, q))
+
+
+def test_quantized_tier_is_a_function_of_the_committed_stream():
+    """A speculative trace (draft appends, rollbacks, verify appends, acceptance, flushes)
+    leaves exactly the codes and metadata of a fresh prefill of the committed tokens."""
+    B, H, D, gamma = 1, 2, 64, 4
+    rng = np.random.default_rng(6)
+    trace = OracleCache(1, B, H, D, G, 6 * G, gamma)
+    committed_k, committed_v = [], []
+    base_k, base_v = synth.kv_host(B, 60, H, D, 61, 62)
+    trace.append(0, base_k, base_v)
+    committed_k.append(base_k)
+    committed_v.append(base_v)
+    rnd = 0
+    while trace.state(0)[0][0] < 3 * G:
+        for _ in range(gamma):                      # draft K/V, discarded before verify
+            dk, dv = synth.kv_host(B, 1, H, D, 1000 + rnd * 10, 2000 + rnd * 10)
+            trace.append(0, dk, dv)
+        trace.rollback(0, [gamma])
+        tk, tv = synth.kv_host(B, gamma + 1, H, D, 3000 + rnd, 4000 + rnd)
+        trace.append(0, tk, tv)
+        a = synth.acceptance(rng, gamma)
+        trace.rollback(0, [gamma - a])
+        committed_k.append(tk[:, : a + 1])
+        committed_v.append(tv[:, : a + 1])
+        trace.flush(0, G)
+        rnd += 1
+    ck = np.concatenate(committed_k, axis=1)
+    cv = np.concatenate(committed_v, axis=1)
+    fresh = OracleCache(1, B, H, D, G, 6 * G, gamma)
+    pos = 0
+    while ck.shape[1] - pos >= G:
+        fresh.append(0, ck[:, pos:pos + G], cv[:, pos:pos + G])
+        fresh.flush(0)
+        pos += G
+    fresh.append(0, ck[:, pos:], cv[:, pos:])
+    nq = trace.state(0)[0][0]
+    assert fresh.state(0)[0][0] == nq and trace.state(0)[1][0] == fresh.state(0)[1][0]
+    for h in range(H):
+        for which in (False, True):
+            assert np.array_equal(trace.codes(0, 0, h, which), fresh.codes(0, 0, h, which))
+        for x, y in zip(trace.meta(0, 0, h), fresh.meta(0, 0, h)):
+            assert np.array_equal(x, y)
+
+
+def test_ring_head_toggles_and_logical_order_survives_flush():
+    H, D = 1, 64
+    k, v = synth.kv_host(1, 3 * G, H, D, 71, 72)
+    c = OracleCache(1, 1, H, D, G, 4 * G, 4)
+    c.append(0, k[:, : G + 30], v[:, : G + 30])
+    assert list(c.state(0)[2]) == [0]
+    c.flush(0)
+    assert [x[0] for x in c.state(0)] == [G, 30, G]
+    c.append(0, k[:, G + 30: 2 * G + 50], v[:, G + 30: 2 * G + 50])
+    c.flush(0)
+    assert [x[0] for x in c.state(0)] == [2 * G, 50, 0]
+    # the remaining tail is tokens 2G .. 2G+49, attended as such
+    q = synth.queries_host(1, None, H, D, 73)
+    ref_c = OracleCache(1, 1, H, D, G, 4 * G, 4)
+    ref_c.append(0, k[:, : G], v[:, : G]); ref_c.flush(0)
+    ref_c.append(0, k[:, G: 2 * G], v[:, G: 2 * G]); ref_c.flush(0)
+    ref_c.append(0, k[:, 2 * G: 2 * G + 50], v[:, 2 * G: 2 * G + 50])
+    assert np.array_equal(c.attend_draft(0, q), ref_c.attend_draft(0, q))
+
+
+def test_error_paths_leave_state_unchanged():
+    H, D = 1, 64
+    k, v = synth.kv_host(1, 2 * G + 1, H, D, 81, 82)
+    c = OracleCache(1, 2, H, D, G, G, 4)
+    k2 = np.concatenate([k, k]); v2 = np.concatenate([v, v])
+    with pytest.raises(OracleError) as e:
+        c.append(0, k2, v2)                          # 2G + 1 > ring
+    assert e.value.code == 2
+    c.append(0, k2[:, :10], v2[:, :10], n=[10, 3])
+    with pytest.raises(OracleError) as e:
+        c.rollback(0, [2, 4])                        # 4 > nt of b = 1
+    assert e.value.code == 3
+    assert list(c.state(0)[1]) == [10, 3]
+    with pytest.raises(OracleError) as e:
+        c.attend_verify(0, np.zeros((2, 4, H, D), np.float16))  # m = 4 > nt = 3
+    assert e.value.code == 3
+    c.append(0, k2[:, :G], v2[:, :G])
+    c.flush(0)                                       # both reach nq = G = capacity
+    c.append(0, k2[:, :G], v2[:, :G], n=[G, 0])
+    with pytest.raises(OracleError) as e:
+        c.flush(0)                                   # b = 0 would exceed max_ctx
+    assert e.value.code == 2
+    assert list(c.state(0)[0]) == [G, G] and list(c.state(0)[1]) == [10 + G, 3]
+    empty = OracleCache(1, 1, H, D, G, G, 4)
+    with pytest.raises(OracleError) as e:
+        empty.attend_draft(0, np.zeros((1, H, D), np.float16))
+    assert e.value.code == 3
+
+
+def test_layout_export_matches_split_identity():
+    """Every packed nibble pair of the exported arena image satisfies C8 = 16 C_U + C_L against
+    the logical codes, at the byte positions the layout defines."""
+    B, H, D = 1, 2, 64
+    c = OracleCache(1, B, H, D, G, 2 * G, 4)
+    k, v = synth.kv_host(B, 2 * G, H, D, 91, 92)
+    for g in range(2):
+        c.append(0, k[:, g * G:(g + 1) * G], v[:, g * G:(g + 1) * G])
+        c.flush(0)
+    img = c.export_layer(0)
+    for h in range(H):
+        ck = c.codes(0, 0, h).astype(np.int64)
+        cv = c.codes(0, 0, h, True).astype(np.int64)
+        uk, lk = img["uk"][0, h].astype(np.int64), img["lk"][0, h].astype(np.int64)
+        even = 16 * (uk & 15) + (lk & 15)
+        odd = 16 * (uk >> 4) + (lk >> 4)
+        assert np.array_equal(even, ck[:, 0::2]) and np.array_equal(odd, ck[:, 1::2])
+        uv, lv = img["uv"][0, h].astype(np.int64), img["lv"][0, h].astype(np.int64)
+        for g in range(2):
+            tok = cv[g * G:(g + 1) * G]                # [G][D]
+            ev = 16 * (uv[g] & 15) + (lv[g] & 15)      # [D][G/2]: tokens 0, 2, 4, ...
+            od = 16 * (uv[g] >> 4) + (lv[g] >> 4)
+            assert np.array_equal(ev, tok[0::2].T) and np.array_equal(od, tok[1::2].T)
+        km, vm = c.meta(0, 0, h)
+        assert np.array_equal(img["kmeta"][0, h], km) and np.array_equal(img["vmeta"][0, h], vm)
