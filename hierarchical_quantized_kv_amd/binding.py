@@ -1,0 +1,215 @@
+"""ctypes binding of libquantspec.so (include/quantspec.h).
+
+Argument marshalling only: torch tensors provide device memory and streams, every step of the
+cache runs in the library's HIP kernels.  There is no fallback: if the library is not built,
+``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "libquantspec.so")
+
+QS_OK, QS_ERR_INVALID_ARG, QS_ERR_CAPACITY, QS_ERR_STATE, QS_ERR_BUFFER, QS_ERR_DEVICE = range(6)
+STATUS = {0: "QS_OK", 1: "QS_ERR_INVALID_ARG", 2: "QS_ERR_CAPACITY", 3: "QS_ERR_STATE",
+          4: "QS_ERR_BUFFER", 5: "QS_ERR_DEVICE"}
+
+# Every symbol include/quantspec.h declares.
+EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_destroy",
+           "qs_append", "qs_rollback", "qs_flush", "qs_attend_draft", "qs_attend_verify",
+           "qs_get_state", "qs_last_error")
+
+
+class QsConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "batch", "n_heads", "head_dim", "group", "max_ctx", "gamma_max",
+        "draft_offset")]
+
+
+class QsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "uk", "lk", "uv", "lv", "kmeta", "vmeta", "tail_k", "tail_v", "work",
+        "uk_bytes", "uv_bytes", "kmeta_bytes", "vmeta_bytes", "tail_bytes", "work_bytes",
+        "total")]
+
+
+class QsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Loads libquantspec.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is not built: run python -m "
+                               "hierarchical_quantized_kv_amd.build_lib (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB)
+        P, I32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        PI = ctypes.POINTER(ctypes.c_int32)
+        L.qs_arena_bytes.argtypes = [ctypes.POINTER(QsConfig)]
+        L.qs_arena_bytes.restype = ctypes.c_size_t
+        L.qs_arena_layout.argtypes = [ctypes.POINTER(QsConfig), ctypes.POINTER(QsLayout)]
+        L.qs_cache_create.argtypes = [ctypes.POINTER(QsConfig), P, ctypes.c_size_t,
+                                      ctypes.POINTER(P)]
+        L.qs_cache_destroy.argtypes = [P]
+        L.qs_append.argtypes = [P, I32, P, P, I32, PI, P]
+        L.qs_rollback.argtypes = [P, I32, PI]
+        L.qs_flush.argtypes = [P, I32, I32, P, PI]
+        L.qs_attend_draft.argtypes = [P, I32, P, F, P, P]
+        L.qs_attend_verify.argtypes = [P, I32, P, I32, F, P, P]
+        L.qs_get_state.argtypes = [P, I32, PI, PI, PI]
+        L.qs_last_error.argtypes = [P]
+        L.qs_last_error.restype = ctypes.c_char_p
+        for f in EXPORTS:
+            if f not in ("qs_arena_bytes", "qs_last_error"):
+                getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _i32(a, n):
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+    assert arr.shape[0] == n
+    return arr
+
+
+def _ptr_i32(arr):
+    return None if arr is None else arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def make_config(n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group=128,
+                draft_offset=8) -> QsConfig:
+    return QsConfig(n_layers, batch, n_heads, head_dim, group, max_ctx, gamma_max, draft_offset)
+
+
+def arena_layout(cfg: QsConfig) -> QsLayout:
+    lay = QsLayout()
+    st = lib().qs_arena_layout(ctypes.byref(cfg), ctypes.byref(lay))
+    if st != QS_OK:
+        raise QsError(st, "invalid configuration")
+    return lay
+
+
+class Cache:
+    """A cache over a torch uint8 arena on the current device; verbs mirror the C ABI."""
+
+    def __init__(self, n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group=128,
+                 draft_offset=8, device="cuda"):
+        import torch
+        self.torch = torch
+        self.cfg = make_config(n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group,
+                               draft_offset)
+        self.L, self.B, self.H, self.D = n_layers, batch, n_heads, head_dim
+        self.G, self.T, self.gamma_max = group, max_ctx, gamma_max
+        self.layout = arena_layout(self.cfg)
+        nbytes = self.layout.total
+        self.arena = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p()
+        st = lib().qs_cache_create(ctypes.byref(self.cfg), ctypes.c_void_p(self.arena.data_ptr()),
+                                   nbytes, ctypes.byref(h))
+        if st != QS_OK:
+            raise QsError(st, "qs_cache_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().qs_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _stream(self, stream):
+        s = stream if stream is not None else self.torch.cuda.current_stream()
+        return ctypes.c_void_p(s.cuda_stream)
+
+    def _check(self, st, what):
+        if st != QS_OK:
+            raise QsError(st, f"{what}: {lib().qs_last_error(self._h).decode()}")
+
+    def _dev(self, t, dtype, name):
+        assert t.is_cuda and t.dtype == dtype and t.is_contiguous(), f"{name}: {t.dtype} {t.device}"
+        return ctypes.c_void_p(t.data_ptr())
+
+    def append(self, layer, k, v, n=None, stream=None):
+        torch = self.torch
+        assert k.shape == v.shape and k.dim() == 4 and k.shape[0] == self.B
+        assert tuple(k.shape[2:]) == (self.H, self.D)
+        nn = _i32(n, self.B)
+        self._check(lib().qs_append(self._h, layer, self._dev(k, torch.float16, "k"),
+                                    self._dev(v, torch.float16, "v"), k.shape[1], _ptr_i32(nn),
+                                    self._stream(stream)), "qs_append")
+
+    def rollback(self, layer, n_drop):
+        nd = _i32(n_drop, self.B)
+        self._check(lib().qs_rollback(self._h, layer, _ptr_i32(nd)), "qs_rollback")
+
+    def flush(self, layer=-1, min_tail=None, stream=None):
+        flushed = np.zeros(self.B, dtype=np.int32)
+        self._check(lib().qs_flush(self._h, layer, self.G if min_tail is None else min_tail,
+                                   self._stream(stream), _ptr_i32(flushed)), "qs_flush")
+        return flushed
+
+    def attend_draft(self, layer, q, sm_scale=1.0, out=None, stream=None):
+        torch = self.torch
+        assert tuple(q.shape) == (self.B, self.H, self.D)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        self._check(lib().qs_attend_draft(self._h, layer, self._dev(q, torch.float16, "q"),
+                                          float(sm_scale), self._dev(out, torch.float32, "out"),
+                                          self._stream(stream)), "qs_attend_draft")
+        return out
+
+    def attend_verify(self, layer, q, sm_scale=1.0, out=None, stream=None):
+        torch = self.torch
+        assert q.dim() == 4 and q.shape[0] == self.B and tuple(q.shape[2:]) == (self.H, self.D)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        self._check(lib().qs_attend_verify(self._h, layer, self._dev(q, torch.float16, "q"),
+                                           q.shape[1], float(sm_scale),
+                                           self._dev(out, torch.float32, "out"),
+                                           self._stream(stream)), "qs_attend_verify")
+        return out
+
+    def state(self, layer):
+        nq = np.zeros(self.B, np.int32)
+        nt = np.zeros(self.B, np.int32)
+        hd = np.zeros(self.B, np.int32)
+        self._check(lib().qs_get_state(self._h, layer, _ptr_i32(nq), _ptr_i32(nt), _ptr_i32(hd)),
+                    "qs_get_state")
+        return nq, nt, hd
+
+    # ---- views of the arena (layout of include/quantspec.h), for inspection -------------
+    def section(self, name, layer):
+        """Device view of one layer of an arena section, shaped as the header documents."""
+        torch = self.torch
+        B, H, T, D, G = self.B, self.H, self.T, self.D, self.G
+        NG = T // G
+        lay = self.layout
+        shapes = {
+            "uk": (torch.uint8, lay.uk, (B, H, T, D // 2)),
+            "lk": (torch.uint8, lay.lk, (B, H, T, D // 2)),
+            "uv": (torch.uint8, lay.uv, (B, H, NG, D, G // 2)),
+            "lv": (torch.uint8, lay.lv, (B, H, NG, D, G // 2)),
+            "kmeta": (torch.float32, lay.kmeta, (B, H, NG, D, 2)),
+            "vmeta": (torch.float32, lay.vmeta, (B, H, T, 2)),
+            "tail_k": (torch.float16, lay.tail_k, (B, H, 2 * G, D)),
+            "tail_v": (torch.float16, lay.tail_v, (B, H, 2 * G, D)),
+        }
+        dtype, off, shape = shapes[name]
+        esize = torch.tensor([], dtype=dtype).element_size()
+        n = int(np.prod(shape))
+        start = off + layer * n * esize
+        return self.arena[start:start + n * esize].view(dtype).view(*shape)

@@ -1,0 +1,266 @@
+// qs_api.cpp -- the C ABI of include/quantspec.h: validation, bookkeeping and kernel launches.
+//
+// Every verb validates all of its arguments against the host-side State first, then enqueues
+// its kernels on the caller's stream, and only then updates the State.  No verb synchronizes
+// with the device or copies host data to it: per-sequence counters travel as kernel arguments.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "../../include/quantspec.h"
+#include "qs_state.h"
+
+namespace qs {
+hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st);
+hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st);
+}  // namespace qs
+
+struct qs_cache {
+  qs_config cfg;
+  qs_layout lay;
+  uint8_t* arena;
+  qs::State st;
+  std::string err;
+};
+
+namespace {
+
+#ifndef QS_TARGET_ITEMS
+#define QS_TARGET_ITEMS 4096
+#endif
+constexpr int kTargetItems = QS_TARGET_ITEMS;  // (sequence, head, chunk) items per attention call
+
+qs_status fail(qs_cache* c, qs_status s, const std::string& m) {
+  if (c) c->err = m;
+  return s;
+}
+
+qs_status device_fail(qs_cache* c, hipError_t e, const char* what) {
+  return fail(c, QS_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t layer_off(const qs_cache* c, size_t per_lbh_bytes, int layer) {
+  return (size_t)layer * c->cfg.batch * c->cfg.n_heads * per_lbh_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qs_arena_bytes(const qs_config* cfg) {
+  if (!cfg || !qs::config_ok(*cfg, nullptr)) return 0;
+  return qs::make_layout(*cfg).total;
+}
+
+qs_status qs_arena_layout(const qs_config* cfg, qs_layout* out) {
+  if (!cfg || !out || !qs::config_ok(*cfg, nullptr)) return QS_ERR_INVALID_ARG;
+  *out = qs::make_layout(*cfg);
+  return QS_OK;
+}
+
+qs_status qs_cache_create(const qs_config* cfg, void* d_arena, size_t arena_bytes, qs_cache** out) {
+  if (!cfg || !out) return QS_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!qs::config_ok(*cfg, nullptr)) return QS_ERR_INVALID_ARG;
+  const qs_layout lay = qs::make_layout(*cfg);
+  if (!d_arena || ((uintptr_t)d_arena & 255) || arena_bytes < lay.total) return QS_ERR_BUFFER;
+  qs_cache* c = new (std::nothrow) qs_cache();
+  if (!c) return QS_ERR_DEVICE;
+  c->cfg = *cfg;
+  c->lay = lay;
+  c->arena = static_cast<uint8_t*>(d_arena);
+  c->st = qs::State(*cfg);
+  *out = c;
+  return QS_OK;
+}
+
+qs_status qs_cache_destroy(qs_cache* cache) {
+  delete cache;
+  return QS_OK;
+}
+
+qs_status qs_append(qs_cache* c, int32_t layer, const void* d_k, const void* d_v, int32_t n_max,
+                    const int32_t* h_n, void* stream) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!d_k || !d_v) return fail(c, QS_ERR_INVALID_ARG, "null k or v");
+  const qs_config& cf = c->cfg;
+  int32_t n[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) n[b] = h_n ? h_n[b] : n_max;
+  std::string err;
+  qs_status s = c->st.check_append(layer, n_max, n, &err);
+  if (s != QS_OK) return fail(c, s, err);
+  qs::AppendArgs a{};
+  a.k = static_cast<const uint16_t*>(d_k);
+  a.v = static_cast<const uint16_t*>(d_v);
+  const size_t tail_lbh = (size_t)2 * cf.group * cf.head_dim * 2;
+  a.tail_k = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_k + layer_off(c, tail_lbh, layer));
+  a.tail_v = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_v + layer_off(c, tail_lbh, layer));
+  a.B = cf.batch;
+  a.H = cf.n_heads;
+  a.n_max = n_max;
+  int total = 0;
+  for (int b = 0; b < cf.batch; ++b) {
+    a.n[b] = n[b];
+    a.start[b] = c->st.at(layer, b).nt;
+    a.head[b] = c->st.at(layer, b).head;
+    total += n[b];
+  }
+  if (total > 0) {
+    hipError_t e = qs::launch_append(a, cf.head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(c, e, "append launch");
+  }
+  c->st.apply_append(layer, n);
+  c->err.clear();
+  return QS_OK;
+}
+
+qs_status qs_rollback(qs_cache* c, int32_t layer, const int32_t* h_n_drop) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  std::string err;
+  qs_status s = c->st.check_rollback(layer, h_n_drop, &err);
+  if (s != QS_OK) return fail(c, s, err);
+  c->st.apply_rollback(layer, h_n_drop);
+  c->err.clear();
+  return QS_OK;
+}
+
+qs_status qs_flush(qs_cache* c, int32_t layer, int32_t min_tail, void* stream, int32_t* h_flushed) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  std::string err;
+  qs_status s = c->st.check_flush(layer, min_tail, &err);
+  if (s != QS_OK) return fail(c, s, err);
+  const qs_config& cf = c->cfg;
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? cf.n_layers : layer + 1;
+  qs::FlushArgs a{};
+  a.uk = c->arena + c->lay.uk;
+  a.lk = c->arena + c->lay.lk;
+  a.uv = c->arena + c->lay.uv;
+  a.lv = c->arena + c->lay.lv;
+  a.kmeta = reinterpret_cast<float*>(c->arena + c->lay.kmeta);
+  a.vmeta = reinterpret_cast<float*>(c->arena + c->lay.vmeta);
+  a.tail_k = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_k);
+  a.tail_v = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_v);
+  a.B = cf.batch;
+  a.H = cf.n_heads;
+  a.T = cf.max_ctx;
+  a.NG = cf.max_ctx / cf.group;
+  // Consecutive layers whose selected sequences share (group index, ring head) go in one launch.
+  auto same = [&](int la, int lb) {
+    for (int b = 0; b < cf.batch; ++b) {
+      const bool sa = c->st.selected(la, b, min_tail), sb = c->st.selected(lb, b, min_tail);
+      if (sa != sb) return false;
+      if (sa && (c->st.at(la, b).nq != c->st.at(lb, b).nq || c->st.at(la, b).head != c->st.at(lb, b).head))
+        return false;
+    }
+    return true;
+  };
+  int32_t last_sel[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) last_sel[b] = c->st.selected(l1 - 1, b, min_tail) ? 1 : 0;
+  int run0 = l0;
+  while (run0 < l1) {
+    int run1 = run0 + 1;
+    while (run1 < l1 && same(run0, run1)) ++run1;
+    a.layer0 = run0;
+    a.n_sel = 0;
+    for (int b = 0; b < cf.batch; ++b)
+      if (c->st.selected(run0, b, min_tail)) {
+        a.b[a.n_sel] = b;
+        a.group[a.n_sel] = c->st.at(run0, b).nq / cf.group;
+        a.head[a.n_sel] = c->st.at(run0, b).head;
+        ++a.n_sel;
+      }
+    if (a.n_sel > 0) {
+      hipError_t e = qs::launch_flush(a, cf.head_dim, run1 - run0, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return device_fail(c, e, "flush launch");
+      for (int l = run0; l < run1; ++l)
+        for (int k = 0; k < a.n_sel; ++k) c->st.apply_flush_one(l, a.b[k]);
+    }
+    run0 = run1;
+  }
+  if (h_flushed)
+    for (int b = 0; b < cf.batch; ++b) h_flushed[b] = last_sel[b];
+  c->err.clear();
+  return QS_OK;
+}
+
+static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
+                        float* d_out, void* stream, bool draft) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
+  if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
+  std::string err;
+  qs_status s = c->st.check_attend(layer, m, draft, &err);
+  if (s != QS_OK) return fail(c, s, err);
+  const qs_config& cf = c->cfg;
+  const int D = cf.head_dim;
+  qs::Seq seqs[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
+  const qs::Plan p = qs::make_plan(seqs, cf.batch, cf.n_heads, cf.group, kTargetItems);
+  qs::AttnArgs a{};
+  const size_t T = cf.max_ctx, G = cf.group, NG = T / G;
+  a.uk = c->arena + c->lay.uk + layer_off(c, T * (D / 2), layer);
+  a.lk = c->arena + c->lay.lk + layer_off(c, T * (D / 2), layer);
+  a.uv = c->arena + c->lay.uv + layer_off(c, NG * D * (G / 2), layer);
+  a.lv = c->arena + c->lay.lv + layer_off(c, NG * D * (G / 2), layer);
+  a.kmeta = reinterpret_cast<const float*>(c->arena + c->lay.kmeta + layer_off(c, NG * D * 8, layer));
+  a.vmeta = reinterpret_cast<const float*>(c->arena + c->lay.vmeta + layer_off(c, T * 8, layer));
+  a.tail_k = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_k + layer_off(c, 2 * G * D * 2, layer));
+  a.tail_v = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_v + layer_off(c, 2 * G * D * 2, layer));
+  a.q = static_cast<const uint16_t*>(d_q);
+  a.out = d_out;
+  a.work = reinterpret_cast<float*>(c->arena + c->lay.work);
+  a.B = cf.batch;
+  a.H = cf.n_heads;
+  a.T = cf.max_ctx;
+  a.NG = (int32_t)NG;
+  a.m = m;
+  a.S = qs::record_slots();
+  a.chunk_groups = p.chunk_groups;
+  a.n_qitems_total = p.qbase[cf.batch];
+  a.n_titems_total = p.tbase[cf.batch];
+  a.qscale = sm_scale * 1.4426950408889634f;
+  a.draft_offset = (float)cf.draft_offset;
+  for (int b = 0; b < cf.batch; ++b) {
+    a.nq[b] = seqs[b].nq;
+    a.nt[b] = seqs[b].nt;
+    a.head[b] = seqs[b].head;
+  }
+  for (int b = 0; b <= cf.batch; ++b) {
+    a.qitem_base[b] = p.qbase[b];
+    a.titem_base[b] = p.tbase[b];
+  }
+  hipError_t e = qs::launch_attention(a, D, draft, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
+  c->err.clear();
+  return QS_OK;
+}
+
+qs_status qs_attend_draft(qs_cache* c, int32_t layer, const void* d_q, float sm_scale, float* d_out,
+                          void* stream) {
+  return attend(c, layer, d_q, 1, sm_scale, d_out, stream, true);
+}
+
+qs_status qs_attend_verify(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
+                           float* d_out, void* stream) {
+  return attend(c, layer, d_q, m, sm_scale, d_out, stream, false);
+}
+
+qs_status qs_get_state(const qs_cache* c, int32_t layer, int32_t* h_nq, int32_t* h_nt, int32_t* h_head) {
+  if (!c || layer < 0 || layer >= c->cfg.n_layers) return QS_ERR_INVALID_ARG;
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    const qs::Seq& s = c->st.at(layer, b);
+    if (h_nq) h_nq[b] = s.nq;
+    if (h_nt) h_nt[b] = s.nt;
+    if (h_head) h_head[b] = s.head;
+  }
+  return QS_OK;
+}
+
+const char* qs_last_error(const qs_cache* c) { return c ? c->err.c_str() : "null cache"; }
+
+}  // extern "C"

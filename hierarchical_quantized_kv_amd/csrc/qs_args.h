@@ -1,0 +1,73 @@
+// qs_args.h -- plain-old-data kernel arguments shared by the host library and the HIP kernels.
+// Everything a kernel needs about the per-sequence bookkeeping is passed by value, so no call
+// copies host data to the device and no host buffer has to outlive its launch.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/quantspec.h"
+
+namespace qs {
+
+constexpr int kGroup = 128;           // G: tokens per quantization group (keys) / ring half
+constexpr int kTailChunk = 64;        // tail tokens handled by one tail work item
+constexpr int kMaxTailItems = 2 * kGroup / kTailChunk;
+constexpr int kMaxQuantSplits = 256;  // quantized work items per (sequence, head), at most
+constexpr int kRecPad = 4;            // partial record = [max, sum, pad, pad, o[D]]
+
+// One attention call (draft or verify) on one layer.
+struct AttnArgs {
+  const uint8_t* uk;     // layer base of each section
+  const uint8_t* lk;
+  const uint8_t* uv;
+  const uint8_t* lv;
+  const float* kmeta;
+  const float* vmeta;
+  const uint16_t* tail_k;
+  const uint16_t* tail_v;
+  const uint16_t* q;     // draft [B][H][D], verify [B][m][H][D]
+  float* out;            // same shape as q, fp32
+  float* work;           // partial records [B][H][S][m][D + kRecPad]
+  int32_t B, H, T, NG;   // batch, heads, token capacity, groups per sequence
+  int32_t m;             // queries per (sequence, head)
+  int32_t S;             // record slots per (sequence, head) = kMaxQuantSplits + kMaxTailItems
+  int32_t chunk_groups;  // quantized groups per quantized work item
+  int32_t n_qitems_total, n_titems_total;
+  float qscale;          // sm_scale * log2(e): scores are kept in the base-2 domain
+  float draft_offset;    // 8 or 0 (draft only)
+  int32_t nq[QS_MAX_BATCH];         // quantized tokens per sequence
+  int32_t nt[QS_MAX_BATCH];         // tail tokens per sequence
+  int32_t head[QS_MAX_BATCH];       // ring slot of logical tail token 0
+  int32_t qitem_base[QS_MAX_BATCH + 1];  // prefix sum over b of quantized items
+  int32_t titem_base[QS_MAX_BATCH + 1];  // prefix sum over b of tail items
+};
+
+struct AppendArgs {
+  const uint16_t* k;     // [B][n_max][H][D]
+  const uint16_t* v;
+  uint16_t* tail_k;      // layer base [B][H][2G][D]
+  uint16_t* tail_v;
+  int32_t B, H, n_max;
+  int32_t n[QS_MAX_BATCH];      // tokens appended per sequence
+  int32_t start[QS_MAX_BATCH];  // logical position nt before the append
+  int32_t head[QS_MAX_BATCH];
+};
+
+struct FlushArgs {
+  uint8_t* uk;           // arena section bases (all layers)
+  uint8_t* lk;
+  uint8_t* uv;
+  uint8_t* lv;
+  float* kmeta;
+  float* vmeta;
+  const uint16_t* tail_k;
+  const uint16_t* tail_v;
+  int32_t B, H, T, NG;
+  int32_t layer0;              // first layer of the launch; blockIdx.z adds to it
+  int32_t n_sel;               // selected sequences
+  int32_t b[QS_MAX_BATCH];     // selected sequence ids
+  int32_t group[QS_MAX_BATCH]; // destination group index nq / G
+  int32_t head[QS_MAX_BATCH];  // ring slot of the oldest tail token (0 or G)
+};
+
+}  // namespace qs

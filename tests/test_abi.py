@@ -1,0 +1,133 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/quantspec.h declares, and
+its host-only paths (sizes, layout, argument validation before any launch) behave as documented.
+No call here reaches the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from hierarchical_quantized_kv_amd import binding
+from hierarchical_quantized_kv_amd.binding import QsConfig, QsLayout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+G = 128
+
+
+def declared_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(qs_\w+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB):
+        pytest.fail("libquantspec.so is not built (run __graft_entry__.build())")
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert decl == set(binding.EXPORTS)
+    nm = subprocess.run(["nm", "-D", "--defined-only", binding.LIB], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\b(qs_\w+)\b", nm))
+    assert decl <= exported, decl - exported
+    for name in decl:
+        getattr(lib, name)
+
+
+def cfg(**kw):
+    base = dict(n_layers=2, batch=3, n_heads=4, head_dim=128, group=G, max_ctx=8 * G,
+                gamma_max=6, draft_offset=8)
+    base.update(kw)
+    return QsConfig(*[base[f] for f, _ in QsConfig._fields_])
+
+
+def test_arena_size_and_layout(lib):
+    c = cfg()
+    n = lib.qs_arena_bytes(ctypes.byref(c))
+    lay = QsLayout()
+    assert lib.qs_arena_layout(ctypes.byref(c), ctypes.byref(lay)) == 0
+    assert n == lay.total > 0
+    offs = [lay.uk, lay.lk, lay.uv, lay.lv, lay.kmeta, lay.vmeta, lay.tail_k, lay.tail_v, lay.work]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    lbh = 2 * 3 * 4
+    assert lay.uk_bytes == lbh * 8 * G * 64 and lay.uv_bytes == lbh * 8 * 128 * 64
+    for bad in (cfg(head_dim=96), cfg(group=64), cfg(max_ctx=100), cfg(batch=0),
+                cfg(batch=65), cfg(gamma_max=15 + 1), cfg(draft_offset=4)):
+        assert lib.qs_arena_bytes(ctypes.byref(bad)) == 0
+        assert lib.qs_arena_layout(ctypes.byref(bad), ctypes.byref(lay)) == binding.QS_ERR_INVALID_ARG
+
+
+FAKE = 1 << 40   # an aligned address that is never dereferenced by host-only paths
+
+
+def create(lib, c):
+    h = ctypes.c_void_p()
+    n = lib.qs_arena_bytes(ctypes.byref(c))
+    st = lib.qs_cache_create(ctypes.byref(c), ctypes.c_void_p(FAKE), n, ctypes.byref(h))
+    assert st == 0
+    return h
+
+
+def test_create_checks_arena(lib):
+    c = cfg()
+    n = lib.qs_arena_bytes(ctypes.byref(c))
+    h = ctypes.c_void_p()
+    assert lib.qs_cache_create(ctypes.byref(c), None, n, ctypes.byref(h)) == binding.QS_ERR_BUFFER
+    assert lib.qs_cache_create(ctypes.byref(c), ctypes.c_void_p(FAKE + 64), n,
+                               ctypes.byref(h)) == binding.QS_ERR_BUFFER
+    assert lib.qs_cache_create(ctypes.byref(c), ctypes.c_void_p(FAKE), n - 1,
+                               ctypes.byref(h)) == binding.QS_ERR_BUFFER
+    bad = cfg(head_dim=80)
+    assert lib.qs_cache_create(ctypes.byref(bad), ctypes.c_void_p(FAKE), n,
+                               ctypes.byref(h)) == binding.QS_ERR_INVALID_ARG
+    h = create(lib, c)
+    assert lib.qs_cache_destroy(h) == 0
+    assert lib.qs_cache_destroy(None) == 0
+
+
+def arr(*v):
+    return (ctypes.c_int32 * len(v))(*v)
+
+
+def test_validation_before_any_launch(lib):
+    c = cfg()
+    h = create(lib, c)
+    P = ctypes.c_void_p(FAKE)
+    # counters start empty
+    nq, nt, hd = arr(9, 9, 9), arr(9, 9, 9), arr(9, 9, 9)
+    assert lib.qs_get_state(h, 1, nq, nt, hd) == 0
+    assert list(nq) == list(nt) == list(hd) == [0, 0, 0]
+    assert lib.qs_get_state(h, 2, nq, nt, hd) == binding.QS_ERR_INVALID_ARG
+    # append: bad layer, null tensors, n > n_max, ring overflow -- all rejected before launch
+    assert lib.qs_append(h, 2, P, P, 1, None, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_append(h, 0, None, P, 1, None, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_append(h, 0, P, P, 4, arr(1, 5, 0), None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_append(h, 0, P, P, 2 * G + 1, None, None) == binding.QS_ERR_CAPACITY
+    assert b"overflow" in lib.qs_last_error(h)
+    # rollback of an empty tail
+    assert lib.qs_rollback(h, -1, arr(0, 1, 0)) == binding.QS_ERR_STATE
+    assert lib.qs_rollback(h, 0, arr(0, 0, -1)) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_rollback(h, -1, arr(0, 0, 0)) == 0
+    assert lib.qs_rollback(h, 0, None) == 0
+    # flush: nothing selected launches nothing; min_tail > 2G rejected
+    fl = arr(7, 7, 7)
+    assert lib.qs_flush(h, -1, G, None, fl) == 0 and list(fl) == [0, 0, 0]
+    assert lib.qs_flush(h, 0, 2 * G + 1, None, fl) == binding.QS_ERR_INVALID_ARG
+    # attention over empty sequences, bad m, bad scale
+    assert lib.qs_attend_draft(h, 0, P, ctypes.c_float(1.0), P, None) == binding.QS_ERR_STATE
+    assert lib.qs_attend_verify(h, 0, P, 0, ctypes.c_float(1.0), P, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_attend_verify(h, 0, P, 8, ctypes.c_float(1.0), P, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_attend_verify(h, 0, P, 1, ctypes.c_float(1.0), P, None) == binding.QS_ERR_STATE
+    assert lib.qs_attend_draft(h, 0, P, ctypes.c_float(float("nan")), P, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_attend_draft(h, 0, None, ctypes.c_float(1.0), P, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_get_state(h, 0, nq, nt, hd) == 0 and list(nt) == [0, 0, 0]
+    lib.qs_cache_destroy(h)

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Planes, metadata, tail slots and counters must be bit-exact; attention outputs must agree within
+max-abs 2e-3.  Inputs are seeded synthetic fp16 tensors (see hierarchical_quantized_kv_amd.synth).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hierarchical_quantized_kv_amd import synth
+from lockstep import Lockstep, log
+
+pytestmark = pytest.mark.gpu
+G = 128
+
+
+def setup_module(_):
+    oracle.build(force=False)
+    assert torch.cuda.is_available()
+
+
+def kv(B, n, H, D, seed, dist="normal", outliers=None):
+    k, v = synth.kv_host(B, n, H, D, seed, seed + 7919, dist_k=dist, outliers=outliers)
+    return torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+
+
+def qd(B, H, D, seed, gain=1.0):
+    return torch.from_numpy(synth.queries_host(B, None, H, D, seed, gain)).cuda()
+
+
+def qv(B, m, H, D, seed, gain=1.0):
+    return torch.from_numpy(synth.queries_host(B, m, H, D, seed, gain)).cuda()
+
+
+def prefill(ls, layer, k, v):
+    """Append + flush G tokens at a time (the 'quantize once' prompt path), remainder in tail."""
+    n = k.shape[1]
+    pos = 0
+    while n - pos >= G:
+        ls.append(layer, k[:, pos:pos + G].contiguous(), v[:, pos:pos + G].contiguous())
+        ls.flush(layer)
+        pos += G
+    if pos < n:
+        ls.append(layer, k[:, pos:].contiguous(), v[:, pos:].contiguous())
+
+
+# ------------------------------------------------------------------------------------------
+# Workload configurations
+# ------------------------------------------------------------------------------------------
+
+def test_config_tiny_every_op():
+    """1 layer, 2 heads, D 64, ctx 1024 (8 groups) + 64-token tail; one draft step; rollback;
+    verify of 5 queries; rollback of 3 rejected tokens.  Compared after every op."""
+    log("case: tiny config, every op")
+    H, D = 2, 64
+    ls = Lockstep(1, 1, H, D, 1024 + 2 * G, 4, tag="tiny")
+    k, v = kv(1, 1024 + 64, H, D, 101)
+    prefill(ls, 0, k[:, :1024], v[:, :1024])
+    ls.check_planes(0)
+    ls.append(0, k[:, 1024:].contiguous(), v[:, 1024:].contiguous())
+    ls.check_planes(0)
+    dk, dv = kv(1, 1, H, D, 102)
+    ls.append(0, dk, dv)
+    ls.draft(0, qd(1, H, D, 103))
+    ls.rollback(0, [1])
+    tk, tv = kv(1, 5, H, D, 104)
+    ls.append(0, tk, tv)
+    ls.verify(0, qv(1, 5, H, D, 105))
+    ls.rollback(0, [3])
+    ls.check_planes(0)
+    ls.draft(0, qd(1, H, D, 106))
+    log(f"tiny: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
+def test_config_llama_layer_8k():
+    """Llama-2-7B-shaped layer: 32 heads, D 128, ctx 8192, 1 % of key channels x8; one gamma=4
+    speculation round."""
+    log("case: llama layer 8k")
+    H, D, gamma = 32, 128, 4
+    out = synth.outlier_channels(H, D, synth.seed_for(2, 0, "outlier"))
+    ls = Lockstep(1, 1, H, D, 8192 + 2 * G, gamma, tag="8k")
+    k, v = kv(1, 8192 + 64, H, D, 201, outliers=out)
+    prefill(ls, 0, k[:, :8192], v[:, :8192])
+    ls.append(0, k[:, 8192:].contiguous(), v[:, 8192:].contiguous())
+    ls.check_planes(0)
+    for s in range(gamma):
+        dk, dv = kv(1, 1, H, D, 210 + s, outliers=out)
+        ls.append(0, dk, dv)
+        ls.draft(0, qd(1, H, D, 220 + s))
+    ls.rollback(0, [gamma])
+    tk, tv = kv(1, gamma + 1, H, D, 230, outliers=out)
+    ls.append(0, tk, tv)
+    ls.verify(0, qv(1, gamma + 1, H, D, 231))
+    ls.rollback(0, [gamma - 2])
+    ls.flush(0)
+    ls.check_planes(0)
+    log(f"8k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
+# ------------------------------------------------------------------------------------------
+# Edge cases
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("nt", [1, 63, 64, 65, 200, 256])
+def test_tail_only(D, nt):
+    log(f"case: tail only D={D} nt={nt}")
+    H = 3
+    ls = Lockstep(1, 1, H, D, 2 * G, 15, tag=f"tail{D}/{nt}")
+    k, v = kv(1, nt, H, D, 300 + nt)
+    ls.append(0, k, v)
+    ls.draft(0, qd(1, H, D, 301), sm_scale=0.9)
+    for m in sorted({1, min(nt, 7), min(nt, 16)}):
+        ls.verify(0, qv(1, m, H, D, 302 + m), sm_scale=1.1)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_quantized_only_and_ring_wrap(D):
+    log(f"case: quantized only / ring wrap D={D}")
+    H = 4
+    ls = Lockstep(1, 1, H, D, 6 * G, 6, tag=f"qonly{D}")
+    k, v = kv(1, 5 * G + 100, H, D, 400)
+    prefill(ls, 0, k[:, :3 * G], v[:, :3 * G])       # nt = 0, head = G
+    ls.draft(0, qd(1, H, D, 401))
+    ls.append(0, k[:, 3 * G:4 * G + 100].contiguous(), v[:, 3 * G:4 * G + 100].contiguous())
+    ls.flush(0)                                       # head back to 0, 100 left in the tail
+    ls.append(0, k[:, 4 * G + 100:].contiguous(), v[:, 4 * G + 100:].contiguous())
+    ls.check_planes(0)
+    ls.draft(0, qd(1, H, D, 402))
+    ls.verify(0, qv(1, 7, H, D, 403))
+
+
+def test_ragged_batch_and_many_chunks():
+    """Sequences with different quantized/tail lengths in one call; 260 groups x 32 heads forces
+    multi-group chunks with a short last chunk."""
+    log("case: ragged batch, many chunks")
+    H, D, B = 32, 128, 3
+    ls = Lockstep(1, B, H, D, 264 * G, 4, heads=[0, 17, 31], tag="ragged")
+    lens = [260 * G + 37, 3 * G + 9, 90]
+    n_max = max(lens)
+    k, v = kv(B, n_max, H, D, 500)
+    pos = 0
+    while pos < n_max:
+        n = [max(0, min(G, L - pos)) for L in lens]
+        ls.append(0, k[:, pos:pos + G].contiguous(), v[:, pos:pos + G].contiguous(), n)
+        ls.flush(0)
+        pos += G
+    ls.check_planes(0)
+    ls.draft(0, qd(B, H, D, 501))
+    ls.verify(0, qv(B, 5, H, D, 502))
+    ls.rollback(0, [3, 4, 2])
+    ls.draft(0, qd(B, H, D, 503))
+
+
+def test_degenerate_groups():
+    """Constant key channels and value rows (scale clamped to 1e-8, huge zero-point) and
+    all-positive groups (zero-point below 0)."""
+    log("case: degenerate groups")
+    H, D = 2, 128
+    ls = Lockstep(1, 1, H, D, 4 * G, 4, tag="degenerate")
+    k, v = kv(1, 3 * G + 20, H, D, 600)
+    k, v = k.clone(), v.clone()
+    k[:, :G, 0, 5] = 0.75           # constant key channel in group 0
+    k[:, G:2 * G, 1, :] = 0.0       # all-zero key group
+    v[:, 10:20, 0, :] = -1.5        # constant value rows
+    k[:, 2 * G:3 * G] = k[:, 2 * G:3 * G].abs() + 2.0   # all-positive keys in group 2
+    v[:, 2 * G:3 * G] = v[:, 2 * G:3 * G].abs() + 0.5
+    prefill(ls, 0, k, v)
+    ls.check_planes(0)
+    ls.draft(0, qd(1, H, D, 601))
+    ls.verify(0, qv(1, 5, H, D, 602))
+
+
+@pytest.mark.parametrize("gain", [4.0, 8.0])
+def test_peaky_softmax(gain):
+    log(f"case: peaky softmax gain={gain}")
+    H, D = 4, 128
+    ls = Lockstep(1, 1, H, D, 8 * G, 6, tag=f"peaky{gain}")
+    out = synth.outlier_channels(H, D, 700)
+    k, v = kv(1, 7 * G + 30, H, D, 701, outliers=out)
+    prefill(ls, 0, k, v)
+    ls.draft(0, qd(1, H, D, 702, gain))
+    ls.verify(0, qv(1, 7, H, D, 703, gain))
+
+
+def test_grid_exact_cache_verify_equals_fp16_attention():
+    """Keys/values on the quantization grid: the verify pass must equal plain fp16 attention
+    (torch float64 on the CPU) -- a check of the GPU path that does not go through the oracle."""
+    log("case: grid-exact cache")
+    rng = np.random.default_rng(800)
+    H, D, ng = 2, 128, 4
+    n = ng * G
+    kk = rng.integers(0, 256, size=(n, H, D))
+    for g in range(ng):
+        kk[g * G] = 0
+        kk[g * G + 1] = 255
+    kz = np.repeat(rng.integers(0, 256, size=(ng, H, D)), G, axis=0)
+    vk = rng.integers(0, 256, size=(n, H, D))
+    vk[:, :, 0], vk[:, :, 1] = 0, 255
+    vz = rng.integers(0, 256, size=(n, H, 1))
+    kx = ((kk - kz) * 2.0 ** -5).astype(np.float16)[None]
+    vx = ((vk - vz) * 2.0 ** -5).astype(np.float16)[None]
+    ls = Lockstep(1, 1, H, D, ng * G, 4, tag="grid")
+    tk, tv = kv(1, 30, H, D, 801)
+    prefill(ls, 0, torch.from_numpy(kx).cuda(), torch.from_numpy(vx).cuda())
+    ls.append(0, tk, tv)
+    q = qv(1, 5, H, D, 802)
+    out = ls.verify(0, q).cpu().numpy()
+    kall = np.concatenate([kx[0], tk[0].cpu().numpy()]).astype(np.float64)
+    vall = np.concatenate([vx[0], tv[0].cpu().numpy()]).astype(np.float64)
+    qq = q[0].cpu().numpy().astype(np.float64)
+    N = kall.shape[0]
+    for h in range(H):
+        s = qq[:, h] @ kall[:, h].T
+        for i in range(5):
+            s[i, N - 5 + i + 1:] = -np.inf
+        p = np.exp(s - s.max(1, keepdims=True))
+        ref = (p @ vall[:, h]) / p.sum(1, keepdims=True)
+        assert np.max(np.abs(out[0, :, h] - ref)) < 2e-3
+
+
+def test_errors_leave_state_unchanged_on_gpu():
+    log("case: error paths")
+    from hierarchical_quantized_kv_amd.binding import Cache, QsError, QS_ERR_CAPACITY, QS_ERR_STATE
+    H, D = 2, 64
+    c = Cache(1, 2, H, D, G, 4)
+    k, v = kv(2, 2 * G + 1, H, D, 900)
+    with pytest.raises(QsError) as e:
+        c.append(0, k, v)
+    assert e.value.status == QS_ERR_CAPACITY
+    c.append(0, k[:, :10].contiguous(), v[:, :10].contiguous(), [10, 3])
+    with pytest.raises(QsError) as e:
+        c.rollback(0, [1, 4])
+    assert e.value.status == QS_ERR_STATE
+    with pytest.raises(QsError) as e:
+        c.attend_verify(0, qv(2, 4, H, D, 901))
+    assert e.value.status == QS_ERR_STATE
+    nq, nt, hd = c.state(0)
+    assert list(nt) == [10, 3] and list(nq) == [0, 0]
