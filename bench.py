@@ -66,6 +66,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this size first (reference "
+                         "kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -85,6 +88,14 @@ def main():
     max_ctx = ctx + 16 * G
     print(f"bench: config {args.config} ({cfg['name']}), {L} layers, ctx {ctx}", file=sys.stderr,
           flush=True)
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 19  # fp16 elements
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cache = Cache(L, 1, H, D, max_ctx, gamma)
     t0 = time.time()

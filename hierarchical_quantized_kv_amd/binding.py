@@ -201,8 +201,8 @@ class Cache:
         shapes = {
             "uk": (torch.uint8, lay.uk, (B, H, T, D // 2)),
             "lk": (torch.uint8, lay.lk, (B, H, T, D // 2)),
-            "uv": (torch.uint8, lay.uv, (B, H, NG, D, G // 2)),
-            "lv": (torch.uint8, lay.lv, (B, H, NG, D, G // 2)),
+            "uv": (torch.uint8, lay.uv, (B, H, NG, 2, D, G // 4)),
+            "lv": (torch.uint8, lay.lv, (B, H, NG, 2, D, G // 4)),
             "kmeta": (torch.float32, lay.kmeta, (B, H, NG, D, 2)),
             "vmeta": (torch.float32, lay.vmeta, (B, H, T, 2)),
             "tail_k": (torch.float16, lay.tail_k, (B, H, 2 * G, D)),

@@ -30,10 +30,14 @@ struct qs_cache {
 
 namespace {
 
-#ifndef QS_TARGET_ITEMS
-#define QS_TARGET_ITEMS 4096
+// (sequence, head, chunk) work items per attention call: about one resident round of waves
+// (256 CUs x waves per CU the pass's register use allows: 12 for draft, 8 for verify).
+#ifndef QS_TARGET_ITEMS_DRAFT
+#define QS_TARGET_ITEMS_DRAFT 3072
 #endif
-constexpr int kTargetItems = QS_TARGET_ITEMS;  // (sequence, head, chunk) items per attention call
+#ifndef QS_TARGET_ITEMS_VERIFY
+#define QS_TARGET_ITEMS_VERIFY 2048
+#endif
 
 qs_status fail(qs_cache* c, qs_status s, const std::string& m) {
   if (c) c->err = m;
@@ -200,7 +204,8 @@ static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, 
   const int D = cf.head_dim;
   qs::Seq seqs[QS_MAX_BATCH];
   for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
-  const qs::Plan p = qs::make_plan(seqs, cf.batch, cf.n_heads, cf.group, kTargetItems);
+  const qs::Plan p = qs::make_plan(seqs, cf.batch, cf.n_heads, cf.group,
+                                   draft ? QS_TARGET_ITEMS_DRAFT : QS_TARGET_ITEMS_VERIFY);
   qs::AttnArgs a{};
   const size_t T = cf.max_ctx, G = cf.group, NG = T / G;
   a.uk = c->arena + c->lay.uk + layer_off(c, T * (D / 2), layer);

@@ -31,6 +31,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qs_args.h"
 
 namespace qs {
@@ -47,7 +49,33 @@ __device__ __forceinline__ uint32_t as_u32(f16x2 x) { return __builtin_bit_cast(
 __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
+// c + a.x b.x + a.y b.y (fp16 products, fp32 accumulate) kept in program order: the draft's
+// inner loops interleave each nibble unpack with its dot products so that only one word's
+// unpacked operands are live at a time.
+__device__ __forceinline__ float dot2_ord(uint32_t a, uint32_t b, float c) {
+  asm volatile("v_dot2c_f32_f16 %0, %1, %2" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+// 2^x with the hardware instruction (results below 2^-126 flush to zero).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Streaming loads of data read once per call (planes, metadata): the non-temporal hint keeps
+// them from displacing cache lines and raises the achievable HBM read rate.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8_nt(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float4 ldf4_nt(const float* p) {
+  const uint4 v = ld16_nt(p);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
 __device__ __forceinline__ float lo_h(uint32_t x) { return (float)as_h2(x).x; }
 __device__ __forceinline__ float hi_h(uint32_t x) { return (float)as_h2(x).y; }
 
@@ -86,6 +114,14 @@ __device__ __forceinline__ Nib4 unpack_nibbles16(uint32_t w) {
 __device__ __forceinline__ void split_f16(float x, f16& hi, f16& lo) {
   hi = (f16)x;
   lo = (f16)(x - (float)hi);
+}
+
+// (x & mask) | c as one v_and_or_b32, mask in an SGPR and c in a VGPR: the compiler does not
+// form it by itself because a gfx9 VOP3 instruction takes no literal and reads one SGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(c));
+  return r;
 }
 
 // 8-bit codes of 8 entries from an upper word u and lower word l (entry e in nibble e of each),
@@ -131,9 +167,181 @@ struct DraftShape {
 
 struct DraftLds {
   uint32_t wts[2][64];   // key weights q' (hi, lo), pair order (D/2 words used)
-  uint32_t pw[64];       // value weights p'_t, pair order (G/2 words)
-  float2 vm[kGroup];     // (s_t, s_t * (128 + off - z_t))
+  uint32_t pw[64];       // value weights in pair order: 16 p'_t (even t), p'_t (odd t)
+  float2 vm[kGroup];     // (s_t, s_t * (off - z_t))
 };
+
+// Planes and metadata of one group, as loaded by one lane.
+template <int D>
+struct DraftBuf {
+  uint4 k[DraftShape<D>::KIT];
+  uint4 v[DraftShape<D>::VIT];
+  float4 km;  // key (s, z) of channels 2*lane, 2*lane+1
+  float4 vm;  // value (s, z) of tokens 2*lane, 2*lane+1
+};
+
+template <int D>
+__device__ __forceinline__ void draft_load_k(const AttnArgs& a, size_t bh, int g, DraftBuf<D>& buf) {
+  using S = DraftShape<D>;
+  const int lane = threadIdx.x;
+  const int kc = lane % S::KL, kt = lane / S::KL;
+  const uint8_t* ukg = a.uk + (bh * a.T + (size_t)g * kGroup) * (D / 2);
+#pragma unroll
+  for (int it = 0; it < S::KIT; ++it)
+    buf.k[it] = ld16_nt(ukg + (size_t)(it * S::TPI + kt) * (D / 2) + kc * 16);
+}
+template <int D>
+__device__ __forceinline__ void draft_load_meta(const AttnArgs& a, size_t bh, int g, DraftBuf<D>& buf) {
+  const int lane = threadIdx.x;
+  buf.km = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (lane < D / 2) buf.km = ldf4_nt(a.kmeta + (((bh * a.NG + g) * D) + 2 * lane) * 2);
+  buf.vm = ldf4_nt(a.vmeta + ((bh * a.T) + (size_t)g * kGroup + 2 * lane) * 2);
+}
+template <int D>
+__device__ __forceinline__ void draft_load_v(const AttnArgs& a, size_t bh, int g, DraftBuf<D>& buf) {
+  using S = DraftShape<D>;
+  const int lane = threadIdx.x;
+  const int vr = lane & 3, vd = lane >> 2;
+  const uint8_t* uvg = a.uv + ((bh * a.NG + g) * D) * (kGroup / 2);
+#pragma unroll
+  for (int i = 0; i < S::VIT; ++i)
+    buf.v[i] = ld16_nt(uvg + (vr >> 1) * (D * kGroup / 4) + (size_t)(16 * i + vd) * (kGroup / 4) +
+                       (vr & 1) * 16);
+}
+
+// Running softmax state of a draft work item (per lane).
+template <int D>
+struct DraftAcc {
+  float m_run, l_run, beta;
+  float o[DraftShape<D>::VIT];
+};
+
+// One group: scores of its 128 keys from the upper key plane, online-softmax update, and the
+// weighted sum of its upper value plane.
+// The registers of `cur` are refilled with group `gnext` (if >= 0) as soon as each part of the
+// current group has been consumed, so the next group's loads overlap this group's arithmetic.
+template <int D>
+__device__ __forceinline__ void draft_group(const AttnArgs& a, size_t bh, DraftBuf<D>& cur,
+                                            int gnext, float q0, float q1, uint32_t magic,
+                                            DraftLds& L, DraftAcc<D>& st) {
+  using S = DraftShape<D>;
+  const int lane = threadIdx.x;
+  const int kc = lane % S::KL, kt = lane / S::KL, vr = lane & 3;
+  const float off = a.draft_offset;
+
+  __syncthreads();  // the previous group's LDS reads are done
+  float bias = 0.f;
+  if (lane < D / 2) {
+    // key weights q' = q s as fp16 hi + lo, against nibble values 1024 + 16 U
+    const float qa = q0 * cur.km.x, qb = q1 * cur.km.z;
+    f16 ah, al, bh, bl;
+    split_f16(qa, ah, al);
+    split_f16(qb, bh, bl);
+    const int c0 = 2 * lane, c1 = 2 * lane + 1;
+    f16* wh = reinterpret_cast<f16*>(L.wts[0]);
+    f16* wl = reinterpret_cast<f16*>(L.wts[1]);
+    wh[2 * pair_word(c0) + pair_half(c0)] = ah;
+    wl[2 * pair_word(c0) + pair_half(c0)] = al;
+    wh[2 * pair_word(c1) + pair_half(c1)] = bh;
+    wl[2 * pair_word(c1) + pair_half(c1)] = bl;
+    bias = qa * (off - cur.km.y) + qb * (off - cur.km.w) -
+           1024.f * (((float)ah + (float)al) + ((float)bh + (float)bl));
+  }
+  L.vm[2 * lane] = make_float2(cur.vm.x, cur.vm.x * (off - cur.vm.y));
+  L.vm[2 * lane + 1] = make_float2(cur.vm.z, cur.vm.z * (off - cur.vm.w));
+  __builtin_amdgcn_sched_barrier(0);
+  if (gnext >= 0) draft_load_meta<D>(a, bh, gnext, cur);
+  bias = wave_sum_from(bias, 1);
+  __syncthreads();
+
+  uint4 W[4], Wl[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    W[k] = reinterpret_cast<const uint4*>(L.wts[0])[4 * kc + k];
+    Wl[k] = reinterpret_cast<const uint4*>(L.wts[1])[4 * kc + k];
+  }
+  float sc[S::KIT];
+#pragma unroll
+  for (int it = 0; it < S::KIT; ++it) {
+    const uint32_t wd[4] = {cur.k[it].x, cur.k[it].y, cur.k[it].z, cur.k[it].w};
+    float p = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = wd[k];
+      const uint32_t na = and_or(w << 4, 0x00F000F0u, magic);  // (e0, e4): 1024 + 16 U
+      p = dot2_ord(na, W[k].x, p);
+      p = dot2_ord(na, Wl[k].x, p);
+      const uint32_t nb = and_or(w, 0x00F000F0u, magic);       // (e1, e5)
+      p = dot2_ord(nb, W[k].y, p);
+      p = dot2_ord(nb, Wl[k].y, p);
+      const uint32_t nc = and_or(w >> 4, 0x00F000F0u, magic);  // (e2, e6)
+      p = dot2_ord(nc, W[k].z, p);
+      p = dot2_ord(nc, Wl[k].z, p);
+      const uint32_t nd = and_or(w >> 8, 0x00F000F0u, magic);  // (e3, e7)
+      p = dot2_ord(nd, W[k].w, p);
+      p = dot2_ord(nd, Wl[k].w, p);
+    }
+#pragma unroll
+    for (int o = 1; o < S::KL; o <<= 1) p += __shfl_xor(p, o);
+    sc[it] = p + bias;
+    __builtin_amdgcn_sched_barrier(0);  // bound the live nibble temporaries to one load
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (gnext >= 0) draft_load_k<D>(a, bh, gnext, cur);
+  float gmax = sc[0];
+#pragma unroll
+  for (int it = 1; it < S::KIT; ++it) gmax = fmaxf(gmax, sc[it]);
+  gmax = wave_max_from(gmax, S::KL);
+  const float m_new = fmaxf(st.m_run, gmax);
+  const float alpha = fast_exp2(st.m_run - m_new);
+  st.m_run = m_new;
+  st.l_run *= alpha;
+  st.beta *= alpha;
+#pragma unroll
+  for (int it = 0; it < S::KIT; ++it) {
+    const int t = it * S::TPI + kt;
+    const float p = fast_exp2(sc[it] - m_new);
+    const float2 sw = L.vm[t];
+    st.l_run += p;
+    st.beta += p * sw.y;
+    // every lane of the key row writes the same value
+    reinterpret_cast<f16*>(L.pw)[2 * pair_word(t) + pair_half(t)] =
+        (f16)((t & 1) ? p * sw.x : 16.f * p * sw.x);
+  }
+  __syncthreads();
+
+  // values: a fresh fp32 sum per group of w_t (1024 + U or 1024 + 16 U); the group's exact
+  // offset 1024 sum_t w_t is removed before it joins the running (rescaled) sum.
+  uint4 P[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) P[k] = reinterpret_cast<const uint4*>(L.pw)[4 * vr + k];
+  const f16x2 k1024 = {(f16)1024.f, (f16)1024.f};
+  float corr = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    corr = dot2(as_h2(P[k].x), k1024, corr);
+    corr = dot2(as_h2(P[k].y), k1024, corr);
+    corr = dot2(as_h2(P[k].z), k1024, corr);
+    corr = dot2(as_h2(P[k].w), k1024, corr);
+  }
+#pragma unroll
+  for (int i = 0; i < S::VIT; ++i) {
+    const uint32_t wd[4] = {cur.v[i].x, cur.v[i].y, cur.v[i].z, cur.v[i].w};
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = wd[k], w8 = w >> 8;
+      o = dot2_ord(and_or(w, 0x000F000Fu, magic), P[k].x, o);   // (t0, t4): 1024 + U
+      o = dot2_ord(and_or(w, 0x00F000F0u, magic), P[k].y, o);   // (t1, t5): 1024 + 16 U
+      o = dot2_ord(and_or(w8, 0x000F000Fu, magic), P[k].z, o);  // (t2, t6)
+      o = dot2_ord(and_or(w8, 0x00F000F0u, magic), P[k].w, o);  // (t3, t7)
+    }
+    st.o[i] = fmaf(st.o[i], alpha, o - corr);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (gnext >= 0) draft_load_v<D>(a, bh, gnext, cur);
+}
 
 template <int D>
 __device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, DraftLds& L) {
@@ -143,7 +351,8 @@ __device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, Draf
   const int g0 = item * a.chunk_groups;
   const int g1 = min(g0 + a.chunk_groups, ng);
   const size_t bh = (size_t)b * a.H + h;
-  const float off = a.draft_offset;
+  uint32_t magic;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
   float q0 = 0.f, q1 = 0.f;  // channels 2*lane, 2*lane+1 (lanes < D/2), times qscale
   if (lane < D / 2) {
@@ -151,176 +360,130 @@ __device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, Draf
     q0 = lo_h(qq) * a.qscale;
     q1 = hi_h(qq) * a.qscale;
   }
-  const int kc = lane % S::KL;   // key chunk (32 channels) of this lane
-  const int kt = lane / S::KL;   // key row of this lane within a load
-  const int vr = lane & 3;       // value quarter: tokens 32*vr .. 32*vr+31 of the group
-  const int vd = lane >> 2;      // value channel offset: channel 16*i + vd
+  DraftAcc<D> st;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+  st.beta = 0.f;
+#pragma unroll
+  for (int i = 0; i < S::VIT; ++i) st.o[i] = 0.f;
 
-  float m_run = -INFINITY, l_run = 0.f, beta = 0.f;
-  float acc[S::VIT];
-#pragma unroll
-  for (int i = 0; i < S::VIT; ++i) acc[i] = 0.f;
-
-  for (int g = g0; g < g1; ++g) {
-    const uint8_t* ukg = a.uk + (bh * a.T + (size_t)g * kGroup) * (D / 2);
-    const uint8_t* uvg = a.uv + ((bh * a.NG + g) * D) * (kGroup / 2);
-    uint4 kw[S::KIT], vw[S::VIT];
-#pragma unroll
-    for (int it = 0; it < S::KIT; ++it)
-      kw[it] = ld16(ukg + (size_t)(it * S::TPI + kt) * (D / 2) + kc * 16);
-#pragma unroll
-    for (int i = 0; i < S::VIT; ++i)
-      vw[i] = ld16(uvg + (size_t)(16 * i + vd) * (kGroup / 2) + vr * 16);
-    float4 km = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane < D / 2)
-      km = *reinterpret_cast<const float4*>(a.kmeta + (((bh * a.NG + g) * D) + 2 * lane) * 2);
-    const float4 vm = *reinterpret_cast<const float4*>(a.vmeta + ((bh * a.T) + (size_t)g * kGroup + 2 * lane) * 2);
-
-    __syncthreads();  // previous group's LDS reads are done
-    // key weights q' = q s as fp16 hi + lo, against nibble values 1024 + 16 U
-    float bias = 0.f;
-    if (lane < D / 2) {
-      const float qa = q0 * km.x, qb = q1 * km.z;
-      f16 ah, al, bh, bl;
-      split_f16(qa, ah, al);
-      split_f16(qb, bh, bl);
-      const int c0 = 2 * lane, c1 = 2 * lane + 1;
-      f16* wh = reinterpret_cast<f16*>(L.wts[0]);
-      f16* wl = reinterpret_cast<f16*>(L.wts[1]);
-      wh[2 * pair_word(c0) + pair_half(c0)] = ah;
-      wl[2 * pair_word(c0) + pair_half(c0)] = al;
-      wh[2 * pair_word(c1) + pair_half(c1)] = bh;
-      wl[2 * pair_word(c1) + pair_half(c1)] = bl;
-      bias = qa * (off - km.y) + qb * (off - km.w) -
-             1024.f * (((float)ah + (float)al) + ((float)bh + (float)bl));
-    }
-    L.vm[2 * lane] = make_float2(vm.x, vm.x * ((128.f + off) - vm.y));
-    L.vm[2 * lane + 1] = make_float2(vm.z, vm.z * ((128.f + off) - vm.w));
-    bias = wave_sum_from(bias, 1);
-    __syncthreads();
-
-    // scores of key rows it*TPI + kt
-    uint4 W[4], Wl[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      W[k] = reinterpret_cast<const uint4*>(L.wts[0])[4 * kc + k];
-      Wl[k] = reinterpret_cast<const uint4*>(L.wts[1])[4 * kc + k];
-    }
-    float sc[S::KIT];
-#pragma unroll
-    for (int it = 0; it < S::KIT; ++it) {
-      const uint32_t wd[4] = {kw[it].x, kw[it].y, kw[it].z, kw[it].w};
-      float p = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const Nib4 n = unpack_nibbles16(wd[k]);
-        p = dot2(n.a, as_h2(W[k].x), p);
-        p = dot2(n.b, as_h2(W[k].y), p);
-        p = dot2(n.c, as_h2(W[k].z), p);
-        p = dot2(n.d, as_h2(W[k].w), p);
-        p = dot2(n.a, as_h2(Wl[k].x), p);
-        p = dot2(n.b, as_h2(Wl[k].y), p);
-        p = dot2(n.c, as_h2(Wl[k].z), p);
-        p = dot2(n.d, as_h2(Wl[k].w), p);
-      }
-#pragma unroll
-      for (int o = 1; o < S::KL; o <<= 1) p += __shfl_xor(p, o);
-      sc[it] = p + bias;
-    }
-    float gmax = sc[0];
-#pragma unroll
-    for (int it = 1; it < S::KIT; ++it) gmax = fmaxf(gmax, sc[it]);
-    gmax = wave_max_from(gmax, S::KL);
-    const float m_new = fmaxf(m_run, gmax);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-    beta *= alpha;
-#pragma unroll
-    for (int i = 0; i < S::VIT; ++i) acc[i] *= alpha;
-#pragma unroll
-    for (int it = 0; it < S::KIT; ++it) {
-      const int t = it * S::TPI + kt;
-      const float p = exp2f(sc[it] - m_new);
-      const float2 sw = L.vm[t];
-      l_run += p;
-      beta += p * sw.y;
-      if (kc == 0)
-        reinterpret_cast<f16*>(L.pw)[2 * pair_word(t) + pair_half(t)] =
-            (f16)((t & 1) ? p * sw.x : 16.f * p * sw.x);
-    }
-    __syncthreads();
-
-    // values: o_d += 16 p'_t (U_td - 8) over the 32 tokens of quarter vr
-    uint4 P[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) P[k] = reinterpret_cast<const uint4*>(L.pw)[4 * vr + k];
-    const f16x2 c1032 = {(f16)1032.f, (f16)1032.f}, c1152 = {(f16)1152.f, (f16)1152.f};
-#pragma unroll
-    for (int i = 0; i < S::VIT; ++i) {
-      const uint32_t wd[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
-      float o = acc[i];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const Nib4 n = unpack_nibbles(wd[k]);
-        o = dot2(n.a - c1032, as_h2(P[k].x), o);
-        o = dot2(n.b - c1152, as_h2(P[k].y), o);
-        o = dot2(n.c - c1032, as_h2(P[k].z), o);
-        o = dot2(n.d - c1152, as_h2(P[k].w), o);
-      }
-      acc[i] = o;
-    }
-  }
+  DraftBuf<D> buf;
+  draft_load_k<D>(a, bh, g0, buf);
+  draft_load_meta<D>(a, bh, g0, buf);
+  draft_load_v<D>(a, bh, g0, buf);
+  for (int g = g0; g < g1; ++g)
+    draft_group<D>(a, bh, buf, g + 1 < g1 ? g + 1 : -1, q0, q1, magic, L, st);
 
   // l and beta were accumulated once per key row in each of its KL lanes
-  l_run = wave_sum_from(l_run, S::KL);
-  beta = wave_sum_from(beta, S::KL);
-#pragma unroll
-  for (int i = 0; i < S::VIT; ++i) {
-    acc[i] += __shfl_xor(acc[i], 1);
-    acc[i] += __shfl_xor(acc[i], 2);
-  }
+  const float l_run = wave_sum_from(st.l_run, S::KL);
+  const float beta = wave_sum_from(st.beta, S::KL);
+  const int vr = lane & 3, vd = lane >> 2;
   float* rec = record(a, D, b, h, item, 0);
   if (lane == 0) {
-    rec[0] = m_run;
+    rec[0] = st.m_run;
     rec[1] = l_run;
   }
 #pragma unroll
-  for (int i = 0; i < S::VIT; ++i)
-    if ((i & 3) == vr) rec[kRecPad + 16 * i + vd] = acc[i] + beta;
+  for (int i = 0; i < S::VIT; ++i) {
+    float o = st.o[i];
+    o += __shfl_xor(o, 1);
+    o += __shfl_xor(o, 2);
+    if ((i & 3) == vr) rec[kRecPad + 16 * i + vd] = o + beta;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
 // Verify: quantized work item (both planes, MFMA)
 // ------------------------------------------------------------------------------------------
 //
-// Per group of 128 tokens and lane l = 16*g + j (j: query column, g: k-group):
-//   S^T tile tau (16 tokens x 16 queries) = sum over KK MFMAs of A (codes) x B (q' slots);
-//   row r of tile tau is token 32*(r/4) + 8*(tau/2) + 2*(r%4) + (tau%2), so that lane group g
-//   ends up holding exactly tokens 32g .. 32g+31 in the slot order PV needs.
+// A group of 128 tokens is processed in two halves of 64.  Lane l = 16 g + j (j: query column of
+// the MFMA B operand and of the results, g: k-group):
+//   S^T tile tau (16 tokens x 16 queries) = sum over D/32 MFMAs of A (key codes) x B (q' slots);
+//   row r of tile tau is token 64(tau/4) + 16(r/4) + 8((tau%4)/2) + 2(r%4) + (tau%2), so that in
+//   half h lane group g holds exactly tokens 64h + 16g .. 64h + 16g + 15, in the slot order the
+//   PV MFMAs need, and reads them as one 8-byte piece of each value-plane row.
 //   O^T tile rt (16 channels x 16 queries) += A (value codes - 128) x B (p' of tiles 2q, 2q+1).
+// q' = q s and p' = p s enter the MFMAs as fp16 hi + lo pairs; the bias sums stay in fp32.
 
 template <int D>
 struct VerifyShape {
   static constexpr int KK = D / 32;   // MFMA k-steps per S^T tile
   static constexpr int CPL = D / 4;   // channels per lane group
   static constexpr int RT = D / 16;   // O^T channel tiles
+  static constexpr int KB = D / 8;    // key-row bytes per lane group
 };
 
 struct VerifyLds {
-  float2 km[128];        // (s_d, z_d) of the group's key channels
-  float2 vm[kGroup];     // (s_t, s_t * (128 - z_t))
+  float2 qs[QS_MAX_QUERIES][64];     // queries times qscale, channels (2 lane, 2 lane + 1)
+  float2 vm[kGroup];                 // (s_t, s_t * (128 - z_t))
+  uint4 bq[2][4][64];                // q' B operands (hi, lo) per k-step and lane
+  float bias[QS_MAX_QUERIES][64];    // per-query bias partials of the lanes' channels
 };
 
-__device__ __forceinline__ int tile_row_token(int tau, int r) {
-  return 32 * (r >> 2) + 8 * (tau >> 1) + 2 * (r & 3) + (tau & 1);
+__device__ __forceinline__ int vtile_token(int tau, int r) {
+  return 64 * (tau >> 2) + 16 * (r >> 2) + 8 * ((tau & 3) >> 1) + 2 * (r & 3) + (tau & 1);
+}
+
+template <int D>
+struct VerifyBuf {
+  uint32_t ku[4][VerifyShape<D>::KK], kl[4][VerifyShape<D>::KK];  // 4 key tiles of a half
+  uint2 vu[VerifyShape<D>::RT], vl[VerifyShape<D>::RT];            // value codes of a half
+  float4 km;  // key (s, z) of channels 2*lane, 2*lane+1
+  float4 vm;  // value (s, z) of tokens 2*lane, 2*lane+1
+};
+
+template <int D>
+__device__ __forceinline__ void verify_load_k(const AttnArgs& a, size_t bh, int gi, int half,
+                                              VerifyBuf<D>& buf) {
+  using S = VerifyShape<D>;
+  const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
+  const uint8_t* ukg = a.uk + (bh * a.T + (size_t)gi * kGroup) * (D / 2);
+  const uint8_t* lkg = a.lk + (bh * a.T + (size_t)gi * kGroup) * (D / 2);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const size_t off = (size_t)vtile_token(4 * half + t, j) * (D / 2) + g * S::KB;
+    if constexpr (S::KK == 4) {
+      const uint4 u = ld16_nt(ukg + off), l = ld16_nt(lkg + off);
+      buf.ku[t][0] = u.x; buf.ku[t][1] = u.y; buf.ku[t][2] = u.z; buf.ku[t][3] = u.w;
+      buf.kl[t][0] = l.x; buf.kl[t][1] = l.y; buf.kl[t][2] = l.z; buf.kl[t][3] = l.w;
+    } else {
+      const uint2 u = ld8_nt(ukg + off);
+      const uint2 l = ld8_nt(lkg + off);
+      buf.ku[t][0] = u.x; buf.ku[t][1] = u.y;
+      buf.kl[t][0] = l.x; buf.kl[t][1] = l.y;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void verify_load_v(const AttnArgs& a, size_t bh, int gi, int half,
+                                              VerifyBuf<D>& buf) {
+  using S = VerifyShape<D>;
+  const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
+  const uint8_t* uvg = a.uv + ((bh * a.NG + gi) * D) * (kGroup / 2);
+  const uint8_t* lvg = a.lv + ((bh * a.NG + gi) * D) * (kGroup / 2);
+#pragma unroll
+  for (int rt = 0; rt < S::RT; ++rt) {
+    const size_t off = (size_t)half * (D * kGroup / 4) + (size_t)(16 * rt + j) * (kGroup / 4) + 8 * g;
+    buf.vu[rt] = ld8_nt(uvg + off);
+    buf.vl[rt] = ld8_nt(lvg + off);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void verify_load_meta(const AttnArgs& a, size_t bh, int gi,
+                                                 VerifyBuf<D>& buf) {
+  const int lane = threadIdx.x;
+  buf.km = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (lane < D / 2) buf.km = ldf4_nt(a.kmeta + (((bh * a.NG + gi) * D) + 2 * lane) * 2);
+  buf.vm = ldf4_nt(a.vmeta + ((bh * a.T) + (size_t)gi * kGroup + 2 * lane) * 2);
 }
 
 template <int D>
 __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, VerifyLds& L) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
-  const int j = lane & 15;   // query
+  const int j = lane & 15;   // query column
   const int g = lane >> 4;   // k-group
   const int m = a.m;
   const int ng = a.nq[b] / kGroup;
@@ -328,146 +491,144 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
   const int g1 = min(g0 + a.chunk_groups, ng);
   const size_t bh = (size_t)b * a.H + h;
 
-  // this lane's query channels g*CPL .. g*CPL+CPL-1, times qscale (zero for padding rows)
-  float qf[S::CPL];
-  if (j < m) {
-    const uint16_t* qrow = a.q + (((size_t)b * m + j) * a.H + h) * D + g * S::CPL;
-#pragma unroll
-    for (int c = 0; c < S::CPL; c += 8) {
-      const uint4 w = ld16(qrow + c);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        qf[c + 2 * k] = lo_h(ws[k]) * a.qscale;
-        qf[c + 2 * k + 1] = hi_h(ws[k]) * a.qscale;
-      }
+  // q times qscale of channels 2*lane, 2*lane+1 for every query, and zeroed B operands so the
+  // padding query columns j >= m stay zero
+  if (lane < D / 2)
+    for (int i = 0; i < m; ++i) {
+      const uint32_t qq =
+          reinterpret_cast<const uint32_t*>(a.q + (((size_t)b * m + i) * a.H + h) * D)[lane];
+      L.qs[i][lane] = make_float2(lo_h(qq) * a.qscale, hi_h(qq) * a.qscale);
     }
-  } else {
-#pragma unroll
-    for (int c = 0; c < S::CPL; ++c) qf[c] = 0.f;
-  }
+  for (int x = lane; x < 2 * 4 * 64; x += 64) (&L.bq[0][0][0])[x] = make_uint4(0, 0, 0, 0);
+  for (int x = lane; x < QS_MAX_QUERIES * 64; x += 64) (&L.bias[0][0])[x] = 0.f;
 
   float m_run = -INFINITY, l_run = 0.f, beta = 0.f;
   f32x4 O[S::RT];
 #pragma unroll
   for (int rt = 0; rt < S::RT; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f16x2 c1152 = {(f16)1152.f, (f16)1152.f};
 
-  constexpr int KB = D / 8;  // key-row bytes per lane group
+  VerifyBuf<D> buf;
+  verify_load_k<D>(a, bh, g0, 0, buf);
+  verify_load_meta<D>(a, bh, g0, buf);
+  verify_load_v<D>(a, bh, g0, 0, buf);
   for (int gi = g0; gi < g1; ++gi) {
-    const uint8_t* ukg = a.uk + (bh * a.T + (size_t)gi * kGroup) * (D / 2);
-    const uint8_t* lkg = a.lk + (bh * a.T + (size_t)gi * kGroup) * (D / 2);
-    const uint8_t* uvg = a.uv + ((bh * a.NG + gi) * D) * (kGroup / 2);
-    const uint8_t* lvg = a.lv + ((bh * a.NG + gi) * D) * (kGroup / 2);
-    uint32_t ku[8][S::KK], kl[8][S::KK];
-#pragma unroll
-    for (int tau = 0; tau < 8; ++tau) {
-      const size_t rowoff = (size_t)tile_row_token(tau, j) * (D / 2) + g * KB;
-      if constexpr (S::KK == 4) {
-        const uint4 u = ld16(ukg + rowoff), l = ld16(lkg + rowoff);
-        ku[tau][0] = u.x; ku[tau][1] = u.y; ku[tau][2] = u.z; ku[tau][3] = u.w;
-        kl[tau][0] = l.x; kl[tau][1] = l.y; kl[tau][2] = l.z; kl[tau][3] = l.w;
-      } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(ukg + rowoff);
-        const uint2 l = *reinterpret_cast<const uint2*>(lkg + rowoff);
-        ku[tau][0] = u.x; ku[tau][1] = u.y;
-        kl[tau][0] = l.x; kl[tau][1] = l.y;
+    __syncthreads();  // the previous group's LDS reads are done
+    // q' = q s for this lane's channels and every query: fp16 hi/lo into the B-operand slots of
+    // the lanes that consume them, and the fp32 bias partials 1024 (q'h + q'l) + q' z
+    if (lane < D / 2) {
+      const float s0 = buf.km.x, z0 = buf.km.y, s1 = buf.km.z, z1 = buf.km.w;
+      const int c0 = 2 * lane;
+      const int gg = c0 / S::CPL, kk = (c0 % S::CPL) / 8, e0 = c0 % 8;  // e0 even, e0+1 odd
+      const int s_even = e0 >> 1, s_odd = 4 + (e0 >> 1);                // slots of e0, e0+1
+      f16* bh16 = reinterpret_cast<f16*>(&L.bq[0][kk][16 * gg]);
+      f16* bl16 = reinterpret_cast<f16*>(&L.bq[1][kk][16 * gg]);
+      for (int i = 0; i < m; ++i) {
+        {
+          const float2 qv = L.qs[i][lane];
+          const float qa = qv.x * s0, qb = qv.y * s1;
+          f16 ah, al, bhh, bl;
+          split_f16(qa, ah, al);
+          split_f16(qb, bhh, bl);
+          bh16[8 * i + s_even] = ah;
+          bl16[8 * i + s_even] = al;
+          bh16[8 * i + s_odd] = bhh;
+          bl16[8 * i + s_odd] = bl;
+          L.bias[i][lane] = 1024.f * (((float)ah + (float)al) + ((float)bhh + (float)bl)) +
+                            (qa * z0 + qb * z1);
+        }
       }
     }
-    uint4 vu[S::RT], vl[S::RT];
-#pragma unroll
-    for (int rt = 0; rt < S::RT; ++rt) {
-      const size_t off = (size_t)(16 * rt + j) * (kGroup / 2) + g * 16;
-      vu[rt] = ld16(uvg + off);
-      vl[rt] = ld16(lvg + off);
-    }
-    float4 km = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane < D / 2)
-      km = *reinterpret_cast<const float4*>(a.kmeta + (((bh * a.NG + gi) * D) + 2 * lane) * 2);
-    const float4 vm = *reinterpret_cast<const float4*>(a.vmeta + ((bh * a.T) + (size_t)gi * kGroup + 2 * lane) * 2);
-
+    L.vm[2 * lane] = make_float2(buf.vm.x, buf.vm.x * (128.f - buf.vm.y));
+    L.vm[2 * lane + 1] = make_float2(buf.vm.z, buf.vm.z * (128.f - buf.vm.w));
     __syncthreads();
-    if (lane < D / 2) {
-      L.km[2 * lane] = make_float2(km.x, km.y);
-      L.km[2 * lane + 1] = make_float2(km.z, km.w);
-    }
-    L.vm[2 * lane] = make_float2(vm.x, vm.x * (128.f - vm.y));
-    L.vm[2 * lane + 1] = make_float2(vm.z, vm.z * (128.f - vm.w));
-    __syncthreads();
-
-    // q' = q * s as fp16 hi + lo (B operands) and bias = sum_d (1024 (q'h + q'l)_d + q'_d z_d)
+    __builtin_amdgcn_sched_barrier(0);
+    if (gi + 1 < g1) verify_load_meta<D>(a, bh, gi + 1, buf);
     f16x8 Bq[S::KK], Bql[S::KK];
-    float bias = 0.f;
 #pragma unroll
     for (int kk = 0; kk < S::KK; ++kk) {
-      f16 qh[8], ql[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 8 * kk + e;
-        const float2 sz = L.km[g * S::CPL + c];
-        const float qp = qf[c] * sz.x;
-        split_f16(qp, qh[e], ql[e]);
-        bias += 1024.f * ((float)qh[e] + (float)ql[e]) + qp * sz.y;
-      }
-      Bq[kk] = f16x8{qh[0], qh[2], qh[4], qh[6], qh[1], qh[3], qh[5], qh[7]};
-      Bql[kk] = f16x8{ql[0], ql[2], ql[4], ql[6], ql[1], ql[3], ql[5], ql[7]};
+      Bq[kk] = __builtin_bit_cast(f16x8, L.bq[0][kk][lane]);
+      Bql[kk] = __builtin_bit_cast(f16x8, L.bq[1][kk][lane]);
     }
-    bias += __shfl_xor(bias, 16);
-    bias += __shfl_xor(bias, 32);
-
-    f32x4 St[8];
+    float bias = 0.f;  // lanes 16g .. 16g+15 of query j, then across the four k-groups
+    {
+      const float4* bp = reinterpret_cast<const float4*>(&L.bias[j][16 * g]);
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < S::KK; ++kk) {
-        const f16x8 A = codes_f16(ku[tau][kk], kl[tau][kk]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq[kk], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bql[kk], acc, 0, 0, 0);
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = bp[k];
+        bias += (v.x + v.y) + (v.z + v.w);
       }
-      St[tau] = acc - bias;
+      bias += __shfl_xor(bias, 16);
+      bias += __shfl_xor(bias, 32);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tau = 0; tau < 8; ++tau)
-      mx = fmaxf(mx, fmaxf(fmaxf(St[tau][0], St[tau][1]), fmaxf(St[tau][2], St[tau][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-    beta *= alpha;
-#pragma unroll
-    for (int rt = 0; rt < S::RT; ++rt) O[rt] *= alpha;
 
-    f16 ph[8][4], pl[8][4];
 #pragma unroll
-    for (int tau = 0; tau < 8; ++tau)
+    for (int half = 0; half < 2; ++half) {
+      f32x4 St[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(St[tau][i] - m_new);
-        const float2 sw = L.vm[32 * g + 8 * (tau >> 1) + 2 * i + (tau & 1)];
-        l_run += p;
-        beta += p * sw.y;
-        split_f16(p * sw.x, ph[tau][i], pl[tau][i]);
+      for (int t = 0; t < 4; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < S::KK; ++kk) {
+          const f16x8 A = codes_f16(buf.ku[t][kk], buf.kl[t][kk]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq[kk], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bql[kk], acc, 0, 0, 0);
+        }
+        St[t] = acc - bias;
+        __builtin_amdgcn_sched_barrier(0);
       }
-    const f16x2 c1152 = {(f16)1152.f, (f16)1152.f};
+      __builtin_amdgcn_sched_barrier(0);
+      {  // next key half: the other half of this group, or the first half of the next group
+        const int ngi = half == 0 ? gi : gi + 1;
+        if (ngi < g1) verify_load_k<D>(a, bh, ngi, half ^ 1, buf);
+      }
+      float mx = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f16x8 Bp = {ph[2 * q][0], ph[2 * q][1], ph[2 * q][2], ph[2 * q][3],
-                        ph[2 * q + 1][0], ph[2 * q + 1][1], ph[2 * q + 1][2], ph[2 * q + 1][3]};
-      const f16x8 Bpl = {pl[2 * q][0], pl[2 * q][1], pl[2 * q][2], pl[2 * q][3],
-                         pl[2 * q + 1][0], pl[2 * q + 1][1], pl[2 * q + 1][2], pl[2 * q + 1][3]};
+      for (int t = 0; t < 4; ++t)
+        mx = fmaxf(mx, fmaxf(fmaxf(St[t][0], St[t][1]), fmaxf(St[t][2], St[t][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      beta *= alpha;
 #pragma unroll
-      for (int rt = 0; rt < S::RT; ++rt) {
-        const uint32_t uw = q == 0 ? vu[rt].x : q == 1 ? vu[rt].y : q == 2 ? vu[rt].z : vu[rt].w;
-        const uint32_t lw = q == 0 ? vl[rt].x : q == 1 ? vl[rt].y : q == 2 ? vl[rt].z : vl[rt].w;
-        f16x8 A = codes_f16(uw, lw);
-        const f16x2 a0 = f16x2{A[0], A[1]} - c1152, a1 = f16x2{A[2], A[3]} - c1152;
-        const f16x2 a2 = f16x2{A[4], A[5]} - c1152, a3 = f16x2{A[6], A[7]} - c1152;
-        A = f16x8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
-        O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bp, O[rt], 0, 0, 0);
-        O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bpl, O[rt], 0, 0, 0);
+      for (int rt = 0; rt < S::RT; ++rt) O[rt] *= alpha;
+      f16 ph[4][4], pl[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(St[t][i] - m_new);
+          const float2 sw = L.vm[64 * half + 16 * g + 8 * (t >> 1) + 2 * i + (t & 1)];
+          l_run += p;
+          beta += p * sw.y;
+          split_f16(p * sw.x, ph[t][i], pl[t][i]);
+        }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f16x8 Bp = {ph[2 * q][0], ph[2 * q][1], ph[2 * q][2], ph[2 * q][3],
+                          ph[2 * q + 1][0], ph[2 * q + 1][1], ph[2 * q + 1][2], ph[2 * q + 1][3]};
+        const f16x8 Bpl = {pl[2 * q][0], pl[2 * q][1], pl[2 * q][2], pl[2 * q][3],
+                           pl[2 * q + 1][0], pl[2 * q + 1][1], pl[2 * q + 1][2], pl[2 * q + 1][3]};
+#pragma unroll
+        for (int rt = 0; rt < S::RT; ++rt) {
+          const uint32_t uw = q == 0 ? buf.vu[rt].x : buf.vu[rt].y;
+          const uint32_t lw = q == 0 ? buf.vl[rt].x : buf.vl[rt].y;
+          f16x8 A = codes_f16(uw, lw);
+          const f16x2 a0 = f16x2{A[0], A[1]} - c1152, a1 = f16x2{A[2], A[3]} - c1152;
+          const f16x2 a2 = f16x2{A[4], A[5]} - c1152, a3 = f16x2{A[6], A[7]} - c1152;
+          A = f16x8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+          O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bp, O[rt], 0, 0, 0);
+          O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bpl, O[rt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int ngi = half == 0 ? gi : gi + 1;
+        if (ngi < g1) verify_load_v<D>(a, bh, ngi, half ^ 1, buf);
       }
     }
   }
@@ -529,7 +690,7 @@ __device__ void tail_item(const AttnArgs& a, int b, int h, int chunk, int split,
     const bool vis = valid && t <= nt - m + i;
     if (!vis) s = -INFINITY;
     const float mx = wave_max_from(s, 1);
-    const float p = vis ? exp2f(s - mx) : 0.f;
+    const float p = vis ? fast_exp2(s - mx) : 0.f;
     const float sum = wave_sum_from(p, 1);
     if (lane == 0) {
       float* rec = record(a, D, b, h, split, i);
@@ -590,10 +751,10 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
 }
 
 template <int D, bool DRAFT>
-__global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgs a) {
+  using PassLds = typename std::conditional<DRAFT, DraftLds, VerifyLds>::type;
   __shared__ union {
-    DraftLds d;
-    VerifyLds v;
+    PassLds p;
     TailLds t;
   } lds;
   const int h = blockIdx.y;
@@ -608,9 +769,9 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
     const int b = find_seq(a.qitem_base, a.B, y);
     const int item = y - a.qitem_base[b];
     if constexpr (DRAFT)
-      draft_quant_item<D>(a, b, h, item, lds.d);
+      draft_quant_item<D>(a, b, h, item, lds.p);
     else
-      verify_quant_item<D>(a, b, h, item, lds.v);
+      verify_quant_item<D>(a, b, h, item, lds.p);
   }
 }
 
@@ -655,7 +816,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   for (int k = 0; k < 2; ++k) {
     const int s = t + 256 * k;
     if (s < ns) {
-      const float w = mv[k] == -INFINITY ? 0.f : exp2f(mv[k] - M);
+      const float w = mv[k] == -INFINITY ? 0.f : fast_exp2(mv[k] - M);
       wsh[s] = w;
       lloc += w * lv[k];
     }
@@ -830,11 +991,13 @@ __global__ __launch_bounds__(256) void flush_kernel(const FlushArgs a) {
       for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); ++d)
         code[t * D + d] = (uint8_t)quant_code((float)tile[t * RS + d], s, z);
       __syncthreads();
-      // value planes: channel-major rows of G/2 bytes, byte jb = token 2jb | 2jb+1
+      // value planes: two halves of G/2 tokens, each channel-major with rows of G/4 bytes,
+      // byte jb of a row = token 2jb (bits 0-3) | 2jb+1 (bits 4-7) of the half
       uint8_t* uv = a.uv + ((lbh * a.NG + grp) * D) * (G / 2);
       uint8_t* lv = a.lv + ((lbh * a.NG + grp) * D) * (G / 2);
       for (int c = tid; c < D * G / 32; c += 256) {  // 16 output bytes = 32 tokens of one channel
         const int d = c / (G / 32), t0 = (c % (G / 32)) * 32;
+        const int half = t0 / (G / 2), tin = t0 % (G / 2);
         uint32_t u[4], l[4];
         for (int k = 0; k < 4; ++k) {
           u[k] = 0; l[k] = 0;
@@ -844,7 +1007,7 @@ __global__ __launch_bounds__(256) void flush_kernel(const FlushArgs a) {
             l[k] |= (cc & 15u) << (4 * e);
           }
         }
-        const size_t o = (size_t)d * (G / 2) + t0 / 2;
+        const size_t o = (size_t)half * (D * G / 4) + (size_t)d * (G / 4) + tin / 2;
         *reinterpret_cast<uint4*>(uv + o) = make_uint4(u[0], u[1], u[2], u[3]);
         *reinterpret_cast<uint4*>(lv + o) = make_uint4(l[0], l[1], l[2], l[3]);
       }

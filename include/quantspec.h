@@ -95,9 +95,10 @@ typedef struct {
  *  uk, lk   u8  [L][B][H][T][D/2]      key planes, token-major rows.  Byte j of a token row
  *                                      holds channel 2j in bits 0-3 and channel 2j+1 in bits
  *                                      4-7 (uk: C_U = C8 >> 4, lk: C_L = C8 & 15).
- *  uv, lv   u8  [L][B][H][NG][D][G/2]  value planes, channel-major inside each group.  Byte j
- *                                      of the row of channel d holds token 2j of the group in
- *                                      bits 0-3 and token 2j+1 in bits 4-7.
+ *  uv, lv   u8  [L][B][H][NG][2][D][G/4]  value planes: each group is stored as two halves
+ *                                      of G/2 tokens, each channel-major.  Byte j of the row of
+ *                                      channel d in half e holds token e*G/2 + 2j of the group
+ *                                      in bits 0-3 and token e*G/2 + 2j + 1 in bits 4-7.
  *  kmeta    f32 [L][B][H][NG][D][2]    key (scale, zero-point) per group and channel.
  *  vmeta    f32 [L][B][H][T][2]        value (scale, zero-point) per token.
  *  tail_k,  f16 [L][B][H][2G][D]       fp16 tail ring.  Logical tail token i of a sequence

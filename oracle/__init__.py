@@ -198,8 +198,8 @@ class OracleCache:
         NG = T // G
         out = dict(
             uk=np.zeros((B, H, T, D // 2), np.uint8), lk=np.zeros((B, H, T, D // 2), np.uint8),
-            uv=np.zeros((B, H, NG, D, G // 2), np.uint8),
-            lv=np.zeros((B, H, NG, D, G // 2), np.uint8),
+            uv=np.zeros((B, H, NG, 2, D, G // 4), np.uint8),
+            lv=np.zeros((B, H, NG, 2, D, G // 4), np.uint8),
             kmeta=np.zeros((B, H, NG, D, 2), np.float32), vmeta=np.zeros((B, H, T, 2), np.float32),
             tail_k=np.zeros((B, H, 2 * G, D), np.uint16),
             tail_v=np.zeros((B, H, 2 * G, D), np.uint16))

@@ -371,9 +371,10 @@ int orc_read_meta(const orc_cache* c, int layer, int b, int h, float* kmeta, flo
 }
 
 /* Arena layout of one layer, written out index by index from its definition:
- *   key planes   [B][H][T][D/2]      byte j of token row t: channel 2j in bits 0-3, 2j+1 in 4-7
- *   value planes [B][H][NG][D][G/2]  byte j of channel row d of group g: token gG+2j in bits
- *                                    0-3, token gG+2j+1 in bits 4-7
+ *   key planes   [B][H][T][D/2]         byte j of token row t: channel 2j in bits 0-3, 2j+1 in
+ *                                       bits 4-7
+ *   value planes [B][H][NG][2][D][G/4]  byte j of channel row d of half e of group g: token
+ *                                       gG + eG/2 + 2j in bits 0-3, the next token in bits 4-7
  *   kmeta [B][H][NG][D][2], vmeta [B][H][T][2], tails [B][H][2G][D] (ring slots). */
 int orc_export_layer(const orc_cache* c, int layer, uint8_t* uk, uint8_t* lk, uint8_t* uv,
                      uint8_t* lv, float* kmeta, float* vmeta, uint16_t* tail_k,
@@ -394,15 +395,16 @@ int orc_export_layer(const orc_cache* c, int layer, uint8_t* uk, uint8_t* lk, ui
           if (lk) lk[o] = (uint8_t)(lower_nibble(c0) | (lower_nibble(c1) << 4));
         }
       for (int g = 0; g < NG; ++g)
-        for (int d = 0; d < D; ++d)
-          for (int j = 0; j < G / 2; ++j) {
-            int t0 = g * G + 2 * j, t1 = t0 + 1;
-            uint8_t c0 = t0 < nq ? c->vc[(r * T + t0) * D + d] : 0;
-            uint8_t c1 = t1 < nq ? c->vc[(r * T + t1) * D + d] : 0;
-            size_t o = ((bh * NG + g) * D + d) * (G / 2) + j;
-            if (uv) uv[o] = (uint8_t)(upper_nibble(c0) | (upper_nibble(c1) << 4));
-            if (lv) lv[o] = (uint8_t)(lower_nibble(c0) | (lower_nibble(c1) << 4));
-          }
+        for (int e = 0; e < 2; ++e)
+          for (int d = 0; d < D; ++d)
+            for (int j = 0; j < G / 4; ++j) {
+              int t0 = g * G + e * (G / 2) + 2 * j, t1 = t0 + 1;
+              uint8_t c0 = t0 < nq ? c->vc[(r * T + t0) * D + d] : 0;
+              uint8_t c1 = t1 < nq ? c->vc[(r * T + t1) * D + d] : 0;
+              size_t o = (((bh * NG + g) * 2 + e) * D + d) * (G / 4) + j;
+              if (uv) uv[o] = (uint8_t)(upper_nibble(c0) | (upper_nibble(c1) << 4));
+              if (lv) lv[o] = (uint8_t)(lower_nibble(c0) | (lower_nibble(c1) << 4));
+            }
       if (kmeta)
         for (int g = 0; g < NG; ++g)
           for (int d = 0; d < D; ++d) {

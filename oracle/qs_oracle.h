@@ -74,7 +74,7 @@ int orc_read_codes(const orc_cache* c, int layer, int b, int h, int which_v, uin
 int orc_read_meta(const orc_cache* c, int layer, int b, int h, float* kmeta, float* vmeta);
 
 /* Packs one layer into the arena layout of the library (per-layer slices of each section):
- *   uk, lk [B][H][T][D/2]; uv, lv [B][H][T/G][D][G/2]; kmeta [B][H][T/G][D][2];
+ *   uk, lk [B][H][T][D/2]; uv, lv [B][H][T/G][2][D][G/4]; kmeta [B][H][T/G][D][2];
  *   vmeta [B][H][T][2]; tail_k, tail_v [B][H][2G][D] (fp16 bits, the ring slots).
  * Quantized rows >= nq and ring slots never written are zero. */
 int orc_export_layer(const orc_cache* c, int layer, uint8_t* uk, uint8_t* lk, uint8_t* uv,

@@ -435,9 +435,10 @@ def test_layout_export_matches_split_identity():
         assert np.array_equal(even, ck[:, 0::2]) and np.array_equal(odd, ck[:, 1::2])
         uv, lv = img["uv"][0, h].astype(np.int64), img["lv"][0, h].astype(np.int64)
         for g in range(2):
-            tok = cv[g * G:(g + 1) * G]                # [G][D]
-            ev = 16 * (uv[g] & 15) + (lv[g] & 15)      # [D][G/2]: tokens 0, 2, 4, ...
-            od = 16 * (uv[g] >> 4) + (lv[g] >> 4)
-            assert np.array_equal(ev, tok[0::2].T) and np.array_equal(od, tok[1::2].T)
+            for e in range(2):                          # two halves of G/2 tokens
+                tok = cv[g * G + e * G // 2: g * G + (e + 1) * G // 2]   # [G/2][D]
+                ev = 16 * (uv[g, e] & 15) + (lv[g, e] & 15)   # [D][G/4]: tokens 0, 2, 4, ...
+                od = 16 * (uv[g, e] >> 4) + (lv[g, e] >> 4)
+                assert np.array_equal(ev, tok[0::2].T) and np.array_equal(od, tok[1::2].T)
         km, vm = c.meta(0, 0, h)
         assert np.array_equal(img["kmeta"][0, h], km) and np.array_equal(img["vmeta"][0, h], vm)
