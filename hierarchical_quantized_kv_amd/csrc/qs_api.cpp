@@ -18,6 +18,7 @@ namespace qs {
 hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st);
 hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st);
+int attention_slots(int D, bool draft);
 }  // namespace qs
 
 struct qs_cache {
@@ -30,14 +31,9 @@ struct qs_cache {
 
 namespace {
 
-// (sequence, head, chunk) work items per attention call: about one resident round of waves
-// (256 CUs x waves per CU the pass's register use allows: 12 for draft, 8 for verify).
-#ifndef QS_TARGET_ITEMS_DRAFT
-#define QS_TARGET_ITEMS_DRAFT 3072
-#endif
-#ifndef QS_TARGET_ITEMS_VERIFY
-#define QS_TARGET_ITEMS_VERIFY 2048
-#endif
+// Work items per attention call: one resident round of waves, i.e. the pass kernel's slots on the
+// device (compute units x resident one-wave workgroups) minus the tail items; 2048 if unknown.
+constexpr int kFallbackSlots = 2048;
 
 qs_status fail(qs_cache* c, qs_status s, const std::string& m) {
   if (c) c->err = m;
@@ -204,8 +200,13 @@ static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, 
   const int D = cf.head_dim;
   qs::Seq seqs[QS_MAX_BATCH];
   for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
-  const qs::Plan p = qs::make_plan(seqs, cf.batch, cf.n_heads, cf.group,
-                                   draft ? QS_TARGET_ITEMS_DRAFT : QS_TARGET_ITEMS_VERIFY);
+  int slots = qs::attention_slots(D, draft);
+  if (slots <= 0) slots = kFallbackSlots;
+  int tail_items = 0;
+  for (int b = 0; b < cf.batch; ++b)
+    tail_items += cf.n_heads * ((seqs[b].nt + qs::kTailChunk - 1) / qs::kTailChunk);
+  const int target = slots - tail_items > slots / 2 ? slots - tail_items : slots / 2;
+  const qs::Plan p = qs::make_plan(seqs, cf.batch, cf.n_heads, cf.group, target);
   qs::AttnArgs a{};
   const size_t T = cf.max_ctx, G = cf.group, NG = T / G;
   a.uk = c->arena + c->lay.uk + layer_off(c, T * (D / 2), layer);

@@ -56,6 +56,74 @@ __device__ __forceinline__ float dot2_ord(uint32_t a, uint32_t b, float c) {
   asm volatile("v_dot2c_f32_f16 %0, %1, %2" : "+v"(c) : "v"(a), "v"(b));
   return c;
 }
+// One 32-bit word of the upper key plane (8 channels) against its weights q'/4, fp16 hi and lo:
+//   p += sum over the pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7) of (1024 + 64 U) . (w_hi + w_lo),
+// each nibble moved into the top mantissa bits 6-9 of an fp16 1024 (the offset then stays about
+// the size of the data, which keeps the fp32 sum accurate) by a shift and one v_and_or_b32.
+// Written as one instruction sequence so that the compiler adds no wait states inside it.
+__device__ __forceinline__ float key_word_dot(float p, uint32_t w, uint32_t magic, uint4 wh,
+                                              uint4 wl) {
+  uint32_t t;
+  asm volatile(
+      "v_lshlrev_b32 %[t], 6, %[w]\n\t"
+      "v_and_or_b32 %[t], %[t], %[m], %[mg]\n\t"
+      "v_dot2c_f32_f16 %[p], %[t], %[h0]\n\t"
+      "v_dot2c_f32_f16 %[p], %[t], %[l0]\n\t"
+      "v_lshlrev_b32 %[t], 2, %[w]\n\t"
+      "v_and_or_b32 %[t], %[t], %[m], %[mg]\n\t"
+      "v_dot2c_f32_f16 %[p], %[t], %[h1]\n\t"
+      "v_dot2c_f32_f16 %[p], %[t], %[l1]\n\t"
+      "v_lshrrev_b32 %[t], 2, %[w]\n\t"
+      "v_and_or_b32 %[t], %[t], %[m], %[mg]\n\t"
+      "v_dot2c_f32_f16 %[p], %[t], %[h2]\n\t"
+      "v_dot2c_f32_f16 %[p], %[t], %[l2]\n\t"
+      "v_lshrrev_b32 %[t], 6, %[w]\n\t"
+      "v_and_or_b32 %[t], %[t], %[m], %[mg]\n\t"
+      "v_dot2c_f32_f16 %[p], %[t], %[h3]\n\t"
+      "v_dot2c_f32_f16 %[p], %[t], %[l3]"
+      : [p] "+v"(p), [t] "=&v"(t)
+      : [w] "v"(w), [m] "s"(0x03C003C0u), [mg] "v"(magic), [h0] "v"(wh.x), [h1] "v"(wh.y),
+        [h2] "v"(wh.z), [h3] "v"(wh.w), [l0] "v"(wl.x), [l1] "v"(wl.y), [l2] "v"(wl.z),
+        [l3] "v"(wl.w));
+  return p;
+}
+
+// One 32-bit word of the upper value plane (8 tokens of one channel) against the tokens'
+// weights, fp16 hi and lo: pairs (t0,t4) and (t2,t6) as 1024 + U, (t1,t5) and (t3,t7) as
+// 1024 + 16 U (the weights of even tokens carry the factor 16).
+__device__ __forceinline__ float value_word_dot(float o, uint32_t w, uint32_t magic, uint4 ph,
+                                                uint4 pl) {
+  uint32_t t, w8;
+  asm volatile(
+      "v_and_or_b32 %[t], %[w], %[mlo], %[mg]\n\t"
+      "v_dot2c_f32_f16 %[o], %[t], %[h0]\n\t"
+      "v_dot2c_f32_f16 %[o], %[t], %[l0]\n\t"
+      "v_and_or_b32 %[t], %[w], %[mhi], %[mg]\n\t"
+      "v_dot2c_f32_f16 %[o], %[t], %[h1]\n\t"
+      "v_dot2c_f32_f16 %[o], %[t], %[l1]\n\t"
+      "v_lshrrev_b32 %[w8], 8, %[w]\n\t"
+      "v_and_or_b32 %[t], %[w8], %[mlo], %[mg]\n\t"
+      "v_dot2c_f32_f16 %[o], %[t], %[h2]\n\t"
+      "v_dot2c_f32_f16 %[o], %[t], %[l2]\n\t"
+      "v_and_or_b32 %[t], %[w8], %[mhi], %[mg]\n\t"
+      "v_dot2c_f32_f16 %[o], %[t], %[h3]\n\t"
+      "v_dot2c_f32_f16 %[o], %[t], %[l3]"
+      : [o] "+v"(o), [t] "=&v"(t), [w8] "=&v"(w8)
+      : [w] "v"(w), [mlo] "s"(0x000F000Fu), [mhi] "s"(0x00F000F0u), [mg] "v"(magic),
+        [h0] "v"(ph.x), [h1] "v"(ph.y), [h2] "v"(ph.z), [h3] "v"(ph.w), [l0] "v"(pl.x),
+        [l1] "v"(pl.y), [l2] "v"(pl.z), [l3] "v"(pl.w));
+  return o;
+}
+
+// Power of two f such that every value weight of a group, at most 16 * smax (even tokens carry the
+// factor 16), scaled by f stays below 2^14: the fp16 hi/lo weights then keep full relative
+// precision instead of falling into the fp16 subnormal range for small softmax probabilities.
+__device__ __forceinline__ float weight_scale(float smax) {
+  int e;
+  frexpf(16.f * smax, &e);  // 16 smax < 2^e
+  return ldexpf(1.f, 14 - e);
+}
+
 // 2^x with the hardware instruction (results below 2^-126 flush to zero).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -71,6 +139,43 @@ __device__ __forceinline__ uint2 ld8_nt(const void* p) {
   const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   return make_uint2(v.x, v.y);
 }
+// Buffer loads: a wave-uniform resource (base address and byte range in SGPRs) plus a per-lane
+// 32-bit offset, with the streaming (non-temporal) cache policy.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr int kNt = 2;
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNt);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 bld8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNt);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float4 bldf4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const uint4 v = bld16(r, voff, soff);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+
+// The four streams of one (sequence, head) of a layer.
+struct Streams {
+  rsrc_t uk, lk, uv, lv, km, vm;
+};
+__device__ __forceinline__ Streams make_streams(const AttnArgs& a, size_t bh, int D) {
+  const uint32_t plane = (uint32_t)a.T * (uint32_t)(D / 2);  // bytes of one plane per (b, h)
+  Streams st;
+  st.uk = make_rsrc(a.uk + bh * plane, plane);
+  st.lk = make_rsrc(a.lk + bh * plane, plane);
+  st.uv = make_rsrc(a.uv + bh * plane, plane);
+  st.lv = make_rsrc(a.lv + bh * plane, plane);
+  st.km = make_rsrc(a.kmeta + bh * (size_t)a.NG * D * 2, (uint32_t)a.NG * D * 8);
+  st.vm = make_rsrc(a.vmeta + bh * (size_t)a.T * 2, (uint32_t)a.T * 8);
+  return st;
+}
+
 __device__ __forceinline__ float4 ldf4_nt(const float* p) {
   const uint4 v = ld16_nt(p);
   return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
@@ -139,6 +244,36 @@ __device__ __forceinline__ f16x8 codes_f16(uint32_t u, uint32_t l) {
 // Slot s of codes_f16() holds entry kSigma[s].
 // kSigma = {0, 2, 4, 6, 1, 3, 5, 7}
 
+// Cross-lane steps with DPP (no LDS round trip): quad_perm swaps inside groups of four lanes,
+// the mirrors inside half rows (8 lanes) and rows (16 lanes); readlane reads the four rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+__device__ __forceinline__ float lane_read(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+// Sum / max over all 64 lanes; every lane gets the result.
+__device__ __forceinline__ float wave_sum_all(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  x += dpp<kDppMirror>(x);
+  return (lane_read(x, 0) + lane_read(x, 16)) + (lane_read(x, 32) + lane_read(x, 48));
+}
+__device__ __forceinline__ float wave_max_all(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  return fmaxf(fmaxf(lane_read(x, 0), lane_read(x, 16)), fmaxf(lane_read(x, 32), lane_read(x, 48)));
+}
+
 __device__ __forceinline__ float wave_max_from(float x, int from) {
   for (int o = from; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
@@ -167,7 +302,7 @@ struct DraftShape {
 
 struct DraftLds {
   uint32_t wts[2][64];   // key weights q' (hi, lo), pair order (D/2 words used)
-  uint32_t pw[64];       // value weights in pair order: 16 p'_t (even t), p'_t (odd t)
+  uint32_t pw[2][64];    // value weights (hi, lo) in pair order: 16 p'_t (even t), p'_t (odd t)
   float2 vm[kGroup];     // (s_t, s_t * (off - z_t))
 };
 
@@ -181,32 +316,31 @@ struct DraftBuf {
 };
 
 template <int D>
-__device__ __forceinline__ void draft_load_k(const AttnArgs& a, size_t bh, int g, DraftBuf<D>& buf) {
+__device__ __forceinline__ void draft_load_k(const Streams& sm, int g, DraftBuf<D>& buf) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
-  const int kc = lane % S::KL, kt = lane / S::KL;
-  const uint8_t* ukg = a.uk + (bh * a.T + (size_t)g * kGroup) * (D / 2);
+  const uint32_t voff = (lane / S::KL) * (D / 2) + (lane % S::KL) * 16;
+  const uint32_t soff = (uint32_t)g * kGroup * (D / 2);
 #pragma unroll
-  for (int it = 0; it < S::KIT; ++it)
-    buf.k[it] = ld16_nt(ukg + (size_t)(it * S::TPI + kt) * (D / 2) + kc * 16);
+  for (int it = 0; it < S::KIT; ++it)  // key rows it*TPI .. : 1 KB apart
+    buf.k[it] = bld16(sm.uk, voff + (it & 3) * 1024, soff + (it >> 2) * 4096);
 }
 template <int D>
-__device__ __forceinline__ void draft_load_meta(const AttnArgs& a, size_t bh, int g, DraftBuf<D>& buf) {
+__device__ __forceinline__ void draft_load_meta(const Streams& sm, int g, DraftBuf<D>& buf) {
   const int lane = threadIdx.x;
-  buf.km = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (lane < D / 2) buf.km = ldf4_nt(a.kmeta + (((bh * a.NG + g) * D) + 2 * lane) * 2);
-  buf.vm = ldf4_nt(a.vmeta + ((bh * a.T) + (size_t)g * kGroup + 2 * lane) * 2);
+  buf.km = bldf4(sm.km, lane * 16, (uint32_t)g * D * 8);
+  if (lane >= D / 2) buf.km = make_float4(0.f, 0.f, 0.f, 0.f);
+  buf.vm = bldf4(sm.vm, lane * 16, (uint32_t)g * kGroup * 8);
 }
 template <int D>
-__device__ __forceinline__ void draft_load_v(const AttnArgs& a, size_t bh, int g, DraftBuf<D>& buf) {
+__device__ __forceinline__ void draft_load_v(const Streams& sm, int g, DraftBuf<D>& buf) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
   const int vr = lane & 3, vd = lane >> 2;
-  const uint8_t* uvg = a.uv + ((bh * a.NG + g) * D) * (kGroup / 2);
+  const uint32_t voff = (vr >> 1) * (D * kGroup / 4) + vd * (kGroup / 4) + (vr & 1) * 16;
+  const uint32_t soff = (uint32_t)g * D * (kGroup / 2);
 #pragma unroll
-  for (int i = 0; i < S::VIT; ++i)
-    buf.v[i] = ld16_nt(uvg + (vr >> 1) * (D * kGroup / 4) + (size_t)(16 * i + vd) * (kGroup / 4) +
-                       (vr & 1) * 16);
+  for (int i = 0; i < S::VIT; ++i) buf.v[i] = bld16(sm.uv, voff + i * 16 * (kGroup / 4), soff);
 }
 
 // Running softmax state of a draft work item (per lane).
@@ -221,7 +355,7 @@ struct DraftAcc {
 // The registers of `cur` are refilled with group `gnext` (if >= 0) as soon as each part of the
 // current group has been consumed, so the next group's loads overlap this group's arithmetic.
 template <int D>
-__device__ __forceinline__ void draft_group(const AttnArgs& a, size_t bh, DraftBuf<D>& cur,
+__device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm, DraftBuf<D>& cur,
                                             int gnext, float q0, float q1, uint32_t magic,
                                             DraftLds& L, DraftAcc<D>& st) {
   using S = DraftShape<D>;
@@ -232,11 +366,11 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, size_t bh, DraftB
   __syncthreads();  // the previous group's LDS reads are done
   float bias = 0.f;
   if (lane < D / 2) {
-    // key weights q' = q s as fp16 hi + lo, against nibble values 1024 + 16 U
+    // key weights q'/4 = q s / 4 as fp16 hi + lo, against nibble values 1024 + 64 U
     const float qa = q0 * cur.km.x, qb = q1 * cur.km.z;
     f16 ah, al, bh, bl;
-    split_f16(qa, ah, al);
-    split_f16(qb, bh, bl);
+    split_f16(0.25f * qa, ah, al);
+    split_f16(0.25f * qb, bh, bl);
     const int c0 = 2 * lane, c1 = 2 * lane + 1;
     f16* wh = reinterpret_cast<f16*>(L.wts[0]);
     f16* wl = reinterpret_cast<f16*>(L.wts[1]);
@@ -249,9 +383,10 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, size_t bh, DraftB
   }
   L.vm[2 * lane] = make_float2(cur.vm.x, cur.vm.x * (off - cur.vm.y));
   L.vm[2 * lane + 1] = make_float2(cur.vm.z, cur.vm.z * (off - cur.vm.w));
+  const float wscale = weight_scale(wave_max_all(fmaxf(cur.vm.x, cur.vm.z)));
   __builtin_amdgcn_sched_barrier(0);
-  if (gnext >= 0) draft_load_meta<D>(a, bh, gnext, cur);
-  bias = wave_sum_from(bias, 1);
+  if (gnext >= 0) draft_load_meta<D>(sm, gnext, cur);
+  bias = wave_sum_all(bias);
   __syncthreads();
 
   uint4 W[4], Wl[4];
@@ -266,32 +401,20 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, size_t bh, DraftB
     const uint32_t wd[4] = {cur.k[it].x, cur.k[it].y, cur.k[it].z, cur.k[it].w};
     float p = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = wd[k];
-      const uint32_t na = and_or(w << 4, 0x00F000F0u, magic);  // (e0, e4): 1024 + 16 U
-      p = dot2_ord(na, W[k].x, p);
-      p = dot2_ord(na, Wl[k].x, p);
-      const uint32_t nb = and_or(w, 0x00F000F0u, magic);       // (e1, e5)
-      p = dot2_ord(nb, W[k].y, p);
-      p = dot2_ord(nb, Wl[k].y, p);
-      const uint32_t nc = and_or(w >> 4, 0x00F000F0u, magic);  // (e2, e6)
-      p = dot2_ord(nc, W[k].z, p);
-      p = dot2_ord(nc, Wl[k].z, p);
-      const uint32_t nd = and_or(w >> 8, 0x00F000F0u, magic);  // (e3, e7)
-      p = dot2_ord(nd, W[k].w, p);
-      p = dot2_ord(nd, Wl[k].w, p);
-    }
-#pragma unroll
-    for (int o = 1; o < S::KL; o <<= 1) p += __shfl_xor(p, o);
+    for (int k = 0; k < 4; ++k) p = key_word_dot(p, wd[k], magic, W[k], Wl[k]);
+    // a DPP read of a VGPR needs two wait states after the VALU write that produced it; the
+    // write is the last instruction of the asm sequence above, invisible to the compiler
+    asm volatile("s_nop 1" : "+v"(p));
+    p += dpp<kDppXor1>(p);                       // the KL lanes of a key row
+    if constexpr (S::KL == 4) p += dpp<kDppXor2>(p);
     sc[it] = p + bias;
-    __builtin_amdgcn_sched_barrier(0);  // bound the live nibble temporaries to one load
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (gnext >= 0) draft_load_k<D>(a, bh, gnext, cur);
+  if (gnext >= 0) draft_load_k<D>(sm, gnext, cur);
   float gmax = sc[0];
 #pragma unroll
   for (int it = 1; it < S::KIT; ++it) gmax = fmaxf(gmax, sc[it]);
-  gmax = wave_max_from(gmax, S::KL);
+  gmax = wave_max_all(gmax);
   const float m_new = fmaxf(st.m_run, gmax);
   const float alpha = fast_exp2(st.m_run - m_new);
   st.m_run = m_new;
@@ -305,17 +428,23 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, size_t bh, DraftB
     st.l_run += p;
     st.beta += p * sw.y;
     // every lane of the key row writes the same value
-    reinterpret_cast<f16*>(L.pw)[2 * pair_word(t) + pair_half(t)] =
-        (f16)((t & 1) ? p * sw.x : 16.f * p * sw.x);
+    f16 wh, wl;
+    split_f16(((t & 1) ? wscale : 16.f * wscale) * (p * sw.x), wh, wl);
+    reinterpret_cast<f16*>(L.pw[0])[2 * pair_word(t) + pair_half(t)] = wh;
+    reinterpret_cast<f16*>(L.pw[1])[2 * pair_word(t) + pair_half(t)] = wl;
   }
   __syncthreads();
 
   // values: a fresh fp32 sum per group of w_t (1024 + U or 1024 + 16 U); the group's exact
   // offset 1024 sum_t w_t is removed before it joins the running (rescaled) sum.
-  uint4 P[4];
+  uint4 P[4], Pl[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) P[k] = reinterpret_cast<const uint4*>(L.pw)[4 * vr + k];
+  for (int k = 0; k < 4; ++k) {
+    P[k] = reinterpret_cast<const uint4*>(L.pw[0])[4 * vr + k];
+    Pl[k] = reinterpret_cast<const uint4*>(L.pw[1])[4 * vr + k];
+  }
   const f16x2 k1024 = {(f16)1024.f, (f16)1024.f};
+  const float winv = 1.f / wscale;  // exact: a power of two
   float corr = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -323,24 +452,22 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, size_t bh, DraftB
     corr = dot2(as_h2(P[k].y), k1024, corr);
     corr = dot2(as_h2(P[k].z), k1024, corr);
     corr = dot2(as_h2(P[k].w), k1024, corr);
+    corr = dot2(as_h2(Pl[k].x), k1024, corr);
+    corr = dot2(as_h2(Pl[k].y), k1024, corr);
+    corr = dot2(as_h2(Pl[k].z), k1024, corr);
+    corr = dot2(as_h2(Pl[k].w), k1024, corr);
   }
 #pragma unroll
   for (int i = 0; i < S::VIT; ++i) {
     const uint32_t wd[4] = {cur.v[i].x, cur.v[i].y, cur.v[i].z, cur.v[i].w};
     float o = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = wd[k], w8 = w >> 8;
-      o = dot2_ord(and_or(w, 0x000F000Fu, magic), P[k].x, o);   // (t0, t4): 1024 + U
-      o = dot2_ord(and_or(w, 0x00F000F0u, magic), P[k].y, o);   // (t1, t5): 1024 + 16 U
-      o = dot2_ord(and_or(w8, 0x000F000Fu, magic), P[k].z, o);  // (t2, t6)
-      o = dot2_ord(and_or(w8, 0x00F000F0u, magic), P[k].w, o);  // (t3, t7)
-    }
-    st.o[i] = fmaf(st.o[i], alpha, o - corr);
+    for (int k = 0; k < 4; ++k) o = value_word_dot(o, wd[k], magic, P[k], Pl[k]);
+    st.o[i] = fmaf(st.o[i], alpha, (o - corr) * winv);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (gnext >= 0) draft_load_v<D>(a, bh, gnext, cur);
+  if (gnext >= 0) draft_load_v<D>(sm, gnext, cur);
 }
 
 template <int D>
@@ -367,12 +494,13 @@ __device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, Draf
 #pragma unroll
   for (int i = 0; i < S::VIT; ++i) st.o[i] = 0.f;
 
+  const Streams sm = make_streams(a, bh, D);
   DraftBuf<D> buf;
-  draft_load_k<D>(a, bh, g0, buf);
-  draft_load_meta<D>(a, bh, g0, buf);
-  draft_load_v<D>(a, bh, g0, buf);
+  draft_load_k<D>(sm, g0, buf);
+  draft_load_meta<D>(sm, g0, buf);
+  draft_load_v<D>(sm, g0, buf);
   for (int g = g0; g < g1; ++g)
-    draft_group<D>(a, bh, buf, g + 1 < g1 ? g + 1 : -1, q0, q1, magic, L, st);
+    draft_group<D>(a, sm, buf, g + 1 < g1 ? g + 1 : -1, q0, q1, magic, L, st);
 
   // l and beta were accumulated once per key row in each of its KL lanes
   const float l_run = wave_sum_from(st.l_run, S::KL);
@@ -433,22 +561,21 @@ struct VerifyBuf {
 };
 
 template <int D>
-__device__ __forceinline__ void verify_load_k(const AttnArgs& a, size_t bh, int gi, int half,
-                                              VerifyBuf<D>& buf) {
+__device__ __forceinline__ void verify_load_k(const Streams& sm, int gi, int half, VerifyBuf<D>& buf) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
-  const uint8_t* ukg = a.uk + (bh * a.T + (size_t)gi * kGroup) * (D / 2);
-  const uint8_t* lkg = a.lk + (bh * a.T + (size_t)gi * kGroup) * (D / 2);
+  // row of tile 4*half + t for lane row j: 16 (j/4) + 2 (j%4) + 64 half + 8 (t/2) + (t%2)
+  const uint32_t voff = (16 * (j >> 2) + 2 * (j & 3)) * (D / 2) + g * S::KB;
+  const uint32_t soff = ((uint32_t)gi * kGroup + 64 * half) * (D / 2);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const size_t off = (size_t)vtile_token(4 * half + t, j) * (D / 2) + g * S::KB;
+    const uint32_t o = voff + (8 * (t >> 1) + (t & 1)) * (D / 2);
     if constexpr (S::KK == 4) {
-      const uint4 u = ld16_nt(ukg + off), l = ld16_nt(lkg + off);
+      const uint4 u = bld16(sm.uk, o, soff), l = bld16(sm.lk, o, soff);
       buf.ku[t][0] = u.x; buf.ku[t][1] = u.y; buf.ku[t][2] = u.z; buf.ku[t][3] = u.w;
       buf.kl[t][0] = l.x; buf.kl[t][1] = l.y; buf.kl[t][2] = l.z; buf.kl[t][3] = l.w;
     } else {
-      const uint2 u = ld8_nt(ukg + off);
-      const uint2 l = ld8_nt(lkg + off);
+      const uint2 u = bld8(sm.uk, o, soff), l = bld8(sm.lk, o, soff);
       buf.ku[t][0] = u.x; buf.ku[t][1] = u.y;
       buf.kl[t][0] = l.x; buf.kl[t][1] = l.y;
     }
@@ -456,27 +583,25 @@ __device__ __forceinline__ void verify_load_k(const AttnArgs& a, size_t bh, int 
 }
 
 template <int D>
-__device__ __forceinline__ void verify_load_v(const AttnArgs& a, size_t bh, int gi, int half,
-                                              VerifyBuf<D>& buf) {
+__device__ __forceinline__ void verify_load_v(const Streams& sm, int gi, int half, VerifyBuf<D>& buf) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
-  const uint8_t* uvg = a.uv + ((bh * a.NG + gi) * D) * (kGroup / 2);
-  const uint8_t* lvg = a.lv + ((bh * a.NG + gi) * D) * (kGroup / 2);
+  const uint32_t voff = j * (kGroup / 4) + 8 * g;
+  const uint32_t soff = (uint32_t)gi * D * (kGroup / 2) + (uint32_t)half * D * (kGroup / 4);
 #pragma unroll
   for (int rt = 0; rt < S::RT; ++rt) {
-    const size_t off = (size_t)half * (D * kGroup / 4) + (size_t)(16 * rt + j) * (kGroup / 4) + 8 * g;
-    buf.vu[rt] = ld8_nt(uvg + off);
-    buf.vl[rt] = ld8_nt(lvg + off);
+    const uint32_t o = voff + rt * 16 * (kGroup / 4);
+    buf.vu[rt] = bld8(sm.uv, o, soff);
+    buf.vl[rt] = bld8(sm.lv, o, soff);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void verify_load_meta(const AttnArgs& a, size_t bh, int gi,
-                                                 VerifyBuf<D>& buf) {
+__device__ __forceinline__ void verify_load_meta(const Streams& sm, int gi, VerifyBuf<D>& buf) {
   const int lane = threadIdx.x;
-  buf.km = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (lane < D / 2) buf.km = ldf4_nt(a.kmeta + (((bh * a.NG + gi) * D) + 2 * lane) * 2);
-  buf.vm = ldf4_nt(a.vmeta + ((bh * a.T) + (size_t)gi * kGroup + 2 * lane) * 2);
+  buf.km = bldf4(sm.km, lane * 16, (uint32_t)gi * D * 8);
+  if (lane >= D / 2) buf.km = make_float4(0.f, 0.f, 0.f, 0.f);
+  buf.vm = bldf4(sm.vm, lane * 16, (uint32_t)gi * kGroup * 8);
 }
 
 template <int D>
@@ -503,15 +628,17 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
   for (int x = lane; x < QS_MAX_QUERIES * 64; x += 64) (&L.bias[0][0])[x] = 0.f;
 
   float m_run = -INFINITY, l_run = 0.f, beta = 0.f;
+  float oinv = 1.f;  // inverse of the weight scale O is kept in
   f32x4 O[S::RT];
 #pragma unroll
   for (int rt = 0; rt < S::RT; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f16x2 c1152 = {(f16)1152.f, (f16)1152.f};
 
+  const Streams sm = make_streams(a, bh, D);
   VerifyBuf<D> buf;
-  verify_load_k<D>(a, bh, g0, 0, buf);
-  verify_load_meta<D>(a, bh, g0, buf);
-  verify_load_v<D>(a, bh, g0, 0, buf);
+  verify_load_k<D>(sm, g0, 0, buf);
+  verify_load_meta<D>(sm, g0, buf);
+  verify_load_v<D>(sm, g0, 0, buf);
   for (int gi = g0; gi < g1; ++gi) {
     __syncthreads();  // the previous group's LDS reads are done
     // q' = q s for this lane's channels and every query: fp16 hi/lo into the B-operand slots of
@@ -541,9 +668,10 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
     }
     L.vm[2 * lane] = make_float2(buf.vm.x, buf.vm.x * (128.f - buf.vm.y));
     L.vm[2 * lane + 1] = make_float2(buf.vm.z, buf.vm.z * (128.f - buf.vm.w));
+    const float wscale = weight_scale(wave_max_all(fmaxf(buf.vm.x, buf.vm.z)));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    if (gi + 1 < g1) verify_load_meta<D>(a, bh, gi + 1, buf);
+    if (gi + 1 < g1) verify_load_meta<D>(sm, gi + 1, buf);
     f16x8 Bq[S::KK], Bql[S::KK];
 #pragma unroll
     for (int kk = 0; kk < S::KK; ++kk) {
@@ -580,7 +708,7 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
       __builtin_amdgcn_sched_barrier(0);
       {  // next key half: the other half of this group, or the first half of the next group
         const int ngi = half == 0 ? gi : gi + 1;
-        if (ngi < g1) verify_load_k<D>(a, bh, ngi, half ^ 1, buf);
+        if (ngi < g1) verify_load_k<D>(sm, ngi, half ^ 1, buf);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -593,8 +721,11 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
       m_run = m_new;
       l_run *= alpha;
       beta *= alpha;
+      // O is kept in the weight scale of the current group
+      const float oscale = alpha * (wscale * oinv);
+      oinv = 1.f / wscale;
 #pragma unroll
-      for (int rt = 0; rt < S::RT; ++rt) O[rt] *= alpha;
+      for (int rt = 0; rt < S::RT; ++rt) O[rt] *= oscale;
       f16 ph[4][4], pl[4][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -604,7 +735,7 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
           const float2 sw = L.vm[64 * half + 16 * g + 8 * (t >> 1) + 2 * i + (t & 1)];
           l_run += p;
           beta += p * sw.y;
-          split_f16(p * sw.x, ph[t][i], pl[t][i]);
+          split_f16(wscale * (p * sw.x), ph[t][i], pl[t][i]);
         }
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -628,7 +759,7 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
       __builtin_amdgcn_sched_barrier(0);
       {
         const int ngi = half == 0 ? gi : gi + 1;
-        if (ngi < g1) verify_load_v<D>(a, bh, ngi, half ^ 1, buf);
+        if (ngi < g1) verify_load_v<D>(sm, ngi, half ^ 1, buf);
       }
     }
   }
@@ -646,7 +777,7 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
 #pragma unroll
     for (int rt = 0; rt < S::RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rec[kRecPad + 16 * rt + 4 * g + i] = O[rt][i] + beta;
+      for (int i = 0; i < 4; ++i) rec[kRecPad + 16 * rt + 4 * g + i] = fmaf(O[rt][i], oinv, beta);
   }
 }
 
@@ -1035,6 +1166,24 @@ hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st)
   if (D == 128) hipLaunchKernelGGL(flush_kernel<128>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(flush_kernel<64>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// Work-item slots of one attention pass on the current device: compute units times the
+// one-wave workgroups of that kernel a compute unit holds at once (cached per device).
+int attention_slots(int D, bool draft) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int& slot = cache[dev][D == 128][draft];
+  if (slot > 0) return slot;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const void* fn = D == 128 ? (draft ? (const void*)attn_kernel<128, true> : (const void*)attn_kernel<128, false>)
+                            : (draft ? (const void*)attn_kernel<64, true> : (const void*)attn_kernel<64, false>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
+  slot = cus * per_cu;
+  return slot;
 }
 
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st) {

@@ -80,9 +80,9 @@ struct Plan {
   int32_t tbase[QS_MAX_BATCH + 1] = {};
 };
 
-// Quantized work items are whole-group chunks; the chunk length is chosen so that the call has
-// about `target_items` (sequence, head, chunk) items in total, bounded so that no sequence needs
-// more than kMaxQuantSplits chunks.
+// Quantized work items are whole-group chunks.  The chunk length is the smallest one that keeps
+// the call at no more than `target_items` (sequence, head, chunk) items (so that they all run in
+// one resident round) and no sequence at more than kMaxQuantSplits chunks.
 inline Plan make_plan(const Seq* s, int B, int H, int G, int target_items) {
   Plan p;
   long long groups = 0;
@@ -92,10 +92,17 @@ inline Plan make_plan(const Seq* s, int B, int H, int G, int target_items) {
     groups += g;
     if (g > max_groups) max_groups = g;
   }
+  if (target_items < 1) target_items = 1;
   long long want = (groups * H + target_items - 1) / target_items;
   int lo = (max_groups + kMaxQuantSplits - 1) / kMaxQuantSplits;
   long long cg = want > lo ? want : lo;
   if (cg < 1) cg = 1;
+  auto items = [&](long long c) {
+    long long n = 0;
+    for (int b = 0; b < B; ++b) n += (long long)H * ((s[b].nq / G + c - 1) / c);
+    return n;
+  };
+  while (cg < max_groups && items(cg) > target_items) ++cg;
   p.chunk_groups = (int32_t)cg;
   for (int b = 0; b < B; ++b) {
     int g = s[b].nq / G;

@@ -139,8 +139,12 @@ def test_plan_covers_every_group(driver):
             total += qi
         groups = sum(L // G for L in lens)
         if groups:
-            # as many items as the target allows, never fewer than needed to cap the splits
-            assert cg == max(1, -(-groups * H // target), -(-max(L // G for L in lens) // 256))
+            # the smallest chunk that fits the target (and caps the splits at 256 per sequence)
+            maxg = max(L // G for L in lens)
+            fits = lambda c: sum(H * -(-(L // G) // c) for L in lens) <= target
+            lo = max(1, -(-groups * H // target), -(-maxg // 256))
+            assert cg >= lo and (fits(cg) or cg >= maxg)
+            assert cg == lo or not fits(cg - 1)
 
 
 def test_layout_sections(driver):

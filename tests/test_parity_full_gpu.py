@@ -1,0 +1,155 @@
+"""GPU parity at the full sizes of the workloads (the launch configurations the benchmark times),
+checked on sampled heads / layers that the CPU oracle can afford.
+
+  * LWM-128k-shaped layer: 32 heads x 128, 131072 prefilled tokens, gamma = 6 round.
+  * Llama-2-7B-32K-shaped stack: 32 layers, 32768 tokens, 64 rounds of gamma = 4 with
+    Bernoulli(0.9) acceptance driving rollback and flush; outputs checked every 8th round on
+    three layers, final planes of every layer checked bit-exact against the oracle's replay.
+  * Batched stress: 8 sequences with ragged lengths in [16384, 32768], Student-t(3) keys,
+    gamma = 4 with per-sequence acceptance until each sequence has 512 generated tokens.
+
+Inputs are generated on the GPU (torch's seeded generator) and the sampled heads are copied to
+the host for the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hierarchical_quantized_kv_amd import synth
+from lockstep import Lockstep, log
+
+pytestmark = pytest.mark.gpu
+G = 128
+
+
+def setup_module(_):
+    oracle.build(force=False)
+    assert torch.cuda.is_available()
+
+
+def dev_kv(config, layer, B, n, H, D, dist="normal", outliers=None, salt=0):
+    return synth.kv_device(torch, B, n, H, D, synth.seed_for(config, layer, "k") + 7 * salt,
+                           synth.seed_for(config, layer, "v") + 7 * salt, "cuda", dist_k=dist,
+                           outliers=outliers)
+
+
+def dev_q(shape, gen, D):
+    return (torch.randn(shape, generator=gen, device="cuda") / math.sqrt(D)).to(torch.float16)
+
+
+def prefill(ls, layer, k, v, lens=None):
+    n = k.shape[1]
+    pos = 0
+    while pos < n:
+        kk, vv = k[:, pos:pos + G].contiguous(), v[:, pos:pos + G].contiguous()
+        cnt = None if lens is None else [max(0, min(G, L - pos)) for L in lens]
+        ls.append(layer, kk, vv, cnt)
+        ls.flush(layer)
+        pos += G
+
+
+def test_lwm_128k_layer():
+    log("case: LWM-128k layer, heads 0/13/31 sampled")
+    H, D, ctx, gamma = 32, 128, 131072, 6
+    ls = Lockstep(1, 1, H, D, ctx + 4 * G, gamma, heads=[0, 13, 31], tag="128k")
+    out = synth.outlier_channels(H, D, synth.seed_for(4, 0, "outlier"))
+    k, v = dev_kv(4, 0, 1, ctx + 64, H, D, outliers=out)
+    prefill(ls, 0, k[:, :ctx], v[:, :ctx])
+    ls.append(0, k[:, ctx:].contiguous(), v[:, ctx:].contiguous())
+    del k, v
+    gen = torch.Generator(device="cuda").manual_seed(4000)
+    for s in range(gamma):
+        dk, dv = dev_kv(4, 0, 1, 1, H, D, outliers=out, salt=s + 1)
+        ls.append(0, dk, dv)
+        ls.draft(0, dev_q((1, H, D), gen, D))
+    ls.rollback(0, [gamma])
+    tk, tv = dev_kv(4, 0, 1, gamma + 1, H, D, outliers=out, salt=100)
+    ls.append(0, tk, tv)
+    ls.verify(0, dev_q((1, gamma + 1, H, D), gen, D))
+    ls.rollback(0, [3])
+    ls.flush(0)
+    ls.check_planes(0)
+    log(f"128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
+def test_llama_32k_full_stack_64_rounds():
+    L, H, D, ctx, gamma = 32, 32, 128, 32768, 4
+    log("case: 32k full stack, 64 rounds")
+    check_layers = [0, 17, 31]
+    ls = Lockstep(L, 1, H, D, ctx + 4 * G, gamma, heads=[0, 31], tag="32k")
+    outs = [synth.outlier_channels(H, D, synth.seed_for(3, l, "outlier")) for l in range(L)]
+    for l in range(L):
+        k, v = dev_kv(3, l, 1, ctx + 64, H, D, outliers=outs[l])
+        prefill(ls, l, k, v)
+    torch.cuda.synchronize()
+    log("32k: prefill done")
+    rng = np.random.Generator(np.random.PCG64(synth.seed_for(3, 0, "accept")))
+    gen = torch.Generator(device="cuda").manual_seed(3000)
+    for rnd in range(64):
+        check = rnd % 8 == 7
+        for s in range(gamma):
+            for l in range(L):
+                dk, dv = dev_kv(3, l, 1, 1, H, D, outliers=outs[l], salt=1000 + 10 * rnd + s)
+                ls.append(l, dk, dv)
+                q = dev_q((1, H, D), gen, D)
+                if check and l in check_layers:
+                    ls.draft(l, q)
+                else:
+                    ls.gpu.attend_draft(l, q)
+        a = synth.acceptance(rng, gamma)
+        for l in range(L):
+            ls.rollback(l, [gamma])
+            tk, tv = dev_kv(3, l, 1, gamma + 1, H, D, outliers=outs[l], salt=5000 + rnd)
+            ls.append(l, tk, tv)
+            q = dev_q((1, gamma + 1, H, D), gen, D)
+            if check and l in check_layers:
+                ls.verify(l, q)
+            else:
+                ls.gpu.attend_verify(l, q)
+            ls.rollback(l, [gamma - a])
+        ls.flush(-1)
+        if check:
+            log(f"32k: round {rnd} checked, max abs {ls.max_abs:.3e}")
+    for l in range(L):
+        ls.check_planes(l)
+    log(f"32k: planes of all {L} layers bit-exact; max abs {ls.max_abs:.3e} rel {ls.max_rel:.3e}")
+
+
+def test_batched_ragged_student_t():
+    B, H, D, gamma = 8, 32, 128, 4
+    log("case: batched ragged stress")
+    lens = [int(x) for x in synth.ragged_lengths(B, 16384, 32768, synth.seed_for(5, 0, "len"))]
+    ls = Lockstep(1, B, H, D, 32768 + 8 * G, gamma, heads=[0, 31], tag="batch8")
+    k, v = dev_kv(5, 0, B, max(lens), H, D, dist="student_t3")
+    prefill(ls, 0, k, v, lens)
+    del k, v
+    nq, nt, _ = ls.check_state(0)
+    log(f"batch8: prefilled {list(nq + nt)}")
+    rng = np.random.Generator(np.random.PCG64(synth.seed_for(5, 0, "accept")))
+    gen = torch.Generator(device="cuda").manual_seed(5000)
+    generated = np.zeros(B, dtype=np.int64)
+    rnd = 0
+    while generated.min() < 512:
+        check = rnd % 16 == 0
+        for s in range(gamma):
+            dk, dv = dev_kv(5, 0, B, 1, H, D, dist="student_t3", salt=1000 + 10 * rnd + s)
+            ls.append(0, dk, dv)
+            q = dev_q((B, H, D), gen, D)
+            ls.draft(0, q) if check else ls.gpu.attend_draft(0, q)
+        ls.rollback(0, [gamma] * B)
+        tk, tv = dev_kv(5, 0, B, gamma + 1, H, D, dist="student_t3", salt=9000 + rnd)
+        ls.append(0, tk, tv)
+        q = dev_q((B, gamma + 1, H, D), gen, D)
+        ls.verify(0, q) if check else ls.gpu.attend_verify(0, q)
+        acc = np.array([synth.acceptance(rng, gamma) for _ in range(B)])
+        ls.rollback(0, list(gamma - acc))
+        generated += acc + 1
+        ls.flush(0)
+        rnd += 1
+    ls.check_planes(0)
+    q = dev_q((B, H, D), gen, D)
+    ls.draft(0, q)
+    log(f"batch8: {rnd} rounds, max abs {ls.max_abs:.3e} rel {ls.max_rel:.3e}")
