@@ -6,16 +6,23 @@ channels scaled x8.  One step is one speculation round over all layers:
   gamma = 6 draft steps (per layer: append 1 token, draft attention),
   per layer: rollback gamma, append gamma+1 target tokens, verify attention (7 queries),
   acceptance a ~ Bernoulli(0.9) until first reject, rollback gamma - a, then one flush call.
-Inputs are seeded synthetic fp16 tensors resident in HBM before timing starts.
+Inputs are seeded synthetic fp16 tensors resident in HBM before timing starts.  After the timed
+steps, a bulk flush (one G-token half of every layer and head in one launch) is timed on its own.
 
-Prints one JSON line: value = algorithmic HBM bytes of the step / step time (GB/s).
+Prints one JSON line: value = algorithmic HBM bytes of the step / step time (GB/s), with the
+roofline of the draft kernel (and of verify and flush), and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -27,6 +34,12 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attention µs/step and HBM GB/s (draft & verify) at 32k/128k ctx"
 PEAK_HBM_GBS = 8000.0
 G = 128
+KERNEL_SRC = os.path.join(ROOT, "hierarchical_quantized_kv_amd", "csrc", "qs_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+# HBM byte counters of rocprofv3, scaled by what they read for a plain device copy of known size
+# (FETCH_SIZE counts half of the bytes a copy kernel reads; WRITE_SIZE counts them all).
+KERNELS = {"draft": "attn_kernel<128, true>", "verify": "attn_kernel<128, false>",
+           "combine": "combine_kernel<128>", "flush": "flush_kernel<128>"}
 
 CONFIGS = {
     3: dict(name="Llama-2-7B-32K-shaped full stack", layers=32, heads=32, D=128, ctx=32768,
@@ -65,11 +78,20 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=sorted(CONFIGS))
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="heads of layer 0 in the CPU-oracle sample")
+    ap.add_argument("--flush-reps", type=int, default=4,
+                    help="timed all-layer flushes (each quantizes one G-token half per head)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this size first (reference "
                          "kernel for scaling HBM byte counters)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM-traffic profile from two rocprofv3 --pmc output folders "
+                         "(FETCH_SIZE, WRITE_SIZE) of this script and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        write_traffic_summary(*args.traffic_summary, args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(got --gpus {args.gpus})", file=sys.stderr)
@@ -185,19 +207,46 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     total_bytes = sum(step_bytes)
     value = total_bytes / elapsed / 1e9
+    print(f"bench: {args.steps} timed steps in {elapsed:.3f}s", file=sys.stderr, flush=True)
 
-    def summarize(kind):
-        t = [a.elapsed_time(b) * 1e3 for a, b, _ in ev[kind]]   # us
-        by = [n for _, _, n in ev[kind]]
+    # Bulk flush (outside the timed steps): every layer gets G more tail tokens, then one
+    # qs_flush(-1) quantizes one G-token half of every (layer, head) in a single launch.
+    fk, fv = rnd(1, G, H, D), rnd(1, G, H, D)
+    fl_ev = []
+    for _ in range(args.flush_reps):
+        for layer in range(L):
+            cache.append(layer, fk, fv)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flushed = cache.flush(-1)
+        e1.record(stream)
+        assert int(flushed[0]) == 1
+        fl_ev.append((e0, e1, L * flush_bytes(H, D)))
+    torch.cuda.synchronize()
+
+    def summarize(events):
+        t = [a.elapsed_time(b) * 1e3 for a, b, _ in events]   # us
+        by = [n for _, _, n in events]
         mean_us = float(np.mean(t))
         return mean_us, float(np.mean(by)) / (mean_us * 1e-6) / 1e9, float(np.mean(by))
 
-    d_us, d_gbs, d_bytes = summarize("draft")
-    v_us, v_gbs, v_bytes = summarize("verify")
+    d_us, d_gbs, d_bytes = summarize(ev["draft"])
+    v_us, v_gbs, v_bytes = summarize(ev["verify"])
+    f_us, f_gbs, f_bytes = summarize(fl_ev)
 
     cpu = None
     if cpu_inputs is not None:
         cpu = cpu_baseline(cpu_inputs, ctx, D, gamma, args.cpu_heads)
+
+    traffic = load_traffic(args.config)
+
+    def roof(kind, gbs, nbytes, us, kernel, launches=1):
+        t = traffic.get(kind) if traffic else None
+        return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "traffic": None if t is None else int(round(t * launches)),
+                "bytes_per_launch": int(nbytes), "avg_launch_us": round(us, 2)}
 
     line = {
         "metric": METRIC,
@@ -221,21 +270,132 @@ def main():
         "draft_gbs": round(d_gbs, 1),
         "verify_us_per_layer": round(v_us, 2),
         "verify_gbs": round(v_gbs, 1),
-        "roofline": {"bound": "hbm", "kernel": "draft attention (attn_kernel<128, draft> + combine)",
-                     "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "bytes_per_launch": int(d_bytes), "avg_launch_us": round(d_us, 2)},
-        "roofline_verify": {"bound": "hbm", "achieved": round(v_gbs, 1), "peak": PEAK_HBM_GBS,
-                            "unit": "GB/s", "frac": round(v_gbs / PEAK_HBM_GBS, 4),
-                            "bytes_per_launch": int(v_bytes), "avg_launch_us": round(v_us, 2)},
+        "flush_us_all_layers": round(f_us, 2),
+        "flush_gbs": round(f_gbs, 1),
+        "roofline": roof("draft", d_gbs, d_bytes, d_us,
+                         "draft call: attn_kernel<128, draft> + combine_kernel<128>"),
+        "roofline_verify": roof("verify", v_gbs, v_bytes, v_us,
+                                "attn_kernel<128, verify> + combine_kernel<128>"),
+        "roofline_flush": roof("flush", f_gbs, f_bytes, f_us,
+                               f"flush_kernel<128>, {L} layers x {H} heads in one launch",
+                               launches=L * H),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_profile_path(config):
+    return os.path.join(PROFILES, f"hbm_traffic_{'lwm128k' if config == 4 else 'llama32k'}.md")
+
+
+def load_traffic(config):
+    """HBM bytes per launch measured by the counter profile of this workload, or None when the
+    kernels have changed since the counters were taken."""
+    path = traffic_profile_path(config)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256: ([0-9a-f]{64})", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    out = {}
+    for kind in ("draft", "verify", "flush"):
+        mm = re.search(rf"traffic_{kind}_bytes: (\d+)", text)
+        if mm:
+            out[kind] = int(mm.group(1))
+    return out
+
+
+def _counter_rows(folder):
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {folder}, found {files}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def write_traffic_summary(fetch_dir, write_dir, args):
+    """Per-launch HBM traffic of the hot kernels from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by the ratio of the known byte count of the calibration copy to what the counter
+    read for it.  The flush launch is normalised per (layer, head) half it quantizes."""
+    copy_kib = args.calibration_copy_mib * 1024
+    if copy_kib <= 0:
+        raise SystemExit("--traffic-summary needs --calibration-copy-mib (the size the runs used)")
+    res = {}
+    for cname, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(folder) if r["Counter_Name"] == cname]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit(f"{cname}: no calibration copy dispatch in {folder}")
+        factor = copy_kib / max(copies)
+        per = {}
+        for kind, kname in KERNELS.items():
+            sel = [r for r in rows if kname in r["Kernel_Name"].replace("qs::", "")]
+            if not sel:
+                continue
+            vals = [float(r["Counter_Value"]) * factor * 1024 for r in sel]
+            if kind == "flush":   # one unit = one (layer, head) half: 8 one-wave blocks at D=128
+                units = [int(r["Grid_Size"]) // (64 * (128 // 32 + G // 32)) for r in sel]
+                per[kind] = (sum(vals) / sum(units), len(sel))
+            else:
+                per[kind] = (sum(vals) / len(vals), len(sel))
+        res[cname] = (factor, max(copies), per)
+    fetch, write = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    lines = [
+        f"# HBM traffic per launch: {CONFIGS[args.config]['name']} "
+        f"(32 heads x head_dim 128, ctx {CONFIGS[args.config]['ctx']})",
+        "",
+        "Made by (on the GPU, from the repository root; `cd /tmp && export TMPDIR=/tmp` style "
+        "temp setup aside):",
+        "",
+        "```",
+        f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
+        f"\"attn_kernel|combine_kernel|flush_kernel|copy\" -d {fetch_dir} -o run "
+        f"--output-format csv -- python -u bench.py --config {args.config} --layers 2 --steps 1 "
+        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --calibration-copy-mib "
+        f"{args.calibration_copy_mib}",
+        f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE (same arguments, -d {write_dir})",
+        f"python bench.py --config {args.config} --calibration-copy-mib "
+        f"{args.calibration_copy_mib} --traffic-summary {fetch_dir} {write_dir}",
+        "```",
+        "",
+        f"Calibration: one device-to-device copy of {args.calibration_copy_mib} MiB "
+        f"(`__amd_rocclr_copyBuffer`) reads and writes {copy_kib} KiB.  The counters read "
+        f"FETCH_SIZE {fetch[1]:.0f} KiB (factor {fetch[0]:.4f}) and WRITE_SIZE {write[1]:.0f} KiB "
+        f"(factor {write[0]:.4f}) for it; every kernel's counts below are scaled by these factors.",
+        "",
+        "| kernel | dispatches | read bytes | written bytes | total bytes |",
+        "|---|---|---|---|---|",
+    ]
+    out = {}
+    for kind in ("draft", "verify", "combine", "flush"):
+        if kind not in fetch[2] or kind not in write[2]:
+            continue
+        rd, n = fetch[2][kind]
+        wr, _ = write[2][kind]
+        unit = " per (layer, head) half" if kind == "flush" else ""
+        lines.append(f"| {KERNELS[kind]}{unit} | {n} | {rd:.0f} | {wr:.0f} | {rd + wr:.0f} |")
+        out[kind] = rd + wr
+    lines += ["", "Machine-read by bench.py (the figures go null once the kernel source changes):",
+              "", "```", f"kernel_source_sha256: {kernel_source_hash()}"]
+    for kind, v in out.items():
+        lines.append(f"traffic_{kind}_bytes: {int(round(v))}")
+    lines += ["```", ""]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = traffic_profile_path(args.config)
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(path)
+
+
 def cpu_baseline(inputs, ctx, D, gamma, n_heads):
     """The CPU oracle, as it is, on a bounded sample of the same workload: layer 0 restricted to
-    the first n_heads heads; one draft call and one verify call timed (single thread)."""
+    its first n_heads heads, one speculation round (gamma draft calls, each after appending one
+    token, then rollback, gamma+1 appended tokens and one verify call) timed on one thread."""
     import oracle
     from oracle import OracleCache
     from hierarchical_quantized_kv_amd import synth
@@ -247,23 +407,28 @@ def cpu_baseline(inputs, ctx, D, gamma, n_heads):
     for pos in range(0, ctx, G):
         c.append(0, k[:, pos:pos + G], v[:, pos:pos + G])
         c.flush(0)
-    c.append(0, k[:, ctx:ctx + 64], v[:, ctx:ctx + 64])
-    q = synth.queries_host(1, None, H, D, 1)
-    t0 = time.perf_counter()
-    c.attend_draft(0, q)
-    t_d = time.perf_counter() - t0
+    c.append(0, k[:, ctx:ctx + 64 - gamma - 1], v[:, ctx:ctx + 64 - gamma - 1])
+    nt = 64 - gamma - 1
     m = gamma + 1
-    c.append(0, k[:, ctx + 64 - m:ctx + 64], v[:, ctx + 64 - m:ctx + 64])
-    qv = synth.queries_host(1, m, H, D, 2)
+    nb = 0
     t0 = time.perf_counter()
-    c.attend_verify(0, qv)
-    t_v = time.perf_counter() - t0
-    nb = draft_bytes(ctx, 64, H, D) + verify_bytes(ctx, 64 + m, H, D, m)
+    for j in range(gamma):
+        c.append(0, k[:, ctx + nt:ctx + nt + 1], v[:, ctx + nt:ctx + nt + 1])
+        c.attend_draft(0, synth.queries_host(1, None, H, D, 10 + j))
+        nb += draft_bytes(ctx, nt + 1, H, D)
+    t_d = time.perf_counter() - t0
+    c.rollback(0, [gamma])
+    c.append(0, k[:, ctx + nt:ctx + nt + m], v[:, ctx + nt:ctx + nt + m])
+    t1 = time.perf_counter()
+    c.attend_verify(0, synth.queries_host(1, m, H, D, 2))
+    t_v = time.perf_counter() - t1
+    nb += verify_bytes(ctx, nt + m, H, D, m)
     return {"value": round(nb / (t_d + t_v) / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"layer 0, heads 0..{H - 1} of the same workload: one draft call "
-                      f"({t_d:.2f}s) and one {m}-query verify call ({t_v:.2f}s) at ctx {ctx}, "
-                      f"single-threaded fp64 oracle; GB/s = algorithmic bytes of those calls / time"}
+            "sample": f"layer 0, heads 0..{H - 1} of the same workload at ctx {ctx}: one "
+                      f"speculation round = {gamma} draft calls ({t_d:.2f}s) + one {m}-query "
+                      f"verify call ({t_v:.2f}s), single-threaded fp64 oracle; GB/s = "
+                      f"algorithmic bytes of those calls / their time"}
 
 
 if __name__ == "__main__":

@@ -3,7 +3,8 @@
 // Kernels (one wave64 per work item unless noted):
 //   append_kernel   fp16 rows -> tail ring slots
 //   flush_kernel    oldest G-token ring half -> per-group asymmetric 8-bit codes, split into the
-//                   upper / lower nibble planes, plus (scale, zero-point) metadata (256 threads)
+//                   upper / lower nibble planes, plus (scale, zero-point) metadata; one wave per
+//                   32-channel key slice or 32-token value slice
 //   attn_kernel     split-K attention work items of one pass:
 //                     draft quantized item : upper key / value planes only, VALU (v_dot2)
 //                     verify quantized item: both planes, MFMA 16x16x32 f16
@@ -786,7 +787,7 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
 // ------------------------------------------------------------------------------------------
 
 struct TailLds {
-  uint32_t q[QS_MAX_QUERIES][64];    // fp16 pairs of the queries (D/2 words used)
+  uint32_t q[QS_MAX_QUERIES][64];    // fp16 pairs of the m queries, packed: query i at word i*D/2
   float p[kTailChunk][QS_MAX_QUERIES];
 };
 
@@ -797,26 +798,55 @@ __device__ void tail_item(const AttnArgs& a, int b, int h, int chunk, int split,
   const int nt = a.nt[b];
   const int ring = 2 * kGroup;
   const size_t bh = (size_t)b * a.H + h;
-  const int t = chunk * kTailChunk + lane;   // logical tail position of this lane's key
+  const int t0 = chunk * kTailChunk;
+  const int t = t0 + lane;                   // logical tail position of this lane's key
   const bool valid = t < nt;
-  const int slot = (a.head[b] + t) % ring;
+  const int nvalid = min(kTailChunk, nt - t0);
+  // head and t0 are multiples of 64, so the chunk's ring slots s0 .. s0 + 63 never wrap
+  const int s0 = (a.head[b] + t0) % ring;
+  const uint16_t* kchunk = a.tail_k + (bh * ring + s0) * D;
+  const uint16_t* vchunk = a.tail_v + (bh * ring + s0) * D;
 
-  for (int i = 0; i < m; ++i)
-    for (int w = lane; w < D / 2; w += 64)
-      L.q[i][w] = reinterpret_cast<const uint32_t*>(a.q + (((size_t)b * m + i) * a.H + h) * D)[w];
+  // Every load of the item is issued before the first use: the m queries (m * D/2 words, in
+  // lane-strided order), this lane's key row, and the D/64 value channels of every token of the
+  // chunk; slots past the nt valid tokens are read (they lie inside the ring) and zeroed.
+  constexpr int QW = QS_MAX_QUERIES * (D / 2) / 64;  // query words per lane, at most
+  const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q);
+  uint32_t qw[QW];
+#pragma unroll
+  for (int k = 0; k < QW; ++k) {
+    const int w = lane + 64 * k;            // word w of the m x D/2 query block
+    const int i = w / (D / 2), c = w % (D / 2);
+    qw[k] = i < m ? qsrc[(((size_t)b * m + i) * a.H + h) * (D / 2) + c] : 0u;
+  }
   uint32_t kr[D / 2];
-  const uint16_t* krow = a.tail_k + (bh * ring + (valid ? slot : 0)) * D;
 #pragma unroll
   for (int c = 0; c < D / 2; c += 4) {
-    const uint4 w = valid ? ld16(krow + 2 * c) : make_uint4(0, 0, 0, 0);
-    kr[c] = w.x; kr[c + 1] = w.y; kr[c + 2] = w.z; kr[c + 3] = w.w;
+    const uint4 w = ld16(kchunk + (size_t)lane * D + 2 * c);
+    kr[c] = valid ? w.x : 0u;
+    kr[c + 1] = valid ? w.y : 0u;
+    kr[c + 2] = valid ? w.z : 0u;
+    kr[c + 3] = valid ? w.w : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < QW; ++k) (&L.q[0][0])[lane + 64 * k] = qw[k];
+  constexpr int CPL = D / 64;  // value channels per lane: lane*CPL ..
+  uint32_t vw[kTailChunk];
+#pragma unroll
+  for (int tt = 0; tt < kTailChunk; ++tt) {
+    uint32_t w;
+    if constexpr (CPL == 2)
+      w = reinterpret_cast<const uint32_t*>(vchunk + tt * D)[lane];
+    else
+      w = vchunk[tt * D + lane];
+    vw[tt] = tt < nvalid ? w : 0u;
   }
   __syncthreads();
 
   for (int i = 0; i < m; ++i) {
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 2; ++c) s = dot2(as_h2(kr[c]), as_h2(L.q[i][c]), s);
+    for (int c = 0; c < D / 2; ++c) s = dot2(as_h2(kr[c]), as_h2(L.q[0][i * (D / 2) + c]), s);
     s *= a.qscale;
     const bool vis = valid && t <= nt - m + i;
     if (!vis) s = -INFINITY;
@@ -832,41 +862,24 @@ __device__ void tail_item(const AttnArgs& a, int b, int h, int chunk, int split,
   }
   __syncthreads();
 
-  // o_i[d] = sum_t p_i[t] v_t[d]; lane owns channels lane*(D/64) ..
-  constexpr int CPL = D / 64;
-  float acc[QS_MAX_QUERIES][CPL];
+  // o_i[d] = sum_t p_i[t] v_t[d]; lane owns channels lane*CPL ..
+  for (int i = 0; i < m; ++i) {
+    float acc[CPL];
 #pragma unroll
-  for (int i = 0; i < QS_MAX_QUERIES; ++i)
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[i][c] = 0.f;
-  const int nvalid = min(kTailChunk, nt - chunk * kTailChunk);
-  for (int tt = 0; tt < nvalid; ++tt) {
-    const int sl = (a.head[b] + chunk * kTailChunk + tt) % ring;
-    const uint16_t* vrow = a.tail_v + (bh * ring + sl) * D;
-    float v[CPL];
-    if constexpr (CPL == 2) {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(vrow)[lane];
-      v[0] = lo_h(w);
-      v[1] = hi_h(w);
-    } else {
-      v[0] = (float)__builtin_bit_cast(f16, vrow[lane]);
-    }
-#pragma unroll
-    for (int i = 0; i < QS_MAX_QUERIES; ++i) {
-      if (i < m) {
-        const float p = L.p[tt][i];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[i][c] += p * v[c];
+    for (int tt = 0; tt < kTailChunk; ++tt) {
+      const float p = L.p[tt][i];
+      if constexpr (CPL == 2) {
+        acc[0] = fmaf(p, lo_h(vw[tt]), acc[0]);
+        acc[1] = fmaf(p, hi_h(vw[tt]), acc[1]);
+      } else {
+        acc[0] = fmaf(p, (float)__builtin_bit_cast(f16, (uint16_t)vw[tt]), acc[0]);
       }
     }
-  }
+    float* rec = record(a, D, b, h, split, i);
 #pragma unroll
-  for (int i = 0; i < QS_MAX_QUERIES; ++i) {
-    if (i < m) {
-      float* rec = record(a, D, b, h, split, i);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) rec[kRecPad + CPL * lane + c] = acc[i][c];
-    }
+    for (int c = 0; c < CPL; ++c) rec[kRecPad + CPL * lane + c] = acc[c];
   }
 }
 
@@ -1024,127 +1037,160 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float z) {
   return (uint32_t)q;
 }
 
+// One wave per block.  The flush of one (layer, sequence, head) is split into independent
+// blocks: D/32 key blocks of 32 channels x G tokens and G/32 value blocks of 32 tokens x D
+// channels, each reading 8 KB of fp16 and writing its slice of both planes and its metadata.
+constexpr int kFlushSlice = 32;
+
+struct FlushKeyLds {
+  uint32_t tile[kGroup][kFlushSlice / 2 + 1];  // fp16 pairs, token-major (padded rows)
+  float sz[kFlushSlice][2];
+};
+struct FlushValLds {
+  uint8_t code[kFlushSlice][128 + 4];          // codes, token-major (padded rows)
+};
+
+// Key block: channels c0 .. c0+31 of the G tokens of ring half `head`.
 template <int D>
-__global__ __launch_bounds__(256) void flush_kernel(const FlushArgs a) {
+__device__ void flush_keys(const FlushArgs& a, size_t lbh, int grp, int head, int c0,
+                           FlushKeyLds& L) {
 #pragma clang fp contract(off)
   constexpr int G = kGroup;
-  constexpr int RS = D + 2;                 // padded fp16 row stride of the staged tile
-  __shared__ f16 tile[G * RS];
-  __shared__ uint8_t code[G * D];
-  __shared__ float red[2][8][D];
-  __shared__ float sz[2][D > G ? D : G];
+  const int lane = threadIdx.x;
+  const uint16_t* src = a.tail_k + (lbh * (2 * G) + head) * D + c0;
+  // lane holds tokens 2 lane, 2 lane + 1: 32 channels each
+  uint32_t w[2][kFlushSlice / 2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int k = 0; k < kFlushSlice / 8; ++k) {
+      const uint4 v = ld16(src + (size_t)(2 * lane + r) * D + 8 * k);
+      w[r][4 * k] = v.x; w[r][4 * k + 1] = v.y; w[r][4 * k + 2] = v.z; w[r][4 * k + 3] = v.w;
+    }
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int k = 0; k < kFlushSlice / 2; ++k) L.tile[2 * lane + r][k] = w[r][k];
+  __syncthreads();
+  {  // min / max of channel pair cp over the tokens q, q + 4, .. (quarter q), then the quarters
+    const int cp = lane & 15, q = lane >> 4;
+    float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+    for (int t = q; t < G; t += 4) {
+      const uint32_t x = L.tile[t][cp];
+      const float x0 = lo_h(x), x1 = hi_h(x);
+      mn0 = fminf(mn0, x0); mx0 = fmaxf(mx0, x0);
+      mn1 = fminf(mn1, x1); mx1 = fmaxf(mx1, x1);
+    }
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      mn0 = fminf(mn0, __shfl_xor(mn0, o)); mx0 = fmaxf(mx0, __shfl_xor(mx0, o));
+      mn1 = fminf(mn1, __shfl_xor(mn1, o)); mx1 = fmaxf(mx1, __shfl_xor(mx1, o));
+    }
+    if (q == 0) {
+      const float s0 = quant_scale(mn0, mx0), s1 = quant_scale(mn1, mx1);
+      const float z0 = rintf(-mn0 / s0), z1 = rintf(-mn1 / s1);
+      L.sz[2 * cp][0] = s0; L.sz[2 * cp][1] = z0;
+      L.sz[2 * cp + 1][0] = s1; L.sz[2 * cp + 1][1] = z1;
+      float* km = a.kmeta + ((lbh * a.NG + grp) * D + c0 + 2 * cp) * 2;
+      *reinterpret_cast<float4*>(km) = make_float4(s0, z0, s1, z1);
+    }
+  }
+  __syncthreads();
+  // codes of this lane's two tokens; key plane rows are token-major, byte j of the slice holds
+  // channel c0 + 2j in bits 0-3 and c0 + 2j + 1 in bits 4-7
+  uint8_t* uk = a.uk + (lbh * a.T + (size_t)grp * G) * (D / 2) + c0 / 2;
+  uint8_t* lk = a.lk + (lbh * a.T + (size_t)grp * G) * (D / 2) + c0 / 2;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    uint32_t u[4] = {0, 0, 0, 0}, l[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kFlushSlice / 2; ++k) {
+      const int ch = 2 * k;
+      const uint32_t c_lo = quant_code(lo_h(w[r][k]), L.sz[ch][0], L.sz[ch][1]);
+      const uint32_t c_hi = quant_code(hi_h(w[r][k]), L.sz[ch + 1][0], L.sz[ch + 1][1]);
+      const int sh = 8 * (k & 3);
+      u[k >> 2] |= ((c_lo >> 4) | ((c_hi >> 4) << 4)) << sh;
+      l[k >> 2] |= ((c_lo & 15u) | ((c_hi & 15u) << 4)) << sh;
+    }
+    const size_t o = (size_t)(2 * lane + r) * (D / 2);
+    *reinterpret_cast<uint4*>(uk + o) = make_uint4(u[0], u[1], u[2], u[3]);
+    *reinterpret_cast<uint4*>(lk + o) = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int h = blockIdx.x;
+// Value block: tokens t0 .. t0+31 of ring half `head`, all D channels.
+template <int D>
+__device__ void flush_values(const FlushArgs& a, size_t lbh, int grp, int head, int t0,
+                             FlushValLds& L) {
+#pragma clang fp contract(off)
+  constexpr int G = kGroup, HALF = D / 2;
+  const int lane = threadIdx.x;
+  const int tk = lane >> 1, hf = lane & 1;  // token t0 + tk, channels hf*D/2 ..
+  const uint16_t* src = a.tail_v + (lbh * (2 * G) + head + t0 + tk) * D + hf * HALF;
+  uint32_t w[HALF / 2];
+#pragma unroll
+  for (int k = 0; k < HALF / 8; ++k) {
+    const uint4 v = ld16(src + 8 * k);
+    w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+  }
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < HALF / 2; ++k) {
+    const float x0 = lo_h(w[k]), x1 = hi_h(w[k]);
+    mn = fminf(mn, fminf(x0, x1));
+    mx = fmaxf(mx, fmaxf(x0, x1));
+  }
+  mn = fminf(mn, __shfl_xor(mn, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  const float s = quant_scale(mn, mx);
+  const float z = rintf(-mn / s);
+  if (hf == 0) {
+    float* vm = a.vmeta + (lbh * a.T + (size_t)grp * G + t0 + tk) * 2;
+    *reinterpret_cast<float2*>(vm) = make_float2(s, z);
+  }
+#pragma unroll
+  for (int k = 0; k < HALF / 2; ++k) {
+    const uint32_t c_lo = quant_code(lo_h(w[k]), s, z), c_hi = quant_code(hi_h(w[k]), s, z);
+    *reinterpret_cast<uint16_t*>(&L.code[tk][hf * HALF + 2 * k]) = (uint16_t)(c_lo | (c_hi << 8));
+  }
+  __syncthreads();
+  // value planes: half e of the group, channel-major rows of G/4 bytes; byte j of a row holds
+  // token e*G/2 + 2j in bits 0-3 and e*G/2 + 2j + 1 in bits 4-7.  This block fills 16 bytes
+  // of the row of every channel.
+  const int e = t0 / (G / 2), tin = t0 % (G / 2);
+  uint8_t* uv = a.uv + ((lbh * a.NG + grp) * D) * (G / 2) + (size_t)e * (D * G / 4) + tin / 2;
+  uint8_t* lv = a.lv + ((lbh * a.NG + grp) * D) * (G / 2) + (size_t)e * (D * G / 4) + tin / 2;
+  for (int d = lane; d < D; d += 64) {
+    uint32_t u[4] = {0, 0, 0, 0}, l[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < kFlushSlice / 2; ++j) {
+      const uint32_t c_lo = L.code[2 * j][d], c_hi = L.code[2 * j + 1][d];
+      const int sh = 8 * (j & 3);
+      u[j >> 2] |= ((c_lo >> 4) | ((c_hi >> 4) << 4)) << sh;
+      l[j >> 2] |= ((c_lo & 15u) | ((c_hi & 15u) << 4)) << sh;
+    }
+    *reinterpret_cast<uint4*>(uv + (size_t)d * (G / 4)) = make_uint4(u[0], u[1], u[2], u[3]);
+    *reinterpret_cast<uint4*>(lv + (size_t)d * (G / 4)) = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+}
+
+// grid: x = head * (D/32 + G/32) + block, y = selected sequence, z = layer - layer0
+template <int D>
+__global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
+  constexpr int NK = D / kFlushSlice, NV = kGroup / kFlushSlice;
+  __shared__ union {
+    FlushKeyLds k;
+    FlushValLds v;
+  } lds;
+  const int h = blockIdx.x / (NK + NV);
+  const int blk = blockIdx.x % (NK + NV);
   const int sel = blockIdx.y;
   const int layer = a.layer0 + blockIdx.z;
-  const int b = a.b[sel];
-  const int grp = a.group[sel];
-  const int head = a.head[sel];
-  const size_t lbh = ((size_t)layer * a.B + b) * a.H + h;
-  const int ring = 2 * G;
-
-  for (int pass = 0; pass < 2; ++pass) {  // 0: keys, 1: values
-    const uint16_t* src = (pass == 0 ? a.tail_k : a.tail_v) + (lbh * ring + head) * D;
-    for (int c = tid; c < G * D / 8; c += 256) {  // G consecutive ring slots, 16 B per thread
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      const uint4 w = ld16(src + (size_t)r * D + col);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[r * RS + col]);
-      dst[0] = w.x; dst[1] = w.y; dst[2] = w.z; dst[3] = w.w;
-    }
-    __syncthreads();
-    if (pass == 0) {
-      // channel pair p = tid % (D/2); token slice r of NR slices
-      constexpr int NP = D / 2, NR = 256 / NP, TPR = G / NR;
-      const int p = tid % NP, r = tid / NP;
-      float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
-      for (int t = r * TPR; t < (r + 1) * TPR; ++t) {
-        const float x0 = (float)tile[t * RS + 2 * p], x1 = (float)tile[t * RS + 2 * p + 1];
-        mn0 = fminf(mn0, x0); mx0 = fmaxf(mx0, x0);
-        mn1 = fminf(mn1, x1); mx1 = fmaxf(mx1, x1);
-      }
-      red[0][r][2 * p] = mn0; red[0][r][2 * p + 1] = mn1;
-      red[1][r][2 * p] = mx0; red[1][r][2 * p + 1] = mx1;
-      __syncthreads();
-      if (tid < D) {
-        float mn = red[0][0][tid], mx = red[1][0][tid];
-        for (int k = 1; k < NR; ++k) { mn = fminf(mn, red[0][k][tid]); mx = fmaxf(mx, red[1][k][tid]); }
-        const float s = quant_scale(mn, mx);
-        const float z = rintf(-mn / s);
-        sz[0][tid] = s;
-        sz[1][tid] = z;
-        float* km = a.kmeta + ((lbh * a.NG + grp) * D + tid) * 2;
-        km[0] = s;
-        km[1] = z;
-      }
-      __syncthreads();
-      for (int e = tid; e < G * D; e += 256) {
-        const int t = e / D, d = e % D;
-        code[e] = (uint8_t)quant_code((float)tile[t * RS + d], sz[0][d], sz[1][d]);
-      }
-      __syncthreads();
-      // key planes: token-major rows, byte jb = channel 2jb (bits 0-3) | 2jb+1 (bits 4-7)
-      uint8_t* uk = a.uk + (lbh * a.T + (size_t)grp * G) * (D / 2);
-      uint8_t* lk = a.lk + (lbh * a.T + (size_t)grp * G) * (D / 2);
-      for (int c = tid; c < G * D / 32; c += 256) {  // 16 output bytes = 32 codes of one row
-        const int t = c / (D / 32), c0 = (c % (D / 32)) * 32;
-        uint32_t u[4], l[4];
-        for (int k = 0; k < 4; ++k) {
-          u[k] = 0; l[k] = 0;
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t cc = code[t * D + c0 + 8 * k + e];
-            u[k] |= (cc >> 4) << (4 * e);
-            l[k] |= (cc & 15u) << (4 * e);
-          }
-        }
-        const size_t o = (size_t)t * (D / 2) + c0 / 2;
-        *reinterpret_cast<uint4*>(uk + o) = make_uint4(u[0], u[1], u[2], u[3]);
-        *reinterpret_cast<uint4*>(lk + o) = make_uint4(l[0], l[1], l[2], l[3]);
-      }
-    } else {
-      // token t = tid / 2, half of its channels each
-      const int t = tid >> 1, hf = tid & 1;
-      float mn = INFINITY, mx = -INFINITY;
-      for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); ++d) {
-        const float x = (float)tile[t * RS + d];
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
-      }
-      mn = fminf(mn, __shfl_xor(mn, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      const float s = quant_scale(mn, mx);
-      const float z = rintf(-mn / s);
-      if (hf == 0) {
-        float* vm = a.vmeta + (lbh * a.T + (size_t)grp * G + t) * 2;
-        vm[0] = s;
-        vm[1] = z;
-      }
-      for (int d = hf * (D / 2); d < (hf + 1) * (D / 2); ++d)
-        code[t * D + d] = (uint8_t)quant_code((float)tile[t * RS + d], s, z);
-      __syncthreads();
-      // value planes: two halves of G/2 tokens, each channel-major with rows of G/4 bytes,
-      // byte jb of a row = token 2jb (bits 0-3) | 2jb+1 (bits 4-7) of the half
-      uint8_t* uv = a.uv + ((lbh * a.NG + grp) * D) * (G / 2);
-      uint8_t* lv = a.lv + ((lbh * a.NG + grp) * D) * (G / 2);
-      for (int c = tid; c < D * G / 32; c += 256) {  // 16 output bytes = 32 tokens of one channel
-        const int d = c / (G / 32), t0 = (c % (G / 32)) * 32;
-        const int half = t0 / (G / 2), tin = t0 % (G / 2);
-        uint32_t u[4], l[4];
-        for (int k = 0; k < 4; ++k) {
-          u[k] = 0; l[k] = 0;
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t cc = code[(t0 + 8 * k + e) * D + d];
-            u[k] |= (cc >> 4) << (4 * e);
-            l[k] |= (cc & 15u) << (4 * e);
-          }
-        }
-        const size_t o = (size_t)half * (D * G / 4) + (size_t)d * (G / 4) + tin / 2;
-        *reinterpret_cast<uint4*>(uv + o) = make_uint4(u[0], u[1], u[2], u[3]);
-        *reinterpret_cast<uint4*>(lv + o) = make_uint4(l[0], l[1], l[2], l[3]);
-      }
-    }
-    __syncthreads();
-  }
+  const size_t lbh = ((size_t)layer * a.B + a.b[sel]) * a.H + h;
+  if (blk < NK)
+    flush_keys<D>(a, lbh, a.group[sel], a.head[sel], blk * kFlushSlice, lds.k);
+  else
+    flush_values<D>(a, lbh, a.group[sel], a.head[sel], (blk - NK) * kFlushSlice, lds.v);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1162,9 +1208,10 @@ hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st) {
 }
 
 hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st) {
-  const dim3 grid(a.H, a.n_sel, n_layers);
-  if (D == 128) hipLaunchKernelGGL(flush_kernel<128>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(flush_kernel<64>, grid, dim3(256), 0, st, a);
+  const int per_head = D / kFlushSlice + kGroup / kFlushSlice;
+  const dim3 grid(a.H * per_head, a.n_sel, n_layers);
+  if (D == 128) hipLaunchKernelGGL(flush_kernel<128>, grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL(flush_kernel<64>, grid, dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
