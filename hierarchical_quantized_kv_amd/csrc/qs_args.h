@@ -31,14 +31,14 @@ struct AttnArgs {
   int32_t B, H, T, NG;   // batch, heads, token capacity, groups per sequence
   int32_t m;             // queries per (sequence, head)
   int32_t S;             // record slots per (sequence, head) = kMaxQuantSplits + kMaxTailItems
-  int32_t chunk_groups;  // quantized groups per quantized work item
+  int32_t chunk_groups;  // quantized groups per worker, at most (sizes the worker count)
   int32_t n_qitems_total, n_titems_total;
   float qscale;          // sm_scale * log2(e): scores are kept in the base-2 domain
   float draft_offset;    // 8 or 0 (draft only)
   int32_t nq[QS_MAX_BATCH];         // quantized tokens per sequence
   int32_t nt[QS_MAX_BATCH];         // tail tokens per sequence
   int32_t head[QS_MAX_BATCH];       // ring slot of logical tail token 0
-  int32_t qitem_base[QS_MAX_BATCH + 1];  // prefix sum over b of quantized items
+  int32_t qitem_base[QS_MAX_BATCH + 1];  // prefix sum over b of quantized workers
   int32_t titem_base[QS_MAX_BATCH + 1];  // prefix sum over b of tail items
 };
 

@@ -50,13 +50,6 @@ __device__ __forceinline__ uint32_t as_u32(f16x2 x) { return __builtin_bit_cast(
 __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
-// c + a.x b.x + a.y b.y (fp16 products, fp32 accumulate) kept in program order: the draft's
-// inner loops interleave each nibble unpack with its dot products so that only one word's
-// unpacked operands are live at a time.
-__device__ __forceinline__ float dot2_ord(uint32_t a, uint32_t b, float c) {
-  asm volatile("v_dot2c_f32_f16 %0, %1, %2" : "+v"(c) : "v"(a), "v"(b));
-  return c;
-}
 // One 32-bit word of the upper key plane (8 channels) against its weights q'/4, fp16 hi and lo:
 //   p += sum over the pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7) of (1024 + 64 U) . (w_hi + w_lo),
 // each nibble moved into the top mantissa bits 6-9 of an fp16 1024 (the offset then stays about
@@ -128,20 +121,10 @@ __device__ __forceinline__ float weight_scale(float smax) {
 // 2^x with the hardware instruction (results below 2^-126 flush to zero).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-// Streaming loads of data read once per call (planes, metadata): the non-temporal hint keeps
-// them from displacing cache lines and raises the achievable HBM read rate.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint4 ld16_nt(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint2 ld8_nt(const void* p) {
-  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(v.x, v.y);
-}
 // Buffer loads: a wave-uniform resource (base address and byte range in SGPRs) plus a per-lane
 // 32-bit offset, with the streaming (non-temporal) cache policy.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -177,11 +160,6 @@ __device__ __forceinline__ Streams make_streams(const AttnArgs& a, size_t bh, in
   return st;
 }
 
-__device__ __forceinline__ float4 ldf4_nt(const float* p) {
-  const uint4 v = ld16_nt(p);
-  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                     __uint_as_float(v.w));
-}
 __device__ __forceinline__ float lo_h(uint32_t x) { return (float)as_h2(x).x; }
 __device__ __forceinline__ float hi_h(uint32_t x) { return (float)as_h2(x).y; }
 
@@ -191,43 +169,10 @@ __device__ __forceinline__ float hi_h(uint32_t x) { return (float)as_h2(x).y; }
 __device__ __forceinline__ int pair_word(int t) { return (t >> 3) * 4 + ((t & 7) & 3); }
 __device__ __forceinline__ int pair_half(int t) { return (t & 7) >> 2; }
 
-// 1024 + nibble pairs of one plane word, see pair_word().
-struct Nib4 {
-  f16x2 a, b, c, d;  // (e0,e4): 1024+n  (e1,e5): 1024+16n  (e2,e6): 1024+n  (e3,e7): 1024+16n
-};
-__device__ __forceinline__ Nib4 unpack_nibbles(uint32_t w) {
-  Nib4 r;
-  const uint32_t w8 = w >> 8;
-  r.a = as_h2((w & 0x000F000Fu) | kMagic);
-  r.b = as_h2((w & 0x00F000F0u) | kMagic);
-  r.c = as_h2((w8 & 0x000F000Fu) | kMagic);
-  r.d = as_h2((w8 & 0x00F000F0u) | kMagic);
-  return r;
-}
-
-// 1024 + 16 * nibble for all 8 entries, pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7): placing every
-// nibble in mantissa bits 4-7 keeps the 1024 offset within a factor ~4 of the data.
-__device__ __forceinline__ Nib4 unpack_nibbles16(uint32_t w) {
-  Nib4 r;
-  r.a = as_h2(((w << 4) & 0x00F000F0u) | kMagic);
-  r.b = as_h2((w & 0x00F000F0u) | kMagic);
-  r.c = as_h2(((w >> 4) & 0x00F000F0u) | kMagic);
-  r.d = as_h2(((w >> 8) & 0x00F000F0u) | kMagic);
-  return r;
-}
-
 // fp16 hi + lo split of x: hi = fp16(x), lo = fp16(x - hi); hi + lo carries ~22 bits.
 __device__ __forceinline__ void split_f16(float x, f16& hi, f16& lo) {
   hi = (f16)x;
   lo = (f16)(x - (float)hi);
-}
-
-// (x & mask) | c as one v_and_or_b32, mask in an SGPR and c in a VGPR: the compiler does not
-// form it by itself because a gfx9 VOP3 instruction takes no literal and reads one SGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t c) {
-  uint32_t r;
-  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(c));
-  return r;
 }
 
 // 8-bit codes of 8 entries from an upper word u and lower word l (entry e in nibble e of each),
@@ -287,6 +232,34 @@ __device__ __forceinline__ float wave_sum_from(float x, int from) {
 // Record of split `split`, query `i` of (b, h).
 __device__ __forceinline__ float* record(const AttnArgs& a, int D, int b, int h, int split, int i) {
   return a.work + ((((size_t)b * a.H + h) * a.S + split) * a.m + i) * (size_t)(D + kRecPad);
+}
+
+// Group assignment of the quantized workers of (b, h): worker w of W takes groups w, w + W,
+// w + 2W, ...  At every step the W workers of a head read one contiguous run of W groups, so the
+// plane traffic of the whole call spreads evenly over the HBM channels (contiguous per-worker
+// chunks were measured to leave some waves twice as slow as others).
+struct GroupStride {
+  int first, step, ng;
+};
+__device__ __forceinline__ GroupStride worker_groups(const AttnArgs& a, int b, int item) {
+  return GroupStride{item, a.qitem_base[b + 1] - a.qitem_base[b], a.nq[b] / kGroup};
+}
+
+// The waves that share a SIMD issue oldest first, so with equal work the oldest finishes far
+// ahead of the youngest, and the SIMD spends the end of the call with a single wave and little
+// memory traffic in flight.  Each worker therefore sets its issue priority from the fraction of
+// its groups still to do (four levels): a worker that falls behind keeps precedence until the
+// others have caught up.
+__device__ __forceinline__ void pace(int remaining, int total) {
+  const int q = (4 * remaining + total - 1) / total;  // 1 .. 4
+  if (q >= 4)
+    __builtin_amdgcn_s_setprio(3);
+  else if (q == 3)
+    __builtin_amdgcn_s_setprio(2);
+  else if (q == 2)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -353,9 +326,11 @@ struct DraftAcc {
 
 // One group: scores of its 128 keys from the upper key plane, online-softmax update, and the
 // weighted sum of its upper value plane.
-// The registers of `cur` are refilled with group `gnext` (if >= 0) as soon as each part of the
+// With PF the registers of `cur` are refilled with group `gnext` as soon as each part of the
 // current group has been consumed, so the next group's loads overlap this group's arithmetic.
-template <int D>
+// (The prefetch is a template flag rather than a run-time test so that the number of loads in
+// flight at every wait is fixed.)
+template <int D, bool PF>
 __device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm, DraftBuf<D>& cur,
                                             int gnext, float q0, float q1, uint32_t magic,
                                             DraftLds& L, DraftAcc<D>& st) {
@@ -386,7 +361,7 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm
   L.vm[2 * lane + 1] = make_float2(cur.vm.z, cur.vm.z * (off - cur.vm.w));
   const float wscale = weight_scale(wave_max_all(fmaxf(cur.vm.x, cur.vm.z)));
   __builtin_amdgcn_sched_barrier(0);
-  if (gnext >= 0) draft_load_meta<D>(sm, gnext, cur);
+  if constexpr (PF) draft_load_meta<D>(sm, gnext, cur);
   bias = wave_sum_all(bias);
   __syncthreads();
 
@@ -403,15 +378,16 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm
     float p = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) p = key_word_dot(p, wd[k], magic, W[k], Wl[k]);
-    // a DPP read of a VGPR needs two wait states after the VALU write that produced it; the
-    // write is the last instruction of the asm sequence above, invisible to the compiler
+    // a DPP read of a VGPR, like any VALU read of a v_dot2c result, needs two wait states after
+    // the write; the write is the last instruction of the asm sequence above, invisible to the
+    // compiler
     asm volatile("s_nop 1" : "+v"(p));
     p += dpp<kDppXor1>(p);                       // the KL lanes of a key row
     if constexpr (S::KL == 4) p += dpp<kDppXor2>(p);
     sc[it] = p + bias;
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (gnext >= 0) draft_load_k<D>(sm, gnext, cur);
+  if constexpr (PF) draft_load_k<D>(sm, gnext, cur);
   float gmax = sc[0];
 #pragma unroll
   for (int it = 1; it < S::KIT; ++it) gmax = fmaxf(gmax, sc[it]);
@@ -464,21 +440,22 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm
     float o = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) o = value_word_dot(o, wd[k], magic, P[k], Pl[k]);
+    // a VALU read of a v_dot2c result needs two wait states; the dot is inside the asm above,
+    // where the compiler cannot see it
+    asm volatile("s_nop 1" : "+v"(o));
     st.o[i] = fmaf(st.o[i], alpha, (o - corr) * winv);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (gnext >= 0) draft_load_v<D>(sm, gnext, cur);
+  if constexpr (PF) draft_load_v<D>(sm, gnext, cur);
 }
 
 template <int D>
 __device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, DraftLds& L) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
-  const int ng = a.nq[b] / kGroup;
-  const int g0 = item * a.chunk_groups;
-  const int g1 = min(g0 + a.chunk_groups, ng);
   const size_t bh = (size_t)b * a.H + h;
+  const GroupStride gs = worker_groups(a, b, item);
   uint32_t magic;
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
@@ -497,11 +474,19 @@ __device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, Draf
 
   const Streams sm = make_streams(a, bh, D);
   DraftBuf<D> buf;
-  draft_load_k<D>(sm, g0, buf);
-  draft_load_meta<D>(sm, g0, buf);
-  draft_load_v<D>(sm, g0, buf);
-  for (int g = g0; g < g1; ++g)
-    draft_group<D>(a, sm, buf, g + 1 < g1 ? g + 1 : -1, q0, q1, magic, L, st);
+  if (gs.first < gs.ng) {
+    draft_load_k<D>(sm, gs.first, buf);
+    draft_load_meta<D>(sm, gs.first, buf);
+    draft_load_v<D>(sm, gs.first, buf);
+    const int total = (gs.ng - gs.first + gs.step - 1) / gs.step;
+    int g = gs.first, done = 0;
+    for (; g + gs.step < gs.ng; g += gs.step, ++done) {
+      pace(total - done, total);
+      draft_group<D, true>(a, sm, buf, g + gs.step, q0, q1, magic, L, st);
+    }
+    pace(1, total);
+    draft_group<D, false>(a, sm, buf, -1, q0, q1, magic, L, st);
+  }
 
   // l and beta were accumulated once per key row in each of its KL lanes
   const float l_run = wave_sum_from(st.l_run, S::KL);
@@ -605,6 +590,151 @@ __device__ __forceinline__ void verify_load_meta(const Streams& sm, int gi, Veri
   buf.vm = bldf4(sm.vm, lane * 16, (uint32_t)gi * kGroup * 8);
 }
 
+// Running state of a verify worker (per lane): softmax max / sum, the value bias sum, and the
+// O^T tiles kept in the weight scale of the last group (oinv is its inverse).
+template <int D>
+struct VerifyAcc {
+  float m_run, l_run, beta, oinv;
+  f32x4 O[VerifyShape<D>::RT];
+};
+
+// One group of a verify worker, in two 64-token halves.  With PF the buffers are refilled with
+// group gn as each part of group gi is consumed (a template flag, so that the number of loads in
+// flight at every wait is fixed).
+template <int D, bool PF>
+__device__ __forceinline__ void verify_group(const AttnArgs& a, const Streams& sm, VerifyBuf<D>& buf,
+                                             int gi, int gn, VerifyLds& L, VerifyAcc<D>& st) {
+  using S = VerifyShape<D>;
+  const int lane = threadIdx.x;
+  const int j = lane & 15;   // query column
+  const int g = lane >> 4;   // k-group
+  const int m = a.m;
+  const f16x2 c1152 = {(f16)1152.f, (f16)1152.f};
+  __syncthreads();  // the previous group's LDS reads are done
+  // q' = q s for this lane's channels and every query: fp16 hi/lo into the B-operand slots of
+  // the lanes that consume them, and the fp32 bias partials 1024 (q'h + q'l) + q' z
+  if (lane < D / 2) {
+    const float s0 = buf.km.x, z0 = buf.km.y, s1 = buf.km.z, z1 = buf.km.w;
+    const int c0 = 2 * lane;
+    const int gg = c0 / S::CPL, kk = (c0 % S::CPL) / 8, e0 = c0 % 8;  // e0 even, e0+1 odd
+    const int s_even = e0 >> 1, s_odd = 4 + (e0 >> 1);                // slots of e0, e0+1
+    f16* bh16 = reinterpret_cast<f16*>(&L.bq[0][kk][16 * gg]);
+    f16* bl16 = reinterpret_cast<f16*>(&L.bq[1][kk][16 * gg]);
+    for (int i = 0; i < m; ++i) {
+      {
+        const float2 qv = L.qs[i][lane];
+        const float qa = qv.x * s0, qb = qv.y * s1;
+        f16 ah, al, bhh, bl;
+        split_f16(qa, ah, al);
+        split_f16(qb, bhh, bl);
+        bh16[8 * i + s_even] = ah;
+        bl16[8 * i + s_even] = al;
+        bh16[8 * i + s_odd] = bhh;
+        bl16[8 * i + s_odd] = bl;
+        L.bias[i][lane] = 1024.f * (((float)ah + (float)al) + ((float)bhh + (float)bl)) +
+                          (qa * z0 + qb * z1);
+      }
+    }
+  }
+  L.vm[2 * lane] = make_float2(buf.vm.x, buf.vm.x * (128.f - buf.vm.y));
+  L.vm[2 * lane + 1] = make_float2(buf.vm.z, buf.vm.z * (128.f - buf.vm.w));
+  const float wscale = weight_scale(wave_max_all(fmaxf(buf.vm.x, buf.vm.z)));
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PF) verify_load_meta<D>(sm, gn, buf);
+  f16x8 Bq[S::KK], Bql[S::KK];
+#pragma unroll
+  for (int kk = 0; kk < S::KK; ++kk) {
+    Bq[kk] = __builtin_bit_cast(f16x8, L.bq[0][kk][lane]);
+    Bql[kk] = __builtin_bit_cast(f16x8, L.bq[1][kk][lane]);
+  }
+  float bias = 0.f;  // lanes 16g .. 16g+15 of query j, then across the four k-groups
+  {
+    const float4* bp = reinterpret_cast<const float4*>(&L.bias[j][16 * g]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 v = bp[k];
+      bias += (v.x + v.y) + (v.z + v.w);
+    }
+    bias += __shfl_xor(bias, 16);
+    bias += __shfl_xor(bias, 32);
+  }
+
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    f32x4 St[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < S::KK; ++kk) {
+        const f16x8 A = codes_f16(buf.ku[t][kk], buf.kl[t][kk]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bql[kk], acc, 0, 0, 0);
+      }
+      St[t] = acc - bias;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // next key half: the other half of this group, or the first half of the next group
+    if (half == 0)
+      verify_load_k<D>(sm, gi, 1, buf);
+    else if constexpr (PF)
+      verify_load_k<D>(sm, gn, 0, buf);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      mx = fmaxf(mx, fmaxf(fmaxf(St[t][0], St[t][1]), fmaxf(St[t][2], St[t][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m_run, mx);
+    const float alpha = fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= alpha;
+    st.beta *= alpha;
+    // O is kept in the weight scale of the current group
+    const float oscale = alpha * (wscale * st.oinv);
+    st.oinv = 1.f / wscale;
+#pragma unroll
+    for (int rt = 0; rt < S::RT; ++rt) st.O[rt] *= oscale;
+    f16 ph[4][4], pl[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(St[t][i] - m_new);
+        const float2 sw = L.vm[64 * half + 16 * g + 8 * (t >> 1) + 2 * i + (t & 1)];
+        st.l_run += p;
+        st.beta += p * sw.y;
+        split_f16(wscale * (p * sw.x), ph[t][i], pl[t][i]);
+      }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const f16x8 Bp = {ph[2 * q][0], ph[2 * q][1], ph[2 * q][2], ph[2 * q][3],
+                        ph[2 * q + 1][0], ph[2 * q + 1][1], ph[2 * q + 1][2], ph[2 * q + 1][3]};
+      const f16x8 Bpl = {pl[2 * q][0], pl[2 * q][1], pl[2 * q][2], pl[2 * q][3],
+                         pl[2 * q + 1][0], pl[2 * q + 1][1], pl[2 * q + 1][2], pl[2 * q + 1][3]};
+#pragma unroll
+      for (int rt = 0; rt < S::RT; ++rt) {
+        const uint32_t uw = q == 0 ? buf.vu[rt].x : buf.vu[rt].y;
+        const uint32_t lw = q == 0 ? buf.vl[rt].x : buf.vl[rt].y;
+        f16x8 A = codes_f16(uw, lw);
+        const f16x2 a0 = f16x2{A[0], A[1]} - c1152, a1 = f16x2{A[2], A[3]} - c1152;
+        const f16x2 a2 = f16x2{A[4], A[5]} - c1152, a3 = f16x2{A[6], A[7]} - c1152;
+        A = f16x8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+        st.O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bp, st.O[rt], 0, 0, 0);
+        st.O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bpl, st.O[rt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (half == 0)
+      verify_load_v<D>(sm, gi, 1, buf);
+    else if constexpr (PF)
+      verify_load_v<D>(sm, gn, 0, buf);
+  }
+}
+
 template <int D>
 __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, VerifyLds& L) {
   using S = VerifyShape<D>;
@@ -612,10 +742,8 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
   const int j = lane & 15;   // query column
   const int g = lane >> 4;   // k-group
   const int m = a.m;
-  const int ng = a.nq[b] / kGroup;
-  const int g0 = item * a.chunk_groups;
-  const int g1 = min(g0 + a.chunk_groups, ng);
   const size_t bh = (size_t)b * a.H + h;
+  const GroupStride gs = worker_groups(a, b, item);
 
   // q times qscale of channels 2*lane, 2*lane+1 for every query, and zeroed B operands so the
   // padding query columns j >= m stay zero
@@ -628,157 +756,44 @@ __device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, Ver
   for (int x = lane; x < 2 * 4 * 64; x += 64) (&L.bq[0][0][0])[x] = make_uint4(0, 0, 0, 0);
   for (int x = lane; x < QS_MAX_QUERIES * 64; x += 64) (&L.bias[0][0])[x] = 0.f;
 
-  float m_run = -INFINITY, l_run = 0.f, beta = 0.f;
-  float oinv = 1.f;  // inverse of the weight scale O is kept in
-  f32x4 O[S::RT];
+  VerifyAcc<D> st;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+  st.beta = 0.f;
+  st.oinv = 1.f;
 #pragma unroll
-  for (int rt = 0; rt < S::RT; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const f16x2 c1152 = {(f16)1152.f, (f16)1152.f};
+  for (int rt = 0; rt < S::RT; ++rt) st.O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const Streams sm = make_streams(a, bh, D);
   VerifyBuf<D> buf;
-  verify_load_k<D>(sm, g0, 0, buf);
-  verify_load_meta<D>(sm, g0, buf);
-  verify_load_v<D>(sm, g0, 0, buf);
-  for (int gi = g0; gi < g1; ++gi) {
-    __syncthreads();  // the previous group's LDS reads are done
-    // q' = q s for this lane's channels and every query: fp16 hi/lo into the B-operand slots of
-    // the lanes that consume them, and the fp32 bias partials 1024 (q'h + q'l) + q' z
-    if (lane < D / 2) {
-      const float s0 = buf.km.x, z0 = buf.km.y, s1 = buf.km.z, z1 = buf.km.w;
-      const int c0 = 2 * lane;
-      const int gg = c0 / S::CPL, kk = (c0 % S::CPL) / 8, e0 = c0 % 8;  // e0 even, e0+1 odd
-      const int s_even = e0 >> 1, s_odd = 4 + (e0 >> 1);                // slots of e0, e0+1
-      f16* bh16 = reinterpret_cast<f16*>(&L.bq[0][kk][16 * gg]);
-      f16* bl16 = reinterpret_cast<f16*>(&L.bq[1][kk][16 * gg]);
-      for (int i = 0; i < m; ++i) {
-        {
-          const float2 qv = L.qs[i][lane];
-          const float qa = qv.x * s0, qb = qv.y * s1;
-          f16 ah, al, bhh, bl;
-          split_f16(qa, ah, al);
-          split_f16(qb, bhh, bl);
-          bh16[8 * i + s_even] = ah;
-          bl16[8 * i + s_even] = al;
-          bh16[8 * i + s_odd] = bhh;
-          bl16[8 * i + s_odd] = bl;
-          L.bias[i][lane] = 1024.f * (((float)ah + (float)al) + ((float)bhh + (float)bl)) +
-                            (qa * z0 + qb * z1);
-        }
-      }
+  if (gs.first < gs.ng) {
+    verify_load_k<D>(sm, gs.first, 0, buf);
+    verify_load_meta<D>(sm, gs.first, buf);
+    verify_load_v<D>(sm, gs.first, 0, buf);
+    const int total = (gs.ng - gs.first + gs.step - 1) / gs.step;
+    int gi = gs.first, done = 0;
+    for (; gi + gs.step < gs.ng; gi += gs.step, ++done) {
+      pace(total - done, total);
+      verify_group<D, true>(a, sm, buf, gi, gi + gs.step, L, st);
     }
-    L.vm[2 * lane] = make_float2(buf.vm.x, buf.vm.x * (128.f - buf.vm.y));
-    L.vm[2 * lane + 1] = make_float2(buf.vm.z, buf.vm.z * (128.f - buf.vm.w));
-    const float wscale = weight_scale(wave_max_all(fmaxf(buf.vm.x, buf.vm.z)));
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    if (gi + 1 < g1) verify_load_meta<D>(sm, gi + 1, buf);
-    f16x8 Bq[S::KK], Bql[S::KK];
-#pragma unroll
-    for (int kk = 0; kk < S::KK; ++kk) {
-      Bq[kk] = __builtin_bit_cast(f16x8, L.bq[0][kk][lane]);
-      Bql[kk] = __builtin_bit_cast(f16x8, L.bq[1][kk][lane]);
-    }
-    float bias = 0.f;  // lanes 16g .. 16g+15 of query j, then across the four k-groups
-    {
-      const float4* bp = reinterpret_cast<const float4*>(&L.bias[j][16 * g]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 v = bp[k];
-        bias += (v.x + v.y) + (v.z + v.w);
-      }
-      bias += __shfl_xor(bias, 16);
-      bias += __shfl_xor(bias, 32);
-    }
-
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x4 St[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < S::KK; ++kk) {
-          const f16x8 A = codes_f16(buf.ku[t][kk], buf.kl[t][kk]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq[kk], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bql[kk], acc, 0, 0, 0);
-        }
-        St[t] = acc - bias;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      {  // next key half: the other half of this group, or the first half of the next group
-        const int ngi = half == 0 ? gi : gi + 1;
-        if (ngi < g1) verify_load_k<D>(sm, ngi, half ^ 1, buf);
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        mx = fmaxf(mx, fmaxf(fmaxf(St[t][0], St[t][1]), fmaxf(St[t][2], St[t][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-      beta *= alpha;
-      // O is kept in the weight scale of the current group
-      const float oscale = alpha * (wscale * oinv);
-      oinv = 1.f / wscale;
-#pragma unroll
-      for (int rt = 0; rt < S::RT; ++rt) O[rt] *= oscale;
-      f16 ph[4][4], pl[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(St[t][i] - m_new);
-          const float2 sw = L.vm[64 * half + 16 * g + 8 * (t >> 1) + 2 * i + (t & 1)];
-          l_run += p;
-          beta += p * sw.y;
-          split_f16(wscale * (p * sw.x), ph[t][i], pl[t][i]);
-        }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const f16x8 Bp = {ph[2 * q][0], ph[2 * q][1], ph[2 * q][2], ph[2 * q][3],
-                          ph[2 * q + 1][0], ph[2 * q + 1][1], ph[2 * q + 1][2], ph[2 * q + 1][3]};
-        const f16x8 Bpl = {pl[2 * q][0], pl[2 * q][1], pl[2 * q][2], pl[2 * q][3],
-                           pl[2 * q + 1][0], pl[2 * q + 1][1], pl[2 * q + 1][2], pl[2 * q + 1][3]};
-#pragma unroll
-        for (int rt = 0; rt < S::RT; ++rt) {
-          const uint32_t uw = q == 0 ? buf.vu[rt].x : buf.vu[rt].y;
-          const uint32_t lw = q == 0 ? buf.vl[rt].x : buf.vl[rt].y;
-          f16x8 A = codes_f16(uw, lw);
-          const f16x2 a0 = f16x2{A[0], A[1]} - c1152, a1 = f16x2{A[2], A[3]} - c1152;
-          const f16x2 a2 = f16x2{A[4], A[5]} - c1152, a3 = f16x2{A[6], A[7]} - c1152;
-          A = f16x8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
-          O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bp, O[rt], 0, 0, 0);
-          O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bpl, O[rt], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        const int ngi = half == 0 ? gi : gi + 1;
-        if (ngi < g1) verify_load_v<D>(sm, ngi, half ^ 1, buf);
-      }
-    }
+    pace(1, total);
+    verify_group<D, false>(a, sm, buf, gi, -1, L, st);
   }
 
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  beta += __shfl_xor(beta, 16);
-  beta += __shfl_xor(beta, 32);
+  st.l_run += __shfl_xor(st.l_run, 16);
+  st.l_run += __shfl_xor(st.l_run, 32);
+  st.beta += __shfl_xor(st.beta, 16);
+  st.beta += __shfl_xor(st.beta, 32);
   if (j < m) {
     float* rec = record(a, D, b, h, item, j);
     if (g == 0) {
-      rec[0] = m_run;
-      rec[1] = l_run;
+      rec[0] = st.m_run;
+      rec[1] = st.l_run;
     }
 #pragma unroll
     for (int rt = 0; rt < S::RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rec[kRecPad + 16 * rt + 4 * g + i] = fmaf(O[rt][i], oinv, beta);
+      for (int i = 0; i < 4; ++i) rec[kRecPad + 16 * rt + 4 * g + i] = fmaf(st.O[rt][i], st.oinv, st.beta);
   }
 }
 

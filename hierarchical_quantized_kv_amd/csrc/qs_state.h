@@ -80,9 +80,10 @@ struct Plan {
   int32_t tbase[QS_MAX_BATCH + 1] = {};
 };
 
-// Quantized work items are whole-group chunks.  The chunk length is the smallest one that keeps
-// the call at no more than `target_items` (sequence, head, chunk) items (so that they all run in
-// one resident round) and no sequence at more than kMaxQuantSplits chunks.
+// Quantized work: each sequence's groups are dealt to ceil(groups / chunk_groups) workers per
+// head.  The chunk length is the smallest one that keeps the call at no more than
+// `target_items` (sequence, head, worker) items (so that they all run in one resident round) and
+// no sequence at more than kMaxQuantSplits workers.
 inline Plan make_plan(const Seq* s, int B, int H, int G, int target_items) {
   Plan p;
   long long groups = 0;
