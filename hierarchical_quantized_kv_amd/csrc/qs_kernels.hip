@@ -19,14 +19,16 @@
 //
 // Arithmetic of the quantized parts.  With per-channel key metadata (s_d, z_d) of the group and
 // the query pre-scaled by sm_scale*log2(e):
-//   draft score  = sum_d q_d s_d (16 U_d + off - z_d) = 16 sum_d q'_d U_d + sum_d q'_d (off - z_d)
+//   draft score  = sum_d q_d s_d (16 U_d + off - z_d)
+//                = 16 sum_d q'_d (U_d - 8) + sum_d q'_d (128 + off - z_d)
 //   verify score = sum_d q'_d C8_d - sum_d q'_d z_d,                 q'_d = q_d s_d
 // and with per-token value metadata (s_t, z_t) and softmax weights p_t:
 //   draft  o_d = 16 sum_t p'_t (U_td - 8) + sum_t p_t s_t (128 + off - z_t)
 //   verify o_d =    sum_t p'_t (C8_td - 128) + sum_t p_t s_t (128 - z_t),   p'_t = p_t s_t
-// The first sums run on fp16 operands built from the nibbles with the magic-number trick
-// (0x6400 | n is the fp16 value 1024 + n); the second (bias) sums stay in fp32, which keeps
-// degenerate groups (scale clamped to 1e-8, huge zero-point) exact.
+// The first sums of the draft run as signed 4-bit integer dot products against fixed-point
+// digits of q' and p'; those of verify on MFMA with fp16 operands built from the codes with the
+// magic-number trick (0x6400 | n is the fp16 value 1024 + n).  The second (bias) sums stay in
+// fp32, which keeps degenerate groups (scale clamped to 1e-8, huge zero-point) exact.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -43,72 +45,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kMagic = 0x64006400u;  // two fp16 1024.0 with empty low mantissa bits
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t x) { return __builtin_bit_cast(f16x2, x); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
-// One 32-bit word of the upper key plane (8 channels) against its weights q'/4, fp16 hi and lo:
-//   p += sum over the pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7) of (1024 + 64 U) . (w_hi + w_lo),
-// each nibble moved into the top mantissa bits 6-9 of an fp16 1024 (the offset then stays about
-// the size of the data, which keeps the fp32 sum accurate) by a shift and one v_and_or_b32.
-// Written as one instruction sequence so that the compiler adds no wait states inside it.
-__device__ __forceinline__ float key_word_dot(float p, uint32_t w, uint32_t magic, uint4 wh,
-                                              uint4 wl) {
-  uint32_t t;
-  asm volatile(
-      "v_lshlrev_b32 %[t], 6, %[w]\n\t"
-      "v_and_or_b32 %[t], %[t], %[m], %[mg]\n\t"
-      "v_dot2c_f32_f16 %[p], %[t], %[h0]\n\t"
-      "v_dot2c_f32_f16 %[p], %[t], %[l0]\n\t"
-      "v_lshlrev_b32 %[t], 2, %[w]\n\t"
-      "v_and_or_b32 %[t], %[t], %[m], %[mg]\n\t"
-      "v_dot2c_f32_f16 %[p], %[t], %[h1]\n\t"
-      "v_dot2c_f32_f16 %[p], %[t], %[l1]\n\t"
-      "v_lshrrev_b32 %[t], 2, %[w]\n\t"
-      "v_and_or_b32 %[t], %[t], %[m], %[mg]\n\t"
-      "v_dot2c_f32_f16 %[p], %[t], %[h2]\n\t"
-      "v_dot2c_f32_f16 %[p], %[t], %[l2]\n\t"
-      "v_lshrrev_b32 %[t], 6, %[w]\n\t"
-      "v_and_or_b32 %[t], %[t], %[m], %[mg]\n\t"
-      "v_dot2c_f32_f16 %[p], %[t], %[h3]\n\t"
-      "v_dot2c_f32_f16 %[p], %[t], %[l3]"
-      : [p] "+v"(p), [t] "=&v"(t)
-      : [w] "v"(w), [m] "s"(0x03C003C0u), [mg] "v"(magic), [h0] "v"(wh.x), [h1] "v"(wh.y),
-        [h2] "v"(wh.z), [h3] "v"(wh.w), [l0] "v"(wl.x), [l1] "v"(wl.y), [l2] "v"(wl.z),
-        [l3] "v"(wl.w));
-  return p;
-}
-
-// One 32-bit word of the upper value plane (8 tokens of one channel) against the tokens'
-// weights, fp16 hi and lo: pairs (t0,t4) and (t2,t6) as 1024 + U, (t1,t5) and (t3,t7) as
-// 1024 + 16 U (the weights of even tokens carry the factor 16).
-__device__ __forceinline__ float value_word_dot(float o, uint32_t w, uint32_t magic, uint4 ph,
-                                                uint4 pl) {
-  uint32_t t, w8;
-  asm volatile(
-      "v_and_or_b32 %[t], %[w], %[mlo], %[mg]\n\t"
-      "v_dot2c_f32_f16 %[o], %[t], %[h0]\n\t"
-      "v_dot2c_f32_f16 %[o], %[t], %[l0]\n\t"
-      "v_and_or_b32 %[t], %[w], %[mhi], %[mg]\n\t"
-      "v_dot2c_f32_f16 %[o], %[t], %[h1]\n\t"
-      "v_dot2c_f32_f16 %[o], %[t], %[l1]\n\t"
-      "v_lshrrev_b32 %[w8], 8, %[w]\n\t"
-      "v_and_or_b32 %[t], %[w8], %[mlo], %[mg]\n\t"
-      "v_dot2c_f32_f16 %[o], %[t], %[h2]\n\t"
-      "v_dot2c_f32_f16 %[o], %[t], %[l2]\n\t"
-      "v_and_or_b32 %[t], %[w8], %[mhi], %[mg]\n\t"
-      "v_dot2c_f32_f16 %[o], %[t], %[h3]\n\t"
-      "v_dot2c_f32_f16 %[o], %[t], %[l3]"
-      : [o] "+v"(o), [t] "=&v"(t), [w8] "=&v"(w8)
-      : [w] "v"(w), [mlo] "s"(0x000F000Fu), [mhi] "s"(0x00F000F0u), [mg] "v"(magic),
-        [h0] "v"(ph.x), [h1] "v"(ph.y), [h2] "v"(ph.z), [h3] "v"(ph.w), [l0] "v"(pl.x),
-        [l1] "v"(pl.y), [l2] "v"(pl.z), [l3] "v"(pl.w));
-  return o;
-}
-
 // Power of two f such that every value weight of a group, at most 16 * smax (even tokens carry the
 // factor 16), scaled by f stays below 2^14: the fp16 hi/lo weights then keep full relative
 // precision instead of falling into the fp16 subnormal range for small softmax probabilities.
@@ -162,12 +104,6 @@ __device__ __forceinline__ Streams make_streams(const AttnArgs& a, size_t bh, in
 
 __device__ __forceinline__ float lo_h(uint32_t x) { return (float)as_h2(x).x; }
 __device__ __forceinline__ float hi_h(uint32_t x) { return (float)as_h2(x).y; }
-
-// Word index and half of token/channel t inside a "pair-ordered" fp16 operand block: the
-// nibbles of one 32-bit plane word w (8 entries, entry e in nibble e) come out as the fp16
-// pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7); the matching weights are stored in that order.
-__device__ __forceinline__ int pair_word(int t) { return (t >> 3) * 4 + ((t & 7) & 3); }
-__device__ __forceinline__ int pair_half(int t) { return (t & 7) >> 2; }
 
 // fp16 hi + lo split of x: hi = fp16(x), lo = fp16(x - hi); hi + lo carries ~22 bits.
 __device__ __forceinline__ void split_f16(float x, f16& hi, f16& lo) {
@@ -274,11 +210,60 @@ struct DraftShape {
   static constexpr int VIT = D / 16;       // value loads per lane per group
 };
 
+// Draft arithmetic in integers.  An upper nibble U is taken as the signed 4-bit u = U - 8
+// (the nibble XOR 8), and a weight x (q' for keys, p' for values) as a fixed-point integer
+// X = round(x / unit) with |X| < 2^22, written in six signed base-16 digits c_j in [-8, 7]
+// (X = sum_j 16^j c_j: the nibbles of X + 0x888888, each XOR 8).  Then
+//   sum_e x_e u_e = unit * sum_j 16^j sum_e c_j,e u_e,
+// and every inner sum over the 8 nibbles of a 32-bit plane word is one v_dot8_i32_i4, exact in
+// int32.  The unit is a power of two chosen per group from the largest weight, so the products
+// lose only the rounding of x to 22 bits relative to that largest weight.
+constexpr int kDigits = 6;
+constexpr uint32_t kDigitBias = 0x888888u;  // 8 in each of the six digit positions
+constexpr uint32_t kNibbleBias = 0x88888888u;
+
 struct DraftLds {
-  uint32_t wts[2][64];   // key weights q' (hi, lo), pair order (D/2 words used)
-  uint32_t pw[2][64];    // value weights (hi, lo) in pair order: 16 p'_t (even t), p'_t (odd t)
-  float2 vm[kGroup];     // (s_t, s_t * (off - z_t))
+  uint32_t qd[kDigits][16];       // key weights q': digit j of channels 8w .. 8w+7 in word w
+  uint32_t pd[kDigits][kGroup / 8];  // value weights p' = p s: digit j of tokens 8w .. 8w+7
+  float2 vm[kGroup];              // (s_t, s_t * (128 + off - z_t))
 };
+
+// Digit bytes of two fixed-point weights a (low nibbles) and b (high nibbles): byte k of `even`
+// is digit 2k, byte k of `odd` digit 2k+1, both already XOR 8.
+__device__ __forceinline__ void digit_bytes(int xa, int xb, uint32_t& even, uint32_t& odd) {
+  const uint32_t a = (uint32_t)xa + kDigitBias, b = (uint32_t)xb + kDigitBias;
+  even = ((a & 0x0F0F0Fu) | ((b & 0x0F0F0Fu) << 4)) ^ kDigitBias;
+  odd = (((a >> 4) & 0x0F0F0Fu) | (((b >> 4) & 0x0F0F0Fu) << 4)) ^ kDigitBias;
+}
+
+// sum over the 4 plane words w[] (32 nibbles) of the digit-weighted signed dot products, as a
+// float in units of the fixed-point weights: sum_j 16^j sum_k dot8(d[j].k, w[k] ^ 0x88888888),
+// evaluated as two Horner chains (digits 5..3 and 2..0; |chain| <= 2048 * 273 fits int32).
+__device__ __forceinline__ float digit_dot(const uint4 (&d)[kDigits], uint4 w) {
+  const int u[4] = {(int)(w.x ^ kNibbleBias), (int)(w.y ^ kNibbleBias), (int)(w.z ^ kNibbleBias),
+                    (int)(w.w ^ kNibbleBias)};
+  auto plane = [&](int j, int acc) {
+    acc = __builtin_amdgcn_sdot8((int)d[j].x, u[0], acc, false);
+    acc = __builtin_amdgcn_sdot8((int)d[j].y, u[1], acc, false);
+    acc = __builtin_amdgcn_sdot8((int)d[j].z, u[2], acc, false);
+    return __builtin_amdgcn_sdot8((int)d[j].w, u[3], acc, false);
+  };
+  int hi = plane(5, 0);
+  hi = plane(4, hi << 4);
+  hi = plane(3, hi << 4);
+  int lo = plane(2, 0);
+  lo = plane(1, lo << 4);
+  lo = plane(0, lo << 4);
+  return fmaf((float)hi, 4096.f, (float)lo);
+}
+
+// Power-of-two fixed-point unit for weights up to xmax: |x| / unit < 2^22.
+__device__ __forceinline__ void fixed_unit(float xmax, float& inv_unit, float& unit) {
+  int e;
+  frexpf(xmax, &e);  // xmax < 2^e (e = 0 for xmax = 0)
+  inv_unit = ldexpf(1.f, 22 - e);
+  unit = ldexpf(1.f, e - 22);
+}
 
 // Planes and metadata of one group, as loaded by one lane.
 template <int D>
@@ -332,59 +317,48 @@ struct DraftAcc {
 // flight at every wait is fixed.)
 template <int D, bool PF>
 __device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm, DraftBuf<D>& cur,
-                                            int gnext, float q0, float q1, uint32_t magic,
-                                            DraftLds& L, DraftAcc<D>& st) {
+                                            int gnext, float q0, float q1, DraftLds& L,
+                                            DraftAcc<D>& st) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
   const int kc = lane % S::KL, kt = lane / S::KL, vr = lane & 3;
-  const float off = a.draft_offset;
+  const float c = 128.f + a.draft_offset;  // 16 U + off - z = 16 u + (128 + off - z)
 
   __syncthreads();  // the previous group's LDS reads are done
-  float bias = 0.f;
+  // key weights q' = q s (channels 2 lane, 2 lane + 1) as digit planes; the score bias
+  // sum_d q'_d (128 + off - z_d) stays in fp32
+  const float qa = q0 * cur.km.x, qb = q1 * cur.km.z;  // zero on lanes >= D/2
+  float bias = qa * (c - cur.km.y) + qb * (c - cur.km.w);
+  float qunit, qinv;
+  fixed_unit(wave_max_all(fmaxf(fabsf(qa), fabsf(qb))), qinv, qunit);
+  L.vm[2 * lane] = make_float2(cur.vm.x, cur.vm.x * (c - cur.vm.y));
+  L.vm[2 * lane + 1] = make_float2(cur.vm.z, cur.vm.z * (c - cur.vm.w));
+  float punit, pinv;  // p' = p s <= max_t s_t
+  fixed_unit(wave_max_all(fmaxf(cur.vm.x, cur.vm.z)), pinv, punit);
   if (lane < D / 2) {
-    // key weights q'/4 = q s / 4 as fp16 hi + lo, against nibble values 1024 + 64 U
-    const float qa = q0 * cur.km.x, qb = q1 * cur.km.z;
-    f16 ah, al, bh, bl;
-    split_f16(0.25f * qa, ah, al);
-    split_f16(0.25f * qb, bh, bl);
-    const int c0 = 2 * lane, c1 = 2 * lane + 1;
-    f16* wh = reinterpret_cast<f16*>(L.wts[0]);
-    f16* wl = reinterpret_cast<f16*>(L.wts[1]);
-    wh[2 * pair_word(c0) + pair_half(c0)] = ah;
-    wl[2 * pair_word(c0) + pair_half(c0)] = al;
-    wh[2 * pair_word(c1) + pair_half(c1)] = bh;
-    wl[2 * pair_word(c1) + pair_half(c1)] = bl;
-    bias = qa * (off - cur.km.y) + qb * (off - cur.km.w) -
-           1024.f * (((float)ah + (float)al) + ((float)bh + (float)bl));
+    uint32_t ev, od;
+    digit_bytes((int)rintf(qa * qinv), (int)rintf(qb * qinv), ev, od);
+    uint8_t* qd = reinterpret_cast<uint8_t*>(&L.qd[0][0]);
+#pragma unroll
+    for (int j = 0; j < kDigits; ++j)
+      qd[j * 64 + lane] = (uint8_t)(((j & 1) ? od : ev) >> (8 * (j >> 1)));
   }
-  L.vm[2 * lane] = make_float2(cur.vm.x, cur.vm.x * (off - cur.vm.y));
-  L.vm[2 * lane + 1] = make_float2(cur.vm.z, cur.vm.z * (off - cur.vm.w));
-  const float wscale = weight_scale(wave_max_all(fmaxf(cur.vm.x, cur.vm.z)));
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (PF) draft_load_meta<D>(sm, gnext, cur);
   bias = wave_sum_all(bias);
   __syncthreads();
 
-  uint4 W[4], Wl[4];
+  uint4 dq[kDigits];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    W[k] = reinterpret_cast<const uint4*>(L.wts[0])[4 * kc + k];
-    Wl[k] = reinterpret_cast<const uint4*>(L.wts[1])[4 * kc + k];
-  }
+  for (int j = 0; j < kDigits; ++j) dq[j] = reinterpret_cast<const uint4*>(L.qd[j])[kc];
+  const float kscale = 16.f * qunit;
   float sc[S::KIT];
 #pragma unroll
   for (int it = 0; it < S::KIT; ++it) {
-    const uint32_t wd[4] = {cur.k[it].x, cur.k[it].y, cur.k[it].z, cur.k[it].w};
-    float p = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) p = key_word_dot(p, wd[k], magic, W[k], Wl[k]);
-    // a DPP read of a VGPR, like any VALU read of a v_dot2c result, needs two wait states after
-    // the write; the write is the last instruction of the asm sequence above, invisible to the
-    // compiler
-    asm volatile("s_nop 1" : "+v"(p));
-    p += dpp<kDppXor1>(p);                       // the KL lanes of a key row
+    float p = digit_dot(dq, cur.k[it]);
+    p += dpp<kDppXor1>(p);  // the KL lanes of a key row
     if constexpr (S::KL == 4) p += dpp<kDppXor2>(p);
-    sc[it] = p + bias;
+    sc[it] = fmaf(p, kscale, bias);
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (PF) draft_load_k<D>(sm, gnext, cur);
@@ -397,6 +371,11 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm
   st.m_run = m_new;
   st.l_run *= alpha;
   st.beta *= alpha;
+  // value weights p' = p s as digit planes.  Token t = it * TPI + kt sits in the KL lanes of its
+  // key row; lanes of even rows pair token t with t + 1 (held KL lanes up) into digit bytes, and
+  // lane kc of the row writes planes kc * PPL ...
+  constexpr int PPL = (kDigits + S::KL - 1) / S::KL;
+  uint8_t* pd = reinterpret_cast<uint8_t*>(&L.pd[0][0]);
 #pragma unroll
   for (int it = 0; it < S::KIT; ++it) {
     const int t = it * S::TPI + kt;
@@ -404,46 +383,27 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm
     const float2 sw = L.vm[t];
     st.l_run += p;
     st.beta += p * sw.y;
-    // every lane of the key row writes the same value
-    f16 wh, wl;
-    split_f16(((t & 1) ? wscale : 16.f * wscale) * (p * sw.x), wh, wl);
-    reinterpret_cast<f16*>(L.pw[0])[2 * pair_word(t) + pair_half(t)] = wh;
-    reinterpret_cast<f16*>(L.pw[1])[2 * pair_word(t) + pair_half(t)] = wl;
+    const int x = (int)rintf(p * sw.x * pinv);
+    const int xn = __shfl_xor(x, S::KL);
+    if ((kt & 1) == 0) {
+      uint32_t ev, od;
+      digit_bytes(x, xn, ev, od);
+#pragma unroll
+      for (int jj = 0; jj < PPL; ++jj) {
+        const int j = kc * PPL + jj;
+        if (j < kDigits) pd[j * (kGroup / 2) + t / 2] = (uint8_t)(((j & 1) ? od : ev) >> (8 * (j >> 1)));
+      }
+    }
   }
   __syncthreads();
 
-  // values: a fresh fp32 sum per group of w_t (1024 + U or 1024 + 16 U); the group's exact
-  // offset 1024 sum_t w_t is removed before it joins the running (rescaled) sum.
-  uint4 P[4], Pl[4];
+  uint4 dp[kDigits];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    P[k] = reinterpret_cast<const uint4*>(L.pw[0])[4 * vr + k];
-    Pl[k] = reinterpret_cast<const uint4*>(L.pw[1])[4 * vr + k];
-  }
-  const f16x2 k1024 = {(f16)1024.f, (f16)1024.f};
-  const float winv = 1.f / wscale;  // exact: a power of two
-  float corr = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    corr = dot2(as_h2(P[k].x), k1024, corr);
-    corr = dot2(as_h2(P[k].y), k1024, corr);
-    corr = dot2(as_h2(P[k].z), k1024, corr);
-    corr = dot2(as_h2(P[k].w), k1024, corr);
-    corr = dot2(as_h2(Pl[k].x), k1024, corr);
-    corr = dot2(as_h2(Pl[k].y), k1024, corr);
-    corr = dot2(as_h2(Pl[k].z), k1024, corr);
-    corr = dot2(as_h2(Pl[k].w), k1024, corr);
-  }
+  for (int j = 0; j < kDigits; ++j) dp[j] = reinterpret_cast<const uint4*>(L.pd[j])[vr];
+  const float vscale = 16.f * punit;
 #pragma unroll
   for (int i = 0; i < S::VIT; ++i) {
-    const uint32_t wd[4] = {cur.v[i].x, cur.v[i].y, cur.v[i].z, cur.v[i].w};
-    float o = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o = value_word_dot(o, wd[k], magic, P[k], Pl[k]);
-    // a VALU read of a v_dot2c result needs two wait states; the dot is inside the asm above,
-    // where the compiler cannot see it
-    asm volatile("s_nop 1" : "+v"(o));
-    st.o[i] = fmaf(st.o[i], alpha, (o - corr) * winv);
+    st.o[i] = fmaf(st.o[i], alpha, digit_dot(dp, cur.v[i]) * vscale);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -456,8 +416,6 @@ __device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, Draf
   const int lane = threadIdx.x;
   const size_t bh = (size_t)b * a.H + h;
   const GroupStride gs = worker_groups(a, b, item);
-  uint32_t magic;
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
   float q0 = 0.f, q1 = 0.f;  // channels 2*lane, 2*lane+1 (lanes < D/2), times qscale
   if (lane < D / 2) {
@@ -482,10 +440,10 @@ __device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, Draf
     int g = gs.first, done = 0;
     for (; g + gs.step < gs.ng; g += gs.step, ++done) {
       pace(total - done, total);
-      draft_group<D, true>(a, sm, buf, g + gs.step, q0, q1, magic, L, st);
+      draft_group<D, true>(a, sm, buf, g + gs.step, q0, q1, L, st);
     }
     pace(1, total);
-    draft_group<D, false>(a, sm, buf, -1, q0, q1, magic, L, st);
+    draft_group<D, false>(a, sm, buf, -1, q0, q1, L, st);
   }
 
   // l and beta were accumulated once per key row in each of its KL lanes
@@ -822,9 +780,9 @@ __device__ void tail_item(const AttnArgs& a, int b, int h, int chunk, int split,
   const uint16_t* kchunk = a.tail_k + (bh * ring + s0) * D;
   const uint16_t* vchunk = a.tail_v + (bh * ring + s0) * D;
 
-  // Every load of the item is issued before the first use: the m queries (m * D/2 words, in
-  // lane-strided order), this lane's key row, and the D/64 value channels of every token of the
-  // chunk; slots past the nt valid tokens are read (they lie inside the ring) and zeroed.
+  // The loads of the queries (m * D/2 words, in lane-strided order) and of this lane's key row
+  // are issued together before their first use; slots past the nt valid tokens are read (they
+  // lie inside the ring) and zeroed.
   constexpr int QW = QS_MAX_QUERIES * (D / 2) / 64;  // query words per lane, at most
   const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q);
   uint32_t qw[QW];
@@ -845,17 +803,6 @@ __device__ void tail_item(const AttnArgs& a, int b, int h, int chunk, int split,
   }
 #pragma unroll
   for (int k = 0; k < QW; ++k) (&L.q[0][0])[lane + 64 * k] = qw[k];
-  constexpr int CPL = D / 64;  // value channels per lane: lane*CPL ..
-  uint32_t vw[kTailChunk];
-#pragma unroll
-  for (int tt = 0; tt < kTailChunk; ++tt) {
-    uint32_t w;
-    if constexpr (CPL == 2)
-      w = reinterpret_cast<const uint32_t*>(vchunk + tt * D)[lane];
-    else
-      w = vchunk[tt * D + lane];
-    vw[tt] = tt < nvalid ? w : 0u;
-  }
   __syncthreads();
 
   for (int i = 0; i < m; ++i) {
@@ -877,24 +824,51 @@ __device__ void tail_item(const AttnArgs& a, int b, int h, int chunk, int split,
   }
   __syncthreads();
 
-  // o_i[d] = sum_t p_i[t] v_t[d]; lane owns channels lane*CPL ..
-  for (int i = 0; i < m; ++i) {
-    float acc[CPL];
+  // o_i[d] = sum_t p_i[t] v_t[d]; lane owns channels lane*CPL ..  The value words of the chunk
+  // are loaded in two batches of half a chunk, each batch issued before its first use.
+  constexpr int CPL = D / 64;
+  constexpr int HB = kTailChunk / 2;
+  float acc[QS_MAX_QUERIES][CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int i = 0; i < QS_MAX_QUERIES; ++i)
 #pragma unroll
-    for (int tt = 0; tt < kTailChunk; ++tt) {
-      const float p = L.p[tt][i];
-      if constexpr (CPL == 2) {
-        acc[0] = fmaf(p, lo_h(vw[tt]), acc[0]);
-        acc[1] = fmaf(p, hi_h(vw[tt]), acc[1]);
-      } else {
-        acc[0] = fmaf(p, (float)__builtin_bit_cast(f16, (uint16_t)vw[tt]), acc[0]);
+    for (int c = 0; c < CPL; ++c) acc[i][c] = 0.f;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    uint32_t vw[HB];
+#pragma unroll
+    for (int u = 0; u < HB; ++u) {
+      const int tt = hb * HB + u;
+      uint32_t w;
+      if constexpr (CPL == 2)
+        w = reinterpret_cast<const uint32_t*>(vchunk + tt * D)[lane];
+      else
+        w = vchunk[tt * D + lane];
+      vw[u] = tt < nvalid ? w : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < QS_MAX_QUERIES; ++i) {
+      if (i < m) {
+#pragma unroll
+        for (int u = 0; u < HB; ++u) {
+          const float p = L.p[hb * HB + u][i];
+          if constexpr (CPL == 2) {
+            acc[i][0] = fmaf(p, lo_h(vw[u]), acc[i][0]);
+            acc[i][1] = fmaf(p, hi_h(vw[u]), acc[i][1]);
+          } else {
+            acc[i][0] = fmaf(p, (float)__builtin_bit_cast(f16, (uint16_t)vw[u]), acc[i][0]);
+          }
+        }
       }
     }
-    float* rec = record(a, D, b, h, split, i);
+  }
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) rec[kRecPad + CPL * lane + c] = acc[c];
+  for (int i = 0; i < QS_MAX_QUERIES; ++i) {
+    if (i < m) {
+      float* rec = record(a, D, b, h, split, i);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) rec[kRecPad + CPL * lane + c] = acc[i][c];
+    }
   }
 }
 
@@ -935,80 +909,64 @@ __global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgs 
 }
 
 // out[(b, i, h)] = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) over the splits s of (b, h),
-// M = max_s m_s.  256 threads: every split's (max, sum) is loaded at once, then the o vectors
-// are read as float4 chunks by 256 / (D/4) split phases in parallel and reduced through LDS.
+// M = max_s m_s.  256 threads in NP phases of D/4 threads: phase p merges the splits p, p + NP,
+// .. with an online log-sum-exp (all of its loads issued before the first merge), then the
+// phases are merged through LDS.
+__device__ __forceinline__ void lse_merge(float& m, float& l, float4& o, float m2, float l2,
+                                          float4 o2) {
+  const float mn = fmaxf(m, m2);
+  const float a1 = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+  const float a2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
+  m = mn;
+  l = l * a1 + l2 * a2;
+  o.x = o.x * a1 + o2.x * a2;
+  o.y = o.y * a1 + o2.y * a2;
+  o.z = o.z * a1 + o2.z * a2;
+  o.w = o.w * a1 + o2.w * a2;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
   constexpr int C4 = D / 4;        // float4 chunks of o
   constexpr int NP = 256 / C4;     // split phases
-  constexpr int SMAX = kMaxQuantSplits + kMaxTailItems;
-  __shared__ float wsh[SMAX];
-  __shared__ float4 part[NP][C4];
-  __shared__ float red[2][4];
+  __shared__ float4 po[NP][C4];
+  __shared__ float2 pml[NP];
   const int h = blockIdx.y;
   const int b = blockIdx.x / a.m;
   const int i = blockIdx.x % a.m;
   const int t = threadIdx.x;
-  const int lane = t & 63, wv = t >> 6;
+  const int c = t % C4, p = t / C4;
   const int ns = (a.qitem_base[b + 1] - a.qitem_base[b]) + (a.titem_base[b + 1] - a.titem_base[b]);
 
-  float mv[2], lv[2];
-  float mloc = -INFINITY;
+  float m = -INFINITY, l = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = p; s0 < ns; s0 += NP * 16) {
+    float2 ml[16];
+    float4 ov[16];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int s = t + 256 * k;
-    mv[k] = -INFINITY;
-    lv[k] = 0.f;
-    if (s < ns) {
-      const float* rec = record(a, D, b, h, s, i);
-      mv[k] = rec[0];
-      lv[k] = rec[1];
+    for (int u = 0; u < 16; ++u) {
+      const int s = s0 + NP * u;
+      const float* rec = record(a, D, b, h, s < ns ? s : 0, i);
+      ml[u] = *reinterpret_cast<const float2*>(rec);
+      ov[u] = reinterpret_cast<const float4*>(rec + kRecPad)[c];
+      if (s >= ns) {
+        ml[u] = make_float2(-INFINITY, 0.f);
+        ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
-    mloc = fmaxf(mloc, mv[k]);
-  }
-  mloc = wave_max_from(mloc, 1);
-  if (lane == 0) red[0][wv] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  float lloc = 0.f;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int s = t + 256 * k;
-    if (s < ns) {
-      const float w = mv[k] == -INFINITY ? 0.f : fast_exp2(mv[k] - M);
-      wsh[s] = w;
-      lloc += w * lv[k];
-    }
+    for (int u = 0; u < 16; ++u) lse_merge(m, l, o, ml[u].x, ml[u].y, ov[u]);
   }
-  lloc = wave_sum_from(lloc, 1);
-  if (lane == 0) red[1][wv] = lloc;
-  __syncthreads();
-  const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-
-  const int c = t % C4, p = t / C4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int s = p; s < ns; s += NP) {
-    const float4 o = reinterpret_cast<const float4*>(record(a, D, b, h, s, i) + kRecPad)[c];
-    const float w = wsh[s];
-    acc.x += w * o.x;
-    acc.y += w * o.y;
-    acc.z += w * o.z;
-    acc.w += w * o.w;
-  }
-  part[p][c] = acc;
+  po[p][c] = o;
+  if (c == 0) pml[p] = make_float2(m, l);
   __syncthreads();
   if (t < C4) {
-    float4 r = part[0][t];
-    for (int q = 1; q < NP; ++q) {
-      r.x += part[q][t].x;
-      r.y += part[q][t].y;
-      r.z += part[q][t].z;
-      r.w += part[q][t].w;
-    }
-    const float inv = 1.f / L;
+    float mm = pml[0].x, ll = pml[0].y;
+    float4 oo = po[0][t];
+    for (int q = 1; q < NP; ++q) lse_merge(mm, ll, oo, pml[q].x, pml[q].y, po[q][t]);
+    const float inv = 1.f / ll;
     float4* out = reinterpret_cast<float4*>(a.out + (((size_t)b * a.m + i) * a.H + h) * D);
-    out[t] = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    out[t] = make_float4(oo.x * inv, oo.y * inv, oo.z * inv, oo.w * inv);
   }
 }
 
