@@ -6,7 +6,8 @@ channels scaled x8.  One step is one speculation round over all layers:
   gamma = 6 draft steps (per layer: append 1 token, draft attention),
   per layer: rollback gamma, append gamma+1 target tokens, verify attention (7 queries),
   acceptance a ~ Bernoulli(0.9) until first reject, rollback gamma - a, then one flush call.
-Inputs are seeded synthetic fp16 tensors resident in HBM before timing starts.  After the timed
+Inputs are seeded synthetic fp16 tensors resident in HBM before timing starts.  HIP events time
+the draft and verify calls of one layer per timed step (rotating over the layers).  After the timed
 steps, a bulk flush (one G-token half of every layer and head in one launch) is timed on its own.
 
 Prints one JSON line: value = algorithmic HBM bytes of the step / step time (GB/s), with the
@@ -161,20 +162,25 @@ def main():
     ev = {"draft": [], "verify": []}
     step_bytes = []
 
+    # HIP events bracket the draft and verify calls of one layer per timed step (the layer
+    # rotates from step to step): recording them around every call would add their own cost to
+    # the step time.
     def run_step(s, timed):
         x = steps_in[s]
         nbytes = 0
+        ev_layer = (s - args.warmup) % L if timed else -1  # -1: no events in warmup
         for j in range(gamma):
             for layer in range(L):
                 cache.append(layer, x["dk"][j, layer], x["dv"][j, layer])
                 nq, nt, _ = cache.state(layer)
                 nbytes += append_bytes(1, H, D) + draft_bytes(int(nq[0]), int(nt[0]), H, D)
-                if timed:
+                rec = layer == ev_layer
+                if rec:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
                 cache.attend_draft(layer, x["qd"][j, layer], out=out_d)
-                if timed:
+                if rec:
                     e1.record(stream)
                     ev["draft"].append((e0, e1, draft_bytes(int(nq[0]), int(nt[0]), H, D)))
         for layer in range(L):
@@ -183,12 +189,13 @@ def main():
             nq, nt, _ = cache.state(layer)
             vb = verify_bytes(int(nq[0]), int(nt[0]), H, D, m)
             nbytes += append_bytes(m, H, D) + vb
-            if timed:
+            rec = layer == ev_layer
+            if rec:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
             cache.attend_verify(layer, x["qv"][layer], out=out_v)
-            if timed:
+            if rec:
                 e1.record(stream)
                 ev["verify"].append((e0, e1, vb))
             cache.rollback(layer, [gamma - accept[s]])

@@ -122,10 +122,11 @@ class Cache:
         if st != QS_OK:
             raise QsError(st, "qs_cache_create")
         self._h = h
+        self._destroy = lib().qs_cache_destroy  # held so that close() still works at shutdown
 
     def close(self):
         if getattr(self, "_h", None):
-            lib().qs_cache_destroy(self._h)
+            self._destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -18,7 +18,7 @@ namespace qs {
 hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st);
 hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st);
-int attention_slots(int D, bool draft);
+int attention_slots(int D, bool draft, int B);
 }  // namespace qs
 
 struct qs_cache {
@@ -200,7 +200,7 @@ static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, 
   const int D = cf.head_dim;
   qs::Seq seqs[QS_MAX_BATCH];
   for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
-  int slots = qs::attention_slots(D, draft);
+  int slots = qs::attention_slots(D, draft, cf.batch);
   if (slots <= 0) slots = kFallbackSlots;
   int tail_items = 0;
   for (int b = 0; b < cf.batch; ++b)

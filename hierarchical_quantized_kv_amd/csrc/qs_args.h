@@ -15,8 +15,8 @@ constexpr int kMaxTailItems = 2 * kGroup / kTailChunk;
 constexpr int kMaxQuantSplits = 256;  // quantized work items per (sequence, head), at most
 constexpr int kRecPad = 4;            // partial record = [max, sum, pad, pad, o[D]]
 
-// One attention call (draft or verify) on one layer.
-struct AttnArgs {
+// One attention call (draft or verify) on one layer: the fields that do not depend on the batch.
+struct AttnHeader {
   const uint8_t* uk;     // layer base of each section
   const uint8_t* lk;
   const uint8_t* uv;
@@ -35,23 +35,40 @@ struct AttnArgs {
   int32_t n_qitems_total, n_titems_total;
   float qscale;          // sm_scale * log2(e): scores are kept in the base-2 domain
   float draft_offset;    // 8 or 0 (draft only)
-  int32_t nq[QS_MAX_BATCH];         // quantized tokens per sequence
-  int32_t nt[QS_MAX_BATCH];         // tail tokens per sequence
-  int32_t head[QS_MAX_BATCH];       // ring slot of logical tail token 0
-  int32_t qitem_base[QS_MAX_BATCH + 1];  // prefix sum over b of quantized workers
-  int32_t titem_base[QS_MAX_BATCH + 1];  // prefix sum over b of tail items
 };
 
-struct AppendArgs {
+// Per-sequence bookkeeping for at most NB sequences.  The kernels are instantiated for a few
+// NB (1, 8, QS_MAX_BATCH) so that a small batch passes a small argument block: every launch
+// copies its argument block, and at NB = QS_MAX_BATCH (about 1.7 KB) that copy costs more
+// than a microsecond of launch latency.
+template <int NB>
+struct AttnArgsN : AttnHeader {
+  int32_t nq[NB];                // quantized tokens per sequence
+  int32_t nt[NB];                // tail tokens per sequence
+  int32_t head[NB];              // ring slot of logical tail token 0
+  int32_t qitem_base[NB + 1];    // prefix sum over b of quantized workers
+  int32_t titem_base[NB + 1];    // prefix sum over b of tail items
+};
+using AttnArgs = AttnArgsN<QS_MAX_BATCH>;
+
+struct AppendHeader {
   const uint16_t* k;     // [B][n_max][H][D]
   const uint16_t* v;
   uint16_t* tail_k;      // layer base [B][H][2G][D]
   uint16_t* tail_v;
   int32_t B, H, n_max;
-  int32_t n[QS_MAX_BATCH];      // tokens appended per sequence
-  int32_t start[QS_MAX_BATCH];  // logical position nt before the append
-  int32_t head[QS_MAX_BATCH];
 };
+
+template <int NB>
+struct AppendArgsN : AppendHeader {
+  int32_t n[NB];      // tokens appended per sequence
+  int32_t start[NB];  // logical position nt before the append
+  int32_t head[NB];
+};
+using AppendArgs = AppendArgsN<QS_MAX_BATCH>;
+
+// Batch bucket of the kernel instantiation that serves a batch of B sequences.
+inline int batch_bucket(int B) { return B <= 1 ? 1 : (B <= 8 ? 8 : QS_MAX_BATCH); }
 
 struct FlushArgs {
   uint8_t* uk;           // arena section bases (all layers)

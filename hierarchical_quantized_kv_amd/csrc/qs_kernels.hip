@@ -90,7 +90,8 @@ __device__ __forceinline__ float4 bldf4(rsrc_t r, uint32_t voff, uint32_t soff) 
 struct Streams {
   rsrc_t uk, lk, uv, lv, km, vm;
 };
-__device__ __forceinline__ Streams make_streams(const AttnArgs& a, size_t bh, int D) {
+template <class Args>
+__device__ __forceinline__ Streams make_streams(const Args& a, size_t bh, int D) {
   const uint32_t plane = (uint32_t)a.T * (uint32_t)(D / 2);  // bytes of one plane per (b, h)
   Streams st;
   st.uk = make_rsrc(a.uk + bh * plane, plane);
@@ -166,7 +167,8 @@ __device__ __forceinline__ float wave_sum_from(float x, int from) {
 }
 
 // Record of split `split`, query `i` of (b, h).
-__device__ __forceinline__ float* record(const AttnArgs& a, int D, int b, int h, int split, int i) {
+template <class Args>
+__device__ __forceinline__ float* record(const Args& a, int D, int b, int h, int split, int i) {
   return a.work + ((((size_t)b * a.H + h) * a.S + split) * a.m + i) * (size_t)(D + kRecPad);
 }
 
@@ -177,7 +179,8 @@ __device__ __forceinline__ float* record(const AttnArgs& a, int D, int b, int h,
 struct GroupStride {
   int first, step, ng;
 };
-__device__ __forceinline__ GroupStride worker_groups(const AttnArgs& a, int b, int item) {
+template <class Args>
+__device__ __forceinline__ GroupStride worker_groups(const Args& a, int b, int item) {
   return GroupStride{item, a.qitem_base[b + 1] - a.qitem_base[b], a.nq[b] / kGroup};
 }
 
@@ -315,8 +318,8 @@ struct DraftAcc {
 // current group has been consumed, so the next group's loads overlap this group's arithmetic.
 // (The prefetch is a template flag rather than a run-time test so that the number of loads in
 // flight at every wait is fixed.)
-template <int D, bool PF>
-__device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm, DraftBuf<D>& cur,
+template <int D, bool PF, class Args>
+__device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, DraftBuf<D>& cur,
                                             int gnext, float q0, float q1, DraftLds& L,
                                             DraftAcc<D>& st) {
   using S = DraftShape<D>;
@@ -410,8 +413,8 @@ __device__ __forceinline__ void draft_group(const AttnArgs& a, const Streams& sm
   if constexpr (PF) draft_load_v<D>(sm, gnext, cur);
 }
 
-template <int D>
-__device__ void draft_quant_item(const AttnArgs& a, int b, int h, int item, DraftLds& L) {
+template <int D, class Args>
+__device__ void draft_quant_item(const Args& a, int b, int h, int item, DraftLds& L) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
   const size_t bh = (size_t)b * a.H + h;
@@ -559,8 +562,8 @@ struct VerifyAcc {
 // One group of a verify worker, in two 64-token halves.  With PF the buffers are refilled with
 // group gn as each part of group gi is consumed (a template flag, so that the number of loads in
 // flight at every wait is fixed).
-template <int D, bool PF>
-__device__ __forceinline__ void verify_group(const AttnArgs& a, const Streams& sm, VerifyBuf<D>& buf,
+template <int D, bool PF, class Args>
+__device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, VerifyBuf<D>& buf,
                                              int gi, int gn, VerifyLds& L, VerifyAcc<D>& st) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
@@ -693,8 +696,8 @@ __device__ __forceinline__ void verify_group(const AttnArgs& a, const Streams& s
   }
 }
 
-template <int D>
-__device__ void verify_quant_item(const AttnArgs& a, int b, int h, int item, VerifyLds& L) {
+template <int D, class Args>
+__device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyLds& L) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
   const int j = lane & 15;   // query column
@@ -764,8 +767,8 @@ struct TailLds {
   float p[kTailChunk][QS_MAX_QUERIES];
 };
 
-template <int D>
-__device__ void tail_item(const AttnArgs& a, int b, int h, int chunk, int split, TailLds& L) {
+template <int D, class Args>
+__device__ void tail_item(const Args& a, int b, int h, int chunk, int split, TailLds& L) {
   const int lane = threadIdx.x;
   const int m = a.m;
   const int nt = a.nt[b];
@@ -877,14 +880,15 @@ __device__ void tail_item(const AttnArgs& a, int b, int h, int chunk, int split,
 // blockIdx.y is the head.  One wave per block.
 // ------------------------------------------------------------------------------------------
 
+template <int NB>
 __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
   int b = 0;
-  while (b + 1 < B && base[b + 1] <= idx) ++b;
+  while (b + 1 < NB && b + 1 < B && base[b + 1] <= idx) ++b;
   return b;
 }
 
-template <int D, bool DRAFT>
-__global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgs a) {
+template <int D, bool DRAFT, int NB>
+__global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgsN<NB> a) {
   using PassLds = typename std::conditional<DRAFT, DraftLds, VerifyLds>::type;
   __shared__ union {
     PassLds p;
@@ -893,13 +897,13 @@ __global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgs 
   const int h = blockIdx.y;
   const int x = blockIdx.x;
   if (x < a.n_titems_total) {
-    const int b = find_seq(a.titem_base, a.B, x);
+    const int b = find_seq<NB>(a.titem_base, a.B, x);
     const int chunk = x - a.titem_base[b];
     const int split = (a.qitem_base[b + 1] - a.qitem_base[b]) + chunk;
     tail_item<D>(a, b, h, chunk, split, lds.t);
   } else {
     const int y = x - a.n_titems_total;
-    const int b = find_seq(a.qitem_base, a.B, y);
+    const int b = find_seq<NB>(a.qitem_base, a.B, y);
     const int item = y - a.qitem_base[b];
     if constexpr (DRAFT)
       draft_quant_item<D>(a, b, h, item, lds.p);
@@ -925,8 +929,8 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float4& o, float m
   o.w = o.w * a1 + o2.w * a2;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
+template <int D, int NB>
+__global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB> a) {
   constexpr int C4 = D / 4;        // float4 chunks of o
   constexpr int NP = 256 / C4;     // split phases
   __shared__ float4 po[NP][C4];
@@ -974,8 +978,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgs a) {
 // Append: n[b] rows of fp16 K/V per sequence into the ring
 // ------------------------------------------------------------------------------------------
 
-template <int D>
-__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+template <int D, int NB>
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgsN<NB> a) {
   constexpr int CH = D / 8;  // 16-byte chunks per row
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = idx / CH, c = idx % CH;
@@ -1170,13 +1174,57 @@ __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
 // Launchers (called by the C ABI in qs_api.cpp)
 // ------------------------------------------------------------------------------------------
 
+// The first NB entries of the per-sequence arrays of a full-size argument block (the host fills
+// the full-size block; the launch passes only the bucket the batch needs).
+template <int NB>
+AttnArgsN<NB> narrow(const AttnArgs& f) {
+  AttnArgsN<NB> a;
+  static_cast<AttnHeader&>(a) = f;
+  for (int b = 0; b < NB; ++b) {
+    a.nq[b] = f.nq[b];
+    a.nt[b] = f.nt[b];
+    a.head[b] = f.head[b];
+  }
+  for (int b = 0; b <= NB; ++b) {
+    a.qitem_base[b] = f.qitem_base[b];
+    a.titem_base[b] = f.titem_base[b];
+  }
+  return a;
+}
+
+template <int NB>
+AppendArgsN<NB> narrow(const AppendArgs& f) {
+  AppendArgsN<NB> a;
+  static_cast<AppendHeader&>(a) = f;
+  for (int b = 0; b < NB; ++b) {
+    a.n[b] = f.n[b];
+    a.start[b] = f.start[b];
+    a.head[b] = f.head[b];
+  }
+  return a;
+}
+
+template <int D, int NB>
+void launch_append_n(const AppendArgs& f, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((append_kernel<D, NB>), grid, dim3(256), 0, st, narrow<NB>(f));
+}
+
+template <int D>
+void launch_append_d(const AppendArgs& a, dim3 grid, hipStream_t st) {
+  switch (batch_bucket(a.B)) {
+    case 1: launch_append_n<D, 1>(a, grid, st); break;
+    case 8: launch_append_n<D, 8>(a, grid, st); break;
+    default: launch_append_n<D, QS_MAX_BATCH>(a, grid, st); break;
+  }
+}
+
 hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st) {
   const long long rows = (long long)a.B * a.n_max * a.H;
   const long long threads = rows * (D / 8);
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256));
-  if (D == 128) hipLaunchKernelGGL(append_kernel<128>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(append_kernel<64>, grid, dim3(256), 0, st, a);
+  if (D == 128) launch_append_d<128>(a, grid, st);
+  else launch_append_d<64>(a, grid, st);
   return hipGetLastError();
 }
 
@@ -1188,39 +1236,58 @@ hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st)
   return hipGetLastError();
 }
 
+template <int D, bool DRAFT>
+const void* attn_fn(int bucket) {
+  switch (bucket) {
+    case 1: return (const void*)attn_kernel<D, DRAFT, 1>;
+    case 8: return (const void*)attn_kernel<D, DRAFT, 8>;
+    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH>;
+  }
+}
+
 // Work-item slots of one attention pass on the current device: compute units times the
 // one-wave workgroups of that kernel a compute unit holds at once (cached per device).
-int attention_slots(int D, bool draft) {
+int attention_slots(int D, bool draft, int B) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev][2][2];
+  static int cache[kMaxDev][2][2][3];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  int& slot = cache[dev][D == 128][draft];
+  const int bucket = batch_bucket(B);
+  int& slot = cache[dev][D == 128][draft][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
   if (slot > 0) return slot;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const void* fn = D == 128 ? (draft ? (const void*)attn_kernel<128, true> : (const void*)attn_kernel<128, false>)
-                            : (draft ? (const void*)attn_kernel<64, true> : (const void*)attn_kernel<64, false>);
+  const void* fn = D == 128 ? (draft ? attn_fn<128, true>(bucket) : attn_fn<128, false>(bucket))
+                            : (draft ? attn_fn<64, true>(bucket) : attn_fn<64, false>(bucket));
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
   slot = cus * per_cu;
   return slot;
 }
 
-hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st) {
+template <int D, bool DRAFT, int NB>
+hipError_t launch_attention_n(const AttnArgs& f, hipStream_t st) {
+  const AttnArgsN<NB> a = narrow<NB>(f);
   const dim3 grid(a.n_titems_total + a.n_qitems_total, a.H);
-  if (D == 128) {
-    if (draft) hipLaunchKernelGGL((attn_kernel<128, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<128, false>), grid, dim3(64), 0, st, a);
-  } else {
-    if (draft) hipLaunchKernelGGL((attn_kernel<64, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((attn_kernel<64, false>), grid, dim3(64), 0, st, a);
-  }
+  hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB>), grid, dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 cgrid(a.B * a.m, a.H);
-  if (D == 128) hipLaunchKernelGGL(combine_kernel<128>, cgrid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(combine_kernel<64>, cgrid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((combine_kernel<D, NB>), cgrid, dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <int D, bool DRAFT>
+hipError_t launch_attention_d(const AttnArgs& a, hipStream_t st) {
+  switch (batch_bucket(a.B)) {
+    case 1: return launch_attention_n<D, DRAFT, 1>(a, st);
+    case 8: return launch_attention_n<D, DRAFT, 8>(a, st);
+    default: return launch_attention_n<D, DRAFT, QS_MAX_BATCH>(a, st);
+  }
+}
+
+hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st) {
+  if (D == 128) return draft ? launch_attention_d<128, true>(a, st) : launch_attention_d<128, false>(a, st);
+  return draft ? launch_attention_d<64, true>(a, st) : launch_attention_d<64, false>(a, st);
 }
 
 }  // namespace qs

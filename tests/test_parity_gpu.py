@@ -155,6 +155,34 @@ def test_ragged_batch_and_many_chunks():
     ls.draft(0, qd(B, H, D, 503))
 
 
+@pytest.mark.parametrize("B", [1, 2, 8, 9, 64])
+def test_batch_buckets(B):
+    """The kernels are instantiated for batches of 1, up to 8 and up to 64 sequences; each size
+    here lands on a bucket edge.  Ragged lengths: tail-only, quantized-only and mixed sequences."""
+    log(f"case: batch bucket B={B}")
+    H, D = 2, 64
+    ls = Lockstep(1, B, H, D, 6 * G, 4, tag=f"bucket{B}")
+    lens = [(97 * b + 61) % (5 * G) + 1 for b in range(B)]
+    lens[-1] = 4 * G
+    n_max = max(lens)
+    k, v = kv(B, n_max, H, D, 700 + B)
+    pos = 0
+    while pos < n_max:
+        n = [max(0, min(G, L - pos)) for L in lens]
+        ls.append(0, k[:, pos:pos + G].contiguous(), v[:, pos:pos + G].contiguous(), n)
+        if pos + G <= n_max:
+            ls.flush(0)
+        pos += G
+    ls.check_planes(0)
+    ls.draft(0, qd(B, H, D, 701 + B))
+    k5, v5 = kv(B, 5, H, D, 704 + B)
+    ls.append(0, k5, v5)
+    ls.verify(0, qv(B, 5, H, D, 702 + B))
+    ls.rollback(0, [b % 5 for b in range(B)])
+    ls.check_state(0)
+    ls.draft(0, qd(B, H, D, 703 + B))
+
+
 def test_degenerate_groups():
     """Constant key channels and value rows (scale clamped to 1e-8, huge zero-point) and
     all-positive groups (zero-point below 0)."""
