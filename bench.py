@@ -39,8 +39,9 @@ KERNEL_SRC = os.path.join(ROOT, "hierarchical_quantized_kv_amd", "csrc", "qs_ker
 PROFILES = os.path.join(ROOT, "profiles")
 # HBM byte counters of rocprofv3, scaled by what they read for a plain device copy of known size
 # (FETCH_SIZE counts half of the bytes a copy kernel reads; WRITE_SIZE counts them all).
-KERNELS = {"draft": "attn_kernel<128, true>", "verify": "attn_kernel<128, false>",
-           "combine": "combine_kernel<128>", "flush": "flush_kernel<128>"}
+# (Batch 1: the kernels' batch-bucket template argument is 1.)
+KERNELS = {"draft": "attn_kernel<128, true, 1>", "verify": "attn_kernel<128, false, 1>",
+           "combine": "combine_kernel<128, 1>", "flush": "flush_kernel<128>"}
 
 CONFIGS = {
     3: dict(name="Llama-2-7B-32K-shaped full stack", layers=32, heads=32, D=128, ctx=32768,
@@ -280,9 +281,9 @@ def main():
         "flush_us_all_layers": round(f_us, 2),
         "flush_gbs": round(f_gbs, 1),
         "roofline": roof("draft", d_gbs, d_bytes, d_us,
-                         "draft call: attn_kernel<128, draft> + combine_kernel<128>"),
+                         "draft call: attn_kernel<128, true, 1> + combine_kernel<128, 1>"),
         "roofline_verify": roof("verify", v_gbs, v_bytes, v_us,
-                                "attn_kernel<128, verify> + combine_kernel<128>"),
+                                "attn_kernel<128, false, 1> + combine_kernel<128, 1>"),
         "roofline_flush": roof("flush", f_gbs, f_bytes, f_us,
                                f"flush_kernel<128>, {L} layers x {H} heads in one launch",
                                launches=L * H),

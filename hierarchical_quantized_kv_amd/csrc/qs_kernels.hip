@@ -880,6 +880,19 @@ __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, Tai
 // blockIdx.y is the head.  One wave per block.
 // ------------------------------------------------------------------------------------------
 
+// Workgroup i of a launch is dispatched to XCD i % kXcds.  The attention kernel renumbers its
+// workgroups so that each XCD receives one contiguous range of (head, item) blocks: the XCD then
+// streams whole heads, whose planes the address interleave spreads over every HBM channel.  With
+// the plain numbering, an XCD's share of a head is every kXcds-th item, and for some grid widths
+// those items all read groups with the same low address bits; the call time then varied by more
+// than 10% with the item count.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous_block(int i, int n) {
+  const int x = i % kXcds, k = i / kXcds;
+  const int per = n / kXcds, rem = n % kXcds;
+  return x * per + (x < rem ? x : rem) + k;  // XCD x holds blocks [start_x, start_x + count_x)
+}
+
 template <int NB>
 __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
   int b = 0;
@@ -894,8 +907,9 @@ __global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgsN
     PassLds p;
     TailLds t;
   } lds;
-  const int h = blockIdx.y;
-  const int x = blockIdx.x;
+  const int lb = xcd_contiguous_block(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const int h = lb / gridDim.x;
+  const int x = lb % gridDim.x;
   if (x < a.n_titems_total) {
     const int b = find_seq<NB>(a.titem_base, a.B, x);
     const int chunk = x - a.titem_base[b];
