@@ -949,9 +949,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB> a) {
   constexpr int NP = 256 / C4;     // split phases
   __shared__ float4 po[NP][C4];
   __shared__ float2 pml[NP];
-  const int h = blockIdx.y;
-  const int b = blockIdx.x / a.m;
-  const int i = blockIdx.x % a.m;
+  // same XCD-contiguous numbering as the attention kernel, so that a head's partials are merged
+  // on the XCD that wrote them
+  const int lb = xcd_contiguous_block(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const int h = lb / gridDim.x;
+  const int b = (lb % gridDim.x) / a.m;
+  const int i = (lb % gridDim.x) % a.m;
   const int t = threadIdx.x;
   const int c = t % C4, p = t / C4;
   const int ns = (a.qitem_base[b + 1] - a.qitem_base[b]) + (a.titem_base[b + 1] - a.titem_base[b]);
@@ -1173,10 +1176,17 @@ __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
     FlushKeyLds k;
     FlushValLds v;
   } lds;
-  const int h = blockIdx.x / (NK + NV);
-  const int blk = blockIdx.x % (NK + NV);
-  const int sel = blockIdx.y;
-  const int layer = a.layer0 + blockIdx.z;
+  // XCD-contiguous numbering: the NK + NV blocks of one (layer, sequence, head) write parts of
+  // the same plane lines, so they run on one XCD and its L2 merges the parts into whole lines
+  // before they reach HBM (blocks of one half spread over several XCDs made partial-line
+  // write-backs: about twice the written bytes and extra reads).
+  const int n = gridDim.x * gridDim.y * gridDim.z;
+  const int lb = xcd_contiguous_block((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, n);
+  const int bx = lb % gridDim.x, by = (lb / gridDim.x) % gridDim.y, bz = lb / (gridDim.x * gridDim.y);
+  const int h = bx / (NK + NV);
+  const int blk = bx % (NK + NV);
+  const int sel = by;
+  const int layer = a.layer0 + bz;
   const size_t lbh = ((size_t)layer * a.B + a.b[sel]) * a.H + h;
   if (blk < NK)
     flush_keys<D>(a, lbh, a.group[sel], a.head[sel], blk * kFlushSlice, lds.k);

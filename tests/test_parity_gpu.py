@@ -212,6 +212,7 @@ def test_peaky_softmax(gain):
     prefill(ls, 0, k, v)
     ls.draft(0, qd(1, H, D, 702, gain))
     ls.verify(0, qv(1, 7, H, D, 703, gain))
+    log(f"peaky{gain}: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
 def test_grid_exact_cache_verify_equals_fp16_attention():
