@@ -183,6 +183,26 @@ def test_batch_buckets(B):
     ls.draft(0, qd(B, H, D, 703 + B))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_max_queries_offset0_odd_heads(D):
+    """The largest verify (m = 16 queries, gamma_max 15), the draft constant off = 0, scales other
+    than 1, an odd head count (uneven XCD shares) and the second layer of a two-layer cache."""
+    log(f"case: m=16, off=0, 5 heads, D={D}")
+    H, B = 5, 2
+    ls = Lockstep(2, B, H, D, 8 * G, 15, draft_offset=0, tag=f"m16_{D}")
+    k, v = kv(B, 5 * G + 40, H, D, 800 + D)
+    prefill(ls, 1, k, v)
+    ls.check_planes(1)
+    ls.draft(1, qd(B, H, D, 801), sm_scale=1.25)
+    k16, v16 = kv(B, 16, H, D, 802 + D)
+    ls.append(1, k16, v16)
+    ls.verify(1, qv(B, 16, H, D, 803), sm_scale=0.8)
+    ls.rollback(1, [9, 16])
+    ls.check_state(1)
+    ls.draft(1, qd(B, H, D, 804), sm_scale=0.8)
+    log(f"m16_{D}: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
 def test_degenerate_groups():
     """Constant key channels and value rows (scale clamped to 1e-8, huge zero-point) and
     all-positive groups (zero-point below 0)."""
