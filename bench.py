@@ -219,11 +219,21 @@ def main():
 
     # Bulk flush (outside the timed steps): every layer gets G more tail tokens, then one
     # qs_flush(-1) quantizes one G-token half of every (layer, head) in a single launch.
+    # A flush is short next to the host time of the appends before it, so the GPU would sit idle
+    # at e0 and the interval would include the host's launch latency of the flush call.  A spin
+    # kernel of ~200 us ahead of e0 keeps the GPU busy until e0 and the flush are both queued.
     fk, fv = rnd(1, G, H, D), rnd(1, G, H, D)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    spin_cycles = int(1_000_000 * 200.0 / max(c0.elapsed_time(c1) * 1e3, 1.0))
     fl_ev = []
     for _ in range(args.flush_reps):
         for layer in range(L):
             cache.append(layer, fk, fv)
+        torch.cuda._sleep(spin_cycles)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
