@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention µs/step and HBM GB/s (draft & verify) at 32k/128k ctx"
 PEAK_HBM_GBS = 8000.0
+CPU_SAMPLE_HEADS = 16   # heads of layer 0 in the CPU-oracle sample
 G = 128
 KERNEL_SRC = os.path.join(ROOT, "hierarchical_quantized_kv_amd", "csrc", "qs_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -80,8 +81,9 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=sorted(CONFIGS))
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16,
-                    help="heads of layer 0 in the CPU-oracle sample")
+    ap.add_argument("--cpu-threads", type=int, default=16,
+                    help="host threads of the second, all-cores oracle timing (at most the "
+                         "host's CPU count)")
     ap.add_argument("--flush-reps", type=int, default=4,
                     help="timed all-layer flushes (each quantizes one G-token half per head)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -134,7 +136,7 @@ def main():
             cache.flush(layer)
         cache.append(layer, k[:, ctx:].contiguous(), v[:, ctx:].contiguous())
         if layer == 0 and not args.no_cpu_baseline:
-            hs = list(range(args.cpu_heads))
+            hs = list(range(CPU_SAMPLE_HEADS))
             cpu_inputs = (k[:, :, hs].cpu().numpy(), v[:, :, hs].cpu().numpy())
         del k, v
     torch.cuda.synchronize()
@@ -253,9 +255,14 @@ def main():
     v_us, v_gbs, v_bytes = summarize(ev["verify"])
     f_us, f_gbs, f_bytes = summarize(fl_ev)
 
+    read_ceiling = measure_read_ceiling(torch, stream)
+
     cpu = None
+    cpu_all = None
     if cpu_inputs is not None:
-        cpu = cpu_baseline(cpu_inputs, ctx, D, gamma, args.cpu_heads)
+        cpu = cpu_baseline(cpu_inputs, ctx, D, gamma, threads=1)
+        cpu_all = cpu_baseline(cpu_inputs, ctx, D, gamma,
+                               threads=max(1, min(args.cpu_threads, os.cpu_count() or 1)))
 
     traffic = load_traffic(args.config)
 
@@ -297,9 +304,45 @@ def main():
         "roofline_flush": roof("flush", f_gbs, f_bytes, f_us,
                                f"flush_kernel<128>, {L} layers x {H} heads in one launch",
                                launches=L * H),
+        "read_ceiling": read_ceiling,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_read_ceiling(torch, stream):
+    """The practical HBM read rate of this device: a plain grid-stride streaming-read kernel
+    (16-byte non-temporal loads, eight in flight per lane; libqs_readprobe.so) over 2 GiB, the
+    best of 4, 8 and 12 waves per compute unit, 20 timed launches each."""
+    import ctypes
+    path = os.path.join(ROOT, "hierarchical_quantized_kv_amd", "libqs_readprobe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built: run python -m hierarchical_quantized_kv_amd.build_lib")
+    lib = ctypes.CDLL(path)
+    lib.qs_probe_stream_read.restype = ctypes.c_int
+    lib.qs_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_float)]
+    buf = torch.zeros(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nbytes = buf.numel() // 16 * 16
+    best = None
+    for bpc in (1, 2, 3):
+        us = ctypes.c_float()
+        rc = lib.qs_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                      ctypes.c_void_p(sink.data_ptr()), bpc, 20,
+                                      ctypes.c_void_p(stream.cuda_stream), ctypes.byref(us))
+        if rc != 0:
+            raise RuntimeError(f"qs_probe_stream_read failed with HIP error {rc}")
+        gbs = nbytes / (us.value * 1e-6) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, bpc, us.value)
+    del buf
+    return {"gbs": round(best[0], 1), "frac_of_peak": round(best[0] / PEAK_HBM_GBS, 4),
+            "kernel": f"grid-stride streaming read, 16 B non-temporal loads, 8 in flight per lane, "
+                      f"{4 * best[1]} waves per CU",
+            "bytes_per_launch": nbytes, "avg_launch_us": round(best[2], 2)}
 
 
 def kernel_source_hash():
@@ -410,43 +453,79 @@ def write_traffic_summary(fetch_dir, write_dir, args):
     print(path)
 
 
-def cpu_baseline(inputs, ctx, D, gamma, n_heads):
-    """The CPU oracle, as it is, on a bounded sample of the same workload: layer 0 restricted to
-    its first n_heads heads, one speculation round (gamma draft calls, each after appending one
-    token, then rollback, gamma+1 appended tokens and one verify call) timed on one thread."""
-    import oracle
+def _oracle_round(k, v, ctx, D, gamma, heads, barrier=None):
+    """One speculation round of the CPU oracle over `heads` of the sample (gamma draft calls,
+    each after appending one token, then rollback, gamma+1 appended tokens and one verify
+    call); the prefill is not timed.  Returns (draft seconds, verify seconds)."""
     from oracle import OracleCache
     from hierarchical_quantized_kv_amd import synth
 
-    oracle.build(force=False)
-    k, v = inputs
-    H = n_heads
+    H = len(heads)
+    k, v = np.ascontiguousarray(k[:, :, heads]), np.ascontiguousarray(v[:, :, heads])
     c = OracleCache(1, 1, H, D, G, ctx + 16 * G, gamma)
     for pos in range(0, ctx, G):
         c.append(0, k[:, pos:pos + G], v[:, pos:pos + G])
         c.flush(0)
-    c.append(0, k[:, ctx:ctx + 64 - gamma - 1], v[:, ctx:ctx + 64 - gamma - 1])
     nt = 64 - gamma - 1
     m = gamma + 1
-    nb = 0
+    c.append(0, k[:, ctx:ctx + nt], v[:, ctx:ctx + nt])
+    qd = [np.ascontiguousarray(synth.queries_host(1, None, CPU_SAMPLE_HEADS, D, 10 + j)[:, heads])
+          for j in range(gamma)]
+    qv = np.ascontiguousarray(synth.queries_host(1, m, CPU_SAMPLE_HEADS, D, 2)[:, :, heads])
+    if barrier is not None:
+        barrier.wait()
     t0 = time.perf_counter()
     for j in range(gamma):
-        c.append(0, k[:, ctx + nt:ctx + nt + 1], v[:, ctx + nt:ctx + nt + 1])
-        c.attend_draft(0, synth.queries_host(1, None, H, D, 10 + j))
-        nb += draft_bytes(ctx, nt + 1, H, D)
+        c.append(0, k[:, ctx + nt + j:ctx + nt + j + 1], v[:, ctx + nt + j:ctx + nt + j + 1])
+        c.attend_draft(0, qd[j])
     t_d = time.perf_counter() - t0
     c.rollback(0, [gamma])
     c.append(0, k[:, ctx + nt:ctx + nt + m], v[:, ctx + nt:ctx + nt + m])
     t1 = time.perf_counter()
-    c.attend_verify(0, synth.queries_host(1, m, H, D, 2))
-    t_v = time.perf_counter() - t1
-    nb += verify_bytes(ctx, nt + m, H, D, m)
-    return {"value": round(nb / (t_d + t_v) / 1e9, 4), "unit": "GB/s", "cores": 1,
+    c.attend_verify(0, qv)
+    return t_d, time.perf_counter() - t1
+
+
+def cpu_baseline(inputs, ctx, D, gamma, threads=1):
+    """The CPU oracle, as it is, on a bounded sample of the same workload: layer 0 restricted to
+    its first CPU_SAMPLE_HEADS heads, one speculation round.  With threads > 1 the heads are
+    dealt to that many host threads (the oracle's C calls release the GIL), each running the
+    same round on its own oracle instance, started together; the wall time is the slowest."""
+    import threading
+
+    import oracle
+
+    oracle.build(force=False)
+    k, v = inputs
+    H = CPU_SAMPLE_HEADS
+    nt = 64 - gamma - 1
+    m = gamma + 1
+    nb = sum(draft_bytes(ctx, nt + 1 + j, H, D) for j in range(gamma))
+    nb_v = verify_bytes(ctx, nt + m, H, D, m)
+    groups = [list(range(t, H, threads)) for t in range(threads)]
+    res = [None] * threads
+    barrier = threading.Barrier(threads) if threads > 1 else None
+
+    def run(t):
+        res[t] = _oracle_round(k, v, ctx, D, gamma, groups[t], barrier)
+
+    if threads == 1:
+        run(0)
+    else:
+        ts = [threading.Thread(target=run, args=(t,)) for t in range(threads)]
+        for th in ts:
+            th.start()
+        for th in ts:
+            th.join()
+    t_d = max(r[0] for r in res)
+    t_v = max(r[1] for r in res)
+    how = "single-threaded" if threads == 1 else f"{threads} host threads, heads dealt round-robin"
+    return {"value": round((nb + nb_v) / (t_d + t_v) / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"layer 0, heads 0..{H - 1} of the same workload at ctx {ctx}: one "
                       f"speculation round = {gamma} draft calls ({t_d:.2f}s) + one {m}-query "
-                      f"verify call ({t_v:.2f}s), single-threaded fp64 oracle; GB/s = "
-                      f"algorithmic bytes of those calls / their time"}
+                      f"verify call ({t_v:.2f}s), fp64 oracle, {how}; GB/s = algorithmic bytes "
+                      f"of those calls / their time"}
 
 
 if __name__ == "__main__":

@@ -12,6 +12,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libquantspec.so")
 SOURCES = [os.path.join(CSRC, "qs_kernels.hip"), os.path.join(CSRC, "qs_api.cpp")]
+# Measurement helper for bench.py (the device's streaming-read ceiling); not part of the library.
+PROBE_LIB = os.path.join(HERE, "libqs_readprobe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "read_probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are disabled for all device code.
@@ -19,9 +22,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wal
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB) -> str:
+def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB,
+          sources: list[str] | None = None) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), *SOURCES, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *(extra or []), *(sources or SOURCES), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,5 +40,10 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB)
     return out
 
 
+def build_probe(verbose: bool = False) -> str:
+    return build(verbose=verbose, out=PROBE_LIB, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

@@ -6,11 +6,14 @@
 //                   upper / lower nibble planes, plus (scale, zero-point) metadata; one wave per
 //                   32-channel key slice or 32-token value slice
 //   attn_kernel     split-K attention work items of one pass:
-//                     draft quantized item : upper key / value planes only, VALU (v_dot2)
+//                     draft quantized item : upper key / value planes only, VALU (signed
+//                                            4-bit integer dot products)
 //                     verify quantized item: both planes, MFMA 16x16x32 f16
 //                     tail item            : up to 64 fp16 tail tokens, VALU, causal mask
 //                   each writes one log-sum-exp partial (max, sum, o[D]) per query
 //   combine_kernel  merges the partials of one (sequence, query, head)
+// The attention, combine and flush kernels number their workgroups XCD-contiguously (see
+// xcd_contiguous_block).
 //
 // Sources: QuantSpec Guide (aifetchly), "Hierarchical Quantizer with Bit-Packing" listing
 // (quantizer, unpack_for_draft, unpack_for_target); Pith review of arXiv:2502.10424, "What carries
@@ -47,16 +50,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t x) { return __builtin_bit_cast(f16x2, x); }
-__device__ __forceinline__ uint32_t as_u32(f16x2 x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
-// Power of two f such that every value weight of a group, at most 16 * smax (even tokens carry the
-// factor 16), scaled by f stays below 2^14: the fp16 hi/lo weights then keep full relative
-// precision instead of falling into the fp16 subnormal range for small softmax probabilities.
+// Power of two f such that every verify value weight of a group, p_t s_t <= smax (p_t <= 1),
+// scaled by f stays below 2^14: the fp16 hi/lo weights then keep full relative precision
+// instead of falling into the fp16 subnormal range for small softmax probabilities.
 __device__ __forceinline__ float weight_scale(float smax) {
   int e;
-  frexpf(16.f * smax, &e);  // 16 smax < 2^e
+  frexpf(smax, &e);  // smax < 2^e
   return ldexpf(1.f, 14 - e);
 }
 
