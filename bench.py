@@ -42,7 +42,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # (FETCH_SIZE counts half of the bytes a copy kernel reads; WRITE_SIZE counts them all).
 # (Batch 1: the kernels' batch-bucket template argument is 1.)
 KERNELS = {"draft": "attn_kernel<128, true, 1>", "verify": "attn_kernel<128, false, 1>",
-           "combine": "combine_kernel<128, 1>", "flush": "flush_kernel<128>"}
+           "combine": "combine_kernel<128, 1>", "flush": "flush_kernel<128>",
+           "prefill": "prefill_kernel<128>"}
 
 CONFIGS = {
     3: dict(name="Llama-2-7B-32K-shaped full stack", layers=32, heads=32, D=128, ctx=32768,
@@ -71,6 +72,12 @@ def flush_bytes(H, D):
 
 def append_bytes(n, H, D):
     return 2 * n * H * D * 2 * 2
+
+
+def prefill_bytes(n, H, D):
+    """One layer's prompt of n tokens: flush bytes for each whole group, append bytes for the
+    rest."""
+    return (n // G) * flush_bytes(H, D) + append_bytes(n % G, H, D)
 
 
 def main():
@@ -123,18 +130,35 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    stream = torch.cuda.current_stream()
+    # Short launches (a layer's prefill, the bulk flush) are timed behind a spin kernel of
+    # ~200 us: otherwise the GPU can sit idle when it reaches the first event and the interval
+    # would include the host's launch latency of the timed call.
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    spin_cycles = int(1_000_000 * 200.0 / max(c0.elapsed_time(c1) * 1e3, 1.0))
+
+    # Prefill ("quantize once"): each layer's ctx + 64-token prompt in one qs_prefill call (ctx / G
+    # groups quantized, 64 tokens to the tail), timed per layer.
     cache = Cache(L, 1, H, D, max_ctx, gamma)
     t0 = time.time()
     cpu_inputs = None
+    pf_ev = []
     for layer in range(L):
         out_ch = synth.outlier_channels(H, D, synth.seed_for(args.config, layer, "outlier"))
         k, v = synth.kv_device(torch, 1, ctx + 64, H, D,
                                synth.seed_for(args.config, layer, "k"),
                                synth.seed_for(args.config, layer, "v"), dev, outliers=out_ch)
-        for pos in range(0, ctx, G):
-            cache.append(layer, k[:, pos:pos + G], v[:, pos:pos + G])
-            cache.flush(layer)
-        cache.append(layer, k[:, ctx:].contiguous(), v[:, ctx:].contiguous())
+        torch.cuda._sleep(spin_cycles)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.prefill(layer, k, v)
+        e1.record(stream)
+        pf_ev.append((e0, e1, prefill_bytes(ctx + 64, H, D)))
         if layer == 0 and not args.no_cpu_baseline:
             hs = list(range(CPU_SAMPLE_HEADS))
             cpu_inputs = (k[:, :, hs].cpu().numpy(), v[:, :, hs].cpu().numpy())
@@ -160,7 +184,6 @@ def main():
             qv=rnd(L, 1, m, H, D, scale=1 / math.sqrt(D))))
     out_d = torch.empty((1, H, D), dtype=torch.float32, device=dev)
     out_v = torch.empty((1, m, H, D), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
 
     ev = {"draft": [], "verify": []}
     step_bytes = []
@@ -221,16 +244,8 @@ def main():
 
     # Bulk flush (outside the timed steps): every layer gets G more tail tokens, then one
     # qs_flush(-1) quantizes one G-token half of every (layer, head) in a single launch.
-    # A flush is short next to the host time of the appends before it, so the GPU would sit idle
-    # at e0 and the interval would include the host's launch latency of the flush call.  A spin
-    # kernel of ~200 us ahead of e0 keeps the GPU busy until e0 and the flush are both queued.
+    # (timed behind the spin kernel, like the prefill)
     fk, fv = rnd(1, G, H, D), rnd(1, G, H, D)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    torch.cuda._sleep(1_000_000)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    spin_cycles = int(1_000_000 * 200.0 / max(c0.elapsed_time(c1) * 1e3, 1.0))
     fl_ev = []
     for _ in range(args.flush_reps):
         for layer in range(L):
@@ -245,15 +260,24 @@ def main():
         fl_ev.append((e0, e1, L * flush_bytes(H, D)))
     torch.cuda.synchronize()
 
-    def summarize(events):
-        t = [a.elapsed_time(b) * 1e3 for a, b, _ in events]   # us
-        by = [n for _, _, n in events]
-        mean_us = float(np.mean(t))
-        return mean_us, float(np.mean(by)) / (mean_us * 1e-6) / 1e9, float(np.mean(by))
+    # Average over the sampled calls.  When the GPU has caught up with the host (short calls at
+    # 32k), an event interval can also hold a stall of the host thread (measured once: one
+    # sample of ~30 ms among 40 of ~38 us); samples above twice the median are left out, and
+    # the count of those is reported.
+    dropped = {}
 
-    d_us, d_gbs, d_bytes = summarize(ev["draft"])
-    v_us, v_gbs, v_bytes = summarize(ev["verify"])
-    f_us, f_gbs, f_bytes = summarize(fl_ev)
+    def summarize(events, kind):
+        t = np.array([a.elapsed_time(b) * 1e3 for a, b, _ in events])   # us
+        by = [n for _, _, n in events]
+        keep = t <= 2.0 * np.median(t)
+        dropped[kind] = int((~keep).sum())
+        avg_us = float(t[keep].mean())
+        return avg_us, float(np.mean(by)) / (avg_us * 1e-6) / 1e9, float(np.mean(by))
+
+    d_us, d_gbs, d_bytes = summarize(ev["draft"], "draft")
+    v_us, v_gbs, v_bytes = summarize(ev["verify"], "verify")
+    f_us, f_gbs, f_bytes = summarize(fl_ev, "flush")
+    p_us, p_gbs, p_bytes = summarize(pf_ev, "prefill")
 
     read_ceiling = measure_read_ceiling(torch, stream)
 
@@ -297,6 +321,8 @@ def main():
         "verify_gbs": round(v_gbs, 1),
         "flush_us_all_layers": round(f_us, 2),
         "flush_gbs": round(f_gbs, 1),
+        "prefill_us_per_layer": round(p_us, 2),
+        "prefill_gbs": round(p_gbs, 1),
         "roofline": roof("draft", d_gbs, d_bytes, d_us,
                          "draft call: attn_kernel<128, true, 1> + combine_kernel<128, 1>"),
         "roofline_verify": roof("verify", v_gbs, v_bytes, v_us,
@@ -304,6 +330,10 @@ def main():
         "roofline_flush": roof("flush", f_gbs, f_bytes, f_us,
                                f"flush_kernel<128>, {L} layers x {H} heads in one launch",
                                launches=L * H),
+        "roofline_prefill": roof("prefill", p_gbs, p_bytes, p_us,
+                                 f"prefill_kernel<128> + append_kernel<128, 1>: one layer's "
+                                 f"{ctx + 64}-token prompt, {H} heads"),
+        "samples_dropped": dropped,
         "read_ceiling": read_ceiling,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
@@ -365,7 +395,7 @@ def load_traffic(config):
     if not m or m.group(1) != kernel_source_hash():
         return None
     out = {}
-    for kind in ("draft", "verify", "flush"):
+    for kind in ("draft", "verify", "flush", "prefill"):
         mm = re.search(rf"traffic_{kind}_bytes: (\d+)", text)
         if mm:
             out[kind] = int(mm.group(1))
@@ -415,7 +445,7 @@ def write_traffic_summary(fetch_dir, write_dir, args):
         "",
         "```",
         f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
-        f"\"attn_kernel|combine_kernel|flush_kernel|copy\" -d {fetch_dir} -o run "
+        f"\"attn_kernel|combine_kernel|flush_kernel|prefill_kernel|copy\" -d {fetch_dir} -o run "
         f"--output-format csv -- python -u bench.py --config {args.config} --layers 2 --steps 1 "
         f"--warmup 0 --flush-reps 2 --no-cpu-baseline --calibration-copy-mib "
         f"{args.calibration_copy_mib}",
@@ -433,7 +463,7 @@ def write_traffic_summary(fetch_dir, write_dir, args):
         "|---|---|---|---|---|",
     ]
     out = {}
-    for kind in ("draft", "verify", "combine", "flush"):
+    for kind in ("draft", "verify", "combine", "flush", "prefill"):
         if kind not in fetch[2] or kind not in write[2]:
             continue
         rd, n = fetch[2][kind]

@@ -20,8 +20,8 @@ STATUS = {0: "QS_OK", 1: "QS_ERR_INVALID_ARG", 2: "QS_ERR_CAPACITY", 3: "QS_ERR_
 
 # Every symbol include/quantspec.h declares.
 EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_destroy",
-           "qs_append", "qs_rollback", "qs_flush", "qs_attend_draft", "qs_attend_verify",
-           "qs_get_state", "qs_last_error")
+           "qs_append", "qs_prefill", "qs_rollback", "qs_flush", "qs_attend_draft",
+           "qs_attend_verify", "qs_get_state", "qs_last_error")
 
 
 class QsConfig(ctypes.Structure):
@@ -63,6 +63,7 @@ def lib():
                                       ctypes.POINTER(P)]
         L.qs_cache_destroy.argtypes = [P]
         L.qs_append.argtypes = [P, I32, P, P, I32, PI, P]
+        L.qs_prefill.argtypes = [P, I32, P, P, I32, PI, P]
         L.qs_rollback.argtypes = [P, I32, PI]
         L.qs_flush.argtypes = [P, I32, I32, P, PI]
         L.qs_attend_draft.argtypes = [P, I32, P, F, P, P]
@@ -152,6 +153,16 @@ class Cache:
         self._check(lib().qs_append(self._h, layer, self._dev(k, torch.float16, "k"),
                                     self._dev(v, torch.float16, "v"), k.shape[1], _ptr_i32(nn),
                                     self._stream(stream)), "qs_append")
+
+    def prefill(self, layer, k, v, n=None, stream=None):
+        """Bulk "quantize once" of a prompt: k, v fp16 [B][n_max][H][D]."""
+        torch = self.torch
+        assert k.shape == v.shape and k.dim() == 4 and k.shape[0] == self.B
+        assert tuple(k.shape[2:]) == (self.H, self.D)
+        nn = _i32(n, self.B)
+        self._check(lib().qs_prefill(self._h, layer, self._dev(k, torch.float16, "k"),
+                                     self._dev(v, torch.float16, "v"), k.shape[1], _ptr_i32(nn),
+                                     self._stream(stream)), "qs_prefill")
 
     def rollback(self, layer, n_drop):
         nd = _i32(n_drop, self.B)

@@ -17,6 +17,7 @@
 namespace qs {
 hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st);
 hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st);
 int attention_slots(int D, bool draft, int B);
 }  // namespace qs
@@ -103,6 +104,7 @@ qs_status qs_append(qs_cache* c, int32_t layer, const void* d_k, const void* d_v
   a.B = cf.batch;
   a.H = cf.n_heads;
   a.n_max = n_max;
+  a.n_rows = n_max;
   int total = 0;
   for (int b = 0; b < cf.batch; ++b) {
     a.n[b] = n[b];
@@ -115,6 +117,71 @@ qs_status qs_append(qs_cache* c, int32_t layer, const void* d_k, const void* d_v
     if (e != hipSuccess) return device_fail(c, e, "append launch");
   }
   c->st.apply_append(layer, n);
+  c->err.clear();
+  return QS_OK;
+}
+
+qs_status qs_prefill(qs_cache* c, int32_t layer, const void* d_k, const void* d_v, int32_t n_max,
+                     const int32_t* h_n, void* stream) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!d_k || !d_v) return fail(c, QS_ERR_INVALID_ARG, "null k or v");
+  const qs_config& cf = c->cfg;
+  int32_t n[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) n[b] = h_n ? h_n[b] : n_max;
+  std::string err;
+  qs_status s = c->st.check_prefill(layer, n_max, n, &err);
+  if (s != QS_OK) return fail(c, s, err);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // whole groups: quantized straight from the prompt
+  qs::PrefillArgs p{};
+  p.uk = c->arena + c->lay.uk;
+  p.lk = c->arena + c->lay.lk;
+  p.uv = c->arena + c->lay.uv;
+  p.lv = c->arena + c->lay.lv;
+  p.kmeta = reinterpret_cast<float*>(c->arena + c->lay.kmeta);
+  p.vmeta = reinterpret_cast<float*>(c->arena + c->lay.vmeta);
+  p.k = static_cast<const uint16_t*>(d_k);
+  p.v = static_cast<const uint16_t*>(d_v);
+  p.B = cf.batch;
+  p.H = cf.n_heads;
+  p.T = cf.max_ctx;
+  p.NG = cf.max_ctx / cf.group;
+  p.layer = layer;
+  p.n_max = n_max;
+  int max_groups = 0, rest = 0;
+  for (int b = 0; b < cf.batch; ++b) {
+    p.groups[b] = n[b] / cf.group;
+    p.group0[b] = c->st.at(layer, b).nq / cf.group;
+    if (p.groups[b] > max_groups) max_groups = p.groups[b];
+    rest += n[b] % cf.group;
+  }
+  hipError_t e = qs::launch_prefill(p, cf.head_dim, max_groups, st);
+  if (e != hipSuccess) return device_fail(c, e, "prefill launch");
+  // the rest of each prompt: into the ring, where the equivalent append / flush sequence leaves
+  // it (the ring head toggles once per quantized group; the tail was empty)
+  if (rest > 0) {
+    qs::AppendArgs a{};
+    a.k = p.k;
+    a.v = p.v;
+    const size_t tail_lbh = (size_t)2 * cf.group * cf.head_dim * 2;
+    a.tail_k = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_k + layer_off(c, tail_lbh, layer));
+    a.tail_v = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_v + layer_off(c, tail_lbh, layer));
+    a.B = cf.batch;
+    a.H = cf.n_heads;
+    a.n_max = n_max;
+    a.n_rows = 0;
+    for (int b = 0; b < cf.batch; ++b) {
+      const qs::Seq& q = c->st.at(layer, b);
+      if (n[b] % cf.group > a.n_rows) a.n_rows = n[b] % cf.group;
+      a.n[b] = n[b] % cf.group;
+      a.start[b] = q.nt;  // 0 whenever n[b] > 0
+      a.head[b] = (p.groups[b] & 1) ? (q.head ^ cf.group) : q.head;
+      a.src0[b] = p.groups[b] * cf.group;
+    }
+    e = qs::launch_append(a, cf.head_dim, st);
+    if (e != hipSuccess) return device_fail(c, e, "prefill tail launch");
+  }
+  c->st.apply_prefill(layer, n);
   c->err.clear();
   return QS_OK;
 }

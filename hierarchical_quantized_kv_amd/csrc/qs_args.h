@@ -57,6 +57,7 @@ struct AppendHeader {
   uint16_t* tail_k;      // layer base [B][H][2G][D]
   uint16_t* tail_v;
   int32_t B, H, n_max;
+  int32_t n_rows;        // tokens per sequence the grid covers (n_max, or a prefill's longest rest)
 };
 
 template <int NB>
@@ -64,11 +65,29 @@ struct AppendArgsN : AppendHeader {
   int32_t n[NB];      // tokens appended per sequence
   int32_t start[NB];  // logical position nt before the append
   int32_t head[NB];
+  int32_t src0[NB];   // first source token of the sequence in k / v (0 but for a prefill's rest)
 };
 using AppendArgs = AppendArgsN<QS_MAX_BATCH>;
 
 // Batch bucket of the kernel instantiation that serves a batch of B sequences.
 inline int batch_bucket(int B) { return B <= 1 ? 1 : (B <= 8 ? 8 : QS_MAX_BATCH); }
+
+// Bulk prefill of one layer: whole G-token groups of a prompt quantized straight from the
+// caller's K / V (the rest of each prompt goes to the tail through the append kernel).
+struct PrefillArgs {
+  uint8_t* uk;           // arena section bases (all layers)
+  uint8_t* lk;
+  uint8_t* uv;
+  uint8_t* lv;
+  float* kmeta;
+  float* vmeta;
+  const uint16_t* k;     // prompt [B][n_max][H][D]
+  const uint16_t* v;
+  int32_t B, H, T, NG;
+  int32_t layer, n_max;
+  int32_t groups[QS_MAX_BATCH];  // whole groups of each sequence's prompt
+  int32_t group0[QS_MAX_BATCH];  // quantized-tier group index of the first of them (nq / G)
+};
 
 struct FlushArgs {
   uint8_t* uk;           // arena section bases (all layers)

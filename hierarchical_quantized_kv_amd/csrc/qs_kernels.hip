@@ -1003,12 +1003,12 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgsN<NB> a) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = idx / CH, c = idx % CH;
   const int h = row % a.H;
-  const int i = (row / a.H) % a.n_max;
-  const int b = row / (a.H * a.n_max);
+  const int i = (row / a.H) % a.n_rows;
+  const int b = row / (a.H * a.n_rows);
   if (b >= a.B || i >= a.n[b]) return;
   const int ring = 2 * kGroup;
   const int slot = (a.head[b] + a.start[b] + i) % ring;
-  const size_t src = (((size_t)b * a.n_max + i) * a.H + h) * D + 8 * c;
+  const size_t src = (((size_t)b * a.n_max + a.src0[b] + i) * a.H + h) * D + 8 * c;
   const size_t dst = (((size_t)b * a.H + h) * ring + slot) * D + 8 * c;
   *reinterpret_cast<uint4*>(a.tail_k + dst) = ld16(a.k + src);
   *reinterpret_cast<uint4*>(a.tail_v + dst) = ld16(a.v + src);
@@ -1057,21 +1057,22 @@ struct FlushValLds {
   uint8_t code[kFlushSlice][128 + 4];          // codes, token-major (padded rows)
 };
 
-// Key block: channels c0 .. c0+31 of the G tokens of ring half `head`.
-template <int D>
-__device__ void flush_keys(const FlushArgs& a, size_t lbh, int grp, int head, int c0,
-                           FlushKeyLds& L) {
+// Key block: channels c0 .. c0+31 of the G fp16 key rows at ksrc (token t at ksrc + t * stride),
+// into group grp of the quantized tier of (layer, sequence, head) lbh.
+template <int D, class Args>
+__device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* ksrc, size_t stride,
+                           int c0, FlushKeyLds& L) {
 #pragma clang fp contract(off)
   constexpr int G = kGroup;
   const int lane = threadIdx.x;
-  const uint16_t* src = a.tail_k + (lbh * (2 * G) + head) * D + c0;
+  const uint16_t* src = ksrc + c0;
   // lane holds tokens 2 lane, 2 lane + 1: 32 channels each
   uint32_t w[2][kFlushSlice / 2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int k = 0; k < kFlushSlice / 8; ++k) {
-      const uint4 v = ld16(src + (size_t)(2 * lane + r) * D + 8 * k);
+      const uint4 v = ld16(src + (size_t)(2 * lane + r) * stride + 8 * k);
       w[r][4 * k] = v.x; w[r][4 * k + 1] = v.y; w[r][4 * k + 2] = v.z; w[r][4 * k + 3] = v.w;
     }
 #pragma unroll
@@ -1130,15 +1131,15 @@ __device__ void flush_keys(const FlushArgs& a, size_t lbh, int grp, int head, in
   }
 }
 
-// Value block: tokens t0 .. t0+31 of ring half `head`, all D channels.
-template <int D>
-__device__ void flush_values(const FlushArgs& a, size_t lbh, int grp, int head, int t0,
-                             FlushValLds& L) {
+// Value block: tokens t0 .. t0+31 of the G fp16 value rows at vsrc, all D channels.
+template <int D, class Args>
+__device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t* vsrc,
+                             size_t stride, int t0, FlushValLds& L) {
 #pragma clang fp contract(off)
   constexpr int G = kGroup, HALF = D / 2;
   const int lane = threadIdx.x;
   const int tk = lane >> 1, hf = lane & 1;  // token t0 + tk, channels hf*D/2 ..
-  const uint16_t* src = a.tail_v + (lbh * (2 * G) + head + t0 + tk) * D + hf * HALF;
+  const uint16_t* src = vsrc + (size_t)(t0 + tk) * stride + hf * HALF;
   uint32_t w[HALF / 2];
 #pragma unroll
   for (int k = 0; k < HALF / 8; ++k) {
@@ -1207,10 +1208,36 @@ __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
   const int sel = by;
   const int layer = a.layer0 + bz;
   const size_t lbh = ((size_t)layer * a.B + a.b[sel]) * a.H + h;
+  const size_t ring0 = (lbh * (2 * kGroup) + a.head[sel]) * D;  // oldest ring half, token-major
   if (blk < NK)
-    flush_keys<D>(a, lbh, a.group[sel], a.head[sel], blk * kFlushSlice, lds.k);
+    flush_keys<D>(a, lbh, a.group[sel], a.tail_k + ring0, D, blk * kFlushSlice, lds.k);
   else
-    flush_values<D>(a, lbh, a.group[sel], a.head[sel], (blk - NK) * kFlushSlice, lds.v);
+    flush_values<D>(a, lbh, a.group[sel], a.tail_v + ring0, D, (blk - NK) * kFlushSlice, lds.v);
+}
+
+// Prefill: group g of sequence b's prompt (tokens g*G .. g*G+G-1 of k / v [B][n_max][H][D]) into
+// quantized group group0[b] + g, with the flush's blocks and arithmetic.
+// grid: x = head * (D/32 + G/32) + block, y = prompt group, z = sequence
+template <int D>
+__global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
+  constexpr int NK = D / kFlushSlice, NV = kGroup / kFlushSlice;
+  __shared__ union {
+    FlushKeyLds k;
+    FlushValLds v;
+  } lds;
+  const int n = gridDim.x * gridDim.y * gridDim.z;
+  const int lb = xcd_contiguous_block((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, n);
+  const int bx = lb % gridDim.x, g = (lb / gridDim.x) % gridDim.y, b = lb / (gridDim.x * gridDim.y);
+  if (g >= a.groups[b]) return;
+  const int h = bx / (NK + NV);
+  const int blk = bx % (NK + NV);
+  const size_t lbh = ((size_t)a.layer * a.B + b) * a.H + h;
+  const size_t stride = (size_t)a.H * D;
+  const size_t src0 = (((size_t)b * a.n_max + (size_t)g * kGroup) * a.H + h) * D;
+  if (blk < NK)
+    flush_keys<D>(a, lbh, a.group0[b] + g, a.k + src0, stride, blk * kFlushSlice, lds.k);
+  else
+    flush_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, (blk - NK) * kFlushSlice, lds.v);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1243,6 +1270,7 @@ AppendArgsN<NB> narrow(const AppendArgs& f) {
     a.n[b] = f.n[b];
     a.start[b] = f.start[b];
     a.head[b] = f.head[b];
+    a.src0[b] = f.src0[b];
   }
   return a;
 }
@@ -1262,12 +1290,21 @@ void launch_append_d(const AppendArgs& a, dim3 grid, hipStream_t st) {
 }
 
 hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st) {
-  const long long rows = (long long)a.B * a.n_max * a.H;
+  const long long rows = (long long)a.B * a.n_rows * a.H;
   const long long threads = rows * (D / 8);
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (D == 128) launch_append_d<128>(a, grid, st);
   else launch_append_d<64>(a, grid, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream_t st) {
+  if (max_groups <= 0) return hipSuccess;
+  const int per_head = D / kFlushSlice + kGroup / kFlushSlice;
+  const dim3 grid(a.H * per_head, max_groups, a.B);
+  if (D == 128) hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -151,6 +151,38 @@ class State {
     for (int b = 0; b < cfg_.batch; ++b) at(layer, b).nt += n[b];
   }
 
+  // n: prompt tokens per sequence.  A prompt is placed after the quantized tier, so a sequence
+  // that receives one must have an empty tail (its tokens would otherwise be older).
+  qs_status check_prefill(int layer, int n_max, const int32_t* n, std::string* err) const {
+    qs_status st = check_layer(layer, false, err);
+    if (st != QS_OK) return st;
+    if (n_max < 0) { *err = "n_max must be >= 0"; return QS_ERR_INVALID_ARG; }
+    if (n_max / cfg_.group > 65535) { *err = "n_max / G must be <= 65535"; return QS_ERR_INVALID_ARG; }
+    for (int b = 0; b < cfg_.batch; ++b) {
+      if (n[b] < 0 || n[b] > n_max) { *err = "n[b] must be in 0..n_max"; return QS_ERR_INVALID_ARG; }
+      if (n[b] == 0) continue;
+      if (at(layer, b).nt != 0) {
+        *err = "prefill needs an empty tail (flush or roll back first)";
+        return QS_ERR_STATE;
+      }
+      if ((long long)at(layer, b).nq + (long long)(n[b] / cfg_.group) * cfg_.group > cfg_.max_ctx) {
+        *err = "prefill would exceed max_ctx";
+        return QS_ERR_CAPACITY;
+      }
+    }
+    return QS_OK;
+  }
+  // The same counters as append(G) + flush repeated n / G times, then append(n mod G).
+  void apply_prefill(int layer, const int32_t* n) {
+    for (int b = 0; b < cfg_.batch; ++b) {
+      Seq& s = at(layer, b);
+      const int groups = n[b] / cfg_.group;
+      s.nq += groups * cfg_.group;
+      if (groups & 1) s.head ^= cfg_.group;
+      s.nt += n[b] % cfg_.group;
+    }
+  }
+
   qs_status check_rollback(int layer, const int32_t* drop, std::string* err) const {
     qs_status st = check_layer(layer, true, err);
     if (st != QS_OK || !drop) return st;

@@ -56,6 +56,7 @@ def lib():
         L.orc_destroy.argtypes = [P]
         L.orc_destroy.restype = None
         L.orc_append.argtypes = [P, i, P, P, i, P]
+        L.orc_prefill.argtypes = [P, i, P, P, i, P]
         L.orc_rollback.argtypes = [P, i, P]
         L.orc_flush.argtypes = [P, i, i, P]
         L.orc_attend_draft.argtypes = [P, i, P, ctypes.c_double, P]
@@ -64,7 +65,7 @@ def lib():
         L.orc_read_codes.argtypes = [P, i, i, i, i, P]
         L.orc_read_meta.argtypes = [P, i, i, i, P, P]
         L.orc_export_layer.argtypes = [P, i, P, P, P, P, P, P, P, P]
-        for f in ("orc_append", "orc_rollback", "orc_flush", "orc_attend_draft",
+        for f in ("orc_append", "orc_prefill", "orc_rollback", "orc_flush", "orc_attend_draft",
                   "orc_attend_verify", "orc_get_state", "orc_read_codes", "orc_read_meta",
                   "orc_export_layer"):
             getattr(L, f).restype = i
@@ -147,6 +148,13 @@ class OracleCache:
         assert k.shape == v.shape and k.shape[0] == self.B and k.shape[2:] == (self.H, self.D)
         self._check(lib().orc_append(self._h, layer, _ptr(k), _ptr(v), k.shape[1],
                                      _ptr(_i32(n))), "append")
+
+    def prefill(self, layer, k, v, n=None):
+        k = _bits16(k)
+        v = _bits16(v)
+        assert k.shape == v.shape and k.shape[0] == self.B and k.shape[2:] == (self.H, self.D)
+        self._check(lib().orc_prefill(self._h, layer, _ptr(k), _ptr(v), k.shape[1],
+                                      _ptr(_i32(n))), "prefill")
 
     def rollback(self, layer, n_drop):
         self._check(lib().orc_rollback(self._h, layer, _ptr(_i32(n_drop))), "rollback")

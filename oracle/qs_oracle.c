@@ -152,6 +152,23 @@ static int slot_of(const orc_cache* c, int l, int b, int i) {
   return (c->head[l * c->B + b] + i) % (2 * c->G);
 }
 
+/* Tokens first .. first+count-1 of sequence b of k, v ([B][n_max][H][D]) to the back of the
+ * full-precision buffer of (l, b). */
+static void push_tokens(orc_cache* c, int l, int b, const uint16_t* k, const uint16_t* v,
+                        int n_max, int first, int count) {
+  int* nt = &c->nt[l * c->B + b];
+  for (int i = 0; i < count; ++i) {
+    int slot = slot_of(c, l, b, *nt + i);
+    for (int h = 0; h < c->H; ++h) {
+      const size_t src = (((size_t)b * n_max + first + i) * c->H + h) * c->D;
+      const size_t dst = (lbh(c, l, b, h) * 2 * c->G + slot) * c->D;
+      memcpy(&c->tk[dst], &k[src], (size_t)c->D * sizeof(uint16_t));
+      memcpy(&c->tv[dst], &v[src], (size_t)c->D * sizeof(uint16_t));
+    }
+  }
+  *nt += count;
+}
+
 /* New tokens go to the back of the full-precision buffer, unquantized ([G]
  * append_speculative_token; [R] "What carries the argument"). */
 int orc_append(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, int n_max,
@@ -162,20 +179,7 @@ int orc_append(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, in
     if (nb < 0 || nb > n_max) return 1;
     if (c->nt[layer * c->B + b] + nb > 2 * c->G) return 2;
   }
-  for (int b = 0; b < c->B; ++b) {
-    int nb = n ? n[b] : n_max;
-    int* nt = &c->nt[layer * c->B + b];
-    for (int i = 0; i < nb; ++i) {
-      int slot = slot_of(c, layer, b, *nt + i);
-      for (int h = 0; h < c->H; ++h) {
-        const size_t src = (((size_t)b * n_max + i) * c->H + h) * c->D;
-        const size_t dst = (lbh(c, layer, b, h) * 2 * c->G + slot) * c->D;
-        memcpy(&c->tk[dst], &k[src], (size_t)c->D * sizeof(uint16_t));
-        memcpy(&c->tv[dst], &v[src], (size_t)c->D * sizeof(uint16_t));
-      }
-    }
-    *nt += nb;
-  }
+  for (int b = 0; b < c->B; ++b) push_tokens(c, layer, b, k, v, n_max, 0, n ? n[b] : n_max);
   return 0;
 }
 
@@ -219,6 +223,34 @@ static void flush_one(orc_cache* c, int l, int b) {
   c->nq[l * c->B + b] += G;
   c->nt[l * c->B + b] -= G;
   c->head[l * c->B + b] = (head + G) % (2 * G);
+}
+
+/* "Quantize once": the prompt of sequence b (n_b tokens of k, v [B][n_max][H][D]) enters the
+ * cache G tokens at a time, each group pushed through the full-precision buffer and quantized
+ * once as it leaves ([G] "Core Architectural Blueprint" figure; "Periodic Group Quantization");
+ * the n_b mod G remaining tokens stay in the buffer.  A prompt needs an empty buffer (its
+ * tokens would otherwise come after younger ones).  Every sequence is checked first: 1 for a
+ * bad argument, 3 for a non-empty buffer, 2 for a prompt past the capacity T. */
+int orc_prefill(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, int n_max,
+                const int* n) {
+  if (!c || layer < 0 || layer >= c->L || !k || !v || n_max < 0) return 1;
+  for (int b = 0; b < c->B; ++b) {
+    int nb = n ? n[b] : n_max;
+    if (nb < 0 || nb > n_max) return 1;
+    if (nb == 0) continue;
+    if (c->nt[layer * c->B + b] != 0) return 3;
+    if (c->nq[layer * c->B + b] + (nb / c->G) * c->G > c->T) return 2;
+  }
+  for (int b = 0; b < c->B; ++b) {
+    int nb = n ? n[b] : n_max;
+    int g = 0;
+    for (; (g + 1) * c->G <= nb; ++g) {
+      push_tokens(c, layer, b, k, v, n_max, g * c->G, c->G);
+      flush_one(c, layer, b);
+    }
+    push_tokens(c, layer, b, k, v, n_max, g * c->G, nb - g * c->G);
+  }
+  return 0;
 }
 
 int orc_flush(orc_cache* c, int layer, int min_tail, int* flushed) {

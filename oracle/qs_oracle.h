@@ -53,6 +53,10 @@ void orc_destroy(orc_cache* c);
 /* k, v: fp16 bits [B][n_max][H][D]; n: [B] or NULL (= n_max). */
 int orc_append(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, int n_max,
                const int* n);
+/* Prompt of n[b] tokens per sequence (k, v as for append): whole groups quantized through the
+ * buffer, the rest left in it; needs an empty buffer for every sequence with n[b] > 0. */
+int orc_prefill(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, int n_max,
+                const int* n);
 /* layer -1 = every layer; n_drop: [B] or NULL. */
 int orc_rollback(orc_cache* c, int layer, const int* n_drop);
 /* layer -1 = every layer; flushed: [B] or NULL. */

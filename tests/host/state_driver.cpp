@@ -4,6 +4,7 @@
 //
 //   create L B H D G T gamma off
 //   append layer n_max n_0 .. n_{B-1}
+//   prefill layer n_max n_0 .. n_{B-1}
 //   rollback layer d_0 .. d_{B-1}
 //   flush layer min_tail
 //   attend layer m draft(0|1)
@@ -42,6 +43,13 @@ int main() {
       for (int b = 0; b < cfg.batch; ++b) in >> n[b];
       status = st.check_append(layer, n_max, n, &err);
       if (status == QS_OK) st.apply_append(layer, n);
+    } else if (op == "prefill") {
+      int layer, n_max;
+      in >> layer >> n_max;
+      int32_t n[QS_MAX_BATCH];
+      for (int b = 0; b < cfg.batch; ++b) in >> n[b];
+      status = st.check_prefill(layer, n_max, n, &err);
+      if (status == QS_OK) st.apply_prefill(layer, n);
     } else if (op == "rollback") {
       int layer;
       in >> layer;

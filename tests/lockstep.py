@@ -49,6 +49,11 @@ class Lockstep:
         if layer in self.orc:
             self.orc[layer].append(0, self._host_heads(k, 2), self._host_heads(v, 2), n)
 
+    def prefill(self, layer, k, v, n=None):
+        self.gpu.prefill(layer, k, v, n)
+        if layer in self.orc:
+            self.orc[layer].prefill(0, self._host_heads(k, 2), self._host_heads(v, 2), n)
+
     def rollback(self, layer, n_drop):
         self.gpu.rollback(layer, n_drop)
         for l in ([layer] if layer >= 0 else self.layers):

@@ -113,6 +113,15 @@ def test_validation_before_any_launch(lib):
     assert lib.qs_append(h, 0, P, P, 4, arr(1, 5, 0), None) == binding.QS_ERR_INVALID_ARG
     assert lib.qs_append(h, 0, P, P, 2 * G + 1, None, None) == binding.QS_ERR_CAPACITY
     assert b"overflow" in lib.qs_last_error(h)
+    # prefill: bad layer, null tensors, n > n_max, past max_ctx, n_max / G too large; n = 0 is a
+    # no-op that launches nothing
+    assert lib.qs_prefill(h, 2, P, P, 1, None, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_prefill(h, 0, P, None, 1, None, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_prefill(h, 0, P, P, 4, arr(1, 5, 0), None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_prefill(h, 0, P, P, 9 * G, None, None) == binding.QS_ERR_CAPACITY
+    assert b"max_ctx" in lib.qs_last_error(h)
+    assert lib.qs_prefill(h, 0, P, P, 65536 * G, arr(0, 0, 0), None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_prefill(h, 0, P, P, 0, None, None) == 0
     # rollback of an empty tail
     assert lib.qs_rollback(h, -1, arr(0, 1, 0)) == binding.QS_ERR_STATE
     assert lib.qs_rollback(h, 0, arr(0, 0, -1)) == binding.QS_ERR_INVALID_ARG

@@ -60,7 +60,7 @@ def test_random_scripts_match_oracle_bookkeeping(driver, seed):
     cmds = [f"create {L} {B} {H} {D} {G} {T} {gamma} 8"]
     expect = []
     for _ in range(400):
-        kind = rng.choice(["append", "append", "rollback", "flush", "attend"])
+        kind = rng.choice(["append", "append", "rollback", "flush", "attend", "prefill"])
         layer = int(rng.integers(-1 if kind in ("rollback", "flush") else 0, L))
         try:
             if kind == "append":
@@ -69,6 +69,17 @@ def test_random_scripts_match_oracle_bookkeeping(driver, seed):
                 cmds.append(f"append {layer} {n_max} " + " ".join(map(str, n)))
                 z = np.zeros((B, n_max, H, D), np.float16)
                 o.append(layer, z, z, n)
+            elif kind == "prefill":
+                if rng.random() < 0.6:                 # often empty the tails first, so that
+                    d = [int(x) for x in o.state(layer)[1]]  # the prompt is accepted
+                    cmds.append(f"rollback {layer} " + " ".join(map(str, d)))
+                    o.rollback(layer, d)
+                    expect.append((0, oracle_cells(o, L, B)))
+                n_max = int(rng.choice([0, 3, G, G + 7, 3 * G + 1]))
+                n = [int(rng.choice([0, int(rng.integers(0, n_max + 1))])) for _ in range(B)]
+                cmds.append(f"prefill {layer} {n_max} " + " ".join(map(str, n)))
+                z = np.zeros((B, n_max, H, D), np.float16)
+                o.prefill(layer, z, z, n)
             elif kind == "rollback":
                 d = [int(rng.integers(0, 8)) for _ in range(B)]
                 cmds.append(f"rollback {layer} " + " ".join(map(str, d)))

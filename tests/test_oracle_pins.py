@@ -367,6 +367,66 @@ def test_quantized_tier_is_a_function_of_the_committed_stream():
             assert np.array_equal(x, y)
 
 
+def test_prefill_equals_group_by_group_append_and_flush():
+    """Quantize once: a prompt whose whole groups pass through the buffer and are quantized as
+    they leave it, the rest left there -- the same counters, codes, metadata and live tail as
+    append(G) + flush per group followed by an append of the rest, for ragged prompts and after
+    an earlier group."""
+    B, H, D = 4, 2, 64
+    lens = [0, G - 1, 3 * G, 2 * G + 77]
+    k, v = synth.kv_host(B, max(lens), H, D, 95, 96)
+    k0, v0 = synth.kv_host(B, G, H, D, 97, 98)
+    a = OracleCache(1, B, H, D, G, 6 * G, 4)
+    ref = OracleCache(1, B, H, D, G, 6 * G, 4)
+    for c in (a, ref):                               # one earlier group on sequence 3
+        c.append(0, k0, v0, n=[0, 0, 0, G])
+        c.flush(0)
+    a.prefill(0, k, v, lens)
+    n_groups = max(L // G for L in lens)
+    for g in range(n_groups):
+        n = [G if L >= (g + 1) * G else 0 for L in lens]
+        ref.append(0, k[:, g * G:(g + 1) * G], v[:, g * G:(g + 1) * G], n=n)
+        ref.flush(0)
+    rest = [L - (L // G) * G for L in lens]
+    rk = np.zeros((B, G, H, D), np.float16)
+    rv = np.zeros((B, G, H, D), np.float16)
+    for b, L in enumerate(lens):
+        rk[b, : rest[b]] = k[b, L - rest[b]: L]
+        rv[b, : rest[b]] = v[b, L - rest[b]: L]
+    ref.append(0, rk, rv, n=rest)
+    for x, y in zip(a.state(0), ref.state(0)):
+        assert np.array_equal(x, y)
+    nq, nt, head = a.state(0)
+    assert list(nq) == [0, 0, 3 * G, 3 * G] and list(nt) == [0, G - 1, 0, 77]
+    assert list(head) == [0, 0, G, G]                # one toggle per quantized group
+    ia, ir = a.export_layer(0), ref.export_layer(0)
+    for name in ("uk", "lk", "uv", "lv", "kmeta", "vmeta"):
+        assert np.array_equal(ia[name], ir[name]), name
+    for b in range(B):
+        slots = [(int(head[b]) + i) % (2 * G) for i in range(int(nt[b]))]
+        assert np.array_equal(ia["tail_k"][b][:, slots], ir["tail_k"][b][:, slots])
+        assert np.array_equal(ia["tail_v"][b][:, slots], ir["tail_v"][b][:, slots])
+
+
+def test_prefill_errors_leave_state_unchanged():
+    H, D = 1, 64
+    k, v = synth.kv_host(2, 3 * G, H, D, 101, 102)
+    c = OracleCache(1, 2, H, D, G, 2 * G, 4)
+    c.append(0, k[:, :5], v[:, :5], n=[5, 0])
+    with pytest.raises(OracleError) as e:
+        c.prefill(0, k, v, [G, G])                   # sequence 0 has a non-empty tail
+    assert e.value.code == 3
+    with pytest.raises(OracleError) as e:
+        c.prefill(0, k, v, [0, 3 * G])               # 3 groups > capacity of 2
+    assert e.value.code == 2
+    with pytest.raises(OracleError) as e:
+        c.prefill(0, k[:, :G], v[:, :G], [0, G + 1])  # n > n_max
+    assert e.value.code == 1
+    assert [list(x) for x in c.state(0)] == [[0, 0], [5, 0], [0, 0]]
+    c.prefill(0, k, v, [0, 2 * G + 9])               # the empty sequence may take a prompt
+    assert [list(x) for x in c.state(0)] == [[0, 2 * G], [5, 9], [0, 0]]
+
+
 def test_ring_head_toggles_and_logical_order_survives_flush():
     H, D = 1, 64
     k, v = synth.kv_host(1, 3 * G, H, D, 71, 72)

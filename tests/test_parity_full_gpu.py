@@ -75,6 +75,26 @@ def test_lwm_128k_layer():
     log(f"128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
+def test_prefill_128k_layer():
+    """One qs_prefill of a 131072 + 64-token prompt (1024 groups quantized straight from the
+    prompt, 64 tokens to the tail), bit-exact against the oracle on sampled heads, then one
+    round of attention on top."""
+    log("case: 128k prefill, heads 0/17/31 sampled")
+    H, D, ctx, gamma = 32, 128, 131072, 6
+    ls = Lockstep(1, 1, H, D, ctx + 4 * G, gamma, heads=[0, 17, 31], tag="prefill128k")
+    out = synth.outlier_channels(H, D, synth.seed_for(4, 1, "outlier"))
+    k, v = dev_kv(4, 1, 1, ctx + 64, H, D, outliers=out)
+    ls.prefill(0, k, v)
+    del k, v
+    ls.check_planes(0)
+    gen = torch.Generator(device="cuda").manual_seed(4100)
+    ls.draft(0, dev_q((1, H, D), gen, D))
+    tk, tv = dev_kv(4, 1, 1, gamma + 1, H, D, outliers=out, salt=200)
+    ls.append(0, tk, tv)
+    ls.verify(0, dev_q((1, gamma + 1, H, D), gen, D))
+    log(f"prefill128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
 def test_llama_32k_full_stack_64_rounds():
     L, H, D, ctx, gamma = 32, 32, 128, 32768, 4
     log("case: 32k full stack, 64 rounds")

@@ -203,6 +203,31 @@ def test_max_queries_offset0_odd_heads(D):
     log(f"m16_{D}: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_matches_quantize_once(D):
+    """qs_prefill (whole groups quantized straight from the prompt, the rest to the tail) against
+    the oracle's quantize-once prefill: ragged prompts (empty, G-1, an exact multiple, and one
+    after an earlier group), then round verbs on top."""
+    log(f"case: prefill D={D}")
+    H, B = 4, 4
+    ls = Lockstep(1, B, H, D, 8 * G, 6, tag=f"prefill{D}")
+    k0, v0 = kv(B, G, H, D, 900)
+    ls.append(0, k0, v0, [0, 0, 0, G])
+    ls.flush(0)
+    lens = [0, G - 1, 3 * G, 5 * G + 77]
+    k, v = kv(B, max(lens), H, D, 901 + D)
+    ls.prefill(0, k, v, lens)
+    ls.check_planes(0)
+    k1, v1 = kv(B, 7, H, D, 902)
+    ls.append(0, k1, v1)
+    ls.draft(0, qd(B, H, D, 903))
+    ls.verify(0, qv(B, 7, H, D, 904))
+    ls.rollback(0, [3, 3, 3, 3])
+    ls.flush(0)
+    ls.check_planes(0)
+    log(f"prefill{D}: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
 def test_degenerate_groups():
     """Constant key channels and value rows (scale clamped to 1e-8, huge zero-point) and
     all-positive groups (zero-point below 0)."""
