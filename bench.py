@@ -260,6 +260,32 @@ def main():
         fl_ev.append((e0, e1, L * flush_bytes(H, D)))
     torch.cuda.synchronize()
 
+    # The accept / correct step after verify (qs_spec_accept): synthetic fp32 logits over a
+    # 32000-token vocabulary, gamma drafted tokens, fresh uniforms per call; for one sequence (the
+    # workload's batch) and for 32 (where the step is bound by reading the logits).  Algorithmic
+    # bytes: every logit read once; the kernels read them twice (row statistics, then the
+    # sampling totals) and one 4096-token part of two rows a third time.
+    from hierarchical_quantized_kv_amd.binding import spec_accept, spec_workspace_bytes
+    V_SPEC = 32000
+    sa_ev = {1: [], 32: []}
+    for sb in sa_ev:
+        sa_t = torch.randn((sb, gamma + 1, V_SPEC), generator=gen, device=dev) * 2
+        sa_d = sa_t[:, :gamma] + torch.randn((sb, gamma, V_SPEC), generator=gen, device=dev)
+        sa_x = torch.randint(0, V_SPEC, (sb, gamma), generator=gen, device=dev, dtype=torch.int32)
+        sa_ws = torch.empty(spec_workspace_bytes(sb, gamma, V_SPEC), dtype=torch.uint8, device=dev)
+        for _ in range(8):
+            sa_u = torch.rand((sb, gamma + 1), generator=gen, device=dev)
+            torch.cuda._sleep(spin_cycles)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            spec_accept(sa_t, sa_d, sa_x, sa_u, workspace=sa_ws, stream=stream)
+            e1.record(stream)
+            sa_ev[sb].append((e0, e1, sb * (2 * gamma + 1) * V_SPEC * 4))
+        torch.cuda.synchronize()
+        del sa_t, sa_d
+    torch.cuda.synchronize()
+
     # Average over the sampled calls.  When the GPU has caught up with the host (short calls at
     # 32k), an event interval can also hold a stall of the host thread (measured once: one
     # sample of ~30 ms among 40 of ~38 us); samples above twice the median are left out, and
@@ -278,6 +304,7 @@ def main():
     v_us, v_gbs, v_bytes = summarize(ev["verify"], "verify")
     f_us, f_gbs, f_bytes = summarize(fl_ev, "flush")
     p_us, p_gbs, p_bytes = summarize(pf_ev, "prefill")
+    sa = {sb: summarize(e, f"spec_accept_batch{sb}") for sb, e in sa_ev.items()}
 
     read_ceiling = measure_read_ceiling(torch, stream)
 
@@ -333,6 +360,13 @@ def main():
         "roofline_prefill": roof("prefill", p_gbs, p_bytes, p_us,
                                  f"prefill_kernel<128> + append_kernel<128, 1>: one layer's "
                                  f"{ctx + 64}-token prompt, {H} heads"),
+        "spec_accept": {
+            f"batch{sb}": {"kernel": f"row_stats_kernel + part_sums_kernel + accept_kernel: "
+                                     f"batch {sb}, gamma {gamma}, vocab {V_SPEC}",
+                           "avg_launch_us": round(us, 2), "bytes_per_launch": int(nb),
+                           "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                           "bound": "latency (dependent round trips)" if sb == 1 else "hbm"}
+            for sb, (us, gbs, nb) in sa.items()},
         "samples_dropped": dropped,
         "read_ceiling": read_ceiling,
         "cpu_baseline": cpu,

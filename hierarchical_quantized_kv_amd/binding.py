@@ -21,7 +21,8 @@ STATUS = {0: "QS_OK", 1: "QS_ERR_INVALID_ARG", 2: "QS_ERR_CAPACITY", 3: "QS_ERR_
 # Every symbol include/quantspec.h declares.
 EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_destroy",
            "qs_append", "qs_prefill", "qs_rollback", "qs_flush", "qs_attend_draft",
-           "qs_attend_verify", "qs_get_state", "qs_last_error")
+           "qs_attend_verify", "qs_get_state", "qs_last_error", "qs_spec_workspace_bytes",
+           "qs_spec_accept")
 
 
 class QsConfig(ctypes.Structure):
@@ -71,8 +72,11 @@ def lib():
         L.qs_get_state.argtypes = [P, I32, PI, PI, PI]
         L.qs_last_error.argtypes = [P]
         L.qs_last_error.restype = ctypes.c_char_p
+        L.qs_spec_workspace_bytes.argtypes = [I32, I32, I32]
+        L.qs_spec_workspace_bytes.restype = ctypes.c_size_t
+        L.qs_spec_accept.argtypes = [P, P, P, P, I32, I32, I32, P, ctypes.c_size_t, P, P, P]
         for f in EXPORTS:
-            if f not in ("qs_arena_bytes", "qs_last_error"):
+            if f not in ("qs_arena_bytes", "qs_last_error", "qs_spec_workspace_bytes"):
                 getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -225,3 +229,37 @@ class Cache:
         n = int(np.prod(shape))
         start = off + layer * n * esize
         return self.arena[start:start + n * esize].view(dtype).view(*shape)
+
+
+def spec_workspace_bytes(batch: int, gamma: int, vocab: int) -> int:
+    """Workspace qs_spec_accept needs (qs_spec_workspace_bytes); 0 for arguments it rejects."""
+    return int(lib().qs_spec_workspace_bytes(batch, gamma, vocab))
+
+
+def spec_accept(target_logits, draft_logits, draft_tokens, uniforms, workspace=None, stream=None):
+    """Speculative accept / correct on the GPU (qs_spec_accept).  target_logits fp32
+    [B][gamma+1][V], draft_logits fp32 [B][gamma][V], draft_tokens int32 [B][gamma], uniforms fp32
+    [B][gamma+1], all on the device.  Returns device int32 tensors (n_accepted, next_token)."""
+    import torch
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    for t, dt, shape, name in ((target_logits, torch.float32, (B, gamma + 1, V), "target_logits"),
+                               (draft_logits, torch.float32, (B, gamma, V), "draft_logits"),
+                               (draft_tokens, torch.int32, (B, gamma), "draft_tokens"),
+                               (uniforms, torch.float32, (B, gamma + 1), "uniforms")):
+        assert t.is_cuda and t.dtype == dt and t.is_contiguous() and tuple(t.shape) == shape, name
+    need = spec_workspace_bytes(B, gamma, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=target_logits.device)
+    n = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    nxt = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    P = ctypes.c_void_p
+    st = lib().qs_spec_accept(P(target_logits.data_ptr()), P(draft_logits.data_ptr()),
+                              P(draft_tokens.data_ptr()), P(uniforms.data_ptr()), B, gamma, V,
+                              P(workspace.data_ptr()), workspace.numel(), P(n.data_ptr()),
+                              P(nxt.data_ptr()), P(s.cuda_stream))
+    if st != QS_OK:
+        raise QsError(st, "qs_spec_accept")
+    return n, nxt
+

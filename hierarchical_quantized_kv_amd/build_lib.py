@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libquantspec.so")
-SOURCES = [os.path.join(CSRC, "qs_kernels.hip"), os.path.join(CSRC, "qs_api.cpp")]
+SOURCES = [os.path.join(CSRC, "qs_kernels.hip"), os.path.join(CSRC, "qs_sample.hip"),
+           os.path.join(CSRC, "qs_api.cpp")]
 # Measurement helper for bench.py (the device's streaming-read ceiling); not part of the library.
 PROBE_LIB = os.path.join(HERE, "libqs_readprobe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "read_probe.hip")]

@@ -1,0 +1,433 @@
+// qs_sample.hip -- the speculative accept / correct step after the verify pass (gfx950).
+//
+// Per sequence b, with target logits t_i (rows i = 0 .. gamma, the target's next-token scores at
+// the gamma drafted positions and one past them), draft logits d_i (rows i = 0 .. gamma-1) and
+// the gamma drafted tokens x_i:
+//   p_i = softmax(t_i),  q_i = softmax(d_i)
+//   drafted token i is accepted iff u_i <= min(1, p_i(x_i) / (q_i(x_i) + 1e-8)), scanning
+//   i = 0, 1, .. and stopping at the first rejection j;
+//   the next token is sampled with u_gamma from (p_j - q_j)_+ normalised if a token was rejected
+//   at j, else from p_gamma.
+// [QuantSpec Guide, "The Self-Speculative Verification Loop" listing: the acceptance test;
+// Pith review of arXiv:2502.10424, major comment 1 on Algorithm 1: VERIFY accepts with
+// min(1, p/q) and CORRECT samples from the normalised residual (p - q)_+; minor comment 5: after
+// gamma acceptances the next token comes from p_{gamma+1}.]
+//
+// Three launches, all fp32:
+//   row_stats_kernel  (max, sum of exp(x - max)) of every row in parts of 4096 tokens, one
+//                     workgroup per (row, part);
+//   part_sums_kernel  per candidate rejection point j = 0 .. gamma and part: the row statistics
+//                     of p_j and q_j merged, the part's totals of the sampling weights
+//                     ((p_j - q_j)_+, or p_gamma, and p_j itself), and (part 0) the acceptance
+//                     ratio of drafted token j, one workgroup each;
+//   accept_kernel     per sequence: the acceptance tests (one lane per drafted token, the first
+//                     failure is j), then the inverse CDF: the part from a scan of the part totals of the chosen j, the
+//                     token from one recomputation of that part.
+// So the whole vocabulary is read by many workgroups in parallel, and the one workgroup per
+// sequence reads only 4096 tokens of two rows.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/quantspec.h"
+
+namespace qs_sample {
+
+constexpr int kPartThreads = 256;                 // one workgroup per row part of kPartTokens
+constexpr int kPartPer = 16;                      //   consecutive tokens, kPartPer per thread
+constexpr int kPartTokens = kPartThreads * kPartPer;
+constexpr int kWaves = kPartThreads / 64;
+constexpr int kMaxParts = 256;                    // vocab <= kMaxParts * kPartTokens = 1048576
+
+__host__ __device__ inline int row_parts(int V) { return (V + kPartTokens - 1) / kPartTokens; }
+
+// Workspace, in floats, for B sequences, gamma drafted tokens and np = row_parts(V):
+//   part_stat [B][2 gamma + 1][np][2]  (max, sum of exp(x - max)) per row part; rows 0 .. gamma
+//                                      are the target rows, gamma+1 .. 2 gamma the draft rows
+//   row_stat  [B][2 gamma + 1][2]      (max, 1 / sum) per row
+//   part_sum  [B][gamma + 1][np][2]    per candidate j: the part's total of the sampling weight
+//                                      ((p_j - q_j)_+ for j < gamma, p_gamma for j = gamma) and
+//                                      of p_j
+//   ratio     [B][gamma]               min(1, p_i(x_i) / (q_i(x_i) + 1e-8)), or -1 for a drafted
+//                                      token outside the vocabulary
+struct WsLayout {
+  size_t part_stat, row_stat, part_sum, ratio, total;
+};
+__host__ __device__ inline WsLayout ws_layout(int B, int gamma, int np) {
+  WsLayout L;
+  const size_t rows = (size_t)B * (2 * gamma + 1);
+  L.part_stat = 0;
+  L.row_stat = L.part_stat + rows * np * 2;
+  L.part_sum = L.row_stat + rows * 2;
+  L.ratio = L.part_sum + (size_t)B * (gamma + 1) * np * 2;
+  L.total = L.ratio + (size_t)B * gamma;
+  return L;
+}
+
+struct RowStat {
+  float m, s;  // max and sum of exp(x - max) of a row (part)
+};
+
+__device__ __forceinline__ RowStat merge(RowStat a, RowStat b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == -INFINITY) return RowStat{-INFINITY, 0.f};
+  return RowStat{m, a.s * expf(a.m - m) + b.s * expf(b.m - m)};
+}
+
+// grid: x = row (0 .. gamma: target rows, gamma+1 .. 2 gamma: draft rows), y = part, z = sequence.
+// Coalesced: thread t reads tokens t, t + kPartThreads, ... of its part, all loads first.
+__global__ __launch_bounds__(kPartThreads) void row_stats_kernel(const float* __restrict__ t,
+                                                                 const float* __restrict__ d,
+                                                                 int gamma, int V, float* ws) {
+  __shared__ RowStat sh[kPartThreads / 64];
+  const int r = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
+  const float* row = r <= gamma ? t + ((size_t)b * (gamma + 1) + r) * V
+                                : d + ((size_t)b * gamma + (r - gamma - 1)) * V;
+  const int v0 = part * kPartTokens + (int)threadIdx.x;
+  float x[kPartPer];
+#pragma unroll
+  for (int k = 0; k < kPartPer; ++k) {
+    const int v = v0 + k * kPartThreads;
+    x[k] = v < V ? row[v] : -INFINITY;
+  }
+  float m = x[0];
+#pragma unroll
+  for (int k = 1; k < kPartPer; ++k) m = fmaxf(m, x[k]);
+  float sum = 0.f;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < kPartPer; ++k) sum += expf(x[k] - m);
+  }
+  RowStat st{m, sum};
+  for (int o = 32; o > 0; o >>= 1)
+    st = merge(st, RowStat{__shfl_xor(st.m, o), __shfl_xor(st.s, o)});
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kPartThreads / 64; ++w) st = merge(st, sh[w]);
+    float* o = ws + (((size_t)b * (2 * gamma + 1) + r) * row_parts(V) + part) * 2;
+    o[0] = st.m;
+    o[1] = st.s;
+  }
+}
+
+__device__ __forceinline__ float prob(float x, float2 st) {
+  return st.y > 0.f ? expf(x - st.x) * st.y : 0.f;
+}
+
+// Sampling weights use the hardware exp2 (a few ulp): the sample is an inverse CDF over up to a
+// million weights summed in fp32, far coarser than that.
+__device__ __forceinline__ float prob_fast(float x, float2 st) {
+  return st.y > 0.f ? __builtin_amdgcn_exp2f((x - st.x) * 1.4426950408889634f) * st.y : 0.f;
+}
+
+// Exclusive prefix of x >= 0 over the workgroup's kPartThreads threads in thread order, into
+// ex[tid]; ex[kPartThreads] receives the total.  ex is non-decreasing (each entry is the rounded
+// inclusive prefix of the previous thread), so [ex[t], ex[t+1]) tile [0, total) without gaps;
+// the same inputs give the same outputs on every call.
+__device__ void block_exclusive_scan(float x, float* ex, float* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float inc = x;
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  float exc = __shfl_up(inc, 1);
+  if (lane == 0) exc = 0.f;
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    float run = 0.f;
+    for (int k = 0; k < kWaves; ++k) {
+      const float v = wsum[k];
+      wsum[k] = run;
+      run += v;
+    }
+    ex[kPartThreads] = run;
+  }
+  __syncthreads();
+  ex[tid] = wsum[w] + exc;
+  __syncthreads();
+}
+
+// Row statistics (max, 1 / sum) of two rows of sequence b, merged from their parts by the
+// whole workgroup (thread t takes part t); rb < 0 skips the second row.
+__device__ void merge_rows(const float* part_stat, int np, size_t ra, long long rb, float2* out,
+                           RowStat (*sh)[kWaves]) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  RowStat a{-INFINITY, 0.f}, c{-INFINITY, 0.f};
+  if (tid < np) {
+    a = RowStat{part_stat[(ra * np + tid) * 2], part_stat[(ra * np + tid) * 2 + 1]};
+    if (rb >= 0) c = RowStat{part_stat[((size_t)rb * np + tid) * 2],
+                             part_stat[((size_t)rb * np + tid) * 2 + 1]};
+  }
+  // lanes at or past np hold the identity: lane 0 of a wave needs only the lanes below np
+  for (int o = 1; o < np && o < 64; o <<= 1) {
+    a = merge(a, RowStat{__shfl_xor(a.m, o), __shfl_xor(a.s, o)});
+    c = merge(c, RowStat{__shfl_xor(c.m, o), __shfl_xor(c.s, o)});
+  }
+  if (lane == 0) {
+    sh[0][wv] = a;
+    sh[1][wv] = c;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    RowStat st = sh[tid][0];
+    for (int w = 1; w < kWaves && w * 64 < np; ++w) st = merge(st, sh[tid][w]);
+    out[tid] = make_float2(st.m, st.s > 0.f ? 1.f / st.s : 0.f);
+  }
+  __syncthreads();
+}
+
+// Weights of tokens part * kPartTokens + k * kPartThreads + tid (k < kPartPer): wp = p_j and
+// wr = (p_j - q_j)_+, or wr = p_j when drow is null.  Tokens at or past V weigh 0.
+__device__ __forceinline__ void part_weights(const float* trow, const float* drow, float2 pst,
+                                             float2 qst, int V, int part, float (&wp)[kPartPer],
+                                             float (&wr)[kPartPer]) {
+  const int v0 = part * kPartTokens + (int)threadIdx.x;
+  float xt[kPartPer], xd[kPartPer];
+#pragma unroll
+  for (int k = 0; k < kPartPer; ++k) {
+    const int v = v0 + k * kPartThreads;
+    xt[k] = v < V ? trow[v] : -INFINITY;
+    xd[k] = (drow && v < V) ? drow[v] : -INFINITY;
+  }
+#pragma unroll
+  for (int k = 0; k < kPartPer; ++k) {
+    wp[k] = prob_fast(xt[k], pst);
+    wr[k] = drow ? fmaxf(0.f, wp[k] - prob_fast(xd[k], qst)) : wp[k];
+  }
+}
+
+// Totals of the kPartPer rows of a part (row k = the tokens of index k in every thread, in
+// token order) into row_tot, and the part total (the rows in order).  Called by every thread.
+// The rows pass through LDS: thread (k, c) sums columns c, c + 16, .. of row k, then thread k
+// sums its row's 16 partial sums (the row stride is padded so that a wave's reads hit 64
+// distinct banks).
+constexpr int kRowPad = kPartThreads + 16;
+__device__ float part_rows(const float (&w)[kPartPer], float* tile, float* partial,
+                           float* row_tot) {
+  static_assert(kPartPer * 16 == kPartThreads, "one thread per (row, column class)");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < kPartPer; ++k) tile[k * kRowPad + tid] = w[k];
+  __syncthreads();
+  {
+    const int k = tid >> 4, c = tid & 15;
+    float x = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPartThreads / 16; ++i) x += tile[k * kRowPad + c + 16 * i];
+    partial[k * 17 + c] = x;
+  }
+  __syncthreads();
+  if (tid < kPartPer) {
+    float r = 0.f;
+    for (int c = 0; c < 16; ++c) r += partial[tid * 17 + c];
+    row_tot[tid] = r;
+  }
+  __syncthreads();
+  float tot = 0.f;
+  for (int k = 0; k < kPartPer; ++k) tot += row_tot[k];
+  return tot;
+}
+
+// grid: x = candidate j (0 .. gamma), y = part, z = sequence.
+__global__ __launch_bounds__(kPartThreads) void part_sums_kernel(const float* __restrict__ t,
+                                                                 const float* __restrict__ d,
+                                                                 const int32_t* __restrict__ tokens,
+                                                                 int gamma, int V, float* ws) {
+  __shared__ RowStat sh[2][kWaves];
+  __shared__ float2 st[2];
+  __shared__ float2 wsum[kWaves];
+  const int j = blockIdx.x, part = blockIdx.y, b = blockIdx.z, B = gridDim.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int np = row_parts(V);
+  const WsLayout L = ws_layout(B, gamma, np);
+  const size_t rp = (size_t)b * (2 * gamma + 1) + j;
+  const long long rq = j < gamma ? (long long)rp + gamma + 1 : -1;
+  merge_rows(ws + L.part_stat, np, rp, rq, st, sh);
+  const float2 pst = st[0], qst = j < gamma ? st[1] : make_float2(0.f, 0.f);
+  const float* trow = t + ((size_t)b * (gamma + 1) + j) * V;
+  const float* drow = j < gamma ? d + ((size_t)b * gamma + j) * V : nullptr;
+  if (part == 0 && tid == 0) {
+    ws[L.row_stat + rp * 2] = pst.x;
+    ws[L.row_stat + rp * 2 + 1] = pst.y;
+    if (rq >= 0) {
+      ws[L.row_stat + rq * 2] = qst.x;
+      ws[L.row_stat + rq * 2 + 1] = qst.y;
+      // the acceptance ratio of drafted token j; a token outside the vocabulary is never
+      // accepted (u >= 0 > -1)
+      const int x = tokens[(size_t)b * gamma + j];
+      float acc = -1.f;
+      if (x >= 0 && x < V) acc = fminf(1.f, prob(trow[x], pst) / (prob(drow[x], qst) + 1e-8f));
+      ws[L.ratio + (size_t)b * gamma + j] = acc;
+    }
+  }
+  float wp[kPartPer], wr[kPartPer];
+  part_weights(trow, drow, pst, qst, V, part, wp, wr);
+  // the part's totals, in any order: the sampler only uses them to pick a part and the point's
+  // fraction of it
+  float sr = 0.f, sp = 0.f;
+#pragma unroll
+  for (int k = 0; k < kPartPer; ++k) {
+    sr += wr[k];
+    sp += wp[k];
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    sr += __shfl_xor(sr, o);
+    sp += __shfl_xor(sp, o);
+  }
+  if (lane == 0) wsum[wv] = make_float2(sr, sp);
+  __syncthreads();
+  if (tid == 0) {
+    float2 tot = wsum[0];
+    for (int w = 1; w < kWaves; ++w) {
+      tot.x += wsum[w].x;
+      tot.y += wsum[w].y;
+    }
+    float* o = ws + L.part_sum + (((size_t)b * (gamma + 1) + j) * np + part) * 2;
+    o[0] = tot.x;
+    o[1] = tot.y;
+  }
+}
+
+// grid: x = sequence.
+__global__ __launch_bounds__(kPartThreads) void accept_kernel(const float* __restrict__ t,
+                                                              const float* __restrict__ d,
+                                                              const float* __restrict__ u,
+                                                              int gamma, int V,
+                                                              const float* __restrict__ ws,
+                                                              int32_t* n_accepted,
+                                                              int32_t* next_token) {
+  const int b = blockIdx.x, B = gridDim.x, tid = threadIdx.x;
+  const int np = row_parts(V);
+  const WsLayout L = ws_layout(B, gamma, np);
+  const float* rs = ws + L.row_stat + (size_t)b * (2 * gamma + 1) * 2;
+  const float* ub = u + (size_t)b * (gamma + 1);
+  __shared__ float ex[kPartThreads + 1];
+  __shared__ float wsum[kWaves];
+  __shared__ float tile[kPartPer * kRowPad];
+  __shared__ float partial[kPartPer * 17];
+  __shared__ float row_tot[kPartPer];
+  __shared__ int s_j, s_part, s_last_part, s_tok, s_row_last, s_part_last;
+  if (tid < 64) {  // wave 0: lane i tests drafted token i; j = the first one that fails
+    const bool ok = tid < gamma && ub[tid] <= ws[L.ratio + (size_t)b * gamma + tid];
+    const unsigned long long fail = __ballot(tid < gamma && !ok);
+    if (tid == 0) {
+      s_j = fail ? __ffsll((long long)fail) - 1 : gamma;
+      s_part = -1;
+      s_last_part = -1;
+      s_tok = -1;
+      s_row_last = -1;
+      s_part_last = -1;
+    }
+  }
+  __syncthreads();
+  const int j = s_j;
+  const float* sums = ws + L.part_sum + ((size_t)b * (gamma + 1) + j) * np * 2;
+  // the residual's part totals (p_gamma's when j = gamma); p_j's if the residual vanished in
+  // rounding
+  int plain = 0;
+  float mine = tid < np ? sums[2 * tid] : 0.f;
+  block_exclusive_scan(mine, ex, wsum);
+  if (!(ex[kPartThreads] > 0.f)) {
+    plain = 1;
+    mine = tid < np ? sums[2 * tid + 1] : 0.f;
+    block_exclusive_scan(mine, ex, wsum);
+  }
+  const float total = ex[kPartThreads];
+  if (!(total > 0.f)) {  // no positive weight at all (rows of -inf logits)
+    if (tid == 0) {
+      n_accepted[b] = j;
+      next_token[b] = 0;
+    }
+    return;
+  }
+  // the part holding u * total, and the point's fraction of it; a point that rounding puts at
+  // or past the total goes to the top of the last part of positive weight
+  const float target = ub[gamma] * total;
+  if (ex[tid] <= target && target < ex[tid + 1]) s_part = tid;
+  if (mine > 0.f) atomicMax(&s_last_part, tid);
+  __syncthreads();
+  const int part = s_part >= 0 ? s_part : s_last_part;
+  const float lo = ex[part], hi = ex[part + 1];
+  const float frac = s_part >= 0 ? fminf(1.f, fmaxf(0.f, (target - lo) / (hi - lo))) : 1.f;
+  // that part again: its rows, the row holding the point, then the token by a scan of the row
+  const float* trow = t + ((size_t)b * (gamma + 1) + j) * V;
+  const float* drow = (j < gamma && !plain) ? d + ((size_t)b * gamma + j) * V : nullptr;
+  const int rq = 2 * (gamma + 1 + j);
+  const float2 pst = make_float2(rs[2 * j], rs[2 * j + 1]);
+  const float2 qst = j < gamma ? make_float2(rs[rq], rs[rq + 1]) : make_float2(0.f, 0.f);
+  float wp[kPartPer], w[kPartPer];
+  part_weights(trow, drow, pst, qst, V, part, wp, w);
+  const float in_part = frac * part_rows(w, tile, partial, row_tot);
+  float pre = 0.f;
+  int row = 0;
+  for (; row < kPartPer - 1; ++row) {
+    if (row_tot[row] > 0.f && in_part - pre < row_tot[row]) break;
+    pre += row_tot[row];
+  }
+  float wrow = 0.f;
+  int last = -1;
+#pragma unroll
+  for (int k = 0; k < kPartPer; ++k) {
+    if (k == row) wrow = w[k];
+    if (w[k] > 0.f) last = part * kPartTokens + k * kPartThreads + tid;
+  }
+  if (last >= 0) atomicMax(&s_part_last, last);
+  if (wrow > 0.f) atomicMax(&s_row_last, part * kPartTokens + row * kPartThreads + tid);
+  block_exclusive_scan(wrow, ex, wsum);
+  // the point within the row, in the scan's own units (its total and the row total differ by
+  // rounding)
+  const float rt = row_tot[row];
+  const float rel = rt > 0.f ? fmaxf(0.f, fminf(in_part - pre, rt)) * (ex[kPartThreads] / rt) : 0.f;
+  if (ex[tid] <= rel && rel < ex[tid + 1]) s_tok = part * kPartTokens + row * kPartThreads + tid;
+  __syncthreads();
+  if (tid == 0) {
+    // a point at the very top of the row or part (rounding) takes the last token of positive
+    // weight there
+    n_accepted[b] = j;
+    next_token[b] = s_tok >= 0 ? s_tok : s_row_last >= 0 ? s_row_last
+                                      : s_part_last >= 0 ? s_part_last : 0;
+  }
+}
+
+}  // namespace qs_sample
+
+extern "C" {
+
+size_t qs_spec_workspace_bytes(int32_t batch, int32_t gamma, int32_t vocab) {
+  if (batch < 1 || batch > 65535 || gamma < 1 || gamma + 1 > QS_MAX_QUERIES || vocab < 1 ||
+      vocab > qs_sample::kMaxParts * qs_sample::kPartTokens)
+    return 0;
+  return qs_sample::ws_layout(batch, gamma, qs_sample::row_parts(vocab)).total * sizeof(float);
+}
+
+qs_status qs_spec_accept(const float* d_target_logits, const float* d_draft_logits,
+                         const int32_t* d_draft_tokens, const float* d_uniforms, int32_t batch,
+                         int32_t gamma, int32_t vocab, void* d_workspace, size_t workspace_bytes,
+                         int32_t* d_n_accepted, int32_t* d_next_token, void* stream) {
+  if (!d_target_logits || !d_draft_logits || !d_draft_tokens || !d_uniforms || !d_workspace ||
+      !d_n_accepted || !d_next_token)
+    return QS_ERR_INVALID_ARG;
+  const size_t need = qs_spec_workspace_bytes(batch, gamma, vocab);
+  if (need == 0) return QS_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return QS_ERR_BUFFER;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(d_workspace);
+  const int np = qs_sample::row_parts(vocab);
+  const dim3 block(qs_sample::kPartThreads);
+  hipLaunchKernelGGL(qs_sample::row_stats_kernel, dim3(2 * gamma + 1, np, batch), block, 0, st,
+                     d_target_logits, d_draft_logits, gamma, vocab, ws);
+  if (hipGetLastError() != hipSuccess) return QS_ERR_DEVICE;
+  hipLaunchKernelGGL(qs_sample::part_sums_kernel, dim3(gamma + 1, np, batch), block, 0, st,
+                     d_target_logits, d_draft_logits, d_draft_tokens, gamma, vocab, ws);
+  if (hipGetLastError() != hipSuccess) return QS_ERR_DEVICE;
+  hipLaunchKernelGGL(qs_sample::accept_kernel, dim3(batch), block, 0, st, d_target_logits,
+                     d_draft_logits, d_uniforms, gamma, vocab, ws, d_n_accepted, d_next_token);
+  if (hipGetLastError() != hipSuccess) return QS_ERR_DEVICE;
+  return QS_OK;
+}
+
+}  // extern "C"

@@ -169,6 +169,34 @@ qs_status qs_rollback(qs_cache* cache, int32_t layer, const int32_t* h_n_drop);
 qs_status qs_flush(qs_cache* cache, int32_t layer, int32_t min_tail, void* stream,
                    int32_t* h_flushed);
 
+/* Speculative accept / correct (the step after the verify pass), for `batch` sequences:
+ *   d_target_logits : fp32 [batch][gamma+1][vocab]  target scores at the gamma drafted
+ *                     positions and one past them (p_i = softmax of row i)
+ *   d_draft_logits  : fp32 [batch][gamma][vocab]    draft scores (q_i = softmax of row i)
+ *   d_draft_tokens  : int32 [batch][gamma]          the drafted tokens x_i
+ *   d_uniforms      : fp32 [batch][gamma+1]         u_0 .. u_{gamma-1} for the acceptance
+ *                     tests, u_gamma for the sample; each in [0, 1)
+ * Drafted token i is accepted iff u_i <= min(1, p_i(x_i) / (q_i(x_i) + 1e-8)), for i = 0, 1, ..
+ * until the first rejection j (a token outside [0, vocab) is rejected); d_n_accepted[b]
+ * receives j (gamma if all are accepted) and d_next_token[b] the token sampled with u_gamma by
+ * inverse CDF in token order from (p_j - q_j)_+ normalised, or from p_gamma when all were
+ * accepted (from p_j if the residual has vanished in rounding).  All arithmetic is fp32.
+ * d_workspace: device memory of at least qs_spec_workspace_bytes(batch, gamma, vocab) bytes
+ * (row statistics and per-part sampling totals, fully rewritten by each call; calls that share
+ * one workspace must be ordered on one stream); the outputs are device int32 [batch].  Asynchronous on `stream`; needs no
+ * cache.  qs_spec_workspace_bytes returns 0 for arguments qs_spec_accept rejects.
+ * Errors: QS_ERR_INVALID_ARG for a null pointer, batch outside 1..65535, gamma outside
+ * 1..QS_MAX_QUERIES-1 or vocab outside 1..1048576; QS_ERR_BUFFER for a short workspace.
+ * [QuantSpec Guide, "The Self-Speculative Verification Loop" listing: the acceptance test;
+ * Pith review of arXiv:2502.10424, major comment 1 (VERIFY with min(1, p/q), CORRECT from the
+ * normalised residual (p - q)_+) and minor comment 5 (the token after gamma acceptances from
+ * p_{gamma+1}).] */
+size_t qs_spec_workspace_bytes(int32_t batch, int32_t gamma, int32_t vocab);
+qs_status qs_spec_accept(const float* d_target_logits, const float* d_draft_logits,
+                         const int32_t* d_draft_tokens, const float* d_uniforms, int32_t batch,
+                         int32_t gamma, int32_t vocab, void* d_workspace, size_t workspace_bytes,
+                         int32_t* d_n_accepted, int32_t* d_next_token, void* stream);
+
 /* Draft attention: one query per (sequence, head) over the upper plane of every quantized
  * token plus every tail token.
  *   d_q   : fp16 [B][H][D]      d_out : fp32 [B][H][D]

@@ -57,6 +57,7 @@ def lib():
         L.orc_destroy.restype = None
         L.orc_append.argtypes = [P, i, P, P, i, P]
         L.orc_prefill.argtypes = [P, i, P, P, i, P]
+        L.orc_spec_accept.argtypes = [P, P, P, P, i, i, i, P, P, P]
         L.orc_rollback.argtypes = [P, i, P]
         L.orc_flush.argtypes = [P, i, i, P]
         L.orc_attend_draft.argtypes = [P, i, P, ctypes.c_double, P]
@@ -65,7 +66,7 @@ def lib():
         L.orc_read_codes.argtypes = [P, i, i, i, i, P]
         L.orc_read_meta.argtypes = [P, i, i, i, P, P]
         L.orc_export_layer.argtypes = [P, i, P, P, P, P, P, P, P, P]
-        for f in ("orc_append", "orc_prefill", "orc_rollback", "orc_flush", "orc_attend_draft",
+        for f in ("orc_append", "orc_prefill", "orc_spec_accept", "orc_rollback", "orc_flush", "orc_attend_draft",
                   "orc_attend_verify", "orc_get_state", "orc_read_codes", "orc_read_meta",
                   "orc_export_layer"):
             getattr(L, f).restype = i
@@ -116,6 +117,26 @@ def dequant_full(c8: int, s: float, z: float) -> float:
 
 def dequant_upper(cu: int, s: float, z: float, off: int) -> float:
     return lib().orc_dequant_upper(int(cu), float(s), float(z), int(off))
+
+
+def spec_accept(target_logits, draft_logits, draft_tokens, uniforms):
+    """Speculative accept / correct in fp64 (orc_spec_accept).  Shapes: [B][gamma+1][V],
+    [B][gamma][V], [B][gamma], [B][gamma+1].  Returns (n_accepted, next_token, margin)."""
+    t = np.ascontiguousarray(target_logits, dtype=np.float32)
+    d = np.ascontiguousarray(draft_logits, dtype=np.float32)
+    x = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    B, g1, V = t.shape
+    gamma = g1 - 1
+    assert d.shape == (B, gamma, V) and x.shape == (B, gamma) and u.shape == (B, gamma + 1)
+    n = np.zeros(B, np.int32)
+    nxt = np.zeros(B, np.int32)
+    mg = np.zeros(B, np.float64)
+    rc = lib().orc_spec_accept(_ptr(t), _ptr(d), _ptr(x), _ptr(u), B, gamma, V, _ptr(n),
+                               _ptr(nxt), _ptr(mg))
+    if rc != 0:
+        raise OracleError(rc, "spec_accept")
+    return n, nxt, mg
 
 
 class OracleCache:

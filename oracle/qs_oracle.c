@@ -457,3 +457,107 @@ int orc_export_layer(const orc_cache* c, int layer, uint8_t* uk, uint8_t* lk, ui
     }
   return 0;
 }
+
+/* ---------------------------------------------------------------------------------------- */
+/* Speculative accept / correct                                                              */
+/* ---------------------------------------------------------------------------------------- */
+
+/* softmax of one row in fp64, into out */
+static void softmax_row(const float* x, int V, double* out) {
+  double m = -INFINITY;
+  for (int v = 0; v < V; ++v)
+    if ((double)x[v] > m) m = x[v];
+  double s = 0.0;
+  for (int v = 0; v < V; ++v) {
+    out[v] = m == -INFINITY ? 0.0 : exp((double)x[v] - m);
+    s += out[v];
+  }
+  for (int v = 0; v < V; ++v) out[v] = s > 0.0 ? out[v] / s : 0.0;
+}
+
+/* The step after the target's verify pass, per sequence b ([G] "The Self-Speculative
+ * Verification Loop" listing for the acceptance test; [R] major comment 1 on Algorithm 1 for
+ * the correction from the normalised residual (p - q)_+, minor comment 5 for the token after
+ * gamma acceptances, from p_{gamma+1}), in fp64:
+ *   p_i = softmax(t_i) (rows 0 .. gamma), q_i = softmax(d_i) (rows 0 .. gamma-1);
+ *   drafted token x_i is accepted iff u_i <= min(1, p_i(x_i) / (q_i(x_i) + 1e-8)), for
+ *   i = 0, 1, .. until the first rejection j (a token outside [0, V) is rejected);
+ *   the next token is the smallest v with sum_{w <= v} r(w) > u_gamma * sum_w r(w), where r is
+ *   (p_j - q_j)_+ after a rejection at j, p_gamma after gamma acceptances, and p_j if the
+ *   residual sums to zero.
+ * margin[b] (test support, may be NULL): how far the decisions were from flipping -- the
+ * smallest |u_i - min(1, ratio_i)| over the tests made, and for the sample the distance of
+ * u_gamma from the CDF values around the chosen token, both in units of probability. */
+int orc_spec_accept(const float* t, const float* d, const int* tokens, const float* u, int B,
+                    int gamma, int V, int* n_acc, int* next, double* margin) {
+  if (!t || !d || !tokens || !u || !n_acc || !next || B < 1 || gamma < 1 || V < 1) return 1;
+  double* p = (double*)malloc(sizeof(double) * V);
+  double* q = (double*)malloc(sizeof(double) * V);
+  double* r = (double*)malloc(sizeof(double) * V);
+  if (!p || !q || !r) {
+    free(p); free(q); free(r);
+    return 1;
+  }
+  for (int b = 0; b < B; ++b) {
+    const float* tb = t + (size_t)b * (gamma + 1) * V;
+    const float* db = d + (size_t)b * gamma * V;
+    const float* ub = u + (size_t)b * (gamma + 1);
+    double mg = INFINITY;
+    int j = 0;
+    for (; j < gamma; ++j) {
+      const int x = tokens[(size_t)b * gamma + j];
+      if (x < 0 || x >= V) break;
+      softmax_row(tb + (size_t)j * V, V, p);
+      softmax_row(db + (size_t)j * V, V, q);
+      double acc = p[x] / (q[x] + 1e-8);
+      if (acc > 1.0) acc = 1.0;
+      const double gap = fabs((double)ub[j] - acc);
+      if (gap < mg) mg = gap;
+      if (!((double)ub[j] <= acc)) break;
+    }
+    softmax_row(tb + (size_t)j * V, V, p);
+    double total = 0.0;
+    if (j < gamma) {
+      softmax_row(db + (size_t)j * V, V, q);
+      for (int v = 0; v < V; ++v) {
+        r[v] = p[v] > q[v] ? p[v] - q[v] : 0.0;
+        total += r[v];
+      }
+    }
+    if (total <= 0.0) {
+      total = 0.0;
+      for (int v = 0; v < V; ++v) {
+        r[v] = p[v];
+        total += r[v];
+      }
+    }
+    int tok = 0;
+    if (total > 0.0) {
+      const double target = (double)ub[gamma] * total;
+      double c = 0.0;
+      tok = -1;
+      for (int v = 0; v < V; ++v) {
+        const double prev = c;
+        c += r[v];
+        if (c > target) {
+          tok = v;
+          const double gap = (target - prev) < (c - target) ? (target - prev) : (c - target);
+          if (gap / total < mg) mg = gap / total;
+          break;
+        }
+      }
+      if (tok < 0)
+        for (int v = V - 1; v >= 0; --v)
+          if (r[v] > 0.0) {
+            tok = v;
+            break;
+          }
+    }
+    n_acc[b] = j;
+    next[b] = tok;
+    if (margin) margin[b] = mg;
+  }
+  free(p); free(q); free(r);
+  return 0;
+}
+

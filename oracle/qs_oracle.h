@@ -57,6 +57,10 @@ int orc_append(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, in
  * buffer, the rest left in it; needs an empty buffer for every sequence with n[b] > 0. */
 int orc_prefill(orc_cache* c, int layer, const uint16_t* k, const uint16_t* v, int n_max,
                 const int* n);
+/* Speculative accept / correct: t fp32 [B][gamma+1][V], d [B][gamma][V], tokens [B][gamma],
+ * u [B][gamma+1]; n_acc, next [B]; margin [B] or NULL. */
+int orc_spec_accept(const float* t, const float* d, const int* tokens, const float* u, int B,
+                    int gamma, int V, int* n_acc, int* next, double* margin);
 /* layer -1 = every layer; n_drop: [B] or NULL. */
 int orc_rollback(orc_cache* c, int layer, const int* n_drop);
 /* layer -1 = every layer; flushed: [B] or NULL. */

@@ -140,3 +140,29 @@ def test_validation_before_any_launch(lib):
     assert lib.qs_attend_draft(h, 0, None, ctypes.c_float(1.0), P, None) == binding.QS_ERR_INVALID_ARG
     assert lib.qs_get_state(h, 0, nq, nt, hd) == 0 and list(nt) == [0, 0, 0]
     lib.qs_cache_destroy(h)
+
+
+def test_spec_accept_validation_before_any_launch(lib):
+    P = ctypes.c_void_p(FAKE)
+    # per sequence, fp32: (max, sum) of each of the 2 gamma + 1 rows per 4096-token part, (max,
+    # 1/sum) per row, two sampling totals per candidate j = 0 .. gamma per part, and gamma
+    # acceptance ratios
+    ws_bytes = lambda B, g, parts: B * (2 * (2 * g + 1) * parts + 2 * (2 * g + 1)
+                                        + 2 * (g + 1) * parts + g) * 4
+    assert lib.qs_spec_workspace_bytes(2, 6, 100) == ws_bytes(2, 6, 1)       # one part
+    assert lib.qs_spec_workspace_bytes(2, 6, 32000) == ws_bytes(2, 6, 8)     # eight parts
+    assert lib.qs_spec_workspace_bytes(1, 15, 1 << 20) == ws_bytes(1, 15, 256)
+    for args in ((0, 6, 100), (65536, 6, 100), (1, 16, 100), (1, 6, 0), (1, 6, (1 << 20) + 1)):
+        assert lib.qs_spec_workspace_bytes(*args) == 0, args
+    ws = lib.qs_spec_workspace_bytes(2, 6, 100)
+    call = lambda *a: lib.qs_spec_accept(*a)
+    ok = (P, P, P, P, 2, 6, 100, P, ws, P, P, None)
+    for i in (0, 1, 2, 3, 7, 9, 10):                     # every pointer is required
+        args = list(ok)
+        args[i] = None
+        assert call(*args) == binding.QS_ERR_INVALID_ARG, i
+    for b_, g_, v_ in ((0, 6, 100), (65536, 6, 100), (2, 0, 100), (2, 16, 100), (2, 6, 0),
+                       (2, 6, (1 << 20) + 1)):
+        assert call(P, P, P, P, b_, g_, v_, P, 1 << 20, P, P, None) == binding.QS_ERR_INVALID_ARG
+    assert call(P, P, P, P, 2, 6, 100, P, ws - 1, P, P, None) == binding.QS_ERR_BUFFER
+

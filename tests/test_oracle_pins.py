@@ -502,3 +502,65 @@ def test_layout_export_matches_split_identity():
                 assert np.array_equal(ev, tok[0::2].T) and np.array_equal(od, tok[1::2].T)
         km, vm = c.meta(0, 0, h)
         assert np.array_equal(img["kmeta"][0, h], km) and np.array_equal(img["vmeta"][0, h], vm)
+
+
+# ------------------------------------------------------------------------------------------
+# Speculative accept / correct
+# ------------------------------------------------------------------------------------------
+
+def _softmax(x):
+    x = np.asarray(x, np.float64)
+    e = np.exp(x - x.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def test_spec_accept_first_token_follows_the_target_distribution():
+    """The point of the correction step: whatever the draft distribution, the first token the
+    round emits (x_0 if accepted, else the resampled one) is distributed as p_0.  30000 rounds
+    with fixed logits, drafted tokens drawn from q_i, fresh uniforms; chi-square against p_0."""
+    rng = np.random.default_rng(2024)
+    V, gamma, N = 6, 3, 30000
+    t = rng.normal(0, 1.5, (gamma + 1, V)).astype(np.float32)
+    d = (t[:gamma] + rng.normal(0, 1.0, (gamma, V))).astype(np.float32)
+    q = _softmax(d)
+    x = np.stack([rng.choice(V, size=N, p=q[i]) for i in range(gamma)], axis=1).astype(np.int32)
+    u = rng.random((N, gamma + 1)).astype(np.float32)
+    n, nxt, _ = oracle.spec_accept(np.broadcast_to(t, (N, gamma + 1, V)),
+                                   np.broadcast_to(d, (N, gamma, V)), x, u)
+    first = np.where(n >= 1, x[:, 0], nxt)
+    p0 = _softmax(t[0])
+    obs = np.bincount(first, minlength=V)
+    chi2 = float((((obs - N * p0) ** 2) / (N * p0)).sum())
+    assert chi2 < 25.7, (chi2, obs, N * p0)     # df 5, p = 1e-4
+    # and the draft is not the target: some rounds reject (the test is not vacuous)
+    assert 0.05 < float((n < gamma).mean()) < 0.95
+
+
+def test_spec_accept_closed_forms():
+    ninf = -np.inf
+    # p_0 = (1/2, 1/2, 0, 0), q_0 = (0, 1, 0, 0), drafted token 1: accepted iff
+    # u_0 <= 1/2 / (1 + 1e-8), just below 1/2; the residual (p_0 - q_0)_+ = (1/2, 0, 0, 0) gives
+    # token 0 whatever u_1; after an acceptance the sample comes from p_1 = (0, 0, 1, 0)
+    t = np.array([[[0, 0, ninf, ninf], [ninf, ninf, 0, ninf]]], np.float32)
+    d = np.array([[[ninf, 0, ninf, ninf]]], np.float32)
+    for u0, u1, n_exp, tok_exp in ((0.7, 0.99, 0, 0), (0.7, 0.0, 0, 0), (0.3, 0.5, 1, 2),
+                                   (0.5, 0.2, 0, 0), (0.4999, 0.2, 1, 2)):
+        n, nxt, _ = oracle.spec_accept(t, d, np.array([[1]], np.int32),
+                                       np.array([[u0, u1]], np.float32))
+        assert (n[0], nxt[0]) == (n_exp, tok_exp), (u0, u1, n[0], nxt[0])
+    # q = p: every test passes (u < 1 - 1e-6), then the inverse CDF of p_gamma
+    rng = np.random.default_rng(5)
+    V, gamma = 7, 4
+    t = rng.normal(0, 1, (1, gamma + 1, V)).astype(np.float32)
+    d = t[:, :gamma].copy()
+    x = rng.integers(0, V, (1, gamma)).astype(np.int32)
+    cdf = np.cumsum(_softmax(t[0, gamma]))
+    for ug in (0.0, 0.3, 0.8, 0.999):
+        n, nxt, _ = oracle.spec_accept(t, d, x, np.array([[0.5] * gamma + [ug]], np.float32))
+        assert n[0] == gamma
+        assert nxt[0] == int(np.searchsorted(cdf, np.float32(ug) * cdf[-1], side="right"))
+    # a drafted token outside the vocabulary is rejected at its position
+    x2 = x.copy()
+    x2[0, 2] = V
+    n, _, _ = oracle.spec_accept(t, d, x2, np.array([[0.5] * gamma + [0.1]], np.float32))
+    assert n[0] == 2
