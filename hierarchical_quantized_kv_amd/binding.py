@@ -22,7 +22,11 @@ STATUS = {0: "QS_OK", 1: "QS_ERR_INVALID_ARG", 2: "QS_ERR_CAPACITY", 3: "QS_ERR_
 EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_destroy",
            "qs_append", "qs_prefill", "qs_rollback", "qs_flush", "qs_attend_draft",
            "qs_attend_verify", "qs_get_state", "qs_last_error", "qs_spec_workspace_bytes",
-           "qs_spec_accept")
+           "qs_spec_accept", "qs_state_to_device", "qs_state_from_device", "qs_append_dev",
+           "qs_rollback_dev", "qs_flush_dev", "qs_attend_draft_dev", "qs_attend_verify_dev")
+
+# Bits of the device-mode error word (include/quantspec.h, device mode).
+DEV_ERR_APPEND, DEV_ERR_ROLLBACK, DEV_ERR_FLUSH, DEV_ERR_ATTEND = 1, 2, 4, 8
 
 
 class QsConfig(ctypes.Structure):
@@ -33,9 +37,9 @@ class QsConfig(ctypes.Structure):
 
 class QsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "uk", "lk", "uv", "lv", "kmeta", "vmeta", "tail_k", "tail_v", "work",
+        "uk", "lk", "uv", "lv", "kmeta", "vmeta", "tail_k", "tail_v", "work", "state",
         "uk_bytes", "uv_bytes", "kmeta_bytes", "vmeta_bytes", "tail_bytes", "work_bytes",
-        "total")]
+        "state_bytes", "total")]
 
 
 class QsError(RuntimeError):
@@ -75,6 +79,13 @@ def lib():
         L.qs_spec_workspace_bytes.argtypes = [I32, I32, I32]
         L.qs_spec_workspace_bytes.restype = ctypes.c_size_t
         L.qs_spec_accept.argtypes = [P, P, P, P, I32, I32, I32, P, ctypes.c_size_t, P, P, P]
+        L.qs_state_to_device.argtypes = [P, P]
+        L.qs_state_from_device.argtypes = [P, P, PI]
+        L.qs_append_dev.argtypes = [P, I32, P, P, I32, P]
+        L.qs_rollback_dev.argtypes = [P, I32, I32, P, P]
+        L.qs_flush_dev.argtypes = [P, I32, I32, P]
+        L.qs_attend_draft_dev.argtypes = [P, I32, P, F, P, P]
+        L.qs_attend_verify_dev.argtypes = [P, I32, P, I32, F, P, P]
         for f in EXPORTS:
             if f not in ("qs_arena_bytes", "qs_last_error", "qs_spec_workspace_bytes"):
                 getattr(L, f).restype = ctypes.c_int
@@ -207,6 +218,55 @@ class Cache:
                     "qs_get_state")
         return nq, nt, hd
 
+    # ---- device mode: the counters in device memory; the _dev verbs only enqueue kernels,
+    # so a sequence of them can be captured in a graph and replayed ------------------------
+    def to_device_state(self, stream=None):
+        self._check(lib().qs_state_to_device(self._h, self._stream(stream)), "qs_state_to_device")
+
+    def from_device_state(self, stream=None) -> int:
+        """Back to host mode; returns the device error word (DEV_ERR_* bits)."""
+        err = np.zeros(1, np.int32)
+        self._check(lib().qs_state_from_device(self._h, self._stream(stream), _ptr_i32(err)),
+                    "qs_state_from_device")
+        return int(err[0])
+
+    def append_dev(self, layer, k, v, stream=None):
+        torch = self.torch
+        assert k.shape == v.shape and k.dim() == 4 and k.shape[0] == self.B
+        assert tuple(k.shape[2:]) == (self.H, self.D)
+        self._check(lib().qs_append_dev(self._h, layer, self._dev(k, torch.float16, "k"),
+                                        self._dev(v, torch.float16, "v"), k.shape[1],
+                                        self._stream(stream)), "qs_append_dev")
+
+    def rollback_dev(self, layer, n, sub=None, stream=None):
+        """Drops n - sub[b] tail tokens of each sequence b (sub: device int32 [B] or None)."""
+        p = None
+        if sub is not None:
+            assert tuple(sub.shape) == (self.B,)
+            p = self._dev(sub, self.torch.int32, "sub")
+        self._check(lib().qs_rollback_dev(self._h, layer, int(n), p, self._stream(stream)),
+                    "qs_rollback_dev")
+
+    def flush_dev(self, layer=-1, min_tail=None, stream=None):
+        self._check(lib().qs_flush_dev(self._h, layer, self.G if min_tail is None else min_tail,
+                                       self._stream(stream)), "qs_flush_dev")
+
+    def attend_draft_dev(self, layer, q, out, sm_scale=1.0, stream=None):
+        torch = self.torch
+        assert tuple(q.shape) == (self.B, self.H, self.D) and out.shape == q.shape
+        self._check(lib().qs_attend_draft_dev(self._h, layer, self._dev(q, torch.float16, "q"),
+                                              float(sm_scale), self._dev(out, torch.float32, "out"),
+                                              self._stream(stream)), "qs_attend_draft_dev")
+
+    def attend_verify_dev(self, layer, q, out, sm_scale=1.0, stream=None):
+        torch = self.torch
+        assert q.dim() == 4 and q.shape[0] == self.B and tuple(q.shape[2:]) == (self.H, self.D)
+        assert out.shape == q.shape
+        self._check(lib().qs_attend_verify_dev(self._h, layer, self._dev(q, torch.float16, "q"),
+                                               q.shape[1], float(sm_scale),
+                                               self._dev(out, torch.float32, "out"),
+                                               self._stream(stream)), "qs_attend_verify_dev")
+
     # ---- views of the arena (layout of include/quantspec.h), for inspection -------------
     def section(self, name, layer):
         """Device view of one layer of an arena section, shaped as the header documents."""
@@ -236,10 +296,12 @@ def spec_workspace_bytes(batch: int, gamma: int, vocab: int) -> int:
     return int(lib().qs_spec_workspace_bytes(batch, gamma, vocab))
 
 
-def spec_accept(target_logits, draft_logits, draft_tokens, uniforms, workspace=None, stream=None):
+def spec_accept(target_logits, draft_logits, draft_tokens, uniforms, workspace=None, stream=None,
+                n_out=None, next_out=None):
     """Speculative accept / correct on the GPU (qs_spec_accept).  target_logits fp32
     [B][gamma+1][V], draft_logits fp32 [B][gamma][V], draft_tokens int32 [B][gamma], uniforms fp32
-    [B][gamma+1], all on the device.  Returns device int32 tensors (n_accepted, next_token)."""
+    [B][gamma+1], all on the device.  Returns device int32 tensors (n_accepted, next_token),
+    written into n_out / next_out when given."""
     import torch
     B, g1, V = target_logits.shape
     gamma = g1 - 1
@@ -251,8 +313,11 @@ def spec_accept(target_logits, draft_logits, draft_tokens, uniforms, workspace=N
     need = spec_workspace_bytes(B, gamma, V)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=target_logits.device)
-    n = torch.empty(B, dtype=torch.int32, device=target_logits.device)
-    nxt = torch.empty(B, dtype=torch.int32, device=target_logits.device)
+    n = torch.empty(B, dtype=torch.int32, device=target_logits.device) if n_out is None else n_out
+    nxt = (torch.empty(B, dtype=torch.int32, device=target_logits.device) if next_out is None
+           else next_out)
+    for t, name in ((n, "n_out"), (nxt, "next_out")):
+        assert t.is_cuda and t.dtype == torch.int32 and t.is_contiguous() and t.numel() == B, name
     s = stream if stream is not None else torch.cuda.current_stream()
     P = ctypes.c_void_p
     st = lib().qs_spec_accept(P(target_logits.data_ptr()), P(draft_logits.data_ptr()),

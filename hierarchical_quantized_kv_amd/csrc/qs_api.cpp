@@ -3,6 +3,9 @@
 // Every verb validates all of its arguments against the host-side State first, then enqueues
 // its kernels on the caller's stream, and only then updates the State.  No verb synchronizes
 // with the device or copies host data to it: per-sequence counters travel as kernel arguments.
+// In device mode (qs_state_to_device .. qs_state_from_device) the counters live in the arena's
+// state section instead: the _dev verbs enqueue their kernels plus a counter-update kernel and
+// touch no host state, so a sequence of them can be captured in a graph and replayed.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -10,6 +13,7 @@
 
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/quantspec.h"
 #include "qs_state.h"
@@ -19,6 +23,7 @@ hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st);
 hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st);
+hipError_t launch_state(const StateArgs& a, hipStream_t st);
 int attention_slots(int D, bool draft, int B);
 }  // namespace qs
 
@@ -28,6 +33,7 @@ struct qs_cache {
   uint8_t* arena;
   qs::State st;
   std::string err;
+  bool dev = false;  // device mode: the counters are in the state section, not in st
 };
 
 namespace {
@@ -47,6 +53,14 @@ qs_status device_fail(qs_cache* c, hipError_t e, const char* what) {
 
 size_t layer_off(const qs_cache* c, size_t per_lbh_bytes, int layer) {
   return (size_t)layer * c->cfg.batch * c->cfg.n_heads * per_lbh_bytes;
+}
+
+const char* const kInDeviceMode = "the counters are on the device (qs_state_from_device first)";
+const char* const kInHostMode = "not in device mode (qs_state_to_device first)";
+
+int32_t* dev_state(const qs_cache* c) { return reinterpret_cast<int32_t*>(c->arena + c->lay.state); }
+int32_t* dev_error(const qs_cache* c) {
+  return dev_state(c) + (size_t)c->cfg.n_layers * c->cfg.batch * qs::kStateInts;
 }
 
 }  // namespace
@@ -88,6 +102,7 @@ qs_status qs_cache_destroy(qs_cache* cache) {
 qs_status qs_append(qs_cache* c, int32_t layer, const void* d_k, const void* d_v, int32_t n_max,
                     const int32_t* h_n, void* stream) {
   if (!c) return QS_ERR_INVALID_ARG;
+  if (c->dev) return fail(c, QS_ERR_STATE, kInDeviceMode);
   if (!d_k || !d_v) return fail(c, QS_ERR_INVALID_ARG, "null k or v");
   const qs_config& cf = c->cfg;
   int32_t n[QS_MAX_BATCH];
@@ -124,6 +139,7 @@ qs_status qs_append(qs_cache* c, int32_t layer, const void* d_k, const void* d_v
 qs_status qs_prefill(qs_cache* c, int32_t layer, const void* d_k, const void* d_v, int32_t n_max,
                      const int32_t* h_n, void* stream) {
   if (!c) return QS_ERR_INVALID_ARG;
+  if (c->dev) return fail(c, QS_ERR_STATE, kInDeviceMode);
   if (!d_k || !d_v) return fail(c, QS_ERR_INVALID_ARG, "null k or v");
   const qs_config& cf = c->cfg;
   int32_t n[QS_MAX_BATCH];
@@ -188,6 +204,7 @@ qs_status qs_prefill(qs_cache* c, int32_t layer, const void* d_k, const void* d_
 
 qs_status qs_rollback(qs_cache* c, int32_t layer, const int32_t* h_n_drop) {
   if (!c) return QS_ERR_INVALID_ARG;
+  if (c->dev) return fail(c, QS_ERR_STATE, kInDeviceMode);
   std::string err;
   qs_status s = c->st.check_rollback(layer, h_n_drop, &err);
   if (s != QS_OK) return fail(c, s, err);
@@ -198,6 +215,7 @@ qs_status qs_rollback(qs_cache* c, int32_t layer, const int32_t* h_n_drop) {
 
 qs_status qs_flush(qs_cache* c, int32_t layer, int32_t min_tail, void* stream, int32_t* h_flushed) {
   if (!c) return QS_ERR_INVALID_ARG;
+  if (c->dev) return fail(c, QS_ERR_STATE, kInDeviceMode);
   std::string err;
   qs_status s = c->st.check_flush(layer, min_tail, &err);
   if (s != QS_OK) return fail(c, s, err);
@@ -255,26 +273,11 @@ qs_status qs_flush(qs_cache* c, int32_t layer, int32_t min_tail, void* stream, i
   return QS_OK;
 }
 
-static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
-                        float* d_out, void* stream, bool draft) {
-  if (!c) return QS_ERR_INVALID_ARG;
-  if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
-  if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
-  std::string err;
-  qs_status s = c->st.check_attend(layer, m, draft, &err);
-  if (s != QS_OK) return fail(c, s, err);
+// Argument block of one attention call of `layer` over the work plan p.
+static void attn_args(const qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
+                      float* d_out, const qs::Plan& p, qs::AttnArgs& a) {
   const qs_config& cf = c->cfg;
   const int D = cf.head_dim;
-  qs::Seq seqs[QS_MAX_BATCH];
-  for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
-  int slots = qs::attention_slots(D, draft, cf.batch);
-  if (slots <= 0) slots = kFallbackSlots;
-  int tail_items = 0;
-  for (int b = 0; b < cf.batch; ++b)
-    tail_items += cf.n_heads * ((seqs[b].nt + qs::kTailChunk - 1) / qs::kTailChunk);
-  const int target = slots - tail_items > slots / 2 ? slots - tail_items : slots / 2;
-  const qs::Plan p = qs::make_plan(seqs, cf.batch, cf.n_heads, cf.group, target);
-  qs::AttnArgs a{};
   const size_t T = cf.max_ctx, G = cf.group, NG = T / G;
   a.uk = c->arena + c->lay.uk + layer_off(c, T * (D / 2), layer);
   a.lk = c->arena + c->lay.lk + layer_off(c, T * (D / 2), layer);
@@ -298,16 +301,46 @@ static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, 
   a.n_titems_total = p.tbase[cf.batch];
   a.qscale = sm_scale * 1.4426950408889634f;
   a.draft_offset = (float)cf.draft_offset;
+  for (int b = 0; b <= cf.batch; ++b) {
+    a.qitem_base[b] = p.qbase[b];
+    a.titem_base[b] = p.tbase[b];
+  }
+}
+
+// Work plan for the sequences `seqs`: quantized workers sized to one resident round of the pass
+// kernel, next to the tail items.
+static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft) {
+  const qs_config& cf = c->cfg;
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch);
+  if (slots <= 0) slots = kFallbackSlots;
+  int tail_items = 0;
+  for (int b = 0; b < cf.batch; ++b)
+    tail_items += cf.n_heads * ((seqs[b].nt + qs::kTailChunk - 1) / qs::kTailChunk);
+  const int target = slots - tail_items > slots / 2 ? slots - tail_items : slots / 2;
+  return qs::make_plan(seqs, cf.batch, cf.n_heads, cf.group, target);
+}
+
+static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
+                        float* d_out, void* stream, bool draft) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (c->dev) return fail(c, QS_ERR_STATE, kInDeviceMode);
+  if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
+  if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
+  std::string err;
+  qs_status s = c->st.check_attend(layer, m, draft, &err);
+  if (s != QS_OK) return fail(c, s, err);
+  const qs_config& cf = c->cfg;
+  qs::Seq seqs[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
+  const qs::Plan p = attn_plan(c, seqs, draft);
+  qs::AttnArgs a{};
+  attn_args(c, layer, d_q, m, sm_scale, d_out, p, a);
   for (int b = 0; b < cf.batch; ++b) {
     a.nq[b] = seqs[b].nq;
     a.nt[b] = seqs[b].nt;
     a.head[b] = seqs[b].head;
   }
-  for (int b = 0; b <= cf.batch; ++b) {
-    a.qitem_base[b] = p.qbase[b];
-    a.titem_base[b] = p.tbase[b];
-  }
-  hipError_t e = qs::launch_attention(a, D, draft, static_cast<hipStream_t>(stream));
+  hipError_t e = qs::launch_attention(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
   c->err.clear();
   return QS_OK;
@@ -325,6 +358,7 @@ qs_status qs_attend_verify(qs_cache* c, int32_t layer, const void* d_q, int32_t 
 
 qs_status qs_get_state(const qs_cache* c, int32_t layer, int32_t* h_nq, int32_t* h_nt, int32_t* h_head) {
   if (!c || layer < 0 || layer >= c->cfg.n_layers) return QS_ERR_INVALID_ARG;
+  if (c->dev) return QS_ERR_STATE;
   for (int b = 0; b < c->cfg.batch; ++b) {
     const qs::Seq& s = c->st.at(layer, b);
     if (h_nq) h_nq[b] = s.nq;
@@ -332,6 +366,200 @@ qs_status qs_get_state(const qs_cache* c, int32_t layer, int32_t* h_nq, int32_t*
     if (h_head) h_head[b] = s.head;
   }
   return QS_OK;
+}
+
+// ---- device mode ---------------------------------------------------------------------------
+
+qs_status qs_state_to_device(qs_cache* c, void* stream) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (c->dev) return fail(c, QS_ERR_STATE, "already in device mode");
+  const qs_config& cf = c->cfg;
+  const size_t n = (size_t)cf.n_layers * cf.batch;
+  std::vector<int32_t> h(n * qs::kStateInts + 1, 0);
+  for (int l = 0; l < cf.n_layers; ++l)
+    for (int b = 0; b < cf.batch; ++b) {
+      const qs::Seq& q = c->st.at(l, b);
+      int32_t* e = &h[((size_t)l * cf.batch + b) * qs::kStateInts];
+      e[0] = q.nq;
+      e[1] = q.nt;
+      e[2] = q.head;
+    }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dev_state(c), h.data(), h.size() * sizeof(int32_t),
+                                hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return device_fail(c, e, "state to device");
+  c->dev = true;
+  c->err.clear();
+  return QS_OK;
+}
+
+qs_status qs_state_from_device(qs_cache* c, void* stream, int32_t* h_error) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!c->dev) return fail(c, QS_ERR_STATE, kInHostMode);
+  const qs_config& cf = c->cfg;
+  const size_t n = (size_t)cf.n_layers * cf.batch;
+  std::vector<int32_t> h(n * qs::kStateInts + 1, 0);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(h.data(), dev_state(c), h.size() * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return device_fail(c, e, "state from device");
+  for (size_t i = 0; i < n; ++i) {  // the device keeps these invariants; check before adopting
+    const int32_t* q = &h[i * qs::kStateInts];
+    if (q[0] < 0 || q[0] > cf.max_ctx || q[0] % cf.group || q[1] < 0 || q[1] > 2 * cf.group ||
+        (q[2] != 0 && q[2] != cf.group))
+      return fail(c, QS_ERR_DEVICE, "device counters out of range");
+  }
+  for (int l = 0; l < cf.n_layers; ++l)
+    for (int b = 0; b < cf.batch; ++b) {
+      const int32_t* q = &h[((size_t)l * cf.batch + b) * qs::kStateInts];
+      qs::Seq& s = c->st.at(l, b);
+      s.nq = q[0];
+      s.nt = q[1];
+      s.head = q[2];
+    }
+  if (h_error) *h_error = h[n * qs::kStateInts];
+  c->dev = false;
+  c->err.clear();
+  return QS_OK;
+}
+
+static qs::StateArgs state_args(const qs_cache* c, int op, int l0, int nl) {
+  qs::StateArgs a{};
+  a.state = dev_state(c);
+  a.err = dev_error(c);
+  a.op = op;
+  a.l0 = l0;
+  a.nl = nl;
+  a.B = c->cfg.batch;
+  a.G = c->cfg.group;
+  a.T = c->cfg.max_ctx;
+  return a;
+}
+
+qs_status qs_append_dev(qs_cache* c, int32_t layer, const void* d_k, const void* d_v, int32_t n,
+                        void* stream) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!c->dev) return fail(c, QS_ERR_STATE, kInHostMode);
+  const qs_config& cf = c->cfg;
+  if (layer < 0 || layer >= cf.n_layers) return fail(c, QS_ERR_INVALID_ARG, "layer out of range");
+  if (n < 0 || n > 2 * cf.group) return fail(c, QS_ERR_INVALID_ARG, "n must be in 0..2G");
+  if (!d_k || !d_v) return fail(c, QS_ERR_INVALID_ARG, "null k or v");
+  if (n == 0) return QS_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  qs::AppendArgs a{};
+  a.k = static_cast<const uint16_t*>(d_k);
+  a.v = static_cast<const uint16_t*>(d_v);
+  const size_t tail_lbh = (size_t)2 * cf.group * cf.head_dim * 2;
+  a.tail_k = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_k + layer_off(c, tail_lbh, layer));
+  a.tail_v = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_v + layer_off(c, tail_lbh, layer));
+  a.B = cf.batch;
+  a.H = cf.n_heads;
+  a.n_max = n;
+  a.n_rows = n;
+  a.dstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
+  for (int b = 0; b < cf.batch; ++b) a.n[b] = n;
+  hipError_t e = qs::launch_append(a, cf.head_dim, st);
+  if (e != hipSuccess) return device_fail(c, e, "append launch");
+  qs::StateArgs sa = state_args(c, 0, layer, 1);
+  sa.n = n;
+  e = qs::launch_state(sa, st);
+  if (e != hipSuccess) return device_fail(c, e, "state launch");
+  c->err.clear();
+  return QS_OK;
+}
+
+qs_status qs_rollback_dev(qs_cache* c, int32_t layer, int32_t n, const int32_t* d_sub,
+                          void* stream) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!c->dev) return fail(c, QS_ERR_STATE, kInHostMode);
+  const qs_config& cf = c->cfg;
+  if (layer < -1 || layer >= cf.n_layers) return fail(c, QS_ERR_INVALID_ARG, "layer out of range");
+  if (n < 0) return fail(c, QS_ERR_INVALID_ARG, "n must be >= 0");
+  const int l0 = layer < 0 ? 0 : layer, nl = layer < 0 ? cf.n_layers : 1;
+  qs::StateArgs sa = state_args(c, 1, l0, nl);
+  sa.n = n;
+  sa.sub = d_sub;
+  hipError_t e = qs::launch_state(sa, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(c, e, "state launch");
+  c->err.clear();
+  return QS_OK;
+}
+
+qs_status qs_flush_dev(qs_cache* c, int32_t layer, int32_t min_tail, void* stream) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!c->dev) return fail(c, QS_ERR_STATE, kInHostMode);
+  const qs_config& cf = c->cfg;
+  if (layer < -1 || layer >= cf.n_layers) return fail(c, QS_ERR_INVALID_ARG, "layer out of range");
+  if (min_tail > 2 * cf.group) return fail(c, QS_ERR_INVALID_ARG, "min_tail must be <= 2G");
+  const int l0 = layer < 0 ? 0 : layer, nl = layer < 0 ? cf.n_layers : 1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  qs::FlushArgs a{};
+  a.uk = c->arena + c->lay.uk;
+  a.lk = c->arena + c->lay.lk;
+  a.uv = c->arena + c->lay.uv;
+  a.lv = c->arena + c->lay.lv;
+  a.kmeta = reinterpret_cast<float*>(c->arena + c->lay.kmeta);
+  a.vmeta = reinterpret_cast<float*>(c->arena + c->lay.vmeta);
+  a.tail_k = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_k);
+  a.tail_v = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_v);
+  a.B = cf.batch;
+  a.H = cf.n_heads;
+  a.T = cf.max_ctx;
+  a.NG = cf.max_ctx / cf.group;
+  a.layer0 = l0;
+  a.n_sel = cf.batch;
+  for (int b = 0; b < cf.batch; ++b) a.b[b] = b;
+  a.dstate = dev_state(c);
+  a.thr = c->st.flush_threshold(min_tail);
+  hipError_t e = qs::launch_flush(a, cf.head_dim, nl, st);
+  if (e != hipSuccess) return device_fail(c, e, "flush launch");
+  qs::StateArgs sa = state_args(c, 2, l0, nl);
+  sa.thr = a.thr;
+  e = qs::launch_state(sa, st);
+  if (e != hipSuccess) return device_fail(c, e, "state launch");
+  c->err.clear();
+  return QS_OK;
+}
+
+static qs_status attend_dev(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
+                            float* d_out, void* stream, bool draft) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!c->dev) return fail(c, QS_ERR_STATE, kInHostMode);
+  const qs_config& cf = c->cfg;
+  if (layer < 0 || layer >= cf.n_layers) return fail(c, QS_ERR_INVALID_ARG, "layer out of range");
+  if (!draft && (m < 1 || m > cf.gamma_max + 1))
+    return fail(c, QS_ERR_INVALID_ARG, "m must be in 1..gamma_max+1");
+  if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
+  if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
+  // the plan of a full cache: every sequence at max_ctx with a full ring; workers and tail
+  // items past a sequence's current counters find no work and write empty records
+  qs::Seq full[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) {
+    full[b].nq = cf.max_ctx;
+    full[b].nt = 2 * cf.group;
+  }
+  const qs::Plan p = attn_plan(c, full, draft);
+  qs::AttnArgs a{};
+  attn_args(c, layer, d_q, m, sm_scale, d_out, p, a);
+  a.dstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
+  a.derr = dev_error(c);
+  a.min_nt = draft ? 0 : m;
+  hipError_t e = qs::launch_attention(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
+  c->err.clear();
+  return QS_OK;
+}
+
+qs_status qs_attend_draft_dev(qs_cache* c, int32_t layer, const void* d_q, float sm_scale,
+                              float* d_out, void* stream) {
+  return attend_dev(c, layer, d_q, 1, sm_scale, d_out, stream, true);
+}
+
+qs_status qs_attend_verify_dev(qs_cache* c, int32_t layer, const void* d_q, int32_t m,
+                               float sm_scale, float* d_out, void* stream) {
+  return attend_dev(c, layer, d_q, m, sm_scale, d_out, stream, false);
 }
 
 const char* qs_last_error(const qs_cache* c) { return c ? c->err.c_str() : "null cache"; }

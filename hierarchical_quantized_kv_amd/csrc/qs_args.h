@@ -1,6 +1,8 @@
 // qs_args.h -- plain-old-data kernel arguments shared by the host library and the HIP kernels.
 // Everything a kernel needs about the per-sequence bookkeeping is passed by value, so no call
-// copies host data to the device and no host buffer has to outlive its launch.
+// copies host data to the device and no host buffer has to outlive its launch -- except in
+// device mode, where the kernels read the counters from the arena's state section (dstate) and
+// the by-value copies are unused.
 #pragma once
 
 #include <stdint.h>
@@ -14,6 +16,15 @@ constexpr int kTailChunk = 64;        // tail tokens handled by one tail work it
 constexpr int kMaxTailItems = 2 * kGroup / kTailChunk;
 constexpr int kMaxQuantSplits = 256;  // quantized work items per (sequence, head), at most
 constexpr int kRecPad = 4;            // partial record = [max, sum, pad, pad, o[D]]
+constexpr int kStateInts = 4;         // device state per (layer, sequence): nq, nt, head, pad
+
+// Bits of the device-mode error word (the int32 after the last (layer, sequence) entry).
+enum : int32_t {
+  kDevErrAppend = 1,    // an append would have overflowed the 2G-slot tail (nothing written)
+  kDevErrRollback = 2,  // a rollback count was negative or past the tail (state unchanged)
+  kDevErrFlush = 4,     // a selected flush would have exceeded max_ctx (nothing written)
+  kDevErrAttend = 8,    // attention over an empty sequence, or verify with m > nt
+};
 
 // One attention call (draft or verify) on one layer: the fields that do not depend on the batch.
 struct AttnHeader {
@@ -35,6 +46,9 @@ struct AttnHeader {
   int32_t n_qitems_total, n_titems_total;
   float qscale;          // sm_scale * log2(e): scores are kept in the base-2 domain
   float draft_offset;    // 8 or 0 (draft only)
+  const int32_t* dstate; // device mode: this layer's [B][kStateInts] counters; else null
+  int32_t* derr;         // device mode: the error word
+  int32_t min_nt;        // device mode: tail tokens the call needs (verify: m; draft: 0)
 };
 
 // Per-sequence bookkeeping for at most NB sequences.  The kernels are instantiated for a few
@@ -58,6 +72,7 @@ struct AppendHeader {
   uint16_t* tail_v;
   int32_t B, H, n_max;
   int32_t n_rows;        // tokens per sequence the grid covers (n_max, or a prefill's longest rest)
+  const int32_t* dstate; // device mode: this layer's [B][kStateInts] counters (start = nt); else null
 };
 
 template <int NB>
@@ -104,6 +119,20 @@ struct FlushArgs {
   int32_t b[QS_MAX_BATCH];     // selected sequence ids
   int32_t group[QS_MAX_BATCH]; // destination group index nq / G
   int32_t head[QS_MAX_BATCH];  // ring slot of the oldest tail token (0 or G)
+  // device mode: the counters of all layers [L][B][kStateInts]; every sequence is in b[], and a
+  // block quantizes only if nt >= thr and nq + G <= T (group and head come from the counters)
+  const int32_t* dstate;
+  int32_t thr;
+};
+
+// Device-mode counter update after a verb's kernels, one thread per (layer, sequence).
+struct StateArgs {
+  int32_t* state;        // [L][B][kStateInts]
+  int32_t* err;          // error word
+  const int32_t* sub;    // rollback: per-sequence device counts subtracted from n (or null)
+  int32_t op;            // 0 append n, 1 rollback n - sub[b], 2 flush (nt >= thr)
+  int32_t l0, nl, B;
+  int32_t n, thr, G, T;
 };
 
 }  // namespace qs

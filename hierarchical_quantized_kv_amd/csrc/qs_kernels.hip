@@ -168,6 +168,20 @@ __device__ __forceinline__ float wave_sum_from(float x, int from) {
   return x;
 }
 
+// Counters of sequence b: the by-value copies, or in device mode this layer's state entries.
+template <class Args>
+__device__ __forceinline__ int seq_nq(const Args& a, int b) {
+  return a.dstate ? a.dstate[kStateInts * b] : a.nq[b];
+}
+template <class Args>
+__device__ __forceinline__ int seq_nt(const Args& a, int b) {
+  return a.dstate ? a.dstate[kStateInts * b + 1] : a.nt[b];
+}
+template <class Args>
+__device__ __forceinline__ int seq_head(const Args& a, int b) {
+  return a.dstate ? a.dstate[kStateInts * b + 2] : a.head[b];
+}
+
 // Record of split `split`, query `i` of (b, h).
 template <class Args>
 __device__ __forceinline__ float* record(const Args& a, int D, int b, int h, int split, int i) {
@@ -183,7 +197,7 @@ struct GroupStride {
 };
 template <class Args>
 __device__ __forceinline__ GroupStride worker_groups(const Args& a, int b, int item) {
-  return GroupStride{item, a.qitem_base[b + 1] - a.qitem_base[b], a.nq[b] / kGroup};
+  return GroupStride{item, a.qitem_base[b + 1] - a.qitem_base[b], seq_nq(a, b) / kGroup};
 }
 
 // The waves that share a SIMD issue oldest first, so with equal work the oldest finishes far
@@ -773,7 +787,7 @@ template <int D, class Args>
 __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, TailLds& L) {
   const int lane = threadIdx.x;
   const int m = a.m;
-  const int nt = a.nt[b];
+  const int nt = seq_nt(a, b);
   const int ring = 2 * kGroup;
   const size_t bh = (size_t)b * a.H + h;
   const int t0 = chunk * kTailChunk;
@@ -781,7 +795,7 @@ __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, Tai
   const bool valid = t < nt;
   const int nvalid = min(kTailChunk, nt - t0);
   // head and t0 are multiples of 64, so the chunk's ring slots s0 .. s0 + 63 never wrap
-  const int s0 = (a.head[b] + t0) % ring;
+  const int s0 = (seq_head(a, b) + t0) % ring;
   const uint16_t* kchunk = a.tail_k + (bh * ring + s0) * D;
   const uint16_t* vchunk = a.tail_v + (bh * ring + s0) * D;
 
@@ -960,6 +974,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB> a) {
   const int t = threadIdx.x;
   const int c = t % C4, p = t / C4;
   const int ns = (a.qitem_base[b + 1] - a.qitem_base[b]) + (a.titem_base[b + 1] - a.titem_base[b]);
+  if (a.derr && h == 0 && i == 0 && t == 0) {  // device mode: the checks the host cannot make
+    const int nq = seq_nq(a, b), nt = seq_nt(a, b);
+    if (nq + nt == 0 || nt < a.min_nt) atomicOr(a.derr, kDevErrAttend);
+  }
 
   float m = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1007,7 +1025,13 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgsN<NB> a) {
   const int b = row / (a.H * a.n_rows);
   if (b >= a.B || i >= a.n[b]) return;
   const int ring = 2 * kGroup;
-  const int slot = (a.head[b] + a.start[b] + i) % ring;
+  int start = a.start[b], head = a.head[b];
+  if (a.dstate) {  // device mode: an append past the ring writes nothing (the state kernel flags it)
+    start = a.dstate[kStateInts * b + 1];
+    head = a.dstate[kStateInts * b + 2];
+    if (start + a.n[b] > ring) return;
+  }
+  const int slot = (head + start + i) % ring;
   const size_t src = (((size_t)b * a.n_max + a.src0[b] + i) * a.H + h) * D + 8 * c;
   const size_t dst = (((size_t)b * a.H + h) * ring + slot) * D + 8 * c;
   *reinterpret_cast<uint4*>(a.tail_k + dst) = ld16(a.k + src);
@@ -1208,11 +1232,19 @@ __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
   const int sel = by;
   const int layer = a.layer0 + bz;
   const size_t lbh = ((size_t)layer * a.B + a.b[sel]) * a.H + h;
-  const size_t ring0 = (lbh * (2 * kGroup) + a.head[sel]) * D;  // oldest ring half, token-major
+  int group = a.group[sel], head = a.head[sel];
+  if (a.dstate) {  // device mode: this sequence flushes only if selected and within capacity
+    const int32_t* st = a.dstate + ((size_t)layer * a.B + a.b[sel]) * kStateInts;
+    const int nq = st[0], nt = st[1];
+    if (nt < a.thr || nq + kGroup > a.T) return;
+    group = nq / kGroup;
+    head = st[2];
+  }
+  const size_t ring0 = (lbh * (2 * kGroup) + head) * D;  // oldest ring half, token-major
   if (blk < NK)
-    flush_keys<D>(a, lbh, a.group[sel], a.tail_k + ring0, D, blk * kFlushSlice, lds.k);
+    flush_keys<D>(a, lbh, group, a.tail_k + ring0, D, blk * kFlushSlice, lds.k);
   else
-    flush_values<D>(a, lbh, a.group[sel], a.tail_v + ring0, D, (blk - NK) * kFlushSlice, lds.v);
+    flush_values<D>(a, lbh, group, a.tail_v + ring0, D, (blk - NK) * kFlushSlice, lds.v);
 }
 
 // Prefill: group g of sequence b's prompt (tokens g*G .. g*G+G-1 of k / v [B][n_max][H][D]) into
@@ -1238,6 +1270,37 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
     flush_keys<D>(a, lbh, a.group0[b] + g, a.k + src0, stride, blk * kFlushSlice, lds.k);
   else
     flush_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, (blk - NK) * kFlushSlice, lds.v);
+}
+
+// ------------------------------------------------------------------------------------------
+// Device-mode counter updates: run after the kernels of the verb they account for (stream
+// order), so those kernels all saw the counters from before the verb.  The same tests as the
+// host-side checks decide; a failing sequence keeps its counters and sets its error bit.
+// ------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void state_kernel(const StateArgs a) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.nl * a.B) return;
+  const int b = idx % a.B, layer = a.l0 + idx / a.B;
+  int32_t* st = a.state + ((size_t)layer * a.B + b) * kStateInts;
+  const int nq = st[0], nt = st[1], head = st[2];
+  const int ring = 2 * a.G;
+  if (a.op == 0) {
+    if (nt + a.n <= ring) st[1] = nt + a.n;
+    else atomicOr(a.err, kDevErrAppend);
+  } else if (a.op == 1) {
+    const int drop = a.n - (a.sub ? a.sub[b] : 0);
+    if (drop >= 0 && drop <= nt) st[1] = nt - drop;
+    else atomicOr(a.err, kDevErrRollback);
+  } else if (nt >= a.thr) {
+    if (nq + a.G <= a.T) {
+      st[0] = nq + a.G;
+      st[1] = nt - a.G;
+      st[2] = head ^ a.G;
+    } else {
+      atomicOr(a.err, kDevErrFlush);
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1305,6 +1368,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream
   const dim3 grid(a.H * per_head, max_groups, a.B);
   if (D == 128) hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(64), 0, st, a);
   else hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_state(const StateArgs& a, hipStream_t st) {
+  const int n = a.nl * a.B;
+  hipLaunchKernelGGL(state_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

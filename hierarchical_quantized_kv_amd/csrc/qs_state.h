@@ -51,6 +51,7 @@ inline qs_layout make_layout(const qs_config& c) {
   L.tail_bytes = align256(lbh * 2 * G * D * 2);
   L.work_bytes = align256((size_t)c.batch * c.n_heads * record_slots() * (c.gamma_max + 1) *
                           (D + kRecPad) * sizeof(float));
+  L.state_bytes = align256(((size_t)c.n_layers * c.batch * kStateInts + 1) * sizeof(int32_t));
   size_t o = 0;
   L.uk = o; o += L.uk_bytes;
   L.lk = o; o += L.uk_bytes;
@@ -61,6 +62,7 @@ inline qs_layout make_layout(const qs_config& c) {
   L.tail_k = o; o += L.tail_bytes;
   L.tail_v = o; o += L.tail_bytes;
   L.work = o; o += L.work_bytes;
+  L.state = o; o += L.state_bytes;
   L.total = o;
   return L;
 }

@@ -104,10 +104,13 @@ typedef struct {
  *  tail_k,  f16 [L][B][H][2G][D]       fp16 tail ring.  Logical tail token i of a sequence
  *  tail_v                              lives in slot (head + i) mod 2G, head in {0, G}.
  *  work     --                         split-softmax workspace (library private).
+ *  state    i32 [L][B][4] + 1          device-mode counters (nq, nt, head, unused) per layer
+ *                                      and sequence, then the device-mode error word.
  */
 typedef struct {
-  size_t uk, lk, uv, lv, kmeta, vmeta, tail_k, tail_v, work;               /* offsets */
-  size_t uk_bytes, uv_bytes, kmeta_bytes, vmeta_bytes, tail_bytes, work_bytes; /* per section */
+  size_t uk, lk, uv, lv, kmeta, vmeta, tail_k, tail_v, work, state;        /* offsets */
+  size_t uk_bytes, uv_bytes, kmeta_bytes, vmeta_bytes, tail_bytes, work_bytes,
+      state_bytes;                                                          /* per section */
   size_t total;                                                             /* = qs_arena_bytes */
 } qs_layout;
 
@@ -222,6 +225,47 @@ qs_status qs_attend_verify(qs_cache* cache, int32_t layer, const void* d_q, int3
  * NULL). */
 qs_status qs_get_state(const qs_cache* cache, int32_t layer, int32_t* h_nq, int32_t* h_nt,
                        int32_t* h_head);
+
+/* ---- Device mode: the bookkeeping in device memory -----------------------------------------
+ * The same verbs with the counters (nq, nt, head) held in the arena's state section and
+ * advanced by the device, so that their calls can be captured in a HIP graph and the graph
+ * replayed round after round, with rollback counts that come from the device (the accept
+ * step's d_n_accepted).  [QuantSpec Guide, "3. Double Full-Precision Cache Buffer (CF1 and
+ * CF2)" and the verification-loop listing (commit, then roll back the speculative buffer);
+ * Pith review, "What carries the argument".]
+ *
+ * qs_state_to_device copies the host counters into the state section, clears the error word
+ * and switches the handle to device mode; qs_state_from_device copies the counters back,
+ * writes the error word to *h_error (if not NULL) and switches back to host mode.  Both
+ * synchronize with `stream` (the only calls that do).  In device mode the host verbs above
+ * (and qs_get_state) return QS_ERR_STATE, and in host mode the _dev verbs do.
+ *
+ * The _dev verbs validate their arguments on the host (QS_ERR_INVALID_ARG) and enqueue kernels
+ * only: no host state changes, no synchronization, no allocation, no memset.  Conditions that
+ * depend on the counters are checked by the device: the affected sequence is left unchanged
+ * and a bit is set in the error word (1: append past 2G; 2: rollback count negative or past
+ * the tail; 4: flush past max_ctx; 8: attention over an empty sequence, or verify with
+ * m > nt).  The outputs of a flagged attention call are unspecified (finite or not).
+ *
+ * qs_append_dev: n tokens for every sequence (d_k, d_v fp16 [B][n][H][D]), 0 <= n <= 2G.
+ * qs_rollback_dev: drops n - d_sub[b] tail tokens of sequence b (n tokens if d_sub is NULL) of
+ *   `layer`, or of every layer when layer == -1; d_sub: device int32 [B].
+ * qs_flush_dev: quantizes the oldest G tail tokens of every sequence with nt >= max(G,
+ *   min_tail), as qs_flush.
+ * qs_attend_draft_dev / qs_attend_verify_dev: as the host verbs, over a fixed work plan sized
+ *   for a full cache (every sequence at max_ctx), so that a captured call stays valid while
+ *   the counters grow. */
+qs_status qs_state_to_device(qs_cache* cache, void* stream);
+qs_status qs_state_from_device(qs_cache* cache, void* stream, int32_t* h_error);
+qs_status qs_append_dev(qs_cache* cache, int32_t layer, const void* d_k, const void* d_v,
+                        int32_t n, void* stream);
+qs_status qs_rollback_dev(qs_cache* cache, int32_t layer, int32_t n, const int32_t* d_sub,
+                          void* stream);
+qs_status qs_flush_dev(qs_cache* cache, int32_t layer, int32_t min_tail, void* stream);
+qs_status qs_attend_draft_dev(qs_cache* cache, int32_t layer, const void* d_q, float sm_scale,
+                              float* d_out, void* stream);
+qs_status qs_attend_verify_dev(qs_cache* cache, int32_t layer, const void* d_q, int32_t m,
+                               float sm_scale, float* d_out, void* stream);
 
 /* Message of the last error on this handle ("" if none).  Valid until the next call. */
 const char* qs_last_error(const qs_cache* cache);

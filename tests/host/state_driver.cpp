@@ -83,8 +83,8 @@ int main() {
       continue;
     } else if (op == "layout") {
       qs_layout L = qs::make_layout(cfg);
-      std::printf("layout %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", L.uk, L.lk, L.uv, L.lv,
-                  L.kmeta, L.vmeta, L.tail_k, L.tail_v, L.work, L.total);
+      std::printf("layout %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", L.uk, L.lk, L.uv, L.lv,
+                  L.kmeta, L.vmeta, L.tail_k, L.tail_v, L.work, L.state, L.total);
       continue;
     } else {
       std::printf("status -1 unknown op\n");

@@ -56,8 +56,10 @@ def test_arena_size_and_layout(lib):
     lay = QsLayout()
     assert lib.qs_arena_layout(ctypes.byref(c), ctypes.byref(lay)) == 0
     assert n == lay.total > 0
-    offs = [lay.uk, lay.lk, lay.uv, lay.lv, lay.kmeta, lay.vmeta, lay.tail_k, lay.tail_v, lay.work]
+    offs = [lay.uk, lay.lk, lay.uv, lay.lv, lay.kmeta, lay.vmeta, lay.tail_k, lay.tail_v, lay.work,
+            lay.state]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.state + lay.state_bytes == lay.total and lay.state_bytes >= (2 * 3 * 4 + 1) * 4
     lbh = 2 * 3 * 4
     assert lay.uk_bytes == lbh * 8 * G * 64 and lay.uv_bytes == lbh * 8 * 128 * 64
     for bad in (cfg(head_dim=96), cfg(group=64), cfg(max_ctx=100), cfg(batch=0),
@@ -139,6 +141,25 @@ def test_validation_before_any_launch(lib):
     assert lib.qs_attend_draft(h, 0, P, ctypes.c_float(float("nan")), P, None) == binding.QS_ERR_INVALID_ARG
     assert lib.qs_attend_draft(h, 0, None, ctypes.c_float(1.0), P, None) == binding.QS_ERR_INVALID_ARG
     assert lib.qs_get_state(h, 0, nq, nt, hd) == 0 and list(nt) == [0, 0, 0]
+    lib.qs_cache_destroy(h)
+
+
+def test_device_mode_verbs_rejected_in_host_mode(lib):
+    """Before qs_state_to_device the _dev verbs (and qs_state_from_device) return QS_ERR_STATE
+    without launching anything; host verbs keep working."""
+    h = create(lib, cfg())
+    P = ctypes.c_void_p(FAKE)
+    F1 = ctypes.c_float(1.0)
+    err = arr(0)
+    for st in (lib.qs_state_from_device(h, None, err),
+               lib.qs_append_dev(h, 0, P, P, 1, None),
+               lib.qs_rollback_dev(h, -1, 1, None, None),
+               lib.qs_flush_dev(h, -1, G, None),
+               lib.qs_attend_draft_dev(h, 0, P, F1, P, None),
+               lib.qs_attend_verify_dev(h, 0, P, 2, F1, P, None)):
+        assert st == binding.QS_ERR_STATE
+        assert b"device mode" in lib.qs_last_error(h)
+    assert lib.qs_rollback(h, -1, arr(0, 0, 0)) == 0
     lib.qs_cache_destroy(h)
 
 

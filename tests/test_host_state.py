@@ -160,8 +160,8 @@ def test_plan_covers_every_group(driver):
 
 def test_layout_sections(driver):
     out = run(driver, ["create 2 3 4 128 128 1024 6 8", "layout"])[-1].split()[1:]
-    uk, lk, uv, lv, km, vm, tk, tv, work, total = map(int, out)
-    offs = [uk, lk, uv, lv, km, vm, tk, tv, work, total]
+    uk, lk, uv, lv, km, vm, tk, tv, work, state, total = map(int, out)
+    offs = [uk, lk, uv, lv, km, vm, tk, tv, work, state, total]
     assert offs == sorted(offs) and all(x % 256 == 0 for x in offs)
     lbh, T, D = 2 * 3 * 4, 1024, 128
     assert lk - uk == uv - lk == lbh * T * D // 2
@@ -169,4 +169,6 @@ def test_layout_sections(driver):
     assert vm - km == lbh * (T // G) * D * 8
     assert tk - vm == lbh * T * 8
     assert tv - tk == work - tv == lbh * 2 * G * D * 2
-    assert total - work == 3 * 4 * (256 + 4) * 7 * (D + 4) * 4
+    assert state - work == 3 * 4 * (256 + 4) * 7 * (D + 4) * 4
+    # device-mode counters: 4 int32 per (layer, sequence) and the error word, 256-byte aligned
+    assert total - state == -(-(2 * 3 * 4 + 1) * 4 // 256) * 256
