@@ -242,6 +242,13 @@ def main():
     value = total_bytes / elapsed / 1e9
     print(f"bench: {args.steps} timed steps in {elapsed:.3f}s", file=sys.stderr, flush=True)
 
+    # The same step replayed from a HIP graph (device mode): the step's calls are captured once
+    # with the counters in device memory, and each replay advances them on the device; only the
+    # step's accepted count is copied into a device word before each replay.  Bytes per step
+    # from a host mirror of the counters (every layer sees the same calls).
+    graph_line = measure_graph_steps(torch, cache, steps_in[0], accept, args, L, H, D, gamma, m,
+                                     out_d, out_v, dev, stream)
+
     # Bulk flush (outside the timed steps): every layer gets G more tail tokens, then one
     # qs_flush(-1) quantizes one G-token half of every (layer, head) in a single launch.
     # (timed behind the spin kernel, like the prefill)
@@ -367,12 +374,77 @@ def main():
                            "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                            "bound": "latency (dependent round trips)" if sb == 1 else "hbm"}
             for sb, (us, gbs, nb) in sa.items()},
+        "graph_step": graph_line,
         "samples_dropped": dropped,
         "read_ceiling": read_ceiling,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_graph_steps(torch, cache, x, accept, args, L, H, D, gamma, m, out_d, out_v, dev,
+                        stream):
+    nq0, nt0, _ = cache.state(0)
+    nq, nt = int(nq0[0]), int(nt0[0])
+    acc_all = torch.tensor(accept, dtype=torch.int32, device=dev)
+    acc = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def ops(st):
+        for j in range(gamma):
+            for layer in range(L):
+                cache.append_dev(layer, x["dk"][j, layer], x["dv"][j, layer], stream=st)
+                cache.attend_draft_dev(layer, x["qd"][j, layer], out_d, stream=st)
+        for layer in range(L):
+            cache.rollback_dev(layer, gamma, stream=st)
+            cache.append_dev(layer, x["tk"][layer], x["tv"][layer], stream=st)
+            cache.attend_verify_dev(layer, x["qv"][layer], out_v, stream=st)
+            cache.rollback_dev(layer, gamma, sub=acc, stream=st)
+        cache.flush_dev(-1, G, stream=st)
+
+    def mirror(nq, nt, a):
+        nbytes = 0
+        for _ in range(gamma):
+            nt += 1
+            nbytes += L * (append_bytes(1, H, D) + draft_bytes(nq, nt, H, D))
+        nt += m - gamma
+        nbytes += L * (append_bytes(m, H, D) + verify_bytes(nq, nt, H, D, m))
+        nt -= gamma - a
+        if nt >= G:
+            nq, nt = nq + G, nt - G
+            nbytes += L * flush_bytes(H, D)
+        return nq, nt, nbytes
+
+    cache.to_device_state()
+    acc.copy_(acc_all[0:1])
+    ops(stream)                                   # one eager step in device mode
+    nq, nt, _ = mirror(nq, nt, accept[0])
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        ops(cap)
+    n = min(args.steps, len(accept) - 1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total = 0
+    e0.record(stream)
+    for s in range(1, n + 1):
+        acc.copy_(acc_all[s:s + 1])
+        graph.replay()
+        nq, nt, b = mirror(nq, nt, accept[s])
+        total += b
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    err = cache.from_device_state()
+    dq, dt, _ = cache.state(L - 1)
+    assert err == 0 and (int(dq[0]), int(dt[0])) == (nq, nt), (err, dq, dt, nq, nt)
+    return {"ms_per_step": round(ms, 4), "steps": n,
+            "gbs": round(total / n / (ms * 1e-3) / 1e9, 1),
+            "calls_per_step": L * (2 * gamma + 4) + 1,
+            "note": "the timed step's calls captured once in a HIP graph (device-mode bookkeeping) "
+                    "and replayed; each replay preceded by a 4-byte device copy of the step's "
+                    "accepted count"}
 
 
 def measure_read_ceiling(torch, stream):

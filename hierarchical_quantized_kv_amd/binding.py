@@ -23,7 +23,8 @@ EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_des
            "qs_append", "qs_prefill", "qs_rollback", "qs_flush", "qs_attend_draft",
            "qs_attend_verify", "qs_get_state", "qs_last_error", "qs_spec_workspace_bytes",
            "qs_spec_accept", "qs_state_to_device", "qs_state_from_device", "qs_append_dev",
-           "qs_rollback_dev", "qs_flush_dev", "qs_attend_draft_dev", "qs_attend_verify_dev")
+           "qs_rollback_dev", "qs_flush_dev", "qs_commit_dev", "qs_attend_draft_dev",
+           "qs_attend_verify_dev")
 
 # Bits of the device-mode error word (include/quantspec.h, device mode).
 DEV_ERR_APPEND, DEV_ERR_ROLLBACK, DEV_ERR_FLUSH, DEV_ERR_ATTEND = 1, 2, 4, 8
@@ -84,6 +85,7 @@ def lib():
         L.qs_append_dev.argtypes = [P, I32, P, P, I32, P]
         L.qs_rollback_dev.argtypes = [P, I32, I32, P, P]
         L.qs_flush_dev.argtypes = [P, I32, I32, P]
+        L.qs_commit_dev.argtypes = [P, I32, P]
         L.qs_attend_draft_dev.argtypes = [P, I32, P, F, P, P]
         L.qs_attend_verify_dev.argtypes = [P, I32, P, I32, F, P, P]
         for f in EXPORTS:
@@ -239,7 +241,8 @@ class Cache:
                                         self._stream(stream)), "qs_append_dev")
 
     def rollback_dev(self, layer, n, sub=None, stream=None):
-        """Drops n - sub[b] tail tokens of each sequence b (sub: device int32 [B] or None)."""
+        """Drops n - sub[b] tail tokens of each sequence b (sub: device int32 [B] or None; it
+        must keep its values until the rollback is committed)."""
         p = None
         if sub is not None:
             assert tuple(sub.shape) == (self.B,)
@@ -250,6 +253,9 @@ class Cache:
     def flush_dev(self, layer=-1, min_tail=None, stream=None):
         self._check(lib().qs_flush_dev(self._h, layer, self.G if min_tail is None else min_tail,
                                        self._stream(stream)), "qs_flush_dev")
+
+    def commit_dev(self, layer=-1, stream=None):
+        self._check(lib().qs_commit_dev(self._h, layer, self._stream(stream)), "qs_commit_dev")
 
     def attend_draft_dev(self, layer, q, out, sm_scale=1.0, stream=None):
         torch = self.torch

@@ -4,8 +4,11 @@
 // its kernels on the caller's stream, and only then updates the State.  No verb synchronizes
 // with the device or copies host data to it: per-sequence counters travel as kernel arguments.
 // In device mode (qs_state_to_device .. qs_state_from_device) the counters live in the arena's
-// state section instead: the _dev verbs enqueue their kernels plus a counter-update kernel and
-// touch no host state, so a sequence of them can be captured in a graph and replayed.
+// state section instead.  Appends and rollbacks are recorded as pending operations of their
+// layer, passed by value to every later kernel that reads the counters and committed by the
+// next attention call (its combine kernel), flush or commit; so the _dev verbs launch the same
+// kernels as the host verbs (plus one small kernel per flush) and a sequence of them can be
+// captured in a graph and replayed, provided it starts and ends with nothing pending.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -34,6 +37,7 @@ struct qs_cache {
   qs::State st;
   std::string err;
   bool dev = false;  // device mode: the counters are in the state section, not in st
+  std::vector<qs::Pending> pend;  // device mode: per layer, operations not yet committed
 };
 
 namespace {
@@ -390,6 +394,64 @@ qs_status qs_state_to_device(qs_cache* c, void* stream) {
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return device_fail(c, e, "state to device");
   c->dev = true;
+  c->pend.assign(cf.n_layers, qs::Pending{});
+  c->err.clear();
+  return QS_OK;
+}
+
+static qs::StateArgs state_args(const qs_cache* c, int op, int l0, int nl) {
+  qs::StateArgs a{};
+  a.state = dev_state(c);
+  a.err = dev_error(c);
+  a.op = op;
+  a.l0 = l0;
+  a.nl = nl;
+  a.B = c->cfg.batch;
+  a.G = c->cfg.group;
+  a.T = c->cfg.max_ctx;
+  return a;
+}
+
+// Writes the pending operations of layers l0 .. l1-1 to the state section (one small launch per
+// layer that has any).
+static hipError_t commit_layers(qs_cache* c, int l0, int l1, hipStream_t st) {
+  for (int l = l0; l < l1; ++l) {
+    if (c->pend[l].count == 0) continue;
+    qs::StateArgs sa = state_args(c, 0, l, 1);
+    sa.pend = c->pend[l];
+    hipError_t e = qs::launch_state(sa, st);
+    if (e != hipSuccess) return e;
+    c->pend[l] = qs::Pending{};
+  }
+  return hipSuccess;
+}
+
+static bool same_pending(const qs::Pending& x, const qs::Pending& y) {
+  if (x.count != y.count) return false;
+  for (int k = 0; k < x.count; ++k)
+    if (x.op[k].kind != y.op[k].kind || x.op[k].n != y.op[k].n || x.op[k].sub != y.op[k].sub)
+      return false;
+  return true;
+}
+
+// Records an operation of `layer`, committing the full list first if needed.
+static hipError_t push_pending(qs_cache* c, int layer, qs::PendingOp op, hipStream_t st) {
+  if (c->pend[layer].count == qs::kMaxPending) {
+    hipError_t e = commit_layers(c, layer, layer + 1, st);
+    if (e != hipSuccess) return e;
+  }
+  qs::Pending& p = c->pend[layer];
+  p.op[p.count++] = op;
+  return hipSuccess;
+}
+
+qs_status qs_commit_dev(qs_cache* c, int32_t layer, void* stream) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (!c->dev) return fail(c, QS_ERR_STATE, kInHostMode);
+  if (layer < -1 || layer >= c->cfg.n_layers) return fail(c, QS_ERR_INVALID_ARG, "layer out of range");
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->cfg.n_layers : layer + 1;
+  hipError_t e = commit_layers(c, l0, l1, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(c, e, "state launch");
   c->err.clear();
   return QS_OK;
 }
@@ -398,6 +460,10 @@ qs_status qs_state_from_device(qs_cache* c, void* stream, int32_t* h_error) {
   if (!c) return QS_ERR_INVALID_ARG;
   if (!c->dev) return fail(c, QS_ERR_STATE, kInHostMode);
   const qs_config& cf = c->cfg;
+  {
+    hipError_t e = commit_layers(c, 0, cf.n_layers, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(c, e, "state launch");
+  }
   const size_t n = (size_t)cf.n_layers * cf.batch;
   std::vector<int32_t> h(n * qs::kStateInts + 1, 0);
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -425,19 +491,6 @@ qs_status qs_state_from_device(qs_cache* c, void* stream, int32_t* h_error) {
   return QS_OK;
 }
 
-static qs::StateArgs state_args(const qs_cache* c, int op, int l0, int nl) {
-  qs::StateArgs a{};
-  a.state = dev_state(c);
-  a.err = dev_error(c);
-  a.op = op;
-  a.l0 = l0;
-  a.nl = nl;
-  a.B = c->cfg.batch;
-  a.G = c->cfg.group;
-  a.T = c->cfg.max_ctx;
-  return a;
-}
-
 qs_status qs_append_dev(qs_cache* c, int32_t layer, const void* d_k, const void* d_v, int32_t n,
                         void* stream) {
   if (!c) return QS_ERR_INVALID_ARG;
@@ -460,11 +513,14 @@ qs_status qs_append_dev(qs_cache* c, int32_t layer, const void* d_k, const void*
   a.n_rows = n;
   a.dstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
   for (int b = 0; b < cf.batch; ++b) a.n[b] = n;
+  if (c->pend[layer].count == qs::kMaxPending) {  // room for this append's own entry
+    hipError_t e = commit_layers(c, layer, layer + 1, st);
+    if (e != hipSuccess) return device_fail(c, e, "state launch");
+  }
+  a.pend = c->pend[layer];
   hipError_t e = qs::launch_append(a, cf.head_dim, st);
   if (e != hipSuccess) return device_fail(c, e, "append launch");
-  qs::StateArgs sa = state_args(c, 0, layer, 1);
-  sa.n = n;
-  e = qs::launch_state(sa, st);
+  e = push_pending(c, layer, qs::PendingOp{0, n, nullptr}, st);
   if (e != hipSuccess) return device_fail(c, e, "state launch");
   c->err.clear();
   return QS_OK;
@@ -477,12 +533,11 @@ qs_status qs_rollback_dev(qs_cache* c, int32_t layer, int32_t n, const int32_t* 
   const qs_config& cf = c->cfg;
   if (layer < -1 || layer >= cf.n_layers) return fail(c, QS_ERR_INVALID_ARG, "layer out of range");
   if (n < 0) return fail(c, QS_ERR_INVALID_ARG, "n must be >= 0");
-  const int l0 = layer < 0 ? 0 : layer, nl = layer < 0 ? cf.n_layers : 1;
-  qs::StateArgs sa = state_args(c, 1, l0, nl);
-  sa.n = n;
-  sa.sub = d_sub;
-  hipError_t e = qs::launch_state(sa, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return device_fail(c, e, "state launch");
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? cf.n_layers : layer + 1;
+  for (int l = l0; l < l1; ++l) {
+    hipError_t e = push_pending(c, l, qs::PendingOp{1, n, d_sub}, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(c, e, "state launch");
+  }
   c->err.clear();
   return QS_OK;
 }
@@ -495,6 +550,13 @@ qs_status qs_flush_dev(qs_cache* c, int32_t layer, int32_t min_tail, void* strea
   if (min_tail > 2 * cf.group) return fail(c, QS_ERR_INVALID_ARG, "min_tail must be <= 2G");
   const int l0 = layer < 0 ? 0 : layer, nl = layer < 0 ? cf.n_layers : 1;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  // one launch serves layers with the same pending operations; otherwise commit them first
+  for (int l = l0 + 1; l < l0 + nl; ++l)
+    if (!same_pending(c->pend[l], c->pend[l0])) {
+      hipError_t e = commit_layers(c, l0, l0 + nl, st);
+      if (e != hipSuccess) return device_fail(c, e, "state launch");
+      break;
+    }
   qs::FlushArgs a{};
   a.uk = c->arena + c->lay.uk;
   a.lk = c->arena + c->lay.lk;
@@ -513,12 +575,15 @@ qs_status qs_flush_dev(qs_cache* c, int32_t layer, int32_t min_tail, void* strea
   for (int b = 0; b < cf.batch; ++b) a.b[b] = b;
   a.dstate = dev_state(c);
   a.thr = c->st.flush_threshold(min_tail);
+  a.pend = c->pend[l0];
   hipError_t e = qs::launch_flush(a, cf.head_dim, nl, st);
   if (e != hipSuccess) return device_fail(c, e, "flush launch");
-  qs::StateArgs sa = state_args(c, 2, l0, nl);
+  qs::StateArgs sa = state_args(c, 1, l0, nl);
   sa.thr = a.thr;
+  sa.pend = c->pend[l0];
   e = qs::launch_state(sa, st);
   if (e != hipSuccess) return device_fail(c, e, "state launch");
+  for (int l = l0; l < l0 + nl; ++l) c->pend[l] = qs::Pending{};
   c->err.clear();
   return QS_OK;
 }
@@ -533,21 +598,35 @@ static qs_status attend_dev(qs_cache* c, int32_t layer, const void* d_q, int32_t
     return fail(c, QS_ERR_INVALID_ARG, "m must be in 1..gamma_max+1");
   if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
   if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
-  // the plan of a full cache: every sequence at max_ctx with a full ring; workers and tail
-  // items past a sequence's current counters find no work and write empty records
-  qs::Seq full[QS_MAX_BATCH];
+  // a plan that holds for any counters: kMaxTailItems tail items per sequence and head, and W
+  // quantized workers filling the rest of one resident round (worker w takes groups w, w + W,
+  // .. of whatever the sequence holds).  Tail items past nt exit at once, so they are counted
+  // as half their number.  Workers and items with no work write empty records.
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch);
+  if (slots <= 0) slots = kFallbackSlots;
+  const int bh = cf.batch * cf.n_heads;
+  int W = (slots - bh * qs::kMaxTailItems / 2) / bh;
+  W = W < 1 ? 1 : (W > qs::kMaxQuantSplits ? qs::kMaxQuantSplits : W);
+  const int NG = cf.max_ctx / cf.group;
+  if (W > NG) W = NG;
+  qs::Plan p;
+  p.chunk_groups = (NG + W - 1) / W;
   for (int b = 0; b < cf.batch; ++b) {
-    full[b].nq = cf.max_ctx;
-    full[b].nt = 2 * cf.group;
+    p.qitems[b] = W;
+    p.titems[b] = qs::kMaxTailItems;
+    p.qbase[b + 1] = p.qbase[b] + W;
+    p.tbase[b + 1] = p.tbase[b] + qs::kMaxTailItems;
   }
-  const qs::Plan p = attn_plan(c, full, draft);
   qs::AttnArgs a{};
   attn_args(c, layer, d_q, m, sm_scale, d_out, p, a);
   a.dstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
+  a.wstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
   a.derr = dev_error(c);
   a.min_nt = draft ? 0 : m;
+  a.pend = c->pend[layer];
   hipError_t e = qs::launch_attention(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
+  c->pend[layer] = qs::Pending{};  // committed by the combine kernel
   c->err.clear();
   return QS_OK;
 }

@@ -18,6 +18,22 @@ constexpr int kMaxQuantSplits = 256;  // quantized work items per (sequence, hea
 constexpr int kRecPad = 4;            // partial record = [max, sum, pad, pad, o[D]]
 constexpr int kStateInts = 4;         // device state per (layer, sequence): nq, nt, head, pad
 
+// Device mode: counter changes of appends and rollbacks not yet written to the state section.
+// Every kernel that reads nt applies them in order (with the same checks as the host verbs, a
+// failing operation being skipped); the next attention call's combine kernel, or the state
+// kernel of a flush or commit, writes the result back -- after every reader of the old value
+// has finished.  So appends and rollbacks launch no kernel of their own for the counters.
+constexpr int kMaxPending = 4;
+struct PendingOp {
+  int32_t kind;        // 0: append n tokens; 1: roll back n - sub[b] tokens
+  int32_t n;
+  const int32_t* sub;  // rollback: device int32 [B] (or null)
+};
+struct Pending {
+  int32_t count;
+  PendingOp op[kMaxPending];
+};
+
 // Bits of the device-mode error word (the int32 after the last (layer, sequence) entry).
 enum : int32_t {
   kDevErrAppend = 1,    // an append would have overflowed the 2G-slot tail (nothing written)
@@ -49,6 +65,8 @@ struct AttnHeader {
   const int32_t* dstate; // device mode: this layer's [B][kStateInts] counters; else null
   int32_t* derr;         // device mode: the error word
   int32_t min_nt;        // device mode: tail tokens the call needs (verify: m; draft: 0)
+  int32_t* wstate;       // device mode: where the combine kernel commits the pending operations
+  Pending pend;          // device mode: this layer's pending operations
 };
 
 // Per-sequence bookkeeping for at most NB sequences.  The kernels are instantiated for a few
@@ -73,6 +91,7 @@ struct AppendHeader {
   int32_t B, H, n_max;
   int32_t n_rows;        // tokens per sequence the grid covers (n_max, or a prefill's longest rest)
   const int32_t* dstate; // device mode: this layer's [B][kStateInts] counters (start = nt); else null
+  Pending pend;          // device mode: this layer's pending operations, before this append
 };
 
 template <int NB>
@@ -123,16 +142,18 @@ struct FlushArgs {
   // block quantizes only if nt >= thr and nq + G <= T (group and head come from the counters)
   const int32_t* dstate;
   int32_t thr;
+  Pending pend;          // pending operations of every layer of the launch (the same list)
 };
 
-// Device-mode counter update after a verb's kernels, one thread per (layer, sequence).
+// Device-mode commit of the pending operations of layers l0 .. l0+nl-1 (the same list for all),
+// then, for op 1, the flush's counter update; one thread per (layer, sequence).
 struct StateArgs {
   int32_t* state;        // [L][B][kStateInts]
   int32_t* err;          // error word
-  const int32_t* sub;    // rollback: per-sequence device counts subtracted from n (or null)
-  int32_t op;            // 0 append n, 1 rollback n - sub[b], 2 flush (nt >= thr)
+  int32_t op;            // 0 commit only, 1 commit then flush (nt >= thr)
   int32_t l0, nl, B;
-  int32_t n, thr, G, T;
+  int32_t thr, G, T;
+  Pending pend;
 };
 
 }  // namespace qs

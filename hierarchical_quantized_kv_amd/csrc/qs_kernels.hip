@@ -168,14 +168,35 @@ __device__ __forceinline__ float wave_sum_from(float x, int from) {
   return x;
 }
 
-// Counters of sequence b: the by-value copies, or in device mode this layer's state entries.
+// Device mode: nt of sequence b after the pending operations, each applied only if it passes
+// the check of the host verb (an append within the 2G ring, a rollback count in 0 .. nt);
+// *bad (if given) receives the error bits of the ones that fail.
+__device__ __forceinline__ int apply_pending(int nt, const Pending& p, int b, int32_t* bad) {
+  int32_t e = 0;
+  for (int k = 0; k < p.count; ++k) {
+    const PendingOp& o = p.op[k];
+    if (o.kind == 0) {
+      if (nt + o.n <= 2 * kGroup) nt += o.n;
+      else e |= kDevErrAppend;
+    } else {
+      const int d = o.n - (o.sub ? o.sub[b] : 0);
+      if (d >= 0 && d <= nt) nt -= d;
+      else e |= kDevErrRollback;
+    }
+  }
+  if (bad) *bad = e;
+  return nt;
+}
+
+// Counters of sequence b: the by-value copies, or in device mode this layer's state entries
+// (nt with the pending operations applied).
 template <class Args>
 __device__ __forceinline__ int seq_nq(const Args& a, int b) {
   return a.dstate ? a.dstate[kStateInts * b] : a.nq[b];
 }
 template <class Args>
 __device__ __forceinline__ int seq_nt(const Args& a, int b) {
-  return a.dstate ? a.dstate[kStateInts * b + 1] : a.nt[b];
+  return a.dstate ? apply_pending(a.dstate[kStateInts * b + 1], a.pend, b, nullptr) : a.nt[b];
 }
 template <class Args>
 __device__ __forceinline__ int seq_head(const Args& a, int b) {
@@ -791,6 +812,17 @@ __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, Tai
   const int ring = 2 * kGroup;
   const size_t bh = (size_t)b * a.H + h;
   const int t0 = chunk * kTailChunk;
+  if (t0 >= nt) {  // no token in this chunk (device mode plans 2G / 64 chunks): empty records
+    for (int i = 0; i < m; ++i) {
+      float* rec = record(a, D, b, h, split, i);
+      if (lane == 0) {
+        rec[0] = -INFINITY;
+        rec[1] = 0.f;
+      }
+      for (int c = lane; c < D; c += 64) rec[kRecPad + c] = 0.f;
+    }
+    return;
+  }
   const int t = t0 + lane;                   // logical tail position of this lane's key
   const bool valid = t < nt;
   const int nvalid = min(kTailChunk, nt - t0);
@@ -974,9 +1006,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB> a) {
   const int t = threadIdx.x;
   const int c = t % C4, p = t / C4;
   const int ns = (a.qitem_base[b + 1] - a.qitem_base[b]) + (a.titem_base[b + 1] - a.titem_base[b]);
-  if (a.derr && h == 0 && i == 0 && t == 0) {  // device mode: the checks the host cannot make
-    const int nq = seq_nq(a, b), nt = seq_nt(a, b);
-    if (nq + nt == 0 || nt < a.min_nt) atomicOr(a.derr, kDevErrAttend);
+  if (a.derr && h == 0 && i == 0 && t == 0) {
+    // device mode: the checks the host cannot make, and the commit of the pending operations
+    // (every attention item has read the counters by now)
+    int32_t bad = 0;
+    const int nq = seq_nq(a, b);
+    const int nt = apply_pending(a.dstate[kStateInts * b + 1], a.pend, b, &bad);
+    if (nq + nt == 0 || nt < a.min_nt) bad |= kDevErrAttend;
+    if (bad) atomicOr(a.derr, bad);
+    if (a.pend.count) a.wstate[kStateInts * b + 1] = nt;
   }
 
   float m = -INFINITY, l = 0.f;
@@ -1026,8 +1064,8 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgsN<NB> a) {
   if (b >= a.B || i >= a.n[b]) return;
   const int ring = 2 * kGroup;
   int start = a.start[b], head = a.head[b];
-  if (a.dstate) {  // device mode: an append past the ring writes nothing (the state kernel flags it)
-    start = a.dstate[kStateInts * b + 1];
+  if (a.dstate) {  // device mode: an append past the ring writes nothing (flagged at the commit)
+    start = apply_pending(a.dstate[kStateInts * b + 1], a.pend, b, nullptr);
     head = a.dstate[kStateInts * b + 2];
     if (start + a.n[b] > ring) return;
   }
@@ -1235,7 +1273,7 @@ __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
   int group = a.group[sel], head = a.head[sel];
   if (a.dstate) {  // device mode: this sequence flushes only if selected and within capacity
     const int32_t* st = a.dstate + ((size_t)layer * a.B + a.b[sel]) * kStateInts;
-    const int nq = st[0], nt = st[1];
+    const int nq = st[0], nt = apply_pending(st[1], a.pend, a.b[sel], nullptr);
     if (nt < a.thr || nq + kGroup > a.T) return;
     group = nq / kGroup;
     head = st[2];
@@ -1273,9 +1311,9 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Device-mode counter updates: run after the kernels of the verb they account for (stream
-// order), so those kernels all saw the counters from before the verb.  The same tests as the
-// host-side checks decide; a failing sequence keeps its counters and sets its error bit.
+// Device-mode commit: the pending operations of a layer, then for a flush its counter update.
+// Runs after every kernel that read the old counters (stream order); the same checks as the
+// host verbs decide, and a failing operation leaves the counters and sets its error bit.
 // ------------------------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void state_kernel(const StateArgs a) {
@@ -1283,24 +1321,22 @@ __global__ __launch_bounds__(256) void state_kernel(const StateArgs a) {
   if (idx >= a.nl * a.B) return;
   const int b = idx % a.B, layer = a.l0 + idx / a.B;
   int32_t* st = a.state + ((size_t)layer * a.B + b) * kStateInts;
-  const int nq = st[0], nt = st[1], head = st[2];
-  const int ring = 2 * a.G;
-  if (a.op == 0) {
-    if (nt + a.n <= ring) st[1] = nt + a.n;
-    else atomicOr(a.err, kDevErrAppend);
-  } else if (a.op == 1) {
-    const int drop = a.n - (a.sub ? a.sub[b] : 0);
-    if (drop >= 0 && drop <= nt) st[1] = nt - drop;
-    else atomicOr(a.err, kDevErrRollback);
-  } else if (nt >= a.thr) {
+  int32_t bad = 0;
+  int nq = st[0], head = st[2];
+  int nt = apply_pending(st[1], a.pend, b, &bad);
+  if (a.op == 1 && nt >= a.thr) {
     if (nq + a.G <= a.T) {
-      st[0] = nq + a.G;
-      st[1] = nt - a.G;
-      st[2] = head ^ a.G;
+      nq += a.G;
+      nt -= a.G;
+      head ^= a.G;
     } else {
-      atomicOr(a.err, kDevErrFlush);
+      bad |= kDevErrFlush;
     }
   }
+  st[0] = nq;
+  st[1] = nt;
+  st[2] = head;
+  if (bad) atomicOr(a.err, bad);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -241,17 +241,26 @@ qs_status qs_get_state(const qs_cache* cache, int32_t layer, int32_t* h_nq, int3
  * (and qs_get_state) return QS_ERR_STATE, and in host mode the _dev verbs do.
  *
  * The _dev verbs validate their arguments on the host (QS_ERR_INVALID_ARG) and enqueue kernels
- * only: no host state changes, no synchronization, no allocation, no memset.  Conditions that
- * depend on the counters are checked by the device: the affected sequence is left unchanged
- * and a bit is set in the error word (1: append past 2G; 2: rollback count negative or past
- * the tail; 4: flush past max_ctx; 8: attention over an empty sequence, or verify with
- * m > nt).  The outputs of a flagged attention call are unspecified (finite or not).
+ * only: no synchronization, no allocation, no memset.  Appends and rollbacks are applied to the
+ * counters lazily: each is recorded on the handle as a pending operation of its layer (at most
+ * 4; a fifth commits the list first), every later kernel of that layer applies the pending
+ * ones, and they are committed to the state section by the next attention call on the layer
+ * (its last kernel), qs_flush_dev, qs_commit_dev or qs_state_from_device.  A rollback's d_sub
+ * must keep its values until then.  A sequence of calls captured in a graph for replay must
+ * begin and end with nothing pending (end it with an attention call, qs_flush_dev or
+ * qs_commit_dev for every layer it appended to or rolled back).
+ * Conditions that depend on the counters are checked by the device: the affected sequence is
+ * left unchanged and a bit is set in the error word at the commit (1: append past 2G;
+ * 2: rollback count negative or past the tail; 4: flush past max_ctx; 8: attention over an
+ * empty sequence, or verify with m > nt).  The outputs of a flagged attention call are
+ * unspecified (finite or not).
  *
  * qs_append_dev: n tokens for every sequence (d_k, d_v fp16 [B][n][H][D]), 0 <= n <= 2G.
  * qs_rollback_dev: drops n - d_sub[b] tail tokens of sequence b (n tokens if d_sub is NULL) of
  *   `layer`, or of every layer when layer == -1; d_sub: device int32 [B].
  * qs_flush_dev: quantizes the oldest G tail tokens of every sequence with nt >= max(G,
  *   min_tail), as qs_flush.
+ * qs_commit_dev: commits the pending operations of `layer` (every layer when layer == -1).
  * qs_attend_draft_dev / qs_attend_verify_dev: as the host verbs, over a fixed work plan sized
  *   for a full cache (every sequence at max_ctx), so that a captured call stays valid while
  *   the counters grow. */
@@ -262,6 +271,7 @@ qs_status qs_append_dev(qs_cache* cache, int32_t layer, const void* d_k, const v
 qs_status qs_rollback_dev(qs_cache* cache, int32_t layer, int32_t n, const int32_t* d_sub,
                           void* stream);
 qs_status qs_flush_dev(qs_cache* cache, int32_t layer, int32_t min_tail, void* stream);
+qs_status qs_commit_dev(qs_cache* cache, int32_t layer, void* stream);
 qs_status qs_attend_draft_dev(qs_cache* cache, int32_t layer, const void* d_q, float sm_scale,
                               float* d_out, void* stream);
 qs_status qs_attend_verify_dev(qs_cache* cache, int32_t layer, const void* d_q, int32_t m,

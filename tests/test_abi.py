@@ -155,6 +155,7 @@ def test_device_mode_verbs_rejected_in_host_mode(lib):
                lib.qs_append_dev(h, 0, P, P, 1, None),
                lib.qs_rollback_dev(h, -1, 1, None, None),
                lib.qs_flush_dev(h, -1, G, None),
+               lib.qs_commit_dev(h, -1, None),
                lib.qs_attend_draft_dev(h, 0, P, F1, P, None),
                lib.qs_attend_verify_dev(h, 0, P, 2, F1, P, None)):
         assert st == binding.QS_ERR_STATE

@@ -197,3 +197,44 @@ def test_device_errors_are_flagged_and_leave_the_state():
     nq, nt, hd = c.state(0)
     assert nq.tolist() == [2 * G, G] and nt.tolist() == [3, 3] and hd.tolist() == [0, G]
     c.close()
+
+
+def test_pending_operations_and_commit_points():
+    """Appends and rollbacks recorded as pending operations give the host verbs' counters and
+    ring contents, through every commit point: a fifth pending operation, qs_commit_dev, and
+    qs_state_from_device."""
+    L, B, H, D = 2, 2, 2, 64
+    log("case: device-mode pending operations")
+    dev_c, host_c = Cache(L, B, H, D, 4 * G, 4), Cache(L, B, H, D, 4 * G, 4)
+    k, v = synth.kv_device(torch, B, G + 8, H, D, 21, 22, "cuda")
+    for c in (dev_c, host_c):
+        for l in range(L):
+            c.prefill(l, k, v, n=[G + 3, 5])
+    dev_c.to_device_state()
+    for i in range(5):                                  # the fifth commits the first four
+        kk, vv = k[:, i:i + 1].contiguous(), v[:, i:i + 1].contiguous()
+        dev_c.append_dev(0, kk, vv)
+        host_c.append(0, kk, vv)
+    dev_c.rollback_dev(0, 2)
+    host_c.rollback(0, [2, 2])
+    dev_c.commit_dev(0)
+    sub = torch.tensor([1, 0], dtype=torch.int32, device="cuda")
+    dev_c.rollback_dev(1, 1, sub=sub)
+    host_c.rollback(1, [0, 1])
+    kk, vv = k[:, 5:7].contiguous(), v[:, 5:7].contiguous()
+    dev_c.append_dev(1, kk, vv)                         # applies the pending rollback first
+    host_c.append(1, kk, vv)
+    assert dev_c.from_device_state() == 0               # commits layer 1
+    for l in range(L):
+        sd, sh = dev_c.state(l), host_c.state(l)
+        assert all(np.array_equal(x, y) for x, y in zip(sd, sh)), (l, sd, sh)
+        nt, head = sh[1], sh[2]
+        for b in range(B):
+            slots = [(int(head[b]) + i) % (2 * G) for i in range(int(nt[b]))]
+            for name in ("tail_k", "tail_v"):
+                got = dev_c.section(name, l)[b][:, slots].view(torch.int16)
+                ref = host_c.section(name, l)[b][:, slots].view(torch.int16)
+                assert torch.equal(got, ref), (l, b, name)
+    assert [dev_c.state(l)[1].tolist() for l in range(L)] == [[6, 8], [5, 6]]
+    dev_c.close()
+    host_c.close()
