@@ -41,8 +41,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # HBM byte counters of rocprofv3, scaled by what they read for a plain device copy of known size
 # (FETCH_SIZE counts half of the bytes a copy kernel reads; WRITE_SIZE counts them all).
 # (Batch 1: the kernels' batch-bucket template argument is 1.)
-KERNELS = {"draft": "attn_kernel<128, true, 1>", "verify": "attn_kernel<128, false, 1>",
-           "combine": "combine_kernel<128, 1>", "flush": "flush_kernel<128>",
+KERNELS = {"draft": "attn_kernel<128, true, 1, false>", "verify": "attn_kernel<128, false, 1, false>",
+           "combine": "combine_kernel<128, 1, false>", "flush": "flush_kernel<128>",
            "prefill": "prefill_kernel<128>"}
 
 CONFIGS = {
@@ -88,6 +88,8 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=sorted(CONFIGS))
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replayed step (graph_step: null)")
     ap.add_argument("--cpu-threads", type=int, default=16,
                     help="host threads of the second, all-cores oracle timing (at most the "
                          "host's CPU count)")
@@ -246,8 +248,8 @@ def main():
     # with the counters in device memory, and each replay advances them on the device; only the
     # step's accepted count is copied into a device word before each replay.  Bytes per step
     # from a host mirror of the counters (every layer sees the same calls).
-    graph_line = measure_graph_steps(torch, cache, steps_in[0], accept, args, L, H, D, gamma, m,
-                                     out_d, out_v, dev, stream)
+    graph_line = None if args.no_graph else measure_graph_steps(
+        torch, cache, steps_in[0], accept, args, L, H, D, gamma, m, out_d, out_v, dev, stream)
 
     # Bulk flush (outside the timed steps): every layer gets G more tail tokens, then one
     # qs_flush(-1) quantizes one G-token half of every (layer, head) in a single launch.
@@ -358,9 +360,9 @@ def main():
         "prefill_us_per_layer": round(p_us, 2),
         "prefill_gbs": round(p_gbs, 1),
         "roofline": roof("draft", d_gbs, d_bytes, d_us,
-                         "draft call: attn_kernel<128, true, 1> + combine_kernel<128, 1>"),
+                         "draft call: attn_kernel<128, true, 1, false> + combine_kernel<128, 1, false>"),
         "roofline_verify": roof("verify", v_gbs, v_bytes, v_us,
-                                "attn_kernel<128, false, 1> + combine_kernel<128, 1>"),
+                                "attn_kernel<128, false, 1, false> + combine_kernel<128, 1, false>"),
         "roofline_flush": roof("flush", f_gbs, f_bytes, f_us,
                                f"flush_kernel<128>, {L} layers x {H} heads in one launch",
                                launches=L * H),
@@ -553,7 +555,7 @@ def write_traffic_summary(fetch_dir, write_dir, args):
         f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
         f"\"attn_kernel|combine_kernel|flush_kernel|prefill_kernel|copy\" -d {fetch_dir} -o run "
         f"--output-format csv -- python -u bench.py --config {args.config} --layers 2 --steps 1 "
-        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --calibration-copy-mib "
+        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --no-graph --calibration-copy-mib "
         f"{args.calibration_copy_mib}",
         f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE (same arguments, -d {write_dir})",
         f"python bench.py --config {args.config} --calibration-copy-mib "

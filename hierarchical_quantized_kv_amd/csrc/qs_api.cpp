@@ -26,8 +26,9 @@ hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st);
 hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st);
+hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_state(const StateArgs& a, hipStream_t st);
-int attention_slots(int D, bool draft, int B);
+int attention_slots(int D, bool draft, int B, bool dev);
 }  // namespace qs
 
 struct qs_cache {
@@ -315,7 +316,7 @@ static void attn_args(const qs_cache* c, int32_t layer, const void* d_q, int32_t
 // kernel, next to the tail items.
 static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft) {
   const qs_config& cf = c->cfg;
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, false);
   if (slots <= 0) slots = kFallbackSlots;
   int tail_items = 0;
   for (int b = 0; b < cf.batch; ++b)
@@ -602,7 +603,7 @@ static qs_status attend_dev(qs_cache* c, int32_t layer, const void* d_q, int32_t
   // quantized workers filling the rest of one resident round (worker w takes groups w, w + W,
   // .. of whatever the sequence holds).  Tail items past nt exit at once, so they are counted
   // as half their number.  Workers and items with no work write empty records.
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, true);
   if (slots <= 0) slots = kFallbackSlots;
   const int bh = cf.batch * cf.n_heads;
   int W = (slots - bh * qs::kMaxTailItems / 2) / bh;
@@ -617,14 +618,14 @@ static qs_status attend_dev(qs_cache* c, int32_t layer, const void* d_q, int32_t
     p.qbase[b + 1] = p.qbase[b] + W;
     p.tbase[b + 1] = p.tbase[b] + qs::kMaxTailItems;
   }
-  qs::AttnArgs a{};
+  qs::AttnDevArgs a{};
   attn_args(c, layer, d_q, m, sm_scale, d_out, p, a);
-  a.dstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
-  a.wstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
-  a.derr = dev_error(c);
-  a.min_nt = draft ? 0 : m;
-  a.pend = c->pend[layer];
-  hipError_t e = qs::launch_attention(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
+  a.dev.dstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
+  a.dev.wstate = dev_state(c) + (size_t)layer * cf.batch * qs::kStateInts;
+  a.dev.derr = dev_error(c);
+  a.dev.min_nt = draft ? 0 : m;
+  a.dev.pend = c->pend[layer];
+  hipError_t e = qs::launch_attention_dev(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
   c->pend[layer] = qs::Pending{};  // committed by the combine kernel
   c->err.clear();

@@ -62,19 +62,15 @@ struct AttnHeader {
   int32_t n_qitems_total, n_titems_total;
   float qscale;          // sm_scale * log2(e): scores are kept in the base-2 domain
   float draft_offset;    // 8 or 0 (draft only)
-  const int32_t* dstate; // device mode: this layer's [B][kStateInts] counters; else null
-  int32_t* derr;         // device mode: the error word
-  int32_t min_nt;        // device mode: tail tokens the call needs (verify: m; draft: 0)
-  int32_t* wstate;       // device mode: where the combine kernel commits the pending operations
-  Pending pend;          // device mode: this layer's pending operations
 };
 
 // Per-sequence bookkeeping for at most NB sequences.  The kernels are instantiated for a few
 // NB (1, 8, QS_MAX_BATCH) so that a small batch passes a small argument block: every launch
 // copies its argument block, and at NB = QS_MAX_BATCH (about 1.7 KB) that copy costs more
 // than a microsecond of launch latency.
-template <int NB>
+template <int NB, bool DEV = false>
 struct AttnArgsN : AttnHeader {
+  static constexpr bool kDev = false;
   int32_t nq[NB];                // quantized tokens per sequence
   int32_t nt[NB];                // tail tokens per sequence
   int32_t head[NB];              // ring slot of logical tail token 0
@@ -82,6 +78,22 @@ struct AttnArgsN : AttnHeader {
   int32_t titem_base[NB + 1];    // prefix sum over b of tail items
 };
 using AttnArgs = AttnArgsN<QS_MAX_BATCH>;
+
+// Device mode: the counters come from the state section instead of nq / nt / head (a separate
+// instantiation of the kernels, so the host-mode ones carry none of this).
+struct AttnDev {
+  const int32_t* dstate; // this layer's [B][kStateInts] counters
+  int32_t* wstate;       // where the combine kernel commits the pending operations (= dstate)
+  int32_t* derr;         // the error word
+  int32_t min_nt;        // tail tokens the call needs (verify: m; draft: 0)
+  Pending pend;          // this layer's pending operations
+};
+template <int NB>
+struct AttnArgsN<NB, true> : AttnArgsN<NB, false> {
+  static constexpr bool kDev = true;
+  AttnDev dev;
+};
+using AttnDevArgs = AttnArgsN<QS_MAX_BATCH, true>;
 
 struct AppendHeader {
   const uint16_t* k;     // [B][n_max][H][D]

@@ -192,15 +192,18 @@ __device__ __forceinline__ int apply_pending(int nt, const Pending& p, int b, in
 // (nt with the pending operations applied).
 template <class Args>
 __device__ __forceinline__ int seq_nq(const Args& a, int b) {
-  return a.dstate ? a.dstate[kStateInts * b] : a.nq[b];
+  if constexpr (Args::kDev) return a.dev.dstate[kStateInts * b];
+  else return a.nq[b];
 }
 template <class Args>
 __device__ __forceinline__ int seq_nt(const Args& a, int b) {
-  return a.dstate ? apply_pending(a.dstate[kStateInts * b + 1], a.pend, b, nullptr) : a.nt[b];
+  if constexpr (Args::kDev) return apply_pending(a.dev.dstate[kStateInts * b + 1], a.dev.pend, b, nullptr);
+  else return a.nt[b];
 }
 template <class Args>
 __device__ __forceinline__ int seq_head(const Args& a, int b) {
-  return a.dstate ? a.dstate[kStateInts * b + 2] : a.head[b];
+  if constexpr (Args::kDev) return a.dev.dstate[kStateInts * b + 2];
+  else return a.head[b];
 }
 
 // Record of split `split`, query `i` of (b, h).
@@ -812,7 +815,7 @@ __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, Tai
   const int ring = 2 * kGroup;
   const size_t bh = (size_t)b * a.H + h;
   const int t0 = chunk * kTailChunk;
-  if (t0 >= nt) {  // no token in this chunk (device mode plans 2G / 64 chunks): empty records
+  if (Args::kDev && t0 >= nt) {  // device mode plans 2G / 64 chunks: this one is empty
     for (int i = 0; i < m; ++i) {
       float* rec = record(a, D, b, h, split, i);
       if (lane == 0) {
@@ -948,8 +951,8 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
   return b;
 }
 
-template <int D, bool DRAFT, int NB>
-__global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgsN<NB> a) {
+template <int D, bool DRAFT, int NB, bool DEV>
+__global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgsN<NB, DEV> a) {
   using PassLds = typename std::conditional<DRAFT, DraftLds, VerifyLds>::type;
   __shared__ union {
     PassLds p;
@@ -991,8 +994,8 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float4& o, float m
   o.w = o.w * a1 + o2.w * a2;
 }
 
-template <int D, int NB>
-__global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB> a) {
+template <int D, int NB, bool DEV>
+__global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB, DEV> a) {
   constexpr int C4 = D / 4;        // float4 chunks of o
   constexpr int NP = 256 / C4;     // split phases
   __shared__ float4 po[NP][C4];
@@ -1006,15 +1009,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB> a) {
   const int t = threadIdx.x;
   const int c = t % C4, p = t / C4;
   const int ns = (a.qitem_base[b + 1] - a.qitem_base[b]) + (a.titem_base[b + 1] - a.titem_base[b]);
-  if (a.derr && h == 0 && i == 0 && t == 0) {
-    // device mode: the checks the host cannot make, and the commit of the pending operations
-    // (every attention item has read the counters by now)
-    int32_t bad = 0;
-    const int nq = seq_nq(a, b);
-    const int nt = apply_pending(a.dstate[kStateInts * b + 1], a.pend, b, &bad);
-    if (nq + nt == 0 || nt < a.min_nt) bad |= kDevErrAttend;
-    if (bad) atomicOr(a.derr, bad);
-    if (a.pend.count) a.wstate[kStateInts * b + 1] = nt;
+  if constexpr (DEV) {
+    if (h == 0 && i == 0 && t == 0) {
+      // device mode: the checks the host cannot make, and the commit of the pending operations
+      // (every attention item has read the counters by now)
+      int32_t bad = 0;
+      const int nq = seq_nq(a, b);
+      const int nt = apply_pending(a.dev.dstate[kStateInts * b + 1], a.dev.pend, b, &bad);
+      if (nq + nt == 0 || nt < a.dev.min_nt) bad |= kDevErrAttend;
+      if (bad) atomicOr(a.dev.derr, bad);
+      if (a.dev.pend.count) a.dev.wstate[kStateInts * b + 1] = nt;
+    }
   }
 
   float m = -INFINITY, l = 0.f;
@@ -1362,6 +1367,14 @@ AttnArgsN<NB> narrow(const AttnArgs& f) {
 }
 
 template <int NB>
+AttnArgsN<NB, true> narrow(const AttnDevArgs& f) {
+  AttnArgsN<NB, true> a;
+  static_cast<AttnArgsN<NB, false>&>(a) = narrow<NB>(static_cast<const AttnArgs&>(f));
+  a.dev = f.dev;
+  return a;
+}
+
+template <int NB>
 AppendArgsN<NB> narrow(const AppendArgs& f) {
   AppendArgsN<NB> a;
   static_cast<AppendHeader&>(a) = f;
@@ -1421,58 +1434,70 @@ hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st)
   return hipGetLastError();
 }
 
-template <int D, bool DRAFT>
+template <int D, bool DRAFT, bool DEV>
 const void* attn_fn(int bucket) {
   switch (bucket) {
-    case 1: return (const void*)attn_kernel<D, DRAFT, 1>;
-    case 8: return (const void*)attn_kernel<D, DRAFT, 8>;
-    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH>;
+    case 1: return (const void*)attn_kernel<D, DRAFT, 1, DEV>;
+    case 8: return (const void*)attn_kernel<D, DRAFT, 8, DEV>;
+    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, DEV>;
   }
 }
 
 // Work-item slots of one attention pass on the current device: compute units times the
 // one-wave workgroups of that kernel a compute unit holds at once (cached per device).
-int attention_slots(int D, bool draft, int B) {
+int attention_slots(int D, bool draft, int B, bool dev) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev][2][2][3];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  static int cache[kMaxDev][2][2][2][3];
+  int id = 0;
+  if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev) return 0;
   const int bucket = batch_bucket(B);
-  int& slot = cache[dev][D == 128][draft][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
+  int& slot = cache[id][D == 128][draft][dev][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
   if (slot > 0) return slot;
   int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const void* fn = D == 128 ? (draft ? attn_fn<128, true>(bucket) : attn_fn<128, false>(bucket))
-                            : (draft ? attn_fn<64, true>(bucket) : attn_fn<64, false>(bucket));
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess) return 0;
+  const void* fn;
+  if (dev)
+    fn = D == 128 ? (draft ? attn_fn<128, true, true>(bucket) : attn_fn<128, false, true>(bucket))
+                  : (draft ? attn_fn<64, true, true>(bucket) : attn_fn<64, false, true>(bucket));
+  else
+    fn = D == 128 ? (draft ? attn_fn<128, true, false>(bucket) : attn_fn<128, false, false>(bucket))
+                  : (draft ? attn_fn<64, true, false>(bucket) : attn_fn<64, false, false>(bucket));
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
   slot = cus * per_cu;
   return slot;
 }
 
-template <int D, bool DRAFT, int NB>
-hipError_t launch_attention_n(const AttnArgs& f, hipStream_t st) {
-  const AttnArgsN<NB> a = narrow<NB>(f);
+template <int D, bool DRAFT, int NB, bool DEV, class Full>
+hipError_t launch_attention_n(const Full& f, hipStream_t st) {
+  const AttnArgsN<NB, DEV> a = narrow<NB>(f);
   const dim3 grid(a.n_titems_total + a.n_qitems_total, a.H);
-  hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB>), grid, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, DEV>), grid, dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 cgrid(a.B * a.m, a.H);
-  hipLaunchKernelGGL((combine_kernel<D, NB>), cgrid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((combine_kernel<D, NB, DEV>), cgrid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, bool DRAFT>
-hipError_t launch_attention_d(const AttnArgs& a, hipStream_t st) {
+template <int D, bool DRAFT, bool DEV, class Full>
+hipError_t launch_attention_d(const Full& a, hipStream_t st) {
   switch (batch_bucket(a.B)) {
-    case 1: return launch_attention_n<D, DRAFT, 1>(a, st);
-    case 8: return launch_attention_n<D, DRAFT, 8>(a, st);
-    default: return launch_attention_n<D, DRAFT, QS_MAX_BATCH>(a, st);
+    case 1: return launch_attention_n<D, DRAFT, 1, DEV>(a, st);
+    case 8: return launch_attention_n<D, DRAFT, 8, DEV>(a, st);
+    default: return launch_attention_n<D, DRAFT, QS_MAX_BATCH, DEV>(a, st);
   }
 }
 
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st) {
-  if (D == 128) return draft ? launch_attention_d<128, true>(a, st) : launch_attention_d<128, false>(a, st);
-  return draft ? launch_attention_d<64, true>(a, st) : launch_attention_d<64, false>(a, st);
+  if (D == 128)
+    return draft ? launch_attention_d<128, true, false>(a, st) : launch_attention_d<128, false, false>(a, st);
+  return draft ? launch_attention_d<64, true, false>(a, st) : launch_attention_d<64, false, false>(a, st);
+}
+
+hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStream_t st) {
+  if (D == 128)
+    return draft ? launch_attention_d<128, true, true>(a, st) : launch_attention_d<128, false, true>(a, st);
+  return draft ? launch_attention_d<64, true, true>(a, st) : launch_attention_d<64, false, true>(a, st);
 }
 
 }  // namespace qs
