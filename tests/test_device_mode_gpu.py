@@ -112,10 +112,16 @@ def oracle_round(ls, h, n_gpu, gamma, rnd):
     return n_g
 
 
-@pytest.mark.parametrize("B,H,lens", [(2, 4, (3 * G + 120, 5 * G + 126)), (1, 8, (2 * G + 127,))])
-def test_graph_round_replays_match_oracle(B, H, lens):
-    L, D, gamma, V, rounds = 2, 128, 4, 1000, 6
-    log(f"case: device-mode graph round B={B} H={H} prompts={lens} gamma={gamma} rounds={rounds}")
+@pytest.mark.parametrize("B,H,D,lens", [
+    (2, 4, 128, (3 * G + 120, 5 * G + 126)),             # the 8-sequence argument bucket
+    (1, 8, 128, (2 * G + 127,)),                          # the 1-sequence bucket
+    # the 64-sequence bucket at D = 64; sequences 0, 4, 8 start with an empty quantized tier
+    (9, 2, 64, tuple(G * (i % 4) + 122 + i % 5 for i in range(9))),
+])
+def test_graph_round_replays_match_oracle(B, H, D, lens):
+    L, gamma, V, rounds = 2, 4, 1000, 6
+    log(f"case: device-mode graph round B={B} H={H} D={D} prompts={lens} gamma={gamma} "
+        f"rounds={rounds}")
     ls = Lockstep(L, B, H, D, 16 * G, gamma, tag="graph")
     n_max = max(lens)
     for l in range(L):
@@ -124,7 +130,7 @@ def test_graph_round_replays_match_oracle(B, H, lens):
     torch.cuda.synchronize()
     # load every kernel once (a scratch cache of the same shape) before capturing
     warm = Cache(L, B, H, D, 16 * G, gamma)
-    kw, vw = synth.kv_device(torch, B, G + 8, H, D, 1, 2, "cuda")
+    kw, vw = synth.kv_device(torch, B, G + 8, H, D, 1, 2, "cuda")   # every sequence non-empty
     for l in range(L):
         warm.prefill(l, kw, vw)
     warm.to_device_state()
@@ -157,7 +163,8 @@ def test_graph_round_replays_match_oracle(B, H, lens):
     nq, nt, _ = ls.gpu.state(0)
     log(f"graph: {rounds} replays, accepted per round {accepted}, final nq {nq.tolist()} nt "
         f"{nt.tolist()}, max abs err {ls.max_abs:.2e}")
-    assert all(int(q) > (n // G) * G for q, n in zip(nq, lens))   # every sequence flushed
+    # every sequence crossed G tail tokens and flushed at least once
+    assert all(int(q) > (n // G) * G for q, n in zip(nq, lens)), (nq, lens)
 
 
 def test_device_errors_are_flagged_and_leave_the_state():
