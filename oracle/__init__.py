@@ -64,11 +64,12 @@ def lib():
         L.orc_attend_verify.argtypes = [P, i, P, i, ctypes.c_double, P]
         L.orc_get_state.argtypes = [P, i, P, P, P]
         L.orc_read_codes.argtypes = [P, i, i, i, i, P]
+        L.orc_set_lower_nibbles.argtypes = [P, i, i]
         L.orc_read_meta.argtypes = [P, i, i, i, P, P]
         L.orc_export_layer.argtypes = [P, i, P, P, P, P, P, P, P, P]
         for f in ("orc_append", "orc_prefill", "orc_spec_accept", "orc_rollback", "orc_flush", "orc_attend_draft",
                   "orc_attend_verify", "orc_get_state", "orc_read_codes", "orc_read_meta",
-                  "orc_export_layer"):
+                  "orc_export_layer", "orc_set_lower_nibbles"):
             getattr(L, f).restype = i
         _lib = L
     return _lib
@@ -209,6 +210,10 @@ class OracleCache:
         hd = np.zeros(self.B, dtype=np.int32)
         self._check(lib().orc_get_state(self._h, layer, _ptr(nq), _ptr(nt), _ptr(hd)), "state")
         return nq, nt, hd
+
+    def set_lower_nibbles(self, layer, value):
+        """Test support: every stored code of `layer` gets lower nibble `value`."""
+        self._check(lib().orc_set_lower_nibbles(self._h, layer, int(value)), "set_lower_nibbles")
 
     def codes(self, layer, b, h, which_v=False):
         out = np.zeros((self.T, self.D), dtype=np.uint8)

@@ -378,6 +378,25 @@ int orc_get_state(const orc_cache* c, int layer, int* nq, int* nt, int* head) {
   return 0;
 }
 
+/* Test support: sets the lower nibble of every stored code of `layer` (keys and values, rows
+ * below nq) to `value`.  With value 8 and draft offset 8 the full code 16 C_U + 8 is exactly the
+ * draft reconstruction's, so verify (m = 1) must then equal draft. */
+int orc_set_lower_nibbles(orc_cache* c, int layer, int value) {
+  if (!c || layer < 0 || layer >= c->L || value < 0 || value > 15) return 1;
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t r = lbh(c, layer, b, h);
+      const size_t n = (size_t)c->nq[layer * c->B + b] * c->D;
+      for (size_t i = 0; i < n; ++i) {
+        uint8_t* k = &c->kc[r * c->T * c->D + i];
+        uint8_t* v = &c->vc[r * c->T * c->D + i];
+        *k = (uint8_t)((*k & 0xF0) | value);
+        *v = (uint8_t)((*v & 0xF0) | value);
+      }
+    }
+  return 0;
+}
+
 int orc_read_codes(const orc_cache* c, int layer, int b, int h, int which_v, uint8_t* codes) {
   if (!c || layer < 0 || layer >= c->L || b < 0 || b >= c->B || h < 0 || h >= c->H || !codes)
     return 1;

@@ -79,6 +79,8 @@ int orc_get_state(const orc_cache* c, int layer, int* nq, int* nt, int* head);
  *   codes  [T][D]   8-bit codes of the quantized tokens (rows >= nq are zero)
  *   kmeta  [T/G][D][2] key (s, z);  vmeta [T][2] value (s, z). */
 int orc_read_codes(const orc_cache* c, int layer, int b, int h, int which_v, uint8_t* codes);
+/* Test support: every stored code of `layer` gets lower nibble `value` (0..15). */
+int orc_set_lower_nibbles(orc_cache* c, int layer, int value);
 int orc_read_meta(const orc_cache* c, int layer, int b, int h, float* kmeta, float* vmeta);
 
 /* Packs one layer into the arena layout of the library (per-layer slices of each section):

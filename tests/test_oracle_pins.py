@@ -229,6 +229,27 @@ def test_grid_exact_cache_verify_equals_unquantized_and_draft_equals_upper_formu
         assert np.max(np.abs(draft[0, h] - refd)) < 1e-6
 
 
+@pytest.mark.parametrize("off,nibble", [(8, 8), (0, 0)])
+def test_draft_equals_verify_when_every_lower_nibble_is_the_draft_offset(off, nibble):
+    """The draft reconstruction (16 C_U + off - z) s is the full one (C8 - z) s of a code whose
+    lower nibble is off: after setting every stored lower nibble to off, a one-query verify
+    (which sees the whole tail) equals the draft, exactly.  A wrong shift, nibble or offset in
+    either dequantization fails it."""
+    H, D = 3, 64
+    c = OracleCache(1, 2, H, D, G, 4 * G, 4, draft_offset=off)
+    k, v = synth.kv_host(2, 2 * G + 50, H, D, 41, 42)
+    c.prefill(0, k, v, n=[2 * G + 50, G + 7])
+    q = synth.queries_host(2, None, H, D, 43, gain=2.0)
+    before = c.attend_draft(0, q)
+    c.set_lower_nibbles(0, nibble)
+    draft = c.attend_draft(0, q)
+    ver = c.attend_verify(0, q[:, None])[:, 0]
+    assert np.array_equal(draft, before)            # the draft never reads the lower nibbles
+    assert np.array_equal(draft, ver)
+    c.set_lower_nibbles(0, nibble ^ 1)              # any other nibble breaks the identity
+    assert not np.array_equal(c.attend_verify(0, q[:, None])[:, 0], draft)
+
+
 def test_single_token_and_zero_query_closed_forms():
     rng = np.random.default_rng(4)
     H, D = 2, 64

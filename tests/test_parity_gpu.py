@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from hierarchical_quantized_kv_amd import synth
+from hierarchical_quantized_kv_amd.binding import Cache
 from lockstep import Lockstep, log
 
 pytestmark = pytest.mark.gpu
@@ -258,6 +259,69 @@ def test_peaky_softmax(gain):
     ls.draft(0, qd(1, H, D, 702, gain))
     ls.verify(0, qv(1, 7, H, D, 703, gain))
     log(f"peaky{gain}: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_draft_equals_one_query_verify_when_lower_planes_are_the_offset(D):
+    """With every lower nibble of the arena set to the draft offset 8, the full code is the draft
+    reconstruction, so a one-query verify equals the draft: two independent GPU paths (signed
+    4-bit integer dot products; MFMA over 1024 + C8) agree, and each matches the oracle with the
+    same nibbles."""
+    log(f"case: draft == verify(m=1) with lower planes 8, D={D}")
+    H = 4
+    ls = Lockstep(1, 2, H, D, 8 * G, 4, tag=f"dv{D}")
+    k, v = kv(2, 6 * G + 45, H, D, 910)
+    ls.prefill(0, k, v, n=[6 * G + 45, 3 * G + 2])
+    ls.gpu.section("lk", 0).fill_(0x88)
+    ls.gpu.section("lv", 0).fill_(0x88)
+    ls.orc[0].set_lower_nibbles(0, 8)
+    q = qd(2, H, D, 911, gain=2.0)
+    d = ls.draft(0, q)
+    vq = ls.verify(0, q[:, None].contiguous())[:, 0]
+    torch.cuda.synchronize()
+    diff = float((d - vq).abs().max())
+    ref = float(d.abs().max())
+    log(f"dv{D}: max |draft - verify| {diff:.3e} (max |out| {ref:.3e}); vs oracle {ls.max_abs:.3e}")
+    assert diff <= 1e-5 * max(ref, 1e-3)
+
+
+def test_result_does_not_depend_on_the_split():
+    """The split-K log-sum-exp merge reaches one softmax whatever the split: one sequence's
+    outputs alone (many workers per head), inside a batch of 8 (few workers per head), and in
+    device mode (a fixed plan) agree to 2e-6 of their size (measured: up to 7e-7)."""
+    log("case: split invariance")
+    H, D, n = 32, 128, 40 * G + 77
+    k, v = kv(1, n, H, D, 920)
+    q = qd(1, H, D, 921)
+    qm = qv(1, 5, H, D, 922)
+    solo = Cache(1, 1, H, D, 48 * G, 4)
+    solo.prefill(0, k, v)
+    batch = Cache(1, 8, H, D, 48 * G, 4)
+    lens = [n if b == 5 else (b * 7 + 3) * G // 2 + 11 * b + 5 for b in range(8)]
+    assert all(L % G >= 5 for L in lens)           # the 5-query verify needs nt >= 5
+    kb, vb = kv(8, n, H, D, 930)
+    kb[5], vb[5] = k[0], v[0]
+    batch.prefill(0, kb, vb, n=lens)
+    qb, qmb = qd(8, H, D, 931), qv(8, 5, H, D, 932)
+    qb[5], qmb[5] = q[0], qm[0]
+    outs = {"solo": (solo.attend_draft(0, q)[0], solo.attend_verify(0, qm)[0]),
+            "batch": (batch.attend_draft(0, qb)[5], batch.attend_verify(0, qmb)[5])}
+    od = torch.empty((1, H, D), dtype=torch.float32, device="cuda")
+    ov = torch.empty((1, 5, H, D), dtype=torch.float32, device="cuda")
+    solo.to_device_state()
+    solo.attend_draft_dev(0, q, od)
+    solo.attend_verify_dev(0, qm, ov)
+    assert solo.from_device_state() == 0
+    outs["device"] = (od[0], ov[0])
+    torch.cuda.synchronize()
+    for name in ("batch", "device"):
+        for i, what in enumerate(("draft", "verify")):
+            a, b = outs["solo"][i], outs[name][i]
+            rel = float((a - b).abs().max()) / float(a.abs().max())
+            log(f"split: {what} solo vs {name}: max rel diff {rel:.2e}")
+            assert rel <= 2e-6, (what, name, rel)
+    solo.close()
+    batch.close()
 
 
 def test_grid_exact_cache_verify_equals_fp16_attention():
