@@ -41,9 +41,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 # HBM byte counters of rocprofv3, scaled by what they read for a plain device copy of known size
 # (FETCH_SIZE counts half of the bytes a copy kernel reads; WRITE_SIZE counts them all).
 # (Batch 1: the kernels' batch-bucket template argument is 1.)
-KERNELS = {"draft": "attn_kernel<128, true, 1, false>", "verify": "attn_kernel<128, false, 1, false>",
-           "combine": "combine_kernel<128, 1, false>", "flush": "flush_kernel<128>",
+# Kernel names (as rocprofv3 prints them) of the default step: the attention kernels of the
+# fused append + attend calls (mode 2); --no-fuse runs the mode-0 ones.
+KERNELS = {"draft": "attn_kernel<128, true, 1, 2>", "verify": "attn_kernel<128, false, 1, 2>",
+           "combine": "combine_kernel<128, 1, 2>", "flush": "flush_kernel<128>",
            "prefill": "prefill_kernel<128>"}
+
+
+def kernel_names(fuse):
+    mode = 2 if fuse else 0
+    return (f"attn_kernel<128, true, 1, {mode}>", f"attn_kernel<128, false, 1, {mode}>",
+            f"combine_kernel<128, 1, {mode}>")
 
 CONFIGS = {
     3: dict(name="Llama-2-7B-32K-shaped full stack", layers=32, heads=32, D=128, ctx=32768,
@@ -88,6 +96,8 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=sorted(CONFIGS))
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="separate append and attention calls instead of the fused ones")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replayed step (graph_step: null)")
     ap.add_argument("--cpu-threads", type=int, default=16,
@@ -188,6 +198,7 @@ def main():
     out_v = torch.empty((1, m, H, D), dtype=torch.float32, device=dev)
 
     ev = {"draft": [], "verify": []}
+    fuse = not args.no_fuse
     step_bytes = []
 
     # HIP events bracket the draft and verify calls of one layer per timed step (the layer
@@ -197,35 +208,49 @@ def main():
         x = steps_in[s]
         nbytes = 0
         ev_layer = (s - args.warmup) % L if timed else -1  # -1: no events in warmup
+        # A draft step is the token's append followed by the draft call; fused (the default)
+        # both are one call, whose event interval and bytes then include the append.
         for j in range(gamma):
             for layer in range(L):
-                cache.append(layer, x["dk"][j, layer], x["dv"][j, layer])
+                if not fuse:
+                    cache.append(layer, x["dk"][j, layer], x["dv"][j, layer])
                 nq, nt, _ = cache.state(layer)
-                nbytes += append_bytes(1, H, D) + draft_bytes(int(nq[0]), int(nt[0]), H, D)
+                nt_call = int(nt[0]) + (1 if fuse else 0)
+                db = draft_bytes(int(nq[0]), nt_call, H, D)
+                nbytes += append_bytes(1, H, D) + db
                 rec = layer == ev_layer
                 if rec:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
-                cache.attend_draft(layer, x["qd"][j, layer], out=out_d)
+                if fuse:
+                    cache.append_attend_draft(layer, x["dk"][j, layer], x["dv"][j, layer],
+                                              x["qd"][j, layer], out=out_d)
+                else:
+                    cache.attend_draft(layer, x["qd"][j, layer], out=out_d)
                 if rec:
                     e1.record(stream)
-                    ev["draft"].append((e0, e1, draft_bytes(int(nq[0]), int(nt[0]), H, D)))
+                    ev["draft"].append((e0, e1, db + (append_bytes(1, H, D) if fuse else 0)))
         for layer in range(L):
             cache.rollback(layer, [gamma])
-            cache.append(layer, x["tk"][layer], x["tv"][layer])
+            if not fuse:
+                cache.append(layer, x["tk"][layer], x["tv"][layer])
             nq, nt, _ = cache.state(layer)
-            vb = verify_bytes(int(nq[0]), int(nt[0]), H, D, m)
+            vb = verify_bytes(int(nq[0]), int(nt[0]) + (m if fuse else 0), H, D, m)
             nbytes += append_bytes(m, H, D) + vb
             rec = layer == ev_layer
             if rec:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            cache.attend_verify(layer, x["qv"][layer], out=out_v)
+            if fuse:
+                cache.append_attend_verify(layer, x["tk"][layer], x["tv"][layer], x["qv"][layer],
+                                           out=out_v)
+            else:
+                cache.attend_verify(layer, x["qv"][layer], out=out_v)
             if rec:
                 e1.record(stream)
-                ev["verify"].append((e0, e1, vb))
+                ev["verify"].append((e0, e1, vb + (append_bytes(m, H, D) if fuse else 0)))
             cache.rollback(layer, [gamma - accept[s]])
         flushed = cache.flush(-1)
         nbytes += int(flushed[0]) * L * flush_bytes(H, D)
@@ -326,6 +351,8 @@ def main():
 
     traffic = load_traffic(args.config)
 
+    kn = kernel_names(fuse)
+
     def roof(kind, gbs, nbytes, us, kernel, launches=1):
         t = traffic.get(kind) if traffic else None
         return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1),
@@ -350,7 +377,7 @@ def main():
                                f"ctx {ctx} + 64-token tail, gamma {gamma} ({m}-query verify), "
                                f"1% key channels x8",
                    "layers": L, "heads": H, "head_dim": D, "ctx": ctx, "gamma": gamma,
-                   "batch": 1, "group": G},
+                   "batch": 1, "group": G, "fused_append": fuse},
         "draft_us_per_layer": round(d_us, 2),
         "draft_gbs": round(d_gbs, 1),
         "verify_us_per_layer": round(v_us, 2),
@@ -360,9 +387,9 @@ def main():
         "prefill_us_per_layer": round(p_us, 2),
         "prefill_gbs": round(p_gbs, 1),
         "roofline": roof("draft", d_gbs, d_bytes, d_us,
-                         "draft call: attn_kernel<128, true, 1, false> + combine_kernel<128, 1, false>"),
+                         f"draft call{' (fused append)' if fuse else ''}: {kn[0]} + {kn[2]}"),
         "roofline_verify": roof("verify", v_gbs, v_bytes, v_us,
-                                "attn_kernel<128, false, 1, false> + combine_kernel<128, 1, false>"),
+                                f"verify call{' (fused append)' if fuse else ''}: {kn[1]} + {kn[2]}"),
         "roofline_flush": roof("flush", f_gbs, f_bytes, f_us,
                                f"flush_kernel<128>, {L} layers x {H} heads in one launch",
                                launches=L * H),

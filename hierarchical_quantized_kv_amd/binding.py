@@ -24,7 +24,7 @@ EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_des
            "qs_attend_verify", "qs_get_state", "qs_last_error", "qs_spec_workspace_bytes",
            "qs_spec_accept", "qs_state_to_device", "qs_state_from_device", "qs_append_dev",
            "qs_rollback_dev", "qs_flush_dev", "qs_commit_dev", "qs_attend_draft_dev",
-           "qs_attend_verify_dev")
+           "qs_attend_verify_dev", "qs_append_attend_draft", "qs_append_attend_verify")
 
 # Bits of the device-mode error word (include/quantspec.h, device mode).
 DEV_ERR_APPEND, DEV_ERR_ROLLBACK, DEV_ERR_FLUSH, DEV_ERR_ATTEND = 1, 2, 4, 8
@@ -75,6 +75,8 @@ def lib():
         L.qs_attend_draft.argtypes = [P, I32, P, F, P, P]
         L.qs_attend_verify.argtypes = [P, I32, P, I32, F, P, P]
         L.qs_get_state.argtypes = [P, I32, PI, PI, PI]
+        L.qs_append_attend_draft.argtypes = [P, I32, P, P, I32, PI, P, F, P, P]
+        L.qs_append_attend_verify.argtypes = [P, I32, P, P, P, I32, F, P, P]
         L.qs_last_error.argtypes = [P]
         L.qs_last_error.restype = ctypes.c_char_p
         L.qs_spec_workspace_bytes.argtypes = [I32, I32, I32]
@@ -210,6 +212,33 @@ class Cache:
                                            q.shape[1], float(sm_scale),
                                            self._dev(out, torch.float32, "out"),
                                            self._stream(stream)), "qs_attend_verify")
+        return out
+
+    def append_attend_draft(self, layer, k, v, q, n=None, sm_scale=1.0, out=None, stream=None):
+        """append(layer, k, v, n) then attend_draft(layer, q), fused into one launch pair."""
+        torch = self.torch
+        assert k.shape == v.shape and k.dim() == 4 and k.shape[0] == self.B
+        assert tuple(k.shape[2:]) == (self.H, self.D) and tuple(q.shape) == (self.B, self.H, self.D)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        nn = _i32(n, self.B)
+        self._check(lib().qs_append_attend_draft(
+            self._h, layer, self._dev(k, torch.float16, "k"), self._dev(v, torch.float16, "v"),
+            k.shape[1], _ptr_i32(nn), self._dev(q, torch.float16, "q"), float(sm_scale),
+            self._dev(out, torch.float32, "out"), self._stream(stream)), "qs_append_attend_draft")
+        return out
+
+    def append_attend_verify(self, layer, k, v, q, sm_scale=1.0, out=None, stream=None):
+        """append(layer, k, v) of the m verified tokens then attend_verify(layer, q), fused."""
+        torch = self.torch
+        assert q.dim() == 4 and q.shape[0] == self.B and tuple(q.shape[2:]) == (self.H, self.D)
+        assert k.shape == v.shape == q.shape
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        self._check(lib().qs_append_attend_verify(
+            self._h, layer, self._dev(k, torch.float16, "k"), self._dev(v, torch.float16, "v"),
+            self._dev(q, torch.float16, "q"), q.shape[1], float(sm_scale),
+            self._dev(out, torch.float32, "out"), self._stream(stream)), "qs_append_attend_verify")
         return out
 
     def state(self, layer):

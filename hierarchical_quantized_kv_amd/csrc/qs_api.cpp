@@ -27,8 +27,9 @@ hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st)
 hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStream_t st);
+hipError_t launch_attention_app(const AttnAppArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_state(const StateArgs& a, hipStream_t st);
-int attention_slots(int D, bool draft, int B, bool dev);
+int attention_slots(int D, bool draft, int B, int mode);
 }  // namespace qs
 
 struct qs_cache {
@@ -314,9 +315,9 @@ static void attn_args(const qs_cache* c, int32_t layer, const void* d_q, int32_t
 
 // Work plan for the sequences `seqs`: quantized workers sized to one resident round of the pass
 // kernel, next to the tail items.
-static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft) {
+static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft, int mode) {
   const qs_config& cf = c->cfg;
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, false);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, mode);
   if (slots <= 0) slots = kFallbackSlots;
   int tail_items = 0;
   for (int b = 0; b < cf.batch; ++b)
@@ -337,7 +338,7 @@ static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, 
   const qs_config& cf = c->cfg;
   qs::Seq seqs[QS_MAX_BATCH];
   for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
-  const qs::Plan p = attn_plan(c, seqs, draft);
+  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeHost);
   qs::AttnArgs a{};
   attn_args(c, layer, d_q, m, sm_scale, d_out, p, a);
   for (int b = 0; b < cf.batch; ++b) {
@@ -351,6 +352,55 @@ static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, 
   return QS_OK;
 }
 
+// Append n[b] tokens of d_k / d_v [B][n_max][H][D], then attend: one launch pair, the tail
+// items writing the new tokens to the ring as they read them.  Validation is that of the two
+// verbs in sequence, all before anything changes.
+static qs_status append_attend(qs_cache* c, int32_t layer, const void* d_k, const void* d_v,
+                               int32_t n_max, const int32_t* h_n, const void* d_q, int32_t m,
+                               float sm_scale, float* d_out, void* stream, bool draft) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (c->dev) return fail(c, QS_ERR_STATE, kInDeviceMode);
+  if (!d_k || !d_v) return fail(c, QS_ERR_INVALID_ARG, "null k or v");
+  if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
+  if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
+  const qs_config& cf = c->cfg;
+  int32_t n[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) n[b] = h_n ? h_n[b] : n_max;
+  std::string err;
+  qs_status s = c->st.check_append(layer, n_max, n, &err);
+  if (s != QS_OK) return fail(c, s, err);
+  qs::Seq seqs[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) {
+    seqs[b] = c->st.at(layer, b);
+    seqs[b].nt += n[b];
+  }
+  if (!draft && (m < 1 || m > cf.gamma_max + 1))
+    return fail(c, QS_ERR_INVALID_ARG, "m must be in 1..gamma_max+1");
+  for (int b = 0; b < cf.batch; ++b) {
+    if (seqs[b].nq + seqs[b].nt == 0) return fail(c, QS_ERR_STATE, "attention over a sequence that holds no token");
+    if (!draft && m > seqs[b].nt) return fail(c, QS_ERR_STATE, "verify needs m <= nt (the m queries are tail tokens)");
+  }
+  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeAppend);
+  qs::AttnAppArgs a{};
+  attn_args(c, layer, d_q, m, sm_scale, d_out, p, a);
+  for (int b = 0; b < cf.batch; ++b) {
+    a.nq[b] = seqs[b].nq;
+    a.nt[b] = seqs[b].nt;
+    a.head[b] = seqs[b].head;
+    a.an[b] = n[b];
+  }
+  a.ak = static_cast<const uint16_t*>(d_k);
+  a.av = static_cast<const uint16_t*>(d_v);
+  a.wtail_k = const_cast<uint16_t*>(a.tail_k);
+  a.wtail_v = const_cast<uint16_t*>(a.tail_v);
+  a.an_max = n_max;
+  hipError_t e = qs::launch_attention_app(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
+  c->st.apply_append(layer, n);
+  c->err.clear();
+  return QS_OK;
+}
+
 qs_status qs_attend_draft(qs_cache* c, int32_t layer, const void* d_q, float sm_scale, float* d_out,
                           void* stream) {
   return attend(c, layer, d_q, 1, sm_scale, d_out, stream, true);
@@ -359,6 +409,20 @@ qs_status qs_attend_draft(qs_cache* c, int32_t layer, const void* d_q, float sm_
 qs_status qs_attend_verify(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
                            float* d_out, void* stream) {
   return attend(c, layer, d_q, m, sm_scale, d_out, stream, false);
+}
+
+qs_status qs_append_attend_draft(qs_cache* c, int32_t layer, const void* d_k, const void* d_v,
+                                 int32_t n_max, const int32_t* h_n, const void* d_q,
+                                 float sm_scale, float* d_out, void* stream) {
+  return append_attend(c, layer, d_k, d_v, n_max, h_n, d_q, 1, sm_scale, d_out, stream, true);
+}
+
+qs_status qs_append_attend_verify(qs_cache* c, int32_t layer, const void* d_k, const void* d_v,
+                                  const void* d_q, int32_t m, float sm_scale, float* d_out,
+                                  void* stream) {
+  if (c && (m < 1 || m > c->cfg.gamma_max + 1))
+    return fail(c, QS_ERR_INVALID_ARG, "m must be in 1..gamma_max+1");
+  return append_attend(c, layer, d_k, d_v, m, nullptr, d_q, m, sm_scale, d_out, stream, false);
 }
 
 qs_status qs_get_state(const qs_cache* c, int32_t layer, int32_t* h_nq, int32_t* h_nt, int32_t* h_head) {
@@ -603,7 +667,7 @@ static qs_status attend_dev(qs_cache* c, int32_t layer, const void* d_q, int32_t
   // quantized workers filling the rest of one resident round (worker w takes groups w, w + W,
   // .. of whatever the sequence holds).  Tail items past nt exit at once, so they are counted
   // as half their number.  Workers and items with no work write empty records.
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, true);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, qs::kModeDev);
   if (slots <= 0) slots = kFallbackSlots;
   const int bh = cf.batch * cf.n_heads;
   int W = (slots - bh * qs::kMaxTailItems / 2) / bh;

@@ -68,9 +68,17 @@ struct AttnHeader {
 // NB (1, 8, QS_MAX_BATCH) so that a small batch passes a small argument block: every launch
 // copies its argument block, and at NB = QS_MAX_BATCH (about 1.7 KB) that copy costs more
 // than a microsecond of launch latency.
-template <int NB, bool DEV = false>
+// Variants of an attention call (a template parameter of the kernels: each its own
+// instantiation, so the plain one carries none of the others' fields or code).
+enum : int {
+  kModeHost = 0,    // counters by value
+  kModeDev = 1,     // counters from the state section (device mode)
+  kModeAppend = 2,  // counters by value, and the call first appends tokens to the tail
+};
+
+template <int NB, int MODE = kModeHost>
 struct AttnArgsN : AttnHeader {
-  static constexpr bool kDev = false;
+  static constexpr int kMode = kModeHost;
   int32_t nq[NB];                // quantized tokens per sequence
   int32_t nt[NB];                // tail tokens per sequence
   int32_t head[NB];              // ring slot of logical tail token 0
@@ -89,11 +97,27 @@ struct AttnDev {
   Pending pend;          // this layer's pending operations
 };
 template <int NB>
-struct AttnArgsN<NB, true> : AttnArgsN<NB, false> {
-  static constexpr bool kDev = true;
+struct AttnArgsN<NB, kModeDev> : AttnArgsN<NB, kModeHost> {
+  static constexpr int kMode = kModeDev;
   AttnDev dev;
 };
-using AttnDevArgs = AttnArgsN<QS_MAX_BATCH, true>;
+using AttnDevArgs = AttnArgsN<QS_MAX_BATCH, kModeDev>;
+
+// Fused append: before attending, the call appends an[b] tokens of ak / av [B][an_max][H][D] to
+// sequence b's tail (nt[] already counts them).  The tail item whose chunk holds a new token's
+// ring slot reads the token from ak / av, writes it to the ring and attends over it in the same
+// pass, so no separate append kernel runs.
+template <int NB>
+struct AttnArgsN<NB, kModeAppend> : AttnArgsN<NB, kModeHost> {
+  static constexpr int kMode = kModeAppend;
+  const uint16_t* ak;
+  const uint16_t* av;
+  uint16_t* wtail_k;     // the ring again, writable (= tail_k / tail_v)
+  uint16_t* wtail_v;
+  int32_t an_max;
+  int32_t an[NB];
+};
+using AttnAppArgs = AttnArgsN<QS_MAX_BATCH, kModeAppend>;
 
 struct AppendHeader {
   const uint16_t* k;     // [B][n_max][H][D]

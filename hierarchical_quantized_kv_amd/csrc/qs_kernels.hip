@@ -192,17 +192,17 @@ __device__ __forceinline__ int apply_pending(int nt, const Pending& p, int b, in
 // (nt with the pending operations applied).
 template <class Args>
 __device__ __forceinline__ int seq_nq(const Args& a, int b) {
-  if constexpr (Args::kDev) return a.dev.dstate[kStateInts * b];
+  if constexpr (Args::kMode == kModeDev) return a.dev.dstate[kStateInts * b];
   else return a.nq[b];
 }
 template <class Args>
 __device__ __forceinline__ int seq_nt(const Args& a, int b) {
-  if constexpr (Args::kDev) return apply_pending(a.dev.dstate[kStateInts * b + 1], a.dev.pend, b, nullptr);
+  if constexpr (Args::kMode == kModeDev) return apply_pending(a.dev.dstate[kStateInts * b + 1], a.dev.pend, b, nullptr);
   else return a.nt[b];
 }
 template <class Args>
 __device__ __forceinline__ int seq_head(const Args& a, int b) {
-  if constexpr (Args::kDev) return a.dev.dstate[kStateInts * b + 2];
+  if constexpr (Args::kMode == kModeDev) return a.dev.dstate[kStateInts * b + 2];
   else return a.head[b];
 }
 
@@ -815,7 +815,7 @@ __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, Tai
   const int ring = 2 * kGroup;
   const size_t bh = (size_t)b * a.H + h;
   const int t0 = chunk * kTailChunk;
-  if (Args::kDev && t0 >= nt) {  // device mode plans 2G / 64 chunks: this one is empty
+  if (Args::kMode == kModeDev && t0 >= nt) {  // device mode plans 2G / 64 chunks: this one is empty
     for (int i = 0; i < m; ++i) {
       float* rec = record(a, D, b, h, split, i);
       if (lane == 0) {
@@ -833,6 +833,22 @@ __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, Tai
   const int s0 = (seq_head(a, b) + t0) % ring;
   const uint16_t* kchunk = a.tail_k + (bh * ring + s0) * D;
   const uint16_t* vchunk = a.tail_v + (bh * ring + s0) * D;
+  if constexpr (Args::kMode == kModeAppend) {
+    // fused append: tail positions nt_old .. nt-1 are the tokens this call appends (row i of the
+    // append at ak / av + ((b * an_max + i) * H + h) * D).  This item copies the ones in its
+    // chunk to their ring slots and waits until the stores are done, then reads the chunk from
+    // the ring like any other (no other item reads these slots).
+    const int nt_old = nt - a.an[b];
+    const int r0 = max(t0, nt_old), r1 = min(t0 + kTailChunk, nt);
+    for (int x = lane; x < (r1 - r0) * (D / 8); x += 64) {
+      const int r = r0 + x / (D / 8), c = x % (D / 8);
+      const size_t src = (((size_t)b * a.an_max + (r - nt_old)) * a.H + h) * D + 8 * c;
+      const size_t dst = (bh * ring + s0 + (r - t0)) * D + 8 * c;
+      *reinterpret_cast<uint4*>(a.wtail_k + dst) = ld16(a.ak + src);
+      *reinterpret_cast<uint4*>(a.wtail_v + dst) = ld16(a.av + src);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every counter drained: the stores have completed
+  }
 
   // The loads of the queries (m * D/2 words, in lane-strided order) and of this lane's key row
   // are issued together before their first use; slots past the nt valid tokens are read (they
@@ -951,8 +967,8 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
   return b;
 }
 
-template <int D, bool DRAFT, int NB, bool DEV>
-__global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgsN<NB, DEV> a) {
+template <int D, bool DRAFT, int NB, int MODE>
+__global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgsN<NB, MODE> a) {
   using PassLds = typename std::conditional<DRAFT, DraftLds, VerifyLds>::type;
   __shared__ union {
     PassLds p;
@@ -994,8 +1010,8 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float4& o, float m
   o.w = o.w * a1 + o2.w * a2;
 }
 
-template <int D, int NB, bool DEV>
-__global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB, DEV> a) {
+template <int D, int NB, int MODE>
+__global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB, MODE> a) {
   constexpr int C4 = D / 4;        // float4 chunks of o
   constexpr int NP = 256 / C4;     // split phases
   __shared__ float4 po[NP][C4];
@@ -1009,7 +1025,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB, DEV> a
   const int t = threadIdx.x;
   const int c = t % C4, p = t / C4;
   const int ns = (a.qitem_base[b + 1] - a.qitem_base[b]) + (a.titem_base[b + 1] - a.titem_base[b]);
-  if constexpr (DEV) {
+  if constexpr (MODE == kModeDev) {
     if (h == 0 && i == 0 && t == 0) {
       // device mode: the checks the host cannot make, and the commit of the pending operations
       // (every attention item has read the counters by now)
@@ -1367,10 +1383,23 @@ AttnArgsN<NB> narrow(const AttnArgs& f) {
 }
 
 template <int NB>
-AttnArgsN<NB, true> narrow(const AttnDevArgs& f) {
-  AttnArgsN<NB, true> a;
-  static_cast<AttnArgsN<NB, false>&>(a) = narrow<NB>(static_cast<const AttnArgs&>(f));
+AttnArgsN<NB, kModeDev> narrow(const AttnDevArgs& f) {
+  AttnArgsN<NB, kModeDev> a;
+  static_cast<AttnArgsN<NB>&>(a) = narrow<NB>(static_cast<const AttnArgs&>(f));
   a.dev = f.dev;
+  return a;
+}
+
+template <int NB>
+AttnArgsN<NB, kModeAppend> narrow(const AttnAppArgs& f) {
+  AttnArgsN<NB, kModeAppend> a;
+  static_cast<AttnArgsN<NB>&>(a) = narrow<NB>(static_cast<const AttnArgs&>(f));
+  a.ak = f.ak;
+  a.av = f.av;
+  a.wtail_k = f.wtail_k;
+  a.wtail_v = f.wtail_v;
+  a.an_max = f.an_max;
+  for (int b = 0; b < NB; ++b) a.an[b] = f.an[b];
   return a;
 }
 
@@ -1434,70 +1463,77 @@ hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st)
   return hipGetLastError();
 }
 
-template <int D, bool DRAFT, bool DEV>
+template <int D, bool DRAFT, int MODE>
 const void* attn_fn(int bucket) {
   switch (bucket) {
-    case 1: return (const void*)attn_kernel<D, DRAFT, 1, DEV>;
-    case 8: return (const void*)attn_kernel<D, DRAFT, 8, DEV>;
-    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, DEV>;
+    case 1: return (const void*)attn_kernel<D, DRAFT, 1, MODE>;
+    case 8: return (const void*)attn_kernel<D, DRAFT, 8, MODE>;
+    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, MODE>;
   }
+}
+
+template <int MODE>
+const void* attn_fn_dm(int D, bool draft, int bucket) {
+  return D == 128 ? (draft ? attn_fn<128, true, MODE>(bucket) : attn_fn<128, false, MODE>(bucket))
+                  : (draft ? attn_fn<64, true, MODE>(bucket) : attn_fn<64, false, MODE>(bucket));
 }
 
 // Work-item slots of one attention pass on the current device: compute units times the
 // one-wave workgroups of that kernel a compute unit holds at once (cached per device).
-int attention_slots(int D, bool draft, int B, bool dev) {
+int attention_slots(int D, bool draft, int B, int mode) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev][2][2][2][3];
+  static int cache[kMaxDev][2][2][3][3];
   int id = 0;
-  if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev) return 0;
+  if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 2) return 0;
   const int bucket = batch_bucket(B);
-  int& slot = cache[id][D == 128][draft][dev][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
+  int& slot = cache[id][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
   if (slot > 0) return slot;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess) return 0;
-  const void* fn;
-  if (dev)
-    fn = D == 128 ? (draft ? attn_fn<128, true, true>(bucket) : attn_fn<128, false, true>(bucket))
-                  : (draft ? attn_fn<64, true, true>(bucket) : attn_fn<64, false, true>(bucket));
-  else
-    fn = D == 128 ? (draft ? attn_fn<128, true, false>(bucket) : attn_fn<128, false, false>(bucket))
-                  : (draft ? attn_fn<64, true, false>(bucket) : attn_fn<64, false, false>(bucket));
+  const void* fn = mode == kModeDev ? attn_fn_dm<kModeDev>(D, draft, bucket)
+                   : mode == kModeAppend ? attn_fn_dm<kModeAppend>(D, draft, bucket)
+                                         : attn_fn_dm<kModeHost>(D, draft, bucket);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
   slot = cus * per_cu;
   return slot;
 }
 
-template <int D, bool DRAFT, int NB, bool DEV, class Full>
+template <int D, bool DRAFT, int NB, int MODE, class Full>
 hipError_t launch_attention_n(const Full& f, hipStream_t st) {
-  const AttnArgsN<NB, DEV> a = narrow<NB>(f);
+  const AttnArgsN<NB, MODE> a = narrow<NB>(f);
   const dim3 grid(a.n_titems_total + a.n_qitems_total, a.H);
-  hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, DEV>), grid, dim3(64), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE>), grid, dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 cgrid(a.B * a.m, a.H);
-  hipLaunchKernelGGL((combine_kernel<D, NB, DEV>), cgrid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((combine_kernel<D, NB, MODE>), cgrid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, bool DRAFT, bool DEV, class Full>
+template <int D, bool DRAFT, int MODE, class Full>
 hipError_t launch_attention_d(const Full& a, hipStream_t st) {
   switch (batch_bucket(a.B)) {
-    case 1: return launch_attention_n<D, DRAFT, 1, DEV>(a, st);
-    case 8: return launch_attention_n<D, DRAFT, 8, DEV>(a, st);
-    default: return launch_attention_n<D, DRAFT, QS_MAX_BATCH, DEV>(a, st);
+    case 1: return launch_attention_n<D, DRAFT, 1, MODE>(a, st);
+    case 8: return launch_attention_n<D, DRAFT, 8, MODE>(a, st);
+    default: return launch_attention_n<D, DRAFT, QS_MAX_BATCH, MODE>(a, st);
   }
 }
 
-hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st) {
+template <int MODE, class Full>
+hipError_t launch_attention_m(const Full& a, int D, bool draft, hipStream_t st) {
   if (D == 128)
-    return draft ? launch_attention_d<128, true, false>(a, st) : launch_attention_d<128, false, false>(a, st);
-  return draft ? launch_attention_d<64, true, false>(a, st) : launch_attention_d<64, false, false>(a, st);
+    return draft ? launch_attention_d<128, true, MODE>(a, st) : launch_attention_d<128, false, MODE>(a, st);
+  return draft ? launch_attention_d<64, true, MODE>(a, st) : launch_attention_d<64, false, MODE>(a, st);
 }
 
+hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st) {
+  return launch_attention_m<kModeHost>(a, D, draft, st);
+}
 hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStream_t st) {
-  if (D == 128)
-    return draft ? launch_attention_d<128, true, true>(a, st) : launch_attention_d<128, false, true>(a, st);
-  return draft ? launch_attention_d<64, true, true>(a, st) : launch_attention_d<64, false, true>(a, st);
+  return launch_attention_m<kModeDev>(a, D, draft, st);
+}
+hipError_t launch_attention_app(const AttnAppArgs& a, int D, bool draft, hipStream_t st) {
+  return launch_attention_m<kModeAppend>(a, D, draft, st);
 }
 
 }  // namespace qs

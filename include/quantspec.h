@@ -221,6 +221,23 @@ qs_status qs_attend_draft(qs_cache* cache, int32_t layer, const void* d_q, float
 qs_status qs_attend_verify(qs_cache* cache, int32_t layer, const void* d_q, int32_t m,
                            float sm_scale, float* d_out, void* stream);
 
+/* Append then attend, fused: the same result, ring contents and counters as qs_append(cache,
+ * layer, d_k, d_v, n_max, h_n, stream) followed by qs_attend_draft(cache, layer, d_q, sm_scale,
+ * d_out, stream), with no separate append launch -- the attention's tail work items read the
+ * new tokens from d_k / d_v and write them to their ring slots as they attend over them.  The
+ * verify form appends the m verified tokens themselves (d_k, d_v: fp16 [B][m][H][D]) and then
+ * runs qs_attend_verify with m queries.  Validation (and errors) are those of the two verbs in
+ * sequence, all made before anything changes.  [QuantSpec Guide, "3. Double Full-Precision
+ * Cache Buffer (CF1 and CF2)" and the verification-loop listing: each drafted token's K/V
+ * enters the buffer before the next draft step attends; Pith review, "What carries the
+ * argument".] */
+qs_status qs_append_attend_draft(qs_cache* cache, int32_t layer, const void* d_k,
+                                 const void* d_v, int32_t n_max, const int32_t* h_n,
+                                 const void* d_q, float sm_scale, float* d_out, void* stream);
+qs_status qs_append_attend_verify(qs_cache* cache, int32_t layer, const void* d_k,
+                                  const void* d_v, const void* d_q, int32_t m, float sm_scale,
+                                  float* d_out, void* stream);
+
 /* Host copies of the bookkeeping of `layer`: h_nq, h_nt, h_head are int32 [B] (any may be
  * NULL). */
 qs_status qs_get_state(const qs_cache* cache, int32_t layer, int32_t* h_nq, int32_t* h_nt,

@@ -285,6 +285,54 @@ def test_draft_equals_one_query_verify_when_lower_planes_are_the_offset(D):
     assert diff <= 1e-5 * max(ref, 1e-3)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fused_append_attend_equals_append_then_attend(D):
+    """qs_append_attend_draft / _verify give the oracle's outputs and, bit for bit, the outputs,
+    ring contents and counters of qs_append followed by qs_attend_*: ragged per-sequence counts,
+    new tokens straddling a 64-token tail chunk, a sequence whose ring head is G, and a fused
+    verify after the draft tokens are rolled back."""
+    log(f"case: fused append + attend D={D}")
+    B, H, gamma = 3, 4, 4
+    ls = Lockstep(1, B, H, D, 8 * G, gamma, tag=f"fused{D}")
+    plain = Cache(1, B, H, D, 8 * G, gamma)
+    lens = [3 * G + 62, 2 * G + 10, 5 * G]              # heads G, 0, G; tails 62, 10, 0
+    k, v = kv(B, max(lens), H, D, 940)
+    ls.prefill(0, k, v, n=lens)
+    plain.prefill(0, k, v, n=lens)
+    step_n = [[1, 1, 1], [2, 0, 1], [1, 2, 0], [1, 1, 1]]   # the second step crosses 64 in seq 0
+    for i, n in enumerate(step_n):
+        kn, vn = kv(B, max(n), H, D, 950 + i)
+        q = qd(B, H, D, 960 + i)
+        out = ls.gpu.append_attend_draft(0, kn, vn, q, n=n)
+        ls.orc[0].append(0, ls._host_heads(kn, 2), ls._host_heads(vn, 2), n)
+        ref = ls.orc[0].attend_draft(0, ls._host_heads(q, 1))
+        torch.cuda.synchronize()
+        ls._cmp_out(out, ref, f"fused draft {i}")
+        plain.append(0, kn, vn, n)
+        assert torch.equal(out, plain.attend_draft(0, q)), i
+    ls.rollback(0, [2, 2, 1])
+    plain.rollback(0, [2, 2, 1])
+    kv_, vv_ = kv(B, gamma + 1, H, D, 970)
+    qm = qv(B, gamma + 1, H, D, 971)
+    out = ls.gpu.append_attend_verify(0, kv_, vv_, qm)
+    ls.orc[0].append(0, ls._host_heads(kv_, 2), ls._host_heads(vv_, 2))
+    ref = ls.orc[0].attend_verify(0, ls._host_heads(qm, 2))
+    torch.cuda.synchronize()
+    ls._cmp_out(out, ref, "fused verify")
+    plain.append(0, kv_, vv_)
+    assert torch.equal(out, plain.attend_verify(0, qm))
+    ls.check_planes(0)                                   # ring slots bit-exact vs the oracle
+    assert all(np.array_equal(x, y) for x, y in zip(ls.gpu.state(0), plain.state(0)))
+    nq, nt, head = plain.state(0)
+    for b in range(B):
+        slots = [(int(head[b]) + j) % (2 * G) for j in range(int(nt[b]))]
+        for name in ("tail_k", "tail_v"):
+            assert torch.equal(ls.gpu.section(name, 0)[b][:, slots].view(torch.int16),
+                               plain.section(name, 0)[b][:, slots].view(torch.int16)), (b, name)
+    assert head.tolist() == [G, 0, G]
+    plain.close()
+
+
 def test_result_does_not_depend_on_the_split():
     """The split-K log-sum-exp merge reaches one softmax whatever the split: one sequence's
     outputs alone (many workers per head), inside a batch of 8 (few workers per head), and in
