@@ -24,7 +24,8 @@ EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_des
            "qs_attend_verify", "qs_get_state", "qs_last_error", "qs_spec_workspace_bytes",
            "qs_spec_accept", "qs_state_to_device", "qs_state_from_device", "qs_append_dev",
            "qs_rollback_dev", "qs_flush_dev", "qs_commit_dev", "qs_attend_draft_dev",
-           "qs_attend_verify_dev", "qs_append_attend_draft", "qs_append_attend_verify")
+           "qs_attend_verify_dev", "qs_append_attend_draft", "qs_append_attend_verify",
+           "qs_attend_draft_gqa", "qs_attend_verify_gqa")
 
 # Bits of the device-mode error word (include/quantspec.h, device mode).
 DEV_ERR_APPEND, DEV_ERR_ROLLBACK, DEV_ERR_FLUSH, DEV_ERR_ATTEND = 1, 2, 4, 8
@@ -76,6 +77,8 @@ def lib():
         L.qs_attend_verify.argtypes = [P, I32, P, I32, F, P, P]
         L.qs_get_state.argtypes = [P, I32, PI, PI, PI]
         L.qs_append_attend_draft.argtypes = [P, I32, P, P, I32, PI, P, F, P, P]
+        L.qs_attend_draft_gqa.argtypes = [P, I32, P, I32, F, P, P]
+        L.qs_attend_verify_gqa.argtypes = [P, I32, P, I32, I32, F, P, P]
         L.qs_append_attend_verify.argtypes = [P, I32, P, P, P, I32, F, P, P]
         L.qs_last_error.argtypes = [P]
         L.qs_last_error.restype = ctypes.c_char_p
@@ -212,6 +215,29 @@ class Cache:
                                            q.shape[1], float(sm_scale),
                                            self._dev(out, torch.float32, "out"),
                                            self._stream(stream)), "qs_attend_verify")
+        return out
+
+    def attend_draft_gqa(self, layer, q, g, sm_scale=1.0, out=None, stream=None):
+        """Grouped queries: q fp16 [B][H*g][D] (query head h*g + r reads cached head h)."""
+        torch = self.torch
+        assert tuple(q.shape) == (self.B, self.H * g, self.D)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        self._check(lib().qs_attend_draft_gqa(self._h, layer, self._dev(q, torch.float16, "q"), g,
+                                              float(sm_scale), self._dev(out, torch.float32, "out"),
+                                              self._stream(stream)), "qs_attend_draft_gqa")
+        return out
+
+    def attend_verify_gqa(self, layer, q, g, sm_scale=1.0, out=None, stream=None):
+        """Grouped queries: q fp16 [B][m][H*g][D]."""
+        torch = self.torch
+        assert q.dim() == 4 and q.shape[0] == self.B and tuple(q.shape[2:]) == (self.H * g, self.D)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        self._check(lib().qs_attend_verify_gqa(self._h, layer, self._dev(q, torch.float16, "q"),
+                                               q.shape[1], g, float(sm_scale),
+                                               self._dev(out, torch.float32, "out"),
+                                               self._stream(stream)), "qs_attend_verify_gqa")
         return out
 
     def append_attend_draft(self, layer, k, v, q, n=None, sm_scale=1.0, out=None, stream=None):

@@ -28,6 +28,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream
 hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_attention_app(const AttnAppArgs& a, int D, bool draft, hipStream_t st);
+hipError_t launch_attention_gqa(const AttnGqaArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_state(const StateArgs& a, hipStream_t st);
 int attention_slots(int D, bool draft, int B, int mode);
 }  // namespace qs
@@ -352,6 +353,43 @@ static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, 
   return QS_OK;
 }
 
+// Grouped queries: g query heads per cached head, mt query tokens (1 for the draft); the m =
+// mt * g query columns of a (sequence, cached head) share its split workspace, so m <= gamma_max
+// + 1.
+static qs_status attend_gqa(qs_cache* c, int32_t layer, const void* d_q, int32_t mt, int32_t g,
+                            float sm_scale, float* d_out, void* stream, bool draft) {
+  if (!c) return QS_ERR_INVALID_ARG;
+  if (c->dev) return fail(c, QS_ERR_STATE, kInDeviceMode);
+  if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
+  if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
+  const qs_config& cf = c->cfg;
+  if (g < 1 || g > QS_MAX_QUERIES) return fail(c, QS_ERR_INVALID_ARG, "g must be in 1..16");
+  if (!draft && (mt < 1 || mt > cf.gamma_max + 1))
+    return fail(c, QS_ERR_INVALID_ARG, "m must be in 1..gamma_max+1");
+  if ((long long)mt * g > cf.gamma_max + 1)
+    return fail(c, QS_ERR_INVALID_ARG, "m * g must be <= gamma_max + 1 (query columns per head)");
+  std::string err;
+  qs_status s = c->st.check_attend(layer, mt, draft, &err);
+  if (s != QS_OK) return fail(c, s, err);
+  qs::Seq seqs[QS_MAX_BATCH];
+  for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
+  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeGqa);
+  qs::AttnGqaArgs a{};
+  attn_args(c, layer, d_q, mt * g, sm_scale, d_out, p, a);
+  for (int b = 0; b < cf.batch; ++b) {
+    a.nq[b] = seqs[b].nq;
+    a.nt[b] = seqs[b].nt;
+    a.head[b] = seqs[b].head;
+  }
+  a.gq = g;
+  a.mt = mt;
+  a.hq = cf.n_heads * g;
+  hipError_t e = qs::launch_attention_gqa(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
+  c->err.clear();
+  return QS_OK;
+}
+
 // Append n[b] tokens of d_k / d_v [B][n_max][H][D], then attend: one launch pair, the tail
 // items writing the new tokens to the ring as they read them.  Validation is that of the two
 // verbs in sequence, all before anything changes.
@@ -409,6 +447,16 @@ qs_status qs_attend_draft(qs_cache* c, int32_t layer, const void* d_q, float sm_
 qs_status qs_attend_verify(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
                            float* d_out, void* stream) {
   return attend(c, layer, d_q, m, sm_scale, d_out, stream, false);
+}
+
+qs_status qs_attend_draft_gqa(qs_cache* c, int32_t layer, const void* d_q, int32_t g,
+                              float sm_scale, float* d_out, void* stream) {
+  return attend_gqa(c, layer, d_q, 1, g, sm_scale, d_out, stream, true);
+}
+
+qs_status qs_attend_verify_gqa(qs_cache* c, int32_t layer, const void* d_q, int32_t m, int32_t g,
+                               float sm_scale, float* d_out, void* stream) {
+  return attend_gqa(c, layer, d_q, m, g, sm_scale, d_out, stream, false);
 }
 
 qs_status qs_append_attend_draft(qs_cache* c, int32_t layer, const void* d_k, const void* d_v,

@@ -74,6 +74,7 @@ enum : int {
   kModeHost = 0,    // counters by value
   kModeDev = 1,     // counters from the state section (device mode)
   kModeAppend = 2,  // counters by value, and the call first appends tokens to the tail
+  kModeGqa = 3,     // counters by value; gq query heads share each cached (key/value) head
 };
 
 template <int NB, int MODE = kModeHost>
@@ -118,6 +119,17 @@ struct AttnArgsN<NB, kModeAppend> : AttnArgsN<NB, kModeHost> {
   int32_t an[NB];
 };
 using AttnAppArgs = AttnArgsN<QS_MAX_BATCH, kModeAppend>;
+
+// Grouped queries: query head h * gq + r (r < gq) reads cached head h.  The m query columns of a
+// (sequence, cached head) are c = i * gq + r for query token i < mt (m = mt * gq <= 16); q and
+// out are [B][mt][hq][D] with hq = H * gq.  Both passes run the MFMA item; the draft one reads
+// only the upper planes.
+template <int NB>
+struct AttnArgsN<NB, kModeGqa> : AttnArgsN<NB, kModeHost> {
+  static constexpr int kMode = kModeGqa;
+  int32_t gq, mt, hq;
+};
+using AttnGqaArgs = AttnArgsN<QS_MAX_BATCH, kModeGqa>;
 
 struct AppendHeader {
   const uint16_t* k;     // [B][n_max][H][D]

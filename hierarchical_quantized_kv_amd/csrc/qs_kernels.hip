@@ -206,6 +206,27 @@ __device__ __forceinline__ int seq_head(const Args& a, int b) {
   else return a.head[b];
 }
 
+// Query column c of (b, h): its row in q and out ([B][m][H][D]; with grouped queries column
+// c = i gq + r is query token i of query head h gq + r, [B][mt][hq][D]), and its query token
+// (for the causal mask among the tail tokens) out of how many.
+template <class Args>
+__device__ __forceinline__ size_t qrow(const Args& a, int b, int h, int c) {
+  if constexpr (Args::kMode == kModeGqa)
+    return ((size_t)b * a.mt + c / a.gq) * a.hq + (size_t)h * a.gq + c % a.gq;
+  else
+    return ((size_t)b * a.m + c) * a.H + h;
+}
+template <class Args>
+__device__ __forceinline__ int col_token(const Args& a, int c) {
+  if constexpr (Args::kMode == kModeGqa) return c / a.gq;
+  else return c;
+}
+template <class Args>
+__device__ __forceinline__ int n_tokens(const Args& a) {
+  if constexpr (Args::kMode == kModeGqa) return a.mt;
+  else return a.m;
+}
+
 // Record of split `split`, query `i` of (b, h).
 template <class Args>
 __device__ __forceinline__ float* record(const Args& a, int D, int b, int h, int split, int i) {
@@ -547,7 +568,9 @@ struct VerifyBuf {
   float4 vm;  // value (s, z) of tokens 2*lane, 2*lane+1
 };
 
-template <int D>
+// UPPER: only the upper planes are read (the draft pass over grouped queries); the lower
+// nibbles are then the draft offset.
+template <int D, bool UPPER = false>
 __device__ __forceinline__ void verify_load_k(const Streams& sm, int gi, int half, VerifyBuf<D>& buf) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
@@ -558,18 +581,24 @@ __device__ __forceinline__ void verify_load_k(const Streams& sm, int gi, int hal
   for (int t = 0; t < 4; ++t) {
     const uint32_t o = voff + (8 * (t >> 1) + (t & 1)) * (D / 2);
     if constexpr (S::KK == 4) {
-      const uint4 u = bld16(sm.uk, o, soff), l = bld16(sm.lk, o, soff);
+      const uint4 u = bld16(sm.uk, o, soff);
       buf.ku[t][0] = u.x; buf.ku[t][1] = u.y; buf.ku[t][2] = u.z; buf.ku[t][3] = u.w;
-      buf.kl[t][0] = l.x; buf.kl[t][1] = l.y; buf.kl[t][2] = l.z; buf.kl[t][3] = l.w;
+      if constexpr (!UPPER) {
+        const uint4 l = bld16(sm.lk, o, soff);
+        buf.kl[t][0] = l.x; buf.kl[t][1] = l.y; buf.kl[t][2] = l.z; buf.kl[t][3] = l.w;
+      }
     } else {
-      const uint2 u = bld8(sm.uk, o, soff), l = bld8(sm.lk, o, soff);
+      const uint2 u = bld8(sm.uk, o, soff);
       buf.ku[t][0] = u.x; buf.ku[t][1] = u.y;
-      buf.kl[t][0] = l.x; buf.kl[t][1] = l.y;
+      if constexpr (!UPPER) {
+        const uint2 l = bld8(sm.lk, o, soff);
+        buf.kl[t][0] = l.x; buf.kl[t][1] = l.y;
+      }
     }
   }
 }
 
-template <int D>
+template <int D, bool UPPER = false>
 __device__ __forceinline__ void verify_load_v(const Streams& sm, int gi, int half, VerifyBuf<D>& buf) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
@@ -579,7 +608,7 @@ __device__ __forceinline__ void verify_load_v(const Streams& sm, int gi, int hal
   for (int rt = 0; rt < S::RT; ++rt) {
     const uint32_t o = voff + rt * 16 * (kGroup / 4);
     buf.vu[rt] = bld8(sm.uv, o, soff);
-    buf.vl[rt] = bld8(sm.lv, o, soff);
+    if constexpr (!UPPER) buf.vl[rt] = bld8(sm.lv, o, soff);
   }
 }
 
@@ -602,11 +631,13 @@ struct VerifyAcc {
 // One group of a verify worker, in two 64-token halves.  With PF the buffers are refilled with
 // group gn as each part of group gi is consumed (a template flag, so that the number of loads in
 // flight at every wait is fixed).
-template <int D, bool PF, class Args>
+template <int D, bool PF, bool UPPER, class Args>
 __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, VerifyBuf<D>& buf,
                                              int gi, int gn, VerifyLds& L, VerifyAcc<D>& st) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
+  // UPPER: every lower nibble is the draft offset
+  const uint32_t loff = UPPER ? (uint32_t)a.draft_offset * 0x11111111u : 0u;
   const int j = lane & 15;   // query column
   const int g = lane >> 4;   // k-group
   const int m = a.m;
@@ -669,7 +700,7 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < S::KK; ++kk) {
-        const f16x8 A = codes_f16(buf.ku[t][kk], buf.kl[t][kk]);
+        const f16x8 A = codes_f16(buf.ku[t][kk], UPPER ? loff : buf.kl[t][kk]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq[kk], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bql[kk], acc, 0, 0, 0);
       }
@@ -679,9 +710,9 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
     __builtin_amdgcn_sched_barrier(0);
     // next key half: the other half of this group, or the first half of the next group
     if (half == 0)
-      verify_load_k<D>(sm, gi, 1, buf);
+      verify_load_k<D, UPPER>(sm, gi, 1, buf);
     else if constexpr (PF)
-      verify_load_k<D>(sm, gn, 0, buf);
+      verify_load_k<D, UPPER>(sm, gn, 0, buf);
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -718,7 +749,7 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
 #pragma unroll
       for (int rt = 0; rt < S::RT; ++rt) {
         const uint32_t uw = q == 0 ? buf.vu[rt].x : buf.vu[rt].y;
-        const uint32_t lw = q == 0 ? buf.vl[rt].x : buf.vl[rt].y;
+        const uint32_t lw = UPPER ? loff : (q == 0 ? buf.vl[rt].x : buf.vl[rt].y);
         f16x8 A = codes_f16(uw, lw);
         const f16x2 a0 = f16x2{A[0], A[1]} - c1152, a1 = f16x2{A[2], A[3]} - c1152;
         const f16x2 a2 = f16x2{A[4], A[5]} - c1152, a3 = f16x2{A[6], A[7]} - c1152;
@@ -730,13 +761,13 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
     }
     __builtin_amdgcn_sched_barrier(0);
     if (half == 0)
-      verify_load_v<D>(sm, gi, 1, buf);
+      verify_load_v<D, UPPER>(sm, gi, 1, buf);
     else if constexpr (PF)
-      verify_load_v<D>(sm, gn, 0, buf);
+      verify_load_v<D, UPPER>(sm, gn, 0, buf);
   }
 }
 
-template <int D, class Args>
+template <int D, bool UPPER, class Args>
 __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyLds& L) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
@@ -750,8 +781,7 @@ __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyL
   // padding query columns j >= m stay zero
   if (lane < D / 2)
     for (int i = 0; i < m; ++i) {
-      const uint32_t qq =
-          reinterpret_cast<const uint32_t*>(a.q + (((size_t)b * m + i) * a.H + h) * D)[lane];
+      const uint32_t qq = reinterpret_cast<const uint32_t*>(a.q + qrow(a, b, h, i) * D)[lane];
       L.qs[i][lane] = make_float2(lo_h(qq) * a.qscale, hi_h(qq) * a.qscale);
     }
   for (int x = lane; x < 2 * 4 * 64; x += 64) (&L.bq[0][0][0])[x] = make_uint4(0, 0, 0, 0);
@@ -768,17 +798,17 @@ __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyL
   const Streams sm = make_streams(a, bh, D);
   VerifyBuf<D> buf;
   if (gs.first < gs.ng) {
-    verify_load_k<D>(sm, gs.first, 0, buf);
+    verify_load_k<D, UPPER>(sm, gs.first, 0, buf);
     verify_load_meta<D>(sm, gs.first, buf);
-    verify_load_v<D>(sm, gs.first, 0, buf);
+    verify_load_v<D, UPPER>(sm, gs.first, 0, buf);
     const int total = (gs.ng - gs.first + gs.step - 1) / gs.step;
     int gi = gs.first, done = 0;
     for (; gi + gs.step < gs.ng; gi += gs.step, ++done) {
       pace(total - done, total);
-      verify_group<D, true>(a, sm, buf, gi, gi + gs.step, L, st);
+      verify_group<D, true, UPPER>(a, sm, buf, gi, gi + gs.step, L, st);
     }
     pace(1, total);
-    verify_group<D, false>(a, sm, buf, gi, -1, L, st);
+    verify_group<D, false, UPPER>(a, sm, buf, gi, -1, L, st);
   }
 
   st.l_run += __shfl_xor(st.l_run, 16);
@@ -860,7 +890,7 @@ __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, Tai
   for (int k = 0; k < QW; ++k) {
     const int w = lane + 64 * k;            // word w of the m x D/2 query block
     const int i = w / (D / 2), c = w % (D / 2);
-    qw[k] = i < m ? qsrc[(((size_t)b * m + i) * a.H + h) * (D / 2) + c] : 0u;
+    qw[k] = i < m ? qsrc[qrow(a, b, h, i) * (D / 2) + c] : 0u;
   }
   uint32_t kr[D / 2];
 #pragma unroll
@@ -880,7 +910,7 @@ __device__ void tail_item(const Args& a, int b, int h, int chunk, int split, Tai
 #pragma unroll
     for (int c = 0; c < D / 2; ++c) s = dot2(as_h2(kr[c]), as_h2(L.q[0][i * (D / 2) + c]), s);
     s *= a.qscale;
-    const bool vis = valid && t <= nt - m + i;
+    const bool vis = valid && t <= nt - n_tokens(a) + col_token(a, i);
     if (!vis) s = -INFINITY;
     const float mx = wave_max_from(s, 1);
     const float p = vis ? fast_exp2(s - mx) : 0.f;
@@ -967,9 +997,13 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
   return b;
 }
 
+// The draft pass runs the VALU item (3 waves per SIMD), except over grouped queries, where both
+// passes run the MFMA item (2 waves per SIMD).
 template <int D, bool DRAFT, int NB, int MODE>
-__global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgsN<NB, MODE> a) {
-  using PassLds = typename std::conditional<DRAFT, DraftLds, VerifyLds>::type;
+__global__ __launch_bounds__(64, (DRAFT && MODE != kModeGqa) ? 3 : 2) void attn_kernel(
+    const AttnArgsN<NB, MODE> a) {
+  constexpr bool kValu = DRAFT && MODE != kModeGqa;
+  using PassLds = typename std::conditional<kValu, DraftLds, VerifyLds>::type;
   __shared__ union {
     PassLds p;
     TailLds t;
@@ -986,10 +1020,10 @@ __global__ __launch_bounds__(64, DRAFT ? 3 : 2) void attn_kernel(const AttnArgsN
     const int y = x - a.n_titems_total;
     const int b = find_seq<NB>(a.qitem_base, a.B, y);
     const int item = y - a.qitem_base[b];
-    if constexpr (DRAFT)
+    if constexpr (kValu)
       draft_quant_item<D>(a, b, h, item, lds.p);
     else
-      verify_quant_item<D>(a, b, h, item, lds.p);
+      verify_quant_item<D, DRAFT>(a, b, h, item, lds.p);
   }
 }
 
@@ -1065,7 +1099,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB, MODE> 
     float4 oo = po[0][t];
     for (int q = 1; q < NP; ++q) lse_merge(mm, ll, oo, pml[q].x, pml[q].y, po[q][t]);
     const float inv = 1.f / ll;
-    float4* out = reinterpret_cast<float4*>(a.out + (((size_t)b * a.m + i) * a.H + h) * D);
+    float4* out = reinterpret_cast<float4*>(a.out + qrow(a, b, h, i) * D);
     out[t] = make_float4(oo.x * inv, oo.y * inv, oo.z * inv, oo.w * inv);
   }
 }
@@ -1404,6 +1438,16 @@ AttnArgsN<NB, kModeAppend> narrow(const AttnAppArgs& f) {
 }
 
 template <int NB>
+AttnArgsN<NB, kModeGqa> narrow(const AttnGqaArgs& f) {
+  AttnArgsN<NB, kModeGqa> a;
+  static_cast<AttnArgsN<NB>&>(a) = narrow<NB>(static_cast<const AttnArgs&>(f));
+  a.gq = f.gq;
+  a.mt = f.mt;
+  a.hq = f.hq;
+  return a;
+}
+
+template <int NB>
 AppendArgsN<NB> narrow(const AppendArgs& f) {
   AppendArgsN<NB> a;
   static_cast<AppendHeader&>(a) = f;
@@ -1482,9 +1526,9 @@ const void* attn_fn_dm(int D, bool draft, int bucket) {
 // one-wave workgroups of that kernel a compute unit holds at once (cached per device).
 int attention_slots(int D, bool draft, int B, int mode) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev][2][2][3][3];
+  static int cache[kMaxDev][2][2][4][3];
   int id = 0;
-  if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 2) return 0;
+  if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 3) return 0;
   const int bucket = batch_bucket(B);
   int& slot = cache[id][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
   if (slot > 0) return slot;
@@ -1492,7 +1536,8 @@ int attention_slots(int D, bool draft, int B, int mode) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess) return 0;
   const void* fn = mode == kModeDev ? attn_fn_dm<kModeDev>(D, draft, bucket)
                    : mode == kModeAppend ? attn_fn_dm<kModeAppend>(D, draft, bucket)
-                                         : attn_fn_dm<kModeHost>(D, draft, bucket);
+                   : mode == kModeGqa ? attn_fn_dm<kModeGqa>(D, draft, bucket)
+                                      : attn_fn_dm<kModeHost>(D, draft, bucket);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
   slot = cus * per_cu;
   return slot;
@@ -1534,6 +1579,9 @@ hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStre
 }
 hipError_t launch_attention_app(const AttnAppArgs& a, int D, bool draft, hipStream_t st) {
   return launch_attention_m<kModeAppend>(a, D, draft, st);
+}
+hipError_t launch_attention_gqa(const AttnGqaArgs& a, int D, bool draft, hipStream_t st) {
+  return launch_attention_m<kModeGqa>(a, D, draft, st);
 }
 
 }  // namespace qs

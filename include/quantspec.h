@@ -221,6 +221,24 @@ qs_status qs_attend_draft(qs_cache* cache, int32_t layer, const void* d_q, float
 qs_status qs_attend_verify(qs_cache* cache, int32_t layer, const void* d_q, int32_t m,
                            float sm_scale, float* d_out, void* stream);
 
+/* Grouped queries: g query heads share each cached (key/value) head -- query head h*g + r
+ * (r < g) attends over cached head h, so the cache holds H = n_heads heads and the queries
+ * H*g.  The draft form takes one query per query head, d_q fp16 [B][H*g][D], d_out fp32
+ * [B][H*g][D]; the verify form m per query head, d_q fp16 [B][m][H*g][D], d_out fp32
+ * [B][m][H*g][D], with the causal tail mask of qs_attend_verify per query token.  The m*g query
+ * columns of a (sequence, cached head) go through one pass over its planes (both passes use
+ * MFMA; the draft reads only the upper planes, its lower nibbles being draft_offset), so the
+ * cached bytes are read once per group of g query heads.
+ * Errors: as qs_attend_draft / qs_attend_verify; QS_ERR_INVALID_ARG if g is outside 1..16 or
+ * m*g > gamma_max + 1 (the split workspace holds gamma_max + 1 query columns per head).
+ * [QuantSpec Guide, "Empirical Evaluation: QuantSpec Benchmark Results" (LLaMA-3.1-8B among the
+ * evaluated models, whose key/value heads are shared by groups of query heads); the passes as
+ * in qs_attend_draft / qs_attend_verify.] */
+qs_status qs_attend_draft_gqa(qs_cache* cache, int32_t layer, const void* d_q, int32_t g,
+                              float sm_scale, float* d_out, void* stream);
+qs_status qs_attend_verify_gqa(qs_cache* cache, int32_t layer, const void* d_q, int32_t m,
+                               int32_t g, float sm_scale, float* d_out, void* stream);
+
 /* Append then attend, fused: the same result, ring contents and counters as qs_append(cache,
  * layer, d_k, d_v, n_max, h_n, stream) followed by qs_attend_draft(cache, layer, d_q, sm_scale,
  * d_out, stream), with no separate append launch -- the attention's tail work items read the

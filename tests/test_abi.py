@@ -141,6 +141,13 @@ def test_validation_before_any_launch(lib):
     assert lib.qs_attend_draft(h, 0, P, ctypes.c_float(float("nan")), P, None) == binding.QS_ERR_INVALID_ARG
     assert lib.qs_attend_draft(h, 0, None, ctypes.c_float(1.0), P, None) == binding.QS_ERR_INVALID_ARG
     assert lib.qs_get_state(h, 0, nq, nt, hd) == 0 and list(nt) == [0, 0, 0]
+    # grouped queries: g in 1..16, m * g within gamma_max + 1 = 7 query columns per head
+    F1 = ctypes.c_float(1.0)
+    assert lib.qs_attend_draft_gqa(h, 0, P, 0, F1, P, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_attend_draft_gqa(h, 0, P, 8, F1, P, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_attend_verify_gqa(h, 0, P, 2, 4, F1, P, None) == binding.QS_ERR_INVALID_ARG
+    assert lib.qs_attend_draft_gqa(h, 0, P, 7, F1, P, None) == binding.QS_ERR_STATE  # empty
+    assert lib.qs_attend_verify_gqa(h, 0, P, 1, 7, F1, P, None) == binding.QS_ERR_STATE
     lib.qs_cache_destroy(h)
 
 

@@ -333,6 +333,41 @@ def test_fused_append_attend_equals_append_then_attend(D):
     plain.close()
 
 
+@pytest.mark.parametrize("D,g,mt", [(128, 4, 4), (64, 2, 3), (128, 8, 1), (64, 16, 1)])
+def test_grouped_queries_match_the_oracle(D, g, mt):
+    """Grouped queries: query head h*g + r attends over cached head h.  The reference is the
+    oracle's own draft / verify over the cached heads, called once per r with the queries of
+    heads h*g + r.  Ragged batch: a tail-only sequence, one with a two-chunk tail."""
+    log(f"case: grouped queries D={D} g={g} m={mt}")
+    B, H = 3, 2
+    ls = Lockstep(1, B, H, D, 8 * G, 15, tag=f"gqa{D}x{g}x{mt}")
+    lens = [5 * G + 70, 100, 3 * G]
+    k, v = kv(B, max(lens), H, D, 980 + g)
+    ls.prefill(0, k, v, n=lens)
+    kt, vt = kv(B, mt, H, D, 985 + g)
+    ls.append(0, kt, vt)                                 # the verified tokens are tail tokens
+    qd_ = qd(B, H * g, D, 990 + g, gain=2.0)
+    qv_ = qv(B, mt, H * g, D, 991 + g)
+    out_d = ls.gpu.attend_draft_gqa(0, qd_, g)
+    out_v = ls.gpu.attend_verify_gqa(0, qv_, g)
+    torch.cuda.synchronize()
+    for r in range(g):
+        heads = [h * g + r for h in range(H)]
+        ref_d = ls.orc[0].attend_draft(0, qd_[:, heads].cpu().numpy())
+        ref_v = ls.orc[0].attend_verify(0, qv_[:, :, heads].contiguous().cpu().numpy())
+        ls._cmp_out(out_d[:, heads], ref_d, f"gqa draft r={r}")
+        ls._cmp_out(out_v[:, :, heads], ref_v, f"gqa verify r={r}")
+    if g == 8:  # one query head per cached head through the grouped path: the plain draft
+        q1 = qd(B, H, D, 995)
+        d1 = ls.gpu.attend_draft_gqa(0, q1, 1)
+        d0 = ls.gpu.attend_draft(0, q1)
+        torch.cuda.synchronize()
+        diff = float((d1 - d0).abs().max())
+        log(f"gqa g=1 MFMA draft vs VALU draft: max abs diff {diff:.2e}")
+        assert diff <= 2e-5
+    log(f"gqa{D}x{g}x{mt}: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
 def test_result_does_not_depend_on_the_split():
     """The split-K log-sum-exp merge reaches one softmax whatever the split: one sequence's
     outputs alone (many workers per head), inside a batch of 8 (few workers per head), and in
