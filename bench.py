@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fuse", action="store_true",
                     help="separate append and attention calls instead of the fused ones")
+    ap.add_argument("--no-gqa", action="store_true",
+                    help="skip the grouped-query layer (gqa: null)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replayed step (graph_step: null)")
     ap.add_argument("--cpu-threads", type=int, default=16,
@@ -340,6 +342,7 @@ def main():
     p_us, p_gbs, p_bytes = summarize(pf_ev, "prefill")
     sa = {sb: summarize(e, f"spec_accept_batch{sb}") for sb, e in sa_ev.items()}
 
+    gqa = None if args.no_gqa else measure_gqa(torch, stream, spin_cycles, dev)
     read_ceiling = measure_read_ceiling(torch, stream)
 
     cpu = None
@@ -404,6 +407,7 @@ def main():
                            "bound": "latency (dependent round trips)" if sb == 1 else "hbm"}
             for sb, (us, gbs, nb) in sa.items()},
         "graph_step": graph_line,
+        "gqa": gqa,
         "samples_dropped": dropped,
         "read_ceiling": read_ceiling,
         "cpu_baseline": cpu,
@@ -474,6 +478,54 @@ def measure_graph_steps(torch, cache, x, accept, args, L, H, D, gamma, m, out_d,
             "note": "the timed step's calls captured once in a HIP graph (device-mode bookkeeping) "
                     "and replayed; each replay preceded by a 4-byte device copy of the step's "
                     "accepted count"}
+
+
+def measure_gqa(torch, stream, spin_cycles, dev, ctx=131072, Hkv=8, g=4, mt=4, reps=20):
+    """Grouped queries on a Llama-3.1-8B-shaped layer: 8 cached heads shared by 4 query heads
+    each (32 query heads), head_dim 128, ctx tokens quantized plus a 64 + mt token tail; the
+    draft (32 queries, upper planes) and the mt-token verify (16 query columns per cached head)
+    timed over `reps` consecutive calls behind the spin kernel.  Bytes: the cached heads' planes
+    and metadata once, the tail, and q / out of every query head."""
+    from hierarchical_quantized_kv_amd import synth
+    from hierarchical_quantized_kv_amd.binding import Cache
+    D = 128
+    cache = Cache(1, 1, Hkv, D, ctx + 16 * G, 15)
+    k, v = synth.kv_device(torch, 1, ctx + 64 + mt, Hkv, D, 4242, 4243, dev,
+                           outliers=synth.outlier_channels(Hkv, D, 4244))
+    cache.prefill(0, k[:, :ctx + 64].contiguous(), v[:, :ctx + 64].contiguous())
+    cache.append(0, k[:, ctx + 64:].contiguous(), v[:, ctx + 64:].contiguous())
+    del k, v
+    gen = torch.Generator(device=dev).manual_seed(4245)
+    qd = (torch.randn((1, Hkv * g, D), generator=gen, device=dev) / math.sqrt(D)).half()
+    qv = (torch.randn((1, mt, Hkv * g, D), generator=gen, device=dev) / math.sqrt(D)).half()
+    od = torch.empty((1, Hkv * g, D), dtype=torch.float32, device=dev)
+    ov = torch.empty((1, mt, Hkv * g, D), dtype=torch.float32, device=dev)
+    nt = 64 + mt
+    out = {"workload": f"Llama-3.1-8B-shaped layer: {Hkv} cached heads x {g} query heads each, "
+                       f"head_dim {D}, ctx {ctx} + {nt}-token tail; verify of {mt} tokens "
+                       f"({mt * g} query columns per cached head)"}
+    for name, fn, nbytes in (
+            ("draft", lambda: cache.attend_draft_gqa(0, qd, g, out=od),
+             Hkv * (ctx * (D + 8 * D // G + 8) + nt * 4 * D) + Hkv * g * (2 * D + 4 * D)),
+            ("verify", lambda: cache.attend_verify_gqa(0, qv, g, out=ov),
+             Hkv * (ctx * (2 * D + 8 * D // G + 8) + nt * 4 * D) + mt * Hkv * g * (2 * D + 4 * D))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(spin_cycles)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[f"{name}_us"] = round(us, 2)
+        out[f"{name}_bytes"] = int(nbytes)
+        out[f"{name}_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        out[f"{name}_frac"] = round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    cache.close()
+    return out
 
 
 def measure_read_ceiling(torch, stream):
