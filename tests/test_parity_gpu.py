@@ -285,21 +285,24 @@ def test_draft_equals_one_query_verify_when_lower_planes_are_the_offset(D):
     assert diff <= 1e-5 * max(ref, 1e-3)
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_fused_append_attend_equals_append_then_attend(D):
+@pytest.mark.parametrize("D,B", [(64, 3), (128, 3), (64, 9)])
+def test_fused_append_attend_equals_append_then_attend(D, B):
     """qs_append_attend_draft / _verify give the oracle's outputs and, bit for bit, the outputs,
     ring contents and counters of qs_append followed by qs_attend_*: ragged per-sequence counts,
     new tokens straddling a 64-token tail chunk, a sequence whose ring head is G, and a fused
     verify after the draft tokens are rolled back."""
-    log(f"case: fused append + attend D={D}")
-    B, H, gamma = 3, 4, 4
-    ls = Lockstep(1, B, H, D, 8 * G, gamma, tag=f"fused{D}")
+    log(f"case: fused append + attend D={D} B={B}")
+    H, gamma = 4, 4
+    ls = Lockstep(1, B, H, D, 8 * G, gamma, tag=f"fused{D}x{B}")
     plain = Cache(1, B, H, D, 8 * G, gamma)
-    lens = [3 * G + 62, 2 * G + 10, 5 * G]              # heads G, 0, G; tails 62, 10, 0
-    k, v = kv(B, max(lens), H, D, 940)
+    base = [3 * G + 62, 2 * G + 10, 5 * G]              # heads G, 0, G; tails 62, 10, 0
+    lens = [base[b % 3] + 5 * (b // 3) for b in range(B)]
+    k, v = kv(B, max(lens), H, D, 940 + B)
     ls.prefill(0, k, v, n=lens)
     plain.prefill(0, k, v, n=lens)
-    step_n = [[1, 1, 1], [2, 0, 1], [1, 2, 0], [1, 1, 1]]   # the second step crosses 64 in seq 0
+    # per-step counts, by sequence mod 3; the second step crosses 64 in sequence 0
+    step_n = [[row[b % 3] for b in range(B)]
+              for row in ([1, 1, 1], [2, 0, 1], [1, 2, 0], [1, 1, 1])]
     for i, n in enumerate(step_n):
         kn, vn = kv(B, max(n), H, D, 950 + i)
         q = qd(B, H, D, 960 + i)
@@ -310,8 +313,9 @@ def test_fused_append_attend_equals_append_then_attend(D):
         ls._cmp_out(out, ref, f"fused draft {i}")
         plain.append(0, kn, vn, n)
         assert torch.equal(out, plain.attend_draft(0, q)), i
-    ls.rollback(0, [2, 2, 1])
-    plain.rollback(0, [2, 2, 1])
+    drop = [[2, 2, 1][b % 3] for b in range(B)]
+    ls.rollback(0, drop)
+    plain.rollback(0, drop)
     kv_, vv_ = kv(B, gamma + 1, H, D, 970)
     qm = qv(B, gamma + 1, H, D, 971)
     out = ls.gpu.append_attend_verify(0, kv_, vv_, qm)
@@ -329,22 +333,23 @@ def test_fused_append_attend_equals_append_then_attend(D):
         for name in ("tail_k", "tail_v"):
             assert torch.equal(ls.gpu.section(name, 0)[b][:, slots].view(torch.int16),
                                plain.section(name, 0)[b][:, slots].view(torch.int16)), (b, name)
-    assert head.tolist() == [G, 0, G]
+    assert head.tolist() == [[G, 0, G][b % 3] for b in range(B)]
     plain.close()
 
 
-@pytest.mark.parametrize("D,g,mt", [(128, 4, 4), (64, 2, 3), (128, 8, 1), (64, 16, 1)])
-def test_grouped_queries_match_the_oracle(D, g, mt):
+@pytest.mark.parametrize("D,g,mt,B", [(128, 4, 4, 3), (64, 2, 3, 3), (128, 8, 1, 3),
+                                      (64, 16, 1, 3), (128, 4, 2, 1), (64, 3, 5, 1)])
+def test_grouped_queries_match_the_oracle(D, g, mt, B):
     """Grouped queries: query head h*g + r attends over cached head h.  The reference is the
     oracle's own draft / verify over the cached heads, called once per r with the queries of
     heads h*g + r.  Ragged batch: a tail-only sequence, one with a two-chunk tail."""
-    log(f"case: grouped queries D={D} g={g} m={mt}")
-    B, H = 3, 2
-    ls = Lockstep(1, B, H, D, 8 * G, 15, tag=f"gqa{D}x{g}x{mt}")
-    lens = [5 * G + 70, 100, 3 * G]
+    log(f"case: grouped queries D={D} g={g} m={mt} B={B}")
+    H = 2
+    ls = Lockstep(1, B, H, D, 8 * G, 15, tag=f"gqa{D}x{g}x{mt}x{B}")
+    lens = [5 * G + 70, 100, 3 * G][:B]
     k, v = kv(B, max(lens), H, D, 980 + g)
     ls.prefill(0, k, v, n=lens)
-    kt, vt = kv(B, mt, H, D, 985 + g)
+    kt, vt = kv(B, mt, H, D, 985 + g + B)
     ls.append(0, kt, vt)                                 # the verified tokens are tail tokens
     qd_ = qd(B, H * g, D, 990 + g, gain=2.0)
     qv_ = qv(B, mt, H * g, D, 991 + g)
