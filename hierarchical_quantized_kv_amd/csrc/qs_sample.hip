@@ -75,8 +75,42 @@ __device__ __forceinline__ RowStat merge(RowStat a, RowStat b) {
   return RowStat{m, a.s * expf(a.m - m) + b.s * expf(b.m - m)};
 }
 
+// The kPartPer logits of this thread in part `part` of a row (-inf past V), in one of two orders
+// (the row statistics and the part totals do not depend on it): with vec, 16-byte loads, thread
+// t holding tokens 4 (t + 256 k) + e; else tokens t + 256 k.  vec needs a 16-byte aligned row
+// and V a multiple of 4 (then 4 (t + 256 k) < V implies the three tokens after it are too).
+__device__ __forceinline__ bool vec_ok(const float* row, int V) {
+  return (V & 3) == 0 && ((uintptr_t)row & 15) == 0;
+}
+__device__ __forceinline__ void load_part_any(const float* row, int V, int part, bool vec,
+                                              float (&x)[kPartPer]) {
+  const int base = part * kPartTokens;
+  if (vec) {
+    const float4* r4 = reinterpret_cast<const float4*>(row + base);
+    float4 q[kPartPer / 4];
+#pragma unroll
+    for (int k = 0; k < kPartPer / 4; ++k) {
+      const int i = k * kPartThreads + (int)threadIdx.x;
+      q[k] = base + 4 * i < V ? r4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int k = 0; k < kPartPer / 4; ++k) {
+      x[4 * k] = q[k].x;
+      x[4 * k + 1] = q[k].y;
+      x[4 * k + 2] = q[k].z;
+      x[4 * k + 3] = q[k].w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPartPer; ++k) {
+      const int v = base + k * kPartThreads + (int)threadIdx.x;
+      x[k] = v < V ? row[v] : -INFINITY;
+    }
+  }
+}
+
 // grid: x = row (0 .. gamma: target rows, gamma+1 .. 2 gamma: draft rows), y = part, z = sequence.
-// Coalesced: thread t reads tokens t, t + kPartThreads, ... of its part, all loads first.
+// Coalesced, all loads first.  The sums use the hardware exp2 (a few ulp per term).
 __global__ __launch_bounds__(kPartThreads) void row_stats_kernel(const float* __restrict__ t,
                                                                  const float* __restrict__ d,
                                                                  int gamma, int V, float* ws) {
@@ -84,20 +118,16 @@ __global__ __launch_bounds__(kPartThreads) void row_stats_kernel(const float* __
   const int r = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
   const float* row = r <= gamma ? t + ((size_t)b * (gamma + 1) + r) * V
                                 : d + ((size_t)b * gamma + (r - gamma - 1)) * V;
-  const int v0 = part * kPartTokens + (int)threadIdx.x;
   float x[kPartPer];
-#pragma unroll
-  for (int k = 0; k < kPartPer; ++k) {
-    const int v = v0 + k * kPartThreads;
-    x[k] = v < V ? row[v] : -INFINITY;
-  }
+  load_part_any(row, V, part, vec_ok(row, V), x);
   float m = x[0];
 #pragma unroll
   for (int k = 1; k < kPartPer; ++k) m = fmaxf(m, x[k]);
   float sum = 0.f;
   if (m != -INFINITY) {
 #pragma unroll
-    for (int k = 0; k < kPartPer; ++k) sum += expf(x[k] - m);
+    for (int k = 0; k < kPartPer; ++k)
+      sum += __builtin_amdgcn_exp2f((x[k] - m) * 1.4426950408889634f);
   }
   RowStat st{m, sum};
   for (int o = 32; o > 0; o >>= 1)
@@ -264,15 +294,18 @@ __global__ __launch_bounds__(kPartThreads) void part_sums_kernel(const float* __
       ws[L.ratio + (size_t)b * gamma + j] = acc;
     }
   }
-  float wp[kPartPer], wr[kPartPer];
-  part_weights(trow, drow, pst, qst, V, part, wp, wr);
-  // the part's totals, in any order: the sampler only uses them to pick a part and the point's
-  // fraction of it
+  // the part's totals, in any order (the sampler only uses them to pick a part and the point's
+  // fraction of it): both rows in the same token order
+  const bool vec = vec_ok(trow, V) && (!drow || vec_ok(drow, V));
+  float xt[kPartPer], xd[kPartPer];
+  load_part_any(trow, V, part, vec, xt);
+  if (drow) load_part_any(drow, V, part, vec, xd);
   float sr = 0.f, sp = 0.f;
 #pragma unroll
   for (int k = 0; k < kPartPer; ++k) {
-    sr += wr[k];
-    sp += wp[k];
+    const float p = prob_fast(xt[k], pst);
+    sp += p;
+    sr += drow ? fmaxf(0.f, p - prob_fast(xd[k], qst)) : p;
   }
   for (int o = 32; o > 0; o >>= 1) {
     sr += __shfl_xor(sr, o);
