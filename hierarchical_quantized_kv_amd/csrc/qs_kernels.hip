@@ -1183,19 +1183,19 @@ __device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* k
   constexpr int G = kGroup;
   const int lane = threadIdx.x;
   const uint16_t* src = ksrc + c0;
-  // lane holds tokens 2 lane, 2 lane + 1: 32 channels each
-  uint32_t w[2][kFlushSlice / 2];
+  // the slice's 64-byte row segments, four lanes per row (16 bytes each, contiguous), 16 rows
+  // per load instruction; staged token-major in LDS
+  {
+    const int sub = lane & 3, rr = lane >> 2;
+    uint4 v[G / 16];
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+    for (int k = 0; k < G / 16; ++k) v[k] = ld16(src + (size_t)(16 * k + rr) * stride + 8 * sub);
 #pragma unroll
-    for (int k = 0; k < kFlushSlice / 8; ++k) {
-      const uint4 v = ld16(src + (size_t)(2 * lane + r) * stride + 8 * k);
-      w[r][4 * k] = v.x; w[r][4 * k + 1] = v.y; w[r][4 * k + 2] = v.z; w[r][4 * k + 3] = v.w;
+    for (int k = 0; k < G / 16; ++k) {  // 4-byte stores: the padded rows are not 16-byte aligned
+      uint32_t* t = &L.tile[16 * k + rr][4 * sub];
+      t[0] = v[k].x; t[1] = v[k].y; t[2] = v[k].z; t[3] = v[k].w;
     }
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int k = 0; k < kFlushSlice / 2; ++k) L.tile[2 * lane + r][k] = w[r][k];
+  }
   __syncthreads();
   {  // min / max of channel pair cp over the tokens q, q + 4, .. (quarter q), then the quarters
     const int cp = lane & 15, q = lane >> 4;
@@ -1225,6 +1225,11 @@ __device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* k
   // channel c0 + 2j in bits 0-3 and c0 + 2j + 1 in bits 4-7
   uint8_t* uk = a.uk + (lbh * a.T + (size_t)grp * G) * (D / 2) + c0 / 2;
   uint8_t* lk = a.lk + (lbh * a.T + (size_t)grp * G) * (D / 2) + c0 / 2;
+  uint32_t w[2][kFlushSlice / 2];  // this lane's tokens 2 lane, 2 lane + 1, from the tile
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int k = 0; k < kFlushSlice / 2; ++k) w[r][k] = L.tile[2 * lane + r][k];
   uint32_t u[2][4] = {}, l[2][4] = {};
 #pragma unroll
   for (int k = 0; k < kFlushSlice / 2; ++k) {  // channel pair k: its (s, y, z) serve both tokens
