@@ -1260,12 +1260,14 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
 #pragma clang fp contract(off)
   constexpr int G = kGroup, HALF = D / 2;
   const int lane = threadIdx.x;
-  const int tk = lane >> 1, hf = lane & 1;  // token t0 + tk, channels hf*D/2 ..
-  const uint16_t* src = vsrc + (size_t)(t0 + tk) * stride + hf * HALF;
+  // token t0 + tk; lane hf of the pair takes the 16-byte chunks 2k + hf of the row, so each load
+  // instruction reads 32 contiguous bytes of every row
+  const int tk = lane >> 1, hf = lane & 1;
+  const uint16_t* src = vsrc + (size_t)(t0 + tk) * stride;
   uint32_t w[HALF / 2];
 #pragma unroll
   for (int k = 0; k < HALF / 8; ++k) {
-    const uint4 v = ld16(src + 8 * k);
+    const uint4 v = ld16(src + 8 * (2 * k + hf));
     w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
   }
   float mn = INFINITY, mx = -INFINITY;
@@ -1285,9 +1287,10 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
     *reinterpret_cast<float2*>(vm) = make_float2(s, z);
   }
 #pragma unroll
-  for (int k = 0; k < HALF / 2; ++k) {
+  for (int k = 0; k < HALF / 2; ++k) {  // word k: channels 8 (2 (k / 4) + hf) + 2 (k % 4), +1
     const uint32_t c_lo = quant_code(lo_h(w[k]), s, y, z), c_hi = quant_code(hi_h(w[k]), s, y, z);
-    *reinterpret_cast<uint16_t*>(&L.code[tk][hf * HALF + 2 * k]) = (uint16_t)(c_lo | (c_hi << 8));
+    const int ch = 8 * (2 * (k >> 2) + hf) + 2 * (k & 3);
+    *reinterpret_cast<uint16_t*>(&L.code[tk][ch]) = (uint16_t)(c_lo | (c_hi << 8));
   }
   __syncthreads();
   // value planes: half e of the group, channel-major rows of G/4 bytes; byte j of a row holds
