@@ -634,7 +634,7 @@ def write_traffic_summary(fetch_dir, write_dir, args):
         f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
         f"\"attn_kernel|combine_kernel|flush_kernel|prefill_kernel|copy\" -d {fetch_dir} -o run "
         f"--output-format csv -- python -u bench.py --config {args.config} --layers 2 --steps 1 "
-        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --no-graph --calibration-copy-mib "
+        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --no-graph --no-gqa --calibration-copy-mib "
         f"{args.calibration_copy_mib}",
         f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE (same arguments, -d {write_dir})",
         f"python bench.py --config {args.config} --calibration-copy-mib "
