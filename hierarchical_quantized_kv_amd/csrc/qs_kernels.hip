@@ -1166,90 +1166,82 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float y, float 
 // channels, each reading 8 KB of fp16 and writing its slice of both planes and its metadata.
 constexpr int kFlushSlice = 32;
 
-struct FlushKeyLds {
-  uint32_t tile[kGroup][kFlushSlice / 2 + 1];  // fp16 pairs, token-major (padded rows)
-  float sz[kFlushSlice][3];  // s, z, 1 / s
-};
 struct FlushValLds {
   uint8_t code[kFlushSlice][128 + 4];          // codes, token-major (padded rows)
 };
 
 // Key block: channels c0 .. c0+31 of the G fp16 key rows at ksrc (token t at ksrc + t * stride),
-// into group grp of the quantized tier of (layer, sequence, head) lbh.
+// into group grp of the quantized tier of (layer, sequence, head) lbh.  Lane (rr, sub) = (lane /
+// 4, lane % 4) holds channels c0 + 8 sub .. + 7 of tokens rr, rr + 16, .. (four lanes read a
+// row's 64 bytes, 16 rows per load instruction).  A channel's min / max over the G tokens is
+// reduced over the lane's 8 tokens and then over the 16 lanes of the same sub; each lane then
+// quantizes its 8 channels of its 8 tokens and writes their 4 bytes of each token's plane rows.
+// No LDS.
 template <int D, class Args>
 __device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* ksrc, size_t stride,
-                           int c0, FlushKeyLds& L) {
+                           int c0) {
 #pragma clang fp contract(off)
-  constexpr int G = kGroup;
-  const int lane = threadIdx.x;
-  const uint16_t* src = ksrc + c0;
-  // the slice's 64-byte row segments, four lanes per row (16 bytes each, contiguous), 16 rows
-  // per load instruction; staged token-major in LDS
-  {
-    const int sub = lane & 3, rr = lane >> 2;
-    uint4 v[G / 16];
+  constexpr int G = kGroup, NR = G / 16;
+  const int lane = threadIdx.x, sub = lane & 3, rr = lane >> 2;
+  const uint16_t* src = ksrc + c0 + 8 * sub;
+  uint4 v[NR];
 #pragma unroll
-    for (int k = 0; k < G / 16; ++k) v[k] = ld16(src + (size_t)(16 * k + rr) * stride + 8 * sub);
+  for (int k = 0; k < NR; ++k) v[k] = ld16(src + (size_t)(16 * k + rr) * stride);
+  // channel e of the lane's 8 (c0 + 8 sub + e): half (e & 1) of word e / 2
+  auto word = [&](int k, int wi) {
+    return wi == 0 ? v[k].x : wi == 1 ? v[k].y : wi == 2 ? v[k].z : v[k].w;
+  };
+  float mn[8], mx[8];
 #pragma unroll
-    for (int k = 0; k < G / 16; ++k) {  // 4-byte stores: the padded rows are not 16-byte aligned
-      uint32_t* t = &L.tile[16 * k + rr][4 * sub];
-      t[0] = v[k].x; t[1] = v[k].y; t[2] = v[k].z; t[3] = v[k].w;
-    }
-  }
-  __syncthreads();
-  {  // min / max of channel pair cp over the tokens q, q + 4, .. (quarter q), then the quarters
-    const int cp = lane & 15, q = lane >> 4;
-    float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
-    for (int t = q; t < G; t += 4) {
-      const uint32_t x = L.tile[t][cp];
-      const float x0 = lo_h(x), x1 = hi_h(x);
-      mn0 = fminf(mn0, x0); mx0 = fmaxf(mx0, x0);
-      mn1 = fminf(mn1, x1); mx1 = fmaxf(mx1, x1);
-    }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-      mn0 = fminf(mn0, __shfl_xor(mn0, o)); mx0 = fmaxf(mx0, __shfl_xor(mx0, o));
-      mn1 = fminf(mn1, __shfl_xor(mn1, o)); mx1 = fmaxf(mx1, __shfl_xor(mx1, o));
-    }
-    if (q == 0) {
-      const float s0 = quant_scale(mn0, mx0), s1 = quant_scale(mn1, mx1);
-      const float z0 = rintf(-mn0 / s0), z1 = rintf(-mn1 / s1);
-      L.sz[2 * cp][0] = s0; L.sz[2 * cp][1] = z0; L.sz[2 * cp][2] = 1.0f / s0;
-      L.sz[2 * cp + 1][0] = s1; L.sz[2 * cp + 1][1] = z1; L.sz[2 * cp + 1][2] = 1.0f / s1;
-      float* km = a.kmeta + ((lbh * a.NG + grp) * D + c0 + 2 * cp) * 2;
-      *reinterpret_cast<float4*>(km) = make_float4(s0, z0, s1, z1);
-    }
-  }
-  __syncthreads();
-  // codes of this lane's two tokens; key plane rows are token-major, byte j of the slice holds
-  // channel c0 + 2j in bits 0-3 and c0 + 2j + 1 in bits 4-7
-  uint8_t* uk = a.uk + (lbh * a.T + (size_t)grp * G) * (D / 2) + c0 / 2;
-  uint8_t* lk = a.lk + (lbh * a.T + (size_t)grp * G) * (D / 2) + c0 / 2;
-  uint32_t w[2][kFlushSlice / 2];  // this lane's tokens 2 lane, 2 lane + 1, from the tile
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int k = 0; k < kFlushSlice / 2; ++k) w[r][k] = L.tile[2 * lane + r][k];
-  uint32_t u[2][4] = {}, l[2][4] = {};
-#pragma unroll
-  for (int k = 0; k < kFlushSlice / 2; ++k) {  // channel pair k: its (s, y, z) serve both tokens
-    const int ch = 2 * k;
-    const float s_lo = L.sz[ch][0], z_lo = L.sz[ch][1], y_lo = L.sz[ch][2];
-    const float s_hi = L.sz[ch + 1][0], z_hi = L.sz[ch + 1][1], y_hi = L.sz[ch + 1][2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const uint32_t c_lo = quant_code(lo_h(w[r][k]), s_lo, y_lo, z_lo);
-      const uint32_t c_hi = quant_code(hi_h(w[r][k]), s_hi, y_hi, z_hi);
-      const int sh = 8 * (k & 3);
-      u[r][k >> 2] |= ((c_lo >> 4) | ((c_hi >> 4) << 4)) << sh;
-      l[r][k >> 2] |= ((c_lo & 15u) | ((c_hi & 15u) << 4)) << sh;
-    }
+  for (int wi = 0; wi < 4; ++wi) {
+    mn[2 * wi] = mx[2 * wi] = lo_h(word(0, wi));
+    mn[2 * wi + 1] = mx[2 * wi + 1] = hi_h(word(0, wi));
   }
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const size_t o = (size_t)(2 * lane + r) * (D / 2);
-    *reinterpret_cast<uint4*>(uk + o) = make_uint4(u[r][0], u[r][1], u[r][2], u[r][3]);
-    *reinterpret_cast<uint4*>(lk + o) = make_uint4(l[r][0], l[r][1], l[r][2], l[r][3]);
+  for (int k = 1; k < NR; ++k)
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      const float x0 = lo_h(word(k, wi)), x1 = hi_h(word(k, wi));
+      mn[2 * wi] = fminf(mn[2 * wi], x0); mx[2 * wi] = fmaxf(mx[2 * wi], x0);
+      mn[2 * wi + 1] = fminf(mn[2 * wi + 1], x1); mx[2 * wi + 1] = fmaxf(mx[2 * wi + 1], x1);
+    }
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = fminf(mn[e], __shfl_xor(mn[e], o));
+      mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], o));
+    }
+  float sc[8], zc[8], yc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sc[e] = quant_scale(mn[e], mx[e]);
+    zc[e] = rintf(-mn[e] / sc[e]);
+    yc[e] = 1.0f / sc[e];
+  }
+  if (rr == 0) {  // (s, z) of the 8 channels: 64 contiguous bytes
+    float4* km = reinterpret_cast<float4*>(a.kmeta + ((lbh * a.NG + grp) * D + c0 + 8 * sub) * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      km[j] = make_float4(sc[2 * j], zc[2 * j], sc[2 * j + 1], zc[2 * j + 1]);
+  }
+  // key plane rows are token-major, byte j of a row holds channel 2j in bits 0-3 and 2j + 1 in
+  // bits 4-7: this lane's channels are bytes (c0 + 8 sub) / 2 .. + 3 of each row
+  const size_t row0 = (lbh * a.T + (size_t)grp * G) * (D / 2) + (c0 + 8 * sub) / 2;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    uint32_t u = 0, l = 0;
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      const uint32_t c_lo = quant_code(lo_h(word(k, wi)), sc[2 * wi], yc[2 * wi], zc[2 * wi]);
+      const uint32_t c_hi =
+          quant_code(hi_h(word(k, wi)), sc[2 * wi + 1], yc[2 * wi + 1], zc[2 * wi + 1]);
+      u |= ((c_lo >> 4) | ((c_hi >> 4) << 4)) << (8 * wi);
+      l |= ((c_lo & 15u) | ((c_hi & 15u) << 4)) << (8 * wi);
+    }
+    const size_t o = row0 + (size_t)(16 * k + rr) * (D / 2);
+    *reinterpret_cast<uint32_t*>(a.uk + o) = u;
+    *reinterpret_cast<uint32_t*>(a.lk + o) = l;
   }
 }
 
@@ -1317,10 +1309,7 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
 template <int D>
 __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
   constexpr int NK = D / kFlushSlice, NV = kGroup / kFlushSlice;
-  __shared__ union {
-    FlushKeyLds k;
-    FlushValLds v;
-  } lds;
+  __shared__ FlushValLds lds;  // the value blocks' code tile (key blocks use no LDS)
   // XCD-contiguous numbering: the NK + NV blocks of one (layer, sequence, head) write parts of
   // the same plane lines, so they run on one XCD and its L2 merges the parts into whole lines
   // before they reach HBM (blocks of one half spread over several XCDs made partial-line
@@ -1343,9 +1332,9 @@ __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
   }
   const size_t ring0 = (lbh * (2 * kGroup) + head) * D;  // oldest ring half, token-major
   if (blk < NK)
-    flush_keys<D>(a, lbh, group, a.tail_k + ring0, D, blk * kFlushSlice, lds.k);
+    flush_keys<D>(a, lbh, group, a.tail_k + ring0, D, blk * kFlushSlice);
   else
-    flush_values<D>(a, lbh, group, a.tail_v + ring0, D, (blk - NK) * kFlushSlice, lds.v);
+    flush_values<D>(a, lbh, group, a.tail_v + ring0, D, (blk - NK) * kFlushSlice, lds);
 }
 
 // Prefill: group g of sequence b's prompt (tokens g*G .. g*G+G-1 of k / v [B][n_max][H][D]) into
@@ -1354,10 +1343,7 @@ __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
 template <int D>
 __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
   constexpr int NK = D / kFlushSlice, NV = kGroup / kFlushSlice;
-  __shared__ union {
-    FlushKeyLds k;
-    FlushValLds v;
-  } lds;
+  __shared__ FlushValLds lds;  // the value blocks' code tile (key blocks use no LDS)
   const int n = gridDim.x * gridDim.y * gridDim.z;
   const int lb = xcd_contiguous_block((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, n);
   const int bx = lb % gridDim.x, g = (lb / gridDim.x) % gridDim.y, b = lb / (gridDim.x * gridDim.y);
@@ -1368,9 +1354,9 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
   const size_t stride = (size_t)a.H * D;
   const size_t src0 = (((size_t)b * a.n_max + (size_t)g * kGroup) * a.H + h) * D;
   if (blk < NK)
-    flush_keys<D>(a, lbh, a.group0[b] + g, a.k + src0, stride, blk * kFlushSlice, lds.k);
+    flush_keys<D>(a, lbh, a.group0[b] + g, a.k + src0, stride, blk * kFlushSlice);
   else
-    flush_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, (blk - NK) * kFlushSlice, lds.v);
+    flush_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, (blk - NK) * kFlushSlice, lds);
 }
 
 // ------------------------------------------------------------------------------------------
