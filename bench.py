@@ -118,7 +118,7 @@ def main():
         write_traffic_summary(*args.traffic_summary, args)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(got --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
