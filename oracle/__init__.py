@@ -51,7 +51,15 @@ def lib():
         L.orc_dequant_full.restype = ctypes.c_double
         L.orc_dequant_upper.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float, i]
         L.orc_dequant_upper.restype = ctypes.c_double
-        L.orc_create.argtypes = [i, i, i, i, i, i, i, i]
+        L.orc_float_to_half.argtypes = [ctypes.c_float]
+        L.orc_float_to_half.restype = ctypes.c_uint16
+        L.orc_meta16.argtypes = [ctypes.c_float, ctypes.c_float, P, P]
+        L.orc_meta16.restype = None
+        L.orc_dequant16_full.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float]
+        L.orc_dequant16_full.restype = ctypes.c_double
+        L.orc_dequant16_upper.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float, i]
+        L.orc_dequant16_upper.restype = ctypes.c_double
+        L.orc_create.argtypes = [i, i, i, i, i, i, i, i, i]
         L.orc_create.restype = P
         L.orc_destroy.argtypes = [P]
         L.orc_destroy.restype = None
@@ -120,6 +128,26 @@ def dequant_upper(cu: int, s: float, z: float, off: int) -> float:
     return lib().orc_dequant_upper(int(cu), float(s), float(z), int(off))
 
 
+def float_to_half(x: float) -> int:
+    """Bits of the binary16 nearest to the fp32 value x (ties to even)."""
+    return int(lib().orc_float_to_half(float(x)))
+
+
+def meta16(s: float, z: float):
+    """fp16 metadata (scale, offset) of fp32 (s, z), as floats."""
+    a, b = ctypes.c_float(), ctypes.c_float()
+    lib().orc_meta16(float(s), float(z), ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def dequant16_full(c8: int, s: float, b: float) -> float:
+    return lib().orc_dequant16_full(int(c8), float(s), float(b))
+
+
+def dequant16_upper(cu: int, s: float, b: float, off: int) -> float:
+    return lib().orc_dequant16_upper(int(cu), float(s), float(b), int(off))
+
+
 def spec_accept(target_logits, draft_logits, draft_tokens, uniforms):
     """Speculative accept / correct in fp64 (orc_spec_accept).  Shapes: [B][gamma+1][V],
     [B][gamma][V], [B][gamma], [B][gamma+1].  Returns (n_accepted, next_token, margin)."""
@@ -144,11 +172,12 @@ class OracleCache:
     """The oracle's cache: same verbs as the C ABI, on host memory."""
 
     def __init__(self, n_layers, batch, n_heads, head_dim, group=128, max_ctx=1024,
-                 gamma_max=6, draft_offset=8):
+                 gamma_max=6, draft_offset=8, meta_fp16=False):
         self.L, self.B, self.H, self.D = n_layers, batch, n_heads, head_dim
         self.G, self.T, self.gamma_max, self.off = group, max_ctx, gamma_max, draft_offset
+        self.meta_fp16 = bool(meta_fp16)
         self._h = lib().orc_create(n_layers, batch, n_heads, head_dim, group, max_ctx, gamma_max,
-                                   draft_offset)
+                                   draft_offset, int(self.meta_fp16))
         if not self._h:
             raise OracleError(1, "create")
 

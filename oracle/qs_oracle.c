@@ -39,6 +39,32 @@ float orc_half_to_float(uint16_t h) {
   return (float)(sign ? -v : v);
 }
 
+/* fp32 -> binary16, rounded to nearest with ties to even.  |x| is located between consecutive
+ * binary16 values: below 2^-14 those are the multiples of 2^-24 (subnormals, bit pattern = the
+ * multiple), from 2^E to 2^(E+1) the multiples of 2^(E-10); the count of quanta is rounded
+ * with rint (ties to even in the default rounding mode) and a carry to 2^11 quanta moves to the
+ * next binade.  Past the largest finite value (65504) the result is infinity. */
+uint16_t orc_float_to_half(float x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return (uint16_t)(sign | 0x7e00);
+  double a = fabs((double)x);
+  if (a == 0.0) return sign;
+  int e2;
+  frexp(a, &e2);           /* a = f 2^e2, f in [0.5, 1): a in [2^(e2-1), 2^e2) */
+  int E = e2 - 1;
+  if (E < -14) {           /* subnormal range: quanta of 2^-24 (1024 of them is 2^-14) */
+    double n = rint(ldexp(a, 24));
+    return (uint16_t)(sign | (uint16_t)n);
+  }
+  double n = rint(ldexp(a, 10 - E)); /* in [1024, 2048] */
+  if (n == 2048.0) {
+    n = 1024.0;
+    ++E;
+  }
+  if (E > 15) return (uint16_t)(sign | 0x7c00);
+  return (uint16_t)(sign | ((E + 15) << 10) | ((int)n - 1024));
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* Quantizer and split                                                                       */
 /* ---------------------------------------------------------------------------------------- */
@@ -73,6 +99,28 @@ void orc_quantize_group(const uint16_t* x, int n, int stride, float* s_out, floa
   *z_out = z;
 }
 
+/* The fp16 metadata format (a variant of the fp32 (scale, zero-point) pair of [G]'s quantizer,
+ * which stores both in the input's dtype): from the fp32 s and z of a group, s and the offset
+ * b = -(s z) -- the fp32 product, clamped to the finite half range -- each rounded to fp16.  A
+ * code C then stands for s C + b = s (C - z) up to the roundings; a degenerate group (s clamped
+ * to 1e-8, which rounds to 0) keeps its value in b. */
+void orc_meta16(float s, float z, float* s16, float* b16) {
+  float b = -(s * z);
+  if (b > 65504.0f) b = 65504.0f;
+  if (b < -65504.0f) b = -65504.0f;
+  *s16 = orc_half_to_float(orc_float_to_half(s));
+  *b16 = orc_half_to_float(orc_float_to_half(b));
+}
+
+/* Dequantizations with fp16 metadata (s, b), in fp64: s C8 + b (verify), s (2^4 C_U + off) + b
+ * (draft). */
+double orc_dequant16_full(uint8_t c8, float s, float b) {
+  return (double)s * (double)c8 + (double)b;
+}
+double orc_dequant16_upper(uint8_t cu, float s, float b, int off) {
+  return (double)s * (double)(16 * (int)cu + off) + (double)b;
+}
+
 /* C8 = 2^4 * C_U + C_L ([R] "What carries the argument", Fig. 3): the upper plane is the high
  * nibble and the lower "error-residual" plane the low nibble of the 8-bit code. */
 static uint8_t upper_nibble(uint8_t c8) { return (uint8_t)(c8 >> 4); }
@@ -95,6 +143,7 @@ double orc_dequant_upper(uint8_t cu, float s, float z, int off) {
 
 struct orc_cache {
   int L, B, H, D, G, T, NG, gamma_max, off;
+  int meta16;       /* 1: ks/kz, vs/vz hold the fp16 (scale, offset) pairs, as floats   */
   uint8_t* kc;      /* [L][B][H][T][D] key codes                        */
   uint8_t* vc;      /* [L][B][H][T][D] value codes                      */
   float* ks;        /* [L][B][H][NG][D] key scale per group and channel */
@@ -112,14 +161,15 @@ static size_t lbh(const orc_cache* c, int l, int b, int h) {
   return ((size_t)l * c->B + b) * c->H + h;
 }
 
-orc_cache* orc_create(int L, int B, int H, int D, int G, int T, int gamma_max, int off) {
+orc_cache* orc_create(int L, int B, int H, int D, int G, int T, int gamma_max, int off,
+                      int meta16) {
   if (L < 1 || B < 1 || H < 1 || D < 2 || (D & 1) || G < 2 || (G & 1) || T < G || T % G ||
-      gamma_max < 0 || gamma_max + 1 > G)
+      gamma_max < 0 || gamma_max + 1 > G || (meta16 != 0 && meta16 != 1))
     return NULL;
   orc_cache* c = (orc_cache*)calloc(1, sizeof(orc_cache));
   if (!c) return NULL;
   c->L = L; c->B = B; c->H = H; c->D = D; c->G = G; c->T = T; c->NG = T / G;
-  c->gamma_max = gamma_max; c->off = off;
+  c->gamma_max = gamma_max; c->off = off; c->meta16 = meta16;
   size_t nbh = (size_t)L * B * H;
   c->kc = (uint8_t*)calloc(nbh * T * D, 1);
   c->vc = (uint8_t*)calloc(nbh * T * D, 1);
@@ -219,6 +269,16 @@ static void flush_one(orc_cache* c, int l, int b) {
     for (int t = 0; t < G; ++t) /* value group: token t over channels 0 .. D-1 */
       orc_quantize_group(&tv[(size_t)t * D], D, 1, &c->vs[r * c->T + t0 + t],
                          &c->vz[r * c->T + t0 + t], &vc[(size_t)t * D], 1);
+    if (c->meta16) { /* the codes stay; the stored pairs become fp16 (scale, offset) */
+      for (int d = 0; d < D; ++d) {
+        float* ps = &c->ks[(r * c->NG + g) * D + d];
+        float* pz = &c->kz[(r * c->NG + g) * D + d];
+        orc_meta16(*ps, *pz, ps, pz);
+      }
+      for (int t = 0; t < G; ++t)
+        orc_meta16(c->vs[r * c->T + t0 + t], c->vz[r * c->T + t0 + t], &c->vs[r * c->T + t0 + t],
+                   &c->vz[r * c->T + t0 + t]);
+    }
   }
   c->nq[l * c->B + b] += G;
   c->nt[l * c->B + b] -= G;
@@ -273,6 +333,13 @@ int orc_flush(orc_cache* c, int layer, int min_tail, int* flushed) {
 /* Attention                                                                                 */
 /* ---------------------------------------------------------------------------------------- */
 
+/* Dequantized code in the cache's metadata format: draft from the upper plane, else both. */
+static double dequant(const orc_cache* c, uint8_t c8, float s, float x, int draft) {
+  if (c->meta16)
+    return draft ? orc_dequant16_upper(upper_nibble(c8), s, x, c->off) : orc_dequant16_full(c8, s, x);
+  return draft ? orc_dequant_upper(upper_nibble(c8), s, x, c->off) : orc_dequant_full(c8, s, x);
+}
+
 /* One query row of one (l, b, h): plain softmax attention in fp64 over the concatenation of
  *   - the nq quantized tokens, dequantized with the draft (upper plane) or verify (both planes)
  *     formula, and
@@ -294,9 +361,7 @@ static void attend_row(const orc_cache* c, int l, int b, int h, const uint16_t* 
     double dot = 0.0;
     for (int d = 0; d < D; ++d) {
       float s = c->ks[(r * c->NG + g) * D + d], z = c->kz[(r * c->NG + g) * D + d];
-      double kd = draft ? orc_dequant_upper(upper_nibble(kc[d]), s, z, c->off)
-                        : orc_dequant_full(kc[d], s, z);
-      dot += qd[d] * kd;
+      dot += qd[d] * dequant(c, kc[d], s, z, draft);
     }
     score[t] = sm_scale * dot;
   }
@@ -317,11 +382,7 @@ static void attend_row(const orc_cache* c, int l, int b, int h, const uint16_t* 
     const double p = exp(score[t] - mx);
     const uint8_t* vc = &c->vc[(r * c->T + t) * D];
     const float s = c->vs[r * c->T + t], z = c->vz[r * c->T + t];
-    for (int d = 0; d < D; ++d) {
-      double vd = draft ? orc_dequant_upper(upper_nibble(vc[d]), s, z, c->off)
-                        : orc_dequant_full(vc[d], s, z);
-      acc[d] += p * vd;
-    }
+    for (int d = 0; d < D; ++d) acc[d] += p * dequant(c, vc[d], s, z, draft);
   }
   for (int j = 0; j < n_vis; ++j) {
     const double p = exp(score[nq + j] - mx);

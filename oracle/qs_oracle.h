@@ -43,11 +43,22 @@ void orc_quantize_group(const uint16_t* x, int n, int stride, float* s, float* z
 double orc_dequant_full(uint8_t c8, float s, float z);
 double orc_dequant_upper(uint8_t cu, float s, float z, int off);
 
+/* fp32 -> binary16 bits, round to nearest even (overflow to infinity). */
+uint16_t orc_float_to_half(float x);
+/* fp16 metadata of a group with fp32 scale s and zero-point z: the fp16 values (as floats) of
+ * s and of the offset b = -(s z) clamped to +-65504. */
+void orc_meta16(float s, float z, float* s16, float* b16);
+/* Dequantizations with fp16 metadata (s, b), in fp64: s C8 + b and s (16 C_U + off) + b. */
+double orc_dequant16_full(uint8_t c8, float s, float b);
+double orc_dequant16_upper(uint8_t cu, float s, float b, int off);
+
 typedef struct orc_cache orc_cache;
 
 /* L layers, B sequences, H heads, head_dim D, group G, quantized capacity T (multiple of G),
- * gamma_max, draft offset off.  Returns NULL on invalid arguments or allocation failure. */
-orc_cache* orc_create(int L, int B, int H, int D, int G, int T, int gamma_max, int off);
+ * gamma_max, draft offset off, metadata format (0: fp32 (s, z); 1: fp16 (s, b)).  Returns NULL
+ * on invalid arguments or allocation failure. */
+orc_cache* orc_create(int L, int B, int H, int D, int G, int T, int gamma_max, int off,
+                      int meta16);
 void orc_destroy(orc_cache* c);
 
 /* k, v: fp16 bits [B][n_max][H][D]; n: [B] or NULL (= n_max). */
@@ -77,7 +88,7 @@ int orc_get_state(const orc_cache* c, int layer, int* nq, int* nt, int* head);
 
 /* Logical read-back for one (layer, b, h):
  *   codes  [T][D]   8-bit codes of the quantized tokens (rows >= nq are zero)
- *   kmeta  [T/G][D][2] key (s, z);  vmeta [T][2] value (s, z). */
+ *   kmeta  [T/G][D][2] key (s, z);  vmeta [T][2] value (s, z)  (fp16 format: (s, b)). */
 int orc_read_codes(const orc_cache* c, int layer, int b, int h, int which_v, uint8_t* codes);
 /* Test support: every stored code of `layer` gets lower nibble `value` (0..15). */
 int orc_set_lower_nibbles(orc_cache* c, int layer, int value);

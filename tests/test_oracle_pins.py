@@ -229,14 +229,15 @@ def test_grid_exact_cache_verify_equals_unquantized_and_draft_equals_upper_formu
         assert np.max(np.abs(draft[0, h] - refd)) < 1e-6
 
 
-@pytest.mark.parametrize("off,nibble", [(8, 8), (0, 0)])
-def test_draft_equals_verify_when_every_lower_nibble_is_the_draft_offset(off, nibble):
+@pytest.mark.parametrize("off,nibble,m16", [(8, 8, False), (0, 0, False), (8, 8, True),
+                                            (0, 0, True)])
+def test_draft_equals_verify_when_every_lower_nibble_is_the_draft_offset(off, nibble, m16):
     """The draft reconstruction (16 C_U + off - z) s is the full one (C8 - z) s of a code whose
-    lower nibble is off: after setting every stored lower nibble to off, a one-query verify
-    (which sees the whole tail) equals the draft, exactly.  A wrong shift, nibble or offset in
-    either dequantization fails it."""
+    lower nibble is off (with fp16 metadata: s (16 C_U + off) + b and s C8 + b): after setting
+    every stored lower nibble to off, a one-query verify (which sees the whole tail) equals the
+    draft, exactly.  A wrong shift, nibble or offset in either dequantization fails it."""
     H, D = 3, 64
-    c = OracleCache(1, 2, H, D, G, 4 * G, 4, draft_offset=off)
+    c = OracleCache(1, 2, H, D, G, 4 * G, 4, draft_offset=off, meta_fp16=m16)
     k, v = synth.kv_host(2, 2 * G + 50, H, D, 41, 42)
     c.prefill(0, k, v, n=[2 * G + 50, G + 7])
     q = synth.queries_host(2, None, H, D, 43, gain=2.0)
@@ -585,3 +586,138 @@ def test_spec_accept_closed_forms():
     x2[0, 2] = V
     n, _, _ = oracle.spec_accept(t, d, x2, np.array([[0.5] * gamma + [0.1]], np.float32))
     assert n[0] == 2
+
+
+# ------------------------------------------------------------------------------------------
+# fp16 metadata (scale s, offset b = -s z)
+# ------------------------------------------------------------------------------------------
+
+def np_half_bits(x):
+    with np.errstate(over="ignore"):
+        return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def test_float_to_half_matches_numpy():
+    """Round to nearest even against numpy's fp32 -> fp16 conversion: every finite half, the
+    midpoints between neighbours (exact ties), points just off them, subnormals, overflow."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    fin = h[np.isfinite(h)].astype(np.float64)
+    pos = np.unique(np.abs(fin))
+    mids = (pos[:-1] + pos[1:]) / 2                       # exact in fp32 (12 significant bits)
+    xs = [fin, mids, -mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+          np.nextafter(mids.astype(np.float32), np.float32(0)),
+          np.random.default_rng(7).standard_normal(20000) * 10.0 ** np.random.default_rng(8).uniform(-9, 5, 20000),
+          np.array([65504.0, 65519.0, 65520.0, 7e4, -7e4, 1e-8, 2.9e-8, 3.0e-8, 2.0 ** -25, 2.0 ** -24])]
+    x = np.concatenate([np.asarray(a, np.float64) for a in xs]).astype(np.float32)
+    got = np.array([oracle.float_to_half(float(v)) for v in x], dtype=np.uint16)
+    assert np.array_equal(got, np_half_bits(x))
+
+
+def _pair_caches(rng_seed, H=3, D=64, groups=3, m16_only=False):
+    k, v = synth.kv_host(1, groups * G, H, D, rng_seed, rng_seed + 1,
+                         outliers=synth.outlier_channels(H, D, rng_seed + 2))
+    caches = []
+    for m16 in (False, True):
+        c = OracleCache(1, 1, H, D, G, groups * G, 4, meta_fp16=m16)
+        c.prefill(0, k, v)
+        caches.append(c)
+    return k, v, caches
+
+
+def test_meta16_pairs_are_the_fp16_values_of_scale_and_offset():
+    """Same input, both formats: identical codes; the fp16 pairs are numpy's fp16 of the fp32
+    cache's s and of -(s z) (fp32 product, clamped to +-65504)."""
+    H, D = 3, 64
+    _, _, (c32, c16) = _pair_caches(51, H, D)
+    for h in range(H):
+        for which in (False, True):
+            assert np.array_equal(c32.codes(0, 0, h, which), c16.codes(0, 0, h, which))
+        for m32, m16 in zip(c32.meta(0, 0, h), c16.meta(0, 0, h)):
+            s, z = m32[..., 0], m32[..., 1]
+            b = np.clip(-(s * z), np.float32(-65504), np.float32(65504))
+            assert b.dtype == np.float32
+            assert np.array_equal(m16[..., 0], s.astype(np.float16).astype(np.float32))
+            assert np.array_equal(m16[..., 1], b.astype(np.float16).astype(np.float32))
+
+
+def test_meta16_dequantization_within_rounding_bound():
+    """|(s C + b)_fp16 - (C - z) s| <= C |s16 - s| + |b16 - b| + |b - (-s z)| with each fp16
+    rounding at most half an ulp (2^-11 relative, 2^-25 absolute below the normal range) and
+    the fp32 product at most 2^-24 relative."""
+    H, D = 3, 64
+    _, _, (c32, c16) = _pair_caches(61, H, D)
+    for h in range(H):
+        for which in (False, True):
+            codes = c32.codes(0, 0, h, which).astype(np.float64)
+            (km32, vm32), (km16, vm16) = c32.meta(0, 0, h), c16.meta(0, 0, h)
+            m32, m16 = (vm32, vm16) if which else (km32, km16)
+            if which:
+                s, z = m32[:, 0:1], m32[:, 1:2]
+                s16, b16 = m16[:, 0:1], m16[:, 1:2]
+            else:
+                s, z = (np.repeat(m32[:, :, i], G, axis=0) for i in (0, 1))
+                s16, b16 = (np.repeat(m16[:, :, i], G, axis=0) for i in (0, 1))
+            s, z, s16, b16 = (a.astype(np.float64) for a in (s, z, s16, b16))
+            x32 = (codes - z) * s
+            x16 = s16 * codes + b16
+            for up in (False, True):
+                cc = 16 * np.floor(codes / 16) + 8 if up else codes
+                x32 = (cc - z) * s
+                x16 = s16 * cc + b16
+                b = np.abs(s * z)
+                bound = (cc * np.maximum(s * 2.0 ** -11, 2.0 ** -25) +
+                         np.maximum(b * 2.0 ** -11, 2.0 ** -25) + b * 2.0 ** -23)
+                assert np.all(np.abs(x16 - x32) <= bound)
+                assert oracle.dequant16_full(int(codes[0, 0]), s16[0, 0], b16[0, 0]) == \
+                    s16[0, 0] * codes[0, 0] + b16[0, 0]
+
+
+@pytest.mark.parametrize("val", [0.0, 1.0, -3.5, 1000.0, -65504.0, 6.0e-8, 0.0999])
+def test_meta16_constant_group_is_exact(val):
+    """A constant group has s clamped to 1e-8 (fp16: 0) and every code 0 (the value sits at
+    -z s): b is the value itself, so fp16 metadata reconstructs it exactly, both passes."""
+    H, D = 1, 64
+    x = np.full((1, G + 1, H, D), val, np.float16)   # one group and one tail token
+    c = OracleCache(1, 1, H, D, G, 2 * G, 4, meta_fp16=True)
+    c.prefill(0, x, x)
+    km, vm = c.meta(0, 0, 0)
+    km, vm = km[:1], vm[:G]                          # the quantized group
+    assert np.all(km[..., 0] == 0) and np.all(vm[:, 0] == 0)
+    assert np.all(km[..., 1] == np.float32(x[0, 0, 0, 0])) and np.all(vm[:, 1] == km[0, 0, 1])
+    q = synth.queries_host(1, None, H, D, 71)
+    ref = np.full(D, float(x[0, 0, 0, 0]), np.float32)
+    assert np.array_equal(c.attend_draft(0, q)[0, 0], ref)
+    assert np.array_equal(c.attend_verify(0, q[:, None])[0, 0, 0], ref)
+
+
+def test_meta16_attention_over_explicit_dequantized_cache():
+    """The oracle's attention with fp16 metadata equals SDPA over keys / values dequantized here
+    as s C + b (draft: s (16 floor(C / 16) + 8) + b) from the read-back codes and pairs."""
+    B, H, D = 1, 2, 64
+    k, v = synth.kv_host(B, 2 * G + 30, H, D, 81, 82, outliers=synth.outlier_channels(H, D, 83))
+    c = OracleCache(1, B, H, D, G, 4 * G, 6, meta_fp16=True)
+    c.prefill(0, k, v)
+    nq = 2 * G
+    q = synth.queries_host(B, None, H, D, 84)
+    m = 3
+    qv = synth.queries_host(B, m, H, D, 85)
+    out, outv = c.attend_draft(0, q, sm_scale=0.9), c.attend_verify(0, qv)
+    for h in range(H):
+        ck = c.codes(0, 0, h)[:nq].astype(np.float64)
+        cv = c.codes(0, 0, h, True)[:nq].astype(np.float64)
+        km, vm = c.meta(0, 0, h)
+        ks, kb = (np.repeat(km[:, :, i], G, axis=0)[:nq].astype(np.float64) for i in (0, 1))
+        vs, vb = vm[:nq, 0:1].astype(np.float64), vm[:nq, 1:2].astype(np.float64)
+        tk, tv = f64(k[0, nq:, h]), f64(v[0, nq:, h])
+        ku = ks * (16 * np.floor(ck / 16) + 8) + kb
+        vu = vs * (16 * np.floor(cv / 16) + 8) + vb
+        ref = sdpa(f64(q[0, h])[None], np.concatenate([ku, tk]), np.concatenate([vu, tv]),
+                   scale=0.9)[0]
+        assert np.max(np.abs(out[0, h] - ref)) < 1e-6
+        ka, va = np.concatenate([ks * ck + kb, tk]), np.concatenate([vs * cv + vb, tv])
+        n = len(ka)
+        mask = np.zeros((m, n), bool)
+        for i in range(m):
+            mask[i, : n - m + i + 1] = True
+        ref = sdpa(f64(qv[0, :, h]), ka, va, mask)
+        assert np.max(np.abs(outv[0, :, h] - ref)) < 1e-6
