@@ -60,15 +60,16 @@ CONFIGS = {
 }
 
 
-def draft_bytes(nq, nt, H, D):
-    """Algorithmic bytes of one draft call: upper key/value planes + fp32 (s, z) metadata of
-    every quantized token-head, the fp16 tail, the query and the fp32 output."""
-    per_tok = D // 2 + D // 2 + 8 * D // G + 8
+def draft_bytes(nq, nt, H, D, mb=8):
+    """Algorithmic bytes of one draft call: upper key/value planes + (s, z) metadata (mb bytes a
+    pair: 8 fp32, 4 fp16) of every quantized token-head, the fp16 tail, the query and the fp32
+    output."""
+    per_tok = D // 2 + D // 2 + mb * D // G + mb
     return H * (nq * per_tok + nt * 4 * D + 2 * D + 4 * D)
 
 
-def verify_bytes(nq, nt, H, D, m):
-    per_tok = D + D + 8 * D // G + 8
+def verify_bytes(nq, nt, H, D, m, mb=8):
+    per_tok = D + D + mb * D // G + mb
     return H * (nq * per_tok + nt * 4 * D + m * (2 * D + 4 * D))
 
 
@@ -100,6 +101,8 @@ def main():
                     help="separate append and attention calls instead of the fused ones")
     ap.add_argument("--no-gqa", action="store_true",
                     help="skip the grouped-query layer (gqa: null)")
+    ap.add_argument("--no-meta16", action="store_true",
+                    help="skip the fp16-metadata comparison (meta16: null)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replayed step (graph_step: null)")
     ap.add_argument("--cpu-threads", type=int, default=16,
@@ -343,6 +346,7 @@ def main():
     sa = {sb: summarize(e, f"spec_accept_batch{sb}") for sb, e in sa_ev.items()}
 
     gqa = None if args.no_gqa else measure_gqa(torch, stream, spin_cycles, dev)
+    meta16 = None if args.no_meta16 else measure_meta16(torch, stream, spin_cycles, dev)
     read_ceiling = measure_read_ceiling(torch, stream)
 
     cpu = None
@@ -408,6 +412,7 @@ def main():
             for sb, (us, gbs, nb) in sa.items()},
         "graph_step": graph_line,
         "gqa": gqa,
+        "meta16": meta16,
         "samples_dropped": dropped,
         "read_ceiling": read_ceiling,
         "cpu_baseline": cpu,
@@ -525,6 +530,60 @@ def measure_gqa(torch, stream, spin_cycles, dev, ctx=131072, Hkv=8, g=4, mt=4, r
         out[f"{name}_gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         out[f"{name}_frac"] = round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
     cache.close()
+    return out
+
+
+def measure_meta16(torch, stream, spin_cycles, dev, ctx=131072, H=32, m=7, reps=20, rounds=3):
+    """fp16 (scale, offset) metadata against fp32 (scale, zero-point) on the same layer: 32
+    heads, head_dim 128, ctx tokens quantized plus a 64 + m token tail, in two caches that differ
+    only in the metadata format.  The draft and the m-query verify are timed over `reps`
+    consecutive calls behind the spin kernel, the two formats alternating for `rounds` rounds;
+    the best round of each is reported."""
+    from hierarchical_quantized_kv_amd import synth
+    from hierarchical_quantized_kv_amd.binding import Cache
+    D, nt = 128, 64 + m
+    k, v = synth.kv_device(torch, 1, ctx + nt, H, D, 5151, 5152, dev,
+                           outliers=synth.outlier_channels(H, D, 5153))
+    gen = torch.Generator(device=dev).manual_seed(5154)
+    qd = (torch.randn((1, H, D), generator=gen, device=dev) / math.sqrt(D)).half()
+    qv = (torch.randn((1, m, H, D), generator=gen, device=dev) / math.sqrt(D)).half()
+    od = torch.empty((1, H, D), dtype=torch.float32, device=dev)
+    ov = torch.empty((1, m, H, D), dtype=torch.float32, device=dev)
+    caches = {}
+    for fmt, m16 in (("fp32", False), ("fp16", True)):
+        c = Cache(1, 1, H, D, ctx + 2 * G, 6, meta_fp16=m16)
+        c.prefill(0, k[:, :ctx + 64].contiguous(), v[:, :ctx + 64].contiguous())
+        c.append(0, k[:, ctx + 64:].contiguous(), v[:, ctx + 64:].contiguous())
+        caches[fmt] = c
+    del k, v
+    out = {"workload": f"one LWM-128k-shaped layer: {H} heads, head_dim {D}, ctx {ctx} + "
+                       f"{nt}-token tail, verify of {m} queries; fp32 vs fp16 metadata, best of "
+                       f"{rounds} alternating rounds of {reps} calls"}
+    best = {}
+    for _ in range(rounds):
+        for fmt, c in caches.items():
+            for name, fn in (("draft", lambda: c.attend_draft(0, qd, out=od)),
+                             ("verify", lambda: c.attend_verify(0, qv, out=ov))):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                torch.cuda._sleep(spin_cycles)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                best[(name, fmt)] = min(us, best.get((name, fmt), us))
+    for (name, fmt), us in sorted(best.items()):
+        mb = 4 if fmt == "fp16" else 8
+        nbytes = draft_bytes(ctx, nt, H, D, mb) if name == "draft" else verify_bytes(ctx, nt, H, D, m, mb)
+        out[f"{name}_{fmt}_us"] = round(us, 2)
+        out[f"{name}_{fmt}_bytes"] = int(nbytes)
+        out[f"{name}_{fmt}_frac"] = round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    for c in caches.values():
+        c.close()
     return out
 
 

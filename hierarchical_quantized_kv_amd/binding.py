@@ -34,7 +34,7 @@ DEV_ERR_APPEND, DEV_ERR_ROLLBACK, DEV_ERR_FLUSH, DEV_ERR_ATTEND = 1, 2, 4, 8
 class QsConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "batch", "n_heads", "head_dim", "group", "max_ctx", "gamma_max",
-        "draft_offset")]
+        "draft_offset", "meta_fp16")]
 
 
 class QsLayout(ctypes.Structure):
@@ -113,8 +113,9 @@ def _ptr_i32(arr):
 
 
 def make_config(n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group=128,
-                draft_offset=8) -> QsConfig:
-    return QsConfig(n_layers, batch, n_heads, head_dim, group, max_ctx, gamma_max, draft_offset)
+                draft_offset=8, meta_fp16=False) -> QsConfig:
+    return QsConfig(n_layers, batch, n_heads, head_dim, group, max_ctx, gamma_max, draft_offset,
+                    int(meta_fp16))
 
 
 def arena_layout(cfg: QsConfig) -> QsLayout:
@@ -129,13 +130,14 @@ class Cache:
     """A cache over a torch uint8 arena on the current device; verbs mirror the C ABI."""
 
     def __init__(self, n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group=128,
-                 draft_offset=8, device="cuda"):
+                 draft_offset=8, device="cuda", meta_fp16=False):
         import torch
         self.torch = torch
         self.cfg = make_config(n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group,
-                               draft_offset)
+                               draft_offset, meta_fp16)
         self.L, self.B, self.H, self.D = n_layers, batch, n_heads, head_dim
         self.G, self.T, self.gamma_max = group, max_ctx, gamma_max
+        self.meta_fp16 = bool(meta_fp16)
         self.layout = arena_layout(self.cfg)
         nbytes = self.layout.total
         self.arena = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -335,13 +337,14 @@ class Cache:
         B, H, T, D, G = self.B, self.H, self.T, self.D, self.G
         NG = T // G
         lay = self.layout
+        mt = torch.float16 if self.meta_fp16 else torch.float32  # (scale, offset) or (scale, zero)
         shapes = {
             "uk": (torch.uint8, lay.uk, (B, H, T, D // 2)),
             "lk": (torch.uint8, lay.lk, (B, H, T, D // 2)),
             "uv": (torch.uint8, lay.uv, (B, H, NG, 2, D, G // 4)),
             "lv": (torch.uint8, lay.lv, (B, H, NG, 2, D, G // 4)),
-            "kmeta": (torch.float32, lay.kmeta, (B, H, NG, D, 2)),
-            "vmeta": (torch.float32, lay.vmeta, (B, H, T, 2)),
+            "kmeta": (mt, lay.kmeta, (B, H, NG, D, 2)),
+            "vmeta": (mt, lay.vmeta, (B, H, T, 2)),
             "tail_k": (torch.float16, lay.tail_k, (B, H, 2 * G, D)),
             "tail_v": (torch.float16, lay.tail_v, (B, H, 2 * G, D)),
         }

@@ -30,7 +30,7 @@ hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStre
 hipError_t launch_attention_app(const AttnAppArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_attention_gqa(const AttnGqaArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_state(const StateArgs& a, hipStream_t st);
-int attention_slots(int D, bool draft, int B, int mode);
+int attention_slots(int D, bool draft, int B, int mode, bool meta16);
 }  // namespace qs
 
 struct qs_cache {
@@ -161,8 +161,9 @@ qs_status qs_prefill(qs_cache* c, int32_t layer, const void* d_k, const void* d_
   p.lk = c->arena + c->lay.lk;
   p.uv = c->arena + c->lay.uv;
   p.lv = c->arena + c->lay.lv;
-  p.kmeta = reinterpret_cast<float*>(c->arena + c->lay.kmeta);
-  p.vmeta = reinterpret_cast<float*>(c->arena + c->lay.vmeta);
+  p.kmeta = c->arena + c->lay.kmeta;
+  p.vmeta = c->arena + c->lay.vmeta;
+  p.meta16 = cf.meta_fp16;
   p.k = static_cast<const uint16_t*>(d_k);
   p.v = static_cast<const uint16_t*>(d_v);
   p.B = cf.batch;
@@ -233,8 +234,9 @@ qs_status qs_flush(qs_cache* c, int32_t layer, int32_t min_tail, void* stream, i
   a.lk = c->arena + c->lay.lk;
   a.uv = c->arena + c->lay.uv;
   a.lv = c->arena + c->lay.lv;
-  a.kmeta = reinterpret_cast<float*>(c->arena + c->lay.kmeta);
-  a.vmeta = reinterpret_cast<float*>(c->arena + c->lay.vmeta);
+  a.kmeta = c->arena + c->lay.kmeta;
+  a.vmeta = c->arena + c->lay.vmeta;
+  a.meta16 = cf.meta_fp16;
   a.tail_k = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_k);
   a.tail_v = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_v);
   a.B = cf.batch;
@@ -290,8 +292,9 @@ static void attn_args(const qs_cache* c, int32_t layer, const void* d_q, int32_t
   a.lk = c->arena + c->lay.lk + layer_off(c, T * (D / 2), layer);
   a.uv = c->arena + c->lay.uv + layer_off(c, NG * D * (G / 2), layer);
   a.lv = c->arena + c->lay.lv + layer_off(c, NG * D * (G / 2), layer);
-  a.kmeta = reinterpret_cast<const float*>(c->arena + c->lay.kmeta + layer_off(c, NG * D * 8, layer));
-  a.vmeta = reinterpret_cast<const float*>(c->arena + c->lay.vmeta + layer_off(c, T * 8, layer));
+  const size_t mb = qs::meta_bytes(cf);
+  a.kmeta = c->arena + c->lay.kmeta + layer_off(c, NG * D * mb, layer);
+  a.vmeta = c->arena + c->lay.vmeta + layer_off(c, T * mb, layer);
   a.tail_k = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_k + layer_off(c, 2 * G * D * 2, layer));
   a.tail_v = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_v + layer_off(c, 2 * G * D * 2, layer));
   a.q = static_cast<const uint16_t*>(d_q);
@@ -308,6 +311,7 @@ static void attn_args(const qs_cache* c, int32_t layer, const void* d_q, int32_t
   a.n_titems_total = p.tbase[cf.batch];
   a.qscale = sm_scale * 1.4426950408889634f;
   a.draft_offset = (float)cf.draft_offset;
+  a.meta16 = cf.meta_fp16;
   for (int b = 0; b <= cf.batch; ++b) {
     a.qitem_base[b] = p.qbase[b];
     a.titem_base[b] = p.tbase[b];
@@ -318,7 +322,7 @@ static void attn_args(const qs_cache* c, int32_t layer, const void* d_q, int32_t
 // kernel, next to the tail items.
 static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft, int mode) {
   const qs_config& cf = c->cfg;
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, mode);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, mode, cf.meta_fp16 != 0);
   if (slots <= 0) slots = kFallbackSlots;
   int tail_items = 0;
   for (int b = 0; b < cf.batch; ++b)
@@ -675,8 +679,9 @@ qs_status qs_flush_dev(qs_cache* c, int32_t layer, int32_t min_tail, void* strea
   a.lk = c->arena + c->lay.lk;
   a.uv = c->arena + c->lay.uv;
   a.lv = c->arena + c->lay.lv;
-  a.kmeta = reinterpret_cast<float*>(c->arena + c->lay.kmeta);
-  a.vmeta = reinterpret_cast<float*>(c->arena + c->lay.vmeta);
+  a.kmeta = c->arena + c->lay.kmeta;
+  a.vmeta = c->arena + c->lay.vmeta;
+  a.meta16 = cf.meta_fp16;
   a.tail_k = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_k);
   a.tail_v = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_v);
   a.B = cf.batch;
@@ -715,7 +720,7 @@ static qs_status attend_dev(qs_cache* c, int32_t layer, const void* d_q, int32_t
   // quantized workers filling the rest of one resident round (worker w takes groups w, w + W,
   // .. of whatever the sequence holds).  Tail items past nt exit at once, so they are counted
   // as half their number.  Workers and items with no work write empty records.
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, qs::kModeDev);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, qs::kModeDev, cf.meta_fp16 != 0);
   if (slots <= 0) slots = kFallbackSlots;
   const int bh = cf.batch * cf.n_heads;
   int W = (slots - bh * qs::kMaxTailItems / 2) / bh;

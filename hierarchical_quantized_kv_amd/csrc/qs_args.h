@@ -48,8 +48,8 @@ struct AttnHeader {
   const uint8_t* lk;
   const uint8_t* uv;
   const uint8_t* lv;
-  const float* kmeta;
-  const float* vmeta;
+  const uint8_t* kmeta;  // (scale, zero-point) fp32 pairs, or (scale, offset) fp16 pairs
+  const uint8_t* vmeta;
   const uint16_t* tail_k;
   const uint16_t* tail_v;
   const uint16_t* q;     // draft [B][H][D], verify [B][m][H][D]
@@ -62,6 +62,7 @@ struct AttnHeader {
   int32_t n_qitems_total, n_titems_total;
   float qscale;          // sm_scale * log2(e): scores are kept in the base-2 domain
   float draft_offset;    // 8 or 0 (draft only)
+  int32_t meta16;        // fp16 metadata (selects the kernel instantiation)
 };
 
 // Per-sequence bookkeeping for at most NB sequences.  The kernels are instantiated for a few
@@ -161,8 +162,9 @@ struct PrefillArgs {
   uint8_t* lk;
   uint8_t* uv;
   uint8_t* lv;
-  float* kmeta;
-  float* vmeta;
+  uint8_t* kmeta;        // fp32 (scale, zero-point) or, with meta16, fp16 (scale, offset)
+  uint8_t* vmeta;
+  int32_t meta16;
   const uint16_t* k;     // prompt [B][n_max][H][D]
   const uint16_t* v;
   int32_t B, H, T, NG;
@@ -176,8 +178,9 @@ struct FlushArgs {
   uint8_t* lk;
   uint8_t* uv;
   uint8_t* lv;
-  float* kmeta;
-  float* vmeta;
+  uint8_t* kmeta;        // fp32 (scale, zero-point) or, with meta16, fp16 (scale, offset)
+  uint8_t* vmeta;
+  int32_t meta16;
   const uint16_t* tail_k;
   const uint16_t* tail_v;
   int32_t B, H, T, NG;

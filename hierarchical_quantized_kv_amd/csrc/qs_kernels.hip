@@ -32,6 +32,8 @@
 // digits of q' and p'; those of verify on MFMA with fp16 operands built from the codes with the
 // magic-number trick (0x6400 | n is the fp16 value 1024 + n).  The second (bias) sums stay in
 // fp32, which keeps degenerate groups (scale clamped to 1e-8, huge zero-point) exact.
+// With fp16 metadata (scale s, offset b = -s z) a code stands for s C + b: the bias sums take
+// s (128 + off) + b and 128 s + b per token, and -q b per channel, in place of the (s, z) forms.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -92,21 +94,45 @@ __device__ __forceinline__ float4 bldf4(rsrc_t r, uint32_t voff, uint32_t soff) 
 struct Streams {
   rsrc_t uk, lk, uv, lv, km, vm;
 };
-template <class Args>
+template <bool M16, class Args>
 __device__ __forceinline__ Streams make_streams(const Args& a, size_t bh, int D) {
   const uint32_t plane = (uint32_t)a.T * (uint32_t)(D / 2);  // bytes of one plane per (b, h)
+  constexpr uint32_t mb = M16 ? 4 : 8;                       // bytes of one metadata pair
   Streams st;
   st.uk = make_rsrc(a.uk + bh * plane, plane);
   st.lk = make_rsrc(a.lk + bh * plane, plane);
   st.uv = make_rsrc(a.uv + bh * plane, plane);
   st.lv = make_rsrc(a.lv + bh * plane, plane);
-  st.km = make_rsrc(a.kmeta + bh * (size_t)a.NG * D * 2, (uint32_t)a.NG * D * 8);
-  st.vm = make_rsrc(a.vmeta + bh * (size_t)a.T * 2, (uint32_t)a.T * 8);
+  st.km = make_rsrc(a.kmeta + bh * (size_t)a.NG * D * mb, (uint32_t)a.NG * D * mb);
+  st.vm = make_rsrc(a.vmeta + bh * (size_t)a.T * mb, (uint32_t)a.T * mb);
   return st;
 }
 
 __device__ __forceinline__ float lo_h(uint32_t x) { return (float)as_h2(x).x; }
 __device__ __forceinline__ float hi_h(uint32_t x) { return (float)as_h2(x).y; }
+
+// Metadata of two channels (keys) or two tokens (values) as one lane loads it: fp32 (s0, z0,
+// s1, z1), or with M16 the fp16 pairs (s0, b0), (s1, b1) in two words, where b = -s z.  meta4
+// gives (s0, x0, s1, x1) with x the zero-point (fp32) or the offset (fp16): a code C stands for
+// s (C - x) or s C + x.
+template <bool M16>
+using MetaT = typename std::conditional<M16, uint2, float4>::type;
+template <bool M16>  // pairs first + 2 lane, first + 2 lane + 1
+__device__ __forceinline__ MetaT<M16> load_meta(rsrc_t r, uint32_t first) {
+  const int lane = threadIdx.x;
+  if constexpr (M16) return bld8(r, lane * 8, first * 4);
+  else return bldf4(r, lane * 16, first * 8);
+}
+template <bool M16>
+__device__ __forceinline__ float4 meta4(const MetaT<M16>& m) {
+  if constexpr (M16) return make_float4(lo_h(m.x), hi_h(m.x), lo_h(m.y), hi_h(m.y));
+  else return m;
+}
+template <bool M16>
+__device__ __forceinline__ MetaT<M16> meta_zero() {
+  if constexpr (M16) return make_uint2(0u, 0u);
+  else return make_float4(0.f, 0.f, 0.f, 0.f);
+}
 
 // fp16 hi + lo split of x: hi = fp16(x), lo = fp16(x - hi); hi + lo carries ~22 bits.
 __device__ __forceinline__ void split_f16(float x, f16& hi, f16& lo) {
@@ -330,16 +356,16 @@ __device__ __forceinline__ void fixed_unit(float xmax, float& inv_unit, float& u
 }
 
 // Planes and metadata of one group, as loaded by one lane.
-template <int D>
+template <int D, bool M16>
 struct DraftBuf {
   uint4 k[DraftShape<D>::KIT];
   uint4 v[DraftShape<D>::VIT];
-  float4 km;  // key (s, z) of channels 2*lane, 2*lane+1
-  float4 vm;  // value (s, z) of tokens 2*lane, 2*lane+1
+  MetaT<M16> km;  // key metadata of channels 2*lane, 2*lane+1
+  MetaT<M16> vm;  // value metadata of tokens 2*lane, 2*lane+1
 };
 
-template <int D>
-__device__ __forceinline__ void draft_load_k(const Streams& sm, int g, DraftBuf<D>& buf) {
+template <int D, bool M16>
+__device__ __forceinline__ void draft_load_k(const Streams& sm, int g, DraftBuf<D, M16>& buf) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
   const uint32_t voff = (lane / S::KL) * (D / 2) + (lane % S::KL) * 16;
@@ -348,15 +374,15 @@ __device__ __forceinline__ void draft_load_k(const Streams& sm, int g, DraftBuf<
   for (int it = 0; it < S::KIT; ++it)  // key rows it*TPI .. : 1 KB apart
     buf.k[it] = bld16(sm.uk, voff + (it & 3) * 1024, soff + (it >> 2) * 4096);
 }
-template <int D>
-__device__ __forceinline__ void draft_load_meta(const Streams& sm, int g, DraftBuf<D>& buf) {
+template <int D, bool M16>
+__device__ __forceinline__ void draft_load_meta(const Streams& sm, int g, DraftBuf<D, M16>& buf) {
   const int lane = threadIdx.x;
-  buf.km = bldf4(sm.km, lane * 16, (uint32_t)g * D * 8);
-  if (lane >= D / 2) buf.km = make_float4(0.f, 0.f, 0.f, 0.f);
-  buf.vm = bldf4(sm.vm, lane * 16, (uint32_t)g * kGroup * 8);
+  buf.km = load_meta<M16>(sm.km, (uint32_t)g * D);
+  if (lane >= D / 2) buf.km = meta_zero<M16>();
+  buf.vm = load_meta<M16>(sm.vm, (uint32_t)g * kGroup);
 }
-template <int D>
-__device__ __forceinline__ void draft_load_v(const Streams& sm, int g, DraftBuf<D>& buf) {
+template <int D, bool M16>
+__device__ __forceinline__ void draft_load_v(const Streams& sm, int g, DraftBuf<D, M16>& buf) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
   const int vr = lane & 3, vd = lane >> 2;
@@ -379,8 +405,8 @@ struct DraftAcc {
 // current group has been consumed, so the next group's loads overlap this group's arithmetic.
 // (The prefetch is a template flag rather than a run-time test so that the number of loads in
 // flight at every wait is fixed.)
-template <int D, bool PF, class Args>
-__device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, DraftBuf<D>& cur,
+template <int D, bool PF, bool M16, class Args>
+__device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, DraftBuf<D, M16>& cur,
                                             int gnext, float q0, float q1, DraftLds& L,
                                             DraftAcc<D>& st) {
   using S = DraftShape<D>;
@@ -391,14 +417,17 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, Dr
   __syncthreads();  // the previous group's LDS reads are done
   // key weights q' = q s (channels 2 lane, 2 lane + 1) as digit planes; the score bias
   // sum_d q'_d (128 + off - z_d) stays in fp32
-  const float qa = q0 * cur.km.x, qb = q1 * cur.km.z;  // zero on lanes >= D/2
-  float bias = qa * (c - cur.km.y) + qb * (c - cur.km.w);
+  const float4 km = meta4<M16>(cur.km), vm = meta4<M16>(cur.vm);
+  const float qa = q0 * km.x, qb = q1 * km.z;  // zero on lanes >= D/2
+  // fp16 metadata: s (16 U + off) + b = 16 s (U - 8) + (s (128 + off) + b)
+  float bias = M16 ? q0 * fmaf(km.x, c, km.y) + q1 * fmaf(km.z, c, km.w)
+                   : qa * (c - km.y) + qb * (c - km.w);
   float qunit, qinv;
   fixed_unit(wave_max_all(fmaxf(fabsf(qa), fabsf(qb))), qinv, qunit);
-  L.vm[2 * lane] = make_float2(cur.vm.x, cur.vm.x * (c - cur.vm.y));
-  L.vm[2 * lane + 1] = make_float2(cur.vm.z, cur.vm.z * (c - cur.vm.w));
+  L.vm[2 * lane] = make_float2(vm.x, M16 ? fmaf(vm.x, c, vm.y) : vm.x * (c - vm.y));
+  L.vm[2 * lane + 1] = make_float2(vm.z, M16 ? fmaf(vm.z, c, vm.w) : vm.z * (c - vm.w));
   float punit, pinv;  // p' = p s <= max_t s_t
-  fixed_unit(wave_max_all(fmaxf(cur.vm.x, cur.vm.z)), pinv, punit);
+  fixed_unit(wave_max_all(fmaxf(vm.x, vm.z)), pinv, punit);
   if (lane < D / 2) {
     uint32_t ev, od;
     digit_bytes((int)rintf(qa * qinv), (int)rintf(qb * qinv), ev, od);
@@ -474,7 +503,7 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, Dr
   if constexpr (PF) draft_load_v<D>(sm, gnext, cur);
 }
 
-template <int D, class Args>
+template <int D, bool M16, class Args>
 __device__ void draft_quant_item(const Args& a, int b, int h, int item, DraftLds& L) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
@@ -494,8 +523,8 @@ __device__ void draft_quant_item(const Args& a, int b, int h, int item, DraftLds
 #pragma unroll
   for (int i = 0; i < S::VIT; ++i) st.o[i] = 0.f;
 
-  const Streams sm = make_streams(a, bh, D);
-  DraftBuf<D> buf;
+  const Streams sm = make_streams<M16>(a, bh, D);
+  DraftBuf<D, M16> buf;
   if (gs.first < gs.ng) {
     draft_load_k<D>(sm, gs.first, buf);
     draft_load_meta<D>(sm, gs.first, buf);
@@ -560,18 +589,18 @@ __device__ __forceinline__ int vtile_token(int tau, int r) {
   return 64 * (tau >> 2) + 16 * (r >> 2) + 8 * ((tau & 3) >> 1) + 2 * (r & 3) + (tau & 1);
 }
 
-template <int D>
+template <int D, bool M16>
 struct VerifyBuf {
   uint32_t ku[4][VerifyShape<D>::KK], kl[4][VerifyShape<D>::KK];  // 4 key tiles of a half
   uint2 vu[VerifyShape<D>::RT], vl[VerifyShape<D>::RT];            // value codes of a half
-  float4 km;  // key (s, z) of channels 2*lane, 2*lane+1
-  float4 vm;  // value (s, z) of tokens 2*lane, 2*lane+1
+  MetaT<M16> km;  // key metadata of channels 2*lane, 2*lane+1
+  MetaT<M16> vm;  // value metadata of tokens 2*lane, 2*lane+1
 };
 
 // UPPER: only the upper planes are read (the draft pass over grouped queries); the lower
 // nibbles are then the draft offset.
-template <int D, bool UPPER = false>
-__device__ __forceinline__ void verify_load_k(const Streams& sm, int gi, int half, VerifyBuf<D>& buf) {
+template <int D, bool UPPER = false, bool M16>
+__device__ __forceinline__ void verify_load_k(const Streams& sm, int gi, int half, VerifyBuf<D, M16>& buf) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
   // row of tile 4*half + t for lane row j: 16 (j/4) + 2 (j%4) + 64 half + 8 (t/2) + (t%2)
@@ -598,8 +627,8 @@ __device__ __forceinline__ void verify_load_k(const Streams& sm, int gi, int hal
   }
 }
 
-template <int D, bool UPPER = false>
-__device__ __forceinline__ void verify_load_v(const Streams& sm, int gi, int half, VerifyBuf<D>& buf) {
+template <int D, bool UPPER = false, bool M16>
+__device__ __forceinline__ void verify_load_v(const Streams& sm, int gi, int half, VerifyBuf<D, M16>& buf) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
   const uint32_t voff = j * (kGroup / 4) + 8 * g;
@@ -612,12 +641,12 @@ __device__ __forceinline__ void verify_load_v(const Streams& sm, int gi, int hal
   }
 }
 
-template <int D>
-__device__ __forceinline__ void verify_load_meta(const Streams& sm, int gi, VerifyBuf<D>& buf) {
+template <int D, bool M16>
+__device__ __forceinline__ void verify_load_meta(const Streams& sm, int gi, VerifyBuf<D, M16>& buf) {
   const int lane = threadIdx.x;
-  buf.km = bldf4(sm.km, lane * 16, (uint32_t)gi * D * 8);
-  if (lane >= D / 2) buf.km = make_float4(0.f, 0.f, 0.f, 0.f);
-  buf.vm = bldf4(sm.vm, lane * 16, (uint32_t)gi * kGroup * 8);
+  buf.km = load_meta<M16>(sm.km, (uint32_t)gi * D);
+  if (lane >= D / 2) buf.km = meta_zero<M16>();
+  buf.vm = load_meta<M16>(sm.vm, (uint32_t)gi * kGroup);
 }
 
 // Running state of a verify worker (per lane): softmax max / sum, the value bias sum, and the
@@ -631,8 +660,8 @@ struct VerifyAcc {
 // One group of a verify worker, in two 64-token halves.  With PF the buffers are refilled with
 // group gn as each part of group gi is consumed (a template flag, so that the number of loads in
 // flight at every wait is fixed).
-template <int D, bool PF, bool UPPER, class Args>
-__device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, VerifyBuf<D>& buf,
+template <int D, bool PF, bool UPPER, bool M16, class Args>
+__device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, VerifyBuf<D, M16>& buf,
                                              int gi, int gn, VerifyLds& L, VerifyAcc<D>& st) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
@@ -644,9 +673,11 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
   const f16x2 c1152 = {(f16)1152.f, (f16)1152.f};
   __syncthreads();  // the previous group's LDS reads are done
   // q' = q s for this lane's channels and every query: fp16 hi/lo into the B-operand slots of
-  // the lanes that consume them, and the fp32 bias partials 1024 (q'h + q'l) + q' z
+  // the lanes that consume them, and the fp32 bias partials 1024 (q'h + q'l) + q' z (fp16
+  // metadata: 1024 (q'h + q'l) - q b, since there a code C stands for s C + b)
   if (lane < D / 2) {
-    const float s0 = buf.km.x, z0 = buf.km.y, s1 = buf.km.z, z1 = buf.km.w;
+    const float4 km = meta4<M16>(buf.km);
+    const float s0 = km.x, z0 = km.y, s1 = km.z, z1 = km.w;
     const int c0 = 2 * lane;
     const int gg = c0 / S::CPL, kk = (c0 % S::CPL) / 8, e0 = c0 % 8;  // e0 even, e0+1 odd
     const int s_even = e0 >> 1, s_odd = 4 + (e0 >> 1);                // slots of e0, e0+1
@@ -664,13 +695,14 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
         bh16[8 * i + s_odd] = bhh;
         bl16[8 * i + s_odd] = bl;
         L.bias[i][lane] = 1024.f * (((float)ah + (float)al) + ((float)bhh + (float)bl)) +
-                          (qa * z0 + qb * z1);
+                          (M16 ? -(qv.x * z0 + qv.y * z1) : qa * z0 + qb * z1);
       }
     }
   }
-  L.vm[2 * lane] = make_float2(buf.vm.x, buf.vm.x * (128.f - buf.vm.y));
-  L.vm[2 * lane + 1] = make_float2(buf.vm.z, buf.vm.z * (128.f - buf.vm.w));
-  const float wscale = weight_scale(wave_max_all(fmaxf(buf.vm.x, buf.vm.z)));
+  const float4 vm = meta4<M16>(buf.vm);
+  L.vm[2 * lane] = make_float2(vm.x, M16 ? fmaf(128.f, vm.x, vm.y) : vm.x * (128.f - vm.y));
+  L.vm[2 * lane + 1] = make_float2(vm.z, M16 ? fmaf(128.f, vm.z, vm.w) : vm.z * (128.f - vm.w));
+  const float wscale = weight_scale(wave_max_all(fmaxf(vm.x, vm.z)));
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (PF) verify_load_meta<D>(sm, gn, buf);
@@ -767,7 +799,7 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
   }
 }
 
-template <int D, bool UPPER, class Args>
+template <int D, bool UPPER, bool M16, class Args>
 __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyLds& L) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
@@ -795,8 +827,8 @@ __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyL
 #pragma unroll
   for (int rt = 0; rt < S::RT; ++rt) st.O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const Streams sm = make_streams(a, bh, D);
-  VerifyBuf<D> buf;
+  const Streams sm = make_streams<M16>(a, bh, D);
+  VerifyBuf<D, M16> buf;
   if (gs.first < gs.ng) {
     verify_load_k<D, UPPER>(sm, gs.first, 0, buf);
     verify_load_meta<D>(sm, gs.first, buf);
@@ -999,7 +1031,7 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
 
 // The draft pass runs the VALU item (3 waves per SIMD), except over grouped queries, where both
 // passes run the MFMA item (2 waves per SIMD).
-template <int D, bool DRAFT, int NB, int MODE>
+template <int D, bool DRAFT, int NB, int MODE, bool M16>
 __global__ __launch_bounds__(64, (DRAFT && MODE != kModeGqa) ? 3 : 2) void attn_kernel(
     const AttnArgsN<NB, MODE> a) {
   constexpr bool kValu = DRAFT && MODE != kModeGqa;
@@ -1021,9 +1053,9 @@ __global__ __launch_bounds__(64, (DRAFT && MODE != kModeGqa) ? 3 : 2) void attn_
     const int b = find_seq<NB>(a.qitem_base, a.B, y);
     const int item = y - a.qitem_base[b];
     if constexpr (kValu)
-      draft_quant_item<D>(a, b, h, item, lds.p);
+      draft_quant_item<D, M16>(a, b, h, item, lds.p);
     else
-      verify_quant_item<D, DRAFT>(a, b, h, item, lds.p);
+      verify_quant_item<D, DRAFT, M16>(a, b, h, item, lds.p);
   }
 }
 
@@ -1166,6 +1198,17 @@ __device__ __forceinline__ uint32_t quant_code(float x, float s, float y, float 
 // channels, each reading 8 KB of fp16 and writing its slice of both planes and its metadata.
 constexpr int kFlushSlice = 32;
 
+// fp16 metadata of a group (keys: a channel; values: a token) with fp32 scale s and zero-point
+// z: s and the offset b = -s z (the fp32 product), each rounded to nearest-even fp16, b clamped
+// to the finite range first.  A code C then stands for s C + b.
+__device__ __forceinline__ uint32_t meta16_pair(float s, float z) {
+#pragma clang fp contract(off)
+  const float b = fminf(fmaxf(-(s * z), -65504.f), 65504.f);
+  const uint32_t hs = __builtin_bit_cast(uint16_t, (_Float16)s);
+  const uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)b);
+  return hs | (hb << 16);
+}
+
 struct FlushValLds {
   uint8_t code[kFlushSlice][128 + 4];          // codes, token-major (padded rows)
 };
@@ -1219,11 +1262,21 @@ __device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* k
     zc[e] = rintf(-mn[e] / sc[e]);
     yc[e] = 1.0f / sc[e];
   }
-  if (rr == 0) {  // (s, z) of the 8 channels: 64 contiguous bytes
-    float4* km = reinterpret_cast<float4*>(a.kmeta + ((lbh * a.NG + grp) * D + c0 + 8 * sub) * 2);
+  if (rr == 0) {  // metadata of the 8 channels: 64 (fp16: 32) contiguous bytes
+    const size_t pair0 = (lbh * a.NG + grp) * D + c0 + 8 * sub;
+    if (a.meta16) {
+      uint4* km = reinterpret_cast<uint4*>(a.kmeta + pair0 * 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      km[j] = make_float4(sc[2 * j], zc[2 * j], sc[2 * j + 1], zc[2 * j + 1]);
+      for (int j = 0; j < 2; ++j)
+        km[j] = make_uint4(meta16_pair(sc[4 * j], zc[4 * j]), meta16_pair(sc[4 * j + 1], zc[4 * j + 1]),
+                           meta16_pair(sc[4 * j + 2], zc[4 * j + 2]),
+                           meta16_pair(sc[4 * j + 3], zc[4 * j + 3]));
+    } else {
+      float4* km = reinterpret_cast<float4*>(a.kmeta + pair0 * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        km[j] = make_float4(sc[2 * j], zc[2 * j], sc[2 * j + 1], zc[2 * j + 1]);
+    }
   }
   // key plane rows are token-major, byte j of a row holds channel 2j in bits 0-3 and 2j + 1 in
   // bits 4-7: this lane's channels are bytes (c0 + 8 sub) / 2 .. + 3 of each row
@@ -1275,8 +1328,11 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
   const float z = rintf(-mn / s);
   const float y = 1.0f / s;
   if (hf == 0) {
-    float* vm = a.vmeta + (lbh * a.T + (size_t)grp * G + t0 + tk) * 2;
-    *reinterpret_cast<float2*>(vm) = make_float2(s, z);
+    const size_t pair = lbh * a.T + (size_t)grp * G + t0 + tk;
+    if (a.meta16)
+      *reinterpret_cast<uint32_t*>(a.vmeta + pair * 4) = meta16_pair(s, z);
+    else
+      *reinterpret_cast<float2*>(a.vmeta + pair * 8) = make_float2(s, z);
   }
 #pragma unroll
   for (int k = 0; k < HALF / 2; ++k) {  // word k: channels 8 (2 (k / 4) + hf) + 2 (k % 4), +1
@@ -1501,37 +1557,42 @@ hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st)
   return hipGetLastError();
 }
 
-template <int D, bool DRAFT, int MODE>
+template <int D, bool DRAFT, int MODE, bool M16>
 const void* attn_fn(int bucket) {
   switch (bucket) {
-    case 1: return (const void*)attn_kernel<D, DRAFT, 1, MODE>;
-    case 8: return (const void*)attn_kernel<D, DRAFT, 8, MODE>;
-    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, MODE>;
+    case 1: return (const void*)attn_kernel<D, DRAFT, 1, MODE, M16>;
+    case 8: return (const void*)attn_kernel<D, DRAFT, 8, MODE, M16>;
+    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, MODE, M16>;
   }
 }
 
-template <int MODE>
+template <int MODE, bool M16>
 const void* attn_fn_dm(int D, bool draft, int bucket) {
-  return D == 128 ? (draft ? attn_fn<128, true, MODE>(bucket) : attn_fn<128, false, MODE>(bucket))
-                  : (draft ? attn_fn<64, true, MODE>(bucket) : attn_fn<64, false, MODE>(bucket));
+  return D == 128 ? (draft ? attn_fn<128, true, MODE, M16>(bucket) : attn_fn<128, false, MODE, M16>(bucket))
+                  : (draft ? attn_fn<64, true, MODE, M16>(bucket) : attn_fn<64, false, MODE, M16>(bucket));
+}
+template <bool M16>
+const void* attn_fn_m(int D, bool draft, int bucket, int mode) {
+  return mode == kModeDev      ? attn_fn_dm<kModeDev, M16>(D, draft, bucket)
+         : mode == kModeAppend ? attn_fn_dm<kModeAppend, M16>(D, draft, bucket)
+         : mode == kModeGqa    ? attn_fn_dm<kModeGqa, M16>(D, draft, bucket)
+                               : attn_fn_dm<kModeHost, M16>(D, draft, bucket);
 }
 
 // Work-item slots of one attention pass on the current device: compute units times the
 // one-wave workgroups of that kernel a compute unit holds at once (cached per device).
-int attention_slots(int D, bool draft, int B, int mode) {
+int attention_slots(int D, bool draft, int B, int mode, bool meta16) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev][2][2][4][3];
+  static int cache[kMaxDev][2][2][2][4][3];
   int id = 0;
   if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 3) return 0;
   const int bucket = batch_bucket(B);
-  int& slot = cache[id][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
+  int& slot = cache[id][meta16][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
   if (slot > 0) return slot;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess) return 0;
-  const void* fn = mode == kModeDev ? attn_fn_dm<kModeDev>(D, draft, bucket)
-                   : mode == kModeAppend ? attn_fn_dm<kModeAppend>(D, draft, bucket)
-                   : mode == kModeGqa ? attn_fn_dm<kModeGqa>(D, draft, bucket)
-                                      : attn_fn_dm<kModeHost>(D, draft, bucket);
+  const void* fn = meta16 ? attn_fn_m<true>(D, draft, bucket, mode)
+                          : attn_fn_m<false>(D, draft, bucket, mode);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
   slot = cus * per_cu;
   return slot;
@@ -1541,7 +1602,10 @@ template <int D, bool DRAFT, int NB, int MODE, class Full>
 hipError_t launch_attention_n(const Full& f, hipStream_t st) {
   const AttnArgsN<NB, MODE> a = narrow<NB>(f);
   const dim3 grid(a.n_titems_total + a.n_qitems_total, a.H);
-  hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE>), grid, dim3(64), 0, st, a);
+  if (a.meta16)
+    hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, true>), grid, dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, false>), grid, dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 cgrid(a.B * a.m, a.H);

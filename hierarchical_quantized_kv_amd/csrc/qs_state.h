@@ -34,8 +34,12 @@ inline bool config_ok(const qs_config& c, std::string* why) {
   if ((long long)c.max_ctx / c.group > (long long)kMaxQuantSplits * 1024) return fail("max_ctx too large");
   if (c.gamma_max < 0 || c.gamma_max + 1 > QS_MAX_QUERIES) return fail("gamma_max + 1 must be in 1..16");
   if (c.draft_offset != 0 && c.draft_offset != 8) return fail("draft_offset must be 0 or 8");
+  if (c.meta_fp16 != 0 && c.meta_fp16 != 1) return fail("meta_fp16 must be 0 or 1");
   return true;
 }
+
+// Bytes of one (scale, zero-point / offset) pair.
+inline size_t meta_bytes(const qs_config& c) { return c.meta_fp16 ? 4 : 8; }
 
 // Record slots per (sequence, head) in the split workspace.
 inline int record_slots() { return kMaxQuantSplits + kMaxTailItems; }
@@ -46,8 +50,9 @@ inline qs_layout make_layout(const qs_config& c) {
   const size_t T = (size_t)c.max_ctx, D = (size_t)c.head_dim, G = (size_t)c.group;
   L.uk_bytes = align256(lbh * T * (D / 2));
   L.uv_bytes = align256(lbh * (T / G) * D * (G / 2));
-  L.kmeta_bytes = align256(lbh * (T / G) * D * 2 * sizeof(float));
-  L.vmeta_bytes = align256(lbh * T * 2 * sizeof(float));
+  const size_t mb = meta_bytes(c);
+  L.kmeta_bytes = align256(lbh * (T / G) * D * mb);
+  L.vmeta_bytes = align256(lbh * T * mb);
   L.tail_bytes = align256(lbh * 2 * G * D * 2);
   L.work_bytes = align256((size_t)c.batch * c.n_heads * record_slots() * (c.gamma_max + 1) *
                           (D + kRecPad) * sizeof(float));

@@ -87,6 +87,14 @@ typedef struct {
   int32_t max_ctx;      /* quantized-token capacity per sequence, positive multiple of G       */
   int32_t gamma_max;    /* verify accepts m <= gamma_max + 1 queries; gamma_max + 1 <= 16      */
   int32_t draft_offset; /* constant added to 16*C_U by the draft dequantization: 8 or 0        */
+  int32_t meta_fp16;    /* metadata format: 0 = fp32 (scale s, zero-point z), a code C stands
+                           for s (C - z); 1 = fp16 (scale s, offset b = -s z), C stands for
+                           s C + b (half the metadata bytes).  The codes are the same in both
+                           formats (computed from the fp32 s and z); the fp16 pair is s and the
+                           fp32 product -s z, each rounded to nearest-even fp16, an offset past
+                           the fp16 range saturating at +-65504.  Storing b rather than z keeps
+                           a degenerate group exact: its scale (clamped to 1e-8) rounds to 0
+                           and b is the group's value.                                         */
 } qs_config;
 
 /* Byte offsets (from the arena base) and sizes of the arena sections.  Every section starts
@@ -99,8 +107,10 @@ typedef struct {
  *                                      of G/2 tokens, each channel-major.  Byte j of the row of
  *                                      channel d in half e holds token e*G/2 + 2j of the group
  *                                      in bits 0-3 and token e*G/2 + 2j + 1 in bits 4-7.
- *  kmeta    f32 [L][B][H][NG][D][2]    key (scale, zero-point) per group and channel.
- *  vmeta    f32 [L][B][H][T][2]        value (scale, zero-point) per token.
+ *  kmeta    f32 [L][B][H][NG][D][2]    key (scale, zero-point) per group and channel;
+ *                                      meta_fp16: f16 [L][B][H][NG][D][2] (scale, offset).
+ *  vmeta    f32 [L][B][H][T][2]        value (scale, zero-point) per token;
+ *                                      meta_fp16: f16 [L][B][H][T][2] (scale, offset).
  *  tail_k,  f16 [L][B][H][2G][D]       fp16 tail ring.  Logical tail token i of a sequence
  *  tail_v                              lives in slot (head + i) mod 2G, head in {0, G}.
  *  work     --                         split-softmax workspace (library private).

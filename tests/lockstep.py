@@ -26,16 +26,16 @@ def log(msg):
 
 class Lockstep:
     def __init__(self, n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, heads=None,
-                 layers=None, draft_offset=8, tag=""):
+                 layers=None, draft_offset=8, tag="", meta_fp16=False):
         self.B, self.H, self.D, self.L = batch, n_heads, head_dim, n_layers
         self.G = 128
         self.heads = list(range(n_heads)) if heads is None else list(heads)
         self.layers = list(range(n_layers)) if layers is None else list(layers)
         self.tag = tag
         self.gpu = Cache(n_layers, batch, n_heads, head_dim, max_ctx, gamma_max,
-                         draft_offset=draft_offset)
+                         draft_offset=draft_offset, meta_fp16=meta_fp16)
         self.orc = {l: OracleCache(1, batch, len(self.heads), head_dim, self.G, max_ctx,
-                                   gamma_max, draft_offset) for l in self.layers}
+                                   gamma_max, draft_offset, meta_fp16) for l in self.layers}
         self.max_rel = 0.0
         self.max_abs = 0.0
 
@@ -113,13 +113,15 @@ class Lockstep:
         for b in range(self.B):
             q = int(nq[b])
             sec = lambda name: self.gpu.section(name, layer)[b].index_select(0, hs)
+            # fp16 metadata is compared through its exact fp32 values (the oracle keeps floats)
+            host = lambda t: t.float().cpu().numpy() if t.dtype == torch.float16 else t.cpu().numpy()
             for name, rows in (("uk", q), ("lk", q), ("vmeta", q)):
-                got = sec(name)[:, :rows].cpu().numpy()
+                got = host(sec(name)[:, :rows])
                 ref = img[name][b, :, :rows]
                 assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), \
                     f"{self.tag} L{layer} b{b} {name} differs"
             for name in ("uv", "lv", "kmeta"):
-                got = sec(name)[:, : q // G].cpu().numpy()
+                got = host(sec(name)[:, : q // G])
                 ref = img[name][b, :, : q // G]
                 assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), \
                     f"{self.tag} L{layer} b{b} {name} differs"

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 def cfg(**kw):
     base = dict(n_layers=2, batch=3, n_heads=4, head_dim=128, group=G, max_ctx=8 * G,
-                gamma_max=6, draft_offset=8)
+                gamma_max=6, draft_offset=8, meta_fp16=0)
     base.update(kw)
     return QsConfig(*[base[f] for f, _ in QsConfig._fields_])
 
@@ -62,8 +62,15 @@ def test_arena_size_and_layout(lib):
     assert lay.state + lay.state_bytes == lay.total and lay.state_bytes >= (2 * 3 * 4 + 1) * 4
     lbh = 2 * 3 * 4
     assert lay.uk_bytes == lbh * 8 * G * 64 and lay.uv_bytes == lbh * 8 * 128 * 64
+    assert lay.kmeta_bytes == lbh * 8 * 128 * 8 and lay.vmeta_bytes == lbh * 8 * G * 8
+    # fp16 metadata: half the metadata bytes, every other section the same size
+    lay16 = QsLayout()
+    assert lib.qs_arena_layout(ctypes.byref(cfg(meta_fp16=1)), ctypes.byref(lay16)) == 0
+    assert lay16.kmeta_bytes == lay.kmeta_bytes // 2 and lay16.vmeta_bytes == lay.vmeta_bytes // 2
+    for f in ("uk_bytes", "uv_bytes", "tail_bytes", "work_bytes", "state_bytes"):
+        assert getattr(lay16, f) == getattr(lay, f)
     for bad in (cfg(head_dim=96), cfg(group=64), cfg(max_ctx=100), cfg(batch=0),
-                cfg(batch=65), cfg(gamma_max=15 + 1), cfg(draft_offset=4)):
+                cfg(batch=65), cfg(gamma_max=15 + 1), cfg(draft_offset=4), cfg(meta_fp16=2)):
         assert lib.qs_arena_bytes(ctypes.byref(bad)) == 0
         assert lib.qs_arena_layout(ctypes.byref(bad), ctypes.byref(lay)) == binding.QS_ERR_INVALID_ARG
 

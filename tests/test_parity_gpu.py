@@ -282,7 +282,10 @@ def test_draft_equals_one_query_verify_when_lower_planes_are_the_offset(D):
     diff = float((d - vq).abs().max())
     ref = float(d.abs().max())
     log(f"dv{D}: max |draft - verify| {diff:.3e} (max |out| {ref:.3e}); vs oracle {ls.max_abs:.3e}")
-    assert diff <= 1e-5 * max(ref, 1e-3)
+    # each pass is within a few 1e-5 of the fp64 result (the draft's fixed-point weights keep
+    # 22 fractional bits of the wave's largest weight; measured: up to 2.2e-5 of max |out|, all
+    # of it the draft's), while a wrong nibble or offset moves the outputs by >= 1e-2
+    assert diff <= 5e-5 * max(ref, 1e-3)
 
 
 @pytest.mark.parametrize("D,B", [(64, 3), (128, 3), (64, 9)])
