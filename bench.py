@@ -43,14 +43,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 # (Batch 1: the kernels' batch-bucket template argument is 1.)
 # Kernel names (as rocprofv3 prints them) of the default step: the attention kernels of the
 # fused append + attend calls (mode 2); --no-fuse runs the mode-0 ones.
-KERNELS = {"draft": "attn_kernel<128, true, 1, 2>", "verify": "attn_kernel<128, false, 1, 2>",
+# The last attention argument is the metadata format (false: fp32 (scale, zero-point)).
+KERNELS = {"draft": "attn_kernel<128, true, 1, 2, false>",
+           "verify": "attn_kernel<128, false, 1, 2, false>",
            "combine": "combine_kernel<128, 1, 2>", "flush": "flush_kernel<128>",
            "prefill": "prefill_kernel<128>"}
 
 
 def kernel_names(fuse):
     mode = 2 if fuse else 0
-    return (f"attn_kernel<128, true, 1, {mode}>", f"attn_kernel<128, false, 1, {mode}>",
+    return (f"attn_kernel<128, true, 1, {mode}, false>", f"attn_kernel<128, false, 1, {mode}, false>",
             f"combine_kernel<128, 1, {mode}>")
 
 CONFIGS = {
@@ -346,7 +348,9 @@ def main():
     sa = {sb: summarize(e, f"spec_accept_batch{sb}") for sb, e in sa_ev.items()}
 
     gqa = None if args.no_gqa else measure_gqa(torch, stream, spin_cycles, dev)
-    meta16 = None if args.no_meta16 else measure_meta16(torch, stream, spin_cycles, dev)
+    meta16 = None if args.no_meta16 else measure_meta16(
+        torch, stream, spin_cycles, dev, cfg["name"], ctx=cfg["ctx"], H=cfg["heads"],
+        m=cfg["gamma"] + 1)
     read_ceiling = measure_read_ceiling(torch, stream)
 
     cpu = None
@@ -533,9 +537,10 @@ def measure_gqa(torch, stream, spin_cycles, dev, ctx=131072, Hkv=8, g=4, mt=4, r
     return out
 
 
-def measure_meta16(torch, stream, spin_cycles, dev, ctx=131072, H=32, m=7, reps=20, rounds=3):
-    """fp16 (scale, offset) metadata against fp32 (scale, zero-point) on the same layer: 32
-    heads, head_dim 128, ctx tokens quantized plus a 64 + m token tail, in two caches that differ
+def measure_meta16(torch, stream, spin_cycles, dev, name, ctx=131072, H=32, m=7, reps=20,
+                   rounds=3):
+    """fp16 (scale, offset) metadata against fp32 (scale, zero-point) on one layer of the
+    workload: H heads, head_dim 128, ctx tokens quantized plus a 64 + m token tail, in two caches that differ
     only in the metadata format.  The draft and the m-query verify are timed over `reps`
     consecutive calls behind the spin kernel, the two formats alternating for `rounds` rounds;
     the best round of each is reported."""
@@ -551,12 +556,12 @@ def measure_meta16(torch, stream, spin_cycles, dev, ctx=131072, H=32, m=7, reps=
     ov = torch.empty((1, m, H, D), dtype=torch.float32, device=dev)
     caches = {}
     for fmt, m16 in (("fp32", False), ("fp16", True)):
-        c = Cache(1, 1, H, D, ctx + 2 * G, 6, meta_fp16=m16)
+        c = Cache(1, 1, H, D, ctx + 2 * G, m - 1, meta_fp16=m16)
         c.prefill(0, k[:, :ctx + 64].contiguous(), v[:, :ctx + 64].contiguous())
         c.append(0, k[:, ctx + 64:].contiguous(), v[:, ctx + 64:].contiguous())
         caches[fmt] = c
     del k, v
-    out = {"workload": f"one LWM-128k-shaped layer: {H} heads, head_dim {D}, ctx {ctx} + "
+    out = {"workload": f"one layer of the {name} workload: {H} heads, head_dim {D}, ctx {ctx} + "
                        f"{nt}-token tail, verify of {m} queries; fp32 vs fp16 metadata, best of "
                        f"{rounds} alternating rounds of {reps} calls"}
     best = {}
@@ -693,7 +698,7 @@ def write_traffic_summary(fetch_dir, write_dir, args):
         f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
         f"\"attn_kernel|combine_kernel|flush_kernel|prefill_kernel|copy\" -d {fetch_dir} -o run "
         f"--output-format csv -- python -u bench.py --config {args.config} --layers 2 --steps 1 "
-        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --no-graph --no-gqa --calibration-copy-mib "
+        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --no-graph --no-gqa --no-meta16 --calibration-copy-mib "
         f"{args.calibration_copy_mib}",
         f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE (same arguments, -d {write_dir})",
         f"python bench.py --config {args.config} --calibration-copy-mib "
