@@ -1,7 +1,8 @@
 """GPU parity at the full sizes of the workloads (the launch configurations the benchmark times),
 checked on sampled heads / layers that the CPU oracle can afford.
 
-  * LWM-128k-shaped layer: 32 heads x 128, 131072 prefilled tokens, gamma = 6 round.
+  * LWM-128k-shaped layer: 32 heads x 128, 131072 prefilled tokens, gamma = 6 round; the same
+    prefilled layer in both metadata formats.
   * Llama-2-7B-32K-shaped stack: 32 layers, 32768 tokens, 64 rounds of gamma = 4 with
     Bernoulli(0.9) acceptance driving rollback and flush; outputs checked every 8th round on
     three layers, final planes of every layer checked bit-exact against the oracle's replay.
@@ -75,13 +76,15 @@ def test_lwm_128k_layer():
     log(f"128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
-def test_prefill_128k_layer():
+@pytest.mark.parametrize("meta_fp16", [False, True])
+def test_prefill_128k_layer(meta_fp16):
     """One qs_prefill of a 131072 + 64-token prompt (1024 groups quantized straight from the
     prompt, 64 tokens to the tail), bit-exact against the oracle on sampled heads, then one
-    round of attention on top."""
-    log("case: 128k prefill, heads 0/17/31 sampled")
+    round of attention on top; in both metadata formats."""
+    log(f"case: 128k prefill, heads 0/17/31 sampled, fp16 metadata {meta_fp16}")
     H, D, ctx, gamma = 32, 128, 131072, 6
-    ls = Lockstep(1, 1, H, D, ctx + 4 * G, gamma, heads=[0, 17, 31], tag="prefill128k")
+    ls = Lockstep(1, 1, H, D, ctx + 4 * G, gamma, heads=[0, 17, 31], tag="prefill128k",
+                  meta_fp16=meta_fp16)
     out = synth.outlier_channels(H, D, synth.seed_for(4, 1, "outlier"))
     k, v = dev_kv(4, 1, 1, ctx + 64, H, D, outliers=out)
     ls.prefill(0, k, v)
