@@ -352,6 +352,7 @@ def main():
         torch, stream, spin_cycles, dev, cfg["name"], ctx=cfg["ctx"], H=cfg["heads"],
         m=cfg["gamma"] + 1)
     read_ceiling = measure_read_ceiling(torch, stream)
+    mixed_ceiling = measure_mixed_ceiling(torch, stream)
 
     cpu = None
     cpu_all = None
@@ -419,6 +420,7 @@ def main():
         "meta16": meta16,
         "samples_dropped": dropped,
         "read_ceiling": read_ceiling,
+        "mixed_ceiling": mixed_ceiling,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
     }
@@ -624,6 +626,43 @@ def measure_read_ceiling(torch, stream):
             "kernel": f"grid-stride streaming read, 16 B non-temporal loads, 8 in flight per lane, "
                       f"{4 * best[1]} waves per CU",
             "bytes_per_launch": nbytes, "avg_launch_us": round(best[2], 2)}
+
+
+def measure_mixed_ceiling(torch, stream, out_mib=1024):
+    """The practical rate of read + write streams on this device: plain grid-stride kernels
+    (16-byte non-temporal loads and stores, libqs_readprobe.so) writing out_mib MiB while reading
+    1 or 2 times as much (a copy; about the 1.9 : 1 read / write ratio of the flush and prefill
+    kernels), best of 4, 8 and 12 waves per compute unit, 20 timed launches each.  Rates count
+    read + written bytes."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "hierarchical_quantized_kv_amd", "libqs_readprobe.so"))
+    lib.qs_probe_stream_mix.restype = ctypes.c_int
+    lib.qs_probe_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    out_bytes = out_mib << 20
+    src = torch.zeros(2 * out_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(out_bytes, dtype=torch.uint8, device="cuda")
+    res = {}
+    for rpw, name in ((1, "copy"), (2, "read2_write1")):
+        best = None
+        for bpc in (1, 2, 3):
+            us = ctypes.c_float()
+            rc = lib.qs_probe_stream_mix(ctypes.c_void_p(src.data_ptr()),
+                                         ctypes.c_void_p(dst.data_ptr()), out_bytes, rpw, bpc,
+                                         20, ctypes.c_void_p(stream.cuda_stream), ctypes.byref(us))
+            if rc != 0:
+                raise RuntimeError(f"qs_probe_stream_mix failed with HIP error {rc}")
+            gbs = (rpw + 1) * out_bytes / (us.value * 1e-6) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, bpc, us.value)
+        res[f"{name}_gbs"] = round(best[0], 1)
+        res[f"{name}_frac_of_peak"] = round(best[0] / PEAK_HBM_GBS, 4)
+        res[f"{name}_waves_per_cu"] = 4 * best[1]
+    del src, dst
+    res["kernel"] = (f"grid-stride streams: 16 B non-temporal loads and stores, {out_mib} MiB "
+                     f"written, 1x or 2x as much read")
+    return res
 
 
 def kernel_source_hash():
