@@ -389,7 +389,8 @@ def main():
                                f"ctx {ctx} + 64-token tail, gamma {gamma} ({m}-query verify), "
                                f"1% key channels x8",
                    "layers": L, "heads": H, "head_dim": D, "ctx": ctx, "gamma": gamma,
-                   "batch": 1, "group": G, "fused_append": fuse},
+                   "batch": 1, "group": G, "fused_append": fuse,
+                   "metadata": "fp32 (scale, zero-point)"},
         "draft_us_per_layer": round(d_us, 2),
         "draft_gbs": round(d_gbs, 1),
         "verify_us_per_layer": round(v_us, 2),
