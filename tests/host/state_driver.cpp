@@ -2,7 +2,7 @@
 // Reads commands on stdin and prints, after each, the status and every layer's counters, so a
 // Python test can replay the same script on the CPU oracle and compare.
 //
-//   create L B H D G T gamma off
+//   create L B H D G T gamma off [meta_fp16]
 //   append layer n_max n_0 .. n_{B-1}
 //   prefill layer n_max n_0 .. n_{B-1}
 //   rollback layer d_0 .. d_{B-1}
@@ -31,6 +31,7 @@ int main() {
     if (op == "create") {
       in >> cfg.n_layers >> cfg.batch >> cfg.n_heads >> cfg.head_dim >> cfg.group >> cfg.max_ctx >>
           cfg.gamma_max >> cfg.draft_offset;
+      if (!(in >> cfg.meta_fp16)) cfg.meta_fp16 = 0;
       if (!qs::config_ok(cfg, &err)) {
         std::printf("status 1 %s\n", err.c_str());
         continue;

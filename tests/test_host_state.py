@@ -158,16 +158,18 @@ def test_plan_covers_every_group(driver):
             assert cg == lo or not fits(cg - 1)
 
 
-def test_layout_sections(driver):
-    out = run(driver, ["create 2 3 4 128 128 1024 6 8", "layout"])[-1].split()[1:]
+@pytest.mark.parametrize("meta_fp16", [0, 1])
+def test_layout_sections(driver, meta_fp16):
+    out = run(driver, [f"create 2 3 4 128 128 1024 6 8 {meta_fp16}", "layout"])[-1].split()[1:]
     uk, lk, uv, lv, km, vm, tk, tv, work, state, total = map(int, out)
     offs = [uk, lk, uv, lv, km, vm, tk, tv, work, state, total]
     assert offs == sorted(offs) and all(x % 256 == 0 for x in offs)
     lbh, T, D = 2 * 3 * 4, 1024, 128
+    mb = 4 if meta_fp16 else 8        # bytes of a (scale, zero-point / offset) pair
     assert lk - uk == uv - lk == lbh * T * D // 2
     assert lv - uv == km - lv == lbh * (T // G) * D * G // 2
-    assert vm - km == lbh * (T // G) * D * 8
-    assert tk - vm == lbh * T * 8
+    assert vm - km == lbh * (T // G) * D * mb
+    assert tk - vm == lbh * T * mb
     assert tv - tk == work - tv == lbh * 2 * G * D * 2
     assert state - work == 3 * 4 * (256 + 4) * 7 * (D + 4) * 4
     # device-mode counters: 4 int32 per (layer, sequence) and the error word, 256-byte aligned
