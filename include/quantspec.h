@@ -172,7 +172,8 @@ qs_status qs_rollback(qs_cache* cache, int32_t layer, const int32_t* h_n_drop);
 /* Quantizes the oldest G tail tokens (one ring half) of every sequence b of `layer` (every
  * layer when layer == -1) whose nt_b >= max(G, min_tail): computes the key and value
  * (scale, zero-point) and 8-bit codes, splits each code into C_U and C_L, writes both planes
- * and the metadata at quantized position nq_b, then nq_b += G, nt_b -= G, head_b ^= G.
+ * and the metadata (in the cache's format, see meta_fp16) at quantized position nq_b, then
+ * nq_b += G, nt_b -= G, head_b ^= G.
  * Sequences below the threshold are left unchanged.  h_flushed: host int32 [B] (or NULL),
  * receives 1 for flushed sequences (of the last layer when layer == -1), else 0.
  * Must be called only when every tail token is committed.
@@ -214,7 +215,8 @@ qs_status qs_spec_accept(const float* d_target_logits, const float* d_draft_logi
  * token plus every tail token.
  *   d_q   : fp16 [B][H][D]      d_out : fp32 [B][H][D]
  *   out = softmax(sm_scale * q . k_j) weighted sum of v_j over all cached tokens j, with
- *   quantized k, v dequantized as ((16*C_U + draft_offset) - z) * s.
+ *   quantized k, v dequantized as ((16*C_U + draft_offset) - z) * s (fp16 metadata:
+ *   s * (16*C_U + draft_offset) + b).
  * Errors: QS_ERR_STATE if a sequence holds no token.  [QuantSpec Guide, "Upper 4-Bit
  * Representation (Draft)"; Pith review, one-line read.] */
 qs_status qs_attend_draft(qs_cache* cache, int32_t layer, const void* d_q, float sm_scale,
@@ -224,7 +226,8 @@ qs_status qs_attend_draft(qs_cache* cache, int32_t layer, const void* d_q, float
  * plus the tail, causally masked: query i sees every quantized token and tail positions
  * 0 .. nt_b - m + i (the last m tail tokens are the m verified tokens themselves).
  *   d_q   : fp16 [B][m][H][D]   d_out : fp32 [B][m][H][D]
- *   quantized k, v dequantized as (C8 - z) * s with C8 = 16*C_U + C_L.
+ *   quantized k, v dequantized as (C8 - z) * s with C8 = 16*C_U + C_L (fp16 metadata:
+ *   s * C8 + b).
  * Errors: QS_ERR_INVALID_ARG if m < 1 or m > gamma_max + 1; QS_ERR_STATE if m > nt_b.
  * [QuantSpec Guide, "Lower 4-Bit Representation (Residual)" and "3. The Self-Speculative
  * Verification Loop"; Pith review, one-line read.] */
