@@ -112,24 +112,25 @@ def oracle_round(ls, h, n_gpu, gamma, rnd):
     return n_g
 
 
-@pytest.mark.parametrize("B,H,D,lens", [
-    (2, 4, 128, (3 * G + 120, 5 * G + 126)),             # the 8-sequence argument bucket
-    (1, 8, 128, (2 * G + 127,)),                          # the 1-sequence bucket
+@pytest.mark.parametrize("B,H,D,lens,m16", [
+    (2, 4, 128, (3 * G + 120, 5 * G + 126), False),      # the 8-sequence argument bucket
+    (1, 8, 128, (2 * G + 127,), False),                   # the 1-sequence bucket
     # the 64-sequence bucket at D = 64; sequences 0, 4, 8 start with an empty quantized tier
-    (9, 2, 64, tuple(G * (i % 4) + 122 + i % 5 for i in range(9))),
+    (9, 2, 64, tuple(G * (i % 4) + 122 + i % 5 for i in range(9)), False),
+    (2, 4, 128, (3 * G + 120, 5 * G + 126), True),       # fp16 metadata
 ])
-def test_graph_round_replays_match_oracle(B, H, D, lens):
+def test_graph_round_replays_match_oracle(B, H, D, lens, m16):
     L, gamma, V, rounds = 2, 4, 1000, 6
     log(f"case: device-mode graph round B={B} H={H} D={D} prompts={lens} gamma={gamma} "
-        f"rounds={rounds}")
-    ls = Lockstep(L, B, H, D, 16 * G, gamma, tag="graph")
+        f"rounds={rounds} fp16 metadata {m16}")
+    ls = Lockstep(L, B, H, D, 16 * G, gamma, tag="graph", meta_fp16=m16)
     n_max = max(lens)
     for l in range(L):
         k, v = synth.kv_device(torch, B, n_max, H, D, 600 + l, 700 + l, "cuda")
         ls.prefill(l, k, v, n=list(lens))
     torch.cuda.synchronize()
     # load every kernel once (a scratch cache of the same shape) before capturing
-    warm = Cache(L, B, H, D, 16 * G, gamma)
+    warm = Cache(L, B, H, D, 16 * G, gamma, meta_fp16=m16)
     kw, vw = synth.kv_device(torch, B, G + 8, H, D, 1, 2, "cuda")   # every sequence non-empty
     for l in range(L):
         warm.prefill(l, kw, vw)
