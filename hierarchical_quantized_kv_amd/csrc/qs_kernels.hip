@@ -39,6 +39,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "qs_args.h"
@@ -1583,19 +1584,22 @@ const void* attn_fn_m(int D, bool draft, int bucket, int mode) {
 // one-wave workgroups of that kernel a compute unit holds at once (cached per device).
 int attention_slots(int D, bool draft, int B, int mode, bool meta16) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev][2][2][2][4][3];
+  // filled on first use; concurrent callers at worst compute the same value twice
+  static std::atomic<int> cache[kMaxDev][2][2][2][4][3];
   int id = 0;
   if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 3) return 0;
   const int bucket = batch_bucket(B);
-  int& slot = cache[id][meta16][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
-  if (slot > 0) return slot;
+  std::atomic<int>& slot = cache[id][meta16][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
+  const int known = slot.load(std::memory_order_relaxed);
+  if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess) return 0;
   const void* fn = meta16 ? attn_fn_m<true>(D, draft, bucket, mode)
                           : attn_fn_m<false>(D, draft, bucket, mode);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
-  slot = cus * per_cu;
-  return slot;
+  const int n = cus * per_cu;
+  slot.store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <int D, bool DRAFT, int NB, int MODE, class Full>

@@ -47,7 +47,7 @@
  *    asynchronous; all bookkeeping (lengths, ring head) lives on the host and is updated at
  *    enqueue time, so no call synchronizes with the device.  All calls on one cache must be
  *    ordered on one stream: they share the arena's split workspace.
- *  - A handle is not thread-safe.
+ *  - A handle is not thread-safe; different handles may be used from different threads.
  *  - fp16 means IEEE binary16; fp32 means IEEE binary32.
  *
  * Supported shapes: group == 128, head_dim in {64, 128}, 1 <= gamma_max + 1 <= 16,
