@@ -1,9 +1,10 @@
 """Randomized GPU parity: seeded random configurations (head_dim, batch across the three argument
 buckets, heads, gamma_max, draft offset, metadata format, key distribution) driven through random
 but valid sequences of the cache's verbs -- prefill of ragged prompts, appends, drafts, fused
-append + draft, verifies of 1 .. min(gamma_max + 1, nt) queries, rollbacks, flushes -- with every
-attention output compared with the CPU oracle (max abs 2e-3) and the planes, metadata, ring
-slots and counters compared bit for bit at the end.
+append + draft, verifies of 1 .. min(gamma_max + 1, nt) queries, grouped-query draft and verify,
+device-mode draft and verify (counters taken to the arena and back), rollbacks, flushes -- with
+every attention output compared with the CPU oracle (max abs 2e-3) and the planes, metadata,
+ring slots and counters compared bit for bit at the end.
 
 QS_RANDOM_CASES sets the number of seeds (default 16).
 """
@@ -61,7 +62,8 @@ def test_random_rounds_match_the_oracle(seed):
     ops = []
     for _ in range(14):
         nq, nt, _ = orc.state(0)
-        op = str(rng.choice(["append", "append", "draft", "fused", "verify", "rollback", "flush"]))
+        op = str(rng.choice(["append", "append", "draft", "fused", "verify", "gqa", "dev",
+                             "rollback", "flush"]))
         if op in ("append", "fused"):
             n = [int(rng.integers(0, min(2 * G - int(t), 9) + 1)) for t in nt]
             if max(n) == 0:
@@ -88,6 +90,44 @@ def test_random_rounds_match_the_oracle(seed):
                 continue
             m = int(rng.integers(1, top + 1))
             ls.verify(0, _q(rng, B, m, H, D))
+        elif op == "gqa":   # g query heads per cached head; the oracle once per r
+            if any(int(a) + int(t) == 0 for a, t in zip(nq, nt)):
+                continue
+            g = int(rng.integers(1, min(4, gmax + 1) + 1))   # g query columns <= gamma_max + 1
+            mt = int(rng.integers(0, min((gmax + 1) // g, int(min(nt))) + 1))
+            qg = _q(rng, B, None, H * g, D)
+            out_d = ls.gpu.attend_draft_gqa(0, qg, g)
+            out_v = None
+            if mt >= 1:
+                qgv = _q(rng, B, mt, H * g, D)
+                out_v = ls.gpu.attend_verify_gqa(0, qgv, g)
+            torch.cuda.synchronize()
+            for r in range(g):
+                heads = [h * g + r for h in range(H)]
+                ls._cmp_out(out_d[:, heads], orc.attend_draft(0, qg[:, heads].cpu().numpy()),
+                            f"gqa draft g={g} r={r}")
+                if out_v is not None:
+                    ls._cmp_out(out_v[:, :, heads],
+                                orc.attend_verify(0, qgv[:, :, heads].contiguous().cpu().numpy()),
+                                f"gqa verify g={g} m={mt} r={r}")
+        elif op == "dev":   # device-mode draft and verify, the counters back on the host after
+            if any(int(a) + int(t) == 0 for a, t in zip(nq, nt)):
+                continue
+            m = int(rng.integers(0, min(gmax + 1, int(min(nt))) + 1))
+            qd = _q(rng, B, None, H, D)
+            od = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+            ls.gpu.to_device_state()
+            ls.gpu.attend_draft_dev(0, qd, od)
+            if m >= 1:
+                qv = _q(rng, B, m, H, D)
+                ov = torch.empty((B, m, H, D), dtype=torch.float32, device="cuda")
+                ls.gpu.attend_verify_dev(0, qv, ov)
+            assert ls.gpu.from_device_state() == 0
+            torch.cuda.synchronize()
+            ls._cmp_out(od, orc.attend_draft(0, ls._host_heads(qd, 1)), "device draft")
+            if m >= 1:
+                ls._cmp_out(ov, orc.attend_verify(0, ls._host_heads(qv, 2)), "device verify")
+            ls.check_state(0)
         elif op == "rollback":
             ls.rollback(0, [int(rng.integers(0, int(t) + 1)) for t in nt])
         else:  # flush, unless a sequence that would be selected has no room left
