@@ -49,7 +49,8 @@ def test_random_rounds_match_the_oracle(seed):
     off = int(rng.choice([0, 8]))
     m16 = bool(rng.integers(0, 2))
     dist = str(rng.choice(["normal", "student_t3"]))
-    T = G * int(rng.integers(2, 7))
+    # up to 70 groups: with many (sequence, head) pairs a worker then takes several groups
+    T = G * int(rng.choice([2, 3, 4, 6, 16, 40, 70]))
     log(f"case: random seed {seed}: D={D} B={B} H={H} gamma_max={gmax} off={off} "
         f"fp16 metadata {m16} keys {dist} max_ctx {T}")
     ls = Lockstep(1, B, H, D, T, gmax, draft_offset=off, tag=f"rand{seed}", meta_fp16=m16)
