@@ -126,3 +126,24 @@ def test_first_token_follows_target_distribution_on_gpu():
     chi2 = float((((obs - N * p0) ** 2) / (N * p0)).sum())
     log(f"spec first-token chi2 {chi2:.1f} (df {V - 1}), rejection rate {float((n < gamma).mean()):.3f}")
     assert chi2 < 42.0, (chi2, obs, N * p0)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_match_oracle(seed):
+    """Seeded random batch (1 .. 64), gamma (1 .. 15), vocabulary (1 .. ~70000, log-uniform, so
+    most are ragged in the 4096-token parts), logit spread and draft noise; decisions exact away
+    from the oracle's 1e-5 margin, valid everywhere."""
+    rng = np.random.default_rng(9000 + seed)
+    B, gamma = int(rng.integers(1, 65)), int(rng.integers(1, 16))
+    V = int(np.exp(rng.uniform(0, np.log(70000))))
+    spread, noise = float(rng.choice([2.0, 3.0, 4.0])), float(rng.choice([0.5, 1.0, 2.0]))
+    log(f"case: spec accept random seed {seed}: B={B} gamma={gamma} V={V} spread={spread} "
+        f"noise={noise}")
+    t, d, x, u = case(9100 + seed, B, gamma, V, spread=spread, noise=noise)
+    n_g, nxt_g = run_gpu(t, d, x, u)
+    n_o, nxt_o, mg = oracle.spec_accept(t, d, x, u)
+    close = mg < 1e-5
+    bad = ~close & ((n_g != n_o) | (nxt_g != nxt_o))
+    log(f"random{seed}: near-boundary {int(close.sum())} of {B}, mismatches {int(bad.sum())}")
+    assert not bad.any(), (np.nonzero(bad)[0][:5], n_g[bad][:5], n_o[bad][:5])
+    assert ((n_g >= 0) & (n_g <= gamma)).all() and ((nxt_g >= 0) & (nxt_g < V)).all()
