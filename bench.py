@@ -34,9 +34,26 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention µs/step and HBM GB/s (draft & verify) at 32k/128k ctx"
 PEAK_HBM_GBS = 8000.0
-CPU_SAMPLE_HEADS = 16   # heads of layer 0 in the CPU-oracle sample
+CPU_SAMPLE_HEADS = 16   # heads of layer 0 in the CPU-oracle sample, at least
+
+
+def host_cpus():
+    """(CPUs this process may run on, CPUs the OS reports)."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return aff, os.cpu_count() or aff
+
+
+def cpu_sample_heads(threads, H):
+    """Heads in the oracle sample: at least CPU_SAMPLE_HEADS, and one per thread (up to H)."""
+    return max(1, min(H, max(CPU_SAMPLE_HEADS, threads)))
 G = 128
-KERNEL_SRC = os.path.join(ROOT, "hierarchical_quantized_kv_amd", "csrc", "qs_kernels.hip")
+# device sources of the cache's kernels (the traffic figures are tied to their hash)
+KERNEL_SRCS = [os.path.join(ROOT, "hierarchical_quantized_kv_amd", "csrc", f) for f in (
+    "qs_args.h", "qs_device.h", "qs_attn_host.hip", "qs_attn_app.hip", "qs_attn_dev.hip",
+    "qs_attn_gqa.hip", "qs_quant.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 # HBM byte counters of rocprofv3, scaled by what they read for a plain device copy of known size
 # (FETCH_SIZE counts half of the bytes a copy kernel reads; WRITE_SIZE counts them all).
@@ -107,9 +124,9 @@ def main():
                     help="skip the fp16-metadata comparison (meta16: null)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replayed step (graph_step: null)")
-    ap.add_argument("--cpu-threads", type=int, default=16,
-                    help="host threads of the second, all-cores oracle timing (at most the "
-                         "host's CPU count)")
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="host threads of the second, all-cores oracle timing (default: the "
+                         "CPUs this process may run on)")
     ap.add_argument("--flush-reps", type=int, default=4,
                     help="timed all-layer flushes (each quantizes one G-token half per head)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -135,6 +152,7 @@ def main():
     L = args.layers or cfg["layers"]
     H, D, ctx, gamma = cfg["heads"], cfg["D"], cfg["ctx"], cfg["gamma"]
     m = gamma + 1
+    cpu_threads = args.cpu_threads or host_cpus()[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     max_ctx = ctx + 16 * G
@@ -179,7 +197,7 @@ def main():
         e1.record(stream)
         pf_ev.append((e0, e1, prefill_bytes(ctx + 64, H, D)))
         if layer == 0 and not args.no_cpu_baseline:
-            hs = list(range(CPU_SAMPLE_HEADS))
+            hs = list(range(cpu_sample_heads(cpu_threads, H)))
             cpu_inputs = (k[:, :, hs].cpu().numpy(), v[:, :, hs].cpu().numpy())
         del k, v
     torch.cuda.synchronize()
@@ -358,8 +376,7 @@ def main():
     cpu_all = None
     if cpu_inputs is not None:
         cpu = cpu_baseline(cpu_inputs, ctx, D, gamma, threads=1)
-        cpu_all = cpu_baseline(cpu_inputs, ctx, D, gamma,
-                               threads=max(1, min(args.cpu_threads, os.cpu_count() or 1)))
+        cpu_all = cpu_baseline(cpu_inputs, ctx, D, gamma, threads=cpu_threads)
 
     traffic = load_traffic(args.config)
 
@@ -667,8 +684,11 @@ def measure_mixed_ceiling(torch, stream, out_mib=1024):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_profile_path(config):
@@ -782,6 +802,7 @@ def _oracle_round(k, v, ctx, D, gamma, heads, barrier=None):
     from hierarchical_quantized_kv_amd import synth
 
     H = len(heads)
+    k_all = k
     k, v = np.ascontiguousarray(k[:, :, heads]), np.ascontiguousarray(v[:, :, heads])
     c = OracleCache(1, 1, H, D, G, ctx + 16 * G, gamma)
     for pos in range(0, ctx, G):
@@ -790,9 +811,10 @@ def _oracle_round(k, v, ctx, D, gamma, heads, barrier=None):
     nt = 64 - gamma - 1
     m = gamma + 1
     c.append(0, k[:, ctx:ctx + nt], v[:, ctx:ctx + nt])
-    qd = [np.ascontiguousarray(synth.queries_host(1, None, CPU_SAMPLE_HEADS, D, 10 + j)[:, heads])
+    HS = k_all.shape[2]  # queries are drawn for all sampled heads, then split by thread
+    qd = [np.ascontiguousarray(synth.queries_host(1, None, HS, D, 10 + j)[:, heads])
           for j in range(gamma)]
-    qv = np.ascontiguousarray(synth.queries_host(1, m, CPU_SAMPLE_HEADS, D, 2)[:, :, heads])
+    qv = np.ascontiguousarray(synth.queries_host(1, m, HS, D, 2)[:, :, heads])
     if barrier is not None:
         barrier.wait()
     t0 = time.perf_counter()
@@ -818,7 +840,8 @@ def cpu_baseline(inputs, ctx, D, gamma, threads=1):
 
     oracle.build(force=False)
     k, v = inputs
-    H = CPU_SAMPLE_HEADS
+    H = k.shape[2]  # the sampled heads
+    threads = max(1, min(threads, H))
     nt = 64 - gamma - 1
     m = gamma + 1
     nb = sum(draft_bytes(ctx, nt + 1 + j, H, D) for j in range(gamma))
@@ -841,8 +864,9 @@ def cpu_baseline(inputs, ctx, D, gamma, threads=1):
     t_d = max(r[0] for r in res)
     t_v = max(r[1] for r in res)
     how = "single-threaded" if threads == 1 else f"{threads} host threads, heads dealt round-robin"
+    aff, ncpu = host_cpus()
     return {"value": round((nb + nb_v) / (t_d + t_v) / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "host_cpus_available": aff, "host_cpus_reported": ncpu, "kind": "oracle",
             "sample": f"layer 0, heads 0..{H - 1} of the same workload at ctx {ctx}: one "
                       f"speculation round = {gamma} draft calls ({t_d:.2f}s) + one {m}-query "
                       f"verify call ({t_v:.2f}s), fp64 oracle, {how}; GB/s = algorithmic bytes "

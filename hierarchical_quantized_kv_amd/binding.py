@@ -100,11 +100,12 @@ def lib():
     return _lib
 
 
-def _i32(a, n):
+def _i32(a, n, name="counts"):
     if a is None:
         return None
     arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
-    assert arr.shape[0] == n
+    if arr.shape[0] != n:
+        raise ValueError(f"{name}: expected {n} entries, got {arr.shape[0]}")
     return arr
 
 
@@ -165,31 +166,50 @@ class Cache:
         if st != QS_OK:
             raise QsError(st, f"{what}: {lib().qs_last_error(self._h).decode()}")
 
-    def _dev(self, t, dtype, name):
-        assert t.is_cuda and t.dtype == dtype and t.is_contiguous(), f"{name}: {t.dtype} {t.device}"
+    def _dev(self, t, dtype, name, shape=None):
+        """Device pointer of t after checking that it is a contiguous tensor of dtype (and of
+        shape, when given) on the arena's device; raises ValueError otherwise (the kernels
+        trust these sizes)."""
+        if not isinstance(t, self.torch.Tensor):
+            raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+        if t.device != self.arena.device:
+            raise ValueError(f"{name}: on {t.device}, the cache's arena is on {self.arena.device}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
         return ctypes.c_void_p(t.data_ptr())
 
+    def _kv(self, k, v, hq=None):
+        """k and v: fp16 [B][n][H][D] of the same shape; returns n."""
+        if not isinstance(k, self.torch.Tensor) or k.dim() != 4:
+            raise ValueError("k: expected a 4-d tensor [B][n][H][D]")
+        n = k.shape[1]
+        shape = (self.B, n, self.H if hq is None else hq, self.D)
+        return n, self._dev(k, self.torch.float16, "k", shape), self._dev(v, self.torch.float16, "v", shape)
+
+    def _out(self, out, shape, device):
+        if out is None:
+            return self.torch.empty(shape, dtype=self.torch.float32, device=device)
+        return out
+
     def append(self, layer, k, v, n=None, stream=None):
-        torch = self.torch
-        assert k.shape == v.shape and k.dim() == 4 and k.shape[0] == self.B
-        assert tuple(k.shape[2:]) == (self.H, self.D)
+        n_max, pk, pv = self._kv(k, v)
         nn = _i32(n, self.B)
-        self._check(lib().qs_append(self._h, layer, self._dev(k, torch.float16, "k"),
-                                    self._dev(v, torch.float16, "v"), k.shape[1], _ptr_i32(nn),
+        self._check(lib().qs_append(self._h, layer, pk, pv, n_max, _ptr_i32(nn),
                                     self._stream(stream)), "qs_append")
 
     def prefill(self, layer, k, v, n=None, stream=None):
         """Bulk "quantize once" of a prompt: k, v fp16 [B][n_max][H][D]."""
-        torch = self.torch
-        assert k.shape == v.shape and k.dim() == 4 and k.shape[0] == self.B
-        assert tuple(k.shape[2:]) == (self.H, self.D)
+        n_max, pk, pv = self._kv(k, v)
         nn = _i32(n, self.B)
-        self._check(lib().qs_prefill(self._h, layer, self._dev(k, torch.float16, "k"),
-                                     self._dev(v, torch.float16, "v"), k.shape[1], _ptr_i32(nn),
+        self._check(lib().qs_prefill(self._h, layer, pk, pv, n_max, _ptr_i32(nn),
                                      self._stream(stream)), "qs_prefill")
 
     def rollback(self, layer, n_drop):
-        nd = _i32(n_drop, self.B)
+        nd = _i32(n_drop, self.B, "n_drop")
         self._check(lib().qs_rollback(self._h, layer, _ptr_i32(nd)), "qs_rollback")
 
     def flush(self, layer=-1, min_tail=None, stream=None):
@@ -200,73 +220,77 @@ class Cache:
 
     def attend_draft(self, layer, q, sm_scale=1.0, out=None, stream=None):
         torch = self.torch
-        assert tuple(q.shape) == (self.B, self.H, self.D)
-        if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        self._check(lib().qs_attend_draft(self._h, layer, self._dev(q, torch.float16, "q"),
-                                          float(sm_scale), self._dev(out, torch.float32, "out"),
+        shape = (self.B, self.H, self.D)
+        pq = self._dev(q, torch.float16, "q", shape)
+        out = self._out(out, shape, q.device)
+        self._check(lib().qs_attend_draft(self._h, layer, pq, float(sm_scale),
+                                          self._dev(out, torch.float32, "out", shape),
                                           self._stream(stream)), "qs_attend_draft")
         return out
 
+    def _verify_q(self, q, hq=None):
+        if not isinstance(q, self.torch.Tensor) or q.dim() != 4:
+            raise ValueError("q: expected a 4-d tensor [B][m][H][D]")
+        shape = (self.B, q.shape[1], self.H if hq is None else hq, self.D)
+        return shape, self._dev(q, self.torch.float16, "q", shape)
+
     def attend_verify(self, layer, q, sm_scale=1.0, out=None, stream=None):
         torch = self.torch
-        assert q.dim() == 4 and q.shape[0] == self.B and tuple(q.shape[2:]) == (self.H, self.D)
-        if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        self._check(lib().qs_attend_verify(self._h, layer, self._dev(q, torch.float16, "q"),
-                                           q.shape[1], float(sm_scale),
-                                           self._dev(out, torch.float32, "out"),
+        shape, pq = self._verify_q(q)
+        out = self._out(out, shape, q.device)
+        self._check(lib().qs_attend_verify(self._h, layer, pq, shape[1], float(sm_scale),
+                                           self._dev(out, torch.float32, "out", shape),
                                            self._stream(stream)), "qs_attend_verify")
         return out
 
     def attend_draft_gqa(self, layer, q, g, sm_scale=1.0, out=None, stream=None):
         """Grouped queries: q fp16 [B][H*g][D] (query head h*g + r reads cached head h)."""
         torch = self.torch
-        assert tuple(q.shape) == (self.B, self.H * g, self.D)
-        if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        self._check(lib().qs_attend_draft_gqa(self._h, layer, self._dev(q, torch.float16, "q"), g,
-                                              float(sm_scale), self._dev(out, torch.float32, "out"),
+        g = int(g)
+        shape = (self.B, self.H * g, self.D)
+        pq = self._dev(q, torch.float16, "q", shape)
+        out = self._out(out, shape, q.device)
+        self._check(lib().qs_attend_draft_gqa(self._h, layer, pq, g, float(sm_scale),
+                                              self._dev(out, torch.float32, "out", shape),
                                               self._stream(stream)), "qs_attend_draft_gqa")
         return out
 
     def attend_verify_gqa(self, layer, q, g, sm_scale=1.0, out=None, stream=None):
         """Grouped queries: q fp16 [B][m][H*g][D]."""
         torch = self.torch
-        assert q.dim() == 4 and q.shape[0] == self.B and tuple(q.shape[2:]) == (self.H * g, self.D)
-        if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        self._check(lib().qs_attend_verify_gqa(self._h, layer, self._dev(q, torch.float16, "q"),
-                                               q.shape[1], g, float(sm_scale),
-                                               self._dev(out, torch.float32, "out"),
+        g = int(g)
+        shape, pq = self._verify_q(q, self.H * g)
+        out = self._out(out, shape, q.device)
+        self._check(lib().qs_attend_verify_gqa(self._h, layer, pq, shape[1], g, float(sm_scale),
+                                               self._dev(out, torch.float32, "out", shape),
                                                self._stream(stream)), "qs_attend_verify_gqa")
         return out
 
     def append_attend_draft(self, layer, k, v, q, n=None, sm_scale=1.0, out=None, stream=None):
         """append(layer, k, v, n) then attend_draft(layer, q), fused into one launch pair."""
         torch = self.torch
-        assert k.shape == v.shape and k.dim() == 4 and k.shape[0] == self.B
-        assert tuple(k.shape[2:]) == (self.H, self.D) and tuple(q.shape) == (self.B, self.H, self.D)
-        if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        n_max, pk, pv = self._kv(k, v)
+        shape = (self.B, self.H, self.D)
+        pq = self._dev(q, torch.float16, "q", shape)
+        out = self._out(out, shape, q.device)
         nn = _i32(n, self.B)
         self._check(lib().qs_append_attend_draft(
-            self._h, layer, self._dev(k, torch.float16, "k"), self._dev(v, torch.float16, "v"),
-            k.shape[1], _ptr_i32(nn), self._dev(q, torch.float16, "q"), float(sm_scale),
-            self._dev(out, torch.float32, "out"), self._stream(stream)), "qs_append_attend_draft")
+            self._h, layer, pk, pv, n_max, _ptr_i32(nn), pq, float(sm_scale),
+            self._dev(out, torch.float32, "out", shape), self._stream(stream)),
+            "qs_append_attend_draft")
         return out
 
     def append_attend_verify(self, layer, k, v, q, sm_scale=1.0, out=None, stream=None):
         """append(layer, k, v) of the m verified tokens then attend_verify(layer, q), fused."""
         torch = self.torch
-        assert q.dim() == 4 and q.shape[0] == self.B and tuple(q.shape[2:]) == (self.H, self.D)
-        assert k.shape == v.shape == q.shape
-        if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        shape, pq = self._verify_q(q)
+        pk = self._dev(k, torch.float16, "k", shape)
+        pv = self._dev(v, torch.float16, "v", shape)
+        out = self._out(out, shape, q.device)
         self._check(lib().qs_append_attend_verify(
-            self._h, layer, self._dev(k, torch.float16, "k"), self._dev(v, torch.float16, "v"),
-            self._dev(q, torch.float16, "q"), q.shape[1], float(sm_scale),
-            self._dev(out, torch.float32, "out"), self._stream(stream)), "qs_append_attend_verify")
+            self._h, layer, pk, pv, pq, shape[1], float(sm_scale),
+            self._dev(out, torch.float32, "out", shape), self._stream(stream)),
+            "qs_append_attend_verify")
         return out
 
     def state(self, layer):
@@ -290,20 +314,16 @@ class Cache:
         return int(err[0])
 
     def append_dev(self, layer, k, v, stream=None):
-        torch = self.torch
-        assert k.shape == v.shape and k.dim() == 4 and k.shape[0] == self.B
-        assert tuple(k.shape[2:]) == (self.H, self.D)
-        self._check(lib().qs_append_dev(self._h, layer, self._dev(k, torch.float16, "k"),
-                                        self._dev(v, torch.float16, "v"), k.shape[1],
-                                        self._stream(stream)), "qs_append_dev")
+        n_max, pk, pv = self._kv(k, v)
+        self._check(lib().qs_append_dev(self._h, layer, pk, pv, n_max, self._stream(stream)),
+                    "qs_append_dev")
 
     def rollback_dev(self, layer, n, sub=None, stream=None):
         """Drops n - sub[b] tail tokens of each sequence b (sub: device int32 [B] or None; it
         must keep its values until the rollback is committed)."""
         p = None
         if sub is not None:
-            assert tuple(sub.shape) == (self.B,)
-            p = self._dev(sub, self.torch.int32, "sub")
+            p = self._dev(sub, self.torch.int32, "sub", (self.B,))
         self._check(lib().qs_rollback_dev(self._h, layer, int(n), p, self._stream(stream)),
                     "qs_rollback_dev")
 
@@ -316,18 +336,17 @@ class Cache:
 
     def attend_draft_dev(self, layer, q, out, sm_scale=1.0, stream=None):
         torch = self.torch
-        assert tuple(q.shape) == (self.B, self.H, self.D) and out.shape == q.shape
-        self._check(lib().qs_attend_draft_dev(self._h, layer, self._dev(q, torch.float16, "q"),
-                                              float(sm_scale), self._dev(out, torch.float32, "out"),
+        shape = (self.B, self.H, self.D)
+        self._check(lib().qs_attend_draft_dev(self._h, layer, self._dev(q, torch.float16, "q", shape),
+                                              float(sm_scale),
+                                              self._dev(out, torch.float32, "out", shape),
                                               self._stream(stream)), "qs_attend_draft_dev")
 
     def attend_verify_dev(self, layer, q, out, sm_scale=1.0, stream=None):
         torch = self.torch
-        assert q.dim() == 4 and q.shape[0] == self.B and tuple(q.shape[2:]) == (self.H, self.D)
-        assert out.shape == q.shape
-        self._check(lib().qs_attend_verify_dev(self._h, layer, self._dev(q, torch.float16, "q"),
-                                               q.shape[1], float(sm_scale),
-                                               self._dev(out, torch.float32, "out"),
+        shape, pq = self._verify_q(q)
+        self._check(lib().qs_attend_verify_dev(self._h, layer, pq, shape[1], float(sm_scale),
+                                               self._dev(out, torch.float32, "out", shape),
                                                self._stream(stream)), "qs_attend_verify_dev")
 
     # ---- views of the arena (layout of include/quantspec.h), for inspection -------------
@@ -373,20 +392,31 @@ def spec_accept(target_logits, draft_logits, draft_tokens, uniforms, workspace=N
                                (draft_logits, torch.float32, (B, gamma, V), "draft_logits"),
                                (draft_tokens, torch.int32, (B, gamma), "draft_tokens"),
                                (uniforms, torch.float32, (B, gamma + 1), "uniforms")):
-        assert t.is_cuda and t.dtype == dt and t.is_contiguous() and tuple(t.shape) == shape, name
+        if not (t.is_cuda and t.dtype == dt and t.is_contiguous() and tuple(t.shape) == shape):
+            raise ValueError(f"{name}: expected a contiguous {dt} device tensor of shape {shape}, "
+                             f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+        if t.device != target_logits.device:
+            raise ValueError(f"{name}: on {t.device}, target_logits on {target_logits.device}")
     need = spec_workspace_bytes(B, gamma, V)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=target_logits.device)
+    elif not (workspace.is_cuda and workspace.is_contiguous()
+              and workspace.device == target_logits.device):
+        raise ValueError("workspace: expected a contiguous device tensor on "
+                         f"{target_logits.device}")
     n = torch.empty(B, dtype=torch.int32, device=target_logits.device) if n_out is None else n_out
     nxt = (torch.empty(B, dtype=torch.int32, device=target_logits.device) if next_out is None
            else next_out)
     for t, name in ((n, "n_out"), (nxt, "next_out")):
-        assert t.is_cuda and t.dtype == torch.int32 and t.is_contiguous() and t.numel() == B, name
+        if not (t.is_cuda and t.dtype == torch.int32 and t.is_contiguous() and t.numel() == B
+                and t.device == target_logits.device):
+            raise ValueError(f"{name}: expected a contiguous int32 tensor of {B} entries on "
+                             f"{target_logits.device}")
     s = stream if stream is not None else torch.cuda.current_stream()
     P = ctypes.c_void_p
     st = lib().qs_spec_accept(P(target_logits.data_ptr()), P(draft_logits.data_ptr()),
                               P(draft_tokens.data_ptr()), P(uniforms.data_ptr()), B, gamma, V,
-                              P(workspace.data_ptr()), workspace.numel(), P(n.data_ptr()),
+                              P(workspace.data_ptr()), workspace.numel() * workspace.element_size(), P(n.data_ptr()),
                               P(nxt.data_ptr()), P(s.cuda_stream))
     if st != QS_OK:
         raise QsError(st, "qs_spec_accept")

@@ -1,4 +1,9 @@
-// qs_kernels.hip -- HIP kernels for gfx950 (MI355X) of the hierarchical INT8 KV cache.
+#pragma once
+
+// qs_device.h -- device code of the hierarchical INT8 KV cache for gfx950 (MI355X): the kernel
+// templates and their helpers.  Each launcher translation unit (qs_attn_*.hip, qs_quant.hip)
+// instantiates the kernels it launches, so the units compile in parallel.
+//
 //
 // Kernels (one wave64 per work item unless noted):
 //   append_kernel   fp16 rows -> tail ring slots
@@ -1416,34 +1421,6 @@ __global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
     flush_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, (blk - NK) * kFlushSlice, lds);
 }
 
-// ------------------------------------------------------------------------------------------
-// Device-mode commit: the pending operations of a layer, then for a flush its counter update.
-// Runs after every kernel that read the old counters (stream order); the same checks as the
-// host verbs decide, and a failing operation leaves the counters and sets its error bit.
-// ------------------------------------------------------------------------------------------
-
-__global__ __launch_bounds__(256) void state_kernel(const StateArgs a) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.nl * a.B) return;
-  const int b = idx % a.B, layer = a.l0 + idx / a.B;
-  int32_t* st = a.state + ((size_t)layer * a.B + b) * kStateInts;
-  int32_t bad = 0;
-  int nq = st[0], head = st[2];
-  int nt = apply_pending(st[1], a.pend, b, &bad);
-  if (a.op == 1 && nt >= a.thr) {
-    if (nq + a.G <= a.T) {
-      nq += a.G;
-      nt -= a.G;
-      head ^= a.G;
-    } else {
-      bad |= kDevErrFlush;
-    }
-  }
-  st[0] = nq;
-  st[1] = nt;
-  st[2] = head;
-  if (bad) atomicOr(a.err, bad);
-}
 
 // ------------------------------------------------------------------------------------------
 // Launchers (called by the C ABI in qs_api.cpp)
@@ -1511,53 +1488,6 @@ AppendArgsN<NB> narrow(const AppendArgs& f) {
   return a;
 }
 
-template <int D, int NB>
-void launch_append_n(const AppendArgs& f, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((append_kernel<D, NB>), grid, dim3(256), 0, st, narrow<NB>(f));
-}
-
-template <int D>
-void launch_append_d(const AppendArgs& a, dim3 grid, hipStream_t st) {
-  switch (batch_bucket(a.B)) {
-    case 1: launch_append_n<D, 1>(a, grid, st); break;
-    case 8: launch_append_n<D, 8>(a, grid, st); break;
-    default: launch_append_n<D, QS_MAX_BATCH>(a, grid, st); break;
-  }
-}
-
-hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st) {
-  const long long rows = (long long)a.B * a.n_rows * a.H;
-  const long long threads = rows * (D / 8);
-  if (threads == 0) return hipSuccess;
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  if (D == 128) launch_append_d<128>(a, grid, st);
-  else launch_append_d<64>(a, grid, st);
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream_t st) {
-  if (max_groups <= 0) return hipSuccess;
-  const int per_head = D / kFlushSlice + kGroup / kFlushSlice;
-  const dim3 grid(a.H * per_head, max_groups, a.B);
-  if (D == 128) hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(64), 0, st, a);
-  else hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(64), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_state(const StateArgs& a, hipStream_t st) {
-  const int n = a.nl * a.B;
-  hipLaunchKernelGGL(state_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st) {
-  const int per_head = D / kFlushSlice + kGroup / kFlushSlice;
-  const dim3 grid(a.H * per_head, a.n_sel, n_layers);
-  if (D == 128) hipLaunchKernelGGL(flush_kernel<128>, grid, dim3(64), 0, st, a);
-  else hipLaunchKernelGGL(flush_kernel<64>, grid, dim3(64), 0, st, a);
-  return hipGetLastError();
-}
-
 template <int D, bool DRAFT, int MODE, bool M16>
 const void* attn_fn(int bucket) {
   switch (bucket) {
@@ -1571,35 +1501,6 @@ template <int MODE, bool M16>
 const void* attn_fn_dm(int D, bool draft, int bucket) {
   return D == 128 ? (draft ? attn_fn<128, true, MODE, M16>(bucket) : attn_fn<128, false, MODE, M16>(bucket))
                   : (draft ? attn_fn<64, true, MODE, M16>(bucket) : attn_fn<64, false, MODE, M16>(bucket));
-}
-template <bool M16>
-const void* attn_fn_m(int D, bool draft, int bucket, int mode) {
-  return mode == kModeDev      ? attn_fn_dm<kModeDev, M16>(D, draft, bucket)
-         : mode == kModeAppend ? attn_fn_dm<kModeAppend, M16>(D, draft, bucket)
-         : mode == kModeGqa    ? attn_fn_dm<kModeGqa, M16>(D, draft, bucket)
-                               : attn_fn_dm<kModeHost, M16>(D, draft, bucket);
-}
-
-// Work-item slots of one attention pass on the current device: compute units times the
-// one-wave workgroups of that kernel a compute unit holds at once (cached per device).
-int attention_slots(int D, bool draft, int B, int mode, bool meta16) {
-  constexpr int kMaxDev = 64;
-  // filled on first use; concurrent callers at worst compute the same value twice
-  static std::atomic<int> cache[kMaxDev][2][2][2][4][3];
-  int id = 0;
-  if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 3) return 0;
-  const int bucket = batch_bucket(B);
-  std::atomic<int>& slot = cache[id][meta16][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
-  const int known = slot.load(std::memory_order_relaxed);
-  if (known > 0) return known;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess) return 0;
-  const void* fn = meta16 ? attn_fn_m<true>(D, draft, bucket, mode)
-                          : attn_fn_m<false>(D, draft, bucket, mode);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
-  const int n = cus * per_cu;
-  slot.store(n, std::memory_order_relaxed);
-  return n;
 }
 
 template <int D, bool DRAFT, int NB, int MODE, class Full>
@@ -1631,19 +1532,6 @@ hipError_t launch_attention_m(const Full& a, int D, bool draft, hipStream_t st) 
   if (D == 128)
     return draft ? launch_attention_d<128, true, MODE>(a, st) : launch_attention_d<128, false, MODE>(a, st);
   return draft ? launch_attention_d<64, true, MODE>(a, st) : launch_attention_d<64, false, MODE>(a, st);
-}
-
-hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st) {
-  return launch_attention_m<kModeHost>(a, D, draft, st);
-}
-hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStream_t st) {
-  return launch_attention_m<kModeDev>(a, D, draft, st);
-}
-hipError_t launch_attention_app(const AttnAppArgs& a, int D, bool draft, hipStream_t st) {
-  return launch_attention_m<kModeAppend>(a, D, draft, st);
-}
-hipError_t launch_attention_gqa(const AttnGqaArgs& a, int D, bool draft, hipStream_t st) {
-  return launch_attention_m<kModeGqa>(a, D, draft, st);
 }
 
 }  // namespace qs

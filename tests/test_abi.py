@@ -202,3 +202,50 @@ def test_spec_accept_validation_before_any_launch(lib):
         assert call(P, P, P, P, b_, g_, v_, P, 1 << 20, P, P, None) == binding.QS_ERR_INVALID_ARG
     assert call(P, P, P, P, 2, 6, 100, P, ws - 1, P, P, None) == binding.QS_ERR_BUFFER
 
+
+
+def _unbound_cache(B=2, H=4, D=64):
+    """A binding Cache object whose arena is a CPU tensor and which holds no library handle:
+    enough to exercise the binding's argument checks, which all run before any library call
+    (a call that passed them would reach the C library with host pointers, so none does)."""
+    import torch
+    c = binding.Cache.__new__(binding.Cache)
+    c.torch = torch
+    c.B, c.H, c.D, c.L, c.G = B, H, D, 1, G
+    c.arena = torch.empty(0, dtype=torch.uint8)
+    c._h = None
+    return c
+
+
+def test_binding_rejects_wrong_tensors_before_any_call():
+    import torch
+    c = _unbound_cache()
+    B, H, D = c.B, c.H, c.D
+    f16, f32 = torch.float16, torch.float32
+    q = torch.zeros(B, H, D, dtype=f16)
+    cases = [
+        ("wrong dtype", lambda: c.attend_draft(0, q.float())),
+        ("wrong shape", lambda: c.attend_draft(0, q[:, :2].contiguous())),
+        ("non-contiguous", lambda: c.attend_draft(0, torch.zeros(B, D, H, dtype=f16).transpose(1, 2))),
+        ("undersized out", lambda: c.attend_draft(0, q, out=torch.empty(B, H, D - 1, dtype=f32))),
+        ("out wrong dtype", lambda: c.attend_draft(0, q, out=torch.empty(B, H, D, dtype=f16))),
+        ("verify q 3-d", lambda: c.attend_verify(0, q)),
+        ("verify out", lambda: c.attend_verify(0, q[:, None].contiguous(),
+                                               out=torch.empty(B, 2, H, D, dtype=f32))),
+        ("gqa shape", lambda: c.attend_draft_gqa(0, torch.zeros(B, H * 3, D, dtype=f16), 2)),
+        ("append k/v differ", lambda: c.append(0, torch.zeros(B, 3, H, D, dtype=f16),
+                                                torch.zeros(B, 2, H, D, dtype=f16))),
+        ("append heads", lambda: c.append(0, torch.zeros(B, 3, H + 1, D, dtype=f16),
+                                           torch.zeros(B, 3, H + 1, D, dtype=f16))),
+        ("counts", lambda: c.append(0, torch.zeros(B, 3, H, D, dtype=f16),
+                                    torch.zeros(B, 3, H, D, dtype=f16), n=[1, 2, 3])),
+        ("fused verify k", lambda: c.append_attend_verify(
+            0, torch.zeros(B, 2, H, D, dtype=f16), torch.zeros(B, 2, H, D, dtype=f16),
+            torch.zeros(B, 3, H, D, dtype=f16))),
+        ("device out", lambda: c.attend_draft_dev(0, q, torch.empty(B, H, D + 1, dtype=f32))),
+        ("not a tensor", lambda: c.attend_draft(0, q.numpy())),
+    ]
+    for what, call in cases:
+        with pytest.raises(ValueError):
+            call()
+        assert c._h is None, what

@@ -1,8 +1,12 @@
 """GPU parity at the full sizes of the workloads (the launch configurations the benchmark times),
 checked on sampled heads / layers that the CPU oracle can afford.
 
-  * LWM-128k-shaped layer: 32 heads x 128, 131072 prefilled tokens, gamma = 6 round; the same
-    prefilled layer in both metadata formats.
+  * LWM-128k-shaped layer: 32 heads x 128, 131072 prefilled tokens, gamma = 6 round, with plain
+    queries and with queries x8 (a peaky softmax); the same prefilled layer in both metadata
+    formats.
+  * LWM-128k-shaped stack: all 32 layers of the 128k cache the benchmark times (4 x 8 GiB of
+    planes), every layer prefilled; a gamma = 6 round on every layer checked on layers 0 and 31
+    (sampled heads), then an all-layer flush and the planes of both layers bit-exact.
   * Llama-2-7B-32K-shaped stack: 32 layers, 32768 tokens, 64 rounds of gamma = 4 with
     Bernoulli(0.9) acceptance driving rollback and flush; outputs checked every 8th round on
     three layers, final planes of every layer checked bit-exact against the oracle's replay.
@@ -66,14 +70,62 @@ def test_lwm_128k_layer():
         dk, dv = dev_kv(4, 0, 1, 1, H, D, outliers=out, salt=s + 1)
         ls.append(0, dk, dv)
         ls.draft(0, dev_q((1, H, D), gen, D))
+    # a peaky softmax: the same cache, queries x8
+    ls.draft(0, (dev_q((1, H, D), gen, D).float() * 8).half())
     ls.rollback(0, [gamma])
     tk, tv = dev_kv(4, 0, 1, gamma + 1, H, D, outliers=out, salt=100)
     ls.append(0, tk, tv)
     ls.verify(0, dev_q((1, gamma + 1, H, D), gen, D))
+    ls.verify(0, (dev_q((1, gamma + 1, H, D), gen, D).float() * 8).half())
     ls.rollback(0, [3])
     ls.flush(0)
     ls.check_planes(0)
     log(f"128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
+def test_lwm_128k_32_layer_stack():
+    """The full 32-layer 128k arena: every layer prefilled, a gamma = 6 round on all layers
+    (outputs of layers 0 and 31 against the oracle on sampled heads), 64 more tokens so that
+    the all-layer flush quantizes a group of every layer at the far end of each plane section,
+    then the live planes, metadata and tail of layers 0 and 31 bit-exact."""
+    L, H, D, ctx, gamma = 32, 32, 128, 131072, 6
+    log("case: LWM-128k 32-layer stack, layers 0/31, heads 0/19/31 sampled")
+    ls = Lockstep(L, 1, H, D, ctx + 4 * G, gamma, heads=[0, 19, 31], layers=[0, L - 1],
+                  tag="128kx32")
+    outs = [synth.outlier_channels(H, D, synth.seed_for(4, l, "outlier")) for l in range(L)]
+    for l in range(L):
+        k, v = dev_kv(4, l, 1, ctx + 64, H, D, outliers=outs[l])
+        ls.prefill(l, k, v)
+        del k, v
+    torch.cuda.synchronize()
+    log("128kx32: prefill of 32 layers done")
+    gen = torch.Generator(device="cuda").manual_seed(4200)
+    for s in range(gamma):
+        for l in range(L):
+            dk, dv = dev_kv(4, l, 1, 1, H, D, outliers=outs[l], salt=300 + s)
+            ls.append(l, dk, dv)
+            q = dev_q((1, H, D), gen, D)
+            if s == gamma - 1:
+                q = (q.float() * 8).half()  # the last draft step with a peaky softmax
+            ls.draft(l, q) if l in ls.orc else ls.gpu.attend_draft(l, q)
+    ls.rollback(-1, [gamma])
+    for l in range(L):
+        tk, tv = dev_kv(4, l, 1, gamma + 1, H, D, outliers=outs[l], salt=400)
+        ls.append(l, tk, tv)
+        q = dev_q((1, gamma + 1, H, D), gen, D)
+        ls.verify(l, q) if l in ls.orc else ls.gpu.attend_verify(l, q)
+    ls.rollback(-1, [2])
+    for l in range(L):
+        tk, tv = dev_kv(4, l, 1, 64, H, D, outliers=outs[l], salt=500)
+        ls.append(l, tk, tv)
+    ls.flush(-1)
+    for l in ls.layers:
+        nq, nt, _ = ls.check_state(l)
+        assert int(nq[0]) == ctx + G and int(nt[0]) == 64 + (gamma + 1 - 2) + 64 - G
+        ls.check_planes(l)
+    ls.draft(L - 1, dev_q((1, H, D), gen, D))
+    log(f"128kx32: layers 0/31 bit-exact after the all-layer flush; max abs {ls.max_abs:.3e} "
+        f"max rel {ls.max_rel:.3e}")
 
 
 @pytest.mark.parametrize("meta_fp16", [False, True])
