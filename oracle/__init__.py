@@ -51,6 +51,10 @@ def lib():
         L.orc_dequant_full.restype = ctypes.c_double
         L.orc_dequant_upper.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float, i]
         L.orc_dequant_upper.restype = ctypes.c_double
+        L.orc_dequant_topk.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float, i, i]
+        L.orc_dequant_topk.restype = ctypes.c_double
+        L.orc_dequant16_topk.argtypes = [ctypes.c_uint8, ctypes.c_float, ctypes.c_float, i, i]
+        L.orc_dequant16_topk.restype = ctypes.c_double
         L.orc_float_to_half.argtypes = [ctypes.c_float]
         L.orc_float_to_half.restype = ctypes.c_uint16
         L.orc_meta16.argtypes = [ctypes.c_float, ctypes.c_float, P, P]
@@ -69,15 +73,19 @@ def lib():
         L.orc_rollback.argtypes = [P, i, P]
         L.orc_flush.argtypes = [P, i, i, P]
         L.orc_attend_draft.argtypes = [P, i, P, ctypes.c_double, P]
+        L.orc_attend_draft_bits.argtypes = [P, i, P, i, ctypes.c_double, P]
         L.orc_attend_verify.argtypes = [P, i, P, i, ctypes.c_double, P]
         L.orc_get_state.argtypes = [P, i, P, P, P]
         L.orc_read_codes.argtypes = [P, i, i, i, i, P]
         L.orc_set_lower_nibbles.argtypes = [P, i, i]
+        L.orc_set_low_bits.argtypes = [P, i, i, i]
+        L.orc_export_upper_split.argtypes = [P, i, P, P, P, P]
         L.orc_read_meta.argtypes = [P, i, i, i, P, P]
         L.orc_export_layer.argtypes = [P, i, P, P, P, P, P, P, P, P]
         for f in ("orc_append", "orc_prefill", "orc_spec_accept", "orc_rollback", "orc_flush", "orc_attend_draft",
                   "orc_attend_verify", "orc_get_state", "orc_read_codes", "orc_read_meta",
-                  "orc_export_layer", "orc_set_lower_nibbles"):
+                  "orc_export_layer", "orc_set_lower_nibbles", "orc_attend_draft_bits",
+                  "orc_set_low_bits", "orc_export_upper_split"):
             getattr(L, f).restype = i
         _lib = L
     return _lib
@@ -126,6 +134,14 @@ def dequant_full(c8: int, s: float, z: float) -> float:
 
 def dequant_upper(cu: int, s: float, z: float, off: int) -> float:
     return lib().orc_dequant_upper(int(cu), float(s), float(z), int(off))
+
+
+def dequant_topk(c8: int, s: float, z: float, k: int, off: int) -> float:
+    return lib().orc_dequant_topk(int(c8), float(s), float(z), int(k), int(off))
+
+
+def dequant16_topk(c8: int, s: float, b: float, k: int, off: int) -> float:
+    return lib().orc_dequant16_topk(int(c8), float(s), float(b), int(k), int(off))
 
 
 def float_to_half(x: float) -> int:
@@ -224,6 +240,16 @@ class OracleCache:
                     "attend_draft")
         return out
 
+    def attend_draft_bits(self, layer, q, bits, sm_scale=1.0):
+        """Draft pass on the top `bits` bits of every code (4: attend_draft; 8: the verify
+        dequantization)."""
+        q = _bits16(q)
+        assert q.shape == (self.B, self.H, self.D)
+        out = np.zeros((self.B, self.H, self.D), dtype=np.float32)
+        self._check(lib().orc_attend_draft_bits(self._h, layer, _ptr(q), int(bits), float(sm_scale),
+                                                _ptr(out)), "attend_draft_bits")
+        return out
+
     def attend_verify(self, layer, q, sm_scale=1.0):
         q = _bits16(q)
         assert q.shape[0] == self.B and q.shape[2:] == (self.H, self.D)
@@ -243,6 +269,23 @@ class OracleCache:
     def set_lower_nibbles(self, layer, value):
         """Test support: every stored code of `layer` gets lower nibble `value`."""
         self._check(lib().orc_set_lower_nibbles(self._h, layer, int(value)), "set_lower_nibbles")
+
+    def set_low_bits(self, layer, nbits, value):
+        """Test support: the low `nbits` bits of every stored code of `layer` become `value`."""
+        self._check(lib().orc_set_low_bits(self._h, layer, int(nbits), int(value)), "set_low_bits")
+
+    def export_upper_split(self, layer):
+        """The split-upper layout's 2-bit planes of one layer (orc_export_upper_split): top
+        bits and middle bits, keys [B][H][T][D/4] and values [B][H][NG][2][D][G/8]."""
+        B, H, T, D, G = self.B, self.H, self.T, self.D, self.G
+        NG = T // G
+        out = dict(tk=np.zeros((B, H, T, D // 4), np.uint8), mk=np.zeros((B, H, T, D // 4), np.uint8),
+                   tv=np.zeros((B, H, NG, 2, D, G // 8), np.uint8),
+                   mv=np.zeros((B, H, NG, 2, D, G // 8), np.uint8))
+        self._check(lib().orc_export_upper_split(self._h, layer, *(_ptr(out[k]) for k in
+                                                                    ("tk", "mk", "tv", "mv"))),
+                    "export_upper_split")
+        return out
 
     def codes(self, layer, b, h, which_v=False):
         out = np.zeros((self.T, self.D), dtype=np.uint8)

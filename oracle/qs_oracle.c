@@ -137,6 +137,23 @@ double orc_dequant_upper(uint8_t cu, float s, float z, int off) {
   return ((double)(16 * (int)cu + off) - (double)z) * (double)s;
 }
 
+/* A draft on the top k bits of the same 8-bit code, the verifier keeping all 8 ([R] "Editorial
+ * extensions", "Reading between the lines": the 4/8 split generalizes to the top k bits for the
+ * draft; the paper itself only uses k = 4).  The 8 - k dropped bits are replaced by off/16 of
+ * their range, which for off = 8 sets the highest dropped bit -- [G]'s "| 0x08" centering of
+ * the 4-bit draft, carried to every k -- and for k = 8 (nothing dropped) adds nothing.  So k = 4
+ * is the draft above and k = 8 the verify dequantization. */
+static int topk_code(uint8_t c8, int k, int off) {
+  const int drop = 8 - k;
+  return ((c8 >> drop) << drop) + ((off << drop) >> 4);
+}
+double orc_dequant_topk(uint8_t c8, float s, float z, int k, int off) {
+  return ((double)topk_code(c8, k, off) - (double)z) * (double)s;
+}
+double orc_dequant16_topk(uint8_t c8, float s, float b, int k, int off) {
+  return (double)s * (double)topk_code(c8, k, off) + (double)b;
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* Cache                                                                                     */
 /* ---------------------------------------------------------------------------------------- */
@@ -333,19 +350,23 @@ int orc_flush(orc_cache* c, int layer, int min_tail, int* flushed) {
 /* Attention                                                                                 */
 /* ---------------------------------------------------------------------------------------- */
 
-/* Dequantized code in the cache's metadata format: draft from the upper plane, else both. */
-static double dequant(const orc_cache* c, uint8_t c8, float s, float x, int draft) {
-  if (c->meta16)
-    return draft ? orc_dequant16_upper(upper_nibble(c8), s, x, c->off) : orc_dequant16_full(c8, s, x);
-  return draft ? orc_dequant_upper(upper_nibble(c8), s, x, c->off) : orc_dequant_full(c8, s, x);
+/* Dequantized code in the cache's metadata format from its top `bits` bits: 4 is the draft
+ * (the upper plane), 8 the verify pass (both planes), 1..7 a top-k-bit draft. */
+static double dequant(const orc_cache* c, uint8_t c8, float s, float x, int bits) {
+  if (bits == 8) return c->meta16 ? orc_dequant16_full(c8, s, x) : orc_dequant_full(c8, s, x);
+  if (bits == 4)
+    return c->meta16 ? orc_dequant16_upper(upper_nibble(c8), s, x, c->off)
+                     : orc_dequant_upper(upper_nibble(c8), s, x, c->off);
+  return c->meta16 ? orc_dequant16_topk(c8, s, x, bits, c->off)
+                   : orc_dequant_topk(c8, s, x, bits, c->off);
 }
 
 /* One query row of one (l, b, h): plain softmax attention in fp64 over the concatenation of
- *   - the nq quantized tokens, dequantized with the draft (upper plane) or verify (both planes)
- *     formula, and
+ *   - the nq quantized tokens, dequantized from the top `bits` bits of their codes (4: the draft
+ *     formula, upper plane; 8: the verify formula, both planes), and
  *   - the first n_vis tail tokens in logical order (fp16 -> exact).
  * out_d = sum_j exp(s_j - max) v_jd / sum_j exp(s_j - max),  s_j = sm_scale * q . k_j. */
-static void attend_row(const orc_cache* c, int l, int b, int h, const uint16_t* q, int draft,
+static void attend_row(const orc_cache* c, int l, int b, int h, const uint16_t* q, int bits,
                        int n_vis, double sm_scale, double* score, float* out) {
   const int D = c->D, G = c->G;
   const size_t r = lbh(c, l, b, h);
@@ -361,7 +382,7 @@ static void attend_row(const orc_cache* c, int l, int b, int h, const uint16_t* 
     double dot = 0.0;
     for (int d = 0; d < D; ++d) {
       float s = c->ks[(r * c->NG + g) * D + d], z = c->kz[(r * c->NG + g) * D + d];
-      dot += qd[d] * dequant(c, kc[d], s, z, draft);
+      dot += qd[d] * dequant(c, kc[d], s, z, bits);
     }
     score[t] = sm_scale * dot;
   }
@@ -382,7 +403,7 @@ static void attend_row(const orc_cache* c, int l, int b, int h, const uint16_t* 
     const double p = exp(score[t] - mx);
     const uint8_t* vc = &c->vc[(r * c->T + t) * D];
     const float s = c->vs[r * c->T + t], z = c->vz[r * c->T + t];
-    for (int d = 0; d < D; ++d) acc[d] += p * dequant(c, vc[d], s, z, draft);
+    for (int d = 0; d < D; ++d) acc[d] += p * dequant(c, vc[d], s, z, bits);
   }
   for (int j = 0; j < n_vis; ++j) {
     const double p = exp(score[nq + j] - mx);
@@ -394,20 +415,26 @@ static void attend_row(const orc_cache* c, int l, int b, int h, const uint16_t* 
   free(acc);
 }
 
-int orc_attend_draft(const orc_cache* c, int layer, const uint16_t* q, double sm_scale,
-                     float* out) {
-  if (!c || layer < 0 || layer >= c->L || !q || !out) return 1;
+/* Draft pass on the top `bits` bits of every code (1..8); orc_attend_draft is bits = 4. */
+int orc_attend_draft_bits(const orc_cache* c, int layer, const uint16_t* q, int bits,
+                          double sm_scale, float* out) {
+  if (!c || layer < 0 || layer >= c->L || !q || !out || bits < 1 || bits > 8) return 1;
   for (int b = 0; b < c->B; ++b)
     if (c->nq[layer * c->B + b] + c->nt[layer * c->B + b] == 0) return 3;
   double* score = (double*)malloc(((size_t)c->T + 2 * c->G) * sizeof(double));
   for (int b = 0; b < c->B; ++b)
     for (int h = 0; h < c->H; ++h) {
       const size_t row = ((size_t)b * c->H + h) * c->D;
-      attend_row(c, layer, b, h, &q[row], 1, c->nt[layer * c->B + b], sm_scale, score,
+      attend_row(c, layer, b, h, &q[row], bits, c->nt[layer * c->B + b], sm_scale, score,
                  &out[row]);
     }
   free(score);
   return 0;
+}
+
+int orc_attend_draft(const orc_cache* c, int layer, const uint16_t* q, double sm_scale,
+                     float* out) {
+  return orc_attend_draft_bits(c, layer, q, 4, sm_scale, out);
 }
 
 /* Query i of the verify block is the (nt - m + i)-th tail token itself: it sees the quantized
@@ -423,7 +450,7 @@ int orc_attend_verify(const orc_cache* c, int layer, const uint16_t* q, int m, d
       for (int h = 0; h < c->H; ++h) {
         const size_t row = (((size_t)b * m + i) * c->H + h) * c->D;
         const int n_vis = c->nt[layer * c->B + b] - m + i + 1;
-        attend_row(c, layer, b, h, &q[row], 0, n_vis, sm_scale, score, &out[row]);
+        attend_row(c, layer, b, h, &q[row], 8, n_vis, sm_scale, score, &out[row]);
       }
   free(score);
   return 0;
@@ -453,6 +480,28 @@ int orc_set_lower_nibbles(orc_cache* c, int layer, int value) {
         uint8_t* v = &c->vc[r * c->T * c->D + i];
         *k = (uint8_t)((*k & 0xF0) | value);
         *v = (uint8_t)((*v & 0xF0) | value);
+      }
+    }
+  return 0;
+}
+
+/* Test support: sets the low `nbits` bits (1..7) of every stored code of `layer` to `value`.
+ * With nbits = 8 - k and value = the k-bit draft's replacement of the dropped bits, every code
+ * equals its top-k reconstruction, so verify (m = 1) must equal the k-bit draft. */
+int orc_set_low_bits(orc_cache* c, int layer, int nbits, int value) {
+  if (!c || layer < 0 || layer >= c->L || nbits < 1 || nbits > 7 || value < 0 ||
+      value >= (1 << nbits))
+    return 1;
+  const int keep = 0xFF ^ ((1 << nbits) - 1);
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t r = lbh(c, layer, b, h);
+      const size_t n = (size_t)c->nq[layer * c->B + b] * c->D;
+      for (size_t i = 0; i < n; ++i) {
+        uint8_t* k = &c->kc[r * c->T * c->D + i];
+        uint8_t* v = &c->vc[r * c->T * c->D + i];
+        *k = (uint8_t)((*k & keep) | value);
+        *v = (uint8_t)((*v & keep) | value);
       }
     }
   return 0;
@@ -534,6 +583,68 @@ int orc_export_layer(const orc_cache* c, int layer, uint8_t* uk, uint8_t* lk, ui
         memcpy(&tail_k[bh * 2 * G * D], &c->tk[r * 2 * G * D], (size_t)2 * G * D * 2);
       if (tail_v)
         memcpy(&tail_v[bh * 2 * G * D], &c->tv[r * 2 * G * D], (size_t)2 * G * D * 2);
+    }
+  return 0;
+}
+
+/* The upper planes of the split-upper layout, in which the upper nibble C_U = 4 C_T + C_M of
+ * every code is stored as two 2-bit planes, the top bits C_T = C8 >> 6 and the middle bits
+ * C_M = (C8 >> 4) & 3, so that a 2-bit draft reads the C_T plane alone, a 4-bit draft both, and
+ * verify both with the lower plane (unchanged, as in orc_export_layer).  A plane row is made of
+ * 32-bit little-endian words, word w covering 16 entries 16w .. 16w+15 (channels of a key row,
+ * tokens of a value row); nibble e (bits 4e .. 4e+3) of a word holds
+ *   C_T plane: C_T(16w + e) in bits 4e+2 .. 4e+3, C_T(16w + 8 + e) in bits 4e .. 4e+1;
+ *   C_M plane: C_M(16w + e) in bits 4e .. 4e+1,   C_M(16w + 8 + e) in bits 4e+2 .. 4e+3.
+ * Shapes: key planes [B][H][T][D/4]; value planes [B][H][NG][2][D][G/8] (half e of group g,
+ * channel d: tokens gG + eG/2 + 16w + ...).  Rows past nq are zero. */
+static void split_word(const uint8_t* code16, size_t stride, uint8_t* tw, uint8_t* mw) {
+  uint32_t t = 0, m = 0;
+  for (int e = 0; e < 8; ++e) {
+    const uint8_t a = code16[(size_t)e * stride], b = code16[(size_t)(8 + e) * stride];
+    t |= (uint32_t)(a >> 6) << (4 * e + 2);
+    t |= (uint32_t)(b >> 6) << (4 * e);
+    m |= (uint32_t)((a >> 4) & 3) << (4 * e);
+    m |= (uint32_t)((b >> 4) & 3) << (4 * e + 2);
+  }
+  for (int j = 0; j < 4; ++j) {
+    tw[j] = (uint8_t)(t >> (8 * j));
+    mw[j] = (uint8_t)(m >> (8 * j));
+  }
+}
+
+int orc_export_upper_split(const orc_cache* c, int layer, uint8_t* tk, uint8_t* mk, uint8_t* tv,
+                           uint8_t* mv) {
+  if (!c || layer < 0 || layer >= c->L || !tk || !mk || !tv || !mv || c->D % 16 || c->G % 32)
+    return 1;
+  const int D = c->D, G = c->G, T = c->T, NG = c->NG;
+  for (int b = 0; b < c->B; ++b)
+    for (int h = 0; h < c->H; ++h) {
+      const size_t r = lbh(c, layer, b, h);
+      const size_t bh = (size_t)b * c->H + h;
+      const int nq = c->nq[layer * c->B + b];
+      for (int t = 0; t < T; ++t)
+        for (int w = 0; w < D / 16; ++w) {
+          const size_t o = (bh * T + t) * (D / 4) + 4 * w;
+          if (t < nq) {
+            split_word(&c->kc[(r * T + t) * D + 16 * w], 1, &tk[o], &mk[o]);
+          } else {
+            memset(&tk[o], 0, 4);
+            memset(&mk[o], 0, 4);
+          }
+        }
+      for (int g = 0; g < NG; ++g)
+        for (int e = 0; e < 2; ++e)
+          for (int d = 0; d < D; ++d)
+            for (int w = 0; w < G / 32; ++w) {
+              const int t0 = g * G + e * (G / 2) + 16 * w;
+              const size_t o = (((bh * NG + g) * 2 + e) * D + d) * (G / 8) + 4 * w;
+              if (t0 + 16 <= nq) {
+                split_word(&c->vc[(r * T + t0) * D + d], (size_t)D, &tv[o], &mv[o]);
+              } else {
+                memset(&tv[o], 0, 4);
+                memset(&mv[o], 0, 4);
+              }
+            }
     }
   return 0;
 }

@@ -42,6 +42,11 @@ void orc_quantize_group(const uint16_t* x, int n, int stride, float* s, float* z
 /* Dequantizations, in fp64. */
 double orc_dequant_full(uint8_t c8, float s, float z);
 double orc_dequant_upper(uint8_t cu, float s, float z, int off);
+/* Top-k-bit draft dequantization (k in 1..8) of an 8-bit code: the top k bits, the dropped
+ * 8 - k bits replaced by off/16 of their range; k = 4 equals orc_dequant_upper(c8 >> 4), k = 8
+ * orc_dequant_full.  The fp16-metadata form takes (s, b). */
+double orc_dequant_topk(uint8_t c8, float s, float z, int k, int off);
+double orc_dequant16_topk(uint8_t c8, float s, float b, int k, int off);
 
 /* fp32 -> binary16 bits, round to nearest even (overflow to infinity). */
 uint16_t orc_float_to_half(float x);
@@ -80,6 +85,9 @@ int orc_flush(orc_cache* c, int layer, int min_tail, int* flushed);
 /* q: fp16 bits [B][H][D]; out [B][H][D]. */
 int orc_attend_draft(const orc_cache* c, int layer, const uint16_t* q, double sm_scale,
                      float* out);
+/* The draft pass on the top `bits` (1..8) bits of every code; bits = 4 is orc_attend_draft. */
+int orc_attend_draft_bits(const orc_cache* c, int layer, const uint16_t* q, int bits,
+                          double sm_scale, float* out);
 /* q: fp16 bits [B][m][H][D]; out [B][m][H][D]. */
 int orc_attend_verify(const orc_cache* c, int layer, const uint16_t* q, int m, double sm_scale,
                       float* out);
@@ -92,6 +100,14 @@ int orc_get_state(const orc_cache* c, int layer, int* nq, int* nt, int* head);
 int orc_read_codes(const orc_cache* c, int layer, int b, int h, int which_v, uint8_t* codes);
 /* Test support: every stored code of `layer` gets lower nibble `value` (0..15). */
 int orc_set_lower_nibbles(orc_cache* c, int layer, int value);
+/* Test support: the low nbits (1..7) bits of every stored code of the layer set to value. */
+int orc_set_low_bits(orc_cache* c, int layer, int nbits, int value);
+/* The split-upper layout's planes of one layer: the top two bits and the middle two bits of
+ * every code, as 2-bit planes (key [B][H][T][D/4], value [B][H][T/G][2][D][G/8]); the word
+ * arrangement is documented at the definition.  The lower planes, metadata and tail are those
+ * of orc_export_layer. */
+int orc_export_upper_split(const orc_cache* c, int layer, uint8_t* tk, uint8_t* mk, uint8_t* tv,
+                           uint8_t* mv);
 int orc_read_meta(const orc_cache* c, int layer, int b, int h, float* kmeta, float* vmeta);
 
 /* Packs one layer into the arena layout of the library (per-layer slices of each section):

@@ -721,3 +721,145 @@ def test_meta16_attention_over_explicit_dequantized_cache():
             mask[i, : n - m + i + 1] = True
         ref = sdpa(f64(qv[0, :, h]), ka, va, mask)
         assert np.max(np.abs(outv[0, :, h] - ref)) < 1e-6
+
+
+# ------------------------------------------------------------------------------------------
+# Top-k-bit draft from the same 8-bit code (Pith review, "Editorial extensions", "Reading
+# between the lines"): the top k bits for the draft, all 8 for the verifier
+# ------------------------------------------------------------------------------------------
+
+def test_topk_dequant_reduces_to_the_4_bit_draft_and_to_verify():
+    """k = 4 is the upper-plane draft and k = 8 the verify dequantization, exactly, for every
+    code and both draft offsets, in both metadata formats."""
+    rng = np.random.default_rng(61)
+    for s, z in [(0.0123, 37.0), (1e-8, -5.0e7), (0.75, 255.0), (3.1, -12.0)]:
+        s = float(np.float32(s))
+        for off in (0, 8):
+            for c8 in range(256):
+                assert oracle.dequant_topk(c8, s, z, 4, off) == oracle.dequant_upper(c8 >> 4, s, z, off)
+                assert oracle.dequant_topk(c8, s, z, 8, off) == oracle.dequant_full(c8, s, z)
+                b = float(rng.standard_normal())
+                assert oracle.dequant16_topk(c8, s, b, 4, off) == oracle.dequant16_upper(c8 >> 4, s, b, off)
+                assert oracle.dequant16_topk(c8, s, b, 8, off) == oracle.dequant16_full(c8, s, b)
+
+
+@pytest.mark.parametrize("n", [64, 128])
+def test_topk_roundtrip_bounds(n):
+    """|x - x^k| <= (2^(7-k) + 1/2 + 2^-14) s with the centred offset (off = 8), and
+    <= (2^(8-k) - 1/2 + 2^-14) s without it; the bounds are nearly reached (a wrong shift or
+    offset breaks one side), and with off = 0 the reconstructions only grow with k (nesting)."""
+    rng = np.random.default_rng(62)
+    slack = 2.0 ** -14
+    worst = {k: 0.0 for k in range(1, 8)}
+    for x in random_groups(rng, 200, n):
+        s, z, c = oracle.quantize_group(x)
+        xf = x.astype(np.float64)
+        prev = None
+        for k in range(1, 9):
+            rec = np.array([oracle.dequant_topk(ci, s, z, k, 8) for ci in c])
+            e = np.max(np.abs(rec - xf)) / s
+            bound = (2.0 ** (7 - k) if k < 8 else 0.0) + 0.5 + slack
+            assert e <= bound, (k, e, bound)
+            if k < 8:
+                worst[k] = max(worst[k], e)
+            rec0 = np.array([oracle.dequant_topk(ci, s, z, k, 0) for ci in c])
+            assert np.max(np.abs(rec0 - xf)) / s <= 2.0 ** (8 - k) - 0.5 + slack
+            if prev is not None:
+                assert np.all(rec0 >= prev - 1e-12 * s)
+            prev = rec0
+    for k in range(1, 8):
+        assert worst[k] >= 0.9 * 2.0 ** (7 - k), (k, worst[k])
+
+
+@pytest.mark.parametrize("k,off,m16", [(2, 8, False), (2, 0, False), (3, 8, False), (2, 8, True),
+                                       (1, 8, False)])
+def test_topk_draft_equals_verify_when_the_low_bits_are_its_replacement(k, off, m16):
+    """With the low 8 - k bits of every stored code set to the k-bit draft's replacement
+    (off/16 of their range), every code is its own top-k reconstruction: a one-query verify then
+    equals the k-bit draft exactly; before, the k-bit draft equals itself on the untouched cache
+    (it reads only the top bits), and k = 4 / k = 8 equal the plain draft / verify."""
+    H, D = 3, 64
+    c = OracleCache(1, 2, H, D, G, 4 * G, 4, draft_offset=off, meta_fp16=m16)
+    kk, vv = synth.kv_host(2, 2 * G + 50, H, D, 141, 142)
+    c.prefill(0, kk, vv, n=[2 * G + 50, G + 7])
+    q = synth.queries_host(2, None, H, D, 143, gain=2.0)
+    assert np.array_equal(c.attend_draft_bits(0, q, 4), c.attend_draft(0, q))
+    assert np.array_equal(c.attend_draft_bits(0, q, 8), c.attend_verify(0, q[:, None])[:, 0])
+    before = c.attend_draft_bits(0, q, k)
+    rep = (off << (8 - k)) >> 4
+    c.set_low_bits(0, 8 - k, rep)
+    draft = c.attend_draft_bits(0, q, k)
+    assert np.array_equal(draft, before)
+    assert np.array_equal(draft, c.attend_verify(0, q[:, None])[:, 0])
+    c.set_low_bits(0, 8 - k, rep ^ 1)
+    assert not np.array_equal(c.attend_verify(0, q[:, None])[:, 0], draft)
+
+
+def test_topk_draft_over_explicit_dequantized_cache():
+    """The 2-bit draft equals SDPA over keys / values dequantized here (with the pinned scalar
+    dequant_topk) from the read-back codes and metadata, the fp16 tail appended."""
+    B, H, D = 1, 2, 64
+    c = OracleCache(1, B, H, D, G, 4 * G, 6)
+    k, v = synth.kv_host(B, 3 * G + 21, H, D, 151, 152, outliers=synth.outlier_channels(H, D, 153))
+    c.prefill(0, k, v)
+    q = synth.queries_host(B, None, H, D, 154, gain=1.5)
+    out = c.attend_draft_bits(0, q, 2, sm_scale=0.9)
+    dq = np.vectorize(lambda c8, s, z: oracle.dequant_topk(int(c8), float(s), float(z), 2, 8))
+    for h in range(H):
+        ck = c.codes(0, 0, h)[:3 * G]
+        cv = c.codes(0, 0, h, True)[:3 * G]
+        km, vm = c.meta(0, 0, h)
+        ks = np.repeat(km[:, :, 0], G, axis=0)[:3 * G]
+        kz = np.repeat(km[:, :, 1], G, axis=0)[:3 * G]
+        ka = np.concatenate([dq(ck, ks, kz), f64(k[0, 3 * G:, h])])
+        va = np.concatenate([dq(cv, vm[:3 * G, 0:1], vm[:3 * G, 1:2]), f64(v[0, 3 * G:, h])])
+        ref = sdpa(f64(q[0, h])[None], ka, va, scale=0.9)[0]
+        assert np.max(np.abs(out[0, h] - ref)) < 1e-6
+
+
+def test_upper_split_export_matches_the_codes():
+    """The 2-bit planes of the split-upper layout hold C8 >> 6 (top) and (C8 >> 4) & 3
+    (middle) of every code at the documented positions; 4 top + middle is the default layout's
+    upper nibble."""
+    B, H, D = 1, 2, 64
+    c = OracleCache(1, B, H, D, G, 3 * G, 4)
+    k, v = synth.kv_host(B, 2 * G + 9, H, D, 161, 162)
+    c.prefill(0, k, v)
+    sp = c.export_upper_split(0)
+    img = c.export_layer(0)
+    for h in range(H):
+        ck = c.codes(0, 0, h).astype(np.int64)[:2 * G]
+        cv = c.codes(0, 0, h, True).astype(np.int64)[:2 * G]
+        # keys: token rows of D/4 bytes
+        tw = sp["tk"][0, h, :2 * G].reshape(2 * G, D // 16, 4)
+        mw = sp["mk"][0, h, :2 * G].reshape(2 * G, D // 16, 4)
+        for wi in range(D // 16):
+            w_t = tw[:, wi].astype(np.uint32) @ (1 << (8 * np.arange(4, dtype=np.uint32)))
+            w_m = mw[:, wi].astype(np.uint32) @ (1 << (8 * np.arange(4, dtype=np.uint32)))
+            for e in range(8):
+                a, b = 16 * wi + e, 16 * wi + 8 + e
+                assert np.array_equal((w_t >> (4 * e + 2)) & 3, ck[:, a] >> 6)
+                assert np.array_equal((w_t >> (4 * e)) & 3, ck[:, b] >> 6)
+                assert np.array_equal((w_m >> (4 * e)) & 3, (ck[:, a] >> 4) & 3)
+                assert np.array_equal((w_m >> (4 * e + 2)) & 3, (ck[:, b] >> 4) & 3)
+        # values: channel rows of G/8 bytes per half group
+        for g in range(2):
+            for e2 in range(2):
+                tok = cv[g * G + e2 * G // 2: g * G + (e2 + 1) * G // 2]   # [G/2][D]
+                for d in range(D):
+                    tv = sp["tv"][0, h, g, e2, d].reshape(G // 32, 4).astype(np.uint32)
+                    mv = sp["mv"][0, h, g, e2, d].reshape(G // 32, 4).astype(np.uint32)
+                    wt = tv @ (1 << (8 * np.arange(4, dtype=np.uint32)))
+                    wm = mv @ (1 << (8 * np.arange(4, dtype=np.uint32)))
+                    for wi in range(G // 32):
+                        for e in range(8):
+                            a, b = 16 * wi + e, 16 * wi + 8 + e
+                            assert (wt[wi] >> (4 * e + 2)) & 3 == tok[a, d] >> 6
+                            assert (wt[wi] >> (4 * e)) & 3 == tok[b, d] >> 6
+                            assert (wm[wi] >> (4 * e)) & 3 == (tok[a, d] >> 4) & 3
+                            assert (wm[wi] >> (4 * e + 2)) & 3 == (tok[b, d] >> 4) & 3
+        # 4 top + middle = the upper nibble of the default layout
+        uk = img["uk"][0, h, :2 * G].astype(np.int64)
+        assert np.array_equal(uk & 15, ck[:, 0::2] >> 4)
+    # rows past nq are zero
+    assert not sp["tk"][:, :, 2 * G:].any() and not sp["tv"][:, :, 2:].any()
