@@ -53,7 +53,7 @@ G = 128
 # device sources of the cache's kernels (the traffic figures are tied to their hash)
 KERNEL_SRCS = [os.path.join(ROOT, "hierarchical_quantized_kv_amd", "csrc", f) for f in (
     "qs_args.h", "qs_device.h", "qs_attn_host.hip", "qs_attn_app.hip", "qs_attn_dev.hip",
-    "qs_attn_gqa.hip", "qs_quant.hip")]
+    "qs_attn_gqa.hip", "qs_attn_split_host.hip", "qs_attn_split_app.hip", "qs_quant.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 # HBM byte counters of rocprofv3, scaled by what they read for a plain device copy of known size
 # (FETCH_SIZE counts half of the bytes a copy kernel reads; WRITE_SIZE counts them all).
@@ -61,16 +61,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 # Kernel names (as rocprofv3 prints them) of the default step: the attention kernels of the
 # fused append + attend calls (mode 2); --no-fuse runs the mode-0 ones.
 # The last attention argument is the metadata format (false: fp32 (scale, zero-point)).
-KERNELS = {"draft": "attn_kernel<128, true, 1, 2, false>",
-           "verify": "attn_kernel<128, false, 1, 2, false>",
-           "combine": "combine_kernel<128, 1, 2>", "flush": "flush_kernel<128>",
+# The last attention argument is the upper-plane layout (0: one 4-bit plane).
+KERNELS = {"draft": "attn_kernel<128, true, 1, 2, false, 0>",
+           "verify": "attn_kernel<128, false, 1, 2, false, 0>",
+           "combine": "combine_kernel<128, 1, 2, 0>", "flush": "flush_kernel<128>",
            "prefill": "prefill_kernel<128>"}
 
 
 def kernel_names(fuse):
     mode = 2 if fuse else 0
-    return (f"attn_kernel<128, true, 1, {mode}, false>", f"attn_kernel<128, false, 1, {mode}, false>",
-            f"combine_kernel<128, 1, {mode}>")
+    return (f"attn_kernel<128, true, 1, {mode}, false, 0>",
+            f"attn_kernel<128, false, 1, {mode}, false, 0>", f"combine_kernel<128, 1, {mode}, 0>")
 
 CONFIGS = {
     3: dict(name="Llama-2-7B-32K-shaped full stack", layers=32, heads=32, D=128, ctx=32768,
@@ -79,11 +80,12 @@ CONFIGS = {
 }
 
 
-def draft_bytes(nq, nt, H, D, mb=8):
-    """Algorithmic bytes of one draft call: upper key/value planes + (s, z) metadata (mb bytes a
-    pair: 8 fp32, 4 fp16) of every quantized token-head, the fp16 tail, the query and the fp32
+def draft_bytes(nq, nt, H, D, mb=8, bits=4):
+    """Algorithmic bytes of one draft call: the key/value bits the draft reads (the upper
+    nibble planes, or the top 2-bit planes for bits = 2) + (s, z) metadata (mb bytes a pair: 8
+    fp32, 4 fp16) of every quantized token-head, the fp16 tail, the query and the fp32
     output."""
-    per_tok = D // 2 + D // 2 + mb * D // G + mb
+    per_tok = 2 * (D * bits // 8) + mb * D // G + mb
     return H * (nq * per_tok + nt * 4 * D + 2 * D + 4 * D)
 
 
@@ -122,6 +124,8 @@ def main():
                     help="skip the grouped-query layer (gqa: null)")
     ap.add_argument("--no-meta16", action="store_true",
                     help="skip the fp16-metadata comparison (meta16: null)")
+    ap.add_argument("--no-topk", action="store_true",
+                    help="skip the top-k-bit draft comparison (topk: null)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replayed step (graph_step: null)")
     ap.add_argument("--cpu-threads", type=int, default=None,
@@ -369,6 +373,9 @@ def main():
     meta16 = None if args.no_meta16 else measure_meta16(
         torch, stream, spin_cycles, dev, cfg["name"], ctx=cfg["ctx"], H=cfg["heads"],
         m=cfg["gamma"] + 1)
+    topk = None if args.no_topk else measure_topk(
+        torch, stream, spin_cycles, dev, cfg["name"], ctx=cfg["ctx"], H=cfg["heads"],
+        m=cfg["gamma"] + 1)
     read_ceiling = measure_read_ceiling(torch, stream)
     mixed_ceiling = measure_mixed_ceiling(torch, stream)
 
@@ -436,6 +443,7 @@ def main():
         "graph_step": graph_line,
         "gqa": gqa,
         "meta16": meta16,
+        "topk": topk,
         "samples_dropped": dropped,
         "read_ceiling": read_ceiling,
         "mixed_ceiling": mixed_ceiling,
@@ -607,6 +615,71 @@ def measure_meta16(torch, stream, spin_cycles, dev, name, ctx=131072, H=32, m=7,
         out[f"{name}_{fmt}_us"] = round(us, 2)
         out[f"{name}_{fmt}_bytes"] = int(nbytes)
         out[f"{name}_{fmt}_frac"] = round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    for c in caches.values():
+        c.close()
+    return out
+
+
+def measure_topk(torch, stream, spin_cycles, dev, name, ctx=131072, H=32, m=7, reps=20,
+                 rounds=3):
+    """The top-k-bit draft: a 2-layer cache in the split-upper layout (the upper nibble as a
+    2-bit top plane and a 2-bit middle plane) against a 2-layer cache in the default layout, on
+    the same input (H heads, head_dim 128, ctx tokens quantized plus a 64 + m token tail).
+    Timed over `reps` consecutive calls behind the spin kernel, alternating between the two
+    layers (each call's bytes are not served from the previous call's cache lines): the 2-bit
+    draft (top planes only), the 4-bit draft and the m-query verify on each layout; `rounds`
+    alternating rounds, the best of each reported."""
+    from hierarchical_quantized_kv_amd import synth
+    from hierarchical_quantized_kv_amd.binding import Cache
+    D, nt = 128, 64 + m
+    gen = torch.Generator(device=dev).manual_seed(6154)
+    qd = (torch.randn((1, H, D), generator=gen, device=dev) / math.sqrt(D)).half()
+    qv = (torch.randn((1, m, H, D), generator=gen, device=dev) / math.sqrt(D)).half()
+    od = torch.empty((1, H, D), dtype=torch.float32, device=dev)
+    ov = torch.empty((1, m, H, D), dtype=torch.float32, device=dev)
+    caches = {lay: Cache(2, 1, H, D, ctx + 2 * G, m - 1, split_upper=(lay == "split"))
+              for lay in ("nibble", "split")}
+    for layer in range(2):
+        k, v = synth.kv_device(torch, 1, ctx + nt, H, D, 6151 + 10 * layer, 6152 + 10 * layer,
+                               dev, outliers=synth.outlier_channels(H, D, 6153 + layer))
+        for c in caches.values():
+            c.prefill(layer, k[:, :ctx + 64].contiguous(), v[:, :ctx + 64].contiguous())
+            c.append(layer, k[:, ctx + 64:].contiguous(), v[:, ctx + 64:].contiguous())
+        del k, v
+    calls = [("draft2", "split", lambda c, l: c.attend_draft_bits(l, qd, 2, out=od)),
+             ("draft4", "split", lambda c, l: c.attend_draft(l, qd, out=od)),
+             ("verify", "split", lambda c, l: c.attend_verify(l, qv, out=ov)),
+             ("draft4", "nibble", lambda c, l: c.attend_draft(l, qd, out=od)),
+             ("verify", "nibble", lambda c, l: c.attend_verify(l, qv, out=ov))]
+    best = {}
+    for _ in range(rounds):
+        for call, lay, fn in calls:
+            c = caches[lay]
+            for i in range(4):
+                fn(c, i & 1)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(spin_cycles)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                fn(c, i & 1)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            best[(call, lay)] = min(us, best.get((call, lay), us))
+    out = {"workload": f"one layer of the {name} workload at a time (two layers alternating): "
+                       f"{H} heads, head_dim {D}, ctx {ctx} + {nt}-token tail, verify of {m} "
+                       f"queries; split-upper vs default layout, best of {rounds} rounds of "
+                       f"{reps} calls"}
+    for (call, lay), us in sorted(best.items()):
+        if call == "verify":
+            nbytes = verify_bytes(ctx, nt, H, D, m)
+        else:
+            nbytes = draft_bytes(ctx, nt, H, D, bits=2 if call == "draft2" else 4)
+        key = f"{call}_{lay}"
+        out[f"{key}_us"] = round(us, 2)
+        out[f"{key}_bytes"] = int(nbytes)
+        out[f"{key}_frac"] = round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
     for c in caches.values():
         c.close()
     return out

@@ -25,7 +25,7 @@ EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_des
            "qs_spec_accept", "qs_state_to_device", "qs_state_from_device", "qs_append_dev",
            "qs_rollback_dev", "qs_flush_dev", "qs_commit_dev", "qs_attend_draft_dev",
            "qs_attend_verify_dev", "qs_append_attend_draft", "qs_append_attend_verify",
-           "qs_attend_draft_gqa", "qs_attend_verify_gqa")
+           "qs_attend_draft_gqa", "qs_attend_verify_gqa", "qs_attend_draft_bits")
 
 # Bits of the device-mode error word (include/quantspec.h, device mode).
 DEV_ERR_APPEND, DEV_ERR_ROLLBACK, DEV_ERR_FLUSH, DEV_ERR_ATTEND = 1, 2, 4, 8
@@ -34,7 +34,7 @@ DEV_ERR_APPEND, DEV_ERR_ROLLBACK, DEV_ERR_FLUSH, DEV_ERR_ATTEND = 1, 2, 4, 8
 class QsConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "batch", "n_heads", "head_dim", "group", "max_ctx", "gamma_max",
-        "draft_offset", "meta_fp16")]
+        "draft_offset", "meta_fp16", "split_upper")]
 
 
 class QsLayout(ctypes.Structure):
@@ -75,6 +75,7 @@ def lib():
         L.qs_flush.argtypes = [P, I32, I32, P, PI]
         L.qs_attend_draft.argtypes = [P, I32, P, F, P, P]
         L.qs_attend_verify.argtypes = [P, I32, P, I32, F, P, P]
+        L.qs_attend_draft_bits.argtypes = [P, I32, P, I32, F, P, P]
         L.qs_get_state.argtypes = [P, I32, PI, PI, PI]
         L.qs_append_attend_draft.argtypes = [P, I32, P, P, I32, PI, P, F, P, P]
         L.qs_attend_draft_gqa.argtypes = [P, I32, P, I32, F, P, P]
@@ -114,9 +115,9 @@ def _ptr_i32(arr):
 
 
 def make_config(n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group=128,
-                draft_offset=8, meta_fp16=False) -> QsConfig:
+                draft_offset=8, meta_fp16=False, split_upper=False) -> QsConfig:
     return QsConfig(n_layers, batch, n_heads, head_dim, group, max_ctx, gamma_max, draft_offset,
-                    int(meta_fp16))
+                    int(meta_fp16), int(split_upper))
 
 
 def arena_layout(cfg: QsConfig) -> QsLayout:
@@ -131,11 +132,12 @@ class Cache:
     """A cache over a torch uint8 arena on the current device; verbs mirror the C ABI."""
 
     def __init__(self, n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group=128,
-                 draft_offset=8, device="cuda", meta_fp16=False):
+                 draft_offset=8, device="cuda", meta_fp16=False, split_upper=False):
         import torch
         self.torch = torch
         self.cfg = make_config(n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, group,
-                               draft_offset, meta_fp16)
+                               draft_offset, meta_fp16, split_upper)
+        self.split_upper = bool(split_upper)
         self.L, self.B, self.H, self.D = n_layers, batch, n_heads, head_dim
         self.G, self.T, self.gamma_max = group, max_ctx, gamma_max
         self.meta_fp16 = bool(meta_fp16)
@@ -233,6 +235,17 @@ class Cache:
             raise ValueError("q: expected a 4-d tensor [B][m][H][D]")
         shape = (self.B, q.shape[1], self.H if hq is None else hq, self.D)
         return shape, self._dev(q, self.torch.float16, "q", shape)
+
+    def attend_draft_bits(self, layer, q, bits, sm_scale=1.0, out=None, stream=None):
+        """Draft on the top `bits` (4, or 2 with split_upper) bits of every code."""
+        torch = self.torch
+        shape = (self.B, self.H, self.D)
+        pq = self._dev(q, torch.float16, "q", shape)
+        out = self._out(out, shape, q.device)
+        self._check(lib().qs_attend_draft_bits(self._h, layer, pq, int(bits), float(sm_scale),
+                                               self._dev(out, torch.float32, "out", shape),
+                                               self._stream(stream)), "qs_attend_draft_bits")
+        return out
 
     def attend_verify(self, layer, q, sm_scale=1.0, out=None, stream=None):
         torch = self.torch
@@ -367,6 +380,16 @@ class Cache:
             "tail_k": (torch.float16, lay.tail_k, (B, H, 2 * G, D)),
             "tail_v": (torch.float16, lay.tail_v, (B, H, 2 * G, D)),
         }
+        if name in ("tk", "mk", "tv", "mv"):
+            # split-upper layout: the C_T (top) and C_M (middle) 2-bit planes are the first and
+            # second halves of each (sequence, head) stripe of uk (keys) and uv (values)
+            if not self.split_upper:
+                raise ValueError(f"section {name}: the cache does not use the split-upper layout")
+            off, shape = ((lay.uk, (B, H, 2, T, D // 4)) if name[1] == "k"
+                          else (lay.uv, (B, H, 2, NG, 2, D, G // 8)))
+            n = int(np.prod(shape))
+            view = self.arena[off + layer * n:off + (layer + 1) * n].view(*shape)
+            return view[:, :, 0] if name[0] == "t" else view[:, :, 1]
         dtype, off, shape = shapes[name]
         esize = torch.tensor([], dtype=dtype).element_size()
         n = int(np.prod(shape))

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libquantspec.so")
 SOURCES = [os.path.join(CSRC, f) for f in (
     "qs_attn_host.hip", "qs_attn_app.hip", "qs_attn_dev.hip", "qs_attn_gqa.hip",
-    "qs_quant.hip", "qs_sample.hip", "qs_api.cpp")]
+    "qs_attn_split_host.hip", "qs_attn_split_app.hip", "qs_quant.hip", "qs_sample.hip",
+    "qs_api.cpp")]
 # Measurement helper for bench.py (the device's streaming-read ceiling); not part of the library.
 PROBE_LIB = os.path.join(HERE, "libqs_readprobe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "read_probe.hip")]

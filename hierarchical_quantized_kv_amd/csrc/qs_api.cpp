@@ -29,8 +29,10 @@ hipError_t launch_attention(const AttnArgs& a, int D, bool draft, hipStream_t st
 hipError_t launch_attention_dev(const AttnDevArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_attention_app(const AttnAppArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_attention_gqa(const AttnGqaArgs& a, int D, bool draft, hipStream_t st);
+hipError_t launch_attention_split(const AttnArgs& a, int D, bool draft, int fmt, hipStream_t st);
+hipError_t launch_attention_app_split(const AttnAppArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_state(const StateArgs& a, hipStream_t st);
-int attention_slots(int D, bool draft, int B, int mode, bool meta16);
+int attention_slots(int D, bool draft, int B, int mode, bool meta16, int fmt);
 }  // namespace qs
 
 struct qs_cache {
@@ -63,6 +65,7 @@ size_t layer_off(const qs_cache* c, size_t per_lbh_bytes, int layer) {
 }
 
 const char* const kInDeviceMode = "the counters are on the device (qs_state_from_device first)";
+const char* const kNotSplit = "not available with split_upper (host-mode and fused calls only)";
 const char* const kInHostMode = "not in device mode (qs_state_to_device first)";
 
 int32_t* dev_state(const qs_cache* c) { return reinterpret_cast<int32_t*>(c->arena + c->lay.state); }
@@ -164,6 +167,7 @@ qs_status qs_prefill(qs_cache* c, int32_t layer, const void* d_k, const void* d_
   p.kmeta = c->arena + c->lay.kmeta;
   p.vmeta = c->arena + c->lay.vmeta;
   p.meta16 = cf.meta_fp16;
+  p.split = cf.split_upper;
   p.k = static_cast<const uint16_t*>(d_k);
   p.v = static_cast<const uint16_t*>(d_v);
   p.B = cf.batch;
@@ -237,6 +241,7 @@ qs_status qs_flush(qs_cache* c, int32_t layer, int32_t min_tail, void* stream, i
   a.kmeta = c->arena + c->lay.kmeta;
   a.vmeta = c->arena + c->lay.vmeta;
   a.meta16 = cf.meta_fp16;
+  a.split = cf.split_upper;
   a.tail_k = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_k);
   a.tail_v = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_v);
   a.B = cf.batch;
@@ -320,9 +325,10 @@ static void attn_args(const qs_cache* c, int32_t layer, const void* d_q, int32_t
 
 // Work plan for the sequences `seqs`: quantized workers sized to one resident round of the pass
 // kernel, next to the tail items.
-static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft, int mode) {
+static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft, int mode,
+                          int fmt = qs::kFmtNibble) {
   const qs_config& cf = c->cfg;
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, mode, cf.meta_fp16 != 0);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, mode, cf.meta_fp16 != 0, fmt);
   if (slots <= 0) slots = kFallbackSlots;
   int tail_items = 0;
   for (int b = 0; b < cf.batch; ++b)
@@ -331,19 +337,24 @@ static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft, in
   return qs::make_plan(seqs, cf.batch, cf.n_heads, cf.group, target);
 }
 
+// bits: the draft's top code bits (4, or 2 with the split-upper layout); verify reads all 8.
 static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
-                        float* d_out, void* stream, bool draft) {
+                        float* d_out, void* stream, bool draft, int bits = 4) {
   if (!c) return QS_ERR_INVALID_ARG;
   if (c->dev) return fail(c, QS_ERR_STATE, kInDeviceMode);
   if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
   if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
+  const qs_config& cf = c->cfg;
+  if (bits != 4 && bits != 2) return fail(c, QS_ERR_INVALID_ARG, "bits must be 2 or 4");
+  if (bits == 2 && !cf.split_upper)
+    return fail(c, QS_ERR_INVALID_ARG, "a 2-bit draft needs the split-upper layout (split_upper = 1)");
   std::string err;
   qs_status s = c->st.check_attend(layer, m, draft, &err);
   if (s != QS_OK) return fail(c, s, err);
-  const qs_config& cf = c->cfg;
+  const int fmt = !cf.split_upper ? qs::kFmtNibble : (bits == 2 ? qs::kFmtSplit2 : qs::kFmtSplit4);
   qs::Seq seqs[QS_MAX_BATCH];
   for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
-  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeHost);
+  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeHost, fmt);
   qs::AttnArgs a{};
   attn_args(c, layer, d_q, m, sm_scale, d_out, p, a);
   for (int b = 0; b < cf.batch; ++b) {
@@ -351,7 +362,10 @@ static qs_status attend(qs_cache* c, int32_t layer, const void* d_q, int32_t m, 
     a.nt[b] = seqs[b].nt;
     a.head[b] = seqs[b].head;
   }
-  hipError_t e = qs::launch_attention(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
+  hipError_t e = fmt == qs::kFmtNibble
+                     ? qs::launch_attention(a, cf.head_dim, draft, static_cast<hipStream_t>(stream))
+                     : qs::launch_attention_split(a, cf.head_dim, draft, fmt,
+                                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
   c->err.clear();
   return QS_OK;
@@ -367,6 +381,7 @@ static qs_status attend_gqa(qs_cache* c, int32_t layer, const void* d_q, int32_t
   if (!d_q || !d_out) return fail(c, QS_ERR_INVALID_ARG, "null q or out");
   if (!isfinite(sm_scale)) return fail(c, QS_ERR_INVALID_ARG, "sm_scale must be finite");
   const qs_config& cf = c->cfg;
+  if (cf.split_upper) return fail(c, QS_ERR_INVALID_ARG, kNotSplit);
   if (g < 1 || g > QS_MAX_QUERIES) return fail(c, QS_ERR_INVALID_ARG, "g must be in 1..16");
   if (!draft && (mt < 1 || mt > cf.gamma_max + 1))
     return fail(c, QS_ERR_INVALID_ARG, "m must be in 1..gamma_max+1");
@@ -422,7 +437,8 @@ static qs_status append_attend(qs_cache* c, int32_t layer, const void* d_k, cons
     if (seqs[b].nq + seqs[b].nt == 0) return fail(c, QS_ERR_STATE, "attention over a sequence that holds no token");
     if (!draft && m > seqs[b].nt) return fail(c, QS_ERR_STATE, "verify needs m <= nt (the m queries are tail tokens)");
   }
-  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeAppend);
+  const int fmt = cf.split_upper ? qs::kFmtSplit4 : qs::kFmtNibble;
+  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeAppend, fmt);
   qs::AttnAppArgs a{};
   attn_args(c, layer, d_q, m, sm_scale, d_out, p, a);
   for (int b = 0; b < cf.batch; ++b) {
@@ -436,7 +452,10 @@ static qs_status append_attend(qs_cache* c, int32_t layer, const void* d_k, cons
   a.wtail_k = const_cast<uint16_t*>(a.tail_k);
   a.wtail_v = const_cast<uint16_t*>(a.tail_v);
   a.an_max = n_max;
-  hipError_t e = qs::launch_attention_app(a, cf.head_dim, draft, static_cast<hipStream_t>(stream));
+  hipError_t e = fmt == qs::kFmtNibble
+                     ? qs::launch_attention_app(a, cf.head_dim, draft, static_cast<hipStream_t>(stream))
+                     : qs::launch_attention_app_split(a, cf.head_dim, draft,
+                                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(c, e, draft ? "draft launch" : "verify launch");
   c->st.apply_append(layer, n);
   c->err.clear();
@@ -451,6 +470,11 @@ qs_status qs_attend_draft(qs_cache* c, int32_t layer, const void* d_q, float sm_
 qs_status qs_attend_verify(qs_cache* c, int32_t layer, const void* d_q, int32_t m, float sm_scale,
                            float* d_out, void* stream) {
   return attend(c, layer, d_q, m, sm_scale, d_out, stream, false);
+}
+
+qs_status qs_attend_draft_bits(qs_cache* c, int32_t layer, const void* d_q, int32_t bits,
+                               float sm_scale, float* d_out, void* stream) {
+  return attend(c, layer, d_q, 1, sm_scale, d_out, stream, true, bits);
 }
 
 qs_status qs_attend_draft_gqa(qs_cache* c, int32_t layer, const void* d_q, int32_t g,
@@ -494,6 +518,7 @@ qs_status qs_get_state(const qs_cache* c, int32_t layer, int32_t* h_nq, int32_t*
 qs_status qs_state_to_device(qs_cache* c, void* stream) {
   if (!c) return QS_ERR_INVALID_ARG;
   if (c->dev) return fail(c, QS_ERR_STATE, "already in device mode");
+  if (c->cfg.split_upper) return fail(c, QS_ERR_INVALID_ARG, kNotSplit);
   const qs_config& cf = c->cfg;
   const size_t n = (size_t)cf.n_layers * cf.batch;
   std::vector<int32_t> h(n * qs::kStateInts + 1, 0);
@@ -682,6 +707,7 @@ qs_status qs_flush_dev(qs_cache* c, int32_t layer, int32_t min_tail, void* strea
   a.kmeta = c->arena + c->lay.kmeta;
   a.vmeta = c->arena + c->lay.vmeta;
   a.meta16 = cf.meta_fp16;
+  a.split = cf.split_upper;
   a.tail_k = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_k);
   a.tail_v = reinterpret_cast<const uint16_t*>(c->arena + c->lay.tail_v);
   a.B = cf.batch;
@@ -720,7 +746,8 @@ static qs_status attend_dev(qs_cache* c, int32_t layer, const void* d_q, int32_t
   // quantized workers filling the rest of one resident round (worker w takes groups w, w + W,
   // .. of whatever the sequence holds).  Tail items past nt exit at once, so they are counted
   // as half their number.  Workers and items with no work write empty records.
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, qs::kModeDev, cf.meta_fp16 != 0);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, qs::kModeDev, cf.meta_fp16 != 0,
+                                  qs::kFmtNibble);
   if (slots <= 0) slots = kFallbackSlots;
   const int bh = cf.batch * cf.n_heads;
   int W = (slots - bh * qs::kMaxTailItems / 2) / bh;

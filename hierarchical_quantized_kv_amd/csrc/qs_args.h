@@ -78,6 +78,14 @@ enum : int {
   kModeGqa = 3,     // counters by value; gq query heads share each cached (key/value) head
 };
 
+// Layout of the upper planes that an attention kernel reads (a template parameter too):
+//   kFmtNibble  the upper nibble C_U as one 4-bit plane per stream (uk, uv);
+//   kFmtSplit4  split-upper layout: C_U = 4 C_T + C_M stored as a 2-bit top plane (first half of
+//               each (layer, sequence, head) stripe of uk / uv) and a 2-bit middle plane (second
+//               half), read back into nibbles by the 4-bit draft and by verify;
+//   kFmtSplit2  split-upper layout, the 2-bit draft: only the top plane is read.
+enum : int { kFmtNibble = 0, kFmtSplit4 = 1, kFmtSplit2 = 2 };
+
 template <int NB, int MODE = kModeHost>
 struct AttnArgsN : AttnHeader {
   static constexpr int kMode = kModeHost;
@@ -165,6 +173,7 @@ struct PrefillArgs {
   uint8_t* kmeta;        // fp32 (scale, zero-point) or, with meta16, fp16 (scale, offset)
   uint8_t* vmeta;
   int32_t meta16;
+  int32_t split;         // split-upper layout: uk / uv hold the top and middle 2-bit planes
   const uint16_t* k;     // prompt [B][n_max][H][D]
   const uint16_t* v;
   int32_t B, H, T, NG;
@@ -181,6 +190,7 @@ struct FlushArgs {
   uint8_t* kmeta;        // fp32 (scale, zero-point) or, with meta16, fp16 (scale, offset)
   uint8_t* vmeta;
   int32_t meta16;
+  int32_t split;         // split-upper layout: uk / uv hold the top and middle 2-bit planes
   const uint16_t* tail_k;
   const uint16_t* tail_v;
   int32_t B, H, T, NG;

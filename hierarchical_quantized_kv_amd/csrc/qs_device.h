@@ -96,22 +96,58 @@ __device__ __forceinline__ float4 bldf4(rsrc_t r, uint32_t voff, uint32_t soff) 
                      __uint_as_float(v.w));
 }
 
-// The four streams of one (sequence, head) of a layer.
+// Layout of the upper planes (kFmtNibble / kFmtSplit4 / kFmtSplit2, qs_args.h), a template
+// argument of the attention kernels.  In a split plane row each 32-bit word covers 16 entries 16w .. 16w+15 (channels of a key row,
+// tokens of a value row); nibble e of the top-plane word holds C_T(16w + e) in its upper two
+// bits and C_T(16w + 8 + e) in its lower two, the middle-plane word C_M(16w + e) in its lower
+// two bits and C_M(16w + 8 + e) in its upper two.  Then the upper-nibble words of entries
+// 16w + 0..7 and 16w + 8..15 are bitfield selects: (T & 0xCC..) | (M & 0x33..) and
+// ((T << 2) & 0xCC..) | ((M >> 2) & 0x33..).
+// The streams of one (sequence, head) of a layer (mk / mv: the middle planes of the split
+// layout, in which uk / uv address the top planes).
 struct Streams {
-  rsrc_t uk, lk, uv, lv, km, vm;
+  rsrc_t uk, lk, uv, lv, km, vm, mk, mv;
 };
-template <bool M16, class Args>
+template <bool M16, int FMT = kFmtNibble, class Args>
 __device__ __forceinline__ Streams make_streams(const Args& a, size_t bh, int D) {
   const uint32_t plane = (uint32_t)a.T * (uint32_t)(D / 2);  // bytes of one plane per (b, h)
   constexpr uint32_t mb = M16 ? 4 : 8;                       // bytes of one metadata pair
   Streams st;
-  st.uk = make_rsrc(a.uk + bh * plane, plane);
+  if constexpr (FMT == kFmtNibble) {
+    st.uk = make_rsrc(a.uk + bh * plane, plane);
+    st.uv = make_rsrc(a.uv + bh * plane, plane);
+    st.mk = st.uk;
+    st.mv = st.uv;
+  } else {
+    st.uk = make_rsrc(a.uk + bh * plane, plane / 2);
+    st.mk = make_rsrc(a.uk + bh * plane + plane / 2, plane / 2);
+    st.uv = make_rsrc(a.uv + bh * plane, plane / 2);
+    st.mv = make_rsrc(a.uv + bh * plane + plane / 2, plane / 2);
+  }
   st.lk = make_rsrc(a.lk + bh * plane, plane);
-  st.uv = make_rsrc(a.uv + bh * plane, plane);
   st.lv = make_rsrc(a.lv + bh * plane, plane);
   st.km = make_rsrc(a.kmeta + bh * (size_t)a.NG * D * mb, (uint32_t)a.NG * D * mb);
   st.vm = make_rsrc(a.vmeta + bh * (size_t)a.T * mb, (uint32_t)a.T * mb);
   return st;
+}
+
+// Upper-nibble words of the 16 entries of a split-layout word pair (top t, middle m): entries
+// 0..7 and 8..15 (see kFmtSplit4).
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
+  return (a & mask) | (b & ~mask);
+}
+__device__ __forceinline__ uint2 split_nibbles(uint32_t t, uint32_t m) {
+  return make_uint2(bfi(0xCCCCCCCCu, t, m), bfi(0xCCCCCCCCu, t << 2, m >> 2));
+}
+// Signed 2-bit draft words of a top-plane word: nibble e = 4 C_T - 8 (as a signed nibble) of
+// entries 0..7 and 8..15.  Flipping the upper bit of every 2-bit field turns C_T into C_T ^ 2,
+// and 4 (C_T ^ 2) read as a signed nibble is 4 C_T - 8.
+__device__ __forceinline__ uint2 top2_signed(uint32_t t) {
+  const uint32_t x = t ^ 0xAAAAAAAAu;
+  return make_uint2(x & 0xCCCCCCCCu, (x << 2) & 0xCCCCCCCCu);
+}
+__device__ __forceinline__ uint32_t bld4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNt);
 }
 
 __device__ __forceinline__ float lo_h(uint32_t x) { return (float)as_h2(x).x; }
@@ -332,12 +368,12 @@ __device__ __forceinline__ void digit_bytes(int xa, int xb, uint32_t& even, uint
   odd = (((a >> 4) & 0x0F0F0Fu) | (((b >> 4) & 0x0F0F0Fu) << 4)) ^ kDigitBias;
 }
 
-// sum over the 4 plane words w[] (32 nibbles) of the digit-weighted signed dot products, as a
-// float in units of the fixed-point weights: sum_j 16^j sum_k dot8(d[j].k, w[k] ^ 0x88888888),
-// evaluated as two Horner chains (digits 5..3 and 2..0; |chain| <= 2048 * 273 fits int32).
+// sum over 4 signed-nibble words u[] (32 nibbles, each the signed 4-bit value of one entry) of
+// the digit-weighted signed dot products, as a float in units of the fixed-point weights:
+// sum_j 16^j sum_k dot8(d[j].k, u[k]), evaluated as two Horner chains (digits 5..3 and 2..0;
+// |chain| <= 2048 * 273 fits int32).
 __device__ __forceinline__ float digit_dot(const uint4 (&d)[kDigits], uint4 w) {
-  const int u[4] = {(int)(w.x ^ kNibbleBias), (int)(w.y ^ kNibbleBias), (int)(w.z ^ kNibbleBias),
-                    (int)(w.w ^ kNibbleBias)};
+  const int u[4] = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
   auto plane = [&](int j, int acc) {
     acc = __builtin_amdgcn_sdot8((int)d[j].x, u[0], acc, false);
     acc = __builtin_amdgcn_sdot8((int)d[j].y, u[1], acc, false);
@@ -361,41 +397,85 @@ __device__ __forceinline__ void fixed_unit(float xmax, float& inv_unit, float& u
   unit = ldexpf(1.f, e - 22);
 }
 
-// Planes and metadata of one group, as loaded by one lane.
-template <int D, bool M16>
+// Planes and metadata of one group, as loaded by one lane: per key load 32 channels of one
+// token row, per value load 32 tokens of one channel row (16 bytes of the nibble plane, or 8
+// bytes of each 2-bit plane).
+template <int FMT>
+using DraftW = typename std::conditional<FMT == kFmtNibble, uint4, uint2>::type;
+template <int D, bool M16, int FMT>
 struct DraftBuf {
-  uint4 k[DraftShape<D>::KIT];
-  uint4 v[DraftShape<D>::VIT];
+  using W = DraftW<FMT>;
+  static constexpr int KM = FMT == kFmtSplit4 ? DraftShape<D>::KIT : 1;  // middle-plane words
+  static constexpr int VM = FMT == kFmtSplit4 ? DraftShape<D>::VIT : 1;
+  W k[DraftShape<D>::KIT];   // upper nibble plane, or top plane
+  W v[DraftShape<D>::VIT];
+  uint2 k2[KM];              // kFmtSplit4: middle plane
+  uint2 v2[VM];
   MetaT<M16> km;  // key metadata of channels 2*lane, 2*lane+1
   MetaT<M16> vm;  // value metadata of tokens 2*lane, 2*lane+1
 };
 
-template <int D, bool M16>
-__device__ __forceinline__ void draft_load_k(const Streams& sm, int g, DraftBuf<D, M16>& buf) {
+// The signed-nibble words digit_dot takes (nibble = upper nibble - 8, or for the 2-bit draft
+// 4 C_T - 8) of one load: its 32 entries in order, 8 per word.
+template <int FMT>
+__device__ __forceinline__ uint4 signed_words(const DraftW<FMT>& x, uint2 mid) {
+  if constexpr (FMT == kFmtNibble) {
+    return make_uint4(x.x ^ kNibbleBias, x.y ^ kNibbleBias, x.z ^ kNibbleBias, x.w ^ kNibbleBias);
+  } else if constexpr (FMT == kFmtSplit4) {
+    const uint2 a = split_nibbles(x.x ^ 0xAAAAAAAAu, mid.x), b = split_nibbles(x.y ^ 0xAAAAAAAAu, mid.y);
+    return make_uint4(a.x, a.y, b.x, b.y);
+  } else {
+    const uint2 a = top2_signed(x.x), b = top2_signed(x.y);
+    return make_uint4(a.x, a.y, b.x, b.y);
+  }
+}
+
+template <int D, int FMT, bool M16>
+__device__ __forceinline__ void draft_load_k(const Streams& sm, int g, DraftBuf<D, M16, FMT>& buf) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
-  const uint32_t voff = (lane / S::KL) * (D / 2) + (lane % S::KL) * 16;
-  const uint32_t soff = (uint32_t)g * kGroup * (D / 2);
+  if constexpr (FMT == kFmtNibble) {
+    const uint32_t voff = (lane / S::KL) * (D / 2) + (lane % S::KL) * 16;
+    const uint32_t soff = (uint32_t)g * kGroup * (D / 2);
 #pragma unroll
-  for (int it = 0; it < S::KIT; ++it)  // key rows it*TPI .. : 1 KB apart
-    buf.k[it] = bld16(sm.uk, voff + (it & 3) * 1024, soff + (it >> 2) * 4096);
+    for (int it = 0; it < S::KIT; ++it)  // key rows it*TPI .. : 1 KB apart
+      buf.k[it] = bld16(sm.uk, voff + (it & 3) * 1024, soff + (it >> 2) * 4096);
+  } else {
+    const uint32_t voff = (lane / S::KL) * (D / 4) + (lane % S::KL) * 8;
+    const uint32_t soff = (uint32_t)g * kGroup * (D / 4);
+#pragma unroll
+    for (int it = 0; it < S::KIT; ++it) {
+      buf.k[it] = bld8(sm.uk, voff + it * S::TPI * (D / 4), soff);
+      if constexpr (FMT == kFmtSplit4) buf.k2[it] = bld8(sm.mk, voff + it * S::TPI * (D / 4), soff);
+    }
+  }
 }
-template <int D, bool M16>
-__device__ __forceinline__ void draft_load_meta(const Streams& sm, int g, DraftBuf<D, M16>& buf) {
+template <int D, int FMT, bool M16>
+__device__ __forceinline__ void draft_load_meta(const Streams& sm, int g, DraftBuf<D, M16, FMT>& buf) {
   const int lane = threadIdx.x;
   buf.km = load_meta<M16>(sm.km, (uint32_t)g * D);
   if (lane >= D / 2) buf.km = meta_zero<M16>();
   buf.vm = load_meta<M16>(sm.vm, (uint32_t)g * kGroup);
 }
-template <int D, bool M16>
-__device__ __forceinline__ void draft_load_v(const Streams& sm, int g, DraftBuf<D, M16>& buf) {
+template <int D, int FMT, bool M16>
+__device__ __forceinline__ void draft_load_v(const Streams& sm, int g, DraftBuf<D, M16, FMT>& buf) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
   const int vr = lane & 3, vd = lane >> 2;
-  const uint32_t voff = (vr >> 1) * (D * kGroup / 4) + vd * (kGroup / 4) + (vr & 1) * 16;
-  const uint32_t soff = (uint32_t)g * D * (kGroup / 2);
+  if constexpr (FMT == kFmtNibble) {
+    const uint32_t voff = (vr >> 1) * (D * kGroup / 4) + vd * (kGroup / 4) + (vr & 1) * 16;
+    const uint32_t soff = (uint32_t)g * D * (kGroup / 2);
 #pragma unroll
-  for (int i = 0; i < S::VIT; ++i) buf.v[i] = bld16(sm.uv, voff + i * 16 * (kGroup / 4), soff);
+    for (int i = 0; i < S::VIT; ++i) buf.v[i] = bld16(sm.uv, voff + i * 16 * (kGroup / 4), soff);
+  } else {
+    const uint32_t voff = (vr >> 1) * (D * kGroup / 8) + vd * (kGroup / 8) + (vr & 1) * 8;
+    const uint32_t soff = (uint32_t)g * D * (kGroup / 4);
+#pragma unroll
+    for (int i = 0; i < S::VIT; ++i) {
+      buf.v[i] = bld8(sm.uv, voff + i * 16 * (kGroup / 8), soff);
+      if constexpr (FMT == kFmtSplit4) buf.v2[i] = bld8(sm.mv, voff + i * 16 * (kGroup / 8), soff);
+    }
+  }
 }
 
 // Running softmax state of a draft work item (per lane).
@@ -411,14 +491,16 @@ struct DraftAcc {
 // current group has been consumed, so the next group's loads overlap this group's arithmetic.
 // (The prefetch is a template flag rather than a run-time test so that the number of loads in
 // flight at every wait is fixed.)
-template <int D, bool PF, bool M16, class Args>
-__device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, DraftBuf<D, M16>& cur,
-                                            int gnext, float q0, float q1, DraftLds& L,
-                                            DraftAcc<D>& st) {
+template <int D, bool PF, bool M16, int FMT, class Args>
+__device__ __forceinline__ void draft_group(const Args& a, const Streams& sm,
+                                            DraftBuf<D, M16, FMT>& cur, int gnext, float q0,
+                                            float q1, DraftLds& L, DraftAcc<D>& st) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
   const int kc = lane % S::KL, kt = lane / S::KL, vr = lane & 3;
-  const float c = 128.f + a.draft_offset;  // 16 U + off - z = 16 u + (128 + off - z)
+  // 16 U + off - z = 16 u + (128 + off - z); the 2-bit draft: 64 C_T + 4 off - z =
+  // 16 (4 C_T - 8) + (128 + 4 off - z)
+  const float c = 128.f + (FMT == kFmtSplit2 ? 4.f : 1.f) * a.draft_offset;
 
   __syncthreads();  // the previous group's LDS reads are done
   // key weights q' = q s (channels 2 lane, 2 lane + 1) as digit planes; the score bias
@@ -443,7 +525,7 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, Dr
       qd[j * 64 + lane] = (uint8_t)(((j & 1) ? od : ev) >> (8 * (j >> 1)));
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (PF) draft_load_meta<D>(sm, gnext, cur);
+  if constexpr (PF) draft_load_meta<D, FMT>(sm, gnext, cur);
   bias = wave_sum_all(bias);
   __syncthreads();
 
@@ -454,13 +536,13 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, Dr
   float sc[S::KIT];
 #pragma unroll
   for (int it = 0; it < S::KIT; ++it) {
-    float p = digit_dot(dq, cur.k[it]);
+    float p = digit_dot(dq, signed_words<FMT>(cur.k[it], cur.k2[FMT == kFmtSplit4 ? it : 0]));
     p += dpp<kDppXor1>(p);  // the KL lanes of a key row
     if constexpr (S::KL == 4) p += dpp<kDppXor2>(p);
     sc[it] = fmaf(p, kscale, bias);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (PF) draft_load_k<D>(sm, gnext, cur);
+  if constexpr (PF) draft_load_k<D, FMT>(sm, gnext, cur);
   float gmax = sc[0];
 #pragma unroll
   for (int it = 1; it < S::KIT; ++it) gmax = fmaxf(gmax, sc[it]);
@@ -502,14 +584,15 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm, Dr
   const float vscale = 16.f * punit;
 #pragma unroll
   for (int i = 0; i < S::VIT; ++i) {
-    st.o[i] = fmaf(st.o[i], alpha, digit_dot(dp, cur.v[i]) * vscale);
+    st.o[i] = fmaf(st.o[i], alpha,
+                   digit_dot(dp, signed_words<FMT>(cur.v[i], cur.v2[FMT == kFmtSplit4 ? i : 0])) * vscale);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (PF) draft_load_v<D>(sm, gnext, cur);
+  if constexpr (PF) draft_load_v<D, FMT>(sm, gnext, cur);
 }
 
-template <int D, bool M16, class Args>
+template <int D, bool M16, int FMT, class Args>
 __device__ void draft_quant_item(const Args& a, int b, int h, int item, DraftLds& L) {
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
@@ -529,20 +612,20 @@ __device__ void draft_quant_item(const Args& a, int b, int h, int item, DraftLds
 #pragma unroll
   for (int i = 0; i < S::VIT; ++i) st.o[i] = 0.f;
 
-  const Streams sm = make_streams<M16>(a, bh, D);
-  DraftBuf<D, M16> buf;
+  const Streams sm = make_streams<M16, FMT>(a, bh, D);
+  DraftBuf<D, M16, FMT> buf;
   if (gs.first < gs.ng) {
-    draft_load_k<D>(sm, gs.first, buf);
-    draft_load_meta<D>(sm, gs.first, buf);
-    draft_load_v<D>(sm, gs.first, buf);
+    draft_load_k<D, FMT>(sm, gs.first, buf);
+    draft_load_meta<D, FMT>(sm, gs.first, buf);
+    draft_load_v<D, FMT>(sm, gs.first, buf);
     const int total = (gs.ng - gs.first + gs.step - 1) / gs.step;
     int g = gs.first, done = 0;
     for (; g + gs.step < gs.ng; g += gs.step, ++done) {
       pace(total - done, total);
-      draft_group<D, true>(a, sm, buf, g + gs.step, q0, q1, L, st);
+      draft_group<D, true, M16, FMT>(a, sm, buf, g + gs.step, q0, q1, L, st);
     }
     pace(1, total);
-    draft_group<D, false>(a, sm, buf, -1, q0, q1, L, st);
+    draft_group<D, false, M16, FMT>(a, sm, buf, -1, q0, q1, L, st);
   }
 
   // l and beta were accumulated once per key row in each of its KL lanes
@@ -604,18 +687,41 @@ struct VerifyBuf {
 };
 
 // UPPER: only the upper planes are read (the draft pass over grouped queries); the lower
-// nibbles are then the draft offset.
-template <int D, bool UPPER = false, bool M16>
+// nibbles are then the draft offset.  FMT: layout of the upper planes (kFmtNibble or
+// kFmtSplit4, whose top and middle 2-bit words are turned into the same upper-nibble words).
+template <int D, bool UPPER = false, int FMT = kFmtNibble, bool M16>
 __device__ __forceinline__ void verify_load_k(const Streams& sm, int gi, int half, VerifyBuf<D, M16>& buf) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
   // row of tile 4*half + t for lane row j: 16 (j/4) + 2 (j%4) + 64 half + 8 (t/2) + (t%2)
-  const uint32_t voff = (16 * (j >> 2) + 2 * (j & 3)) * (D / 2) + g * S::KB;
+  const uint32_t row0 = 16 * (j >> 2) + 2 * (j & 3);
+  const uint32_t voff = row0 * (D / 2) + g * S::KB;
   const uint32_t soff = ((uint32_t)gi * kGroup + 64 * half) * (D / 2);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const uint32_t o = voff + (8 * (t >> 1) + (t & 1)) * (D / 2);
-    if constexpr (S::KK == 4) {
+    const uint32_t dr = 8 * (t >> 1) + (t & 1);
+    const uint32_t o = voff + dr * (D / 2);
+    if constexpr (FMT != kFmtNibble) {  // split layout: rows of D/4 bytes, D/16 per lane group
+      const uint32_t os = (row0 + dr) * (D / 4) + g * (D / 16);
+      const uint32_t ss = ((uint32_t)gi * kGroup + 64 * half) * (D / 4);
+      if constexpr (S::KK == 4) {
+        const uint2 tw = bld8(sm.uk, os, ss), mw = bld8(sm.mk, os, ss);
+        const uint2 a = split_nibbles(tw.x, mw.x), b = split_nibbles(tw.y, mw.y);
+        buf.ku[t][0] = a.x; buf.ku[t][1] = a.y; buf.ku[t][2] = b.x; buf.ku[t][3] = b.y;
+      } else {
+        const uint2 a = split_nibbles(bld4(sm.uk, os, ss), bld4(sm.mk, os, ss));
+        buf.ku[t][0] = a.x; buf.ku[t][1] = a.y;
+      }
+      if constexpr (!UPPER) {
+        if constexpr (S::KK == 4) {
+          const uint4 l = bld16(sm.lk, o, soff);
+          buf.kl[t][0] = l.x; buf.kl[t][1] = l.y; buf.kl[t][2] = l.z; buf.kl[t][3] = l.w;
+        } else {
+          const uint2 l = bld8(sm.lk, o, soff);
+          buf.kl[t][0] = l.x; buf.kl[t][1] = l.y;
+        }
+      }
+    } else if constexpr (S::KK == 4) {
       const uint4 u = bld16(sm.uk, o, soff);
       buf.ku[t][0] = u.x; buf.ku[t][1] = u.y; buf.ku[t][2] = u.z; buf.ku[t][3] = u.w;
       if constexpr (!UPPER) {
@@ -633,7 +739,7 @@ __device__ __forceinline__ void verify_load_k(const Streams& sm, int gi, int hal
   }
 }
 
-template <int D, bool UPPER = false, bool M16>
+template <int D, bool UPPER = false, int FMT = kFmtNibble, bool M16>
 __device__ __forceinline__ void verify_load_v(const Streams& sm, int gi, int half, VerifyBuf<D, M16>& buf) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
@@ -642,7 +748,13 @@ __device__ __forceinline__ void verify_load_v(const Streams& sm, int gi, int hal
 #pragma unroll
   for (int rt = 0; rt < S::RT; ++rt) {
     const uint32_t o = voff + rt * 16 * (kGroup / 4);
-    buf.vu[rt] = bld8(sm.uv, o, soff);
+    if constexpr (FMT != kFmtNibble) {  // split layout: channel rows of G/8 bytes per half
+      const uint32_t os = j * (kGroup / 8) + 4 * g + rt * 16 * (kGroup / 8);
+      const uint32_t ss = (uint32_t)gi * D * (kGroup / 4) + (uint32_t)half * D * (kGroup / 8);
+      buf.vu[rt] = split_nibbles(bld4(sm.uv, os, ss), bld4(sm.mv, os, ss));
+    } else {
+      buf.vu[rt] = bld8(sm.uv, o, soff);
+    }
     if constexpr (!UPPER) buf.vl[rt] = bld8(sm.lv, o, soff);
   }
 }
@@ -666,7 +778,7 @@ struct VerifyAcc {
 // One group of a verify worker, in two 64-token halves.  With PF the buffers are refilled with
 // group gn as each part of group gi is consumed (a template flag, so that the number of loads in
 // flight at every wait is fixed).
-template <int D, bool PF, bool UPPER, bool M16, class Args>
+template <int D, bool PF, bool UPPER, bool M16, int FMT, class Args>
 __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, VerifyBuf<D, M16>& buf,
                                              int gi, int gn, VerifyLds& L, VerifyAcc<D>& st) {
   using S = VerifyShape<D>;
@@ -748,9 +860,9 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
     __builtin_amdgcn_sched_barrier(0);
     // next key half: the other half of this group, or the first half of the next group
     if (half == 0)
-      verify_load_k<D, UPPER>(sm, gi, 1, buf);
+      verify_load_k<D, UPPER, FMT>(sm, gi, 1, buf);
     else if constexpr (PF)
-      verify_load_k<D, UPPER>(sm, gn, 0, buf);
+      verify_load_k<D, UPPER, FMT>(sm, gn, 0, buf);
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -799,13 +911,13 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
     }
     __builtin_amdgcn_sched_barrier(0);
     if (half == 0)
-      verify_load_v<D, UPPER>(sm, gi, 1, buf);
+      verify_load_v<D, UPPER, FMT>(sm, gi, 1, buf);
     else if constexpr (PF)
-      verify_load_v<D, UPPER>(sm, gn, 0, buf);
+      verify_load_v<D, UPPER, FMT>(sm, gn, 0, buf);
   }
 }
 
-template <int D, bool UPPER, bool M16, class Args>
+template <int D, bool UPPER, bool M16, int FMT, class Args>
 __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyLds& L) {
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
@@ -833,20 +945,20 @@ __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyL
 #pragma unroll
   for (int rt = 0; rt < S::RT; ++rt) st.O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const Streams sm = make_streams<M16>(a, bh, D);
+  const Streams sm = make_streams<M16, FMT>(a, bh, D);
   VerifyBuf<D, M16> buf;
   if (gs.first < gs.ng) {
-    verify_load_k<D, UPPER>(sm, gs.first, 0, buf);
+    verify_load_k<D, UPPER, FMT>(sm, gs.first, 0, buf);
     verify_load_meta<D>(sm, gs.first, buf);
-    verify_load_v<D, UPPER>(sm, gs.first, 0, buf);
+    verify_load_v<D, UPPER, FMT>(sm, gs.first, 0, buf);
     const int total = (gs.ng - gs.first + gs.step - 1) / gs.step;
     int gi = gs.first, done = 0;
     for (; gi + gs.step < gs.ng; gi += gs.step, ++done) {
       pace(total - done, total);
-      verify_group<D, true, UPPER>(a, sm, buf, gi, gi + gs.step, L, st);
+      verify_group<D, true, UPPER, M16, FMT>(a, sm, buf, gi, gi + gs.step, L, st);
     }
     pace(1, total);
-    verify_group<D, false, UPPER>(a, sm, buf, gi, -1, L, st);
+    verify_group<D, false, UPPER, M16, FMT>(a, sm, buf, gi, -1, L, st);
   }
 
   st.l_run += __shfl_xor(st.l_run, 16);
@@ -1037,7 +1149,7 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
 
 // The draft pass runs the VALU item (3 waves per SIMD), except over grouped queries, where both
 // passes run the MFMA item (2 waves per SIMD).
-template <int D, bool DRAFT, int NB, int MODE, bool M16>
+template <int D, bool DRAFT, int NB, int MODE, bool M16, int FMT = kFmtNibble>
 __global__ __launch_bounds__(64, (DRAFT && MODE != kModeGqa) ? 3 : 2) void attn_kernel(
     const AttnArgsN<NB, MODE> a) {
   constexpr bool kValu = DRAFT && MODE != kModeGqa;
@@ -1059,9 +1171,9 @@ __global__ __launch_bounds__(64, (DRAFT && MODE != kModeGqa) ? 3 : 2) void attn_
     const int b = find_seq<NB>(a.qitem_base, a.B, y);
     const int item = y - a.qitem_base[b];
     if constexpr (kValu)
-      draft_quant_item<D, M16>(a, b, h, item, lds.p);
+      draft_quant_item<D, M16, FMT>(a, b, h, item, lds.p);
     else
-      verify_quant_item<D, DRAFT, M16>(a, b, h, item, lds.p);
+      verify_quant_item<D, DRAFT, M16, FMT>(a, b, h, item, lds.p);
   }
 }
 
@@ -1082,7 +1194,9 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float4& o, float m
   o.w = o.w * a1 + o2.w * a2;
 }
 
-template <int D, int NB, int MODE>
+// FMT (the upper-plane layout of the attention kernel it follows) only keeps the instantiations
+// of the launcher translation units apart.
+template <int D, int NB, int MODE, int FMT = kFmtNibble>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB, MODE> a) {
   constexpr int C4 = D / 4;        // float4 chunks of o
   constexpr int NP = 256 / C4;     // split phases
@@ -1287,6 +1401,11 @@ __device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* k
   // key plane rows are token-major, byte j of a row holds channel 2j in bits 0-3 and 2j + 1 in
   // bits 4-7: this lane's channels are bytes (c0 + 8 sub) / 2 .. + 3 of each row
   const size_t row0 = (lbh * a.T + (size_t)grp * G) * (D / 2) + (c0 + 8 * sub) / 2;
+  // split-upper layout: rows of D/4 bytes in the top and middle planes (the two halves of the
+  // (layer, sequence, head) stripe); the 16 channels of word (c0 + 8 sub) / 16 are this lane's
+  // 8 (entries 0..7 if sub is even, 8..15 if odd) and its neighbour's
+  const size_t srow0 = lbh * a.T * (D / 2) + (size_t)grp * G * (D / 4) + (c0 + 8 * (sub & ~1)) / 4;
+  const size_t mid = (size_t)a.T * (D / 4);
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
     uint32_t u = 0, l = 0;
@@ -1299,7 +1418,20 @@ __device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* k
       l |= ((c_lo & 15u) | ((c_hi & 15u) << 4)) << (8 * wi);
     }
     const size_t o = row0 + (size_t)(16 * k + rr) * (D / 2);
-    *reinterpret_cast<uint32_t*>(a.uk + o) = u;
+    if (a.split) {
+      // nibble e of u is C_U of entry e: entries 0..7 keep C_T in the upper and C_M in the lower
+      // two bits of their nibble, entries 8..15 the other way round
+      const uint32_t t = (sub & 1) ? (u >> 2) & 0x33333333u : u & 0xCCCCCCCCu;
+      const uint32_t m = (sub & 1) ? (u << 2) & 0xCCCCCCCCu : u & 0x33333333u;
+      const uint32_t other = __shfl_xor((sub & 1) ? t : m, 1);  // what the neighbour lacks
+      const size_t so = srow0 + (size_t)(16 * k + rr) * (D / 4);
+      if (sub & 1)
+        *reinterpret_cast<uint32_t*>(a.uk + so + mid) = m | other;
+      else
+        *reinterpret_cast<uint32_t*>(a.uk + so) = t | other;
+    } else {
+      *reinterpret_cast<uint32_t*>(a.uk + o) = u;
+    }
     *reinterpret_cast<uint32_t*>(a.lk + o) = l;
   }
 }
@@ -1353,6 +1485,10 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
   const int e = t0 / (G / 2), tin = t0 % (G / 2);
   uint8_t* uv = a.uv + ((lbh * a.NG + grp) * D) * (G / 2) + (size_t)e * (D * G / 4) + tin / 2;
   uint8_t* lv = a.lv + ((lbh * a.NG + grp) * D) * (G / 2) + (size_t)e * (D * G / 4) + tin / 2;
+  // split-upper layout: channel rows of G/8 bytes per half in the top and middle planes (the two
+  // halves of the stripe); this block's 32 tokens are words tin/16 and tin/16 + 1 of a row
+  uint8_t* tv = a.uv + lbh * a.NG * D * (G / 2) + ((size_t)grp * 2 + e) * D * (G / 8) + tin / 4;
+  const size_t mid = (size_t)a.NG * D * (G / 4);
   for (int d = lane; d < D; d += 64) {
     uint32_t u[4] = {0, 0, 0, 0}, l[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -1362,7 +1498,19 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
       u[j >> 2] |= ((c_lo >> 4) | ((c_hi >> 4) << 4)) << sh;
       l[j >> 2] |= ((c_lo & 15u) | ((c_hi & 15u) << 4)) << sh;
     }
-    *reinterpret_cast<uint4*>(uv + (size_t)d * (G / 4)) = make_uint4(u[0], u[1], u[2], u[3]);
+    if (a.split) {
+      // word w of u holds C_U of tokens 8w .. 8w+7 (nibble e = token 8w + e); a split word
+      // covers tokens 16v .. 16v+15: C_T of the first 8 in the upper, of the next 8 in the
+      // lower two bits of each nibble, C_M the other way round
+      const uint32_t t0w = (u[0] & 0xCCCCCCCCu) | ((u[1] >> 2) & 0x33333333u);
+      const uint32_t t1w = (u[2] & 0xCCCCCCCCu) | ((u[3] >> 2) & 0x33333333u);
+      const uint32_t m0w = (u[0] & 0x33333333u) | ((u[1] << 2) & 0xCCCCCCCCu);
+      const uint32_t m1w = (u[2] & 0x33333333u) | ((u[3] << 2) & 0xCCCCCCCCu);
+      *reinterpret_cast<uint2*>(tv + (size_t)d * (G / 8)) = make_uint2(t0w, t1w);
+      *reinterpret_cast<uint2*>(tv + mid + (size_t)d * (G / 8)) = make_uint2(m0w, m1w);
+    } else {
+      *reinterpret_cast<uint4*>(uv + (size_t)d * (G / 4)) = make_uint4(u[0], u[1], u[2], u[3]);
+    }
     *reinterpret_cast<uint4*>(lv + (size_t)d * (G / 4)) = make_uint4(l[0], l[1], l[2], l[3]);
   }
 }
@@ -1488,50 +1636,60 @@ AppendArgsN<NB> narrow(const AppendArgs& f) {
   return a;
 }
 
-template <int D, bool DRAFT, int MODE, bool M16>
+template <int D, bool DRAFT, int MODE, bool M16, int FMT = kFmtNibble>
 const void* attn_fn(int bucket) {
   switch (bucket) {
-    case 1: return (const void*)attn_kernel<D, DRAFT, 1, MODE, M16>;
-    case 8: return (const void*)attn_kernel<D, DRAFT, 8, MODE, M16>;
-    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, MODE, M16>;
+    case 1: return (const void*)attn_kernel<D, DRAFT, 1, MODE, M16, FMT>;
+    case 8: return (const void*)attn_kernel<D, DRAFT, 8, MODE, M16, FMT>;
+    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, MODE, M16, FMT>;
   }
 }
 
-template <int MODE, bool M16>
+template <int MODE, bool M16, int FMT = kFmtNibble>
 const void* attn_fn_dm(int D, bool draft, int bucket) {
-  return D == 128 ? (draft ? attn_fn<128, true, MODE, M16>(bucket) : attn_fn<128, false, MODE, M16>(bucket))
-                  : (draft ? attn_fn<64, true, MODE, M16>(bucket) : attn_fn<64, false, MODE, M16>(bucket));
+  if constexpr (FMT == kFmtSplit2)  // the 2-bit layout serves only the draft
+    return D == 128 ? attn_fn<128, true, MODE, M16, FMT>(bucket) : attn_fn<64, true, MODE, M16, FMT>(bucket);
+  else
+    return D == 128 ? (draft ? attn_fn<128, true, MODE, M16, FMT>(bucket) : attn_fn<128, false, MODE, M16, FMT>(bucket))
+                    : (draft ? attn_fn<64, true, MODE, M16, FMT>(bucket) : attn_fn<64, false, MODE, M16, FMT>(bucket));
 }
 
-template <int D, bool DRAFT, int NB, int MODE, class Full>
+template <int D, bool DRAFT, int NB, int MODE, int FMT, class Full>
 hipError_t launch_attention_n(const Full& f, hipStream_t st) {
   const AttnArgsN<NB, MODE> a = narrow<NB>(f);
   const dim3 grid(a.n_titems_total + a.n_qitems_total, a.H);
-  if (a.meta16)
+  if constexpr (FMT != kFmtNibble)  // the split layout is built with fp32 metadata only
+    hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, false, FMT>), grid, dim3(64), 0, st, a);
+  else if (a.meta16)
     hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, true>), grid, dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, false>), grid, dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 cgrid(a.B * a.m, a.H);
-  hipLaunchKernelGGL((combine_kernel<D, NB, MODE>), cgrid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((combine_kernel<D, NB, MODE, FMT>), cgrid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, bool DRAFT, int MODE, class Full>
+template <int D, bool DRAFT, int MODE, int FMT, class Full>
 hipError_t launch_attention_d(const Full& a, hipStream_t st) {
   switch (batch_bucket(a.B)) {
-    case 1: return launch_attention_n<D, DRAFT, 1, MODE>(a, st);
-    case 8: return launch_attention_n<D, DRAFT, 8, MODE>(a, st);
-    default: return launch_attention_n<D, DRAFT, QS_MAX_BATCH, MODE>(a, st);
+    case 1: return launch_attention_n<D, DRAFT, 1, MODE, FMT>(a, st);
+    case 8: return launch_attention_n<D, DRAFT, 8, MODE, FMT>(a, st);
+    default: return launch_attention_n<D, DRAFT, QS_MAX_BATCH, MODE, FMT>(a, st);
   }
 }
 
-template <int MODE, class Full>
+template <int MODE, int FMT = kFmtNibble, class Full>
 hipError_t launch_attention_m(const Full& a, int D, bool draft, hipStream_t st) {
-  if (D == 128)
-    return draft ? launch_attention_d<128, true, MODE>(a, st) : launch_attention_d<128, false, MODE>(a, st);
-  return draft ? launch_attention_d<64, true, MODE>(a, st) : launch_attention_d<64, false, MODE>(a, st);
+  if constexpr (FMT == kFmtSplit2) {
+    if (!draft) return hipErrorInvalidValue;
+    return D == 128 ? launch_attention_d<128, true, MODE, FMT>(a, st) : launch_attention_d<64, true, MODE, FMT>(a, st);
+  } else {
+    if (D == 128)
+      return draft ? launch_attention_d<128, true, MODE, FMT>(a, st) : launch_attention_d<128, false, MODE, FMT>(a, st);
+    return draft ? launch_attention_d<64, true, MODE, FMT>(a, st) : launch_attention_d<64, false, MODE, FMT>(a, st);
+  }
 }
 
 }  // namespace qs

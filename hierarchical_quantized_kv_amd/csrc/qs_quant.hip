@@ -87,7 +87,12 @@ const void* attn_fn_host(int D, bool draft, int bucket, bool meta16);
 const void* attn_fn_dev(int D, bool draft, int bucket, bool meta16);
 const void* attn_fn_app(int D, bool draft, int bucket, bool meta16);
 const void* attn_fn_gqa(int D, bool draft, int bucket, bool meta16);
-static const void* attn_fn_mode(int mode, int D, bool draft, int bucket, bool meta16) {
+const void* attn_fn_split_host(int D, bool draft, int bucket, int fmt);
+const void* attn_fn_split_app(int D, bool draft, int bucket);
+static const void* attn_fn_mode(int mode, int D, bool draft, int bucket, bool meta16, int fmt) {
+  if (fmt != kFmtNibble)  // split-upper layout: host mode and fused append only
+    return mode == kModeAppend ? attn_fn_split_app(D, draft, bucket)
+                               : attn_fn_split_host(D, draft, bucket, fmt);
   switch (mode) {
     case kModeDev: return attn_fn_dev(D, draft, bucket, meta16);
     case kModeAppend: return attn_fn_app(D, draft, bucket, meta16);
@@ -98,19 +103,22 @@ static const void* attn_fn_mode(int mode, int D, bool draft, int bucket, bool me
 
 // Work-item slots of one attention pass on the current device: compute units times the
 // one-wave workgroups of that kernel a compute unit holds at once (cached per device).
-int attention_slots(int D, bool draft, int B, int mode, bool meta16) {
+int attention_slots(int D, bool draft, int B, int mode, bool meta16, int fmt) {
   constexpr int kMaxDev = 64;
   // filled on first use; concurrent callers at worst compute the same value twice
-  static std::atomic<int> cache[kMaxDev][2][2][2][4][3];
+  static std::atomic<int> cache[kMaxDev][3][2][2][2][4][3];
   int id = 0;
-  if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 3) return 0;
+  if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 3 ||
+      fmt < 0 || fmt > 2)
+    return 0;
   const int bucket = batch_bucket(B);
-  std::atomic<int>& slot = cache[id][meta16][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
+  std::atomic<int>& slot =
+      cache[id][fmt][meta16][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
   const int known = slot.load(std::memory_order_relaxed);
   if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess) return 0;
-  const void* fn = attn_fn_mode(mode, D, draft, bucket, meta16);
+  const void* fn = attn_fn_mode(mode, D, draft, bucket, meta16, fmt);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
   const int n = cus * per_cu;
   slot.store(n, std::memory_order_relaxed);

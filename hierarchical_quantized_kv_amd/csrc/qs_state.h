@@ -35,6 +35,8 @@ inline bool config_ok(const qs_config& c, std::string* why) {
   if (c.gamma_max < 0 || c.gamma_max + 1 > QS_MAX_QUERIES) return fail("gamma_max + 1 must be in 1..16");
   if (c.draft_offset != 0 && c.draft_offset != 8) return fail("draft_offset must be 0 or 8");
   if (c.meta_fp16 != 0 && c.meta_fp16 != 1) return fail("meta_fp16 must be 0 or 1");
+  if (c.split_upper != 0 && c.split_upper != 1) return fail("split_upper must be 0 or 1");
+  if (c.split_upper && c.meta_fp16) return fail("split_upper is built with fp32 metadata only");
   return true;
 }
 

@@ -95,6 +95,13 @@ typedef struct {
                            the fp16 range saturating at +-65504.  Storing b rather than z keeps
                            a degenerate group exact: its scale (clamped to 1e-8) rounds to 0
                            and b is the group's value.                                         */
+  int32_t split_upper;  /* upper-plane layout: 0 = one 4-bit plane C_U; 1 = C_U = 4*C_T + C_M
+                           stored as two 2-bit planes, the top bits C_T = C8 >> 6 and the
+                           middle bits C_M = (C8 >> 4) & 3, so that a 2-bit draft
+                           (qs_attend_draft_bits) reads C_T alone while the 4-bit draft and
+                           verify read both (same bytes as layout 0).  Needs meta_fp16 = 0;
+                           serves the host-mode and fused calls (not grouped queries or device
+                           mode, which return QS_ERR_INVALID_ARG).                             */
 } qs_config;
 
 /* Byte offsets (from the arena base) and sizes of the arena sections.  Every section starts
@@ -107,6 +114,14 @@ typedef struct {
  *                                      of G/2 tokens, each channel-major.  Byte j of the row of
  *                                      channel d in half e holds token e*G/2 + 2j of the group
  *                                      in bits 0-3 and token e*G/2 + 2j + 1 in bits 4-7.
+ *  split_upper = 1: within the (layer, sequence, head) stripe of uk (T*D/2 bytes) the first
+ *                 half is the C_T plane and the second the C_M plane, each [T][D/4]; within
+ *                 the stripe of uv (NG*D*G/2 bytes) likewise, each [NG][2][D][G/8].  A row of
+ *                 either plane is made of 32-bit little-endian words, word w covering 16
+ *                 entries 16w .. 16w+15 (channels of a key row, tokens of a value row): nibble
+ *                 e of a C_T word holds C_T(16w + e) in bits 2-3 and C_T(16w + 8 + e) in bits
+ *                 0-1; nibble e of a C_M word holds C_M(16w + e) in bits 0-1 and C_M(16w + 8 + e)
+ *                 in bits 2-3.  lk, lv are as above.
  *  kmeta    f32 [L][B][H][NG][D][2]    key (scale, zero-point) per group and channel;
  *                                      meta_fp16: f16 [L][B][H][NG][D][2] (scale, offset).
  *  vmeta    f32 [L][B][H][T][2]        value (scale, zero-point) per token;
@@ -233,6 +248,20 @@ qs_status qs_attend_draft(qs_cache* cache, int32_t layer, const void* d_q, float
  * Verification Loop"; Pith review, one-line read.] */
 qs_status qs_attend_verify(qs_cache* cache, int32_t layer, const void* d_q, int32_t m,
                            float sm_scale, float* d_out, void* stream);
+
+/* Draft attention on the top `bits` bits of every code: the same call as qs_attend_draft with
+ * quantized k, v dequantized as ((C8 with its low 8 - bits bits replaced by
+ * draft_offset * 2^(4 - bits)) - z) * s.  bits = 4 is qs_attend_draft; bits = 2 reads only the
+ * C_T plane of the split-upper layout: ((64*C_T + 4*draft_offset) - z) * s, 80 bytes per
+ * quantized token-head at head_dim 128 against 144 for the 4-bit draft.
+ *   d_q   : fp16 [B][H][D]      d_out : fp32 [B][H][D]
+ * Errors: as qs_attend_draft; QS_ERR_INVALID_ARG if bits is not 2 or 4, or bits = 2 without
+ * split_upper.  [Pith review of arXiv:2502.10424, "Editorial extensions" / "Reading between
+ * the lines": the top k bits for the draft and all bits for the verifier, the paper using
+ * k = 4; the replacement of the dropped bits carries the centring of QuantSpec Guide's
+ * unpack_for_draft ("| 0x08" for k = 4) to every k.] */
+qs_status qs_attend_draft_bits(qs_cache* cache, int32_t layer, const void* d_q, int32_t bits,
+                               float sm_scale, float* d_out, void* stream);
 
 /* Grouped queries: g query heads share each cached (key/value) head -- query head h*g + r
  * (r < g) attends over cached head h, so the cache holds H = n_heads heads and the queries

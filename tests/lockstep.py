@@ -26,14 +26,15 @@ def log(msg):
 
 class Lockstep:
     def __init__(self, n_layers, batch, n_heads, head_dim, max_ctx, gamma_max, heads=None,
-                 layers=None, draft_offset=8, tag="", meta_fp16=False):
+                 layers=None, draft_offset=8, tag="", meta_fp16=False, split_upper=False):
         self.B, self.H, self.D, self.L = batch, n_heads, head_dim, n_layers
         self.G = 128
         self.heads = list(range(n_heads)) if heads is None else list(heads)
         self.layers = list(range(n_layers)) if layers is None else list(layers)
         self.tag = tag
+        self.split_upper = split_upper
         self.gpu = Cache(n_layers, batch, n_heads, head_dim, max_ctx, gamma_max,
-                         draft_offset=draft_offset, meta_fp16=meta_fp16)
+                         draft_offset=draft_offset, meta_fp16=meta_fp16, split_upper=split_upper)
         self.orc = {l: OracleCache(1, batch, len(self.heads), head_dim, self.G, max_ctx,
                                    gamma_max, draft_offset, meta_fp16) for l in self.layers}
         self.max_rel = 0.0
@@ -84,6 +85,14 @@ class Lockstep:
             self._cmp_out(out[:, self.heads], ref, f"draft L{layer}")
         return out
 
+    def draft_bits(self, layer, q, bits, sm_scale=1.0):
+        out = self.gpu.attend_draft_bits(layer, q, bits, sm_scale)
+        if layer in self.orc:
+            ref = self.orc[layer].attend_draft_bits(0, self._host_heads(q, 1), bits, sm_scale)
+            torch.cuda.synchronize()
+            self._cmp_out(out[:, self.heads], ref, f"draft{bits} L{layer}")
+        return out
+
     def verify(self, layer, q, sm_scale=1.0):
         out = self.gpu.attend_verify(layer, q, sm_scale)
         if layer in self.orc:
@@ -103,6 +112,8 @@ class Lockstep:
         """Bit-exact comparison of the live part of every section for the sampled heads."""
         nq, nt, head = self.check_state(layer)
         img = self.orc[layer].export_layer(0)
+        if self.split_upper:  # the upper planes as the top and middle 2-bit planes
+            img.update(self.orc[layer].export_upper_split(0))
         hs = torch.as_tensor(self.heads, device="cuda")
         G = self.G
         torch.cuda.synchronize()
@@ -111,12 +122,13 @@ class Lockstep:
             sec = lambda name: self.gpu.section(name, layer)[b].index_select(0, hs)
             # fp16 metadata is compared through its exact fp32 values (the oracle keeps floats)
             host = lambda t: t.float().cpu().numpy() if t.dtype == torch.float16 else t.cpu().numpy()
-            for name, rows in (("uk", q), ("lk", q), ("vmeta", q)):
+            upper_k, upper_v = (("tk", "mk"), ("tv", "mv")) if self.split_upper else (("uk",), ("uv",))
+            for name, rows in [(n, q) for n in upper_k] + [("lk", q), ("vmeta", q)]:
                 got = host(sec(name)[:, :rows])
                 ref = img[name][b, :, :rows]
                 assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), \
                     f"{self.tag} L{layer} b{b} {name} differs"
-            for name in ("uv", "lv", "kmeta"):
+            for name in upper_v + ("lv", "kmeta"):
                 got = host(sec(name)[:, : q // G])
                 ref = img[name][b, :, : q // G]
                 assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), \

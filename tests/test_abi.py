@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 def cfg(**kw):
     base = dict(n_layers=2, batch=3, n_heads=4, head_dim=128, group=G, max_ctx=8 * G,
-                gamma_max=6, draft_offset=8, meta_fp16=0)
+                gamma_max=6, draft_offset=8, meta_fp16=0, split_upper=0)
     base.update(kw)
     return QsConfig(*[base[f] for f, _ in QsConfig._fields_])
 
