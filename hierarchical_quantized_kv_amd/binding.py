@@ -25,7 +25,8 @@ EXPORTS = ("qs_arena_bytes", "qs_arena_layout", "qs_cache_create", "qs_cache_des
            "qs_spec_accept", "qs_state_to_device", "qs_state_from_device", "qs_append_dev",
            "qs_rollback_dev", "qs_flush_dev", "qs_commit_dev", "qs_attend_draft_dev",
            "qs_attend_verify_dev", "qs_append_attend_draft", "qs_append_attend_verify",
-           "qs_attend_draft_gqa", "qs_attend_verify_gqa", "qs_attend_draft_bits")
+           "qs_attend_draft_gqa", "qs_attend_verify_gqa", "qs_attend_draft_bits",
+           "qs_spec_accept_static")
 
 # Bits of the device-mode error word (include/quantspec.h, device mode).
 DEV_ERR_APPEND, DEV_ERR_ROLLBACK, DEV_ERR_FLUSH, DEV_ERR_ATTEND = 1, 2, 4, 8
@@ -86,6 +87,7 @@ def lib():
         L.qs_spec_workspace_bytes.argtypes = [I32, I32, I32]
         L.qs_spec_workspace_bytes.restype = ctypes.c_size_t
         L.qs_spec_accept.argtypes = [P, P, P, P, I32, I32, I32, P, ctypes.c_size_t, P, P, P]
+        L.qs_spec_accept_static.argtypes = [P, P, P, P, I32, I32, I32, P, P, P]
         L.qs_state_to_device.argtypes = [P, P]
         L.qs_state_from_device.argtypes = [P, P, PI]
         L.qs_append_dev.argtypes = [P, I32, P, P, I32, P]
@@ -444,4 +446,35 @@ def spec_accept(target_logits, draft_logits, draft_tokens, uniforms, workspace=N
     if st != QS_OK:
         raise QsError(st, "qs_spec_accept")
     return n, nxt
+
+
+SPEC_STATIC_BYTES = 4 << 20  # the library's own workspace of qs_spec_accept_static, per GPU
+
+
+def spec_accept_static(target_logits, draft_logits, draft_tokens, uniforms, n_out, next_out,
+                       stream=None):
+    """qs_spec_accept_static: the accept / correct step with the library's device-resident
+    workspace, for callers that cannot allocate (graph capture).  Same tensors as spec_accept;
+    the outputs n_out / next_out (device int32 [B]) must be given."""
+    import torch
+    B, g1, V = target_logits.shape
+    gamma = g1 - 1
+    for t, dt, shape, name in ((target_logits, torch.float32, (B, gamma + 1, V), "target_logits"),
+                               (draft_logits, torch.float32, (B, gamma, V), "draft_logits"),
+                               (draft_tokens, torch.int32, (B, gamma), "draft_tokens"),
+                               (uniforms, torch.float32, (B, gamma + 1), "uniforms"),
+                               (n_out, torch.int32, (B,), "n_out"),
+                               (next_out, torch.int32, (B,), "next_out")):
+        if not (t.is_cuda and t.dtype == dt and t.is_contiguous() and tuple(t.shape) == shape
+                and t.device == target_logits.device):
+            raise ValueError(f"{name}: expected a contiguous {dt} tensor of shape {shape} on "
+                             f"{target_logits.device}")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    P = ctypes.c_void_p
+    st = lib().qs_spec_accept_static(P(target_logits.data_ptr()), P(draft_logits.data_ptr()),
+                                     P(draft_tokens.data_ptr()), P(uniforms.data_ptr()), B, gamma,
+                                     V, P(n_out.data_ptr()), P(next_out.data_ptr()),
+                                     P(s.cuda_stream))
+    if st != QS_OK:
+        raise QsError(st, "qs_spec_accept_static")
 

@@ -30,6 +30,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/quantspec.h"
 
 namespace qs_sample {
@@ -426,6 +428,38 @@ __global__ __launch_bounds__(kPartThreads) void accept_kernel(const float* __res
   }
 }
 
+// Workspace of qs_spec_accept_static: a file-scope device array, one copy per GPU, held until
+// the process ends.  Host code never uses its name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress (scratch_ptr).
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of the current GPU's scratch array, looked up once per device (with that
+// device current) and kept; null if the lookup fails.
+void* scratch_ptr(hipError_t* err) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDev] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  *err = hipSuccess;
+  return ptr[dev];
+}
+
 }  // namespace qs_sample
 
 extern "C" {
@@ -461,6 +495,20 @@ qs_status qs_spec_accept(const float* d_target_logits, const float* d_draft_logi
                      d_draft_logits, d_uniforms, gamma, vocab, ws, d_n_accepted, d_next_token);
   if (hipGetLastError() != hipSuccess) return QS_ERR_DEVICE;
   return QS_OK;
+}
+
+qs_status qs_spec_accept_static(const float* d_target_logits, const float* d_draft_logits,
+                                const int32_t* d_draft_tokens, const float* d_uniforms,
+                                int32_t batch, int32_t gamma, int32_t vocab, int32_t* d_n_accepted,
+                                int32_t* d_next_token, void* stream) {
+  const size_t need = qs_spec_workspace_bytes(batch, gamma, vocab);
+  if (need == 0) return QS_ERR_INVALID_ARG;
+  if (need > qs_sample::kScratchBytes) return QS_ERR_BUFFER;
+  hipError_t e = hipSuccess;
+  void* ws = qs_sample::scratch_ptr(&e);
+  if (!ws) return QS_ERR_DEVICE;
+  return qs_spec_accept(d_target_logits, d_draft_logits, d_draft_tokens, d_uniforms, batch, gamma,
+                        vocab, ws, qs_sample::kScratchBytes, d_n_accepted, d_next_token, stream);
 }
 
 }  // extern "C"

@@ -226,6 +226,23 @@ qs_status qs_spec_accept(const float* d_target_logits, const float* d_draft_logi
                          int32_t gamma, int32_t vocab, void* d_workspace, size_t workspace_bytes,
                          int32_t* d_n_accepted, int32_t* d_next_token, void* stream);
 
+/* qs_spec_accept for callers that cannot allocate (code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc): the same step and arguments without the workspace,
+ * which is instead a device array inside the library (one copy per GPU of 4 MiB = 4194304
+ * bytes, held until the process ends; its device address is looked up once per GPU, with that
+ * GPU current, on the first call there).  Allocates nothing, on the host or the device.  The
+ * array is fully rewritten before it is read by every call, so nothing carries over between
+ * calls; but all calls on one GPU share it, so calls whose kernels may overlap on one GPU (on
+ * different streams, or from different threads without ordering) race: order them on one
+ * stream.
+ * Errors: as qs_spec_accept; QS_ERR_BUFFER if qs_spec_workspace_bytes(batch, gamma, vocab)
+ * exceeds 4 MiB (e.g. batch 256, gamma 15, vocab 128256 fits: 3.2 MB); QS_ERR_DEVICE if the
+ * array's address cannot be found. */
+qs_status qs_spec_accept_static(const float* d_target_logits, const float* d_draft_logits,
+                                const int32_t* d_draft_tokens, const float* d_uniforms,
+                                int32_t batch, int32_t gamma, int32_t vocab, int32_t* d_n_accepted,
+                                int32_t* d_next_token, void* stream);
+
 /* Draft attention: one query per (sequence, head) over the upper plane of every quantized
  * token plus every tail token.
  *   d_q   : fp16 [B][H][D]      d_out : fp32 [B][H][D]
