@@ -110,107 +110,17 @@ def prefill_bytes(n, H, D):
     return (n // G) * flush_bytes(H, D) + append_bytes(n % G, H, D)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=4, choices=sorted(CONFIGS))
-    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-fuse", action="store_true",
-                    help="separate append and attention calls instead of the fused ones")
-    ap.add_argument("--no-gqa", action="store_true",
-                    help="skip the grouped-query layer (gqa: null)")
-    ap.add_argument("--no-meta16", action="store_true",
-                    help="skip the fp16-metadata comparison (meta16: null)")
-    ap.add_argument("--no-topk", action="store_true",
-                    help="skip the top-k-bit draft comparison (topk: null)")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the graph-replayed step (graph_step: null)")
-    ap.add_argument("--cpu-threads", type=int, default=None,
-                    help="host threads of the second, all-cores oracle timing (default: the "
-                         "CPUs this process may run on)")
-    ap.add_argument("--flush-reps", type=int, default=4,
-                    help="timed all-layer flushes (each quantizes one G-token half per head)")
-    ap.add_argument("--calibration-copy-mib", type=int, default=0,
-                    help="run one plain device-to-device copy of this size first (reference "
-                         "kernel for scaling HBM byte counters)")
-    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the HBM-traffic profile from two rocprofv3 --pmc output folders "
-                         "(FETCH_SIZE, WRITE_SIZE) of this script and exit")
-    args = ap.parse_args()
-    if args.traffic_summary:
-        write_traffic_summary(*args.traffic_summary, args)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
-              f"(got --gpus {args.gpus})", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
+def time_steps(torch, cache, stream, dev, config, L, H, D, gamma, steps, warmup, fuse):
+    """Runs `warmup` untimed and `steps` timed speculation rounds over all L layers of `cache`
+    (each: gamma x (append 1 + draft) per layer, rollback gamma, append gamma+1 + verify,
+    rollback by the rejected count, flush), inputs resident in HBM.  HIP events bracket the
+    draft and verify calls of one layer per timed step (the layer rotates from step to step):
+    recording them around every call would add their own cost to the step time."""
     from hierarchical_quantized_kv_amd import synth
-    from hierarchical_quantized_kv_amd.binding import Cache
-
-    cfg = CONFIGS[args.config]
-    L = args.layers or cfg["layers"]
-    H, D, ctx, gamma = cfg["heads"], cfg["D"], cfg["ctx"], cfg["gamma"]
     m = gamma + 1
-    cpu_threads = args.cpu_threads or host_cpus()[0]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    max_ctx = ctx + 16 * G
-    print(f"bench: config {args.config} ({cfg['name']}), {L} layers, ctx {ctx}", file=sys.stderr,
-          flush=True)
-
-    if args.calibration_copy_mib:
-        n = args.calibration_copy_mib << 19  # fp16 elements
-        src = torch.ones(n, dtype=torch.float16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    stream = torch.cuda.current_stream()
-    # Short launches (a layer's prefill, the bulk flush) are timed behind a spin kernel of
-    # ~200 us: otherwise the GPU can sit idle when it reaches the first event and the interval
-    # would include the host's launch latency of the timed call.
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    torch.cuda._sleep(1_000_000)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    spin_cycles = int(1_000_000 * 200.0 / max(c0.elapsed_time(c1) * 1e3, 1.0))
-
-    # Prefill ("quantize once"): each layer's ctx + 64-token prompt in one qs_prefill call (ctx / G
-    # groups quantized, 64 tokens to the tail), timed per layer.
-    cache = Cache(L, 1, H, D, max_ctx, gamma)
-    t0 = time.time()
-    cpu_inputs = None
-    pf_ev = []
-    for layer in range(L):
-        out_ch = synth.outlier_channels(H, D, synth.seed_for(args.config, layer, "outlier"))
-        k, v = synth.kv_device(torch, 1, ctx + 64, H, D,
-                               synth.seed_for(args.config, layer, "k"),
-                               synth.seed_for(args.config, layer, "v"), dev, outliers=out_ch)
-        torch.cuda._sleep(spin_cycles)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        cache.prefill(layer, k, v)
-        e1.record(stream)
-        pf_ev.append((e0, e1, prefill_bytes(ctx + 64, H, D)))
-        if layer == 0 and not args.no_cpu_baseline:
-            hs = list(range(cpu_sample_heads(cpu_threads, H)))
-            cpu_inputs = (k[:, :, hs].cpu().numpy(), v[:, :, hs].cpu().numpy())
-        del k, v
-    torch.cuda.synchronize()
-    print(f"bench: prefill done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-
-    # per-step inputs, generated up front (resident in HBM before timing)
-    n_steps = args.warmup + args.steps
+    n_steps = warmup + steps
     gen = torch.Generator(device=dev).manual_seed(12345)
-    rng = np.random.Generator(np.random.PCG64(synth.seed_for(args.config, 0, "accept")))
+    rng = np.random.Generator(np.random.PCG64(synth.seed_for(config, 0, "accept")))
     accept = [synth.acceptance(rng, gamma) for _ in range(n_steps)]
 
     def rnd(*shape, scale=1.0):
@@ -225,18 +135,12 @@ def main():
             qv=rnd(L, 1, m, H, D, scale=1 / math.sqrt(D))))
     out_d = torch.empty((1, H, D), dtype=torch.float32, device=dev)
     out_v = torch.empty((1, m, H, D), dtype=torch.float32, device=dev)
-
     ev = {"draft": [], "verify": []}
-    fuse = not args.no_fuse
-    step_bytes = []
 
-    # HIP events bracket the draft and verify calls of one layer per timed step (the layer
-    # rotates from step to step): recording them around every call would add their own cost to
-    # the step time.
     def run_step(s, timed):
         x = steps_in[s]
         nbytes = 0
-        ev_layer = (s - args.warmup) % L if timed else -1  # -1: no events in warmup
+        ev_layer = (s - warmup) % L if timed else -1  # -1: no events in warmup
         # A draft step is the token's append followed by the draft call; fused (the default)
         # both are one call, whose event interval and bytes then include the append.
         for j in range(gamma):
@@ -285,18 +189,178 @@ def main():
         nbytes += int(flushed[0]) * L * flush_bytes(H, D)
         return nbytes
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         run_step(s, False)
     torch.cuda.synchronize()
+    step_bytes = []
     t0 = time.perf_counter()
-    for s in range(args.warmup, n_steps):
+    for s in range(warmup, n_steps):
         step_bytes.append(run_step(s, True))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
     total_bytes = sum(step_bytes)
-    value = total_bytes / elapsed / 1e9
+    return dict(ms_per_step=elapsed * 1e3 / steps, value=total_bytes / elapsed / 1e9,
+                elapsed=elapsed, total_bytes=total_bytes, ev=ev, steps_in=steps_in,
+                accept=accept, out_d=out_d, out_v=out_v, gen=gen)
+
+
+def summarize_events(events):
+    """(average us, GB/s, bytes, samples dropped) of (event, event, bytes) samples.  When the
+    GPU has caught up with the host (short calls at 32k), an event interval can also hold a
+    stall of the host thread (measured once: one sample of ~30 ms among 40 of ~38 us); samples
+    above twice the median are left out, and counted."""
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b, _ in events])   # us
+    by = [n for _, _, n in events]
+    keep = t <= 2.0 * np.median(t)
+    avg_us = float(t[keep].mean())
+    return avg_us, float(np.mean(by)) / (avg_us * 1e-6) / 1e9, float(np.mean(by)), int((~keep).sum())
+
+
+def measure_ctx32k(torch, stream, dev, steps, warmup, fuse):
+    """The Llama-2-7B-32K-shaped stack (32 layers x 32 heads x head_dim 128, ctx 32768 + 64-token
+    tail, gamma 4) run with the same step as the headline workload on a cache of its own:
+    step time, and the draft / verify calls of one layer per step (events, as for the
+    headline)."""
+    from hierarchical_quantized_kv_amd import synth
+    from hierarchical_quantized_kv_amd.binding import Cache
+    cfg = CONFIGS[3]
+    L, H, D, ctx, gamma = cfg["layers"], cfg["heads"], cfg["D"], cfg["ctx"], cfg["gamma"]
+    cache = Cache(L, 1, H, D, ctx + 16 * G, gamma)
+    for layer in range(L):
+        out_ch = synth.outlier_channels(H, D, synth.seed_for(3, layer, "outlier"))
+        k, v = synth.kv_device(torch, 1, ctx + 64, H, D, synth.seed_for(3, layer, "k"),
+                               synth.seed_for(3, layer, "v"), dev, outliers=out_ch)
+        cache.prefill(layer, k, v)
+        del k, v
+    torch.cuda.synchronize()
+    st = time_steps(torch, cache, stream, dev, 3, L, H, D, gamma, steps, warmup, fuse)
+    d_us, d_gbs, d_bytes, d_drop = summarize_events(st["ev"]["draft"])
+    v_us, v_gbs, v_bytes, v_drop = summarize_events(st["ev"]["verify"])
+    ms_per_step, value = st["ms_per_step"], st["value"]
+    cache.close()
+    del cache, st
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg['name']}: {L} layers x {H} heads x head_dim {D}, batch 1, ctx "
+                        f"{ctx} + 64-token tail, gamma {gamma} ({gamma + 1}-query verify), 1% key "
+                        f"channels x8; fused append + attend calls",
+            "ms_per_step": round(ms_per_step, 4), "value_gbs": round(value, 2),
+            "draft_us": round(d_us, 2), "draft_bytes": int(d_bytes), "draft_gbs": round(d_gbs, 1),
+            "draft_frac": round(d_gbs / PEAK_HBM_GBS, 4),
+            "verify_us": round(v_us, 2), "verify_bytes": int(v_bytes),
+            "verify_gbs": round(v_gbs, 1), "verify_frac": round(v_gbs / PEAK_HBM_GBS, 4),
+            "samples_dropped": {"draft": d_drop, "verify": v_drop}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4, choices=sorted(CONFIGS))
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="separate append and attention calls instead of the fused ones")
+    ap.add_argument("--no-gqa", action="store_true",
+                    help="skip the grouped-query layer (gqa: null)")
+    ap.add_argument("--no-meta16", action="store_true",
+                    help="skip the fp16-metadata comparison (meta16: null)")
+    ap.add_argument("--no-ctx32k", action="store_true",
+                    help="skip the 32k stack's step (ctx32k: null; implied by --config 3)")
+    ap.add_argument("--no-topk", action="store_true",
+                    help="skip the top-k-bit draft comparison (topk: null)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replayed step (graph_step: null)")
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="host threads of the second, all-cores oracle timing (default: the "
+                         "CPUs this process may run on)")
+    ap.add_argument("--flush-reps", type=int, default=20,
+                    help="timed all-layer flushes (each quantizes one G-token half per head)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this size first (reference "
+                         "kernel for scaling HBM byte counters)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM-traffic profile from two rocprofv3 --pmc output folders "
+                         "(FETCH_SIZE, WRITE_SIZE) of this script and exit")
+    args = ap.parse_args()
+    if args.traffic_summary:
+        write_traffic_summary(*args.traffic_summary, args)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(got --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hierarchical_quantized_kv_amd import synth
+    from hierarchical_quantized_kv_amd.binding import Cache
+
+    cfg = CONFIGS[args.config]
+    L = args.layers or cfg["layers"]
+    H, D, ctx, gamma = cfg["heads"], cfg["D"], cfg["ctx"], cfg["gamma"]
+    m = gamma + 1
+    cpu_threads = args.cpu_threads or host_cpus()[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    max_ctx = ctx + 32 * G  # room for the steps' flushes and the timed bulk flushes
+    print(f"bench: config {args.config} ({cfg['name']}), {L} layers, ctx {ctx}", file=sys.stderr,
+          flush=True)
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 19  # fp16 elements
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    # Short launches (a layer's prefill, the bulk flush) are timed behind a spin kernel of
+    # ~200 us: otherwise the GPU can sit idle when it reaches the first event and the interval
+    # would include the host's launch latency of the timed call.
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    spin_cycles = int(1_000_000 * 200.0 / max(c0.elapsed_time(c1) * 1e3, 1.0))
+
+    # Prefill ("quantize once"): each layer's ctx + 64-token prompt in one qs_prefill call (ctx / G
+    # groups quantized, 64 tokens to the tail), timed per layer.
+    cache = Cache(L, 1, H, D, max_ctx, gamma)
+    t0 = time.time()
+    cpu_inputs = None
+    pf_ev = []
+    for layer in range(L):
+        out_ch = synth.outlier_channels(H, D, synth.seed_for(args.config, layer, "outlier"))
+        k, v = synth.kv_device(torch, 1, ctx + 64, H, D,
+                               synth.seed_for(args.config, layer, "k"),
+                               synth.seed_for(args.config, layer, "v"), dev, outliers=out_ch)
+        torch.cuda._sleep(spin_cycles)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.prefill(layer, k, v)
+        e1.record(stream)
+        pf_ev.append((e0, e1, prefill_bytes(ctx + 64, H, D)))
+        if layer == 0 and not args.no_cpu_baseline:
+            hs = list(range(cpu_sample_heads(cpu_threads, H)))
+            cpu_inputs = (k[:, :, hs].cpu().numpy(), v[:, :, hs].cpu().numpy())
+        del k, v
+    torch.cuda.synchronize()
+    print(f"bench: prefill done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    fuse = not args.no_fuse
+    st = time_steps(torch, cache, stream, dev, args.config, L, H, D, gamma, args.steps,
+                    args.warmup, fuse)
+    steps_in, accept, out_d, out_v, ev = st["steps_in"], st["accept"], st["out_d"], st["out_v"], st["ev"]
+    ms_per_step, value, elapsed = st["ms_per_step"], st["value"], st["elapsed"]
+    total_bytes = st["total_bytes"]
     print(f"bench: {args.steps} timed steps in {elapsed:.3f}s", file=sys.stderr, flush=True)
+    gen = st["gen"]
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(shape, generator=gen, device=dev) * scale).to(torch.float16)
 
     # The same step replayed from a HIP graph (device mode): the step's calls are captured once
     # with the counters in device memory, and each replay advances them on the device; only the
@@ -356,12 +420,9 @@ def main():
     dropped = {}
 
     def summarize(events, kind):
-        t = np.array([a.elapsed_time(b) * 1e3 for a, b, _ in events])   # us
-        by = [n for _, _, n in events]
-        keep = t <= 2.0 * np.median(t)
-        dropped[kind] = int((~keep).sum())
-        avg_us = float(t[keep].mean())
-        return avg_us, float(np.mean(by)) / (avg_us * 1e-6) / 1e9, float(np.mean(by))
+        us, gbs, nbytes, n_drop = summarize_events(events)
+        dropped[kind] = n_drop
+        return us, gbs, nbytes
 
     d_us, d_gbs, d_bytes = summarize(ev["draft"], "draft")
     v_us, v_gbs, v_bytes = summarize(ev["verify"], "verify")
@@ -369,6 +430,8 @@ def main():
     p_us, p_gbs, p_bytes = summarize(pf_ev, "prefill")
     sa = {sb: summarize(e, f"spec_accept_batch{sb}") for sb, e in sa_ev.items()}
 
+    ctx32k = None if (args.no_ctx32k or args.config == 3) else measure_ctx32k(
+        torch, stream, dev, args.steps, args.warmup, fuse)
     gqa = None if args.no_gqa else measure_gqa(torch, stream, spin_cycles, dev)
     meta16 = None if args.no_meta16 else measure_meta16(
         torch, stream, spin_cycles, dev, cfg["name"], ctx=cfg["ctx"], H=cfg["heads"],
@@ -441,6 +504,7 @@ def main():
                            "bound": "latency (dependent round trips)" if sb == 1 else "hbm"}
             for sb, (us, gbs, nb) in sa.items()},
         "graph_step": graph_line,
+        "ctx32k": ctx32k,
         "gqa": gqa,
         "meta16": meta16,
         "topk": topk,

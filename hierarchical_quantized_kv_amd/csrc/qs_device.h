@@ -139,12 +139,10 @@ __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint2 split_nibbles(uint32_t t, uint32_t m) {
   return make_uint2(bfi(0xCCCCCCCCu, t, m), bfi(0xCCCCCCCCu, t << 2, m >> 2));
 }
-// Signed 2-bit draft words of a top-plane word: nibble e = 4 C_T - 8 (as a signed nibble) of
-// entries 0..7 and 8..15.  Flipping the upper bit of every 2-bit field turns C_T into C_T ^ 2,
-// and 4 (C_T ^ 2) read as a signed nibble is 4 C_T - 8.
-__device__ __forceinline__ uint2 top2_signed(uint32_t t) {
-  const uint32_t x = t ^ 0xAAAAAAAAu;
-  return make_uint2(x & 0xCCCCCCCCu, (x << 2) & 0xCCCCCCCCu);
+// 2-bit draft words of a top-plane word: nibble e = C_T (0..3, a non-negative signed nibble)
+// of entries 0..7 and of entries 8..15.
+__device__ __forceinline__ uint2 top2_values(uint32_t t) {
+  return make_uint2((t >> 2) & 0x33333333u, t & 0x33333333u);
 }
 __device__ __forceinline__ uint32_t bld4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNt);
@@ -370,9 +368,11 @@ __device__ __forceinline__ void digit_bytes(int xa, int xb, uint32_t& even, uint
 
 // sum over 4 signed-nibble words u[] (32 nibbles, each the signed 4-bit value of one entry) of
 // the digit-weighted signed dot products, as a float in units of the fixed-point weights:
-// sum_j 16^j sum_k dot8(d[j].k, u[k]), evaluated as two Horner chains (digits 5..3 and 2..0;
-// |chain| <= 2048 * 273 fits int32).
+// sum_j 16^j sum_k dot8(d[j].k, u[k]) over the ND lowest digit planes, evaluated as two Horner
+// chains (digits ND-1..3 and 2..0; |chain| <= 2048 * 273 fits int32).
+template <int ND = kDigits>
 __device__ __forceinline__ float digit_dot(const uint4 (&d)[kDigits], uint4 w) {
+  static_assert(ND == 5 || ND == 6, "five or six digit planes");
   const int u[4] = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
   auto plane = [&](int j, int acc) {
     acc = __builtin_amdgcn_sdot8((int)d[j].x, u[0], acc, false);
@@ -380,8 +380,8 @@ __device__ __forceinline__ float digit_dot(const uint4 (&d)[kDigits], uint4 w) {
     acc = __builtin_amdgcn_sdot8((int)d[j].z, u[2], acc, false);
     return __builtin_amdgcn_sdot8((int)d[j].w, u[3], acc, false);
   };
-  int hi = plane(5, 0);
-  hi = plane(4, hi << 4);
+  int hi = plane(ND - 1, 0);
+  if constexpr (ND == 6) hi = plane(4, hi << 4);
   hi = plane(3, hi << 4);
   int lo = plane(2, 0);
   lo = plane(1, lo << 4);
@@ -389,12 +389,14 @@ __device__ __forceinline__ float digit_dot(const uint4 (&d)[kDigits], uint4 w) {
   return fmaf((float)hi, 4096.f, (float)lo);
 }
 
-// Power-of-two fixed-point unit for weights up to xmax: |x| / unit < 2^22.
+// Power-of-two fixed-point unit for weights up to xmax: |x| / unit < 2^BITS (22 for six
+// digits; 18 for five, whose top digit then stays zero).
+template <int BITS = 22>
 __device__ __forceinline__ void fixed_unit(float xmax, float& inv_unit, float& unit) {
   int e;
   frexpf(xmax, &e);  // xmax < 2^e (e = 0 for xmax = 0)
-  inv_unit = ldexpf(1.f, 22 - e);
-  unit = ldexpf(1.f, e - 22);
+  inv_unit = ldexpf(1.f, BITS - e);
+  unit = ldexpf(1.f, e - BITS);
 }
 
 // Planes and metadata of one group, as loaded by one lane: per key load 32 channels of one
@@ -415,8 +417,8 @@ struct DraftBuf {
   MetaT<M16> vm;  // value metadata of tokens 2*lane, 2*lane+1
 };
 
-// The signed-nibble words digit_dot takes (nibble = upper nibble - 8, or for the 2-bit draft
-// 4 C_T - 8) of one load: its 32 entries in order, 8 per word.
+// The signed-nibble words digit_dot takes (nibble = upper nibble - 8; for the 2-bit draft the
+// top bits C_T in 0..3) of one load: its 32 entries in order, 8 per word.
 template <int FMT>
 __device__ __forceinline__ uint4 signed_words(const DraftW<FMT>& x, uint2 mid) {
   if constexpr (FMT == kFmtNibble) {
@@ -425,7 +427,7 @@ __device__ __forceinline__ uint4 signed_words(const DraftW<FMT>& x, uint2 mid) {
     const uint2 a = split_nibbles(x.x ^ 0xAAAAAAAAu, mid.x), b = split_nibbles(x.y ^ 0xAAAAAAAAu, mid.y);
     return make_uint4(a.x, a.y, b.x, b.y);
   } else {
-    const uint2 a = top2_signed(x.x), b = top2_signed(x.y);
+    const uint2 a = top2_values(x.x), b = top2_values(x.y);
     return make_uint4(a.x, a.y, b.x, b.y);
   }
 }
@@ -498,9 +500,13 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm,
   using S = DraftShape<D>;
   const int lane = threadIdx.x;
   const int kc = lane % S::KL, kt = lane / S::KL, vr = lane & 3;
-  // 16 U + off - z = 16 u + (128 + off - z); the 2-bit draft: 64 C_T + 4 off - z =
-  // 16 (4 C_T - 8) + (128 + 4 off - z)
-  const float c = 128.f + (FMT == kFmtSplit2 ? 4.f : 1.f) * a.draft_offset;
+  // 16 U + off - z = 16 u + (128 + off - z); the 2-bit draft: 64 C_T + (4 off - z), its
+  // weights on five digits (18 bits: the rounding stays far below the 2-bit codes' steps)
+  constexpr bool k2 = FMT == kFmtSplit2;
+  constexpr int ND = k2 ? 5 : kDigits;
+  constexpr int WB = k2 ? 18 : 22;
+  constexpr float kStep = k2 ? 64.f : 16.f;  // weight of one unit of the dot-product entries
+  const float c = k2 ? 4.f * a.draft_offset : 128.f + a.draft_offset;
 
   __syncthreads();  // the previous group's LDS reads are done
   // key weights q' = q s (channels 2 lane, 2 lane + 1) as digit planes; the score bias
@@ -511,17 +517,17 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm,
   float bias = M16 ? q0 * fmaf(km.x, c, km.y) + q1 * fmaf(km.z, c, km.w)
                    : qa * (c - km.y) + qb * (c - km.w);
   float qunit, qinv;
-  fixed_unit(wave_max_all(fmaxf(fabsf(qa), fabsf(qb))), qinv, qunit);
+  fixed_unit<WB>(wave_max_all(fmaxf(fabsf(qa), fabsf(qb))), qinv, qunit);
   L.vm[2 * lane] = make_float2(vm.x, M16 ? fmaf(vm.x, c, vm.y) : vm.x * (c - vm.y));
   L.vm[2 * lane + 1] = make_float2(vm.z, M16 ? fmaf(vm.z, c, vm.w) : vm.z * (c - vm.w));
   float punit, pinv;  // p' = p s <= max_t s_t
-  fixed_unit(wave_max_all(fmaxf(vm.x, vm.z)), pinv, punit);
+  fixed_unit<WB>(wave_max_all(fmaxf(vm.x, vm.z)), pinv, punit);
   if (lane < D / 2) {
     uint32_t ev, od;
     digit_bytes((int)rintf(qa * qinv), (int)rintf(qb * qinv), ev, od);
     uint8_t* qd = reinterpret_cast<uint8_t*>(&L.qd[0][0]);
 #pragma unroll
-    for (int j = 0; j < kDigits; ++j)
+    for (int j = 0; j < ND; ++j)
       qd[j * 64 + lane] = (uint8_t)(((j & 1) ? od : ev) >> (8 * (j >> 1)));
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -532,11 +538,11 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm,
   uint4 dq[kDigits];
 #pragma unroll
   for (int j = 0; j < kDigits; ++j) dq[j] = reinterpret_cast<const uint4*>(L.qd[j])[kc];
-  const float kscale = 16.f * qunit;
+  const float kscale = kStep * qunit;
   float sc[S::KIT];
 #pragma unroll
   for (int it = 0; it < S::KIT; ++it) {
-    float p = digit_dot(dq, signed_words<FMT>(cur.k[it], cur.k2[FMT == kFmtSplit4 ? it : 0]));
+    float p = digit_dot<ND>(dq, signed_words<FMT>(cur.k[it], cur.k2[FMT == kFmtSplit4 ? it : 0]));
     p += dpp<kDppXor1>(p);  // the KL lanes of a key row
     if constexpr (S::KL == 4) p += dpp<kDppXor2>(p);
     sc[it] = fmaf(p, kscale, bias);
@@ -555,7 +561,7 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm,
   // value weights p' = p s as digit planes.  Token t = it * TPI + kt sits in the KL lanes of its
   // key row; lanes of even rows pair token t with t + 1 (held KL lanes up) into digit bytes, and
   // lane kc of the row writes planes kc * PPL ...
-  constexpr int PPL = (kDigits + S::KL - 1) / S::KL;
+  constexpr int PPL = (ND + S::KL - 1) / S::KL;
   uint8_t* pd = reinterpret_cast<uint8_t*>(&L.pd[0][0]);
 #pragma unroll
   for (int it = 0; it < S::KIT; ++it) {
@@ -572,7 +578,7 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm,
 #pragma unroll
       for (int jj = 0; jj < PPL; ++jj) {
         const int j = kc * PPL + jj;
-        if (j < kDigits) pd[j * (kGroup / 2) + t / 2] = (uint8_t)(((j & 1) ? od : ev) >> (8 * (j >> 1)));
+        if (j < ND) pd[j * (kGroup / 2) + t / 2] = (uint8_t)(((j & 1) ? od : ev) >> (8 * (j >> 1)));
       }
     }
   }
@@ -581,11 +587,11 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm,
   uint4 dp[kDigits];
 #pragma unroll
   for (int j = 0; j < kDigits; ++j) dp[j] = reinterpret_cast<const uint4*>(L.pd[j])[vr];
-  const float vscale = 16.f * punit;
+  const float vscale = kStep * punit;
 #pragma unroll
   for (int i = 0; i < S::VIT; ++i) {
     st.o[i] = fmaf(st.o[i], alpha,
-                   digit_dot(dp, signed_words<FMT>(cur.v[i], cur.v2[FMT == kFmtSplit4 ? i : 0])) * vscale);
+                   digit_dot<ND>(dp, signed_words<FMT>(cur.v[i], cur.v2[FMT == kFmtSplit4 ? i : 0])) * vscale);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_sched_barrier(0);
