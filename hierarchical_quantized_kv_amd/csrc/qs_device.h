@@ -368,8 +368,9 @@ __device__ __forceinline__ void digit_bytes(int xa, int xb, uint32_t& even, uint
 
 // sum over 4 signed-nibble words u[] (32 nibbles, each the signed 4-bit value of one entry) of
 // the digit-weighted signed dot products, as a float in units of the fixed-point weights:
-// sum_j 16^j sum_k dot8(d[j].k, u[k]) over the ND lowest digit planes, evaluated as two Horner
-// chains (digits ND-1..3 and 2..0; |chain| <= 2048 * 273 fits int32).
+// sum_j 16^j sum_k dot8(d[j].k, u[k]) over the ND lowest digit planes.  Six planes of signed
+// nibbles run as two Horner chains (digits 5..3 and 2..0; |chain| <= 2048 * 273 fits int32);
+// five planes of 2-bit values as one.
 template <int ND = kDigits>
 __device__ __forceinline__ float digit_dot(const uint4 (&d)[kDigits], uint4 w) {
   static_assert(ND == 5 || ND == 6, "five or six digit planes");
@@ -380,13 +381,23 @@ __device__ __forceinline__ float digit_dot(const uint4 (&d)[kDigits], uint4 w) {
     acc = __builtin_amdgcn_sdot8((int)d[j].z, u[2], acc, false);
     return __builtin_amdgcn_sdot8((int)d[j].w, u[3], acc, false);
   };
-  int hi = plane(ND - 1, 0);
-  if constexpr (ND == 6) hi = plane(4, hi << 4);
-  hi = plane(3, hi << 4);
-  int lo = plane(2, 0);
-  lo = plane(1, lo << 4);
-  lo = plane(0, lo << 4);
-  return fmaf((float)hi, 4096.f, (float)lo);
+  if constexpr (ND == 5) {
+    // entries in 0..3 (the 2-bit draft): |plane| <= 768, so one chain stays below 768 * 69905
+    int acc = plane(4, 0);
+    acc = plane(3, acc << 4);
+    acc = plane(2, acc << 4);
+    acc = plane(1, acc << 4);
+    acc = plane(0, acc << 4);
+    return (float)acc;
+  } else {
+    int hi = plane(5, 0);
+    hi = plane(4, hi << 4);
+    hi = plane(3, hi << 4);
+    int lo = plane(2, 0);
+    lo = plane(1, lo << 4);
+    lo = plane(0, lo << 4);
+    return fmaf((float)hi, 4096.f, (float)lo);
+  }
 }
 
 // Power-of-two fixed-point unit for weights up to xmax: |x| / unit < 2^BITS (22 for six
@@ -571,7 +582,9 @@ __device__ __forceinline__ void draft_group(const Args& a, const Streams& sm,
     st.l_run += p;
     st.beta += p * sw.y;
     const int x = (int)rintf(p * sw.x * pinv);
-    const int xn = __shfl_xor(x, S::KL);
+    // any lane of the next key row holds that token's weight: half-row mirror (KL = 4) or
+    // quad swap (KL = 2), without a round trip through LDS
+    const int xn = __builtin_amdgcn_update_dpp(0, x, S::KL == 4 ? kDppHalfMirror : kDppXor2, 0xF, 0xF, false);
     if ((kt & 1) == 0) {
       uint32_t ev, od;
       digit_bytes(x, xn, ev, od);
