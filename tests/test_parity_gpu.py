@@ -469,3 +469,45 @@ def test_errors_leave_state_unchanged_on_gpu():
     assert e.value.status == QS_ERR_STATE
     nq, nt, hd = c.state(0)
     assert list(nt) == [10, 3] and list(nq) == [0, 0]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_draft_over_many_calls(D):
+    """60 consecutive drafts -- plain and fused with the token's append, a ragged batch whose
+    work plans change as the contexts grow and flush (a tail-only sequence among them) -- each
+    against the oracle; then a device-mode draft (its own plan and kernels) on the same state
+    agrees within 1e-5 of max |out|."""
+    log(f"case: draft, 60 calls, D={D}")
+    B, H = 3, 4
+    ls = Lockstep(1, B, H, D, 24 * G, 6, tag=f"calls{D}")
+    lens = [9 * G + 17, 2 * G + 100, 30]
+    k, v = kv(B, max(lens), H, D, 1500 + D)
+    ls.prefill(0, k, v, n=lens)
+    for call in range(60):
+        kn, vn = kv(B, 1, H, D, 1600 + call)
+        q = qd(B, H, D, 1700 + call, gain=1.0 + (call % 5))
+        if call % 2:
+            out = ls.gpu.append_attend_draft(0, kn, vn, q)
+            ls.orc[0].append(0, ls._host_heads(kn, 2), ls._host_heads(vn, 2))
+            ref = ls.orc[0].attend_draft(0, ls._host_heads(q, 1))
+            torch.cuda.synchronize()
+            ls._cmp_out(out, ref, f"fused draft {call}")
+        else:
+            ls.append(0, kn, vn)
+            ls.draft(0, q)
+        if call % 10 == 9:
+            big_k, big_v = kv(B, G, H, D, 1800 + call)
+            ls.append(0, big_k, big_v, n=[G, G // 2, 3])
+            ls.flush(0)
+    q = qd(B, H, D, 1900)
+    host = ls.draft(0, q)
+    od = torch.empty_like(host)
+    ls.gpu.to_device_state()
+    ls.gpu.attend_draft_dev(0, q, od)
+    assert ls.gpu.from_device_state() == 0
+    torch.cuda.synchronize()
+    diff = float((host - od).abs().max())
+    ref = float(host.abs().max())
+    log(f"calls{D}: 60 calls, max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}; "
+        f"host vs device mode {diff:.2e} of {ref:.2e}")
+    assert diff <= 1e-5 * ref
