@@ -1310,8 +1310,16 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgsN<NB> a) {
 //   s = max((max - min) / 255, 1e-8);  z = rint(-min / s);  c = clamp(rint(x / s) + z, 0, 255)
 // keys: one (s, z) per channel over the G tokens; values: one per token over D channels.
 
+// (mx - mn) / 255 correctly rounded, as q0 = d y, q = fma(fma(-q0, 255, d), y, q0) with
+// y = 1/255 correctly rounded (Markstein's correction step, three instructions instead of an
+// IEEE division): for every pair of finite fp16 values the same scale as the division once
+// clamped (an unclamped difference only in the sign of a zero difference), checked on the CPU.
 __device__ __forceinline__ float quant_scale(float mn, float mx) {
-  float s = (mx - mn) / 255.0f;
+#pragma clang fp contract(off)
+  const float d = mx - mn;
+  constexpr float y = 1.0f / 255.0f;
+  const float q0 = d * y;
+  const float s = __builtin_fmaf(__builtin_fmaf(-q0, 255.0f, d), y, q0);
   return s < 1e-8f ? 1e-8f : s;
 }
 // x / s, correctly rounded, from y = 1 / s (correctly rounded, once per scale) and one
@@ -1325,11 +1333,17 @@ __device__ __forceinline__ float div_by(float x, float s, float y) {
   const float r = __builtin_fmaf(-q0, s, x);
   return __builtin_fmaf(r, y, q0);
 }
+// z = rint(-mn / s) through the codes' division (-mn is an fp16 value), its sign that of -mn as
+// the division's is: the corrected quotient of a zero is +0 whatever the zero's sign, and the
+// zero-point is stored bit for bit.
+__device__ __forceinline__ float zero_point(float mn, float s, float y) {
+  return copysignf(rintf(div_by(-mn, s, y)), -mn);
+}
+
+// The clamp to [0, 255] as one median-of-three (the operands are finite).
 __device__ __forceinline__ uint32_t quant_code(float x, float s, float y, float z) {
-  float q = rintf(div_by(x, s, y)) + z;
-  q = q < 0.f ? 0.f : q;
-  q = q > 255.f ? 255.f : q;
-  return (uint32_t)q;
+  const float q = rintf(div_by(x, s, y)) + z;
+  return (uint32_t)__builtin_amdgcn_fmed3f(q, 0.f, 255.f);
 }
 
 // One wave per block.  The flush of one (layer, sequence, head) is split into independent
@@ -1398,8 +1412,8 @@ __device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* k
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     sc[e] = quant_scale(mn[e], mx[e]);
-    zc[e] = rintf(-mn[e] / sc[e]);
     yc[e] = 1.0f / sc[e];
+    zc[e] = zero_point(mn[e], sc[e], yc[e]);
   }
   if (rr == 0) {  // metadata of the 8 channels: 64 (fp16: 32) contiguous bytes
     const size_t pair0 = (lbh * a.NG + grp) * D + c0 + 8 * sub;
@@ -1482,8 +1496,8 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
   mn = fminf(mn, __shfl_xor(mn, 1));
   mx = fmaxf(mx, __shfl_xor(mx, 1));
   const float s = quant_scale(mn, mx);
-  const float z = rintf(-mn / s);
   const float y = 1.0f / s;
+  const float z = zero_point(mn, s, y);
   if (hf == 0) {
     const size_t pair = lbh * a.T + (size_t)grp * G + t0 + tk;
     if (a.meta16)
