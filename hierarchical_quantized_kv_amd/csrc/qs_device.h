@@ -1340,10 +1340,44 @@ __device__ __forceinline__ float zero_point(float mn, float s, float y) {
   return copysignf(rintf(div_by(-mn, s, y)), -mn);
 }
 
-// The clamp to [0, 255] as one median-of-three (the operands are finite).
-__device__ __forceinline__ uint32_t quant_code(float x, float s, float y, float z) {
-  const float q = rintf(div_by(x, s, y)) + z;
-  return (uint32_t)__builtin_amdgcn_fmed3f(q, 0.f, 255.f);
+// The code (an integer in [0, 255], held as a float) as byte `sel` of acc: v_cvt_pk_u8_f32 converts
+// and inserts in one instruction, exactly since the value is already an integer in range.
+__device__ __forceinline__ uint32_t put_code(float c, int sel, uint32_t acc) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(c, sel, acc);
+}
+// Packed fp16 minimum / maximum of two words, per half (chains of them become
+// v_pk_minimum3_f16 / v_pk_maximum3_f16).
+__device__ __forceinline__ uint32_t min_h2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_minimum(as_h2(a), as_h2(b)));
+}
+__device__ __forceinline__ uint32_t max_h2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(as_h2(a), as_h2(b)));
+}
+// The code of the fp16 value x in half HI of w, clamped to [0, 255] by one median-of-three (the
+// operands are finite): div_by's steps with the first product taken as fma(x, y, +0), which
+// v_fma_mix_f32 computes from the half itself (no conversion instruction; the residual's fma
+// reads it the same way).  It differs from x y only in the sign of a zero product (x = -0),
+// which the corrected quotient does not see: both give +0.
+template <int HI>
+__device__ __forceinline__ float code_h(uint32_t w, float s, float y, float z) {
+#pragma clang fp contract(off)
+  const float x = HI ? hi_h(w) : lo_h(w);
+  const float q0 = __builtin_fmaf(x, y, 0.0f);
+  const float q = __builtin_fmaf(__builtin_fmaf(-q0, s, x), y, q0);
+  return __builtin_amdgcn_fmed3f(rintf(q) + z, 0.f, 255.f);
+}
+__device__ __forceinline__ void load8(const float* p, float* out) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+// Upper and lower nibble words of 8 codes: bytes 0..3 of A hold the codes of entries 0, 2, 4, 6,
+// those of B entries 1, 3, 5, 7; byte j of u (of l) then holds the upper (lower) nibble of entry
+// 2j in bits 0-3 and that of entry 2j + 1 in bits 4-7 -- each a bit-field insert and a shift.
+__device__ __forceinline__ void nibble_planes(uint32_t A, uint32_t B, uint32_t& u, uint32_t& l) {
+  constexpr uint32_t m = 0x0F0F0F0Fu;
+  u = ((A >> 4) & m) | (B & ~m);
+  l = (A & m) | ((B << 4) & ~m);
 }
 
 // One wave per block.  The flush of one (layer, sequence, head) is split into independent
@@ -1362,118 +1396,197 @@ __device__ __forceinline__ uint32_t meta16_pair(float s, float z) {
   return hs | (hb << 16);
 }
 
+constexpr int kTileRow = 128 + 8;  // bytes per token row of a value code tile (8-byte aligned)
+// A value row's codes into a token-major tile row: the lane holds words k < HALF / 2 of the row
+// (word k: channels 8 (2 (k / 4) + hf) + 2 (k % 4) and + 1), so words 4 q .. 4 q + 3 are the 8
+// consecutive channels 8 (2 q + hf) .. + 7, stored as one 8-byte write.
+template <int HALF>
+__device__ __forceinline__ void store_code_row(const uint32_t* w, float s, float y, float z, int hf,
+                                               uint8_t* row) {
+#pragma unroll
+  for (int q = 0; q < HALF / 8; ++q) {
+    uint32_t c[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i >> 1] = put_code(code_h<0>(w[4 * q + i], s, y, z), 2 * (i & 1), c[i >> 1]);
+      c[i >> 1] = put_code(code_h<1>(w[4 * q + i], s, y, z), 2 * (i & 1) + 1, c[i >> 1]);
+    }
+    *reinterpret_cast<uint2*>(row + 8 * (2 * q + hf)) = make_uint2(c[0], c[1]);
+  }
+}
+// One channel's plane words over NT tokens of a token-major tile (col = the channel's byte in
+// token row 0): word i covers tokens 8 i .. 8 i + 7.
+template <int NT>
+__device__ __forceinline__ void tile_column_planes(const uint8_t* col, uint32_t* u, uint32_t* l) {
+#pragma unroll
+  for (int i = 0; i < NT / 8; ++i) {
+    uint32_t A = 0, B = 0;  // tokens 8 i + 2 j (A) and 8 i + 2 j + 1 (B) as byte j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      A |= (uint32_t)col[(8 * i + 2 * j) * kTileRow] << (8 * j);
+      B |= (uint32_t)col[(8 * i + 2 * j + 1) * kTileRow] << (8 * j);
+    }
+    nibble_planes(A, B, u[i], l[i]);
+  }
+}
+
+// Per-channel key scales of one block.  The lanes first reduce their rows to packed fp16 partial
+// minima / maxima (exact: a minimum of fp16 values is one of them), one partial per wave in mn /
+// mx; thread t < NC then takes channel t's (s, 1/s, z) over the NW partials, stores them in s / y
+// / z for every lane of the block, and writes the channel's metadata -- once per channel rather
+// than once per lane that quantizes it.
+template <int NC, int NW>
+struct KeyScaleLds {
+  uint32_t mn[NW][NC / 2];  // packed fp16 partials: word i = channels 2 i, 2 i + 1
+  uint32_t mx[NW][NC / 2];
+  float s[NC], y[NC], z[NC];
+};
+
+template <int NC, int NW, class Args>
+__device__ __forceinline__ void key_scales(const Args& a, KeyScaleLds<NC, NW>& L, size_t pair0) {
+  const int t = threadIdx.x;
+  if (t < NC) {
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      mn = fminf(mn, (float)reinterpret_cast<const f16*>(L.mn[ww])[t]);
+      mx = fmaxf(mx, (float)reinterpret_cast<const f16*>(L.mx[ww])[t]);
+    }
+    const float s = quant_scale(mn, mx);
+    const float y = 1.0f / s;
+    const float z = zero_point(mn, s, y);
+    L.s[t] = s;
+    L.y[t] = y;
+    L.z[t] = z;
+    if (a.meta16)
+      *reinterpret_cast<uint32_t*>(a.kmeta + (pair0 + t) * 4) = meta16_pair(s, z);
+    else
+      *reinterpret_cast<float2*>(a.kmeta + (pair0 + t) * 8) = make_float2(s, z);
+  }
+}
+
+// Packed minima / maxima of a lane's 8 channels (words wi: channels 2 wi, 2 wi + 1) over its NL
+// rows, reduced over the lanes whose lane bits from `first` up differ (same channels, other
+// rows), and stored as partial `slot` of channels 8 c .. 8 c + 7 by the lanes with no such bits.
+template <int NL, int NC, int NW>
+__device__ __forceinline__ void key_partials(const uint4* v, int first, int c, int slot,
+                                             KeyScaleLds<NC, NW>& L) {
+  uint32_t pmn[4] = {v[0].x, v[0].y, v[0].z, v[0].w}, pmx[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+  for (int k = 1; k < NL; ++k) {
+    const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      pmn[wi] = min_h2(pmn[wi], w4[wi]);
+      pmx[wi] = max_h2(pmx[wi], w4[wi]);
+    }
+  }
+#pragma unroll
+  for (int o = first; o < 64; o <<= 1)
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      pmn[wi] = min_h2(pmn[wi], __shfl_xor(pmn[wi], o));
+      pmx[wi] = max_h2(pmx[wi], __shfl_xor(pmx[wi], o));
+    }
+  if ((threadIdx.x & 63) < first) {
+    *reinterpret_cast<uint4*>(&L.mn[slot][4 * c]) = make_uint4(pmn[0], pmn[1], pmn[2], pmn[3]);
+    *reinterpret_cast<uint4*>(&L.mx[slot][4 * c]) = make_uint4(pmx[0], pmx[1], pmx[2], pmx[3]);
+  }
+}
+
+// One key row of a lane: codes of its 8 channels (scales sc / yc / zc) as the row's 4 bytes of
+// each plane.  Split-upper layout: lane pair (c even, c odd) shares word c / 2 of the top and
+// middle planes; the even lane returns the top word, the odd one the middle word.
+__device__ __forceinline__ void key_row(const uint4& v, const float* sc, const float* yc,
+                                        const float* zc, bool split, bool odd, uint32_t& hi_word,
+                                        uint32_t& lo_word) {
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  uint32_t A = 0, B = 0, u, l;  // codes of the even / odd channels of the lane's 8
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    A = put_code(code_h<0>(w4[wi], sc[2 * wi], yc[2 * wi], zc[2 * wi]), wi, A);
+    B = put_code(code_h<1>(w4[wi], sc[2 * wi + 1], yc[2 * wi + 1], zc[2 * wi + 1]), wi, B);
+  }
+  nibble_planes(A, B, u, l);
+  if (split) {
+    // nibble e of u is C_U of entry e: entries 0..7 keep C_T in the upper and C_M in the lower
+    // two bits of their nibble, entries 8..15 the other way round
+    const uint32_t t = odd ? (u >> 2) & 0x33333333u : u & 0xCCCCCCCCu;
+    const uint32_t m = odd ? (u << 2) & 0xCCCCCCCCu : u & 0x33333333u;
+    const uint32_t other = __shfl_xor(odd ? t : m, 1);  // what the neighbour lacks
+    u = (odd ? m : t) | other;
+  }
+  hi_word = u;
+  lo_word = l;
+}
+
 struct FlushValLds {
-  uint8_t code[kFlushSlice][128 + 4];          // codes, token-major (padded rows)
+  uint8_t code[kFlushSlice][kTileRow];  // codes, token-major (padded rows)
+};
+union FlushLds {
+  KeyScaleLds<kFlushSlice, 1> k;
+  FlushValLds v;
 };
 
 // Key block: channels c0 .. c0+31 of the G fp16 key rows at ksrc (token t at ksrc + t * stride),
 // into group grp of the quantized tier of (layer, sequence, head) lbh.  Lane (rr, sub) = (lane /
 // 4, lane % 4) holds channels c0 + 8 sub .. + 7 of tokens rr, rr + 16, .. (four lanes read a
-// row's 64 bytes, 16 rows per load instruction).  A channel's min / max over the G tokens is
-// reduced over the lane's 8 tokens and then over the 16 lanes of the same sub; each lane then
-// quantizes its 8 channels of its 8 tokens and writes their 4 bytes of each token's plane rows.
-// No LDS.
+// row's 64 bytes, 16 rows per load instruction).  Each lane then quantizes its 8 channels of its
+// 8 tokens and writes their 4 bytes of each token's plane rows.
 template <int D, class Args>
 __device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* ksrc, size_t stride,
-                           int c0) {
-#pragma clang fp contract(off)
+                           int c0, KeyScaleLds<kFlushSlice, 1>& L) {
   constexpr int G = kGroup, NR = G / 16;
   const int lane = threadIdx.x, sub = lane & 3, rr = lane >> 2;
   const uint16_t* src = ksrc + c0 + 8 * sub;
   uint4 v[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) v[k] = ld16(src + (size_t)(16 * k + rr) * stride);
-  // channel e of the lane's 8 (c0 + 8 sub + e): half (e & 1) of word e / 2
-  auto word = [&](int k, int wi) {
-    return wi == 0 ? v[k].x : wi == 1 ? v[k].y : wi == 2 ? v[k].z : v[k].w;
-  };
-  float mn[8], mx[8];
-#pragma unroll
-  for (int wi = 0; wi < 4; ++wi) {
-    mn[2 * wi] = mx[2 * wi] = lo_h(word(0, wi));
-    mn[2 * wi + 1] = mx[2 * wi + 1] = hi_h(word(0, wi));
-  }
-#pragma unroll
-  for (int k = 1; k < NR; ++k)
-#pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-      const float x0 = lo_h(word(k, wi)), x1 = hi_h(word(k, wi));
-      mn[2 * wi] = fminf(mn[2 * wi], x0); mx[2 * wi] = fmaxf(mx[2 * wi], x0);
-      mn[2 * wi + 1] = fminf(mn[2 * wi + 1], x1); mx[2 * wi + 1] = fmaxf(mx[2 * wi + 1], x1);
-    }
-#pragma unroll
-  for (int o = 4; o < 64; o <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      mn[e] = fminf(mn[e], __shfl_xor(mn[e], o));
-      mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], o));
-    }
-  float sc[8], zc[8], yc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    sc[e] = quant_scale(mn[e], mx[e]);
-    yc[e] = 1.0f / sc[e];
-    zc[e] = zero_point(mn[e], sc[e], yc[e]);
-  }
-  if (rr == 0) {  // metadata of the 8 channels: 64 (fp16: 32) contiguous bytes
-    const size_t pair0 = (lbh * a.NG + grp) * D + c0 + 8 * sub;
-    if (a.meta16) {
-      uint4* km = reinterpret_cast<uint4*>(a.kmeta + pair0 * 4);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        km[j] = make_uint4(meta16_pair(sc[4 * j], zc[4 * j]), meta16_pair(sc[4 * j + 1], zc[4 * j + 1]),
-                           meta16_pair(sc[4 * j + 2], zc[4 * j + 2]),
-                           meta16_pair(sc[4 * j + 3], zc[4 * j + 3]));
-    } else {
-      float4* km = reinterpret_cast<float4*>(a.kmeta + pair0 * 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        km[j] = make_float4(sc[2 * j], zc[2 * j], sc[2 * j + 1], zc[2 * j + 1]);
-    }
-  }
+  key_partials<NR>(v, 4, sub, 0, L);
+  __syncthreads();
+  key_scales(a, L, (lbh * a.NG + grp) * D + c0);
+  __syncthreads();
+  float sc[8], yc[8], zc[8];
+  load8(&L.s[8 * sub], sc);
+  load8(&L.y[8 * sub], yc);
+  load8(&L.z[8 * sub], zc);
   // key plane rows are token-major, byte j of a row holds channel 2j in bits 0-3 and 2j + 1 in
   // bits 4-7: this lane's channels are bytes (c0 + 8 sub) / 2 .. + 3 of each row
-  const size_t row0 = (lbh * a.T + (size_t)grp * G) * (D / 2) + (c0 + 8 * sub) / 2;
+  const size_t row0 = (lbh * a.T + (size_t)grp * G + rr) * (D / 2) + (c0 + 8 * sub) / 2;
   // split-upper layout: rows of D/4 bytes in the top and middle planes (the two halves of the
   // (layer, sequence, head) stripe); the 16 channels of word (c0 + 8 sub) / 16 are this lane's
   // 8 (entries 0..7 if sub is even, 8..15 if odd) and its neighbour's
-  const size_t srow0 = lbh * a.T * (D / 2) + (size_t)grp * G * (D / 4) + (c0 + 8 * (sub & ~1)) / 4;
-  const size_t mid = (size_t)a.T * (D / 4);
+  uint8_t* const srow = a.uk + lbh * a.T * (D / 2) + ((sub & 1) ? (size_t)a.T * (D / 4) : 0) +
+                        ((size_t)grp * G + rr) * (D / 4) + (c0 + 8 * (sub & ~1)) / 4;
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
-    uint32_t u = 0, l = 0;
-#pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-      const uint32_t c_lo = quant_code(lo_h(word(k, wi)), sc[2 * wi], yc[2 * wi], zc[2 * wi]);
-      const uint32_t c_hi =
-          quant_code(hi_h(word(k, wi)), sc[2 * wi + 1], yc[2 * wi + 1], zc[2 * wi + 1]);
-      u |= ((c_lo >> 4) | ((c_hi >> 4) << 4)) << (8 * wi);
-      l |= ((c_lo & 15u) | ((c_hi & 15u) << 4)) << (8 * wi);
-    }
-    const size_t o = row0 + (size_t)(16 * k + rr) * (D / 2);
-    if (a.split) {
-      // nibble e of u is C_U of entry e: entries 0..7 keep C_T in the upper and C_M in the lower
-      // two bits of their nibble, entries 8..15 the other way round
-      const uint32_t t = (sub & 1) ? (u >> 2) & 0x33333333u : u & 0xCCCCCCCCu;
-      const uint32_t m = (sub & 1) ? (u << 2) & 0xCCCCCCCCu : u & 0x33333333u;
-      const uint32_t other = __shfl_xor((sub & 1) ? t : m, 1);  // what the neighbour lacks
-      const size_t so = srow0 + (size_t)(16 * k + rr) * (D / 4);
-      if (sub & 1)
-        *reinterpret_cast<uint32_t*>(a.uk + so + mid) = m | other;
-      else
-        *reinterpret_cast<uint32_t*>(a.uk + so) = t | other;
-    } else {
-      *reinterpret_cast<uint32_t*>(a.uk + o) = u;
-    }
-    *reinterpret_cast<uint32_t*>(a.lk + o) = l;
+    uint32_t u, l;
+    key_row(v[k], sc, yc, zc, a.split, sub & 1, u, l);
+    *reinterpret_cast<uint32_t*>((a.split ? srow + 16 * k * (D / 4) : a.uk + row0 + 16 * k * (D / 2))) = u;
+    *reinterpret_cast<uint32_t*>(a.lk + row0 + 16 * k * (D / 2)) = l;
   }
+}
+
+// The scale of a value row over its D channels, held by a lane pair (hf = 0, 1) as HALF / 2
+// words each: packed minima / maxima over the lane's words, then over the pair.
+template <int NW>
+__device__ __forceinline__ void row_min_max(const uint32_t* w, float& mn, float& mx) {
+  uint32_t pmn = w[0], pmx = w[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) {
+    pmn = min_h2(pmn, w[k]);
+    pmx = max_h2(pmx, w[k]);
+  }
+  mn = fminf(lo_h(pmn), hi_h(pmn));
+  mx = fmaxf(lo_h(pmx), hi_h(pmx));
+  mn = fminf(mn, __shfl_xor(mn, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
 }
 
 // Value block: tokens t0 .. t0+31 of the G fp16 value rows at vsrc, all D channels.
 template <int D, class Args>
 __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t* vsrc,
                              size_t stride, int t0, FlushValLds& L) {
-#pragma clang fp contract(off)
   constexpr int G = kGroup, HALF = D / 2;
   const int lane = threadIdx.x;
   // token t0 + tk; lane hf of the pair takes the 16-byte chunks 2k + hf of the row, so each load
@@ -1486,15 +1599,8 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
     const uint4 v = ld16(src + 8 * (2 * k + hf));
     w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
   }
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < HALF / 2; ++k) {
-    const float x0 = lo_h(w[k]), x1 = hi_h(w[k]);
-    mn = fminf(mn, fminf(x0, x1));
-    mx = fmaxf(mx, fmaxf(x0, x1));
-  }
-  mn = fminf(mn, __shfl_xor(mn, 1));
-  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  float mn, mx;
+  row_min_max<HALF / 2>(w, mn, mx);
   const float s = quant_scale(mn, mx);
   const float y = 1.0f / s;
   const float z = zero_point(mn, s, y);
@@ -1505,12 +1611,7 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
     else
       *reinterpret_cast<float2*>(a.vmeta + pair * 8) = make_float2(s, z);
   }
-#pragma unroll
-  for (int k = 0; k < HALF / 2; ++k) {  // word k: channels 8 (2 (k / 4) + hf) + 2 (k % 4), +1
-    const uint32_t c_lo = quant_code(lo_h(w[k]), s, y, z), c_hi = quant_code(hi_h(w[k]), s, y, z);
-    const int ch = 8 * (2 * (k >> 2) + hf) + 2 * (k & 3);
-    *reinterpret_cast<uint16_t*>(&L.code[tk][ch]) = (uint16_t)(c_lo | (c_hi << 8));
-  }
+  store_code_row<HALF>(w, s, y, z, hf, &L.code[tk][0]);
   __syncthreads();
   // value planes: half e of the group, channel-major rows of G/4 bytes; byte j of a row holds
   // token e*G/2 + 2j in bits 0-3 and e*G/2 + 2j + 1 in bits 4-7.  This block fills 16 bytes
@@ -1523,14 +1624,8 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
   uint8_t* tv = a.uv + lbh * a.NG * D * (G / 2) + ((size_t)grp * 2 + e) * D * (G / 8) + tin / 4;
   const size_t mid = (size_t)a.NG * D * (G / 4);
   for (int d = lane; d < D; d += 64) {
-    uint32_t u[4] = {0, 0, 0, 0}, l[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < kFlushSlice / 2; ++j) {
-      const uint32_t c_lo = L.code[2 * j][d], c_hi = L.code[2 * j + 1][d];
-      const int sh = 8 * (j & 3);
-      u[j >> 2] |= ((c_lo >> 4) | ((c_hi >> 4) << 4)) << sh;
-      l[j >> 2] |= ((c_lo & 15u) | ((c_hi & 15u) << 4)) << sh;
-    }
+    uint32_t u[4], l[4];
+    tile_column_planes<kFlushSlice>(&L.code[0][d], u, l);
     if (a.split) {
       // word w of u holds C_U of tokens 8w .. 8w+7 (nibble e = token 8w + e); a split word
       // covers tokens 16v .. 16v+15: C_T of the first 8 in the upper, of the next 8 in the
@@ -1552,7 +1647,7 @@ __device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t*
 template <int D>
 __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
   constexpr int NK = D / kFlushSlice, NV = kGroup / kFlushSlice;
-  __shared__ FlushValLds lds;  // the value blocks' code tile (key blocks use no LDS)
+  __shared__ FlushLds lds;  // key blocks: the channel scales; value blocks: the code tile
   // XCD-contiguous numbering: the NK + NV blocks of one (layer, sequence, head) write parts of
   // the same plane lines, so they run on one XCD and its L2 merges the parts into whole lines
   // before they reach HBM (blocks of one half spread over several XCDs made partial-line
@@ -1575,31 +1670,138 @@ __global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
   }
   const size_t ring0 = (lbh * (2 * kGroup) + head) * D;  // oldest ring half, token-major
   if (blk < NK)
-    flush_keys<D>(a, lbh, group, a.tail_k + ring0, D, blk * kFlushSlice);
+    flush_keys<D>(a, lbh, group, a.tail_k + ring0, D, blk * kFlushSlice, lds.k);
   else
-    flush_values<D>(a, lbh, group, a.tail_v + ring0, D, (blk - NK) * kFlushSlice, lds);
+    flush_values<D>(a, lbh, group, a.tail_v + ring0, D, (blk - NK) * kFlushSlice, lds.v);
 }
 
-// Prefill: group g of sequence b's prompt (tokens g*G .. g*G+G-1 of k / v [B][n_max][H][D]) into
-// quantized group group0[b] + g, with the flush's blocks and arithmetic.
-// grid: x = head * (D/32 + G/32) + block, y = prompt group, z = sequence
+// Prefill: whole groups of a prompt quantized straight from the caller's k / v [B][n_max][H][D]
+// (a head's G rows of 2 D bytes lie H * 2 D bytes apart), with the flush's arithmetic, by
+// four-wave workgroups that each own a whole (group, head) of keys or of values, so that every
+// load reads whole head rows and every store writes whole plane lines.
+constexpr int kPrefillWaves = 4;
+struct PrefillValLds {
+  uint8_t code[2][kGroup / 2][kTileRow];  // per half group: codes, token-major (padded rows)
+};
+
+// Keys of one (group, head): wave w holds rows 32 w .. 32 w + 31, each lane 8 channels (16
+// bytes) of 32 / RPI of them -- LPR lanes read a row, RPI rows per load instruction.  Each lane
+// quantizes its channels of its rows and writes their 4 bytes of each plane row, so a store
+// instruction writes RPI whole consecutive rows.
+template <int D, class Args>
+__device__ void prefill_keys(const Args& a, size_t lbh, int grp, const uint16_t* ksrc, size_t stride,
+                             KeyScaleLds<D, kPrefillWaves>& L) {
+  constexpr int G = kGroup, LPR = D / 8, RPI = 64 / LPR, NL = 32 / RPI;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane % LPR, r = lane / LPR;  // channels 8 c .. 8 c + 7 of rows 32 w + RPI k + r
+  const uint16_t* src = ksrc + 8 * c;
+  uint4 v[NL];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) v[k] = ld16(src + (size_t)(32 * w + RPI * k + r) * stride);
+  key_partials<NL>(v, LPR, c, w, L);
+  __syncthreads();
+  key_scales(a, L, (lbh * a.NG + grp) * D);
+  __syncthreads();
+  float sc[8], yc[8], zc[8];
+  load8(&L.s[8 * c], sc);
+  load8(&L.y[8 * c], yc);
+  load8(&L.z[8 * c], zc);
+  // plane rows: this lane's channels are bytes 4 c .. 4 c + 3 of a row.  Split-upper layout: rows
+  // of D/4 bytes in the top and middle planes, word c / 2 of a row holding this lane's 8
+  // channels (entries 0..7 if c is even) and its neighbour's
+  const size_t row0 = (lbh * a.T + (size_t)grp * G + 32 * w + r) * (D / 2) + 4 * c;
+  // the even lane of a pair writes the top plane's word, the odd lane the middle plane's
+  uint8_t* const srow = a.uk + lbh * a.T * (D / 2) + ((c & 1) ? (size_t)a.T * (D / 4) : 0) +
+                        ((size_t)grp * G + 32 * w + r) * (D / 4) + 4 * (c >> 1);
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    uint32_t u, l;
+    key_row(v[k], sc, yc, zc, a.split, c & 1, u, l);
+    *reinterpret_cast<uint32_t*>((a.split ? srow + RPI * k * (D / 4) : a.uk + row0 + RPI * k * (D / 2))) = u;
+    *reinterpret_cast<uint32_t*>(a.lk + row0 + RPI * k * (D / 2)) = l;
+  }
+}
+
+// Values of one (group, head): wave w quantizes tokens 32 w .. 32 w + 31 (a lane pair per row,
+// as in the flush's value block) into the code tile of its half group; after one barrier wave w
+// writes the whole rows of channels (D/2) (w % 2) .. + D/2 - 1 of half w / 2.
+template <int D, class Args>
+__device__ void prefill_values(const Args& a, size_t lbh, int grp, const uint16_t* vsrc, size_t stride,
+                               PrefillValLds& L) {
+  constexpr int G = kGroup, HALF = D / 2;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int half = w >> 1, trow = 32 * (w & 1);  // tokens (G/2) half + trow + tk of the group
+  const int tk = lane >> 1, hf = lane & 1;
+  const uint16_t* src = vsrc + (size_t)((G / 2) * half + trow + tk) * stride;
+  uint32_t wv[HALF / 2];
+#pragma unroll
+  for (int k = 0; k < HALF / 8; ++k) {
+    const uint4 v = ld16(src + 8 * (2 * k + hf));
+    wv[4 * k] = v.x; wv[4 * k + 1] = v.y; wv[4 * k + 2] = v.z; wv[4 * k + 3] = v.w;
+  }
+  float mn, mx;
+  row_min_max<HALF / 2>(wv, mn, mx);
+  const float s = quant_scale(mn, mx);
+  const float y = 1.0f / s;
+  const float z = zero_point(mn, s, y);
+  if (hf == 0) {
+    const size_t pair = lbh * a.T + (size_t)grp * G + (G / 2) * half + trow + tk;
+    if (a.meta16)
+      *reinterpret_cast<uint32_t*>(a.vmeta + pair * 4) = meta16_pair(s, z);
+    else
+      *reinterpret_cast<float2*>(a.vmeta + pair * 8) = make_float2(s, z);
+  }
+  store_code_row<HALF>(wv, s, y, z, hf, &L.code[half][trow + tk][0]);
+  __syncthreads();
+  // the plane row of channel dch in half `half` holds the half's G/2 tokens, byte j tokens 2j
+  // (bits 0-3) and 2j + 1 (bits 4-7)
+  const int dch = (D / 2) * (w & 1) + lane;
+  if (lane < D / 2) {
+    uint32_t u[8], l[8];
+    tile_column_planes<G / 2>(&L.code[half][0][dch], u, l);
+    const size_t rowb = (((lbh * a.NG + grp) * 2 + half) * D + dch) * (G / 4);
+    if (a.split) {
+      // a split word covers tokens 16 v .. 16 v + 15: C_T of the first 8 in the upper, of the
+      // next 8 in the lower two bits of each nibble, C_M the other way round
+      uint32_t t[4], m[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        t[q] = (u[2 * q] & 0xCCCCCCCCu) | ((u[2 * q + 1] >> 2) & 0x33333333u);
+        m[q] = (u[2 * q] & 0x33333333u) | ((u[2 * q + 1] << 2) & 0xCCCCCCCCu);
+      }
+      uint8_t* tv = a.uv + lbh * a.NG * D * (G / 2) + (((size_t)grp * 2 + half) * D + dch) * (G / 8);
+      const size_t smid = (size_t)a.NG * D * (G / 4);
+      *reinterpret_cast<uint4*>(tv) = make_uint4(t[0], t[1], t[2], t[3]);
+      *reinterpret_cast<uint4*>(tv + smid) = make_uint4(m[0], m[1], m[2], m[3]);
+    } else {
+      *reinterpret_cast<uint4*>(a.uv + rowb) = make_uint4(u[0], u[1], u[2], u[3]);
+      *reinterpret_cast<uint4*>(a.uv + rowb + 16) = make_uint4(u[4], u[5], u[6], u[7]);
+    }
+    *reinterpret_cast<uint4*>(a.lv + rowb) = make_uint4(l[0], l[1], l[2], l[3]);
+    *reinterpret_cast<uint4*>(a.lv + rowb + 16) = make_uint4(l[4], l[5], l[6], l[7]);
+  }
+}
+
+// grid: x = 2 head + kind (0 keys, 1 values), y = prompt group, z = sequence; 256 threads.  Group
+// g of sequence b's prompt (its tokens g G .. g G + G - 1) goes to quantized group group0[b] + g.
 template <int D>
-__global__ __launch_bounds__(64) void prefill_kernel(const PrefillArgs a) {
-  constexpr int NK = D / kFlushSlice, NV = kGroup / kFlushSlice;
-  __shared__ FlushValLds lds;  // the value blocks' code tile (key blocks use no LDS)
+__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(4))) void prefill_kernel(const PrefillArgs a) {
+  __shared__ union {
+    KeyScaleLds<D, kPrefillWaves> k;
+    PrefillValLds v;
+  } lds;
   const int n = gridDim.x * gridDim.y * gridDim.z;
   const int lb = xcd_contiguous_block((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, n);
   const int bx = lb % gridDim.x, g = (lb / gridDim.x) % gridDim.y, b = lb / (gridDim.x * gridDim.y);
-  if (g >= a.groups[b]) return;
-  const int h = bx / (NK + NV);
-  const int blk = bx % (NK + NV);
+  if (g >= a.groups[b]) return;  // the whole workgroup, before its barriers
+  const int h = bx >> 1;
   const size_t lbh = ((size_t)a.layer * a.B + b) * a.H + h;
   const size_t stride = (size_t)a.H * D;
   const size_t src0 = (((size_t)b * a.n_max + (size_t)g * kGroup) * a.H + h) * D;
-  if (blk < NK)
-    flush_keys<D>(a, lbh, a.group0[b] + g, a.k + src0, stride, blk * kFlushSlice);
+  if ((bx & 1) == 0)
+    prefill_keys<D>(a, lbh, a.group0[b] + g, a.k + src0, stride, lds.k);
   else
-    flush_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, (blk - NK) * kFlushSlice, lds);
+    prefill_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, lds.v);
 }
 
 
