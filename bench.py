@@ -877,8 +877,8 @@ def write_traffic_summary(fetch_dir, write_dir, args):
             if not sel:
                 continue
             vals = [float(r["Counter_Value"]) * factor * 1024 for r in sel]
-            if kind == "flush":   # one unit = one (layer, head) half: 8 one-wave blocks at D=128
-                units = [int(r["Grid_Size"]) // (64 * (128 // 32 + G // 32)) for r in sel]
+            if kind == "flush":   # one unit = one (layer, head) half: two 256-thread workgroups
+                units = [int(r["Grid_Size"]) // (2 * 256) for r in sel]
                 per[kind] = (sum(vals) / sum(units), len(sel))
             else:
                 per[kind] = (sum(vals) / len(vals), len(sel))

@@ -1303,12 +1303,15 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgsN<NB> a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Flush: quantize and bit-split one G-token ring half of (layer, b, h)
+// Quantizer: one G-token group of (layer, b, h) into both planes and its metadata -- the flush
+// (the ring's oldest half) and the prefill (a prompt's whole groups)
 // ------------------------------------------------------------------------------------------
 //
 // Quantizer, in fp32 and in this order (QuantSpec Guide, quantizer listing):
 //   s = max((max - min) / 255, 1e-8);  z = rint(-min / s);  c = clamp(rint(x / s) + z, 0, 255)
 // keys: one (s, z) per channel over the G tokens; values: one per token over D channels.
+// Four-wave workgroups each own a whole (group, head) of keys or of values, so that every load
+// reads whole head rows and every store writes whole plane lines.
 
 // (mx - mn) / 255 correctly rounded, as q0 = d y, q = fma(fma(-q0, 255, d), y, q0) with
 // y = 1/255 correctly rounded (Markstein's correction step, three instructions instead of an
@@ -1379,11 +1382,6 @@ __device__ __forceinline__ void nibble_planes(uint32_t A, uint32_t B, uint32_t& 
   u = ((A >> 4) & m) | (B & ~m);
   l = (A & m) | ((B << 4) & ~m);
 }
-
-// One wave per block.  The flush of one (layer, sequence, head) is split into independent
-// blocks: D/32 key blocks of 32 channels x G tokens and G/32 value blocks of 32 tokens x D
-// channels, each reading 8 KB of fp16 and writing its slice of both planes and its metadata.
-constexpr int kFlushSlice = 32;
 
 // fp16 metadata of a group (keys: a channel; values: a token) with fp32 scale s and zero-point
 // z: s and the offset b = -s z (the fp32 product), each rounded to nearest-even fp16, b clamped
@@ -1520,53 +1518,6 @@ __device__ __forceinline__ void key_row(const uint4& v, const float* sc, const f
   lo_word = l;
 }
 
-struct FlushValLds {
-  uint8_t code[kFlushSlice][kTileRow];  // codes, token-major (padded rows)
-};
-union FlushLds {
-  KeyScaleLds<kFlushSlice, 1> k;
-  FlushValLds v;
-};
-
-// Key block: channels c0 .. c0+31 of the G fp16 key rows at ksrc (token t at ksrc + t * stride),
-// into group grp of the quantized tier of (layer, sequence, head) lbh.  Lane (rr, sub) = (lane /
-// 4, lane % 4) holds channels c0 + 8 sub .. + 7 of tokens rr, rr + 16, .. (four lanes read a
-// row's 64 bytes, 16 rows per load instruction).  Each lane then quantizes its 8 channels of its
-// 8 tokens and writes their 4 bytes of each token's plane rows.
-template <int D, class Args>
-__device__ void flush_keys(const Args& a, size_t lbh, int grp, const uint16_t* ksrc, size_t stride,
-                           int c0, KeyScaleLds<kFlushSlice, 1>& L) {
-  constexpr int G = kGroup, NR = G / 16;
-  const int lane = threadIdx.x, sub = lane & 3, rr = lane >> 2;
-  const uint16_t* src = ksrc + c0 + 8 * sub;
-  uint4 v[NR];
-#pragma unroll
-  for (int k = 0; k < NR; ++k) v[k] = ld16(src + (size_t)(16 * k + rr) * stride);
-  key_partials<NR>(v, 4, sub, 0, L);
-  __syncthreads();
-  key_scales(a, L, (lbh * a.NG + grp) * D + c0);
-  __syncthreads();
-  float sc[8], yc[8], zc[8];
-  load8(&L.s[8 * sub], sc);
-  load8(&L.y[8 * sub], yc);
-  load8(&L.z[8 * sub], zc);
-  // key plane rows are token-major, byte j of a row holds channel 2j in bits 0-3 and 2j + 1 in
-  // bits 4-7: this lane's channels are bytes (c0 + 8 sub) / 2 .. + 3 of each row
-  const size_t row0 = (lbh * a.T + (size_t)grp * G + rr) * (D / 2) + (c0 + 8 * sub) / 2;
-  // split-upper layout: rows of D/4 bytes in the top and middle planes (the two halves of the
-  // (layer, sequence, head) stripe); the 16 channels of word (c0 + 8 sub) / 16 are this lane's
-  // 8 (entries 0..7 if sub is even, 8..15 if odd) and its neighbour's
-  uint8_t* const srow = a.uk + lbh * a.T * (D / 2) + ((sub & 1) ? (size_t)a.T * (D / 4) : 0) +
-                        ((size_t)grp * G + rr) * (D / 4) + (c0 + 8 * (sub & ~1)) / 4;
-#pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    uint32_t u, l;
-    key_row(v[k], sc, yc, zc, a.split, sub & 1, u, l);
-    *reinterpret_cast<uint32_t*>((a.split ? srow + 16 * k * (D / 4) : a.uk + row0 + 16 * k * (D / 2))) = u;
-    *reinterpret_cast<uint32_t*>(a.lk + row0 + 16 * k * (D / 2)) = l;
-  }
-}
-
 // The scale of a value row over its D channels, held by a lane pair (hf = 0, 1) as HALF / 2
 // words each: packed minima / maxima over the lane's words, then over the pair.
 template <int NW>
@@ -1583,114 +1534,19 @@ __device__ __forceinline__ void row_min_max(const uint32_t* w, float& mn, float&
   mx = fmaxf(mx, __shfl_xor(mx, 1));
 }
 
-// Value block: tokens t0 .. t0+31 of the G fp16 value rows at vsrc, all D channels.
-template <int D, class Args>
-__device__ void flush_values(const Args& a, size_t lbh, int grp, const uint16_t* vsrc,
-                             size_t stride, int t0, FlushValLds& L) {
-  constexpr int G = kGroup, HALF = D / 2;
-  const int lane = threadIdx.x;
-  // token t0 + tk; lane hf of the pair takes the 16-byte chunks 2k + hf of the row, so each load
-  // instruction reads 32 contiguous bytes of every row
-  const int tk = lane >> 1, hf = lane & 1;
-  const uint16_t* src = vsrc + (size_t)(t0 + tk) * stride;
-  uint32_t w[HALF / 2];
-#pragma unroll
-  for (int k = 0; k < HALF / 8; ++k) {
-    const uint4 v = ld16(src + 8 * (2 * k + hf));
-    w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
-  }
-  float mn, mx;
-  row_min_max<HALF / 2>(w, mn, mx);
-  const float s = quant_scale(mn, mx);
-  const float y = 1.0f / s;
-  const float z = zero_point(mn, s, y);
-  if (hf == 0) {
-    const size_t pair = lbh * a.T + (size_t)grp * G + t0 + tk;
-    if (a.meta16)
-      *reinterpret_cast<uint32_t*>(a.vmeta + pair * 4) = meta16_pair(s, z);
-    else
-      *reinterpret_cast<float2*>(a.vmeta + pair * 8) = make_float2(s, z);
-  }
-  store_code_row<HALF>(w, s, y, z, hf, &L.code[tk][0]);
-  __syncthreads();
-  // value planes: half e of the group, channel-major rows of G/4 bytes; byte j of a row holds
-  // token e*G/2 + 2j in bits 0-3 and e*G/2 + 2j + 1 in bits 4-7.  This block fills 16 bytes
-  // of the row of every channel.
-  const int e = t0 / (G / 2), tin = t0 % (G / 2);
-  uint8_t* uv = a.uv + ((lbh * a.NG + grp) * D) * (G / 2) + (size_t)e * (D * G / 4) + tin / 2;
-  uint8_t* lv = a.lv + ((lbh * a.NG + grp) * D) * (G / 2) + (size_t)e * (D * G / 4) + tin / 2;
-  // split-upper layout: channel rows of G/8 bytes per half in the top and middle planes (the two
-  // halves of the stripe); this block's 32 tokens are words tin/16 and tin/16 + 1 of a row
-  uint8_t* tv = a.uv + lbh * a.NG * D * (G / 2) + ((size_t)grp * 2 + e) * D * (G / 8) + tin / 4;
-  const size_t mid = (size_t)a.NG * D * (G / 4);
-  for (int d = lane; d < D; d += 64) {
-    uint32_t u[4], l[4];
-    tile_column_planes<kFlushSlice>(&L.code[0][d], u, l);
-    if (a.split) {
-      // word w of u holds C_U of tokens 8w .. 8w+7 (nibble e = token 8w + e); a split word
-      // covers tokens 16v .. 16v+15: C_T of the first 8 in the upper, of the next 8 in the
-      // lower two bits of each nibble, C_M the other way round
-      const uint32_t t0w = (u[0] & 0xCCCCCCCCu) | ((u[1] >> 2) & 0x33333333u);
-      const uint32_t t1w = (u[2] & 0xCCCCCCCCu) | ((u[3] >> 2) & 0x33333333u);
-      const uint32_t m0w = (u[0] & 0x33333333u) | ((u[1] << 2) & 0xCCCCCCCCu);
-      const uint32_t m1w = (u[2] & 0x33333333u) | ((u[3] << 2) & 0xCCCCCCCCu);
-      *reinterpret_cast<uint2*>(tv + (size_t)d * (G / 8)) = make_uint2(t0w, t1w);
-      *reinterpret_cast<uint2*>(tv + mid + (size_t)d * (G / 8)) = make_uint2(m0w, m1w);
-    } else {
-      *reinterpret_cast<uint4*>(uv + (size_t)d * (G / 4)) = make_uint4(u[0], u[1], u[2], u[3]);
-    }
-    *reinterpret_cast<uint4*>(lv + (size_t)d * (G / 4)) = make_uint4(l[0], l[1], l[2], l[3]);
-  }
-}
-
-// grid: x = head * (D/32 + G/32) + block, y = selected sequence, z = layer - layer0
-template <int D>
-__global__ __launch_bounds__(64) void flush_kernel(const FlushArgs a) {
-  constexpr int NK = D / kFlushSlice, NV = kGroup / kFlushSlice;
-  __shared__ FlushLds lds;  // key blocks: the channel scales; value blocks: the code tile
-  // XCD-contiguous numbering: the NK + NV blocks of one (layer, sequence, head) write parts of
-  // the same plane lines, so they run on one XCD and its L2 merges the parts into whole lines
-  // before they reach HBM (blocks of one half spread over several XCDs made partial-line
-  // write-backs: about twice the written bytes and extra reads).
-  const int n = gridDim.x * gridDim.y * gridDim.z;
-  const int lb = xcd_contiguous_block((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, n);
-  const int bx = lb % gridDim.x, by = (lb / gridDim.x) % gridDim.y, bz = lb / (gridDim.x * gridDim.y);
-  const int h = bx / (NK + NV);
-  const int blk = bx % (NK + NV);
-  const int sel = by;
-  const int layer = a.layer0 + bz;
-  const size_t lbh = ((size_t)layer * a.B + a.b[sel]) * a.H + h;
-  int group = a.group[sel], head = a.head[sel];
-  if (a.dstate) {  // device mode: this sequence flushes only if selected and within capacity
-    const int32_t* st = a.dstate + ((size_t)layer * a.B + a.b[sel]) * kStateInts;
-    const int nq = st[0], nt = apply_pending(st[1], a.pend, a.b[sel], nullptr);
-    if (nt < a.thr || nq + kGroup > a.T) return;
-    group = nq / kGroup;
-    head = st[2];
-  }
-  const size_t ring0 = (lbh * (2 * kGroup) + head) * D;  // oldest ring half, token-major
-  if (blk < NK)
-    flush_keys<D>(a, lbh, group, a.tail_k + ring0, D, blk * kFlushSlice, lds.k);
-  else
-    flush_values<D>(a, lbh, group, a.tail_v + ring0, D, (blk - NK) * kFlushSlice, lds.v);
-}
-
-// Prefill: whole groups of a prompt quantized straight from the caller's k / v [B][n_max][H][D]
-// (a head's G rows of 2 D bytes lie H * 2 D bytes apart), with the flush's arithmetic, by
-// four-wave workgroups that each own a whole (group, head) of keys or of values, so that every
-// load reads whole head rows and every store writes whole plane lines.
-constexpr int kPrefillWaves = 4;
-struct PrefillValLds {
+constexpr int kQuantWaves = 4;
+struct GroupValLds {
   uint8_t code[2][kGroup / 2][kTileRow];  // per half group: codes, token-major (padded rows)
 };
 
-// Keys of one (group, head): wave w holds rows 32 w .. 32 w + 31, each lane 8 channels (16
-// bytes) of 32 / RPI of them -- LPR lanes read a row, RPI rows per load instruction.  Each lane
+// Keys of one (group, head), the G fp16 rows at ksrc (token t at ksrc + t * stride), into group
+// grp of the quantized tier of (layer, sequence, head) lbh: wave w holds rows 32 w .. 32 w + 31,
+// each lane 8 channels (16 bytes) of 32 / RPI of them -- LPR lanes read a row, RPI rows per load instruction.  Each lane
 // quantizes its channels of its rows and writes their 4 bytes of each plane row, so a store
 // instruction writes RPI whole consecutive rows.
 template <int D, class Args>
-__device__ void prefill_keys(const Args& a, size_t lbh, int grp, const uint16_t* ksrc, size_t stride,
-                             KeyScaleLds<D, kPrefillWaves>& L) {
+__device__ void quant_keys(const Args& a, size_t lbh, int grp, const uint16_t* ksrc, size_t stride,
+                             KeyScaleLds<D, kQuantWaves>& L) {
   constexpr int G = kGroup, LPR = D / 8, RPI = 64 / LPR, NL = 32 / RPI;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane % LPR, r = lane / LPR;  // channels 8 c .. 8 c + 7 of rows 32 w + RPI k + r
@@ -1722,12 +1578,13 @@ __device__ void prefill_keys(const Args& a, size_t lbh, int grp, const uint16_t*
   }
 }
 
-// Values of one (group, head): wave w quantizes tokens 32 w .. 32 w + 31 (a lane pair per row,
-// as in the flush's value block) into the code tile of its half group; after one barrier wave w
+// Values of one (group, head), the G fp16 rows at vsrc: wave w quantizes tokens 32 w .. 32 w + 31
+// (a lane pair per row: lane hf of the pair takes the row's 16-byte chunks 2 k + hf, so a load
+// instruction reads 32 contiguous bytes of every row) into the code tile of its half group; after one barrier wave w
 // writes the whole rows of channels (D/2) (w % 2) .. + D/2 - 1 of half w / 2.
 template <int D, class Args>
-__device__ void prefill_values(const Args& a, size_t lbh, int grp, const uint16_t* vsrc, size_t stride,
-                               PrefillValLds& L) {
+__device__ void quant_values(const Args& a, size_t lbh, int grp, const uint16_t* vsrc, size_t stride,
+                               GroupValLds& L) {
   constexpr int G = kGroup, HALF = D / 2;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int half = w >> 1, trow = 32 * (w & 1);  // tokens (G/2) half + trow + tk of the group
@@ -1782,13 +1639,19 @@ __device__ void prefill_values(const Args& a, size_t lbh, int grp, const uint16_
   }
 }
 
+// Prefill: whole groups of a prompt quantized straight from the caller's k / v [B][n_max][H][D]
+// (a head's G rows of 2 D bytes lie H * 2 D bytes apart).
 // grid: x = 2 head + kind (0 keys, 1 values), y = prompt group, z = sequence; 256 threads.  Group
 // g of sequence b's prompt (its tokens g G .. g G + G - 1) goes to quantized group group0[b] + g.
 template <int D>
-__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(4))) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * kQuantWaves) __attribute__((amdgpu_waves_per_eu(4))) void prefill_kernel(const PrefillArgs a) {
+  // 32 KB per workgroup, so that at most five share a compute unit: more in flight only adds
+  // contention to the mixed read / write stream (measured at 128k: 608 us with five per unit,
+  // 613 us with four, 617 us with seven)
   __shared__ union {
-    KeyScaleLds<D, kPrefillWaves> k;
-    PrefillValLds v;
+    KeyScaleLds<D, kQuantWaves> k;
+    GroupValLds v;
+    uint8_t occupancy[32 * 1024];
   } lds;
   const int n = gridDim.x * gridDim.y * gridDim.z;
   const int lb = xcd_contiguous_block((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, n);
@@ -1799,11 +1662,42 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
   const size_t stride = (size_t)a.H * D;
   const size_t src0 = (((size_t)b * a.n_max + (size_t)g * kGroup) * a.H + h) * D;
   if ((bx & 1) == 0)
-    prefill_keys<D>(a, lbh, a.group0[b] + g, a.k + src0, stride, lds.k);
+    quant_keys<D>(a, lbh, a.group0[b] + g, a.k + src0, stride, lds.k);
   else
-    prefill_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, lds.v);
+    quant_values<D>(a, lbh, a.group0[b] + g, a.v + src0, stride, lds.v);
 }
 
+
+// Flush: the ring's oldest half (rows of D fp16, contiguous) of each selected (layer, sequence,
+// head) into its next quantized group.
+// grid: x = 2 head + kind (0 keys, 1 values), y = selected sequence, z = layer - layer0; 256
+// threads.  A whole launch's halves fit in about one resident round of workgroups.
+template <int D>
+__global__ __launch_bounds__(64 * kQuantWaves) void flush_kernel(const FlushArgs a) {
+  __shared__ union {
+    KeyScaleLds<D, kQuantWaves> k;
+    GroupValLds v;
+  } lds;
+  const int n = gridDim.x * gridDim.y * gridDim.z;
+  const int lb = xcd_contiguous_block((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, n);
+  const int bx = lb % gridDim.x, sel = (lb / gridDim.x) % gridDim.y, bz = lb / (gridDim.x * gridDim.y);
+  const int h = bx >> 1;
+  const int layer = a.layer0 + bz;
+  const size_t lbh = ((size_t)layer * a.B + a.b[sel]) * a.H + h;
+  int group = a.group[sel], head = a.head[sel];
+  if (a.dstate) {  // device mode: this sequence flushes only if selected and within capacity
+    const int32_t* st = a.dstate + ((size_t)layer * a.B + a.b[sel]) * kStateInts;
+    const int nq = st[0], nt = apply_pending(st[1], a.pend, a.b[sel], nullptr);
+    if (nt < a.thr || nq + kGroup > a.T) return;  // the whole workgroup, before its barriers
+    group = nq / kGroup;
+    head = st[2];
+  }
+  const size_t ring0 = (lbh * (2 * kGroup) + head) * D;  // oldest ring half, token-major
+  if ((bx & 1) == 0)
+    quant_keys<D>(a, lbh, group, a.tail_k + ring0, D, lds.k);
+  else
+    quant_values<D>(a, lbh, group, a.tail_v + ring0, D, lds.v);
+}
 
 // ------------------------------------------------------------------------------------------
 // Launchers (called by the C ABI in qs_api.cpp)

@@ -62,8 +62,8 @@ hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st) {
 hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream_t st) {
   if (max_groups <= 0) return hipSuccess;
   const dim3 grid(a.H * 2, max_groups, a.B);  // per head: a key and a value workgroup
-  if (D == 128) hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(64 * kPrefillWaves), 0, st, a);
-  else hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(64 * kPrefillWaves), 0, st, a);
+  if (D == 128) hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(64 * kQuantWaves), 0, st, a);
+  else hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(64 * kQuantWaves), 0, st, a);
   return hipGetLastError();
 }
 
@@ -74,10 +74,9 @@ hipError_t launch_state(const StateArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st) {
-  const int per_head = D / kFlushSlice + kGroup / kFlushSlice;
-  const dim3 grid(a.H * per_head, a.n_sel, n_layers);
-  if (D == 128) hipLaunchKernelGGL(flush_kernel<128>, grid, dim3(64), 0, st, a);
-  else hipLaunchKernelGGL(flush_kernel<64>, grid, dim3(64), 0, st, a);
+  const dim3 grid(a.H * 2, a.n_sel, n_layers);  // per head: a key and a value workgroup
+  if (D == 128) hipLaunchKernelGGL(flush_kernel<128>, grid, dim3(64 * kQuantWaves), 0, st, a);
+  else hipLaunchKernelGGL(flush_kernel<64>, grid, dim3(64 * kQuantWaves), 0, st, a);
   return hipGetLastError();
 }
 
