@@ -7,8 +7,9 @@ channels scaled x8.  One step is one speculation round over all layers:
   per layer: rollback gamma, append gamma+1 target tokens, verify attention (7 queries),
   acceptance a ~ Bernoulli(0.9) until first reject, rollback gamma - a, then one flush call.
 Inputs are seeded synthetic fp16 tensors resident in HBM before timing starts.  HIP events time
-the draft and verify calls of one layer per timed step (rotating over the layers).  After the timed
-steps, a bulk flush (one G-token half of every layer and head in one launch) is timed on its own.
+each timed step's run of draft calls and its run of verify calls (a call's time is its share of
+the run).  After the timed steps, a bulk flush (one G-token half of every layer and head in one
+launch) is timed on its own.
 
 Prints one JSON line: value = algorithmic HBM bytes of the step / step time (GB/s), with the
 roofline of the draft kernel (and of verify and flush), and the CPU oracle timed on a bounded
@@ -113,9 +114,13 @@ def prefill_bytes(n, H, D):
 def time_steps(torch, cache, stream, dev, config, L, H, D, gamma, steps, warmup, fuse):
     """Runs `warmup` untimed and `steps` timed speculation rounds over all L layers of `cache`
     (each: gamma x (append 1 + draft) per layer, rollback gamma, append gamma+1 + verify,
-    rollback by the rejected count, flush), inputs resident in HBM.  HIP events bracket the
-    draft and verify calls of one layer per timed step (the layer rotates from step to step):
-    recording them around every call would add their own cost to the step time."""
+    rollback by the rejected count, flush), inputs resident in HBM.  In each timed step, one
+    pair of HIP events brackets the step's gamma x L draft calls and one pair its L verify calls
+    (with fused calls nothing else runs on the GPU between them; a rollback is host bookkeeping),
+    so a call's time is its share of the run of calls as the step executes them: events around
+    single calls add their own marker cost (measured: ~6 us per call at 32k, where the step's
+    128 draft and 32 verify calls at those per-call times would add up to more than the whole
+    step)."""
     from hierarchical_quantized_kv_amd import synth
     m = gamma + 1
     n_steps = warmup + steps
@@ -137,12 +142,21 @@ def time_steps(torch, cache, stream, dev, config, L, H, D, gamma, steps, warmup,
     out_v = torch.empty((1, m, H, D), dtype=torch.float32, device=dev)
     ev = {"draft": [], "verify": []}
 
+    def events(timed):
+        if not timed:
+            return None, None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        return e0, e1
+
     def run_step(s, timed):
         x = steps_in[s]
         nbytes = 0
-        ev_layer = (s - warmup) % L if timed else -1  # -1: no events in warmup
         # A draft step is the token's append followed by the draft call; fused (the default)
-        # both are one call, whose event interval and bytes then include the append.
+        # both are one call, whose bytes then include the append (without fusion the bracketed
+        # run also holds the append kernels).
+        e0, e1 = events(timed)
+        call_bytes = 0
         for j in range(gamma):
             for layer in range(L):
                 if not fuse:
@@ -151,19 +165,17 @@ def time_steps(torch, cache, stream, dev, config, L, H, D, gamma, steps, warmup,
                 nt_call = int(nt[0]) + (1 if fuse else 0)
                 db = draft_bytes(int(nq[0]), nt_call, H, D)
                 nbytes += append_bytes(1, H, D) + db
-                rec = layer == ev_layer
-                if rec:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+                call_bytes += db + (append_bytes(1, H, D) if fuse else 0)
                 if fuse:
                     cache.append_attend_draft(layer, x["dk"][j, layer], x["dv"][j, layer],
                                               x["qd"][j, layer], out=out_d)
                 else:
                     cache.attend_draft(layer, x["qd"][j, layer], out=out_d)
-                if rec:
-                    e1.record(stream)
-                    ev["draft"].append((e0, e1, db + (append_bytes(1, H, D) if fuse else 0)))
+        if timed:
+            e1.record(stream)
+            ev["draft"].append((e0, e1, call_bytes, gamma * L))
+        e0, e1 = events(timed)
+        call_bytes = 0
         for layer in range(L):
             cache.rollback(layer, [gamma])
             if not fuse:
@@ -171,20 +183,16 @@ def time_steps(torch, cache, stream, dev, config, L, H, D, gamma, steps, warmup,
             nq, nt, _ = cache.state(layer)
             vb = verify_bytes(int(nq[0]), int(nt[0]) + (m if fuse else 0), H, D, m)
             nbytes += append_bytes(m, H, D) + vb
-            rec = layer == ev_layer
-            if rec:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+            call_bytes += vb + (append_bytes(m, H, D) if fuse else 0)
             if fuse:
                 cache.append_attend_verify(layer, x["tk"][layer], x["tv"][layer], x["qv"][layer],
                                            out=out_v)
             else:
                 cache.attend_verify(layer, x["qv"][layer], out=out_v)
-            if rec:
-                e1.record(stream)
-                ev["verify"].append((e0, e1, vb + (append_bytes(m, H, D) if fuse else 0)))
             cache.rollback(layer, [gamma - accept[s]])
+        if timed:
+            e1.record(stream)
+            ev["verify"].append((e0, e1, call_bytes, L))
         flushed = cache.flush(-1)
         nbytes += int(flushed[0]) * L * flush_bytes(H, D)
         return nbytes
@@ -205,22 +213,23 @@ def time_steps(torch, cache, stream, dev, config, L, H, D, gamma, steps, warmup,
 
 
 def summarize_events(events):
-    """(average us, GB/s, bytes, samples dropped) of (event, event, bytes) samples.  When the
-    GPU has caught up with the host (short calls at 32k), an event interval can also hold a
-    stall of the host thread (measured once: one sample of ~30 ms among 40 of ~38 us); samples
-    above twice the median are left out, and counted."""
-    t = np.array([a.elapsed_time(b) * 1e3 for a, b, _ in events])   # us
-    by = [n for _, _, n in events]
-    keep = t <= 2.0 * np.median(t)
-    avg_us = float(t[keep].mean())
-    return avg_us, float(np.mean(by)) / (avg_us * 1e-6) / 1e9, float(np.mean(by)), int((~keep).sum())
+    """(us per call, GB/s, bytes per call, samples dropped) of (event, event, bytes, calls)
+    samples, each a run of consecutive calls.  A sample whose time per call is above twice the
+    median is left out, and counted (an interval can hold a stall of the host thread)."""
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b, _, _ in events])   # us
+    by = np.array([n for _, _, n, _ in events], dtype=np.float64)
+    calls = np.array([c for _, _, _, c in events], dtype=np.float64)
+    per = t / calls
+    keep = per <= 2.0 * np.median(per)
+    avg_us = float(t[keep].sum() / calls[keep].sum())
+    bytes_per_call = float(by[keep].sum() / calls[keep].sum())
+    return avg_us, bytes_per_call / (avg_us * 1e-6) / 1e9, bytes_per_call, int((~keep).sum())
 
 
 def measure_ctx32k(torch, stream, dev, steps, warmup, fuse):
     """The Llama-2-7B-32K-shaped stack (32 layers x 32 heads x head_dim 128, ctx 32768 + 64-token
     tail, gamma 4) run with the same step as the headline workload on a cache of its own:
-    step time, and the draft / verify calls of one layer per step (events, as for the
-    headline)."""
+    step time, and the draft / verify calls' times (events, as for the headline)."""
     from hierarchical_quantized_kv_amd import synth
     from hierarchical_quantized_kv_amd.binding import Cache
     cfg = CONFIGS[3]
@@ -342,7 +351,7 @@ def main():
         e0.record(stream)
         cache.prefill(layer, k, v)
         e1.record(stream)
-        pf_ev.append((e0, e1, prefill_bytes(ctx + 64, H, D)))
+        pf_ev.append((e0, e1, prefill_bytes(ctx + 64, H, D), 1))
         if layer == 0 and not args.no_cpu_baseline:
             hs = list(range(cpu_sample_heads(cpu_threads, H)))
             cpu_inputs = (k[:, :, hs].cpu().numpy(), v[:, :, hs].cpu().numpy())
@@ -384,7 +393,7 @@ def main():
         flushed = cache.flush(-1)
         e1.record(stream)
         assert int(flushed[0]) == 1
-        fl_ev.append((e0, e1, L * flush_bytes(H, D)))
+        fl_ev.append((e0, e1, L * flush_bytes(H, D), 1))
     torch.cuda.synchronize()
 
     # The accept / correct step after verify (qs_spec_accept): synthetic fp32 logits over a
@@ -408,15 +417,14 @@ def main():
             e0.record(stream)
             spec_accept(sa_t, sa_d, sa_x, sa_u, workspace=sa_ws, stream=stream)
             e1.record(stream)
-            sa_ev[sb].append((e0, e1, sb * (2 * gamma + 1) * V_SPEC * 4))
+            sa_ev[sb].append((e0, e1, sb * (2 * gamma + 1) * V_SPEC * 4, 1))
         torch.cuda.synchronize()
         del sa_t, sa_d
     torch.cuda.synchronize()
 
-    # Average over the sampled calls.  When the GPU has caught up with the host (short calls at
-    # 32k), an event interval can also hold a stall of the host thread (measured once: one
-    # sample of ~30 ms among 40 of ~38 us); samples above twice the median are left out, and
-    # the count of those is reported.
+    # Average over the sampled calls.  An event interval can also hold a stall of the host
+    # thread; samples above twice the median (per call) are left out, and the count of those is
+    # reported.
     dropped = {}
 
     def summarize(events, kind):
