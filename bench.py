@@ -378,22 +378,28 @@ def main():
     graph_line = None if args.no_graph else measure_graph_steps(
         torch, cache, steps_in[0], accept, args, L, H, D, gamma, m, out_d, out_v, dev, stream)
 
-    # Bulk flush (outside the timed steps): every layer gets G more tail tokens, then one
-    # qs_flush(-1) quantizes one G-token half of every (layer, head) in a single launch.
-    # (timed behind the spin kernel, like the prefill)
-    fk, fv = rnd(1, G, H, D), rnd(1, G, H, D)
+    # Bulk flush (outside the timed steps): each qs_flush(-1) quantizes one G-token half of
+    # every (layer, head) in a single launch.  Every layer's tail is emptied (rolled back) and
+    # refilled with 2G tokens, then two flushes run back to back between one pair of events,
+    # behind the spin kernel (like the prefill): a call's time is half the pair's, so one
+    # launch's marker and dispatch latency is shared by two calls, as calls queued behind other
+    # work share it in a round.
+    fk, fv = rnd(1, 2 * G, H, D), rnd(1, 2 * G, H, D)
     fl_ev = []
-    for _ in range(args.flush_reps):
+    for _ in range((args.flush_reps + 1) // 2):
         for layer in range(L):
+            _, nt_l, _ = cache.state(layer)
+            cache.rollback(layer, [int(nt_l[0])])
             cache.append(layer, fk, fv)
         torch.cuda._sleep(spin_cycles)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        flushed = cache.flush(-1)
+        f1 = cache.flush(-1)
+        f2 = cache.flush(-1)
         e1.record(stream)
-        assert int(flushed[0]) == 1
-        fl_ev.append((e0, e1, L * flush_bytes(H, D), 1))
+        assert int(f1[0]) == 1 and int(f2[0]) == 1
+        fl_ev.append((e0, e1, 2 * L * flush_bytes(H, D), 2))
     torch.cuda.synchronize()
 
     # The accept / correct step after verify (qs_spec_accept): synthetic fp32 logits over a
