@@ -4,6 +4,8 @@ checked on sampled heads / layers that the CPU oracle can afford.
   * LWM-128k-shaped layer: 32 heads x 128, 131072 prefilled tokens, gamma = 6 round, with plain
     queries and with queries x8 (a peaky softmax); the same prefilled layer in both metadata
     formats.
+  * LWM-128k-shaped layer in the split-upper layout: the 2-bit draft (plain and x8 queries),
+    the 4-bit draft and verify over one prefilled layer.
   * LWM-128k-shaped stack: all 32 layers of the 128k cache the benchmark times (4 x 8 GiB of
     planes), every layer prefilled; a gamma = 6 round on every layer checked on layers 0 and 31
     (sampled heads), then an all-layer flush and the planes of both layers bit-exact.
@@ -126,6 +128,35 @@ def test_lwm_128k_32_layer_stack():
     ls.draft(L - 1, dev_q((1, H, D), gen, D))
     log(f"128kx32: layers 0/31 bit-exact after the all-layer flush; max abs {ls.max_abs:.3e} "
         f"max rel {ls.max_rel:.3e}")
+
+
+def test_lwm_128k_split_upper_layer():
+    """A 128k layer in the split-upper layout (top and middle 2-bit planes): one qs_prefill of
+    131072 + 64 tokens, the 2-bit draft (qs_attend_draft_bits) with plain queries and with
+    queries x8, the 4-bit draft and a 7-query verify over the same planes, all against the
+    oracle on sampled heads (the 2-bit draft's weights are on five digits: this checks their
+    rounding over a whole 128k context), then the planes bit-exact."""
+    log("case: LWM-128k layer, split-upper layout, heads 0/17/31 sampled")
+    H, D, ctx, gamma = 32, 128, 131072, 6
+    ls = Lockstep(1, 1, H, D, ctx + 4 * G, gamma, heads=[0, 17, 31], tag="128ksplit",
+                  split_upper=True)
+    out = synth.outlier_channels(H, D, synth.seed_for(4, 2, "outlier"))
+    k, v = dev_kv(4, 2, 1, ctx + 64, H, D, outliers=out)
+    ls.prefill(0, k, v)
+    del k, v
+    ls.check_planes(0)
+    gen = torch.Generator(device="cuda").manual_seed(4300)
+    for s in range(2):
+        dk, dv = dev_kv(4, 2, 1, 1, H, D, outliers=out, salt=600 + s)
+        ls.append(0, dk, dv)
+        q = dev_q((1, H, D), gen, D)
+        ls.draft_bits(0, q, 2)
+        ls.draft_bits(0, (q.float() * 8).half(), 2)
+        ls.draft(0, q)
+    tk, tv = dev_kv(4, 2, 1, gamma + 1, H, D, outliers=out, salt=700)
+    ls.append(0, tk, tv)
+    ls.verify(0, dev_q((1, gamma + 1, H, D), gen, D))
+    log(f"128ksplit: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
 @pytest.mark.parametrize("meta_fp16", [False, True])
