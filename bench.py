@@ -508,8 +508,8 @@ def main():
                                f"flush_kernel<128>, {L} layers x {H} heads in one launch",
                                launches=L * H),
         "roofline_prefill": roof("prefill", p_gbs, p_bytes, p_us,
-                                 f"prefill_kernel<128> + append_kernel<128, 1>: one layer's "
-                                 f"{ctx + 64}-token prompt, {H} heads"),
+                                 f"prefill_kernel<128> (whole groups and the rest to the ring "
+                                 f"in one launch): one layer's {ctx + 64}-token prompt, {H} heads"),
         "spec_accept": {
             f"batch{sb}": {"kernel": f"row_stats_kernel + part_sums_kernel + accept_kernel: "
                                      f"batch {sb}, gamma {gamma}, vocab {V_SPEC}",

@@ -176,39 +176,25 @@ qs_status qs_prefill(qs_cache* c, int32_t layer, const void* d_k, const void* d_
   p.NG = cf.max_ctx / cf.group;
   p.layer = layer;
   p.n_max = n_max;
+  // the rest of each prompt goes into the ring in the same launch, where the equivalent append /
+  // flush sequence leaves it (the ring head toggles once per quantized group; the tail was empty)
+  const size_t tail_lbh = (size_t)2 * cf.group * cf.head_dim * 2;
+  p.tail_k = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_k + layer_off(c, tail_lbh, layer));
+  p.tail_v = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_v + layer_off(c, tail_lbh, layer));
   int max_groups = 0, rest = 0;
   for (int b = 0; b < cf.batch; ++b) {
+    const qs::Seq& q = c->st.at(layer, b);
     p.groups[b] = n[b] / cf.group;
-    p.group0[b] = c->st.at(layer, b).nq / cf.group;
+    p.group0[b] = q.nq / cf.group;
     if (p.groups[b] > max_groups) max_groups = p.groups[b];
-    rest += n[b] % cf.group;
+    p.rest[b] = n[b] % cf.group;
+    const int head = (p.groups[b] & 1) ? (q.head ^ cf.group) : q.head;
+    p.rest_slot[b] = (head + q.nt) % (2 * cf.group);  // nt is 0 whenever n[b] > 0
+    rest += p.rest[b];
   }
+  p.rest_row = rest > 0 ? max_groups : -1;
   hipError_t e = qs::launch_prefill(p, cf.head_dim, max_groups, st);
   if (e != hipSuccess) return device_fail(c, e, "prefill launch");
-  // the rest of each prompt: into the ring, where the equivalent append / flush sequence leaves
-  // it (the ring head toggles once per quantized group; the tail was empty)
-  if (rest > 0) {
-    qs::AppendArgs a{};
-    a.k = p.k;
-    a.v = p.v;
-    const size_t tail_lbh = (size_t)2 * cf.group * cf.head_dim * 2;
-    a.tail_k = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_k + layer_off(c, tail_lbh, layer));
-    a.tail_v = reinterpret_cast<uint16_t*>(c->arena + c->lay.tail_v + layer_off(c, tail_lbh, layer));
-    a.B = cf.batch;
-    a.H = cf.n_heads;
-    a.n_max = n_max;
-    a.n_rows = 0;
-    for (int b = 0; b < cf.batch; ++b) {
-      const qs::Seq& q = c->st.at(layer, b);
-      if (n[b] % cf.group > a.n_rows) a.n_rows = n[b] % cf.group;
-      a.n[b] = n[b] % cf.group;
-      a.start[b] = q.nt;  // 0 whenever n[b] > 0
-      a.head[b] = (p.groups[b] & 1) ? (q.head ^ cf.group) : q.head;
-      a.src0[b] = p.groups[b] * cf.group;
-    }
-    e = qs::launch_append(a, cf.head_dim, st);
-    if (e != hipSuccess) return device_fail(c, e, "prefill tail launch");
-  }
   c->st.apply_prefill(layer, n);
   c->err.clear();
   return QS_OK;

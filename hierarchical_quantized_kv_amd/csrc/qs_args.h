@@ -180,6 +180,13 @@ struct PrefillArgs {
   int32_t layer, n_max;
   int32_t groups[QS_MAX_BATCH];  // whole groups of each sequence's prompt
   int32_t group0[QS_MAX_BATCH];  // quantized-tier group index of the first of them (nq / G)
+  // the rest of each prompt (n mod G tokens after its whole groups) goes to the ring in the same
+  // launch, by the workgroups of row rest_row (-1: no rest anywhere)
+  uint16_t* tail_k;              // this layer's ring [B][H][2G][D]
+  uint16_t* tail_v;
+  int32_t rest_row;
+  int32_t rest[QS_MAX_BATCH];       // n mod G of each prompt
+  int32_t rest_slot[QS_MAX_BATCH];  // ring slot of its first rest token
 };
 
 struct FlushArgs {

@@ -1639,8 +1639,24 @@ __device__ void quant_values(const Args& a, size_t lbh, int grp, const uint16_t*
   }
 }
 
+// The rest of a prompt (its tokens after the whole groups) of head h into the ring: rows of D
+// fp16, a row's 16-byte chunks over D/8 lanes, 256 / (D/8) rows per pass.
+template <int D>
+__device__ void prefill_rest(const PrefillArgs& a, int b, int h, const uint16_t* src,
+                             uint16_t* ring) {
+  constexpr int CH = D / 8, RPP = 64 * kQuantWaves / CH;
+  const int c = threadIdx.x % CH;
+  for (int i = threadIdx.x / CH; i < a.rest[b]; i += RPP) {
+    const int slot = (a.rest_slot[b] + i) % (2 * kGroup);
+    const size_t s = (((size_t)b * a.n_max + (size_t)a.groups[b] * kGroup + i) * a.H + h) * D + 8 * c;
+    const size_t d = (((size_t)b * a.H + h) * (2 * kGroup) + slot) * D + 8 * c;
+    *reinterpret_cast<uint4*>(ring + d) = ld16(src + s);
+  }
+}
+
 // Prefill: whole groups of a prompt quantized straight from the caller's k / v [B][n_max][H][D]
-// (a head's G rows of 2 D bytes lie H * 2 D bytes apart).
+// (a head's G rows of 2 D bytes lie H * 2 D bytes apart), and the rest of the prompt into the
+// ring by the workgroups of row rest_row.
 // grid: x = 2 head + kind (0 keys, 1 values), y = prompt group, z = sequence; 256 threads.  Group
 // g of sequence b's prompt (its tokens g G .. g G + G - 1) goes to quantized group group0[b] + g.
 template <int D>
@@ -1656,8 +1672,15 @@ __global__ __launch_bounds__(64 * kQuantWaves) __attribute__((amdgpu_waves_per_e
   const int n = gridDim.x * gridDim.y * gridDim.z;
   const int lb = xcd_contiguous_block((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x, n);
   const int bx = lb % gridDim.x, g = (lb / gridDim.x) % gridDim.y, b = lb / (gridDim.x * gridDim.y);
-  if (g >= a.groups[b]) return;  // the whole workgroup, before its barriers
   const int h = bx >> 1;
+  if (g == a.rest_row) {  // no barriers on this path
+    if ((bx & 1) == 0)
+      prefill_rest<D>(a, b, h, a.k, a.tail_k);
+    else
+      prefill_rest<D>(a, b, h, a.v, a.tail_v);
+    return;
+  }
+  if (g >= a.groups[b]) return;  // the whole workgroup, before its barriers
   const size_t lbh = ((size_t)a.layer * a.B + b) * a.H + h;
   const size_t stride = (size_t)a.H * D;
   const size_t src0 = (((size_t)b * a.n_max + (size_t)g * kGroup) * a.H + h) * D;

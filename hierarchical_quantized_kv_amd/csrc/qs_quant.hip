@@ -60,8 +60,9 @@ hipError_t launch_append(const AppendArgs& a, int D, hipStream_t st) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int D, int max_groups, hipStream_t st) {
-  if (max_groups <= 0) return hipSuccess;
-  const dim3 grid(a.H * 2, max_groups, a.B);  // per head: a key and a value workgroup
+  const int rows = max_groups + (a.rest_row >= 0 ? 1 : 0);
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid(a.H * 2, rows, a.B);  // per head: a key and a value workgroup
   if (D == 128) hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(64 * kQuantWaves), 0, st, a);
   else hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(64 * kQuantWaves), 0, st, a);
   return hipGetLastError();

@@ -166,7 +166,8 @@ class State {
     qs_status st = check_layer(layer, false, err);
     if (st != QS_OK) return st;
     if (n_max < 0) { *err = "n_max must be >= 0"; return QS_ERR_INVALID_ARG; }
-    if (n_max / cfg_.group > 65535) { *err = "n_max / G must be <= 65535"; return QS_ERR_INVALID_ARG; }
+    // grid rows: the whole groups, plus one for the rest (at most 65535)
+    if (n_max / cfg_.group > 65534) { *err = "n_max / G must be <= 65534"; return QS_ERR_INVALID_ARG; }
     for (int b = 0; b < cfg_.batch; ++b) {
       if (n[b] < 0 || n[b] > n_max) { *err = "n[b] must be in 0..n_max"; return QS_ERR_INVALID_ARG; }
       if (n[b] == 0) continue;

@@ -165,13 +165,13 @@ qs_status qs_append(qs_cache* cache, int32_t layer, const void* d_k, const void*
 
 /* Bulk prefill ("quantize once"): appends a prompt of n_b tokens to every sequence b of
  * `layer`, with the result of append(G) + flush repeated floor(n_b / G) times followed by
- * append(n_b mod G), bit for bit (planes, metadata, tail slots and counters), in two launches:
+ * append(n_b mod G), bit for bit (planes, metadata, tail slots and counters), in one launch:
  * the whole groups are quantized straight from the prompt, the rest goes to the tail.
  *   d_k, d_v : fp16 [B][n_max][H][D], rows (b, i) for i < n_b are read.
  *   h_n      : host int32 [B] with 0 <= n_b <= n_max, or NULL for n_b = n_max.
  * Then nq_b += G floor(n_b / G), head_b ^= G if floor(n_b / G) is odd, nt_b = n_b mod G.
  * Errors: QS_ERR_STATE if n_b > 0 and the tail of b is not empty (nt_b != 0);
- * QS_ERR_CAPACITY if nq_b + G floor(n_b / G) > max_ctx; QS_ERR_INVALID_ARG if n_max / G > 65535.
+ * QS_ERR_CAPACITY if nq_b + G floor(n_b / G) > max_ctx; QS_ERR_INVALID_ARG if n_max / G > 65534.
  * [QuantSpec Guide, "Core Architectural Blueprint" figure: the prefill context is quantized
  * once into the hierarchical cache; "Periodic Group Quantization" and the quantizer listing for
  * the per-group codes.] */
