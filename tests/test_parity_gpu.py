@@ -229,6 +229,29 @@ def test_prefill_matches_quantize_once(D):
     log(f"prefill{D}: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
+def test_prefill_of_whole_groups_only():
+    """Prompts that are whole groups (no rest row in the launch), an empty prompt (no launch at
+    all), then a prompt with a rest on top of the first: planes, tail and counters against the
+    oracle."""
+    log("case: prefill of whole groups only")
+    H, B, D = 3, 2, 128
+    ls = Lockstep(1, B, H, D, 8 * G, 4, tag="prefillwhole")
+    k, v = kv(B, 2 * G, H, D, 950)
+    ls.prefill(0, k, v, [2 * G, G])
+    ls.check_planes(0)
+    nq, nt, _ = ls.check_state(0)
+    assert list(nq) == [2 * G, G] and list(nt) == [0, 0]
+    ls.prefill(0, k, v, [0, 0])
+    ls.check_state(0)
+    k2, v2 = kv(B, G + 9, H, D, 951)
+    ls.prefill(0, k2, v2, [G + 9, 5])
+    ls.check_planes(0)
+    nq, nt, _ = ls.check_state(0)
+    assert list(nq) == [3 * G, G] and list(nt) == [9, 5]
+    ls.draft(0, qd(B, H, D, 952))
+    log(f"prefillwhole: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
 def test_degenerate_groups():
     """Constant key channels and value rows (scale clamped to 1e-8, huge zero-point) and
     all-positive groups (zero-point below 0)."""
