@@ -299,26 +299,16 @@ __device__ __forceinline__ float* record(const Args& a, int D, int b, int h, int
   return a.work + ((((size_t)b * a.H + h) * a.S + split) * a.m + i) * (size_t)(D + kRecPad);
 }
 
-// Group assignment of the quantized workers of (b, h), groups first, first + step, .. < ng.
-// Draft: worker w of W takes groups w, w + W, w + 2W, ...  At every step the W workers of a head
-// read one contiguous run of W groups, so the plane traffic of the whole call spreads evenly
-// over the HBM channels (for the draft, contiguous per-worker runs were measured to leave some
-// waves twice as slow as others).
+// Group assignment of the quantized workers of (b, h): worker w of W takes groups w, w + W,
+// w + 2W, ...  At every step the W workers of a head read one contiguous run of W groups, so the
+// plane traffic of the whole call spreads evenly over the HBM channels (contiguous per-worker
+// chunks were measured to leave some waves twice as slow as others).
 struct GroupStride {
   int first, step, ng;
 };
 template <class Args>
 __device__ __forceinline__ GroupStride worker_groups(const Args& a, int b, int item) {
   return GroupStride{item, a.qitem_base[b + 1] - a.qitem_base[b], seq_nq(a, b) / kGroup};
-}
-// Verify (both planes, or the grouped-query draft's upper planes, on the MFMA item): worker w of
-// W takes the contiguous run of groups w ng / W .. (w + 1) ng / W - 1, so that each of its reads
-// continues where the last one ended; with a few groups per worker (32k contexts) this took the
-// verify call from 65.3 to 58.6 us, and it is neutral at 128k.
-template <class Args>
-__device__ __forceinline__ GroupStride worker_run(const Args& a, int b, int item) {
-  const int W = a.qitem_base[b + 1] - a.qitem_base[b], ng = seq_nq(a, b) / kGroup;
-  return GroupStride{(int)((long long)item * ng / W), 1, (int)((long long)(item + 1) * ng / W)};
 }
 
 // The waves that share a SIMD issue oldest first, so with equal work the oldest finishes far
@@ -955,7 +945,7 @@ __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyL
   const int g = lane >> 4;   // k-group
   const int m = a.m;
   const size_t bh = (size_t)b * a.H + h;
-  const GroupStride gs = worker_run(a, b, item);
+  const GroupStride gs = worker_groups(a, b, item);
 
   // q times qscale of channels 2*lane, 2*lane+1 for every query, and zeroed B operands so the
   // padding query columns j >= m stay zero
