@@ -1260,16 +1260,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnArgsN<NB, MODE> 
         ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
+    // the batch's largest max first, then its weighted sums: independent terms instead of a
+    // chain of sixteen rescalings (a record with max -inf weighs 0)
+    float bm = ml[0].x;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) lse_merge(m, l, o, ml[u].x, ml[u].y, ov[u]);
+    for (int u = 1; u < 16; ++u) bm = fmaxf(bm, ml[u].x);
+    if (bm != -INFINITY) {
+      float bl = 0.f;
+      float4 bo = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float w = fast_exp2(ml[u].x - bm);
+        bl = fmaf(ml[u].y, w, bl);
+        bo.x = fmaf(ov[u].x, w, bo.x);
+        bo.y = fmaf(ov[u].y, w, bo.y);
+        bo.z = fmaf(ov[u].z, w, bo.z);
+        bo.w = fmaf(ov[u].w, w, bo.w);
+      }
+      lse_merge(m, l, o, bm, bl, bo);
+    }
   }
   po[p][c] = o;
   if (c == 0) pml[p] = make_float2(m, l);
   __syncthreads();
   if (t < C4) {
-    float mm = pml[0].x, ll = pml[0].y;
-    float4 oo = po[0][t];
-    for (int q = 1; q < NP; ++q) lse_merge(mm, ll, oo, pml[q].x, pml[q].y, po[q][t]);
+    // the phases, max first as above (mm is finite unless the sequence holds no token, which
+    // the host verbs reject and device mode flags in its error word)
+    float mm = pml[0].x;
+#pragma unroll
+    for (int q = 1; q < NP; ++q) mm = fmaxf(mm, pml[q].x);
+    float ll = 0.f;
+    float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const float w = fast_exp2(pml[q].x - mm);
+      const float4 v = po[q][t];
+      ll = fmaf(pml[q].y, w, ll);
+      oo.x = fmaf(v.x, w, oo.x);
+      oo.y = fmaf(v.y, w, oo.y);
+      oo.z = fmaf(v.z, w, oo.z);
+      oo.w = fmaf(v.w, w, oo.w);
+    }
     const float inv = 1.f / ll;
     float4* out = reinterpret_cast<float4*>(a.out + qrow(a, b, h, i) * D);
     out[t] = make_float4(oo.x * inv, oo.y * inv, oo.z * inv, oo.w * inv);
