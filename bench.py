@@ -459,7 +459,7 @@ def main():
     topk = None if args.no_topk else measure_topk(
         torch, stream, spin_cycles, dev, cfg["name"], ctx=cfg["ctx"], H=cfg["heads"],
         m=cfg["gamma"] + 1)
-    read_ceiling = measure_read_ceiling(torch, stream)
+    read_ceiling = measure_read_ceiling(torch, stream, {"draft": d_bytes, "verify": v_bytes})
     mixed_ceiling = measure_mixed_ceiling(torch, stream)
 
     cpu = None
@@ -769,10 +769,13 @@ def measure_topk(torch, stream, spin_cycles, dev, name, ctx=131072, H=32, m=7, r
     return out
 
 
-def measure_read_ceiling(torch, stream):
+def measure_read_ceiling(torch, stream, call_bytes=None):
     """The practical HBM read rate of this device: a plain grid-stride streaming-read kernel
     (16-byte non-temporal loads, eight in flight per lane; libqs_readprobe.so) over 2 GiB, the
-    best of 4, 8 and 12 waves per compute unit, 20 timed launches each."""
+    best of 4, 8 and 12 waves per compute unit, 20 timed launches each.  With call_bytes
+    ({name: bytes}), the same kernel (at the best wave count) also reads each call's byte count
+    once per launch: the streaming rate a call of that size could reach, ramp and drain
+    included."""
     import ctypes
     path = os.path.join(ROOT, "hierarchical_quantized_kv_amd", "libqs_readprobe.so")
     if not os.path.exists(path):
@@ -796,11 +799,26 @@ def measure_read_ceiling(torch, stream):
         gbs = nbytes / (us.value * 1e-6) / 1e9
         if best is None or gbs > best[0]:
             best = (gbs, bpc, us.value)
+    at_size = {}
+    for name, nb in (call_bytes or {}).items():
+        nb = min(int(nb), buf.numel()) // 16 * 16
+        us = ctypes.c_float()
+        rc = lib.qs_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nb,
+                                      ctypes.c_void_p(sink.data_ptr()), best[1], 20,
+                                      ctypes.c_void_p(stream.cuda_stream), ctypes.byref(us))
+        if rc != 0:
+            raise RuntimeError(f"qs_probe_stream_read failed with HIP error {rc}")
+        gbs = nb / (us.value * 1e-6) / 1e9
+        at_size[name] = {"bytes": nb, "avg_launch_us": round(us.value, 2), "gbs": round(gbs, 1),
+                         "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
     del buf
-    return {"gbs": round(best[0], 1), "frac_of_peak": round(best[0] / PEAK_HBM_GBS, 4),
-            "kernel": f"grid-stride streaming read, 16 B non-temporal loads, 8 in flight per lane, "
-                      f"{4 * best[1]} waves per CU",
-            "bytes_per_launch": nbytes, "avg_launch_us": round(best[2], 2)}
+    out = {"gbs": round(best[0], 1), "frac_of_peak": round(best[0] / PEAK_HBM_GBS, 4),
+           "kernel": f"grid-stride streaming read, 16 B non-temporal loads, 8 in flight per lane, "
+                     f"{4 * best[1]} waves per CU",
+           "bytes_per_launch": nbytes, "avg_launch_us": round(best[2], 2)}
+    if at_size:
+        out["at_call_size"] = at_size
+    return out
 
 
 def measure_mixed_ceiling(torch, stream, out_mib=1024):
