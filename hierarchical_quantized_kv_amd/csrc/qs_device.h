@@ -1199,8 +1199,9 @@ __global__ __launch_bounds__(64, (DRAFT && MODE != kModeGqa) ? 3 : 2) void attn_
 
 // out[(b, i, h)] = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) over the splits s of (b, h),
 // M = max_s m_s.  256 threads in NP phases of D/4 threads: phase p merges the splits p, p + NP,
-// .. with an online log-sum-exp (all of its loads issued before the first merge), then the
-// phases are merged through LDS.
+// .. sixteen at a time (all of a batch's loads issued before its first use; each batch max-first,
+// then one log-sum-exp step into the phase's running result), then the phases are merged through
+// LDS, max-first as well.
 __device__ __forceinline__ void lse_merge(float& m, float& l, float4& o, float m2, float l2,
                                           float4 o2) {
   const float mn = fmaxf(m, m2);
