@@ -4,6 +4,7 @@ checked on sampled heads / layers that the CPU oracle can afford.
   * LWM-128k-shaped layer: 32 heads x 128, 131072 prefilled tokens, gamma = 6 round, with plain
     queries and with queries x8 (a peaky softmax); the same prefilled layer in both metadata
     formats.
+  * head_dim 64: the same round on a 128k layer of 32 heads x 64 channels.
   * LWM-128k-shaped layer in the split-upper layout: the 2-bit draft (plain and x8 queries),
     the 4-bit draft and verify over one prefilled layer.
   * LWM-128k-shaped stack: all 32 layers of the 128k cache the benchmark times (4 x 8 GiB of
@@ -83,6 +84,33 @@ def test_lwm_128k_layer():
     ls.flush(0)
     ls.check_planes(0)
     log(f"128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
+def test_head_dim_64_128k_layer():
+    """The same round on a 128k layer of 32 heads x 64 channels (the head_dim-64 instantiations
+    at full size: two lanes per key row in the draft, the verify's half-width tiles)."""
+    log("case: head_dim 64, 128k layer, heads 0/17/31 sampled")
+    H, D, ctx, gamma = 32, 64, 131072, 6
+    ls = Lockstep(1, 1, H, D, ctx + 4 * G, gamma, heads=[0, 17, 31], tag="128k-d64")
+    out = synth.outlier_channels(H, D, synth.seed_for(4, 1, "outlier"))
+    k, v = dev_kv(4, 1, 1, ctx + 64, H, D, outliers=out)
+    prefill(ls, 0, k[:, :ctx], v[:, :ctx])
+    ls.append(0, k[:, ctx:].contiguous(), v[:, ctx:].contiguous())
+    del k, v
+    gen = torch.Generator(device="cuda").manual_seed(4064)
+    for s in range(gamma):
+        dk, dv = dev_kv(4, 1, 1, 1, H, D, outliers=out, salt=s + 1)
+        ls.append(0, dk, dv)
+        ls.draft(0, dev_q((1, H, D), gen, D))
+    ls.draft(0, (dev_q((1, H, D), gen, D).float() * 8).half())
+    ls.rollback(0, [gamma])
+    tk, tv = dev_kv(4, 1, 1, gamma + 1, H, D, outliers=out, salt=100)
+    ls.append(0, tk, tv)
+    ls.verify(0, dev_q((1, gamma + 1, H, D), gen, D))
+    ls.rollback(0, [3])
+    ls.flush(0)
+    ls.check_planes(0)
+    log(f"128k d64: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
 def test_lwm_128k_32_layer_stack():
