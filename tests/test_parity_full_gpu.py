@@ -5,6 +5,8 @@ checked on sampled heads / layers that the CPU oracle can afford.
     queries and with queries x8 (a peaky softmax); the same prefilled layer in both metadata
     formats.
   * head_dim 64: the same round on a 128k layer of 32 heads x 64 channels.
+  * Grouped queries: a Llama-3.1-8B-shaped 128k layer (8 cached heads x 4 query heads), the
+    grouped draft and a 4-token grouped verify on sampled cached heads.
   * LWM-128k-shaped layer in the split-upper layout: the 2-bit draft (plain and x8 queries),
     the 4-bit draft and verify over one prefilled layer.
   * LWM-128k-shaped stack: all 32 layers of the 128k cache the benchmark times (4 x 8 GiB of
@@ -111,6 +113,35 @@ def test_head_dim_64_128k_layer():
     ls.flush(0)
     ls.check_planes(0)
     log(f"128k d64: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
+def test_grouped_queries_128k_layer():
+    """Grouped queries at the size the benchmark times: a Llama-3.1-8B-shaped layer of 8 cached
+    heads shared by 4 query heads each, head_dim 128, 131072 prefilled tokens plus a tail, the
+    grouped draft (32 query heads) and a 4-token grouped verify (16 query columns per cached
+    head), checked on cached heads 0, 5 and 7 against the oracle's passes over those heads."""
+    log("case: grouped queries, 128k layer, 8 cached heads x 4, cached heads 0/5/7 sampled")
+    H, D, ctx, g, mt = 8, 128, 131072, 4, 4
+    sampled = [0, 5, 7]
+    ls = Lockstep(1, 1, H, D, ctx + 4 * G, 15, heads=sampled, tag="gqa128k")
+    out = synth.outlier_channels(H, D, synth.seed_for(4, 2, "outlier"))
+    k, v = dev_kv(4, 2, 1, ctx + 64 + mt, H, D, outliers=out)
+    ls.prefill(0, k[:, :ctx + 64].contiguous(), v[:, :ctx + 64].contiguous())
+    ls.append(0, k[:, ctx + 64:].contiguous(), v[:, ctx + 64:].contiguous())
+    del k, v
+    gen = torch.Generator(device="cuda").manual_seed(4128)
+    qd_ = dev_q((1, H * g, D), gen, D)
+    qv_ = dev_q((1, mt, H * g, D), gen, D)
+    out_d = ls.gpu.attend_draft_gqa(0, qd_, g)
+    out_v = ls.gpu.attend_verify_gqa(0, qv_, g)
+    torch.cuda.synchronize()
+    for r in range(g):
+        heads = [h * g + r for h in sampled]
+        ref_d = ls.orc[0].attend_draft(0, qd_[:, heads].cpu().numpy())
+        ref_v = ls.orc[0].attend_verify(0, qv_[:, :, heads].contiguous().cpu().numpy())
+        ls._cmp_out(out_d[:, heads], ref_d, f"gqa draft r={r}")
+        ls._cmp_out(out_v[:, :, heads], ref_v, f"gqa verify r={r}")
+    log(f"gqa 128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
 def test_lwm_128k_32_layer_stack():
