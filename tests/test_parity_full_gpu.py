@@ -7,6 +7,7 @@ checked on sampled heads / layers that the CPU oracle can afford.
   * head_dim 64: the same round on a 128k layer of 32 heads x 64 channels.
   * Grouped queries: a Llama-3.1-8B-shaped 128k layer (8 cached heads x 4 query heads), the
     grouped draft and a 4-token grouped verify on sampled cached heads.
+  * Device mode: a gamma = 6 round and a flush through the device-mode verbs on a 128k layer.
   * LWM-128k-shaped layer in the split-upper layout: the 2-bit draft (plain and x8 queries),
     the 4-bit draft and verify over one prefilled layer.
   * LWM-128k-shaped stack: all 32 layers of the 128k cache the benchmark times (4 x 8 GiB of
@@ -142,6 +143,50 @@ def test_grouped_queries_128k_layer():
         ls._cmp_out(out_d[:, heads], ref_d, f"gqa draft r={r}")
         ls._cmp_out(out_v[:, :, heads], ref_v, f"gqa verify r={r}")
     log(f"gqa 128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
+def test_device_mode_128k_layer():
+    """Device mode at full size: the fixed work plan of the device-mode verbs (workers dealt
+    groups w, w + W, .. of whatever the sequence holds) over a 128k layer, one gamma = 6 round
+    of appends, drafts, rollback and verify, then an all-layer flush, against the oracle on
+    heads 0 and 31, and the counters and planes once back in host mode."""
+    log("case: device mode, 128k layer, heads 0/31 sampled")
+    H, D, ctx, gamma = 32, 128, 131072, 6
+    ls = Lockstep(1, 1, H, D, ctx + 4 * G, gamma, heads=[0, 31], tag="dev128k")
+    out = synth.outlier_channels(H, D, synth.seed_for(4, 3, "outlier"))
+    k, v = dev_kv(4, 3, 1, ctx + 64, H, D, outliers=out)
+    ls.prefill(0, k, v)
+    del k, v
+    ls.gpu.to_device_state()
+    gen = torch.Generator(device="cuda").manual_seed(4200)
+    od = torch.empty((1, H, D), dtype=torch.float32, device="cuda")
+    for s in range(gamma):
+        dk, dv = dev_kv(4, 3, 1, 1, H, D, outliers=out, salt=s + 1)
+        q = dev_q((1, H, D), gen, D)
+        ls.gpu.append_dev(0, dk, dv)
+        ls.gpu.attend_draft_dev(0, q, od)
+        ls.orc[0].append(0, ls._host_heads(dk, 2), ls._host_heads(dv, 2))
+        ref = ls.orc[0].attend_draft(0, ls._host_heads(q, 1))
+        torch.cuda.synchronize()
+        ls._cmp_out(od[:, ls.heads], ref, f"dev draft {s}")
+    tk, tv = dev_kv(4, 3, 1, gamma + 1, H, D, outliers=out, salt=100)
+    qv_ = dev_q((1, gamma + 1, H, D), gen, D)
+    ov = torch.empty((1, gamma + 1, H, D), dtype=torch.float32, device="cuda")
+    ls.gpu.rollback_dev(0, gamma)
+    ls.gpu.append_dev(0, tk, tv)
+    ls.gpu.attend_verify_dev(0, qv_, ov)
+    ls.orc[0].rollback(0, [gamma])
+    ls.orc[0].append(0, ls._host_heads(tk, 2), ls._host_heads(tv, 2))
+    ref = ls.orc[0].attend_verify(0, ls._host_heads(qv_, 2))
+    torch.cuda.synchronize()
+    ls._cmp_out(ov[:, :, ls.heads], ref, "dev verify")
+    ls.gpu.rollback_dev(0, 3)
+    ls.orc[0].rollback(0, [3])
+    ls.gpu.flush_dev(-1, G)
+    ls.orc[0].flush(0, G)
+    assert ls.gpu.from_device_state() == 0
+    ls.check_planes(0)
+    log(f"dev 128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
 def test_lwm_128k_32_layer_stack():
