@@ -32,7 +32,7 @@ hipError_t launch_attention_gqa(const AttnGqaArgs& a, int D, bool draft, hipStre
 hipError_t launch_attention_split(const AttnArgs& a, int D, bool draft, int fmt, hipStream_t st);
 hipError_t launch_attention_app_split(const AttnAppArgs& a, int D, bool draft, hipStream_t st);
 hipError_t launch_state(const StateArgs& a, hipStream_t st);
-int attention_slots(int D, bool draft, int B, int mode, bool meta16, int fmt);
+int attention_slots(int D, bool draft, int B, int mode, bool meta16, int fmt, bool pair = false);
 }  // namespace qs
 
 struct qs_cache {
@@ -310,11 +310,11 @@ static void attn_args(const qs_cache* c, int32_t layer, const void* d_q, int32_t
 }
 
 // Work plan for the sequences `seqs`: quantized workers sized to one resident round of the pass
-// kernel, next to the tail items.
+// kernel (pair: the grouped-query draft's paired form), next to the tail items.
 static qs::Plan attn_plan(const qs_cache* c, const qs::Seq* seqs, bool draft, int mode,
-                          int fmt = qs::kFmtNibble) {
+                          int fmt = qs::kFmtNibble, bool pair = false) {
   const qs_config& cf = c->cfg;
-  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, mode, cf.meta_fp16 != 0, fmt);
+  int slots = qs::attention_slots(cf.head_dim, draft, cf.batch, mode, cf.meta_fp16 != 0, fmt, pair);
   if (slots <= 0) slots = kFallbackSlots;
   int tail_items = 0;
   for (int b = 0; b < cf.batch; ++b)
@@ -378,7 +378,7 @@ static qs_status attend_gqa(qs_cache* c, int32_t layer, const void* d_q, int32_t
   if (s != QS_OK) return fail(c, s, err);
   qs::Seq seqs[QS_MAX_BATCH];
   for (int b = 0; b < cf.batch; ++b) seqs[b] = c->st.at(layer, b);
-  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeGqa);
+  const qs::Plan p = attn_plan(c, seqs, draft, qs::kModeGqa, qs::kFmtNibble, qs::gqa_paired(draft, mt * g));
   qs::AttnGqaArgs a{};
   attn_args(c, layer, d_q, mt * g, sm_scale, d_out, p, a);
   for (int b = 0; b < cf.batch; ++b) {

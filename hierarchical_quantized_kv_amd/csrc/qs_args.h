@@ -78,6 +78,11 @@ enum : int {
   kModeGqa = 3,     // counters by value; gq query heads share each cached (key/value) head
 };
 
+// The grouped-query draft runs the MFMA item's paired form (hi and lo parts of a query in the
+// columns j and j + 8 of one B operand) when its query columns fit in half an MFMA tile.
+constexpr int kPairMaxQueries = 8;
+constexpr bool gqa_paired(bool draft, int m) { return draft && m <= kPairMaxQueries; }
+
 // Layout of the upper planes that an attention kernel reads (a template parameter too):
 //   kFmtNibble  the upper nibble C_U as one 4-bit plane per stream (uk, uv);
 //   kFmtSplit4  split-upper layout: C_U = 4 C_T + C_M stored as a 2-bit top plane (first half of

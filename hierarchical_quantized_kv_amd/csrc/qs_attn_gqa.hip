@@ -7,7 +7,8 @@ hipError_t launch_attention_gqa(const AttnGqaArgs& a, int D, bool draft, hipStre
   return launch_attention_m<kModeGqa>(a, D, draft, st);
 }
 
-const void* attn_fn_gqa(int D, bool draft, int bucket, bool meta16) {
+const void* attn_fn_gqa(int D, bool draft, int bucket, bool meta16, bool pair) {
+  if (pair) return meta16 ? attn_fn_gqa_pair<true>(D, bucket) : attn_fn_gqa_pair<false>(D, bucket);
   return meta16 ? attn_fn_dm<kModeGqa, true>(D, draft, bucket) : attn_fn_dm<kModeGqa, false>(D, draft, bucket);
 }
 

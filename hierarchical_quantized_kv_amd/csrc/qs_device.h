@@ -206,6 +206,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppRor8 = 0x128;       // row_ror:8: lane j of a row reads lane j ^ 8
 __device__ __forceinline__ float lane_read(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
@@ -679,6 +680,11 @@ __device__ void draft_quant_item(const Args& a, int b, int h, int item, DraftLds
 //   PV MFMAs need, and reads them as one 8-byte piece of each value-plane row.
 //   O^T tile rt (16 channels x 16 queries) += A (value codes - 128) x B (p' of tiles 2q, 2q+1).
 // q' = q s and p' = p s enter the MFMAs as fp16 hi + lo pairs; the bias sums stay in fp32.
+// With up to kPairMaxQueries query columns (the paired form, PAIR), column j < 8 of a B operand
+// holds the hi part of query j and column j + 8 its lo part, so one MFMA takes both: S^T column
+// j and j ^ 8 are summed across the row (one DPP step per value), both lanes then hold the same
+// score and weight and feed p' hi (j < 8) or lo (j >= 8) to the PV MFMAs, and the O^T columns j
+// and j + 8 are summed once at the end.  Half the MFMAs and B registers of the 16-column form.
 
 template <int D>
 struct VerifyShape {
@@ -688,12 +694,18 @@ struct VerifyShape {
   static constexpr int KB = D / 8;    // key-row bytes per lane group
 };
 
-struct VerifyLds {
-  float2 qs[QS_MAX_QUERIES][64];     // queries times qscale, channels (2 lane, 2 lane + 1)
-  float2 vm[kGroup];                 // (s_t, s_t * (128 - z_t))
-  uint4 bq[2][4][64];                // q' B operands (hi, lo) per k-step and lane
-  float bias[QS_MAX_QUERIES][64];    // per-query bias partials of the lanes' channels
+// MQ: query capacity; PAIR: the paired form (hi and lo in the columns of one B operand)
+template <int MQ, bool PAIR>
+struct VerifyLdsQ {
+  static constexpr int kPlanes = PAIR ? 1 : 2;  // B operand sets: (hi, lo), or both in one
+  static constexpr int kCols = PAIR ? 16 : MQ;  // B columns held per k-step and k-group
+  float2 qs[MQ][64];                      // queries times qscale, channels (2 lane, 2 lane + 1)
+  float2 vm[kGroup];                      // (s_t, s_t * (128 - z_t))
+  uint4 bq[kPlanes][4][4 * kCols];        // q' B operands per k-step, k-group and column
+  float bias[MQ][64];                     // per-query bias partials of the lanes' channels
 };
+using VerifyLds = VerifyLdsQ<QS_MAX_QUERIES, false>;
+using VerifyLdsPair = VerifyLdsQ<kPairMaxQueries, true>;
 
 __device__ __forceinline__ int vtile_token(int tau, int r) {
   return 64 * (tau >> 2) + 16 * (r >> 2) + 8 * ((tau & 3) >> 1) + 2 * (r & 3) + (tau & 1);
@@ -798,9 +810,10 @@ struct VerifyAcc {
 // One group of a verify worker, in two 64-token halves.  With PF the buffers are refilled with
 // group gn as each part of group gi is consumed (a template flag, so that the number of loads in
 // flight at every wait is fixed).
-template <int D, bool PF, bool UPPER, bool M16, int FMT, class Args>
+template <int D, bool PF, bool UPPER, bool M16, int FMT, class Args, int MQ, bool PAIR>
 __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, VerifyBuf<D, M16>& buf,
-                                             int gi, int gn, VerifyLds& L, VerifyAcc<D>& st) {
+                                             int gi, int gn, VerifyLdsQ<MQ, PAIR>& L, VerifyAcc<D>& st) {
+  constexpr int COLS = VerifyLdsQ<MQ, PAIR>::kCols;
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
   // UPPER: every lower nibble is the draft offset
@@ -819,8 +832,8 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
     const int c0 = 2 * lane;
     const int gg = c0 / S::CPL, kk = (c0 % S::CPL) / 8, e0 = c0 % 8;  // e0 even, e0+1 odd
     const int s_even = e0 >> 1, s_odd = 4 + (e0 >> 1);                // slots of e0, e0+1
-    f16* bh16 = reinterpret_cast<f16*>(&L.bq[0][kk][16 * gg]);
-    f16* bl16 = reinterpret_cast<f16*>(&L.bq[1][kk][16 * gg]);
+    f16* bh16 = reinterpret_cast<f16*>(&L.bq[0][kk][COLS * gg]);
+    f16* bl16 = PAIR ? bh16 + 8 * 8 : reinterpret_cast<f16*>(&L.bq[PAIR ? 0 : 1][kk][COLS * gg]);
     for (int i = 0; i < m; ++i) {
       {
         const float2 qv = L.qs[i][lane];
@@ -848,11 +861,13 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
 #pragma unroll
   for (int kk = 0; kk < S::KK; ++kk) {
     Bq[kk] = __builtin_bit_cast(f16x8, L.bq[0][kk][lane]);
-    Bql[kk] = __builtin_bit_cast(f16x8, L.bq[1][kk][lane]);
+    if constexpr (!PAIR) Bql[kk] = __builtin_bit_cast(f16x8, L.bq[1][kk][lane]);
   }
-  float bias = 0.f;  // lanes 16g .. 16g+15 of query j, then across the four k-groups
+  // lanes 16g .. 16g+15 of query j, then across the four k-groups (paired form: only the hi
+  // columns j < 8 carry it)
+  float bias = 0.f;
   {
-    const float4* bp = reinterpret_cast<const float4*>(&L.bias[j][16 * g]);
+    const float4* bp = reinterpret_cast<const float4*>(&L.bias[PAIR ? (j & 7) : j][16 * g]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float4 v = bp[k];
@@ -860,6 +875,7 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
     }
     bias += __shfl_xor(bias, 16);
     bias += __shfl_xor(bias, 32);
+    if (PAIR && j >= 8) bias = 0.f;
   }
 
 #pragma unroll
@@ -872,9 +888,13 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
       for (int kk = 0; kk < S::KK; ++kk) {
         const f16x8 A = codes_f16(buf.ku[t][kk], UPPER ? loff : buf.kl[t][kk]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq[kk], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bql[kk], acc, 0, 0, 0);
+        if constexpr (!PAIR) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bql[kk], acc, 0, 0, 0);
       }
       St[t] = acc - bias;
+      if constexpr (PAIR) {  // hi products of column j plus lo products of column j ^ 8
+#pragma unroll
+        for (int i = 0; i < 4; ++i) St[t][i] += dpp<kDppRor8>(St[t][i]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -909,6 +929,7 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
         st.l_run += p;
         st.beta += p * sw.y;
         split_f16(wscale * (p * sw.x), ph[t][i], pl[t][i]);
+        if constexpr (PAIR) ph[t][i] = (j & 8) ? pl[t][i] : ph[t][i];
       }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -925,7 +946,7 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
         const f16x2 a2 = f16x2{A[4], A[5]} - c1152, a3 = f16x2{A[6], A[7]} - c1152;
         A = f16x8{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
         st.O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bp, st.O[rt], 0, 0, 0);
-        st.O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bpl, st.O[rt], 0, 0, 0);
+        if constexpr (!PAIR) st.O[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bpl, st.O[rt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -937,8 +958,9 @@ __device__ __forceinline__ void verify_group(const Args& a, const Streams& sm, V
   }
 }
 
-template <int D, bool UPPER, bool M16, int FMT, class Args>
-__device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyLds& L) {
+template <int D, bool UPPER, bool M16, int FMT, class Args, int MQ, bool PAIR>
+__device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyLdsQ<MQ, PAIR>& L) {
+  constexpr int NBQ = VerifyLdsQ<MQ, PAIR>::kPlanes * 4 * 4 * VerifyLdsQ<MQ, PAIR>::kCols;
   using S = VerifyShape<D>;
   const int lane = threadIdx.x;
   const int j = lane & 15;   // query column
@@ -954,8 +976,8 @@ __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyL
       const uint32_t qq = reinterpret_cast<const uint32_t*>(a.q + qrow(a, b, h, i) * D)[lane];
       L.qs[i][lane] = make_float2(lo_h(qq) * a.qscale, hi_h(qq) * a.qscale);
     }
-  for (int x = lane; x < 2 * 4 * 64; x += 64) (&L.bq[0][0][0])[x] = make_uint4(0, 0, 0, 0);
-  for (int x = lane; x < QS_MAX_QUERIES * 64; x += 64) (&L.bias[0][0])[x] = 0.f;
+  for (int x = lane; x < NBQ; x += 64) (&L.bq[0][0][0])[x] = make_uint4(0, 0, 0, 0);
+  for (int x = lane; x < MQ * 64; x += 64) (&L.bias[0][0])[x] = 0.f;
 
   VerifyAcc<D> st;
   st.m_run = -INFINITY;
@@ -985,6 +1007,12 @@ __device__ void verify_quant_item(const Args& a, int b, int h, int item, VerifyL
   st.l_run += __shfl_xor(st.l_run, 32);
   st.beta += __shfl_xor(st.beta, 16);
   st.beta += __shfl_xor(st.beta, 32);
+  if constexpr (PAIR) {  // O^T column j + 8 holds the lo part of query column j
+#pragma unroll
+    for (int rt = 0; rt < S::RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.O[rt][i] += dpp<kDppRor8>(st.O[rt][i]);
+  }
   if (j < m) {
     float* rec = record(a, D, b, h, item, j);
     if (g == 0) {
@@ -1168,12 +1196,15 @@ __device__ __forceinline__ int find_seq(const int32_t* base, int B, int idx) {
 }
 
 // The draft pass runs the VALU item (3 waves per SIMD), except over grouped queries, where both
-// passes run the MFMA item (2 waves per SIMD).
-template <int D, bool DRAFT, int NB, int MODE, bool M16, int FMT = kFmtNibble>
-__global__ __launch_bounds__(64, (DRAFT && MODE != kModeGqa) ? 3 : 2) void attn_kernel(
+// passes run the MFMA item: the draft in the paired form (PAIR, up to kPairMaxQueries query
+// columns; 11 KB of LDS and 3 waves per SIMD), the verify (and a draft of more columns) in the
+// 16-column form (21 KB, 2 waves per SIMD).
+template <int D, bool DRAFT, int NB, int MODE, bool M16, int FMT = kFmtNibble, bool PAIR = false>
+__global__ __launch_bounds__(64, (DRAFT && (MODE != kModeGqa || PAIR)) ? 3 : 2) void attn_kernel(
     const AttnArgsN<NB, MODE> a) {
   constexpr bool kValu = DRAFT && MODE != kModeGqa;
-  using PassLds = typename std::conditional<kValu, DraftLds, VerifyLds>::type;
+  using PassLds = typename std::conditional<kValu, DraftLds,
+      typename std::conditional<PAIR, VerifyLdsPair, VerifyLds>::type>::type;
   __shared__ union {
     PassLds p;
     TailLds t;
@@ -1821,12 +1852,12 @@ AppendArgsN<NB> narrow(const AppendArgs& f) {
   return a;
 }
 
-template <int D, bool DRAFT, int MODE, bool M16, int FMT = kFmtNibble>
+template <int D, bool DRAFT, int MODE, bool M16, int FMT = kFmtNibble, bool PAIR = false>
 const void* attn_fn(int bucket) {
   switch (bucket) {
-    case 1: return (const void*)attn_kernel<D, DRAFT, 1, MODE, M16, FMT>;
-    case 8: return (const void*)attn_kernel<D, DRAFT, 8, MODE, M16, FMT>;
-    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, MODE, M16, FMT>;
+    case 1: return (const void*)attn_kernel<D, DRAFT, 1, MODE, M16, FMT, PAIR>;
+    case 8: return (const void*)attn_kernel<D, DRAFT, 8, MODE, M16, FMT, PAIR>;
+    default: return (const void*)attn_kernel<D, DRAFT, QS_MAX_BATCH, MODE, M16, FMT, PAIR>;
   }
 }
 
@@ -1839,12 +1870,24 @@ const void* attn_fn_dm(int D, bool draft, int bucket) {
                     : (draft ? attn_fn<64, true, MODE, M16, FMT>(bucket) : attn_fn<64, false, MODE, M16, FMT>(bucket));
 }
 
+// The grouped-query draft in the paired form (m <= kPairMaxQueries query columns).
+template <bool M16>
+const void* attn_fn_gqa_pair(int D, int bucket) {
+  return D == 128 ? attn_fn<128, true, kModeGqa, M16, kFmtNibble, true>(bucket)
+                  : attn_fn<64, true, kModeGqa, M16, kFmtNibble, true>(bucket);
+}
+
 template <int D, bool DRAFT, int NB, int MODE, int FMT, class Full>
 hipError_t launch_attention_n(const Full& f, hipStream_t st) {
   const AttnArgsN<NB, MODE> a = narrow<NB>(f);
   const dim3 grid(a.n_titems_total + a.n_qitems_total, a.H);
+  constexpr bool kMayPair = MODE == kModeGqa && DRAFT && FMT == kFmtNibble;
   if constexpr (FMT != kFmtNibble)  // the split layout is built with fp32 metadata only
     hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, false, FMT>), grid, dim3(64), 0, st, a);
+  else if (kMayPair && gqa_paired(DRAFT, a.m) && a.meta16)
+    hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, true, FMT, kMayPair>), grid, dim3(64), 0, st, a);
+  else if (kMayPair && gqa_paired(DRAFT, a.m))
+    hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, false, FMT, kMayPair>), grid, dim3(64), 0, st, a);
   else if (a.meta16)
     hipLaunchKernelGGL((attn_kernel<D, DRAFT, NB, MODE, true>), grid, dim3(64), 0, st, a);
   else

@@ -85,39 +85,42 @@ hipError_t launch_flush(const FlushArgs& a, int D, int n_layers, hipStream_t st)
 const void* attn_fn_host(int D, bool draft, int bucket, bool meta16);
 const void* attn_fn_dev(int D, bool draft, int bucket, bool meta16);
 const void* attn_fn_app(int D, bool draft, int bucket, bool meta16);
-const void* attn_fn_gqa(int D, bool draft, int bucket, bool meta16);
+const void* attn_fn_gqa(int D, bool draft, int bucket, bool meta16, bool pair);
 const void* attn_fn_split_host(int D, bool draft, int bucket, int fmt);
 const void* attn_fn_split_app(int D, bool draft, int bucket);
-static const void* attn_fn_mode(int mode, int D, bool draft, int bucket, bool meta16, int fmt) {
+static const void* attn_fn_mode(int mode, int D, bool draft, int bucket, bool meta16, int fmt,
+                                bool pair) {
   if (fmt != kFmtNibble)  // split-upper layout: host mode and fused append only
     return mode == kModeAppend ? attn_fn_split_app(D, draft, bucket)
                                : attn_fn_split_host(D, draft, bucket, fmt);
   switch (mode) {
     case kModeDev: return attn_fn_dev(D, draft, bucket, meta16);
     case kModeAppend: return attn_fn_app(D, draft, bucket, meta16);
-    case kModeGqa: return attn_fn_gqa(D, draft, bucket, meta16);
+    case kModeGqa: return attn_fn_gqa(D, draft, bucket, meta16, pair);
     default: return attn_fn_host(D, draft, bucket, meta16);
   }
 }
 
 // Work-item slots of one attention pass on the current device: compute units times the
-// one-wave workgroups of that kernel a compute unit holds at once (cached per device).
-int attention_slots(int D, bool draft, int B, int mode, bool meta16, int fmt) {
+// one-wave workgroups of that kernel a compute unit holds at once (cached per device).  pair:
+// the grouped-query draft's paired form (gqa_paired).
+int attention_slots(int D, bool draft, int B, int mode, bool meta16, int fmt, bool pair) {
   constexpr int kMaxDev = 64;
   // filled on first use; concurrent callers at worst compute the same value twice
-  static std::atomic<int> cache[kMaxDev][3][2][2][2][4][3];
+  static std::atomic<int> cache[kMaxDev][3][2][2][2][4][3][2];
   int id = 0;
   if (hipGetDevice(&id) != hipSuccess || id < 0 || id >= kMaxDev || mode < 0 || mode > 3 ||
       fmt < 0 || fmt > 2)
     return 0;
+  pair = pair && mode == kModeGqa && draft && fmt == kFmtNibble;
   const int bucket = batch_bucket(B);
   std::atomic<int>& slot =
-      cache[id][fmt][meta16][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)];
+      cache[id][fmt][meta16][D == 128][draft][mode][bucket == 1 ? 0 : (bucket == 8 ? 1 : 2)][pair];
   const int known = slot.load(std::memory_order_relaxed);
   if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, id) != hipSuccess) return 0;
-  const void* fn = attn_fn_mode(mode, D, draft, bucket, meta16, fmt);
+  const void* fn = attn_fn_mode(mode, D, draft, bucket, meta16, fmt, pair);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess) return 0;
   const int n = cus * per_cu;
   slot.store(n, std::memory_order_relaxed);

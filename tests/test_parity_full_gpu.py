@@ -6,7 +6,7 @@ checked on sampled heads / layers that the CPU oracle can afford.
     formats.
   * head_dim 64: the same round on a 128k layer of 32 heads x 64 channels.
   * Grouped queries: a Llama-3.1-8B-shaped 128k layer (8 cached heads x 4 query heads), the
-    grouped draft and a 4-token grouped verify on sampled cached heads.
+    grouped draft (plain and x8 queries) and a 4-token grouped verify on sampled cached heads.
   * Device mode: a gamma = 6 round and a flush through the device-mode verbs on a 128k layer.
   * LWM-128k-shaped layer in the split-upper layout: the 2-bit draft (plain and x8 queries),
     the 4-bit draft and verify over one prefilled layer.
@@ -119,8 +119,9 @@ def test_head_dim_64_128k_layer():
 def test_grouped_queries_128k_layer():
     """Grouped queries at the size the benchmark times: a Llama-3.1-8B-shaped layer of 8 cached
     heads shared by 4 query heads each, head_dim 128, 131072 prefilled tokens plus a tail, the
-    grouped draft (32 query heads) and a 4-token grouped verify (16 query columns per cached
-    head), checked on cached heads 0, 5 and 7 against the oracle's passes over those heads."""
+    grouped draft (32 query heads, plain and x8) and a 4-token grouped verify (16 query columns
+    per cached head), checked on cached heads 0, 5 and 7 against the oracle's passes over those
+    heads."""
     log("case: grouped queries, 128k layer, 8 cached heads x 4, cached heads 0/5/7 sampled")
     H, D, ctx, g, mt = 8, 128, 131072, 4, 4
     sampled = [0, 5, 7]
@@ -132,15 +133,19 @@ def test_grouped_queries_128k_layer():
     del k, v
     gen = torch.Generator(device="cuda").manual_seed(4128)
     qd_ = dev_q((1, H * g, D), gen, D)
+    qd8 = (dev_q((1, H * g, D), gen, D).float() * 8).half()   # a peaky softmax
     qv_ = dev_q((1, mt, H * g, D), gen, D)
     out_d = ls.gpu.attend_draft_gqa(0, qd_, g)
+    out_d8 = ls.gpu.attend_draft_gqa(0, qd8, g)
     out_v = ls.gpu.attend_verify_gqa(0, qv_, g)
     torch.cuda.synchronize()
     for r in range(g):
         heads = [h * g + r for h in sampled]
         ref_d = ls.orc[0].attend_draft(0, qd_[:, heads].cpu().numpy())
+        ref_d8 = ls.orc[0].attend_draft(0, qd8[:, heads].cpu().numpy())
         ref_v = ls.orc[0].attend_verify(0, qv_[:, :, heads].contiguous().cpu().numpy())
         ls._cmp_out(out_d[:, heads], ref_d, f"gqa draft r={r}")
+        ls._cmp_out(out_d8[:, heads], ref_d8, f"gqa draft x8 r={r}")
         ls._cmp_out(out_v[:, :, heads], ref_v, f"gqa verify r={r}")
     log(f"gqa 128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
