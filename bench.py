@@ -61,18 +61,20 @@ PROFILES = os.path.join(ROOT, "profiles")
 # (Batch 1: the kernels' batch-bucket template argument is 1.)
 # Kernel names (as rocprofv3 prints them) of the default step: the attention kernels of the
 # fused append + attend calls (mode 2); --no-fuse runs the mode-0 ones.
-# The last attention argument is the metadata format (false: fp32 (scale, zero-point)).
-# The last attention argument is the upper-plane layout (0: one 4-bit plane).
-KERNELS = {"draft": "attn_kernel<128, true, 1, 2, false, 0>",
-           "verify": "attn_kernel<128, false, 1, 2, false, 0>",
+# The attention kernels' last three arguments: the metadata format (false: fp32 (scale,
+# zero-point)), the upper-plane layout (0: one 4-bit plane) and the paired MFMA form (used by the
+# grouped-query draft only).
+KERNELS = {"draft": "attn_kernel<128, true, 1, 2, false, 0, false>",
+           "verify": "attn_kernel<128, false, 1, 2, false, 0, false>",
            "combine": "combine_kernel<128, 1, 2, 0>", "flush": "flush_kernel<128>",
            "prefill": "prefill_kernel<128>"}
 
 
 def kernel_names(fuse):
     mode = 2 if fuse else 0
-    return (f"attn_kernel<128, true, 1, {mode}, false, 0>",
-            f"attn_kernel<128, false, 1, {mode}, false, 0>", f"combine_kernel<128, 1, {mode}, 0>")
+    return (f"attn_kernel<128, true, 1, {mode}, false, 0, false>",
+            f"attn_kernel<128, false, 1, {mode}, false, 0, false>",
+            f"combine_kernel<128, 1, {mode}, 0>")
 
 CONFIGS = {
     3: dict(name="Llama-2-7B-32K-shaped full stack", layers=32, heads=32, D=128, ctx=32768,
