@@ -932,12 +932,12 @@ def write_traffic_summary(fetch_dir, write_dir, args):
         "temp setup aside):",
         "",
         "```",
-        f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
+        f"timeout -s KILL 200 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
         f"\"attn_kernel|combine_kernel|flush_kernel|prefill_kernel|copy\" -d {fetch_dir} -o run "
         f"--output-format csv -- python -u bench.py --config {args.config} --layers 2 --steps 1 "
-        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --no-graph --no-gqa --no-meta16 --calibration-copy-mib "
-        f"{args.calibration_copy_mib}",
-        f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE (same arguments, -d {write_dir})",
+        f"--warmup 0 --flush-reps 2 --no-cpu-baseline --no-graph --no-gqa --no-meta16 --no-ctx32k "
+        f"--no-topk --calibration-copy-mib {args.calibration_copy_mib}",
+        f"timeout -s KILL 200 rocprofv3 --pmc WRITE_SIZE (same arguments, -d {write_dir})",
         f"python bench.py --config {args.config} --calibration-copy-mib "
         f"{args.calibration_copy_mib} --traffic-summary {fetch_dir} {write_dir}",
         "```",
