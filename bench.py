@@ -413,8 +413,9 @@ def main():
     # The accept / correct step after verify (qs_spec_accept): synthetic fp32 logits over a
     # 32000-token vocabulary, gamma drafted tokens, fresh uniforms per call; for one sequence (the
     # workload's batch) and for 32 (where the step is bound by reading the logits).  Algorithmic
-    # bytes: every logit read once; the kernels read them twice (row statistics, then the
-    # sampling totals) and one 4096-token part of two rows a third time.
+    # bytes: every logit read once; the kernels read them once for the row statistics, the one
+    # or two rows of each sequence's rejection point again, and one 4096-token part of those a
+    # third time.
     from hierarchical_quantized_kv_amd.binding import spec_accept, spec_workspace_bytes
     V_SPEC = 32000
     sa_ev = {1: [], 32: []}

@@ -16,15 +16,16 @@
 // Three launches, all fp32:
 //   row_stats_kernel  (max, sum of exp(x - max)) of every row in parts of 4096 tokens, one
 //                     workgroup per (row, part);
-//   part_sums_kernel  per candidate rejection point j = 0 .. gamma and part: the row statistics
-//                     of p_j and q_j merged, the part's totals of the sampling weights
-//                     ((p_j - q_j)_+, or p_gamma, and p_j itself), and (part 0) the acceptance
-//                     ratio of drafted token j, one workgroup each;
+//   part_sums_kernel  per part of a sequence: every row's statistics merged, the acceptance
+//                     tests (so the rejection point j), then the part's totals of the sampling
+//                     weights for that j only ((p_j - q_j)_+, or p_gamma, and p_j itself); part
+//                     0 also stores the row statistics and the acceptance ratios;
 //   accept_kernel     per sequence: the acceptance tests (one lane per drafted token, the first
 //                     failure is j), then the inverse CDF: the part from a scan of the part totals of the chosen j, the
 //                     token from one recomputation of that part.
-// So the whole vocabulary is read by many workgroups in parallel, and the one workgroup per
-// sequence reads only 4096 tokens of two rows.
+// So the whole vocabulary is read once by many workgroups in parallel, then the one or two rows
+// of the rejection point once more, and the one workgroup per sequence reads only 4096 tokens
+// of two rows.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -48,13 +49,16 @@ __host__ __device__ inline int row_parts(int V) { return (V + kPartTokens - 1) /
 //   part_stat [B][2 gamma + 1][np][2]  (max, sum of exp(x - max)) per row part; rows 0 .. gamma
 //                                      are the target rows, gamma+1 .. 2 gamma the draft rows
 //   row_stat  [B][2 gamma + 1][2]      (max, 1 / sum) per row
-//   part_sum  [B][gamma + 1][np][2]    per candidate j: the part's total of the sampling weight
-//                                      ((p_j - q_j)_+ for j < gamma, p_gamma for j = gamma) and
-//                                      of p_j
+//   part_sum  [B][np][2]               for the sequence's rejection point j: the part's total of
+//                                      the sampling weight ((p_j - q_j)_+ for j < gamma, p_gamma
+//                                      for j = gamma) and of p_j
 //   ratio     [B][gamma]               min(1, p_i(x_i) / (q_i(x_i) + 1e-8)), or -1 for a drafted
 //                                      token outside the vocabulary
+//   xlogit    [B][gamma][2]            the target and draft logits of drafted token x_i (rows i
+//                                      and gamma+1+i), stored by the row-statistics pass (not
+//                                      written for a token outside the vocabulary)
 struct WsLayout {
-  size_t part_stat, row_stat, part_sum, ratio, total;
+  size_t part_stat, row_stat, part_sum, ratio, xlogit, total;
 };
 __host__ __device__ inline WsLayout ws_layout(int B, int gamma, int np) {
   WsLayout L;
@@ -62,8 +66,9 @@ __host__ __device__ inline WsLayout ws_layout(int B, int gamma, int np) {
   L.part_stat = 0;
   L.row_stat = L.part_stat + rows * np * 2;
   L.part_sum = L.row_stat + rows * 2;
-  L.ratio = L.part_sum + (size_t)B * (gamma + 1) * np * 2;
-  L.total = L.ratio + (size_t)B * gamma;
+  L.ratio = L.part_sum + (size_t)B * np * 2;
+  L.xlogit = L.ratio + (size_t)B * gamma;
+  L.total = L.xlogit + (size_t)B * gamma * 2;
   return L;
 }
 
@@ -112,16 +117,38 @@ __device__ __forceinline__ void load_part_any(const float* row, int V, int part,
 }
 
 // grid: x = row (0 .. gamma: target rows, gamma+1 .. 2 gamma: draft rows), y = part, z = sequence.
-// Coalesced, all loads first.  The sums use the hardware exp2 (a few ulp per term).
+// Coalesced, all loads first.  The sums use the hardware exp2 (a few ulp per term).  The thread
+// that holds the logit of the row's drafted token (rows i < gamma and gamma+1+i: token x_i)
+// also stores it for the acceptance test.
 __global__ __launch_bounds__(kPartThreads) void row_stats_kernel(const float* __restrict__ t,
                                                                  const float* __restrict__ d,
+                                                                 const int32_t* __restrict__ tokens,
                                                                  int gamma, int V, float* ws) {
   __shared__ RowStat sh[kPartThreads / 64];
   const int r = blockIdx.x, part = blockIdx.y, b = blockIdx.z;
   const float* row = r <= gamma ? t + ((size_t)b * (gamma + 1) + r) * V
                                 : d + ((size_t)b * gamma + (r - gamma - 1)) * V;
+  const int di = r < gamma ? r : r - gamma - 1;  // the drafted token of this row, or -1
+  const int xtok = di >= 0 ? tokens[(size_t)b * gamma + di] : -1;
+  const bool vec = vec_ok(row, V);
   float x[kPartPer];
-  load_part_any(row, V, part, vec_ok(row, V), x);
+  load_part_any(row, V, part, vec, x);
+  {
+    const int off = xtok - part * kPartTokens;
+    if (xtok >= 0 && xtok < V && off >= 0 && off < kPartTokens) {
+      // the token's thread and slot in load_part_any's order
+      const int owner = vec ? ((off >> 2) & (kPartThreads - 1)) : (off & (kPartThreads - 1));
+      const int slot = vec ? ((off >> 10) * 4 + (off & 3)) : (off >> 8);
+      if ((int)threadIdx.x == owner) {
+        float val = x[0];
+#pragma unroll
+        for (int k = 1; k < kPartPer; ++k)
+          if (k == slot) val = x[k];
+        const WsLayout L = ws_layout(gridDim.z, gamma, row_parts(V));
+        ws[L.xlogit + ((size_t)b * gamma + di) * 2 + (r < gamma ? 0 : 1)] = val;
+      }
+    }
+  }
   float m = x[0];
 #pragma unroll
   for (int k = 1; k < kPartPer; ++k) m = fmaxf(m, x[k]);
@@ -183,31 +210,86 @@ __device__ void block_exclusive_scan(float x, float* ex, float* wsum) {
   __syncthreads();
 }
 
-// Row statistics (max, 1 / sum) of two rows of sequence b, merged from their parts by the
-// whole workgroup (thread t takes part t); rb < 0 skips the second row.
-__device__ void merge_rows(const float* part_stat, int np, size_t ra, long long rb, float2* out,
-                           RowStat (*sh)[kWaves]) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  RowStat a{-INFINITY, 0.f}, c{-INFINITY, 0.f};
-  if (tid < np) {
-    a = RowStat{part_stat[(ra * np + tid) * 2], part_stat[(ra * np + tid) * 2 + 1]};
-    if (rb >= 0) c = RowStat{part_stat[((size_t)rb * np + tid) * 2],
-                             part_stat[((size_t)rb * np + tid) * 2 + 1]};
+// Cross-lane steps with DPP inside rows of 16 lanes: quad_perm swaps inside groups of four, the
+// mirrors inside half rows and rows (for a max or a sum over a row, a mirror serves as well as
+// an exchange).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Row statistics (max, 1 / sum) of the R = 2 gamma + 1 rows of sequence b, merged from their
+// parts into out[r]: wave w takes rows w, w + kWaves, .. (all of its loads issued first), lane l
+// the parts l, l + 64, .. (merged in order), then per row the largest max over the lanes
+// holding parts, each lane's sum scaled to it once, and the scaled sums added.
+constexpr int kMaxRows = 2 * (QS_MAX_QUERIES - 1) + 1;
+constexpr int kRowsPerWave = (kMaxRows + kWaves - 1) / kWaves;
+__device__ void merge_all_rows(const float* part_stat, int np, int R, float2* out) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  RowStat a[kRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int r = wv + kWaves * k;
+    a[k] = (r < R && lane < np) ? RowStat{part_stat[((size_t)r * np + lane) * 2],
+                                          part_stat[((size_t)r * np + lane) * 2 + 1]}
+                                : RowStat{-INFINITY, 0.f};
   }
-  // lanes at or past np hold the identity: lane 0 of a wave needs only the lanes below np
-  for (int o = 1; o < np && o < 64; o <<= 1) {
-    a = merge(a, RowStat{__shfl_xor(a.m, o), __shfl_xor(a.s, o)});
-    c = merge(c, RowStat{__shfl_xor(c.m, o), __shfl_xor(c.s, o)});
+  for (int p0 = 64; p0 < np; p0 += 64) {  // vocabularies above 64 parts
+    const int pt = p0 + lane;
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) {
+      const int r = wv + kWaves * k;
+      if (r < R && pt < np)
+        a[k] = merge(a[k], RowStat{part_stat[((size_t)r * np + pt) * 2],
+                                   part_stat[((size_t)r * np + pt) * 2 + 1]});
+    }
   }
-  if (lane == 0) {
-    sh[0][wv] = a;
-    sh[1][wv] = c;
+  // lanes at or past np hold (-inf, 0), so lane 0 needs only the lanes below np: DPP steps
+  // within the first 16 lanes, then shuffles across rows of 16 lanes when there are more parts;
+  // every row of the wave goes through each step before the next
+  float m[kRowsPerWave], sum[kRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) m[k] = a[k].m;
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) m[k] = fmaxf(m[k], dpp<kDppXor1>(m[k]));
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) m[k] = fmaxf(m[k], dpp<kDppXor2>(m[k]));
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) m[k] = fmaxf(m[k], dpp<kDppHalfMirror>(m[k]));
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) m[k] = fmaxf(m[k], dpp<kDppMirror>(m[k]));
+  if (np > 16) {
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) m[k] = fmaxf(m[k], __shfl_xor(m[k], 16));
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) m[k] = fmaxf(m[k], __shfl_xor(m[k], 32));
   }
-  __syncthreads();
-  if (tid < 2) {
-    RowStat st = sh[tid][0];
-    for (int w = 1; w < kWaves && w * 64 < np; ++w) st = merge(st, sh[tid][w]);
-    out[tid] = make_float2(st.m, st.s > 0.f ? 1.f / st.s : 0.f);
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k)
+    sum[k] = a[k].m == -INFINITY ? 0.f : a[k].s * expf(a[k].m - m[k]);
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) sum[k] += dpp<kDppXor1>(sum[k]);
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) sum[k] += dpp<kDppXor2>(sum[k]);
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) sum[k] += dpp<kDppHalfMirror>(sum[k]);
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) sum[k] += dpp<kDppMirror>(sum[k]);
+  if (np > 16) {
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) sum[k] += __shfl_xor(sum[k], 16);
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k) sum[k] += __shfl_xor(sum[k], 32);
+  }
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int r = wv + kWaves * k;
+    if (lane == 0 && r < R) out[r] = make_float2(m[k], sum[k] > 0.f ? 1.f / sum[k] : 0.f);
   }
   __syncthreads();
 }
@@ -264,38 +346,52 @@ __device__ float part_rows(const float (&w)[kPartPer], float* tile, float* parti
   return tot;
 }
 
-// grid: x = candidate j (0 .. gamma), y = part, z = sequence.
+// grid: x = part, y = sequence.  Every workgroup of a sequence merges the row statistics, takes
+// the acceptance tests (the same fp32 operations on the same data in every workgroup, so all of
+// them find the same j) and then sums the sampling weights of its part for that j only.
 __global__ __launch_bounds__(kPartThreads) void part_sums_kernel(const float* __restrict__ t,
                                                                  const float* __restrict__ d,
                                                                  const int32_t* __restrict__ tokens,
+                                                                 const float* __restrict__ u,
                                                                  int gamma, int V, float* ws) {
-  __shared__ RowStat sh[2][kWaves];
-  __shared__ float2 st[2];
+  __shared__ float2 rowst[kMaxRows];
   __shared__ float2 wsum[kWaves];
-  const int j = blockIdx.x, part = blockIdx.y, b = blockIdx.z, B = gridDim.z;
+  __shared__ int s_j;
+  const int part = blockIdx.x, b = blockIdx.y, B = gridDim.y;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int np = row_parts(V);
+  const int np = row_parts(V), R = 2 * gamma + 1;
   const WsLayout L = ws_layout(B, gamma, np);
-  const size_t rp = (size_t)b * (2 * gamma + 1) + j;
-  const long long rq = j < gamma ? (long long)rp + gamma + 1 : -1;
-  merge_rows(ws + L.part_stat, np, rp, rq, st, sh);
-  const float2 pst = st[0], qst = j < gamma ? st[1] : make_float2(0.f, 0.f);
+  // the drafted tokens and their logits (lane i of wave 0: token i; the logits as the row
+  // statistics pass stored them, read whatever the token so that no load waits on another)
+  int x = -1;
+  float tx = 0.f, dx = 0.f, ui = 0.f;
+  if (tid < gamma) {
+    x = tokens[(size_t)b * gamma + tid];
+    tx = ws[L.xlogit + ((size_t)b * gamma + tid) * 2];
+    dx = ws[L.xlogit + ((size_t)b * gamma + tid) * 2 + 1];
+    ui = u[(size_t)b * (gamma + 1) + tid];
+  }
+  merge_all_rows(ws + L.part_stat + (size_t)b * R * np * 2, np, R, rowst);
+  if (tid < 64) {
+    // the acceptance ratio of drafted token i; a token outside the vocabulary is never
+    // accepted (u >= 0 > -1)
+    float acc = -1.f;
+    if (tid < gamma && x >= 0 && x < V)
+      acc = fminf(1.f, prob(tx, rowst[tid]) / (prob(dx, rowst[gamma + 1 + tid]) + 1e-8f));
+    const bool ok = tid < gamma && ui <= acc;
+    const unsigned long long fail = __ballot(tid < gamma && !ok);
+    if (tid == 0) s_j = fail ? __ffsll((long long)fail) - 1 : gamma;
+    if (part == 0 && tid < gamma) ws[L.ratio + (size_t)b * gamma + tid] = acc;
+  }
+  if (part == 0 && tid < R) {
+    ws[L.row_stat + ((size_t)b * R + tid) * 2] = rowst[tid].x;
+    ws[L.row_stat + ((size_t)b * R + tid) * 2 + 1] = rowst[tid].y;
+  }
+  __syncthreads();
+  const int j = s_j;
+  const float2 pst = rowst[j], qst = j < gamma ? rowst[gamma + 1 + j] : make_float2(0.f, 0.f);
   const float* trow = t + ((size_t)b * (gamma + 1) + j) * V;
   const float* drow = j < gamma ? d + ((size_t)b * gamma + j) * V : nullptr;
-  if (part == 0 && tid == 0) {
-    ws[L.row_stat + rp * 2] = pst.x;
-    ws[L.row_stat + rp * 2 + 1] = pst.y;
-    if (rq >= 0) {
-      ws[L.row_stat + rq * 2] = qst.x;
-      ws[L.row_stat + rq * 2 + 1] = qst.y;
-      // the acceptance ratio of drafted token j; a token outside the vocabulary is never
-      // accepted (u >= 0 > -1)
-      const int x = tokens[(size_t)b * gamma + j];
-      float acc = -1.f;
-      if (x >= 0 && x < V) acc = fminf(1.f, prob(trow[x], pst) / (prob(drow[x], qst) + 1e-8f));
-      ws[L.ratio + (size_t)b * gamma + j] = acc;
-    }
-  }
   // the part's totals, in any order (the sampler only uses them to pick a part and the point's
   // fraction of it): both rows in the same token order
   const bool vec = vec_ok(trow, V) && (!drow || vec_ok(drow, V));
@@ -321,7 +417,7 @@ __global__ __launch_bounds__(kPartThreads) void part_sums_kernel(const float* __
       tot.x += wsum[w].x;
       tot.y += wsum[w].y;
     }
-    float* o = ws + L.part_sum + (((size_t)b * (gamma + 1) + j) * np + part) * 2;
+    float* o = ws + L.part_sum + ((size_t)b * np + part) * 2;
     o[0] = tot.x;
     o[1] = tot.y;
   }
@@ -346,6 +442,9 @@ __global__ __launch_bounds__(kPartThreads) void accept_kernel(const float* __res
   __shared__ float partial[kPartPer * 17];
   __shared__ float row_tot[kPartPer];
   __shared__ int s_j, s_part, s_last_part, s_tok, s_row_last, s_part_last;
+  // the part totals of the rejection point (j-independent slots), loaded with the tests' inputs
+  const float* sums = ws + L.part_sum + (size_t)b * np * 2;
+  const float sum_r = tid < np ? sums[2 * tid] : 0.f, sum_p = tid < np ? sums[2 * tid + 1] : 0.f;
   if (tid < 64) {  // wave 0: lane i tests drafted token i; j = the first one that fails
     const bool ok = tid < gamma && ub[tid] <= ws[L.ratio + (size_t)b * gamma + tid];
     const unsigned long long fail = __ballot(tid < gamma && !ok);
@@ -360,15 +459,14 @@ __global__ __launch_bounds__(kPartThreads) void accept_kernel(const float* __res
   }
   __syncthreads();
   const int j = s_j;
-  const float* sums = ws + L.part_sum + ((size_t)b * (gamma + 1) + j) * np * 2;
   // the residual's part totals (p_gamma's when j = gamma); p_j's if the residual vanished in
   // rounding
   int plain = 0;
-  float mine = tid < np ? sums[2 * tid] : 0.f;
+  float mine = sum_r;
   block_exclusive_scan(mine, ex, wsum);
   if (!(ex[kPartThreads] > 0.f)) {
     plain = 1;
-    mine = tid < np ? sums[2 * tid + 1] : 0.f;
+    mine = sum_p;
     block_exclusive_scan(mine, ex, wsum);
   }
   const float total = ex[kPartThreads];
@@ -486,10 +584,10 @@ qs_status qs_spec_accept(const float* d_target_logits, const float* d_draft_logi
   const int np = qs_sample::row_parts(vocab);
   const dim3 block(qs_sample::kPartThreads);
   hipLaunchKernelGGL(qs_sample::row_stats_kernel, dim3(2 * gamma + 1, np, batch), block, 0, st,
-                     d_target_logits, d_draft_logits, gamma, vocab, ws);
-  if (hipGetLastError() != hipSuccess) return QS_ERR_DEVICE;
-  hipLaunchKernelGGL(qs_sample::part_sums_kernel, dim3(gamma + 1, np, batch), block, 0, st,
                      d_target_logits, d_draft_logits, d_draft_tokens, gamma, vocab, ws);
+  if (hipGetLastError() != hipSuccess) return QS_ERR_DEVICE;
+  hipLaunchKernelGGL(qs_sample::part_sums_kernel, dim3(np, batch), block, 0, st, d_target_logits,
+                     d_draft_logits, d_draft_tokens, d_uniforms, gamma, vocab, ws);
   if (hipGetLastError() != hipSuccess) return QS_ERR_DEVICE;
   hipLaunchKernelGGL(qs_sample::accept_kernel, dim3(batch), block, 0, st, d_target_logits,
                      d_draft_logits, d_uniforms, gamma, vocab, ws, d_n_accepted, d_next_token);

@@ -211,8 +211,9 @@ qs_status qs_flush(qs_cache* cache, int32_t layer, int32_t min_tail, void* strea
  * inverse CDF in token order from (p_j - q_j)_+ normalised, or from p_gamma when all were
  * accepted (from p_j if the residual has vanished in rounding).  All arithmetic is fp32.
  * d_workspace: device memory of at least qs_spec_workspace_bytes(batch, gamma, vocab) bytes
- * (row statistics and per-part sampling totals, fully rewritten by each call; calls that share
- * one workspace must be ordered on one stream); the outputs are device int32 [batch].  Asynchronous on `stream`; needs no
+ * (row statistics, the drafted tokens' logits and the rejection point's per-part sampling
+ * totals; every value a call uses is written earlier in that call; calls that share one
+ * workspace must be ordered on one stream); the outputs are device int32 [batch].  Asynchronous on `stream`; needs no
  * cache.  qs_spec_workspace_bytes returns 0 for arguments qs_spec_accept rejects.
  * Errors: QS_ERR_INVALID_ARG for a null pointer, batch outside 1..65535, gamma outside
  * 1..QS_MAX_QUERIES-1 or vocab outside 1..1048576; QS_ERR_BUFFER for a short workspace.

@@ -181,10 +181,10 @@ def test_device_mode_verbs_rejected_in_host_mode(lib):
 def test_spec_accept_validation_before_any_launch(lib):
     P = ctypes.c_void_p(FAKE)
     # per sequence, fp32: (max, sum) of each of the 2 gamma + 1 rows per 4096-token part, (max,
-    # 1/sum) per row, two sampling totals per candidate j = 0 .. gamma per part, and gamma
-    # acceptance ratios
+    # 1/sum) per row, the two sampling totals of the rejection point per part, gamma acceptance
+    # ratios and the target and draft logits of the gamma drafted tokens
     ws_bytes = lambda B, g, parts: B * (2 * (2 * g + 1) * parts + 2 * (2 * g + 1)
-                                        + 2 * (g + 1) * parts + g) * 4
+                                        + 2 * parts + g + 2 * g) * 4
     assert lib.qs_spec_workspace_bytes(2, 6, 100) == ws_bytes(2, 6, 1)       # one part
     assert lib.qs_spec_workspace_bytes(2, 6, 32000) == ws_bytes(2, 6, 8)     # eight parts
     assert lib.qs_spec_workspace_bytes(1, 15, 1 << 20) == ws_bytes(1, 15, 256)

@@ -55,7 +55,7 @@ def test_static_workspace_matches_caller_workspace_on_two_calls():
 
 
 def test_static_workspace_rejects_what_does_not_fit():
-    # 2048 sequences, gamma 15, a 128256-token vocabulary need ~25 MB of workspace (> 4 MiB);
+    # 2048 sequences, gamma 15, a 128256-token vocabulary need ~18 MB of workspace (> 4 MiB);
     # the check comes before any launch, so small placeholder tensors are never read
     B, gamma, V = 2048, 15, 128256
     assert binding.spec_workspace_bytes(B, gamma, V) > binding.SPEC_STATIC_BYTES
@@ -71,5 +71,5 @@ def test_static_workspace_rejects_what_does_not_fit():
                                              P(idx.data_ptr()), P(one.data_ptr()), 1, 0, 10,
                                              P(idx.data_ptr()), P(idx.data_ptr()), None)
     assert st == QS_ERR_INVALID_ARG
-    # a size that fits: batch 256, gamma 15, vocab 128256 (3.2 MB)
+    # a size that fits: batch 256, gamma 15, vocab 128256 (2.2 MB)
     assert binding.spec_workspace_bytes(256, 15, 128256) <= binding.SPEC_STATIC_BYTES
