@@ -364,11 +364,14 @@ def test_fused_append_attend_equals_append_then_attend(D, B):
 
 
 @pytest.mark.parametrize("D,g,mt,B", [(128, 4, 4, 3), (64, 2, 3, 3), (128, 8, 1, 3),
-                                      (64, 16, 1, 3), (128, 4, 2, 1), (64, 3, 5, 1)])
+                                      (64, 16, 1, 3), (128, 4, 2, 1), (64, 3, 5, 1),
+                                      (64, 8, 2, 2), (128, 9, 1, 2)])
 def test_grouped_queries_match_the_oracle(D, g, mt, B):
     """Grouped queries: query head h*g + r attends over cached head h.  The reference is the
     oracle's own draft / verify over the cached heads, called once per r with the queries of
-    heads h*g + r.  Ragged batch: a tail-only sequence, one with a two-chunk tail."""
+    heads h*g + r.  Ragged batch: a tail-only sequence, one with a two-chunk tail.  The drafts
+    with g <= 8 run the paired MFMA form (g = 8: all 16 columns), g = 9 and 16 the 16-column
+    form."""
     log(f"case: grouped queries D={D} g={g} m={mt} B={B}")
     H = 2
     ls = Lockstep(1, B, H, D, 8 * G, 15, tag=f"gqa{D}x{g}x{mt}x{B}")
