@@ -363,6 +363,32 @@ def test_fused_append_attend_equals_append_then_attend(D, B):
     plain.close()
 
 
+def test_grouped_verify_in_two_calls_matches_one_causal_verify():
+    """A grouped verify wider than one call's query columns (7 tokens x 4 query heads = 28 >
+    gamma_max + 1) run as two append + verify calls (4 tokens, then 3): each call's tokens see the
+    tail causally, so together they equal the oracle's single 7-token verify of every query head
+    (per r, over the cached heads)."""
+    log("case: grouped verify of 7 tokens x 4 query heads in two calls")
+    H, D, g, m = 2, 128, 4, 7
+    ls = Lockstep(1, 1, H, D, 8 * G, 15, tag="gqa-split")
+    k, v = kv(1, 3 * G + 50, H, D, 1201)
+    ls.prefill(0, k, v)
+    kt, vt = kv(1, m, H, D, 1202)
+    q = qv(1, m, H * g, D, 1203)
+    ls.gpu.append(0, kt[:, :4].contiguous(), vt[:, :4].contiguous())
+    out1 = ls.gpu.attend_verify_gqa(0, q[:, :4].contiguous(), g)
+    ls.gpu.append(0, kt[:, 4:].contiguous(), vt[:, 4:].contiguous())
+    out2 = ls.gpu.attend_verify_gqa(0, q[:, 4:].contiguous(), g)
+    torch.cuda.synchronize()
+    ls.orc[0].append(0, kt.cpu().numpy(), vt.cpu().numpy())
+    for r in range(g):
+        heads = [h * g + r for h in range(H)]
+        ref = ls.orc[0].attend_verify(0, q[:, :, heads].contiguous().cpu().numpy())
+        ls._cmp_out(out1[:, :, heads], ref[:, :4], f"split verify first r={r}")
+        ls._cmp_out(out2[:, :, heads], ref[:, 4:], f"split verify second r={r}")
+    log(f"gqa split verify: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+
+
 @pytest.mark.parametrize("D,g,mt,B", [(128, 4, 4, 3), (64, 2, 3, 3), (128, 8, 1, 3),
                                       (64, 16, 1, 3), (128, 4, 2, 1), (64, 3, 5, 1),
                                       (64, 8, 2, 2), (128, 9, 1, 2)])
