@@ -116,16 +116,19 @@ def test_head_dim_64_128k_layer():
     log(f"128k d64: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
-def test_grouped_queries_128k_layer():
+@pytest.mark.parametrize("D", [128, 64])
+def test_grouped_queries_128k_layer(D):
     """Grouped queries at the size the benchmark times: a Llama-3.1-8B-shaped layer of 8 cached
-    heads shared by 4 query heads each, head_dim 128, 131072 prefilled tokens plus a tail, the
+    heads shared by 4 query heads each, head_dim 128 (and the same at head_dim 64, whose paired
+    draft runs at 4 waves per SIMD), 131072 prefilled tokens plus a tail, the
     grouped draft (32 query heads, plain and x8) and a 4-token grouped verify (16 query columns
     per cached head), checked on cached heads 0, 5 and 7 against the oracle's passes over those
     heads."""
-    log("case: grouped queries, 128k layer, 8 cached heads x 4, cached heads 0/5/7 sampled")
-    H, D, ctx, g, mt = 8, 128, 131072, 4, 4
+    log(f"case: grouped queries, 128k layer, head_dim {D}, 8 cached heads x 4, cached heads "
+        f"0/5/7 sampled")
+    H, ctx, g, mt = 8, 131072, 4, 4
     sampled = [0, 5, 7]
-    ls = Lockstep(1, 1, H, D, ctx + 4 * G, 15, heads=sampled, tag="gqa128k")
+    ls = Lockstep(1, 1, H, D, ctx + 4 * G, 15, heads=sampled, tag=f"gqa128k-d{D}")
     out = synth.outlier_channels(H, D, synth.seed_for(4, 2, "outlier"))
     k, v = dev_kv(4, 2, 1, ctx + 64 + mt, H, D, outliers=out)
     ls.prefill(0, k[:, :ctx + 64].contiguous(), v[:, :ctx + 64].contiguous())
@@ -147,7 +150,7 @@ def test_grouped_queries_128k_layer():
         ls._cmp_out(out_d[:, heads], ref_d, f"gqa draft r={r}")
         ls._cmp_out(out_d8[:, heads], ref_d8, f"gqa draft x8 r={r}")
         ls._cmp_out(out_v[:, :, heads], ref_v, f"gqa verify r={r}")
-    log(f"gqa 128k: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
+    log(f"gqa 128k d{D}: max abs {ls.max_abs:.3e} max rel {ls.max_rel:.3e}")
 
 
 def test_device_mode_128k_layer():
