@@ -290,7 +290,9 @@ qs_status qs_attend_draft_bits(qs_cache* cache, int32_t layer, const void* d_q, 
  * MFMA; the draft reads only the upper planes, its lower nibbles being draft_offset), so the
  * cached bytes are read once per group of g query heads.
  * Errors: as qs_attend_draft / qs_attend_verify; QS_ERR_INVALID_ARG if g is outside 1..16 or
- * m*g > gamma_max + 1 (the split workspace holds gamma_max + 1 query columns per head).
+ * m*g > gamma_max + 1 (the split workspace holds gamma_max + 1 query columns per head).  A
+ * wider verify splits into calls in token order, each after the append of its own tokens (the
+ * causal mask then gives every token the same view of the tail as one call would).
  * [QuantSpec Guide, "Empirical Evaluation: QuantSpec Benchmark Results" (LLaMA-3.1-8B among the
  * evaluated models, whose key/value heads are shared by groups of query heads); the passes as
  * in qs_attend_draft / qs_attend_verify.] */
